@@ -1,0 +1,225 @@
+/*
+ * flashot.h -- streamed log-domain Sinkhorn for squared-Euclidean entropic
+ * optimal transport on AMD Instinct MI355X (gfx950).
+ *
+ * The method is the one on the page "FlashSinkhorn: IO-Aware Entropic
+ * Optimal Transport on GPU" (arXiv 2602.03067): each stabilised Sinkhorn
+ * half-step is a row-wise log-sum-exp of a biased dot-product score
+ * (Prop. 1, §3.1, App. D.1), evaluated tile by tile with an online max /
+ * sum-of-exponentials so that only the n- and m-length potentials are
+ * written to memory (App. D.2, D.3, G.1-G.2); the transport plan is applied
+ * to a matrix the same way without ever forming it (§3.2, Prop. 3, App. E.1).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Measures mu = sum_i a_i delta_{x_i} (n points) and nu = sum_j b_j
+ *    delta_{y_j} (m points) in R^d, cost C_ij = ||x_i - y_j||^2.
+ *  - Potentials f (n) and g (m) are the UNSHIFTED dual potentials. The
+ *    coupling they induce is P_ij = a_i b_j exp((f_i + g_j - C_ij) / eps).
+ *  - Half-steps (§3.1, alternating schedule eq. 2-3):
+ *        f_i = -eps * LSE_j((g_j - C_ij)/eps + log b_j)
+ *        g_j = -eps * LSE_i((f_i - C_ij)/eps + log a_i)
+ *    computed as f_i = ||x_i||^2 - eps * LSE_j(2 x_i.y_j/eps + (g_j - ||y_j||^2)/eps
+ *    + log b_j), the biased dot-product form of Prop. 1 / App. D.1.
+ *  - All array arguments are DEVICE pointers on the current HIP device unless
+ *    stated otherwise; the caller owns every buffer. The library never
+ *    allocates or frees device memory: scratch comes from the caller's
+ *    workspace. Calling with ws == NULL writes the required workspace size to
+ *    *ws_bytes and does nothing else (returns OT_OK).
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *    and returns without synchronising, except where a function says so.
+ *  - Point arrays are row-major: element (i, k) of X is at x[i * ldx + k],
+ *    ldx >= d. Their storage type is OT_F32 (float) or OT_BF16 (bfloat16);
+ *    products are accumulated in fp32, potentials and weights are fp32.
+ *  - Outputs must not alias inputs, except that f (resp. g) may be updated in
+ *    place where documented.
+ *  - Weights a, b must be strictly positive; NULL means uniform (1/n, 1/m).
+ *    They are used as given (not renormalised).
+ *  - Return value: an OT_* status. Argument checks run on the host before any
+ *    HIP call. A HIP failure (launch, runtime) returns OT_ERR_HIP; the message
+ *    of the last failure is available from ot_last_error().
+ */
+#ifndef FLASHOT_H
+#define FLASHOT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define OT_OK              0
+#define OT_ERR_INVALID_ARG 1  /* null pointer, size < 1, eps <= 0, ld < d, bad flag */
+#define OT_ERR_UNSUPPORTED 2  /* dtype or size outside what the kernels handle */
+#define OT_ERR_WORKSPACE   3  /* workspace smaller than required */
+#define OT_ERR_HIP         4  /* HIP runtime / launch error */
+#define OT_ERR_NONFINITE   5  /* a potential became NaN or infinite (reported by ot_solve) */
+
+/* Storage types of point / value arrays. */
+#define OT_F32  0
+#define OT_BF16 1
+
+/* ot_solve initialisation. */
+#define OT_INIT_ZERO  0  /* start from f = g = 0 */
+#define OT_INIT_GIVEN 1  /* start from the caller's f, g (warm start / resume) */
+
+/* ot_apply_plan flags. */
+#define OT_TRANSPOSE 1  /* compute P^T U (U has n rows) instead of P V (V has m rows) */
+#define OT_GRAD      2  /* out = 2 (r * X - P Y), the X-gradient (Y-gradient with OT_TRANSPOSE); V is ignored */
+#define OT_BARY      4  /* out = (P V) / r row-wise: entropic barycentric projection */
+
+/* Largest supported point dimension and value-column count. */
+#define OT_MAX_D    8192
+#define OT_MAX_COLS 8192
+
+/*
+ * The problem: two point clouds, their weights and eps (App. H.2 problem
+ * statement: discrete measures, squared-Euclidean cost, entropic
+ * regularisation eps).
+ *   x, y        device, row-major n x d (resp. m x d), storage `dtype`
+ *   n, m        number of points, >= 1
+ *   d           dimension, 1 <= d <= OT_MAX_D
+ *   ldx, ldy    row strides in elements, >= d
+ *   dtype       OT_F32 or OT_BF16 (both clouds)
+ *   eps         regularisation, > 0
+ *   a, b        device fp32 weights (n, m) or NULL for uniform
+ *   x_sqn,y_sqn device fp32 squared norms ||x_i||^2, ||y_j||^2, or NULL to
+ *               have them computed into the workspace
+ */
+typedef struct ot_problem {
+  const void* x;
+  const void* y;
+  int64_t n, m, d, ldx, ldy;
+  int32_t dtype;
+  float eps;
+  const float* a;
+  const float* b;
+  const float* x_sqn;
+  const float* y_sqn;
+} ot_problem;
+
+/* ot_solve options. Zero-initialise and set what you need. */
+typedef struct ot_solve_opts {
+  int32_t iters;        /* number of alternating iterations T (>= 0) */
+  float tol;            /* > 0: stop early once the row-marginal L1 error falls below tol */
+  int32_t check_every;  /* iterations between tolerance checks (>= 1 when tol > 0) */
+  int32_t init;         /* OT_INIT_ZERO or OT_INIT_GIVEN */
+  int32_t use_graph;    /* 1: replay a captured HIP graph per block of iterations; 0: plain launches */
+  int32_t splits_f;     /* column splits of the f half-step (0 = automatic) */
+  int32_t splits_g;     /* column splits of the g half-step (0 = automatic) */
+  int32_t timing;       /* 1: time every log-sum-exp kernel with HIP events (needs info) */
+} ot_solve_opts;
+
+/* ot_solve results (host memory). */
+typedef struct ot_solve_info {
+  int32_t iters_done;    /* iterations actually run */
+  int32_t nonfinite;     /* 1 if the final f or g holds NaN / Inf */
+  float marg_err_row;    /* ||P 1 - a||_1 of the returned (f, g) */
+  float marg_err_col;    /* ||P^T 1 - b||_1 of the returned (f, g) */
+  float lse_ms;          /* with opts.timing: summed duration of the log-sum-exp kernels (ms) */
+  int32_t lse_launches;  /* with opts.timing: number of log-sum-exp kernel launches timed */
+  int32_t splits_f;      /* column splits used by the f half-step */
+  int32_t splits_g;      /* column splits used by the g half-step */
+} ot_solve_info;
+
+/*
+ * ot_sqnorms -- out[i] = sum_k pts[i*ld + k]^2 in fp32 (App. D.1: alpha_i =
+ * ||x_i||^2, beta_j = ||y_j||^2, the per-point terms of the affine cost
+ * decomposition of §3.1 "Scope of cost structure").
+ *   pts    device, rows x d, storage dtype (OT_F32 / OT_BF16), row stride ld
+ *   out    device fp32, rows
+ * Errors: OT_ERR_INVALID_ARG (null, rows < 1, d < 1, ld < d),
+ *         OT_ERR_UNSUPPORTED (dtype, d > OT_MAX_D), OT_ERR_HIP.
+ */
+int ot_sqnorms(const void* pts, int dtype, int64_t rows, int64_t d, int64_t ld,
+               float* out, void* stream);
+
+/*
+ * ot_update_f -- one f half-step from g (Algorithm 1 of the page, §3.1 eq. 2,
+ * Prop. 1): f_i = -eps * LSE_j((g_j - C_ij)/eps + log b_j), streamed over the
+ * columns with an online max / sum of exponentials (App. D.3).
+ *   g     device fp32, m (input)
+ *   f     device fp32, n (output; may be the caller's previous f, updated in place)
+ *   err   device fp32 scalar or NULL. When set, f must hold the previous
+ *         potential f_old on entry and *err receives ||P(f_old, g) 1 - a||_1
+ *         = sum_i a_i |exp((f_old_i - f_i)/eps) - 1| (App. E.1 induced row
+ *         marginal), the row-marginal error of the coupling before the update.
+ *   ws, ws_bytes  workspace (see conventions)
+ * Errors: OT_ERR_INVALID_ARG, OT_ERR_UNSUPPORTED, OT_ERR_WORKSPACE, OT_ERR_HIP.
+ */
+int ot_update_f(const ot_problem* p, const float* g, float* f, float* err,
+                void* ws, size_t* ws_bytes, void* stream);
+
+/*
+ * ot_update_g -- one g half-step from f (Algorithm 3 of the page, §3.1 eq. 3,
+ * App. D.1 "the g-hat update"): g_j = -eps * LSE_i((f_i - C_ij)/eps + log a_i),
+ * the f half-step with the roles of (x, a, f) and (y, b, g) exchanged.
+ *   f     device fp32, n (input);  g  device fp32, m (output, in place allowed)
+ *   err   as in ot_update_f with columns: ||P(f, g_old)^T 1 - b||_1.
+ * Errors: as ot_update_f.
+ */
+int ot_update_g(const ot_problem* p, const float* f, float* g, float* err,
+                void* ws, size_t* ws_bytes, void* stream);
+
+/*
+ * ot_solve -- `opts->iters` alternating iterations (§3.1 eq. 2-3; §4.1 / App.
+ * H.2: fixed iteration count, no eps-scaling, no debiasing): each iteration is
+ * an f half-step from the current g followed by a g half-step from the new f.
+ *   f, g   device fp32 (n, m): output potentials; with OT_INIT_GIVEN also the
+ *          starting point (k then k' iterations equal k + k' iterations).
+ *   opts   host, required
+ *   info   host or NULL. When non-NULL the call synchronises the stream at the
+ *          end and fills every field; marg_err_row / marg_err_col are then the
+ *          exact L1 marginal errors of the returned (f, g), at the cost of two
+ *          extra streamed passes.
+ *   With opts->tol > 0 the row-marginal error of the current coupling is
+ *   evaluated inside every f half-step (it is r - a for r of App. E.1) and the
+ *   host reads it every opts->check_every iterations (one synchronisation per
+ *   check); the loop stops after the iteration in which it fell below tol.
+ * Errors: as ot_update_f, plus OT_ERR_NONFINITE when info is given and the
+ * final potentials are not finite.
+ */
+int ot_solve(const ot_problem* p, float* f, float* g, const ot_solve_opts* opts,
+             ot_solve_info* info, void* ws, size_t* ws_bytes, void* stream);
+
+/*
+ * ot_apply_plan -- apply the coupling induced by (f, g) to a matrix without
+ * forming it (Algorithm 2 / Prop. 3 for P V, Algorithm 4 / App. E.1 for
+ * P^T U): out = P V, or P^T U with OT_TRANSPOSE. The identity holds for any
+ * potentials (§3.2), so early-stopped potentials apply their own coupling.
+ *   f, g    device fp32 (n, m)
+ *   V       device, (m x cols) for P V or (n x cols) for P^T U, row stride ldv,
+ *           storage v_dtype (OT_F32 / OT_BF16); products run in fp32
+ *   cols    1 <= cols <= OT_MAX_COLS
+ *   flags   0 or OT_TRANSPOSE, optionally with one of OT_GRAD / OT_BARY
+ *   out     device fp32, row-major (n x cols) or (m x cols), stride cols
+ *           - default:      out = P V            (resp. P^T U)
+ *           - OT_BARY:      out = (P V) / r      (resp. (P^T U) / c), the
+ *                           entropic barycentric projection of §3.2
+ *           - OT_GRAD:      out = 2 (r * X - P Y) (n x d), the gradient in X of
+ *                           sum_ij P_ij ||x_i - y_j||^2 with P held fixed
+ *                           (§2.2 / App. G.1, induced marginals); with
+ *                           OT_TRANSPOSE the Y-gradient 2 (c * Y - P^T X)
+ *                           (m x d). V, v_dtype, cols and ldv are ignored:
+ *                           the other cloud is the value matrix.
+ *   marg    device fp32 (n, or m with OT_TRANSPOSE) or NULL: receives the
+ *           induced marginal r = P 1 (resp. c = P^T 1)
+ * Errors: OT_ERR_INVALID_ARG, OT_ERR_UNSUPPORTED, OT_ERR_WORKSPACE, OT_ERR_HIP.
+ */
+int ot_apply_plan(const ot_problem* p, const float* f, const float* g,
+                  const void* V, int v_dtype, int64_t cols, int64_t ldv, int flags,
+                  float* out, float* marg, void* ws, size_t* ws_bytes, void* stream);
+
+/* Text of the most recent error in this thread ("" if none). Host pointer, valid until the next call. */
+const char* ot_last_error(void);
+
+/* Library version, e.g. "flashot 0.1 gfx950". */
+const char* ot_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLASHOT_H */

@@ -1,0 +1,263 @@
+"""Python binding of ``libflashot.so``: streamed log-domain Sinkhorn on MI355X.
+
+Argument marshalling only. Every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/flashot.h``; this module turns
+torch tensors into device pointers, allocates the caller-owned workspace with
+torch, passes torch's current stream, and maps status codes to exceptions.
+There is no CPU fallback: if the library is not built every entry point raises.
+
+Functions (same names as the C entry points):
+    ot_sqnorms(pts, out=None)
+    ot_update_f(prob, g, f, err=None)
+    ot_update_g(prob, f, g, err=None)
+    ot_solve(prob, f, g, iters, ...)
+    ot_apply_plan(prob, f, g, V=None, flags=0, out=None, marg=None)
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from dataclasses import dataclass
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libflashot.so")
+HEADER_PATH = os.path.join(os.path.dirname(HERE), "include", "flashot.h")
+
+OT_OK, OT_ERR_INVALID_ARG, OT_ERR_UNSUPPORTED, OT_ERR_WORKSPACE, OT_ERR_HIP, OT_ERR_NONFINITE = range(6)
+OT_F32, OT_BF16 = 0, 1
+OT_INIT_ZERO, OT_INIT_GIVEN = 0, 1
+OT_TRANSPOSE, OT_GRAD, OT_BARY = 1, 2, 4
+
+
+class OtError(RuntimeError):
+    def __init__(self, code: int, where: str, msg: str):
+        super().__init__(f"{where} failed with status {code}: {msg}")
+        self.code = code
+
+
+class OtProblem(ctypes.Structure):
+    _fields_ = [
+        ("x", ctypes.c_void_p), ("y", ctypes.c_void_p),
+        ("n", ctypes.c_int64), ("m", ctypes.c_int64), ("d", ctypes.c_int64),
+        ("ldx", ctypes.c_int64), ("ldy", ctypes.c_int64),
+        ("dtype", ctypes.c_int32), ("eps", ctypes.c_float),
+        ("a", ctypes.c_void_p), ("b", ctypes.c_void_p),
+        ("x_sqn", ctypes.c_void_p), ("y_sqn", ctypes.c_void_p),
+    ]
+
+
+class OtSolveOpts(ctypes.Structure):
+    _fields_ = [
+        ("iters", ctypes.c_int32), ("tol", ctypes.c_float), ("check_every", ctypes.c_int32),
+        ("init", ctypes.c_int32), ("use_graph", ctypes.c_int32),
+        ("splits_f", ctypes.c_int32), ("splits_g", ctypes.c_int32), ("timing", ctypes.c_int32),
+    ]
+
+
+class OtSolveInfo(ctypes.Structure):
+    _fields_ = [
+        ("iters_done", ctypes.c_int32), ("nonfinite", ctypes.c_int32),
+        ("marg_err_row", ctypes.c_float), ("marg_err_col", ctypes.c_float),
+        ("lse_ms", ctypes.c_float), ("lse_launches", ctypes.c_int32),
+        ("splits_f", ctypes.c_int32), ("splits_g", ctypes.c_int32),
+    ]
+
+    def as_dict(self):
+        return {k: getattr(self, k) for k, _ in self._fields_}
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libflashot.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m streaming_sinkhorn_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+    szp = ctypes.POINTER(ctypes.c_size_t)
+    pp = ctypes.POINTER(OtProblem)
+    L.ot_sqnorms.argtypes = [vp, i32, i64, i64, i64, vp, vp]
+    L.ot_update_f.argtypes = [pp, vp, vp, vp, vp, szp, vp]
+    L.ot_update_g.argtypes = [pp, vp, vp, vp, vp, szp, vp]
+    L.ot_solve.argtypes = [pp, vp, vp, ctypes.POINTER(OtSolveOpts), ctypes.POINTER(OtSolveInfo), vp, szp, vp]
+    L.ot_apply_plan.argtypes = [pp, vp, vp, vp, i32, i64, i64, i32, vp, vp, vp, szp, vp]
+    for fn in ("ot_sqnorms", "ot_update_f", "ot_update_g", "ot_solve", "ot_apply_plan"):
+        getattr(L, fn).restype = ctypes.c_int
+    L.ot_last_error.restype = ctypes.c_char_p
+    L.ot_last_error.argtypes = []
+    L.ot_version.restype = ctypes.c_char_p
+    L.ot_version.argtypes = []
+    _lib = L
+    return L
+
+
+def header_entry_points() -> list[str]:
+    """Names of the functions declared in include/flashot.h."""
+    txt = open(HEADER_PATH).read()
+    return re.findall(r"^\s*(?:int|const char\*)\s+(ot_\w+)\s*\(", txt, re.M)
+
+
+def _check(code: int, where: str):
+    if code != OT_OK:
+        msg = lib().ot_last_error().decode(errors="replace")
+        raise OtError(code, where, msg)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return OT_F32
+    if t.dtype == torch.bfloat16:
+        return OT_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}: use float32 or bfloat16")
+
+
+def _rows(t: torch.Tensor, name: str):
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be 2-D with unit stride along dimension 1")
+    return t.shape[0], t.shape[1], t.stride(0)
+
+
+def _vec(t, name, length, device):
+    if t is None:
+        return None
+    if t.dtype != torch.float32 or t.dim() != 1 or t.numel() != length or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 vector of length {length}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    return t
+
+
+@dataclass
+class Problem:
+    """Keeps the tensors of an ot_problem alive next to its C struct."""
+    X: torch.Tensor
+    Y: torch.Tensor
+    eps: float
+    a: torch.Tensor | None = None
+    b: torch.Tensor | None = None
+    x_sqn: torch.Tensor | None = None
+    y_sqn: torch.Tensor | None = None
+
+    def __post_init__(self):
+        n, d, ldx = _rows(self.X, "X")
+        m, d2, ldy = _rows(self.Y, "Y")
+        if d != d2:
+            raise ValueError("X and Y must have the same number of columns")
+        if self.X.dtype != self.Y.dtype:
+            raise ValueError("X and Y must have the same dtype")
+        dev = self.X.device
+        self.device = dev
+        self.n, self.m, self.d = n, m, d
+        self.c = OtProblem(
+            _ptr(self.X), _ptr(self.Y), n, m, d, ldx, ldy, _dtype_code(self.X), float(self.eps),
+            _ptr(_vec(self.a, "a", n, dev)), _ptr(_vec(self.b, "b", m, dev)),
+            _ptr(_vec(self.x_sqn, "x_sqn", n, dev)), _ptr(_vec(self.y_sqn, "y_sqn", m, dev)))
+
+
+def problem(X, Y, eps, a=None, b=None, x_sqn=None, y_sqn=None) -> Problem:
+    return Problem(X, Y, eps, a, b, x_sqn, y_sqn)
+
+
+def _workspace(query, ws, device):
+    size = ctypes.c_size_t(0)
+    _check(query(None, ctypes.byref(size)), "workspace query")
+    need = size.value
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    elif ws.numel() < need:
+        raise ValueError(f"workspace holds {ws.numel()} bytes, {need} needed")
+    size.value = ws.numel()
+    return ws, size
+
+
+def ot_sqnorms(pts: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    rows, d, ld = _rows(pts, "pts")
+    if out is None:
+        out = torch.empty(rows, dtype=torch.float32, device=pts.device)
+    _check(lib().ot_sqnorms(_ptr(pts), _dtype_code(pts), rows, d, ld, _ptr(out), _stream(pts.device)),
+           "ot_sqnorms")
+    return out
+
+
+def _update(fn, name, prob, src, dst, err, ws):
+    L = lib()
+    c_fn = getattr(L, fn)
+    st = _stream(prob.device)
+    pp = ctypes.byref(prob.c)
+    ws, size = _workspace(lambda w, s: c_fn(pp, _ptr(src), _ptr(dst), _ptr(err), w, s, st), ws, prob.device)
+    _check(c_fn(pp, _ptr(src), _ptr(dst), _ptr(err), _ptr(ws), ctypes.byref(size), st), name)
+    return dst
+
+
+def ot_update_f(prob: Problem, g, f, err=None, ws=None):
+    """One f half-step from g, written into f (in place); optional device scalar err."""
+    return _update("ot_update_f", "ot_update_f", prob, g, f, err, ws)
+
+
+def ot_update_g(prob: Problem, f, g, err=None, ws=None):
+    """One g half-step from f, written into g (in place); optional device scalar err."""
+    return _update("ot_update_g", "ot_update_g", prob, f, g, err, ws)
+
+
+def ot_solve(prob: Problem, f, g, iters: int, tol: float = 0.0, check_every: int = 1,
+             init_given: bool = False, use_graph: bool = True, splits_f: int = 0,
+             splits_g: int = 0, timing: bool = False, want_info: bool = True, ws=None):
+    """Alternating Sinkhorn into f, g. Returns the info dict (None if want_info is False)."""
+    L = lib()
+    opts = OtSolveOpts(int(iters), float(tol), int(check_every),
+                       OT_INIT_GIVEN if init_given else OT_INIT_ZERO, int(bool(use_graph)),
+                       int(splits_f), int(splits_g), int(bool(timing)))
+    info = OtSolveInfo()
+    pinfo = ctypes.byref(info) if want_info else None
+    st = _stream(prob.device)
+    pp = ctypes.byref(prob.c)
+    ws, size = _workspace(lambda w, s: L.ot_solve(pp, _ptr(f), _ptr(g), ctypes.byref(opts), pinfo, w, s, st),
+                          ws, prob.device)
+    _check(L.ot_solve(pp, _ptr(f), _ptr(g), ctypes.byref(opts), pinfo, _ptr(ws), ctypes.byref(size), st),
+           "ot_solve")
+    return info.as_dict() if want_info else None
+
+
+def ot_apply_plan(prob: Problem, f, g, V=None, flags: int = 0, out=None, marg=None, ws=None):
+    """out = P V (P^T U with OT_TRANSPOSE; barycentric with OT_BARY; X-gradient with OT_GRAD)."""
+    L = lib()
+    tr = bool(flags & OT_TRANSPOSE)
+    rows = prob.m if tr else prob.n
+    if flags & OT_GRAD:
+        vptr, vdt, cols, ldv = None, 0, prob.d, 0
+    else:
+        if V is None:
+            raise ValueError("V is required unless OT_GRAD is set")
+        vrows, cols, ldv = _rows(V, "V")
+        if vrows != (prob.n if tr else prob.m):
+            raise ValueError("V has the wrong number of rows")
+        vptr, vdt = _ptr(V), _dtype_code(V)
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.float32, device=prob.device)
+    st = _stream(prob.device)
+    pp = ctypes.byref(prob.c)
+    args = lambda w, s: L.ot_apply_plan(pp, _ptr(f), _ptr(g), vptr, vdt, cols, ldv, int(flags),
+                                        _ptr(out), _ptr(marg), w, s, st)
+    ws, size = _workspace(args, ws, prob.device)
+    _check(args(_ptr(ws), ctypes.byref(size)), "ot_apply_plan")
+    return out
+
+
+def version() -> str:
+    return lib().ot_version().decode()

@@ -1,0 +1,672 @@
+// C ABI and host driver of the streamed Sinkhorn solver (declarations and
+// semantics in include/flashot.h).
+//
+// The driver validates arguments on the host, carves the caller's workspace,
+// packs both point clouds once per call into the MFMA operand layout, and
+// enqueues one f half-step (streamed LSE partials + merge) and one g
+// half-step per iteration on the caller's stream (alternating schedule of
+// "FlashSinkhorn: IO-Aware Entropic Optimal Transport on GPU", §3.1 eq. 2-3).
+// Blocks of iterations are captured once into a HIP graph and replayed.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "flashot.h"
+#include "kernels.h"
+
+using namespace flashot;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+#define OT_HIP(expr)                                                                     \
+  do {                                                                                   \
+    hipError_t e_ = (expr);                                                              \
+    if (e_ != hipSuccess) return fail(OT_ERR_HIP, std::string(#expr) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+int env_int(const char* name, int dflt) {
+  const char* v = std::getenv(name);
+  if (!v || !*v) return dflt;
+  return std::atoi(v);
+}
+
+// Kernel configuration for a point dimension / storage type.
+struct KConf {
+  int kbw;      // dimension values per k-block (8 fp32, 16 bf16)
+  int kblocks;  // k-blocks needed to cover d
+  int kb;       // k-blocks in registers at a time
+  int kbp;      // padded k-blocks per tile
+  bool xres;    // row operand resident in registers
+  int ri;       // row tiles per wave in the LSE pass
+};
+
+KConf kernel_conf(int64_t d, int bf16) {
+  KConf k{};
+  k.kbw = bf16 ? 16 : 8;
+  k.kblocks = ceil_div(d, k.kbw);
+  if (k.kblocks <= 16) {
+    k.kb = 1;
+    while (k.kb < k.kblocks) k.kb *= 2;
+    k.kbp = k.kb;
+    k.xres = true;
+    k.ri = (k.kb <= 8) ? 2 : 1;
+  } else {
+    k.kb = 8;
+    k.kbp = (k.kblocks + 7) / 8 * 8;
+    k.xres = false;
+    k.ri = 2;
+  }
+  const int ri_env = env_int("FLASHOT_RI", 0);
+  if (ri_env == 1 || ri_env == 2) k.ri = ri_env;
+  return k;
+}
+
+// Column splits: enough workgroups to fill 256 CUs several times over, at
+// least ~4 column tiles per split, a multiple of 8 when large (XCD locality).
+void choose_splits(PassShape& s, int forced, int max_splits) {
+  int S;
+  if (forced > 0) {
+    S = forced;
+  } else {
+    const int target = env_int("FLASHOT_TARGET_WG", 2048);
+    S = ceil_div(target, s.nrowgroups);
+    const int most = s.ctiles / 4 > 1 ? s.ctiles / 4 : 1;
+    if (S > most) S = most;
+    if (S >= 8) S = (S + 7) / 8 * 8;
+  }
+  if (S > max_splits) S = max_splits;
+  if (S > s.ctiles) S = s.ctiles;
+  if (S < 1) S = 1;
+  s.tps = ceil_div(s.ctiles, S);
+  s.splits = ceil_div(s.ctiles, s.tps);
+}
+
+PassShape make_pass(int rtiles, int ctiles, const KConf& k, int ri, int forced, int max_splits) {
+  PassShape s{};
+  s.rtiles = rtiles;
+  s.ctiles = ctiles;
+  s.kbp = k.kbp;
+  s.kb = k.kb;
+  s.xres = k.xres;
+  s.ri = ri;
+  s.nrowgroups = ceil_div(rtiles, (int64_t)kWaves * ri);
+  choose_splits(s, forced, max_splits);
+  return s;
+}
+
+int check_problem(const ot_problem* p) {
+  if (!p) return fail(OT_ERR_INVALID_ARG, "problem is NULL");
+  if (!p->x || !p->y) return fail(OT_ERR_INVALID_ARG, "x or y is NULL");
+  if (p->n < 1 || p->m < 1) return fail(OT_ERR_INVALID_ARG, "n and m must be >= 1");
+  if (p->d < 1) return fail(OT_ERR_INVALID_ARG, "d must be >= 1");
+  if (p->ldx < p->d || p->ldy < p->d) return fail(OT_ERR_INVALID_ARG, "ldx and ldy must be >= d");
+  if (p->dtype != OT_F32 && p->dtype != OT_BF16) return fail(OT_ERR_UNSUPPORTED, "dtype must be OT_F32 or OT_BF16");
+  if (p->d > OT_MAX_D) return fail(OT_ERR_UNSUPPORTED, "d exceeds OT_MAX_D");
+  if (p->n > (int64_t)1 << 30 || p->m > (int64_t)1 << 30) return fail(OT_ERR_UNSUPPORTED, "n or m exceeds 2^30");
+  if (!(p->eps > 0.f) || !std::isfinite(p->eps)) return fail(OT_ERR_INVALID_ARG, "eps must be finite and > 0");
+  const float c = 2.f * kLog2e / p->eps;
+  if (!std::isfinite(c)) return fail(OT_ERR_UNSUPPORTED, "eps too small: 2 log2(e)/eps overflows fp32");
+  const size_t es = p->dtype == OT_BF16 ? 2 : 4;
+  if (((uintptr_t)p->x % es) || ((uintptr_t)p->y % es)) return fail(OT_ERR_INVALID_ARG, "x or y misaligned for its dtype");
+  return OT_OK;
+}
+
+// Workspace of the half-step / solve entry points.
+struct SolveWs {
+  KConf k;
+  int ntiles, mtiles, npad, mpad;
+  PassShape F, G;
+  size_t o_xp, o_yp, o_nx, o_ny, o_wx, o_hx, o_bx, o_wy, o_hy, o_by, o_part, o_errp, o_errv;
+  int errblocks_f, errblocks_g;
+  size_t total;
+};
+
+SolveWs solve_layout(const ot_problem* p, int splits_f, int splits_g) {
+  SolveWs w{};
+  w.k = kernel_conf(p->d, p->dtype == OT_BF16);
+  w.ntiles = ceil_div(p->n, kTile);
+  w.mtiles = ceil_div(p->m, kTile);
+  w.npad = w.ntiles * kTile;
+  w.mpad = w.mtiles * kTile;
+  w.F = make_pass(w.ntiles, w.mtiles, w.k, w.k.ri, splits_f, 4096);
+  w.G = make_pass(w.mtiles, w.ntiles, w.k, w.k.ri, splits_g, 4096);
+  w.errblocks_f = lse_merge_blocks(w.npad);
+  w.errblocks_g = lse_merge_blocks(w.mpad);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes, 256);
+    return at;
+  };
+  w.o_xp = take((size_t)w.ntiles * w.k.kbp * 1024);
+  w.o_yp = take((size_t)w.mtiles * w.k.kbp * 1024);
+  w.o_nx = take((size_t)w.npad * 4);
+  w.o_ny = take((size_t)w.mpad * 4);
+  w.o_wx = take((size_t)w.npad * 4);
+  w.o_hx = take((size_t)w.npad * 4);
+  w.o_bx = take((size_t)w.npad * 4);
+  w.o_wy = take((size_t)w.mpad * 4);
+  w.o_hy = take((size_t)w.mpad * 4);
+  w.o_by = take((size_t)w.mpad * 4);
+  const size_t pf = (size_t)w.F.splits * w.npad, pg = (size_t)w.G.splits * w.mpad;
+  w.o_part = take((pf > pg ? pf : pg) * 8);
+  w.o_errp = take((size_t)(w.errblocks_f + w.errblocks_g) * 4);
+  w.o_errv = take(64);
+  w.total = o;
+  return w;
+}
+
+// Resolved device pointers of one solve / half-step call.
+struct Ctx {
+  const ot_problem* p;
+  SolveWs L;
+  char* ws;
+  float c, eps;
+  const float* nx;
+  const float* ny;
+  float *wx, *hx, *bx, *wy, *hy, *by, *errp, *errv;
+  float2* part;
+  void *xp, *yp;
+  float *f, *g;
+};
+
+Ctx make_ctx(const ot_problem* p, const SolveWs& L, void* ws, float* f, float* g) {
+  Ctx x{};
+  x.p = p;
+  x.L = L;
+  x.ws = (char*)ws;
+  x.eps = p->eps;
+  x.c = 2.f * kLog2e / p->eps;
+  x.xp = x.ws + L.o_xp;
+  x.yp = x.ws + L.o_yp;
+  x.nx = p->x_sqn ? p->x_sqn : (const float*)(x.ws + L.o_nx);
+  x.ny = p->y_sqn ? p->y_sqn : (const float*)(x.ws + L.o_ny);
+  x.wx = (float*)(x.ws + L.o_wx);
+  x.hx = (float*)(x.ws + L.o_hx);
+  x.bx = (float*)(x.ws + L.o_bx);
+  x.wy = (float*)(x.ws + L.o_wy);
+  x.hy = (float*)(x.ws + L.o_hy);
+  x.by = (float*)(x.ws + L.o_by);
+  x.part = (float2*)(x.ws + L.o_part);
+  x.errp = (float*)(x.ws + L.o_errp);
+  x.errv = (float*)(x.ws + L.o_errv);
+  x.f = f;
+  x.g = g;
+  return x;
+}
+
+// Norms, packed operands, weights: once per call.
+int prepare(const Ctx& x, hipStream_t st) {
+  const ot_problem* p = x.p;
+  const int bf = p->dtype == OT_BF16;
+  if (!p->x_sqn) OT_HIP(launch_sqnorms(p->x, bf, p->n, p->d, p->ldx, (float*)x.nx, st));
+  if (!p->y_sqn) OT_HIP(launch_sqnorms(p->y, bf, p->m, p->d, p->ldy, (float*)x.ny, st));
+  OT_HIP(launch_pack_points(p->x, bf, p->n, p->d, p->ldx, x.L.ntiles, x.L.k.kbp, x.xp, st));
+  OT_HIP(launch_pack_points(p->y, bf, p->m, p->d, p->ldy, x.L.mtiles, x.L.k.kbp, x.yp, st));
+  OT_HIP(launch_weights(p->a, (int)p->n, x.L.npad, x.eps, x.wx, x.hx, st));
+  OT_HIP(launch_weights(p->b, (int)p->m, x.L.mpad, x.eps, x.wy, x.hy, st));
+  return OT_OK;
+}
+
+// f half-step: LSE over columns y with bias by, merge into f (bias bx for the g side).
+int half_f(const Ctx& x, hipStream_t st, int with_err, int write) {
+  OT_HIP(launch_lse_partial(x.L.F, x.p->dtype == OT_BF16, x.xp, x.yp, x.by, x.c, x.part, st));
+  OT_HIP(launch_lse_merge(x.part, x.L.F.splits, x.L.npad, (int)x.p->n, x.c, x.eps, x.nx, x.hx, x.wx,
+                          x.f, x.bx, x.errp, with_err, write, st));
+  return OT_OK;
+}
+
+int half_g(const Ctx& x, hipStream_t st, int with_err, int write) {
+  OT_HIP(launch_lse_partial(x.L.G, x.p->dtype == OT_BF16, x.yp, x.xp, x.bx, x.c, x.part, st));
+  OT_HIP(launch_lse_merge(x.part, x.L.G.splits, x.L.mpad, (int)x.p->m, x.c, x.eps, x.ny, x.hy, x.wy,
+                          x.g, x.by, x.errp + x.L.errblocks_f, with_err, write, st));
+  return OT_OK;
+}
+
+int enqueue_iterations(const Ctx& x, hipStream_t st, int count, int with_err) {
+  for (int t = 0; t < count; ++t) {
+    int rc = half_f(x, st, with_err, 1);
+    if (rc) return rc;
+    rc = half_g(x, st, 0, 1);
+    if (rc) return rc;
+  }
+  return OT_OK;
+}
+
+// ---- HIP graph cache: one entry per distinct (device, problem, workspace, options) ----
+struct GraphKey {
+  int device;
+  uintptr_t ws, f, g, nx, ny;
+  int64_t n, m, d;
+  int dtype;
+  float eps;
+  int count, with_err;
+  PassShape F, G;
+  bool operator==(const GraphKey& o) const { return std::memcmp(this, &o, sizeof(*this)) == 0; }
+};
+
+struct GraphEntry {
+  GraphKey key;
+  hipGraphExec_t exec;
+};
+
+std::mutex g_graph_mu;
+std::vector<GraphEntry> g_graphs;  // most recent last
+hipStream_t g_capture_stream[64] = {};
+
+int get_graph(const Ctx& x, int count, int with_err, hipGraphExec_t* out) {
+  int dev = 0;
+  OT_HIP(hipGetDevice(&dev));
+  GraphKey key;
+  std::memset(&key, 0, sizeof(key));
+  key.device = dev;
+  key.ws = (uintptr_t)x.ws;
+  key.f = (uintptr_t)x.f;
+  key.g = (uintptr_t)x.g;
+  key.nx = (uintptr_t)x.nx;
+  key.ny = (uintptr_t)x.ny;
+  key.n = x.p->n;
+  key.m = x.p->m;
+  key.d = x.p->d;
+  key.dtype = x.p->dtype;
+  key.eps = x.p->eps;
+  key.count = count;
+  key.with_err = with_err;
+  key.F = x.L.F;
+  key.G = x.L.G;
+  std::lock_guard<std::mutex> lk(g_graph_mu);
+  for (size_t i = 0; i < g_graphs.size(); ++i) {
+    if (g_graphs[i].key == key) {
+      GraphEntry e = g_graphs[i];
+      g_graphs.erase(g_graphs.begin() + i);
+      g_graphs.push_back(e);
+      *out = e.exec;
+      return OT_OK;
+    }
+  }
+  if (dev < 0 || dev >= 64) return fail(OT_ERR_UNSUPPORTED, "device index >= 64");
+  if (!g_capture_stream[dev]) OT_HIP(hipStreamCreateWithFlags(&g_capture_stream[dev], hipStreamNonBlocking));
+  hipStream_t cs = g_capture_stream[dev];
+  OT_HIP(hipStreamBeginCapture(cs, hipStreamCaptureModeRelaxed));
+  const int rc = enqueue_iterations(x, cs, count, with_err);
+  hipGraph_t graph = nullptr;
+  const hipError_t ec = hipStreamEndCapture(cs, &graph);
+  if (rc) {
+    if (graph) (void)hipGraphDestroy(graph);
+    return rc;
+  }
+  if (ec != hipSuccess) return fail(OT_ERR_HIP, std::string("hipStreamEndCapture: ") + hipGetErrorString(ec));
+  hipGraphExec_t exec = nullptr;
+  const hipError_t ei = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  (void)hipGraphDestroy(graph);
+  if (ei != hipSuccess) return fail(OT_ERR_HIP, std::string("hipGraphInstantiate: ") + hipGetErrorString(ei));
+  if (g_graphs.size() >= 8) {
+    (void)hipGraphExecDestroy(g_graphs.front().exec);
+    g_graphs.erase(g_graphs.begin());
+  }
+  g_graphs.push_back(GraphEntry{key, exec});
+  *out = exec;
+  return OT_OK;
+}
+
+int run_iterations(const Ctx& x, hipStream_t st, int count, int with_err, bool use_graph) {
+  if (count <= 0) return OT_OK;
+  if (!use_graph) return enqueue_iterations(x, st, count, with_err);
+  const int block = count < 16 ? count : 16;
+  hipGraphExec_t gb = nullptr;
+  int rc = get_graph(x, block, with_err, &gb);
+  if (rc) return rc;
+  int done = 0;
+  for (; done + block <= count; done += block) OT_HIP(hipGraphLaunch(gb, st));
+  if (done < count) {
+    hipGraphExec_t g1 = nullptr;
+    rc = get_graph(x, 1, with_err, &g1);
+    if (rc) return rc;
+    for (; done < count; ++done) OT_HIP(hipGraphLaunch(g1, st));
+  }
+  return OT_OK;
+}
+
+// Timed variant: plain launches with a HIP event pair around every LSE kernel.
+struct EventPool {
+  std::vector<hipEvent_t> ev;
+  int ensure(size_t count) {
+    while (ev.size() < count) {
+      hipEvent_t e;
+      OT_HIP(hipEventCreate(&e));
+      ev.push_back(e);
+    }
+    return OT_OK;
+  }
+};
+thread_local EventPool g_events;
+
+int run_iterations_timed(const Ctx& x, hipStream_t st, int count, int with_err, float* ms,
+                         int* launches) {
+  const size_t need = (size_t)count * 4;
+  int rc = g_events.ensure(need);
+  if (rc) return rc;
+  const int bf = x.p->dtype == OT_BF16;
+  for (int t = 0; t < count; ++t) {
+    hipEvent_t* e = &g_events.ev[(size_t)t * 4];
+    OT_HIP(hipEventRecord(e[0], st));
+    OT_HIP(launch_lse_partial(x.L.F, bf, x.xp, x.yp, x.by, x.c, x.part, st));
+    OT_HIP(hipEventRecord(e[1], st));
+    OT_HIP(launch_lse_merge(x.part, x.L.F.splits, x.L.npad, (int)x.p->n, x.c, x.eps, x.nx, x.hx,
+                            x.wx, x.f, x.bx, x.errp, with_err, 1, st));
+    OT_HIP(hipEventRecord(e[2], st));
+    OT_HIP(launch_lse_partial(x.L.G, bf, x.yp, x.xp, x.bx, x.c, x.part, st));
+    OT_HIP(hipEventRecord(e[3], st));
+    OT_HIP(launch_lse_merge(x.part, x.L.G.splits, x.L.mpad, (int)x.p->m, x.c, x.eps, x.ny, x.hy,
+                            x.wy, x.g, x.by, x.errp + x.L.errblocks_f, 0, 1, st));
+  }
+  OT_HIP(hipStreamSynchronize(st));
+  float tot = 0.f;
+  for (int t = 0; t < count; ++t) {
+    hipEvent_t* e = &g_events.ev[(size_t)t * 4];
+    float a = 0.f, b = 0.f;
+    OT_HIP(hipEventElapsedTime(&a, e[0], e[1]));
+    OT_HIP(hipEventElapsedTime(&b, e[2], e[3]));
+    tot += a + b;
+  }
+  *ms += tot;
+  *launches += 2 * count;
+  return OT_OK;
+}
+
+int check_ws(void* ws, size_t* ws_bytes, size_t need, bool* query) {
+  if (!ws_bytes) return fail(OT_ERR_INVALID_ARG, "ws_bytes is NULL");
+  if (!ws) {
+    *ws_bytes = need;
+    *query = true;
+    return OT_OK;
+  }
+  *query = false;
+  if (*ws_bytes < need) return fail(OT_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need) + " bytes");
+  if ((uintptr_t)ws % 256) return fail(OT_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  return OT_OK;
+}
+
+int update_impl(const ot_problem* p, const float* other, float* pot, float* err, void* ws,
+                size_t* ws_bytes, void* stream, bool is_f) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  const SolveWs L = solve_layout(p, 0, 0);
+  bool query = false;
+  rc = check_ws(ws, ws_bytes, L.total, &query);
+  if (rc || query) return rc;
+  if (!other || !pot) return fail(OT_ERR_INVALID_ARG, "potential pointer is NULL");
+  hipStream_t st = (hipStream_t)stream;
+  Ctx x = make_ctx(p, L, ws, is_f ? pot : const_cast<float*>(other), is_f ? const_cast<float*>(other) : pot);
+  rc = prepare(x, st);
+  if (rc) return rc;
+  const int with_err = err != nullptr;
+  if (is_f) {
+    OT_HIP(launch_bias_from_pot(x.g, x.ny, x.hy, (int)p->m, L.mpad, x.by, st));
+    rc = half_f(x, st, with_err, 1);
+    if (rc) return rc;
+    if (with_err) OT_HIP(launch_err_reduce(x.errp, L.errblocks_f, err, st));
+  } else {
+    OT_HIP(launch_bias_from_pot(x.f, x.nx, x.hx, (int)p->n, L.npad, x.bx, st));
+    rc = half_g(x, st, with_err, 1);
+    if (rc) return rc;
+    if (with_err) OT_HIP(launch_err_reduce(x.errp + L.errblocks_f, L.errblocks_g, err, st));
+  }
+  return OT_OK;
+}
+
+// ---- transport application ------------------------------------------------
+struct ApplyWs {
+  KConf k;
+  int rtiles, ctiles, rpad, cpad, pblocks, pb_per_pass, ppad;
+  PassShape S;
+  size_t o_xp, o_yp, o_nx, o_ny, o_wr, o_hr, o_wc, o_hc, o_bc, o_vp, o_ms, o_o;
+  size_t total;
+};
+
+ApplyWs apply_layout(const ot_problem* p, int64_t cols, bool transpose) {
+  ApplyWs w{};
+  w.k = kernel_conf(p->d, p->dtype == OT_BF16);
+  const int64_t rows = transpose ? p->m : p->n;
+  const int64_t strm = transpose ? p->n : p->m;
+  w.rtiles = ceil_div(rows, kTile);
+  w.ctiles = ceil_div(strm, kTile);
+  w.rpad = w.rtiles * kTile;
+  w.cpad = w.ctiles * kTile;
+  w.pblocks = ceil_div(cols, 32);
+  w.pb_per_pass = w.pblocks >= 4 ? 4 : (w.pblocks >= 2 ? 2 : 1);
+  w.ppad = w.pblocks * 32;
+  w.S = make_pass(w.rtiles, w.ctiles, w.k, 1, 0, 64);
+  const int ntiles = ceil_div(p->n, kTile), mtiles = ceil_div(p->m, kTile);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes, 256);
+    return at;
+  };
+  w.o_xp = take((size_t)ntiles * w.k.kbp * 1024);
+  w.o_yp = take((size_t)mtiles * w.k.kbp * 1024);
+  w.o_nx = take((size_t)ntiles * kTile * 4);
+  w.o_ny = take((size_t)mtiles * kTile * 4);
+  w.o_wr = take((size_t)w.rpad * 4);
+  w.o_hr = take((size_t)w.rpad * 4);
+  w.o_wc = take((size_t)w.cpad * 4);
+  w.o_hc = take((size_t)w.cpad * 4);
+  w.o_bc = take((size_t)w.cpad * 4);
+  w.o_vp = take((size_t)w.ctiles * w.pblocks * 4096);
+  w.o_ms = take((size_t)w.S.splits * w.rpad * 8);
+  w.o_o = take((size_t)w.S.splits * w.ppad * w.rpad * 4);
+  w.total = o;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ot_last_error(void) { return g_err.c_str(); }
+
+const char* ot_version(void) { return "flashot 0.1 gfx950"; }
+
+int ot_sqnorms(const void* pts, int dtype, int64_t rows, int64_t d, int64_t ld, float* out,
+               void* stream) {
+  try {
+    if (!pts || !out) return fail(OT_ERR_INVALID_ARG, "pts or out is NULL");
+    if (rows < 1 || d < 1 || ld < d) return fail(OT_ERR_INVALID_ARG, "need rows >= 1, d >= 1, ld >= d");
+    if (dtype != OT_F32 && dtype != OT_BF16) return fail(OT_ERR_UNSUPPORTED, "dtype must be OT_F32 or OT_BF16");
+    if (d > OT_MAX_D) return fail(OT_ERR_UNSUPPORTED, "d exceeds OT_MAX_D");
+    OT_HIP(launch_sqnorms(pts, dtype == OT_BF16, rows, d, ld, out, (hipStream_t)stream));
+    return OT_OK;
+  } catch (...) {
+    return fail(OT_ERR_HIP, "unexpected host exception");
+  }
+}
+
+int ot_update_f(const ot_problem* p, const float* g, float* f, float* err, void* ws,
+                size_t* ws_bytes, void* stream) {
+  try {
+    return update_impl(p, g, f, err, ws, ws_bytes, stream, true);
+  } catch (...) {
+    return fail(OT_ERR_HIP, "unexpected host exception");
+  }
+}
+
+int ot_update_g(const ot_problem* p, const float* f, float* g, float* err, void* ws,
+                size_t* ws_bytes, void* stream) {
+  try {
+    return update_impl(p, f, g, err, ws, ws_bytes, stream, false);
+  } catch (...) {
+    return fail(OT_ERR_HIP, "unexpected host exception");
+  }
+}
+
+int ot_solve(const ot_problem* p, float* f, float* g, const ot_solve_opts* o,
+             ot_solve_info* info, void* ws, size_t* ws_bytes, void* stream) {
+  try {
+    int rc = check_problem(p);
+    if (rc) return rc;
+    if (!o) return fail(OT_ERR_INVALID_ARG, "opts is NULL");
+    if (o->iters < 0) return fail(OT_ERR_INVALID_ARG, "iters must be >= 0");
+    if (!(o->tol >= 0.f) || !std::isfinite(o->tol)) return fail(OT_ERR_INVALID_ARG, "tol must be finite and >= 0");
+    if (o->tol > 0.f && o->check_every < 1) return fail(OT_ERR_INVALID_ARG, "check_every must be >= 1 when tol > 0");
+    if (o->init != OT_INIT_ZERO && o->init != OT_INIT_GIVEN) return fail(OT_ERR_INVALID_ARG, "init must be OT_INIT_ZERO or OT_INIT_GIVEN");
+    if (o->splits_f < 0 || o->splits_g < 0) return fail(OT_ERR_INVALID_ARG, "splits must be >= 0");
+    if (o->timing && !info) return fail(OT_ERR_INVALID_ARG, "timing needs info");
+    const SolveWs L = solve_layout(p, o->splits_f, o->splits_g);
+    bool query = false;
+    rc = check_ws(ws, ws_bytes, L.total, &query);
+    if (rc || query) return rc;
+    if (!f || !g) return fail(OT_ERR_INVALID_ARG, "f or g is NULL");
+    hipStream_t st = (hipStream_t)stream;
+    Ctx x = make_ctx(p, L, ws, f, g);
+    rc = prepare(x, st);
+    if (rc) return rc;
+    if (o->init == OT_INIT_ZERO) {
+      OT_HIP(launch_fill(f, 0.f, p->n, st));
+      OT_HIP(launch_fill(g, 0.f, p->m, st));
+    }
+    OT_HIP(launch_bias_from_pot(g, x.ny, x.hy, (int)p->m, L.mpad, x.by, st));
+    const bool use_graph = o->use_graph != 0 && st != nullptr;
+    float lse_ms = 0.f;
+    int lse_launches = 0;
+    int done = 0;
+    if (o->tol > 0.f) {
+      while (done < o->iters) {
+        const int chunk = (o->iters - done) < o->check_every ? (o->iters - done) : o->check_every;
+        rc = o->timing ? run_iterations_timed(x, st, chunk, 1, &lse_ms, &lse_launches)
+                       : run_iterations(x, st, chunk, 1, use_graph);
+        if (rc) return rc;
+        done += chunk;
+        OT_HIP(launch_err_reduce(x.errp, L.errblocks_f, x.errv, st));
+        float herr = 0.f;
+        OT_HIP(hipMemcpyAsync(&herr, x.errv, sizeof(float), hipMemcpyDeviceToHost, st));
+        OT_HIP(hipStreamSynchronize(st));
+        if (!(herr >= o->tol)) break;  // also stops on NaN
+      }
+    } else {
+      rc = o->timing ? run_iterations_timed(x, st, o->iters, 0, &lse_ms, &lse_launches)
+                     : run_iterations(x, st, o->iters, 0, use_graph);
+      if (rc) return rc;
+      done = o->iters;
+    }
+    if (info) {
+      // Exact marginal errors of the returned (f, g): one dry pass per side.
+      if (done == 0) OT_HIP(launch_bias_from_pot(f, x.nx, x.hx, (int)p->n, L.npad, x.bx, st));
+      rc = half_f(x, st, 1, 0);
+      if (rc) return rc;
+      OT_HIP(launch_err_reduce(x.errp, L.errblocks_f, x.errv, st));
+      rc = half_g(x, st, 1, 0);
+      if (rc) return rc;
+      OT_HIP(launch_err_reduce(x.errp + L.errblocks_f, L.errblocks_g, x.errv + 1, st));
+      OT_HIP(launch_nonfinite(f, (int)p->n, g, (int)p->m, x.errv + 2, st));
+      float h[3] = {0.f, 0.f, 0.f};
+      OT_HIP(hipMemcpyAsync(h, x.errv, sizeof(h), hipMemcpyDeviceToHost, st));
+      OT_HIP(hipStreamSynchronize(st));
+      info->iters_done = done;
+      info->marg_err_row = h[0];
+      info->marg_err_col = h[1];
+      info->nonfinite = h[2] != 0.f;
+      info->lse_ms = lse_ms;
+      info->lse_launches = lse_launches;
+      info->splits_f = L.F.splits;
+      info->splits_g = L.G.splits;
+      if (info->nonfinite) return fail(OT_ERR_NONFINITE, "potentials are not finite");
+    }
+    return OT_OK;
+  } catch (...) {
+    return fail(OT_ERR_HIP, "unexpected host exception");
+  }
+}
+
+int ot_apply_plan(const ot_problem* p, const float* f, const float* g, const void* V, int v_dtype,
+                  int64_t cols, int64_t ldv, int flags, float* out, float* marg, void* ws,
+                  size_t* ws_bytes, void* stream) {
+  try {
+    int rc = check_problem(p);
+    if (rc) return rc;
+    if (flags & ~(OT_TRANSPOSE | OT_GRAD | OT_BARY)) return fail(OT_ERR_INVALID_ARG, "unknown flag");
+    if ((flags & OT_GRAD) && (flags & OT_BARY)) return fail(OT_ERR_INVALID_ARG, "OT_GRAD and OT_BARY are exclusive");
+    const bool tr = (flags & OT_TRANSPOSE) != 0;
+    const bool grad = (flags & OT_GRAD) != 0;
+    if (grad) {  // V is the other cloud itself
+      V = tr ? p->x : p->y;
+      v_dtype = p->dtype;
+      cols = p->d;
+      ldv = tr ? p->ldx : p->ldy;
+    }
+    if (cols < 1) return fail(OT_ERR_INVALID_ARG, "cols must be >= 1");
+    if (cols > OT_MAX_COLS) return fail(OT_ERR_UNSUPPORTED, "cols exceeds OT_MAX_COLS");
+    if (v_dtype != OT_F32 && v_dtype != OT_BF16) return fail(OT_ERR_UNSUPPORTED, "v_dtype must be OT_F32 or OT_BF16");
+    const ApplyWs L = apply_layout(p, cols, tr);
+    bool query = false;
+    rc = check_ws(ws, ws_bytes, L.total, &query);
+    if (rc || query) return rc;
+    if (!f || !g || !V || !out) return fail(OT_ERR_INVALID_ARG, "f, g, V or out is NULL");
+    if (ldv < cols) return fail(OT_ERR_INVALID_ARG, "ldv must be >= cols");
+    if ((uintptr_t)V % (v_dtype == OT_BF16 ? 2 : 4)) return fail(OT_ERR_INVALID_ARG, "V misaligned");
+    hipStream_t st = (hipStream_t)stream;
+    char* w = (char*)ws;
+    const int bf = p->dtype == OT_BF16;
+    const float eps = p->eps, c = 2.f * kLog2e / p->eps;
+    const int ntiles = ceil_div(p->n, kTile), mtiles = ceil_div(p->m, kTile);
+    void* xp = w + L.o_xp;
+    void* yp = w + L.o_yp;
+    const float* nx = p->x_sqn ? p->x_sqn : (const float*)(w + L.o_nx);
+    const float* ny = p->y_sqn ? p->y_sqn : (const float*)(w + L.o_ny);
+    if (!p->x_sqn) OT_HIP(launch_sqnorms(p->x, bf, p->n, p->d, p->ldx, (float*)nx, st));
+    if (!p->y_sqn) OT_HIP(launch_sqnorms(p->y, bf, p->m, p->d, p->ldy, (float*)ny, st));
+    OT_HIP(launch_pack_points(p->x, bf, p->n, p->d, p->ldx, ntiles, L.k.kbp, xp, st));
+    OT_HIP(launch_pack_points(p->y, bf, p->m, p->d, p->ldy, mtiles, L.k.kbp, yp, st));
+    // Row side r (outputs) and column side s (streamed).
+    const int64_t rows = tr ? p->m : p->n, srows = tr ? p->n : p->m;
+    const float* wr_user = tr ? p->b : p->a;
+    const float* ws_user = tr ? p->a : p->b;
+    const float* pot_r = tr ? g : f;
+    const float* pot_s = tr ? f : g;
+    const float* norm_r = tr ? ny : nx;
+    const float* norm_s = tr ? nx : ny;
+    const void* Rp = tr ? yp : xp;
+    const void* Cp = tr ? xp : yp;
+    float* wr = (float*)(w + L.o_wr);
+    float* hr = (float*)(w + L.o_hr);
+    float* wc = (float*)(w + L.o_wc);
+    float* hc = (float*)(w + L.o_hc);
+    float* bc = (float*)(w + L.o_bc);
+    float* vp = (float*)(w + L.o_vp);
+    float2* pms = (float2*)(w + L.o_ms);
+    float* po = (float*)(w + L.o_o);
+    OT_HIP(launch_weights(wr_user, (int)rows, L.rpad, eps, wr, hr, st));
+    OT_HIP(launch_weights(ws_user, (int)srows, L.cpad, eps, wc, hc, st));
+    OT_HIP(launch_bias_from_pot(pot_s, norm_s, hc, (int)srows, L.cpad, bc, st));
+    OT_HIP(launch_pack_values(V, v_dtype == OT_BF16, srows, cols, ldv, L.ctiles, L.pblocks, vp, st));
+    OT_HIP(launch_apply_partial(L.S, bf, L.pblocks, L.pb_per_pass, Rp, Cp, bc, vp, c, pms, po,
+                                L.ppad, st));
+    const int mode = grad ? kApplyGrad : ((flags & OT_BARY) ? kApplyBary : kApplyPlain);
+    const void* Xsrc = tr ? p->y : p->x;
+    const int64_t ldx = tr ? p->ldy : p->ldx;
+    OT_HIP(launch_apply_merge(pms, po, L.S.splits, L.rpad, L.ppad, (int)rows, (int)cols, c, eps,
+                              pot_r, norm_r, wr, mode, Xsrc, bf, ldx, out, marg, st));
+    return OT_OK;
+  } catch (...) {
+    return fail(OT_ERR_HIP, "unexpected host exception");
+  }
+}
+
+}  // extern "C"

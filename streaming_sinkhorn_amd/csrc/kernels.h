@@ -1,0 +1,67 @@
+// Internal interface between the host driver (api.hip) and the gfx950 kernels
+// (kernels.hip). Not part of the public C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace flashot {
+
+// Every packed operand is a sequence of 32-row tiles. A tile holds `kbp`
+// k-blocks of 1 KiB: 64 lanes x 16 bytes. Lane l of k-block kb carries row
+// (l % 32) and the (l / 32)-th half of the block's k range, i.e. 4 fp32
+// (k-block = 8 values of the dimension) or 8 bf16 (k-block = 16 values).
+// Rows past the end and dimensions past d are zero.
+constexpr int kTile = 32;
+constexpr int kWaves = 4;  // waves per workgroup of the streamed kernels
+constexpr float kSentinel = -1.0e20f;  // bias of padded columns: exp underflows to 0
+
+// Shape of one streamed pass: "rows" are the outputs (one LSE per row) and
+// "cols" are streamed. For the f half-step rows = x, cols = y.
+struct PassShape {
+  int rtiles, ctiles;   // 32-row tiles of the row and column operands
+  int kbp;              // k-blocks per tile (padded)
+  int kb;               // k-blocks held in registers at a time (1,2,4,8,16)
+  bool xres;            // row operand resident in registers (kbp == kb)
+  int ri;               // 32-row tiles per wave
+  int splits, tps;      // column splits and column tiles per split
+  int nrowgroups;       // workgroups along the rows
+};
+
+hipError_t launch_sqnorms(const void* pts, int bf16, int64_t rows, int64_t d, int64_t ld,
+                          float* out, hipStream_t st);
+hipError_t launch_pack_points(const void* src, int bf16, int64_t rows, int64_t d, int64_t ld,
+                              int rtiles, int kbp, void* dst, hipStream_t st);
+hipError_t launch_pack_values(const void* V, int bf16, int64_t rows, int64_t cols, int64_t ldv,
+                              int ctiles, int pblocks, float* dst, hipStream_t st);
+hipError_t launch_weights(const float* w, int rows, int rpad, float eps, float* wgt, float* hlw,
+                          hipStream_t st);
+hipError_t launch_fill(float* p, float v, int64_t count, hipStream_t st);
+hipError_t launch_bias_from_pot(const float* pot, const float* norm, const float* hlw, int rows,
+                                int rpad, float* bias, hipStream_t st);
+hipError_t launch_lse_partial(const PassShape& s, int bf16, const void* Rp, const void* Cp,
+                              const float* cbias, float c, float2* part, hipStream_t st);
+hipError_t launch_lse_merge(const float2* part, int splits, int rpad, int rows, float c, float eps,
+                            const float* norm, const float* hlw, const float* wgt, float* pot,
+                            float* bias_out, float* err_part, int with_err, int write_pot,
+                            hipStream_t st);
+int lse_merge_blocks(int rows);
+hipError_t launch_err_reduce(const float* part, int count, float* out, hipStream_t st);
+hipError_t launch_nonfinite(const float* f, int n, const float* g, int m, float* out,
+                            hipStream_t st);
+hipError_t launch_apply_partial(const PassShape& s, int bf16, int pblocks, int pb_per_pass,
+                                const void* Rp, const void* Cp, const float* cbias,
+                                const float* Vp, float c, float2* partMS, float* partO, int ppad,
+                                hipStream_t st);
+hipError_t launch_apply_merge(const float2* partMS, const float* partO, int splits, int rpad,
+                              int ppad, int rows, int cols, float c, float eps, const float* pot,
+                              const float* norm, const float* wgt, int mode, const void* Xsrc,
+                              int xbf16, int64_t ldx, float* out, float* marg, hipStream_t st);
+
+// apply_merge modes
+constexpr int kApplyPlain = 0;
+constexpr int kApplyBary = 1;
+constexpr int kApplyGrad = 2;
+
+}  // namespace flashot

@@ -1,0 +1,782 @@
+// gfx950 kernels of the streamed log-domain Sinkhorn solver.
+//
+// Method: "FlashSinkhorn: IO-Aware Entropic Optimal Transport on GPU"
+// (arXiv 2602.03067). A Sinkhorn half-step is a row-wise log-sum-exp of the
+// biased dot-product score 2 x_i.y_j/eps + bias_j (Prop. 1, App. D.1); it is
+// streamed over column tiles with a running max and rescaled sum (App. D.3)
+// and only the potentials are written back (App. D.2, G.1). Transport
+// application P V reuses the same row softmax and accumulates V tiles
+// (Prop. 3, App. E.1, Algorithm 2; G.2 row-stationary loop order).
+//
+// MI355X design (not the page's Triton/A100 one):
+//  * the score tile is formed on the matrix cores with a 32x32 output per
+//    wave, computed TRANSPOSED (columns j on the M axis, rows i on the N
+//    axis). In the 32x32 accumulator layout lane l then holds 16 values of
+//    ONE output row (i = l % 32), so the online LSE is lane-local: no
+//    cross-lane traffic inside the column loop, one exchange with lane
+//    l ^ 32 at the very end;
+//  * the per-column bias enters the accumulator through one extra fp32 MFMA
+//    (A = bias column, B = ones), so a score needs one FMA (scale and
+//    subtract the running max) plus one exp2 and one add on the VALU;
+//  * operands are pre-packed once per call into the exact register layout of
+//    the MFMA (16 contiguous bytes per lane, zero-padded tiles), so every
+//    load in the hot loop is a full 1 KiB coalesced wave load with no masks;
+//  * the streamed axis is split over workgroups when the output axis alone
+//    cannot fill 256 CUs; partial (max, sum) pairs are merged afterwards in a
+//    fixed order with the exact merge of App. D.3, so results are
+//    deterministic. Split indices are the fastest-varying part of the
+//    workgroup index, which keeps one split's column tiles on one XCD (its
+//    own L2) when the split count is a multiple of 8.
+//  * P V reuses the exponentiated score registers directly as the B operand
+//    of a second MFMA: O^T (p x i) += V^T (p x j) P^T (j x i). The rows of V
+//    are pre-permuted into the accumulator's row order, so P never leaves
+//    registers and the running rescale of O is lane-local.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace flashot {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kMaxApplySplits = 64;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t u) {
+  return __uint_as_float(static_cast<uint32_t>(u) << 16);
+}
+
+template <typename T>
+__device__ __forceinline__ float load_as_f32(const T* p, int64_t idx);
+template <>
+__device__ __forceinline__ float load_as_f32<float>(const float* p, int64_t idx) {
+  return p[idx];
+}
+template <>
+__device__ __forceinline__ float load_as_f32<uint16_t>(const uint16_t* p, int64_t idx) {
+  return bf16_to_f32(p[idx]);
+}
+
+// One packed k-block of the score tile: acc[j][i] += sum_k A[j][k] B[k][i].
+template <bool BF16>
+__device__ __forceinline__ f32x16 mfma_kblock(u32x4 a, u32x4 b, f32x16 acc) {
+  if constexpr (BF16) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+  } else {
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0,
+                                               0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0,
+                                               0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0,
+                                               0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0,
+                                               0, 0);
+    return acc;
+  }
+}
+
+// Adds bias_j to every accumulator entry of column j: k-slot 0 carries
+// (bias_j, 1), k-slot 1 carries (0, 1).
+__device__ __forceinline__ f32x16 mfma_bias(float wv, int h, f32x16 acc) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(h ? 0.0f : wv, 1.0f, acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ float max16(const f32x16& v) {
+  float a = fmaxf(fmaxf(v[0], v[1]), v[2]);
+  float b = fmaxf(fmaxf(v[3], v[4]), v[5]);
+  float d = fmaxf(fmaxf(v[6], v[7]), v[8]);
+  float e = fmaxf(fmaxf(v[9], v[10]), v[11]);
+  float f = fmaxf(fmaxf(v[12], v[13]), v[14]);
+  return fmaxf(fmaxf(a, b), fmaxf(fmaxf(d, e), fmaxf(f, v[15])));
+}
+
+// Online LSE step of App. D.3 on 16 scores of one row, in "dot-product units":
+// the natural-log score is (2/eps) * v, and c = 2 log2(e) / eps, so
+// exp(score - max) = exp2(c * (v - M)).
+__device__ __forceinline__ void lse_tile(const f32x16& v, float& M, float& S, float c) {
+  const float Mn = fmaxf(M, max16(v));
+  const float cm = c * Mn;
+  const float sc = __builtin_amdgcn_exp2f(fmaf(c, M, -cm));
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; r += 4) {
+    s0 += __builtin_amdgcn_exp2f(fmaf(c, v[r + 0], -cm));
+    s1 += __builtin_amdgcn_exp2f(fmaf(c, v[r + 1], -cm));
+    s2 += __builtin_amdgcn_exp2f(fmaf(c, v[r + 2], -cm));
+    s3 += __builtin_amdgcn_exp2f(fmaf(c, v[r + 3], -cm));
+  }
+  S = fmaf(S, sc, (s0 + s1) + (s2 + s3));
+  M = Mn;
+}
+
+// ---------------------------------------------------------------------------
+// Streamed log-sum-exp partials (Algorithm 1 / 3 of the page).
+//   part[s][row] = (M, S) with LSE_row over split s = (2/eps) M + ln S.
+// Grid: nrowgroups * splits workgroups of 4 waves; wave w of row group g owns
+// row tiles (4 g + w) * RI ... + RI - 1 and streams the column tiles of its split.
+// ---------------------------------------------------------------------------
+template <bool BF16, int KB, int RI, bool XRES>
+__global__ __launch_bounds__(256) void lse_partial_kernel(
+    const u32x4* __restrict__ Rp, const u32x4* __restrict__ Cp, const float* __restrict__ cbias,
+    int rtiles, int ctiles, int kbp, int splits, int tps, float c, float2* __restrict__ part,
+    int rpad) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int h = lane >> 5;
+  const int s = blockIdx.x % splits;
+  const int rg = blockIdx.x / splits;
+  const int rt0 = (rg * kWaves + wave) * RI;
+  if (rt0 >= rtiles) return;
+  const int jt0 = s * tps;
+  const int jt1 = min(jt0 + tps, ctiles);
+
+  int rt[RI];
+#pragma unroll
+  for (int ri = 0; ri < RI; ++ri) rt[ri] = min(rt0 + ri, rtiles - 1);
+
+  u32x4 xr[RI][KB];
+  if constexpr (XRES) {
+#pragma unroll
+    for (int ri = 0; ri < RI; ++ri)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) xr[ri][kb] = Rp[((size_t)rt[ri] * KB + kb) * 64 + lane];
+  }
+
+  float M[RI], S[RI];
+#pragma unroll
+  for (int ri = 0; ri < RI; ++ri) {
+    M[ri] = -1.0e30f;
+    S[ri] = 0.f;
+  }
+
+  if constexpr (XRES) {
+    // Double-buffered column operand: tile jt+1 is in flight while jt is used.
+    u32x4 yn[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) yn[kb] = Cp[((size_t)jt0 * KB + kb) * 64 + lane];
+    float wn = cbias[jt0 * kTile + (lane & 31)];
+    for (int jt = jt0; jt < jt1; ++jt) {
+      u32x4 yc[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) yc[kb] = yn[kb];
+      const float wv = wn;
+      const int jn = min(jt + 1, jt1 - 1);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) yn[kb] = Cp[((size_t)jn * KB + kb) * 64 + lane];
+      wn = cbias[jn * kTile + (lane & 31)];
+
+      f32x16 acc[RI];
+#pragma unroll
+      for (int ri = 0; ri < RI; ++ri) acc[ri] = f32x16{};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int ri = 0; ri < RI; ++ri) acc[ri] = mfma_kblock<BF16>(yc[kb], xr[ri][kb], acc[ri]);
+#pragma unroll
+      for (int ri = 0; ri < RI; ++ri) acc[ri] = mfma_bias(wv, h, acc[ri]);
+#pragma unroll
+      for (int ri = 0; ri < RI; ++ri) lse_tile(acc[ri], M[ri], S[ri], c);
+    }
+  } else {
+    for (int jt = jt0; jt < jt1; ++jt) {
+      f32x16 acc[RI];
+#pragma unroll
+      for (int ri = 0; ri < RI; ++ri) acc[ri] = f32x16{};
+      for (int kc = 0; kc < kbp; kc += KB) {
+        u32x4 yc[KB];
+        u32x4 xc[RI][KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) yc[kb] = Cp[((size_t)jt * kbp + kc + kb) * 64 + lane];
+#pragma unroll
+        for (int ri = 0; ri < RI; ++ri)
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb)
+            xc[ri][kb] = Rp[((size_t)rt[ri] * kbp + kc + kb) * 64 + lane];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int ri = 0; ri < RI; ++ri) acc[ri] = mfma_kblock<BF16>(yc[kb], xc[ri][kb], acc[ri]);
+      }
+      const float wv = cbias[jt * kTile + (lane & 31)];
+#pragma unroll
+      for (int ri = 0; ri < RI; ++ri) acc[ri] = mfma_bias(wv, h, acc[ri]);
+#pragma unroll
+      for (int ri = 0; ri < RI; ++ri) lse_tile(acc[ri], M[ri], S[ri], c);
+    }
+  }
+
+  // Merge the two half-waves that share a row (App. D.3 merge of partial statistics).
+#pragma unroll
+  for (int ri = 0; ri < RI; ++ri) {
+    const float Mp = __shfl_xor(M[ri], 32);
+    const float Sp = __shfl_xor(S[ri], 32);
+    const float Mt = fmaxf(M[ri], Mp);
+    const float cm = c * Mt;
+    const float St = S[ri] * __builtin_amdgcn_exp2f(fmaf(c, M[ri], -cm)) +
+                     Sp * __builtin_amdgcn_exp2f(fmaf(c, Mp, -cm));
+    if (h == 0 && rt0 + ri < rtiles)
+      part[(size_t)s * rpad + (size_t)(rt0 + ri) * kTile + (lane & 31)] = make_float2(Mt, St);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Merge of split partials + half-step epilogue (App. D.1 / D.2: write the
+// potential once). For row i:
+//   L = (2/eps) M + ln S over all splits,  shifted potential = -eps L = -2M - eps ln S,
+//   pot_i = norm_i + shifted, next bias_i = (pot_i - norm_i)/2 + (eps/2) log w_i,
+//   err_i = w_i |exp((pot_old_i - pot_i)/eps) - 1|   (App. E.1 induced marginal).
+// The bias is rebuilt from the stored fp32 potential, so resuming from
+// returned potentials reproduces an uninterrupted run bit for bit.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float block_sum_256(float v, float* sh) {
+  const int t = threadIdx.x;
+  sh[t] = v;
+  __syncthreads();
+#pragma unroll
+  for (int w = 128; w > 0; w >>= 1) {
+    if (t < w) sh[t] += sh[t + w];
+    __syncthreads();
+  }
+  return sh[0];
+}
+
+__global__ __launch_bounds__(256) void lse_merge_kernel(
+    const float2* __restrict__ part, int splits, int rpad, int rows, float c, float eps,
+    const float* __restrict__ norm, const float* __restrict__ hlw, const float* __restrict__ wgt,
+    float* __restrict__ pot, float* __restrict__ bias_out, float* __restrict__ err_part,
+    int with_err, int write_pot) {
+  __shared__ float sh[256];
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  float e = 0.f;
+  if (i < rows) {
+    float M = part[i].x;
+    for (int s = 1; s < splits; ++s) M = fmaxf(M, part[(size_t)s * rpad + i].x);
+    const float cm = c * M;
+    float S = 0.f;
+    for (int s = 0; s < splits; ++s) {
+      const float2 ps = part[(size_t)s * rpad + i];
+      S += ps.y * exp2f(fmaf(c, ps.x, -cm));
+    }
+    const float shifted = -2.f * M - eps * kLn2 * log2f(S);
+    const float nrm = norm[i];
+    const float pnew = nrm + shifted;
+    if (with_err) {
+      const float pold = pot[i];
+      e = wgt[i] * fabsf(exp2f((pold - pnew) * (kLog2e / eps)) - 1.f);
+    }
+    if (write_pot) {
+      pot[i] = pnew;
+      bias_out[i] = 0.5f * (pnew - nrm) + hlw[i];
+    }
+  } else if (i < rpad && write_pot) {
+    bias_out[i] = kSentinel;
+  }
+  if (with_err) {
+    const float tot = block_sum_256(e, sh);
+    if (threadIdx.x == 0) err_part[blockIdx.x] = tot;
+  }
+}
+
+int lse_merge_blocks(int rows) { return (rows + 255) / 256; }
+
+// Deterministic single-workgroup sum of `count` partials (fixed order).
+__global__ __launch_bounds__(256) void err_reduce_kernel(const float* __restrict__ part, int count,
+                                                          float* __restrict__ out) {
+  __shared__ float sh[256];
+  float v = 0.f;
+  for (int k = threadIdx.x; k < count; k += 256) v += part[k];
+  const float tot = block_sum_256(v, sh);
+  if (threadIdx.x == 0) out[0] = tot;
+}
+
+__global__ __launch_bounds__(256) void nonfinite_kernel(const float* __restrict__ f, int n,
+                                                         const float* __restrict__ g, int m,
+                                                         float* __restrict__ out) {
+  __shared__ float sh[256];
+  // Exponent-bit test: independent of the no-NaN compile flags of this file.
+  auto bad = [](float x) { return ((__float_as_uint(x) >> 23) & 0xffu) == 0xffu ? 1.f : 0.f; };
+  float v = 0.f;
+  for (int k = threadIdx.x; k < n; k += 256) v += bad(f[k]);
+  for (int k = threadIdx.x; k < m; k += 256) v += bad(g[k]);
+  const float tot = block_sum_256(v, sh);
+  if (threadIdx.x == 0) out[0] = tot;
+}
+
+// ---------------------------------------------------------------------------
+// Small per-problem kernels.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void sqnorms_kernel(const T* __restrict__ pts, int64_t rows,
+                                                       int64_t d, int64_t ld,
+                                                       float* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  float s = 0.f;
+  for (int64_t k = lane; k < d; k += 64) {
+    const float v = load_as_f32<T>(pts, row * ld + k);
+    s = fmaf(v, v, s);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+  if (lane == 0) out[row] = s;
+}
+
+// Packs a row-major point cloud into the MFMA operand layout of kernels.h.
+template <typename T>
+__global__ __launch_bounds__(256) void pack_points_kernel(const T* __restrict__ src, int64_t rows,
+                                                           int64_t d, int64_t ld, int64_t total,
+                                                           int kbp, u32x4* __restrict__ dst) {
+  constexpr int KW = 16 / sizeof(T);  // values per lane per k-block
+  for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * 256) {
+    const int lane = (int)(idx & 63);
+    const int64_t tk = idx >> 6;
+    const int kb = (int)(tk % kbp);
+    const int64_t t = tk / kbp;
+    const int64_t row = t * kTile + (lane & 31);
+    const int64_t k0 = (int64_t)kb * (2 * KW) + (lane >> 5) * KW;
+    T v[KW];
+#pragma unroll
+    for (int e = 0; e < KW; ++e)
+      v[e] = (row < rows && k0 + e < d) ? src[row * ld + k0 + e] : T(0);
+    dst[idx] = __builtin_bit_cast(u32x4, v);
+  }
+}
+
+// Packs V (rows streamed x cols) as the A operand of O^T += V^T P^T: for
+// column tile t, column block pb (32 values of p), quad q and lane l the four
+// floats are V[32t + 8q + 4(l/32) + e][32pb + l%32], e = 0..3 -- the row order
+// of the score accumulator registers 4q..4q+3.
+template <typename T>
+__global__ __launch_bounds__(256) void pack_values_kernel(const T* __restrict__ V, int64_t rows,
+                                                           int64_t cols, int64_t ldv,
+                                                           int64_t total, int pblocks,
+                                                           f32x4* __restrict__ dst) {
+  for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * 256) {
+    const int lane = (int)(idx & 63);
+    const int q = (int)((idx >> 6) & 3);
+    const int64_t tp = idx >> 8;
+    const int pb = (int)(tp % pblocks);
+    const int64_t t = tp / pblocks;
+    const int64_t col = (int64_t)pb * 32 + (lane & 31);
+    const int64_t r0 = t * kTile + 8 * q + 4 * (lane >> 5);
+    f32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      v[e] = (col < cols && r0 + e < rows) ? load_as_f32<T>(V, (r0 + e) * ldv + col) : 0.f;
+    dst[idx] = v;
+  }
+}
+
+__global__ __launch_bounds__(256) void weights_kernel(const float* __restrict__ w, int rows,
+                                                       int rpad, float eps,
+                                                       float* __restrict__ wgt,
+                                                       float* __restrict__ hlw) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= rpad) return;
+  if (i < rows) {
+    const float wi = w ? w[i] : 1.0f / (float)rows;
+    wgt[i] = wi;
+    hlw[i] = 0.5f * eps * logf(wi);
+  } else {
+    wgt[i] = 0.f;
+    hlw[i] = 0.f;
+  }
+}
+
+__global__ __launch_bounds__(256) void fill_kernel(float* __restrict__ p, float v, int64_t count) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < count;
+       i += (int64_t)gridDim.x * 256)
+    p[i] = v;
+}
+
+__global__ __launch_bounds__(256) void bias_from_pot_kernel(const float* __restrict__ pot,
+                                                             const float* __restrict__ norm,
+                                                             const float* __restrict__ hlw,
+                                                             int rows, int rpad,
+                                                             float* __restrict__ bias) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= rpad) return;
+  bias[i] = (i < rows) ? 0.5f * (pot[i] - norm[i]) + hlw[i] : kSentinel;
+}
+
+// ---------------------------------------------------------------------------
+// Streamed transport application partials (Algorithm 2 / 4 of the page).
+// Per split s and row i: (M, S) as in the LSE pass, and
+//   O[p] = sum_j exp2(c (v_ij - M)) V[j][p]
+// accumulated as O^T (p x i) += V^T (p x j) P^T (j x i) on the matrix cores.
+// Both half-waves of a row share the running max, so O needs no merge.
+// Grid: (nrowgroups * splits, passes); pass y covers value blocks
+// [y * PB, y * PB + PB) of 32 columns each.
+// ---------------------------------------------------------------------------
+template <bool BF16, int KB, bool XRES, int PB>
+__global__ __launch_bounds__(256) void apply_partial_kernel(
+    const u32x4* __restrict__ Rp, const u32x4* __restrict__ Cp, const float* __restrict__ cbias,
+    const f32x4* __restrict__ Vp, int rtiles, int ctiles, int kbp, int splits, int tps, float c,
+    int pblocks, float2* __restrict__ partMS, float* __restrict__ partO, int rpad, int ppad) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int h = lane >> 5;
+  const int s = blockIdx.x % splits;
+  const int rg = blockIdx.x / splits;
+  const int rt = rg * kWaves + wave;
+  if (rt >= rtiles) return;
+  const int pb0 = blockIdx.y * PB;
+  const int jt0 = s * tps;
+  const int jt1 = min(jt0 + tps, ctiles);
+
+  u32x4 xr[KB];
+  if constexpr (XRES) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) xr[kb] = Rp[((size_t)rt * KB + kb) * 64 + lane];
+  }
+  float M = -1.0e30f, S = 0.f;
+  f32x16 O[PB];
+#pragma unroll
+  for (int pb = 0; pb < PB; ++pb) O[pb] = f32x16{};
+
+  for (int jt = jt0; jt < jt1; ++jt) {
+    f32x16 acc = f32x16{};
+    if constexpr (XRES) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        acc = mfma_kblock<BF16>(Cp[((size_t)jt * KB + kb) * 64 + lane], xr[kb], acc);
+    } else {
+      for (int kc = 0; kc < kbp; kc += KB) {
+        u32x4 yc[KB], xc[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          yc[kb] = Cp[((size_t)jt * kbp + kc + kb) * 64 + lane];
+          xc[kb] = Rp[((size_t)rt * kbp + kc + kb) * 64 + lane];
+        }
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) acc = mfma_kblock<BF16>(yc[kb], xc[kb], acc);
+      }
+    }
+    acc = mfma_bias(cbias[jt * kTile + (lane & 31)], h, acc);
+
+    // Running max shared by the lane pair (l, l ^ 32) that holds row i.
+    float mx = max16(acc);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float Mn = fmaxf(M, mx);
+    const float cm = c * Mn;
+    const float sc = __builtin_amdgcn_exp2f(fmaf(c, M, -cm));
+    M = Mn;
+    S *= sc;
+#pragma unroll
+    for (int pb = 0; pb < PB; ++pb) O[pb] *= sc;
+    float p[16];
+    float ssum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      p[r] = __builtin_amdgcn_exp2f(fmaf(c, acc[r], -cm));
+      ssum += p[r];
+    }
+    S += ssum;
+#pragma unroll
+    for (int pb = 0; pb < PB; ++pb) {
+      if (pb0 + pb < pblocks) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 vv = Vp[(((size_t)jt * pblocks + pb0 + pb) * 4 + q) * 64 + lane];
+          O[pb] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv[0], p[4 * q + 0], O[pb], 0, 0, 0);
+          O[pb] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv[1], p[4 * q + 1], O[pb], 0, 0, 0);
+          O[pb] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv[2], p[4 * q + 2], O[pb], 0, 0, 0);
+          O[pb] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv[3], p[4 * q + 3], O[pb], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  S += __shfl_xor(S, 32);
+  const size_t row = (size_t)rt * kTile + (lane & 31);
+  if (blockIdx.y == 0 && h == 0) partMS[(size_t)s * rpad + row] = make_float2(M, S);
+#pragma unroll
+  for (int pb = 0; pb < PB; ++pb) {
+    if (pb0 + pb < pblocks) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int pcol = 32 * (pb0 + pb) + 8 * (r >> 2) + 4 * h + (r & 3);
+        partO[((size_t)s * ppad + pcol) * rpad + row] = O[pb][r];
+      }
+    }
+  }
+}
+
+// Merge of P V partials and epilogue. For row i of the coupling induced by
+// (pot, other potential):
+//   P_ij = w_i exp((pot_i - norm_i)/eps) exp((2/eps) v_ij)   (v = x.y + bias)
+//   factor_i = w_i exp((pot_i - norm_i + 2 M_i)/eps),  (P V)_i = factor_i O_i,
+//   r_i = factor_i S_i, barycentric = O_i / S_i, gradient = 2 (r_i x_i - (P Y)_i).
+// Workgroup: 32 rows x 32 columns, transposed through LDS for coalesced stores.
+template <typename T>
+__global__ __launch_bounds__(256) void apply_merge_kernel(
+    const float2* __restrict__ partMS, const float* __restrict__ partO, int splits, int rpad,
+    int ppad, int rows, int cols, float c, float eps, const float* __restrict__ pot,
+    const float* __restrict__ norm, const float* __restrict__ wgt, int mode,
+    const T* __restrict__ Xsrc, int64_t ldx, float* __restrict__ out, float* __restrict__ marg) {
+  __shared__ float scl[kMaxApplySplits][32];
+  __shared__ float fac[32], rr[32], ss[32];
+  __shared__ float tile[32][33];
+  const int t = threadIdx.x;
+  const int i0 = blockIdx.x * 32;
+  const int p0 = blockIdx.y * 32;
+  if (t < 32) {
+    const int i = i0 + t;
+    if (i < rows) {
+      float M = partMS[i].x;
+      for (int s = 1; s < splits; ++s) M = fmaxf(M, partMS[(size_t)s * rpad + i].x);
+      const float cm = c * M;
+      float S = 0.f;
+      for (int s = 0; s < splits; ++s) {
+        const float2 ps = partMS[(size_t)s * rpad + i];
+        const float e = exp2f(fmaf(c, ps.x, -cm));
+        scl[s][t] = e;
+        S += ps.y * e;
+      }
+      const float f = wgt[i] * exp2f((pot[i] - norm[i] + 2.f * M) * (kLog2e / eps));
+      fac[t] = f;
+      ss[t] = S;
+      rr[t] = f * S;
+    }
+  }
+  __syncthreads();
+  const int tx = t & 31;
+  const int ty = t >> 5;
+  const int i = i0 + tx;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int pl = ty + 8 * k;
+    const int p = p0 + pl;
+    float val = 0.f;
+    if (i < rows && p < cols) {
+      float O = 0.f;
+      for (int s = 0; s < splits; ++s) O += partO[((size_t)s * ppad + p) * rpad + i] * scl[s][tx];
+      if (mode == kApplyBary) {
+        val = O / ss[tx];
+      } else if (mode == kApplyGrad) {
+        const float xv = load_as_f32<T>(Xsrc, (int64_t)i * ldx + p);
+        val = 2.f * (rr[tx] * xv - fac[tx] * O);
+      } else {
+        val = fac[tx] * O;
+      }
+    }
+    tile[tx][pl] = val;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int rl = ty + 8 * k;
+    const int ii = i0 + rl;
+    const int p = p0 + tx;
+    if (ii < rows && p < cols) out[(size_t)ii * cols + p] = tile[rl][tx];
+  }
+  if (marg && blockIdx.y == 0 && t < 32 && i0 + t < rows) marg[i0 + t] = rr[t];
+}
+
+// ---------------------------------------------------------------------------
+// Launchers.
+// ---------------------------------------------------------------------------
+static int grid_for(int64_t total, int64_t per_block, int64_t cap = 1 << 20) {
+  int64_t g = (total + per_block - 1) / per_block;
+  if (g < 1) g = 1;
+  if (g > cap) g = cap;
+  return (int)g;
+}
+
+hipError_t launch_sqnorms(const void* pts, int bf16, int64_t rows, int64_t d, int64_t ld,
+                          float* out, hipStream_t st) {
+  const int grid = (int)((rows + 3) / 4);
+  if (bf16)
+    sqnorms_kernel<uint16_t><<<grid, 256, 0, st>>>((const uint16_t*)pts, rows, d, ld, out);
+  else
+    sqnorms_kernel<float><<<grid, 256, 0, st>>>((const float*)pts, rows, d, ld, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_points(const void* src, int bf16, int64_t rows, int64_t d, int64_t ld,
+                              int rtiles, int kbp, void* dst, hipStream_t st) {
+  const int64_t total = (int64_t)rtiles * kbp * 64;
+  const int grid = grid_for(total, 256, 65536);
+  if (bf16)
+    pack_points_kernel<uint16_t>
+        <<<grid, 256, 0, st>>>((const uint16_t*)src, rows, d, ld, total, kbp, (u32x4*)dst);
+  else
+    pack_points_kernel<float>
+        <<<grid, 256, 0, st>>>((const float*)src, rows, d, ld, total, kbp, (u32x4*)dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_values(const void* V, int bf16, int64_t rows, int64_t cols, int64_t ldv,
+                              int ctiles, int pblocks, float* dst, hipStream_t st) {
+  const int64_t total = (int64_t)ctiles * pblocks * 4 * 64;
+  const int grid = grid_for(total, 256, 65536);
+  if (bf16)
+    pack_values_kernel<uint16_t><<<grid, 256, 0, st>>>((const uint16_t*)V, rows, cols, ldv, total,
+                                                       pblocks, (f32x4*)dst);
+  else
+    pack_values_kernel<float>
+        <<<grid, 256, 0, st>>>((const float*)V, rows, cols, ldv, total, pblocks, (f32x4*)dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_weights(const float* w, int rows, int rpad, float eps, float* wgt, float* hlw,
+                          hipStream_t st) {
+  weights_kernel<<<(rpad + 255) / 256, 256, 0, st>>>(w, rows, rpad, eps, wgt, hlw);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill(float* p, float v, int64_t count, hipStream_t st) {
+  fill_kernel<<<grid_for(count, 256, 65536), 256, 0, st>>>(p, v, count);
+  return hipGetLastError();
+}
+
+hipError_t launch_bias_from_pot(const float* pot, const float* norm, const float* hlw, int rows,
+                                int rpad, float* bias, hipStream_t st) {
+  bias_from_pot_kernel<<<(rpad + 255) / 256, 256, 0, st>>>(pot, norm, hlw, rows, rpad, bias);
+  return hipGetLastError();
+}
+
+template <bool BF16, int KB, int RI, bool XRES>
+static void lse_go(const PassShape& s, const void* Rp, const void* Cp, const float* cbias,
+                   float c, float2* part, hipStream_t st) {
+  lse_partial_kernel<BF16, KB, RI, XRES><<<s.nrowgroups * s.splits, 256, 0, st>>>(
+      (const u32x4*)Rp, (const u32x4*)Cp, cbias, s.rtiles, s.ctiles, s.kbp, s.splits, s.tps, c,
+      part, s.rtiles * kTile);
+}
+
+template <bool BF16>
+static hipError_t lse_dispatch(const PassShape& s, const void* Rp, const void* Cp,
+                               const float* cbias, float c, float2* part, hipStream_t st) {
+  if (!s.xres) {
+    if (s.ri == 2)
+      lse_go<BF16, 8, 2, false>(s, Rp, Cp, cbias, c, part, st);
+    else
+      lse_go<BF16, 8, 1, false>(s, Rp, Cp, cbias, c, part, st);
+    return hipGetLastError();
+  }
+#define FLASHOT_LSE_CASE(KBV)                                  \
+  case KBV:                                                    \
+    if (s.ri == 2)                                             \
+      lse_go<BF16, KBV, 2, true>(s, Rp, Cp, cbias, c, part, st); \
+    else                                                       \
+      lse_go<BF16, KBV, 1, true>(s, Rp, Cp, cbias, c, part, st); \
+    break;
+  switch (s.kb) {
+    FLASHOT_LSE_CASE(1)
+    FLASHOT_LSE_CASE(2)
+    FLASHOT_LSE_CASE(4)
+    FLASHOT_LSE_CASE(8)
+    FLASHOT_LSE_CASE(16)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef FLASHOT_LSE_CASE
+  return hipGetLastError();
+}
+
+hipError_t launch_lse_partial(const PassShape& s, int bf16, const void* Rp, const void* Cp,
+                              const float* cbias, float c, float2* part, hipStream_t st) {
+  return bf16 ? lse_dispatch<true>(s, Rp, Cp, cbias, c, part, st)
+              : lse_dispatch<false>(s, Rp, Cp, cbias, c, part, st);
+}
+
+hipError_t launch_lse_merge(const float2* part, int splits, int rpad, int rows, float c, float eps,
+                            const float* norm, const float* hlw, const float* wgt, float* pot,
+                            float* bias_out, float* err_part, int with_err, int write_pot,
+                            hipStream_t st) {
+  lse_merge_kernel<<<(rpad + 255) / 256, 256, 0, st>>>(part, splits, rpad, rows, c, eps, norm,
+                                                       hlw, wgt, pot, bias_out, err_part,
+                                                       with_err, write_pot);
+  return hipGetLastError();
+}
+
+hipError_t launch_err_reduce(const float* part, int count, float* out, hipStream_t st) {
+  err_reduce_kernel<<<1, 256, 0, st>>>(part, count, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_nonfinite(const float* f, int n, const float* g, int m, float* out,
+                            hipStream_t st) {
+  nonfinite_kernel<<<1, 256, 0, st>>>(f, n, g, m, out);
+  return hipGetLastError();
+}
+
+template <bool BF16, int KB, bool XRES, int PB>
+static void apply_go(const PassShape& s, int pblocks, const void* Rp, const void* Cp,
+                     const float* cbias, const float* Vp, float c, float2* partMS, float* partO,
+                     int ppad, hipStream_t st) {
+  dim3 grid(s.nrowgroups * s.splits, (pblocks + PB - 1) / PB);
+  apply_partial_kernel<BF16, KB, XRES, PB><<<grid, 256, 0, st>>>(
+      (const u32x4*)Rp, (const u32x4*)Cp, cbias, (const f32x4*)Vp, s.rtiles, s.ctiles, s.kbp,
+      s.splits, s.tps, c, pblocks, partMS, partO, s.rtiles * kTile, ppad);
+}
+
+template <bool BF16, int PB>
+static hipError_t apply_dispatch_kb(const PassShape& s, int pblocks, const void* Rp,
+                                    const void* Cp, const float* cbias, const float* Vp, float c,
+                                    float2* partMS, float* partO, int ppad, hipStream_t st) {
+  if (!s.xres) {
+    apply_go<BF16, 8, false, PB>(s, pblocks, Rp, Cp, cbias, Vp, c, partMS, partO, ppad, st);
+    return hipGetLastError();
+  }
+  switch (s.kb) {
+    case 1: apply_go<BF16, 1, true, PB>(s, pblocks, Rp, Cp, cbias, Vp, c, partMS, partO, ppad, st); break;
+    case 2: apply_go<BF16, 2, true, PB>(s, pblocks, Rp, Cp, cbias, Vp, c, partMS, partO, ppad, st); break;
+    case 4: apply_go<BF16, 4, true, PB>(s, pblocks, Rp, Cp, cbias, Vp, c, partMS, partO, ppad, st); break;
+    case 8: apply_go<BF16, 8, true, PB>(s, pblocks, Rp, Cp, cbias, Vp, c, partMS, partO, ppad, st); break;
+    case 16: apply_go<BF16, 16, true, PB>(s, pblocks, Rp, Cp, cbias, Vp, c, partMS, partO, ppad, st); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <bool BF16>
+static hipError_t apply_dispatch(const PassShape& s, int pblocks, int pb_per_pass, const void* Rp,
+                                 const void* Cp, const float* cbias, const float* Vp, float c,
+                                 float2* partMS, float* partO, int ppad, hipStream_t st) {
+  switch (pb_per_pass) {
+    case 1: return apply_dispatch_kb<BF16, 1>(s, pblocks, Rp, Cp, cbias, Vp, c, partMS, partO, ppad, st);
+    case 2: return apply_dispatch_kb<BF16, 2>(s, pblocks, Rp, Cp, cbias, Vp, c, partMS, partO, ppad, st);
+    case 4: return apply_dispatch_kb<BF16, 4>(s, pblocks, Rp, Cp, cbias, Vp, c, partMS, partO, ppad, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_apply_partial(const PassShape& s, int bf16, int pblocks, int pb_per_pass,
+                                const void* Rp, const void* Cp, const float* cbias,
+                                const float* Vp, float c, float2* partMS, float* partO, int ppad,
+                                hipStream_t st) {
+  return bf16 ? apply_dispatch<true>(s, pblocks, pb_per_pass, Rp, Cp, cbias, Vp, c, partMS, partO,
+                                     ppad, st)
+              : apply_dispatch<false>(s, pblocks, pb_per_pass, Rp, Cp, cbias, Vp, c, partMS,
+                                      partO, ppad, st);
+}
+
+hipError_t launch_apply_merge(const float2* partMS, const float* partO, int splits, int rpad,
+                              int ppad, int rows, int cols, float c, float eps, const float* pot,
+                              const float* norm, const float* wgt, int mode, const void* Xsrc,
+                              int xbf16, int64_t ldx, float* out, float* marg, hipStream_t st) {
+  if (splits > kMaxApplySplits) return hipErrorInvalidValue;
+  dim3 grid((rows + 31) / 32, (cols + 31) / 32);
+  if (xbf16)
+    apply_merge_kernel<uint16_t><<<grid, 256, 0, st>>>(partMS, partO, splits, rpad, ppad, rows,
+                                                       cols, c, eps, pot, norm, wgt, mode,
+                                                       (const uint16_t*)Xsrc, ldx, out, marg);
+  else
+    apply_merge_kernel<float><<<grid, 256, 0, st>>>(partMS, partO, splits, rpad, ppad, rows, cols,
+                                                    c, eps, pot, norm, wgt, mode,
+                                                    (const float*)Xsrc, ldx, out, marg);
+  return hipGetLastError();
+}
+
+}  // namespace flashot

@@ -1,0 +1,146 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+the header declares, and rejects bad arguments on the host before any HIP call
+(workspace-size queries are host-only as well)."""
+
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import streaming_sinkhorn_amd as ssa
+
+LIB = ssa.LIB_PATH
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libflashot.so not built")
+
+
+def _problem(n=100, m=70, d=16, dtype=ssa.OT_F32, eps=0.1, x=1 << 20, y=2 << 20):
+    # Fake, never dereferenced device addresses: every call below fails or
+    # returns during host-side validation / size queries.
+    return ssa.OtProblem(x, y, n, m, d, d, d, dtype, eps, None, None, None, None)
+
+
+def _size(fn, *args):
+    sz = ctypes.c_size_t(0)
+    rc = fn(*args, None, ctypes.byref(sz), None)
+    return rc, sz.value
+
+
+def test_exports_every_header_symbol():
+    names = ssa.header_entry_points()
+    assert set(["ot_sqnorms", "ot_update_f", "ot_update_g", "ot_solve", "ot_apply_plan"]) <= set(names)
+    L = ssa.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    for n in names:
+        assert n in exported, f"{n} not exported with C linkage"
+    assert ssa.version().startswith("flashot")
+
+
+def test_workspace_query_is_host_only_and_monotone():
+    L = ssa.lib()
+    p1 = _problem(1000, 1000, 64)
+    p2 = _problem(2000, 1000, 64)
+    rc1, s1 = _size(L.ot_update_f, ctypes.byref(p1), None, None, None)
+    rc2, s2 = _size(L.ot_update_f, ctypes.byref(p2), None, None, None)
+    assert rc1 == 0 and rc2 == 0 and 0 < s1 < s2
+    opts = ssa.OtSolveOpts(10, 0.0, 1, 0, 1, 0, 0, 0)
+    sz = ctypes.c_size_t(0)
+    assert L.ot_solve(ctypes.byref(p1), None, None, ctypes.byref(opts), None, None, ctypes.byref(sz), None) == 0
+    assert sz.value >= s1
+    sz = ctypes.c_size_t(0)
+    assert L.ot_apply_plan(ctypes.byref(p1), None, None, None, 0, 64, 64, 0, None, None, None,
+                           ctypes.byref(sz), None) == 0
+    assert sz.value > 0
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("n", 0, ssa.OT_ERR_INVALID_ARG),
+    ("m", -3, ssa.OT_ERR_INVALID_ARG),
+    ("d", 0, ssa.OT_ERR_INVALID_ARG),
+    ("ldx", 8, ssa.OT_ERR_INVALID_ARG),
+    ("eps", 0.0, ssa.OT_ERR_INVALID_ARG),
+    ("eps", -1.0, ssa.OT_ERR_INVALID_ARG),
+    ("eps", float("nan"), ssa.OT_ERR_INVALID_ARG),
+    ("eps", 1e-45, ssa.OT_ERR_UNSUPPORTED),
+    ("dtype", 7, ssa.OT_ERR_UNSUPPORTED),
+    ("d", 100000, ssa.OT_ERR_UNSUPPORTED),
+    ("x", 0, ssa.OT_ERR_INVALID_ARG),
+    ("x", (1 << 20) + 2, ssa.OT_ERR_INVALID_ARG),   # fp32 data must be 4-byte aligned
+])
+def test_problem_validation(field, value, code):
+    L = ssa.lib()
+    p = _problem()
+    setattr(p, field, value)
+    if field == "d" and value > 16:
+        p.ldx = p.ldy = value
+    for fn in (L.ot_update_f, L.ot_update_g):
+        rc, _ = _size(fn, ctypes.byref(p), None, None, None)
+        assert rc == code, (field, value, rc, L.ot_last_error())
+    assert L.ot_last_error()
+
+
+def test_null_problem_and_null_sizes():
+    L = ssa.lib()
+    assert L.ot_update_f(None, None, None, None, None, None, None) == ssa.OT_ERR_INVALID_ARG
+    p = _problem()
+    assert L.ot_update_f(ctypes.byref(p), None, None, None, None, None, None) == ssa.OT_ERR_INVALID_ARG
+    assert L.ot_sqnorms(None, 0, 10, 4, 4, None, None) == ssa.OT_ERR_INVALID_ARG
+    assert L.ot_sqnorms(1 << 20, 0, 0, 4, 4, 2 << 20, None) == ssa.OT_ERR_INVALID_ARG
+    assert L.ot_sqnorms(1 << 20, 5, 10, 4, 4, 2 << 20, None) == ssa.OT_ERR_UNSUPPORTED
+
+
+def test_workspace_too_small_and_misaligned():
+    L = ssa.lib()
+    p = _problem()
+    rc, need = _size(L.ot_update_f, ctypes.byref(p), None, None, None)
+    small = ctypes.c_size_t(need - 1)
+    assert L.ot_update_f(ctypes.byref(p), 3 << 20, 4 << 20, None, 5 << 20, ctypes.byref(small), None) \
+        == ssa.OT_ERR_WORKSPACE
+    ok = ctypes.c_size_t(need)
+    assert L.ot_update_f(ctypes.byref(p), 3 << 20, 4 << 20, None, (5 << 20) + 4, ctypes.byref(ok), None) \
+        == ssa.OT_ERR_INVALID_ARG
+
+
+def test_solve_option_validation():
+    L = ssa.lib()
+    p = _problem()
+    sz = ctypes.c_size_t(1 << 40)
+    bad = [
+        ssa.OtSolveOpts(-1, 0.0, 1, 0, 1, 0, 0, 0),      # iters < 0
+        ssa.OtSolveOpts(5, -1.0, 1, 0, 1, 0, 0, 0),      # tol < 0
+        ssa.OtSolveOpts(5, 1e-3, 0, 0, 1, 0, 0, 0),      # tol > 0 needs check_every
+        ssa.OtSolveOpts(5, 0.0, 1, 9, 1, 0, 0, 0),       # init
+        ssa.OtSolveOpts(5, 0.0, 1, 0, 1, -2, 0, 0),      # splits
+        ssa.OtSolveOpts(5, 0.0, 1, 0, 1, 0, 0, 1),       # timing without info
+    ]
+    for o in bad:
+        assert L.ot_solve(ctypes.byref(p), 1 << 21, 1 << 22, ctypes.byref(o), None, 1 << 23,
+                          ctypes.byref(sz), None) == ssa.OT_ERR_INVALID_ARG
+    assert L.ot_solve(ctypes.byref(p), 1 << 21, 1 << 22, None, None, 1 << 23, ctypes.byref(sz), None) \
+        == ssa.OT_ERR_INVALID_ARG
+
+
+def test_apply_plan_validation():
+    L = ssa.lib()
+    p = _problem()
+    sz = ctypes.c_size_t(1 << 40)
+    args = lambda v_dtype, cols, ldv, flags: L.ot_apply_plan(
+        ctypes.byref(p), 1 << 21, 1 << 22, 1 << 23, v_dtype, cols, ldv, flags, 1 << 24, None,
+        1 << 25, ctypes.byref(sz), None)
+    assert args(0, 0, 0, 0) == ssa.OT_ERR_INVALID_ARG          # cols < 1
+    assert args(0, 8, 4, 0) == ssa.OT_ERR_INVALID_ARG          # ldv < cols
+    assert args(3, 8, 8, 0) == ssa.OT_ERR_UNSUPPORTED          # v dtype
+    assert args(0, 8, 8, 64) == ssa.OT_ERR_INVALID_ARG         # unknown flag
+    assert args(0, 8, 8, ssa.OT_GRAD | ssa.OT_BARY) == ssa.OT_ERR_INVALID_ARG
+    assert args(0, 100000, 100000, 0) == ssa.OT_ERR_UNSUPPORTED
+
+
+def test_binding_refuses_to_run_without_library(tmp_path, monkeypatch):
+    """The product path has no fallback: a missing library raises on use."""
+    monkeypatch.setattr(ssa, "_lib", None)
+    monkeypatch.setattr(ssa, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        ssa.lib()

@@ -1,0 +1,284 @@
+"""GPU parity of the HIP path against the fp64 oracle, element by element.
+
+All calls go through the C ABI (via the ctypes binding). Sizes are chosen so
+that the dense oracle finishes in seconds while the GPU side spans several
+32-row tiles, several column splits and a ragged tail. Tolerances are the
+ones the project is held to: max |df|, |dg| <= 1e-4 for fp32 inputs and
+<= 2e-2 for bf16 inputs; relative Frobenius error of P V <= 1e-4 for fp32
+with identical potentials fed to both sides (bf16 inputs use the same gate:
+the oracle receives the exact bf16 values, so only fp32 rounding separates
+the two sides).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import streaming_sinkhorn_amd as ssa
+import workloads
+from gpu_util import DEV, host64, make_problem, oracle_inputs, say, zeros
+
+pytestmark = pytest.mark.gpu
+
+POT_TOL = {"f32": 1e-4, "bf16": 2e-2}
+PV_TOL = 1e-4
+
+
+def _rel(a, b):
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+# --- building blocks -------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("rows,d", [(1, 1), (37, 3), (100, 64), (333, 1000)])
+def test_sqnorms(dtype, rows, d):
+    say(f"sqnorms dtype={dtype} rows={rows} d={d}")
+    data = workloads.make("c3_d16_f32", n=rows, m=1, d=d)
+    X = torch.from_numpy(data["X"]).to(DEV)
+    if dtype == "bf16":
+        X = X.to(torch.bfloat16)
+    out = ssa.ot_sqnorms(X)
+    torch.cuda.synchronize()
+    ref = oracle.sqnorms(host64(X))
+    np.testing.assert_allclose(host64(out), ref, rtol=2e-6, atol=1e-6)
+
+
+# --- single half-steps (teacher-forced: identical inputs on both sides) -----------
+
+HALF_CASES = [
+    # (n, m, d, dtype, eps)
+    (333, 517, 16, "f32", 0.1),
+    (517, 333, 64, "f32", 0.1),
+    (70, 1500, 1, "f32", 0.1),
+    (129, 95, 3, "f32", 0.05),
+    (260, 300, 17, "f32", 0.1),
+    (300, 260, 100, "f32", 0.1),
+    (200, 190, 128, "f32", 0.1),
+    (150, 210, 200, "f32", 0.1),
+    (120, 140, 512, "f32", 0.1),
+    (97, 64, 1024, "f32", 0.01),
+    (333, 517, 16, "bf16", 0.1),
+    (300, 260, 64, "bf16", 0.1),
+    (200, 190, 128, "bf16", 0.1),
+    (150, 210, 256, "bf16", 0.1),
+    (120, 140, 512, "bf16", 0.1),
+    (97, 64, 1024, "bf16", 0.01),
+]
+
+
+@pytest.mark.parametrize("n,m,d,dtype,eps", HALF_CASES)
+def test_half_steps_teacher_forced(n, m, d, dtype, eps):
+    say(f"half-steps n={n} m={m} d={d} dtype={dtype} eps={eps}")
+    base = "c3_d16_bf16" if dtype == "bf16" else "c3_d16_f32"
+    data = workloads.make(base, n=n, m=m, d=d)
+    prob = make_problem(data, eps=eps)
+    X, Y, a, b = oracle_inputs(prob)
+    C = oracle.cost_matrix(X, Y)
+    rng = np.random.default_rng(n * 7 + m)
+    g0 = (rng.standard_normal(m) * 0.3).astype(np.float32)
+    f0 = (rng.standard_normal(n) * 0.3).astype(np.float32)
+    g = torch.from_numpy(g0).to(DEV)
+    f = torch.from_numpy(f0).to(DEV)
+    err = torch.zeros(1, dtype=torch.float32, device=DEV)
+    ssa.ot_update_f(prob, g, f, err=err)
+    torch.cuda.synchronize()
+    f_ref = oracle.update_f(C, g0.astype(np.float64), b, eps)
+    tol = POT_TOL[dtype]
+    df = np.abs(host64(f) - f_ref).max()
+    assert df <= tol, f"max|df| = {df}"
+    # err = ||P(f0, g0) 1 - a||_1
+    r, _ = oracle.marginals(oracle.plan(C, a, b, f0.astype(np.float64), g0.astype(np.float64), eps))
+    e_ref = np.abs(r - a).sum()
+    assert abs(float(err.item()) - e_ref) <= 1e-3 * max(e_ref, 1.0)
+    # g half-step from the GPU's f
+    f_in = host64(f)
+    g2 = torch.from_numpy(g0).to(DEV)
+    ssa.ot_update_g(prob, f, g2, err=err)
+    torch.cuda.synchronize()
+    g_ref = oracle.update_g(C, f_in, a, eps)
+    dg = np.abs(host64(g2) - g_ref).max()
+    assert dg <= tol, f"max|dg| = {dg}"
+    # after the g half-step the column marginals of P(f, g) are b, up to the
+    # potential error: c_j = b_j exp((g_gpu - g_exact)_j / eps)
+    _, c = oracle.marginals(oracle.plan(C, a, b, f_in, host64(g2), eps))
+    assert np.abs(c - b).sum() <= np.expm1(dg / eps) * b.sum() * 1.01 + 1e-7
+
+
+# --- full trajectories ----------------------------------------------------------------
+
+TRAJ_CASES = [
+    # workload, n, m, d override (None = workload's), iters override
+    ("c1", None, None, None, None),
+    ("c2", 700, 555, None, None),
+    ("c3_d16_f32", 500, 650, None, None),
+    ("c3_d128_f32", 500, 650, None, None),
+    ("c3_d512_f32", 300, 420, None, None),
+    ("c3_d1024_f32", 300, 250, None, None),
+    ("c3_d16_bf16", 500, 650, None, None),
+    ("c3_d128_bf16", 500, 650, None, None),
+    ("c3_d512_bf16", 300, 420, None, None),
+    ("c3_d1024_bf16", 300, 250, None, None),
+    ("c4", 800, 700, None, 200),
+    ("c5", 1000, 120, None, 300),
+]
+
+
+@pytest.mark.parametrize("name,n,m,d,iters", TRAJ_CASES)
+def test_solve_trajectory(name, n, m, d, iters):
+    data = workloads.make(name, n=n, m=m, d=d)
+    w = data["w"]
+    T = w.iters if iters is None else iters
+    say(f"trajectory {name} n={w.n} m={w.m} d={w.d} dtype={w.dtype} eps={w.eps} T={T}")
+    prob = make_problem(data)
+    X, Y, a, b = oracle_inputs(prob)
+    f = zeros(w.n)
+    g = zeros(w.m)
+    info = ssa.ot_solve(prob, f, g, T)
+    torch.cuda.synchronize()
+    C = oracle.cost_matrix(X, Y)
+    f_ref, g_ref = oracle.sinkhorn(C, a, b, w.eps, T)
+    tol = POT_TOL[w.dtype]
+    df = np.abs(host64(f) - f_ref).max()
+    dg = np.abs(host64(g) - g_ref).max()
+    say(f"  max|df|={df:.3e} max|dg|={dg:.3e} info={info}")
+    assert df <= tol and dg <= tol
+    # the reported marginal errors are those of the returned potentials
+    er, ec = oracle.marginal_errors(oracle.plan(C, a, b, host64(f), host64(g), w.eps), a, b)
+    assert info["iters_done"] == T and not info["nonfinite"]
+    slack = 5e-6 * (0.1 / w.eps)
+    assert abs(info["marg_err_row"] - er) <= 1e-2 * er + slack
+    assert abs(info["marg_err_col"] - ec) <= 1e-2 * ec + slack
+
+
+# --- transport application ------------------------------------------------------------
+
+APPLY_CASES = [
+    # n, m, d, dtype, eps, cols
+    (333, 517, 16, "f32", 0.1, 64),
+    (517, 333, 64, "f32", 0.1, 64),
+    (300, 260, 128, "f32", 0.1, 128),
+    (200, 150, 1024, "f32", 0.01, 128),
+    (260, 300, 64, "bf16", 0.1, 64),
+    (150, 170, 512, "bf16", 0.1, 33),
+    (90, 75, 17, "f32", 0.05, 1),
+    (64, 1, 8, "f32", 0.1, 5),
+]
+
+
+@pytest.mark.parametrize("n,m,d,dtype,eps,cols", APPLY_CASES)
+def test_apply_plan(n, m, d, dtype, eps, cols):
+    say(f"apply n={n} m={m} d={d} dtype={dtype} eps={eps} cols={cols}")
+    base = "c3_d16_bf16" if dtype == "bf16" else "c3_d16_f32"
+    data = workloads.make(base, n=n, m=m, d=d)
+    prob = make_problem(data, eps=eps)
+    X, Y, a, b = oracle_inputs(prob)
+    f = zeros(n)
+    g = zeros(m)
+    ssa.ot_solve(prob, f, g, 20, want_info=False)
+    torch.cuda.synchronize()
+    fh, gh = host64(f), host64(g)
+    C = oracle.cost_matrix(X, Y)
+    P = oracle.plan(C, a, b, fh, gh, eps)
+    rng = np.random.default_rng(n + m + d)
+    V = rng.standard_normal((m, cols)).astype(np.float32)
+    U = rng.standard_normal((n, cols)).astype(np.float32)
+    Vt = torch.from_numpy(V).to(DEV)
+    Ut = torch.from_numpy(U).to(DEV)
+    if dtype == "bf16":
+        Vt, Ut = Vt.to(torch.bfloat16), Ut.to(torch.bfloat16)
+    r = torch.empty(n, dtype=torch.float32, device=DEV)
+    c = torch.empty(m, dtype=torch.float32, device=DEV)
+    pv = ssa.ot_apply_plan(prob, f, g, Vt, marg=r)
+    ptu = ssa.ot_apply_plan(prob, f, g, Ut, flags=ssa.OT_TRANSPOSE, marg=c)
+    bary = ssa.ot_apply_plan(prob, f, g, Vt, flags=ssa.OT_BARY)
+    grad = ssa.ot_apply_plan(prob, f, g, flags=ssa.OT_GRAD)
+    gy = ssa.ot_apply_plan(prob, f, g, flags=ssa.OT_GRAD | ssa.OT_TRANSPOSE)
+    torch.cuda.synchronize()
+    Vh, Uh = host64(Vt), host64(Ut)
+    r_ref, c_ref = oracle.marginals(P)
+    assert _rel(host64(pv), oracle.apply_plan(P, Vh)) <= PV_TOL
+    assert _rel(host64(ptu), oracle.apply_plan_t(P, Uh)) <= PV_TOL
+    assert _rel(host64(bary), oracle.barycentric(P, Vh)) <= PV_TOL
+    assert _rel(host64(r), r_ref) <= PV_TOL
+    assert _rel(host64(c), c_ref) <= PV_TOL
+    g_ref = oracle.grad_x(X, Y, P)
+    assert _rel(host64(grad), g_ref) <= 10 * PV_TOL
+    gy_ref = oracle.grad_x(Y, X, P.T)
+    assert _rel(host64(gy), gy_ref) <= 10 * PV_TOL
+
+
+# --- execution properties ---------------------------------------------------------------
+
+def test_deterministic_graph_eager_and_resume():
+    """Bitwise: two runs agree; graph replay equals plain launches; k then k'
+    iterations equal k + k' (the bias is rebuilt from the stored potential)."""
+    data = workloads.make("c2", n=1500, m=1300)
+    prob = make_problem(data)
+    outs = []
+    for use_graph in (True, True, False):
+        f, g = zeros(1500), zeros(1300)
+        ssa.ot_solve(prob, f, g, 23, use_graph=use_graph, want_info=False)
+        outs.append((f.clone(), g.clone()))
+    torch.cuda.synchronize()
+    for f, g in outs[1:]:
+        assert torch.equal(f, outs[0][0]) and torch.equal(g, outs[0][1])
+    f, g = zeros(1500), zeros(1300)
+    ssa.ot_solve(prob, f, g, 10, want_info=False)
+    ssa.ot_solve(prob, f, g, 13, init_given=True, want_info=False)
+    torch.cuda.synchronize()
+    assert torch.equal(f, outs[0][0]) and torch.equal(g, outs[0][1])
+
+
+def test_split_count_changes_only_rounding():
+    """The ⊕ merge of partial (max, sum) pairs is exact (App. D.3): any split count
+    gives the same potentials up to fp32 rounding."""
+    data = workloads.make("c3_d128_f32", n=900, m=1100)
+    prob = make_problem(data)
+    ref = None
+    for sf, sg in ((1, 1), (3, 5), (8, 8), (34, 28)):
+        f, g = zeros(900), zeros(1100)
+        info = ssa.ot_solve(prob, f, g, 15, splits_f=sf, splits_g=sg)
+        torch.cuda.synchronize()
+        say(f"splits {sf},{sg} -> used {info['splits_f']},{info['splits_g']}")
+        if ref is None:
+            ref = (host64(f), host64(g))
+        else:
+            assert np.abs(host64(f) - ref[0]).max() <= 2e-5
+            assert np.abs(host64(g) - ref[1]).max() <= 2e-5
+
+
+def test_tolerance_stops_early():
+    data = workloads.make("c1", n=400, m=300)
+    prob = make_problem(data)
+    f, g = zeros(400), zeros(300)
+    info = ssa.ot_solve(prob, f, g, 500, tol=1e-3, check_every=5)
+    torch.cuda.synchronize()
+    assert info["iters_done"] < 500 and info["iters_done"] % 5 == 0
+    assert info["marg_err_row"] < 1e-3
+
+
+def test_single_target_point_closed_form():
+    """m = 1: f_i = C_i1 - g_1 - eps log b_1 and P V = a V_1^T (oracle pin, on the GPU)."""
+    data = workloads.make("c3_d16_f32", n=77, m=1, d=5)
+    prob = make_problem(data, weights=False)
+    f, g = zeros(77), zeros(1)
+    ssa.ot_solve(prob, f, g, 3, want_info=False)
+    V = torch.from_numpy(np.random.default_rng(11).standard_normal((1, 4)).astype(np.float32)).to(DEV)
+    pv = ssa.ot_apply_plan(prob, f, g, V)
+    torch.cuda.synchronize()
+    X, Y, a, b = oracle_inputs(prob)
+    np.testing.assert_allclose(host64(pv), a[:, None] * host64(V)[0][None, :], rtol=1e-5, atol=1e-9)
+    assert abs(host64(g)[0]) < 1e-5
+
+
+def test_nonfinite_reported():
+    """A NaN weight propagates to the potentials; ot_solve with info says so."""
+    data = workloads.make("c1", n=100, m=90)
+    data["a"][5] = np.nan
+    prob = make_problem(data)
+    f, g = zeros(100), zeros(90)
+    with pytest.raises(ssa.OtError) as ei:
+        ssa.ot_solve(prob, f, g, 3)
+    assert ei.value.code == ssa.OT_ERR_NONFINITE
