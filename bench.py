@@ -69,7 +69,7 @@ def main():
     ap.add_argument("--workload", default="c2")
     ap.add_argument("--iters", type=int, default=None)
     ap.add_argument("--splits", type=int, default=0)
-    ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--cpu-rows", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -121,7 +121,7 @@ def main():
         # allocate workspaces via one untimed call each
         import ctypes
         sz = ctypes.c_size_t(0)
-        opts = ssa.OtSolveOpts(T, 0.0, 1, 0, 0, args.splits, args.splits, 1)
+        opts = ssa.OtSolveOpts(T, 0.0, 1, 0, 0, args.splits, args.splits, 0)
         ssa._check(ssa.lib().ot_solve(ctypes.byref(prob.c), None, None, ctypes.byref(opts), None, None,
                                       ctypes.byref(sz), None), "size")
         ws_solve[0] = torch.empty(sz.value, dtype=torch.uint8, device=dev)

@@ -26,11 +26,12 @@ COMMON = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
-# Kernel file only: MFMA results in ordinary VGPRs (the LSE reads them with the
-# VALU right away) and no NaN canonicalisation around fmaxf in the hot loop.
+# Hot-loop kernels only (kernels.hip): MFMA results in ordinary VGPRs (the LSE
+# reads them with the VALU right away) and no NaN canonicalisation around
+# fmaxf. The auxiliary kernels keep full NaN semantics.
 KERNEL_FLAGS = ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 
-SOURCES = [("kernels.hip", KERNEL_FLAGS), ("api.hip", [])]
+SOURCES = [("kernels.hip", KERNEL_FLAGS), ("aux_kernels.hip", []), ("api.hip", [])]
 
 
 def _run(cmd):

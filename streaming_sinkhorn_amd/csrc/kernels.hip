@@ -44,25 +44,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kMaxApplySplits = 64;
-
-__device__ __forceinline__ float bf16_to_f32(uint16_t u) {
-  return __uint_as_float(static_cast<uint32_t>(u) << 16);
-}
-
-template <typename T>
-__device__ __forceinline__ float load_as_f32(const T* p, int64_t idx);
-template <>
-__device__ __forceinline__ float load_as_f32<float>(const float* p, int64_t idx) {
-  return p[idx];
-}
-template <>
-__device__ __forceinline__ float load_as_f32<uint16_t>(const uint16_t* p, int64_t idx) {
-  return bf16_to_f32(p[idx]);
-}
-
 // One packed k-block of the score tile: acc[j][i] += sum_k A[j][k] B[k][i].
 template <bool BF16>
 __device__ __forceinline__ f32x16 mfma_kblock(u32x4 a, u32x4 b, f32x16 acc) {
@@ -227,189 +208,6 @@ __global__ __launch_bounds__(256) void lse_partial_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Merge of split partials + half-step epilogue (App. D.1 / D.2: write the
-// potential once). For row i:
-//   L = (2/eps) M + ln S over all splits,  shifted potential = -eps L = -2M - eps ln S,
-//   pot_i = norm_i + shifted, next bias_i = (pot_i - norm_i)/2 + (eps/2) log w_i,
-//   err_i = w_i |exp((pot_old_i - pot_i)/eps) - 1|   (App. E.1 induced marginal).
-// The bias is rebuilt from the stored fp32 potential, so resuming from
-// returned potentials reproduces an uninterrupted run bit for bit.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ float block_sum_256(float v, float* sh) {
-  const int t = threadIdx.x;
-  sh[t] = v;
-  __syncthreads();
-#pragma unroll
-  for (int w = 128; w > 0; w >>= 1) {
-    if (t < w) sh[t] += sh[t + w];
-    __syncthreads();
-  }
-  return sh[0];
-}
-
-__global__ __launch_bounds__(256) void lse_merge_kernel(
-    const float2* __restrict__ part, int splits, int rpad, int rows, float c, float eps,
-    const float* __restrict__ norm, const float* __restrict__ hlw, const float* __restrict__ wgt,
-    float* __restrict__ pot, float* __restrict__ bias_out, float* __restrict__ err_part,
-    int with_err, int write_pot) {
-  __shared__ float sh[256];
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  float e = 0.f;
-  if (i < rows) {
-    float M = part[i].x;
-    for (int s = 1; s < splits; ++s) M = fmaxf(M, part[(size_t)s * rpad + i].x);
-    const float cm = c * M;
-    float S = 0.f;
-    for (int s = 0; s < splits; ++s) {
-      const float2 ps = part[(size_t)s * rpad + i];
-      S += ps.y * exp2f(fmaf(c, ps.x, -cm));
-    }
-    const float shifted = -2.f * M - eps * kLn2 * log2f(S);
-    const float nrm = norm[i];
-    const float pnew = nrm + shifted;
-    if (with_err) {
-      const float pold = pot[i];
-      e = wgt[i] * fabsf(exp2f((pold - pnew) * (kLog2e / eps)) - 1.f);
-    }
-    if (write_pot) {
-      pot[i] = pnew;
-      bias_out[i] = 0.5f * (pnew - nrm) + hlw[i];
-    }
-  } else if (i < rpad && write_pot) {
-    bias_out[i] = kSentinel;
-  }
-  if (with_err) {
-    const float tot = block_sum_256(e, sh);
-    if (threadIdx.x == 0) err_part[blockIdx.x] = tot;
-  }
-}
-
-int lse_merge_blocks(int rows) { return (rows + 255) / 256; }
-
-// Deterministic single-workgroup sum of `count` partials (fixed order).
-__global__ __launch_bounds__(256) void err_reduce_kernel(const float* __restrict__ part, int count,
-                                                          float* __restrict__ out) {
-  __shared__ float sh[256];
-  float v = 0.f;
-  for (int k = threadIdx.x; k < count; k += 256) v += part[k];
-  const float tot = block_sum_256(v, sh);
-  if (threadIdx.x == 0) out[0] = tot;
-}
-
-__global__ __launch_bounds__(256) void nonfinite_kernel(const float* __restrict__ f, int n,
-                                                         const float* __restrict__ g, int m,
-                                                         float* __restrict__ out) {
-  __shared__ float sh[256];
-  // Exponent-bit test: independent of the no-NaN compile flags of this file.
-  auto bad = [](float x) { return ((__float_as_uint(x) >> 23) & 0xffu) == 0xffu ? 1.f : 0.f; };
-  float v = 0.f;
-  for (int k = threadIdx.x; k < n; k += 256) v += bad(f[k]);
-  for (int k = threadIdx.x; k < m; k += 256) v += bad(g[k]);
-  const float tot = block_sum_256(v, sh);
-  if (threadIdx.x == 0) out[0] = tot;
-}
-
-// ---------------------------------------------------------------------------
-// Small per-problem kernels.
-// ---------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(256) void sqnorms_kernel(const T* __restrict__ pts, int64_t rows,
-                                                       int64_t d, int64_t ld,
-                                                       float* __restrict__ out) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  float s = 0.f;
-  for (int64_t k = lane; k < d; k += 64) {
-    const float v = load_as_f32<T>(pts, row * ld + k);
-    s = fmaf(v, v, s);
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
-  if (lane == 0) out[row] = s;
-}
-
-// Packs a row-major point cloud into the MFMA operand layout of kernels.h.
-template <typename T>
-__global__ __launch_bounds__(256) void pack_points_kernel(const T* __restrict__ src, int64_t rows,
-                                                           int64_t d, int64_t ld, int64_t total,
-                                                           int kbp, u32x4* __restrict__ dst) {
-  constexpr int KW = 16 / sizeof(T);  // values per lane per k-block
-  for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total;
-       idx += (int64_t)gridDim.x * 256) {
-    const int lane = (int)(idx & 63);
-    const int64_t tk = idx >> 6;
-    const int kb = (int)(tk % kbp);
-    const int64_t t = tk / kbp;
-    const int64_t row = t * kTile + (lane & 31);
-    const int64_t k0 = (int64_t)kb * (2 * KW) + (lane >> 5) * KW;
-    T v[KW];
-#pragma unroll
-    for (int e = 0; e < KW; ++e)
-      v[e] = (row < rows && k0 + e < d) ? src[row * ld + k0 + e] : T(0);
-    dst[idx] = __builtin_bit_cast(u32x4, v);
-  }
-}
-
-// Packs V (rows streamed x cols) as the A operand of O^T += V^T P^T: for
-// column tile t, column block pb (32 values of p), quad q and lane l the four
-// floats are V[32t + 8q + 4(l/32) + e][32pb + l%32], e = 0..3 -- the row order
-// of the score accumulator registers 4q..4q+3.
-template <typename T>
-__global__ __launch_bounds__(256) void pack_values_kernel(const T* __restrict__ V, int64_t rows,
-                                                           int64_t cols, int64_t ldv,
-                                                           int64_t total, int pblocks,
-                                                           f32x4* __restrict__ dst) {
-  for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total;
-       idx += (int64_t)gridDim.x * 256) {
-    const int lane = (int)(idx & 63);
-    const int q = (int)((idx >> 6) & 3);
-    const int64_t tp = idx >> 8;
-    const int pb = (int)(tp % pblocks);
-    const int64_t t = tp / pblocks;
-    const int64_t col = (int64_t)pb * 32 + (lane & 31);
-    const int64_t r0 = t * kTile + 8 * q + 4 * (lane >> 5);
-    f32x4 v;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      v[e] = (col < cols && r0 + e < rows) ? load_as_f32<T>(V, (r0 + e) * ldv + col) : 0.f;
-    dst[idx] = v;
-  }
-}
-
-__global__ __launch_bounds__(256) void weights_kernel(const float* __restrict__ w, int rows,
-                                                       int rpad, float eps,
-                                                       float* __restrict__ wgt,
-                                                       float* __restrict__ hlw) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= rpad) return;
-  if (i < rows) {
-    const float wi = w ? w[i] : 1.0f / (float)rows;
-    wgt[i] = wi;
-    hlw[i] = 0.5f * eps * logf(wi);
-  } else {
-    wgt[i] = 0.f;
-    hlw[i] = 0.f;
-  }
-}
-
-__global__ __launch_bounds__(256) void fill_kernel(float* __restrict__ p, float v, int64_t count) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < count;
-       i += (int64_t)gridDim.x * 256)
-    p[i] = v;
-}
-
-__global__ __launch_bounds__(256) void bias_from_pot_kernel(const float* __restrict__ pot,
-                                                             const float* __restrict__ norm,
-                                                             const float* __restrict__ hlw,
-                                                             int rows, int rpad,
-                                                             float* __restrict__ bias) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= rpad) return;
-  bias[i] = (i < rows) ? 0.5f * (pot[i] - norm[i]) + hlw[i] : kSentinel;
-}
-
-// ---------------------------------------------------------------------------
 // Streamed transport application partials (Algorithm 2 / 4 of the page).
 // Per split s and row i: (M, S) as in the LSE pass, and
 //   O[p] = sum_j exp2(c (v_ij - M)) V[j][p]
@@ -512,139 +310,15 @@ __global__ __launch_bounds__(256) void apply_partial_kernel(
   }
 }
 
-// Merge of P V partials and epilogue. For row i of the coupling induced by
-// (pot, other potential):
-//   P_ij = w_i exp((pot_i - norm_i)/eps) exp((2/eps) v_ij)   (v = x.y + bias)
-//   factor_i = w_i exp((pot_i - norm_i + 2 M_i)/eps),  (P V)_i = factor_i O_i,
-//   r_i = factor_i S_i, barycentric = O_i / S_i, gradient = 2 (r_i x_i - (P Y)_i).
-// Workgroup: 32 rows x 32 columns, transposed through LDS for coalesced stores.
-template <typename T>
-__global__ __launch_bounds__(256) void apply_merge_kernel(
-    const float2* __restrict__ partMS, const float* __restrict__ partO, int splits, int rpad,
-    int ppad, int rows, int cols, float c, float eps, const float* __restrict__ pot,
-    const float* __restrict__ norm, const float* __restrict__ wgt, int mode,
-    const T* __restrict__ Xsrc, int64_t ldx, float* __restrict__ out, float* __restrict__ marg) {
-  __shared__ float scl[kMaxApplySplits][32];
-  __shared__ float fac[32], rr[32], ss[32];
-  __shared__ float tile[32][33];
-  const int t = threadIdx.x;
-  const int i0 = blockIdx.x * 32;
-  const int p0 = blockIdx.y * 32;
-  if (t < 32) {
-    const int i = i0 + t;
-    if (i < rows) {
-      float M = partMS[i].x;
-      for (int s = 1; s < splits; ++s) M = fmaxf(M, partMS[(size_t)s * rpad + i].x);
-      const float cm = c * M;
-      float S = 0.f;
-      for (int s = 0; s < splits; ++s) {
-        const float2 ps = partMS[(size_t)s * rpad + i];
-        const float e = exp2f(fmaf(c, ps.x, -cm));
-        scl[s][t] = e;
-        S += ps.y * e;
-      }
-      const float f = wgt[i] * exp2f((pot[i] - norm[i] + 2.f * M) * (kLog2e / eps));
-      fac[t] = f;
-      ss[t] = S;
-      rr[t] = f * S;
-    }
-  }
-  __syncthreads();
-  const int tx = t & 31;
-  const int ty = t >> 5;
-  const int i = i0 + tx;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int pl = ty + 8 * k;
-    const int p = p0 + pl;
-    float val = 0.f;
-    if (i < rows && p < cols) {
-      float O = 0.f;
-      for (int s = 0; s < splits; ++s) O += partO[((size_t)s * ppad + p) * rpad + i] * scl[s][tx];
-      if (mode == kApplyBary) {
-        val = O / ss[tx];
-      } else if (mode == kApplyGrad) {
-        const float xv = load_as_f32<T>(Xsrc, (int64_t)i * ldx + p);
-        val = 2.f * (rr[tx] * xv - fac[tx] * O);
-      } else {
-        val = fac[tx] * O;
-      }
-    }
-    tile[tx][pl] = val;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int rl = ty + 8 * k;
-    const int ii = i0 + rl;
-    const int p = p0 + tx;
-    if (ii < rows && p < cols) out[(size_t)ii * cols + p] = tile[rl][tx];
-  }
-  if (marg && blockIdx.y == 0 && t < 32 && i0 + t < rows) marg[i0 + t] = rr[t];
-}
-
 // ---------------------------------------------------------------------------
 // Launchers.
 // ---------------------------------------------------------------------------
-static int grid_for(int64_t total, int64_t per_block, int64_t cap = 1 << 20) {
-  int64_t g = (total + per_block - 1) / per_block;
-  if (g < 1) g = 1;
-  if (g > cap) g = cap;
-  return (int)g;
-}
 
-hipError_t launch_sqnorms(const void* pts, int bf16, int64_t rows, int64_t d, int64_t ld,
-                          float* out, hipStream_t st) {
-  const int grid = (int)((rows + 3) / 4);
-  if (bf16)
-    sqnorms_kernel<uint16_t><<<grid, 256, 0, st>>>((const uint16_t*)pts, rows, d, ld, out);
-  else
-    sqnorms_kernel<float><<<grid, 256, 0, st>>>((const float*)pts, rows, d, ld, out);
-  return hipGetLastError();
-}
 
-hipError_t launch_pack_points(const void* src, int bf16, int64_t rows, int64_t d, int64_t ld,
-                              int rtiles, int kbp, void* dst, hipStream_t st) {
-  const int64_t total = (int64_t)rtiles * kbp * 64;
-  const int grid = grid_for(total, 256, 65536);
-  if (bf16)
-    pack_points_kernel<uint16_t>
-        <<<grid, 256, 0, st>>>((const uint16_t*)src, rows, d, ld, total, kbp, (u32x4*)dst);
-  else
-    pack_points_kernel<float>
-        <<<grid, 256, 0, st>>>((const float*)src, rows, d, ld, total, kbp, (u32x4*)dst);
-  return hipGetLastError();
-}
 
-hipError_t launch_pack_values(const void* V, int bf16, int64_t rows, int64_t cols, int64_t ldv,
-                              int ctiles, int pblocks, float* dst, hipStream_t st) {
-  const int64_t total = (int64_t)ctiles * pblocks * 4 * 64;
-  const int grid = grid_for(total, 256, 65536);
-  if (bf16)
-    pack_values_kernel<uint16_t><<<grid, 256, 0, st>>>((const uint16_t*)V, rows, cols, ldv, total,
-                                                       pblocks, (f32x4*)dst);
-  else
-    pack_values_kernel<float>
-        <<<grid, 256, 0, st>>>((const float*)V, rows, cols, ldv, total, pblocks, (f32x4*)dst);
-  return hipGetLastError();
-}
 
-hipError_t launch_weights(const float* w, int rows, int rpad, float eps, float* wgt, float* hlw,
-                          hipStream_t st) {
-  weights_kernel<<<(rpad + 255) / 256, 256, 0, st>>>(w, rows, rpad, eps, wgt, hlw);
-  return hipGetLastError();
-}
 
-hipError_t launch_fill(float* p, float v, int64_t count, hipStream_t st) {
-  fill_kernel<<<grid_for(count, 256, 65536), 256, 0, st>>>(p, v, count);
-  return hipGetLastError();
-}
 
-hipError_t launch_bias_from_pot(const float* pot, const float* norm, const float* hlw, int rows,
-                                int rpad, float* bias, hipStream_t st) {
-  bias_from_pot_kernel<<<(rpad + 255) / 256, 256, 0, st>>>(pot, norm, hlw, rows, rpad, bias);
-  return hipGetLastError();
-}
 
 template <bool BF16, int KB, int RI, bool XRES>
 static void lse_go(const PassShape& s, const void* Rp, const void* Cp, const float* cbias,
@@ -690,26 +364,8 @@ hipError_t launch_lse_partial(const PassShape& s, int bf16, const void* Rp, cons
               : lse_dispatch<false>(s, Rp, Cp, cbias, c, part, st);
 }
 
-hipError_t launch_lse_merge(const float2* part, int splits, int rpad, int rows, float c, float eps,
-                            const float* norm, const float* hlw, const float* wgt, float* pot,
-                            float* bias_out, float* err_part, int with_err, int write_pot,
-                            hipStream_t st) {
-  lse_merge_kernel<<<(rpad + 255) / 256, 256, 0, st>>>(part, splits, rpad, rows, c, eps, norm,
-                                                       hlw, wgt, pot, bias_out, err_part,
-                                                       with_err, write_pot);
-  return hipGetLastError();
-}
 
-hipError_t launch_err_reduce(const float* part, int count, float* out, hipStream_t st) {
-  err_reduce_kernel<<<1, 256, 0, st>>>(part, count, out);
-  return hipGetLastError();
-}
 
-hipError_t launch_nonfinite(const float* f, int n, const float* g, int m, float* out,
-                            hipStream_t st) {
-  nonfinite_kernel<<<1, 256, 0, st>>>(f, n, g, m, out);
-  return hipGetLastError();
-}
 
 template <bool BF16, int KB, bool XRES, int PB>
 static void apply_go(const PassShape& s, int pblocks, const void* Rp, const void* Cp,
@@ -762,21 +418,5 @@ hipError_t launch_apply_partial(const PassShape& s, int bf16, int pblocks, int p
                                       partO, ppad, st);
 }
 
-hipError_t launch_apply_merge(const float2* partMS, const float* partO, int splits, int rpad,
-                              int ppad, int rows, int cols, float c, float eps, const float* pot,
-                              const float* norm, const float* wgt, int mode, const void* Xsrc,
-                              int xbf16, int64_t ldx, float* out, float* marg, hipStream_t st) {
-  if (splits > kMaxApplySplits) return hipErrorInvalidValue;
-  dim3 grid((rows + 31) / 32, (cols + 31) / 32);
-  if (xbf16)
-    apply_merge_kernel<uint16_t><<<grid, 256, 0, st>>>(partMS, partO, splits, rpad, ppad, rows,
-                                                       cols, c, eps, pot, norm, wgt, mode,
-                                                       (const uint16_t*)Xsrc, ldx, out, marg);
-  else
-    apply_merge_kernel<float><<<grid, 256, 0, st>>>(partMS, partO, splits, rpad, ppad, rows, cols,
-                                                    c, eps, pot, norm, wgt, mode,
-                                                    (const float*)Xsrc, ldx, out, marg);
-  return hipGetLastError();
-}
 
 }  // namespace flashot
