@@ -1,23 +1,31 @@
 """Throughput of the streamed Sinkhorn hot path on one MI355X.
 
-A step is one pass of the whole path over the n = m = 20000, d = 64 fp32
-workload (eps = 0.1): squared norms of both clouds, 100 alternating
-log-domain Sinkhorn iterations from zero potentials (graph-free plain
-launches with a HIP event pair around every log-sum-exp kernel), the exact
-marginal errors of the returned potentials, and one streamed P Y application
-that yields the X-gradient. Inputs are resident in HBM before timing starts.
+A step is one pass of the whole path over one workload (default: the
+n = m = 20000, d = 64 fp32 point clouds, eps = 0.1): squared norms of both
+clouds, T alternating log-domain Sinkhorn iterations from zero potentials
+(plain launches with a HIP event pair around every log-sum-exp kernel, on the
+stream the kernels run on), the exact marginal errors of the returned
+potentials, and the workload's transport applications (the P Y gradient for
+the default workload; P V and P^T U where the workload has value matrices).
+Inputs are resident in HBM before the timed region starts.
 
-Prints ONE JSON line. ``value`` = n * m * iterations / second of the whole
-step. ``roofline`` prices the dominant kernel (the streamed log-sum-exp pass)
-at 2 d flops per (i, j) pair against the fp32 MFMA peak; its duration is the
-average of the HIP-event timings taken inside the timed steps.
-``cpu_baseline`` times the fp64 oracle on a bounded sample of the same
-workload on the host.
+Prints ONE JSON line. ``value`` = n * m * T / second of the whole step.
+``roofline`` prices the dominant kernel (the streamed log-sum-exp pass) from
+its average HIP-event duration inside the timed steps: against the dense
+MFMA peak of the input type at 2 d flops per (i, j) pair, or -- when the
+exponentials and vector work dominate (small d in bf16) -- against the ALU
+bound of the online log-sum-exp in pairs per second. ``cpu_baseline`` times
+the fp64 oracle on a bounded sample of the same workload on the host.
+
+Other modes:
+  --copy-probe MIB   copy a MIB-MiB buffer a few times with torch and exit:
+                     the calibration run for the HBM byte counters.
 """
 
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -27,18 +35,52 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-FP32_MFMA_PEAK_TFLOPS = 157.3     # MI355X dense fp32 matrix peak
+# MI355X published dense peaks.
+MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}
 HBM_PEAK_GBS = 8000.0
+# ALU bound of the online log-sum-exp, derived from the unit counts. The
+# published fp32 vector peak (157.3 TFLOP/s = 256 CUs x 2.4 GHz x 128 FMA
+# lanes) gives 7.86e13 full-rate lane-ops/s, i.e. 32 lanes per clock per SIMD
+# for plain (unpacked) fp32 ops; an exponential is taken at a quarter of that
+# rate (1.97e13/s; 1.64e13/s measured with dependent chains). Per (i, j) pair
+# and half-step the online LSE needs one exponential (4 lane-op slots), one
+# FMA (scale and subtract the running max), one add (the sum) and half of a
+# three-input max: 6.5 slots.
+ALU_LANE_SLOTS_PER_S = 256 * 2.4e9 * 128
+ALU_SLOTS_PER_PAIR = 6.5
+ALU_PAIRS_PEAK = ALU_LANE_SLOTS_PER_S / ALU_SLOTS_PER_PAIR
+
+# HBM bytes of one launch of the dominant kernel, from rocprofv3 --pmc
+# FETCH_SIZE / WRITE_SIZE runs (scaled by the copy-kernel calibration), valid
+# only for the kernel source they were taken on.
+TRAFFIC = {}
+KERNEL_SRC = os.path.join(ROOT, "streaming_sinkhorn_amd", "csrc", "kernels.hip")
+
+METRIC = "Sinkhorn n*m*iters/sec + % MFMA/exp roofline at n=m=20k, d=64, eps=0.1"
 
 
-def cpu_baseline(data, rows: int):
+def kernel_sha():
+    with open(KERNEL_SRC, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()
+
+
+def traffic_for(workload):
+    rec = TRAFFIC.get(workload)
+    if not rec or rec["kernels_sha256"] != kernel_sha():
+        return None
+    return rec["bytes_per_launch"]
+
+
+def cpu_baseline(data, budget=1.05e10):
     """fp64 oracle on a row sample: one f half-step for `rows` rows of X and one
-    g half-step for `rows` columns of Y, reported in n*m*iterations/s."""
+    g half-step for `rows` columns of Y, reported in n*m*iterations/s.
+    `budget` bounds pairs x d (about 10 s of single-threaded numpy)."""
     import numpy as np
 
     import oracle
 
     w = data["w"]
+    rows = int(max(8, min(w.n, w.m, budget / (w.d * (w.n + w.m)))))
     X = data["X"].astype(np.float64)
     Y = data["Y"].astype(np.float64)
     a = data["a"].astype(np.float64)
@@ -55,10 +97,22 @@ def cpu_baseline(data, rows: int):
         "unit": "n*m*iters/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"fp64 numpy oracle: f half-step on {rows} rows x {w.m} columns and g half-step on "
-                  f"{rows} columns x {w.n} rows of the same workload ({pairs} pairs, {dt:.1f} s); "
-                  f"1 pair-update per half-step = 0.5 n*m*iter",
+        "sample": f"fp64 numpy oracle (single-threaded; host has {os.cpu_count()} CPUs): f half-step "
+                  f"on {rows} rows x {w.m} columns and g half-step on {rows} columns x {w.n} rows of "
+                  f"the same workload ({pairs} pairs, {dt:.1f} s); one iteration = two half-steps",
     }
+
+
+def copy_probe(mib):
+    import torch
+
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n * 4, "copies": 3}), flush=True)
 
 
 def main():
@@ -69,65 +123,76 @@ def main():
     ap.add_argument("--workload", default="c2")
     ap.add_argument("--iters", type=int, default=None)
     ap.add_argument("--splits", type=int, default=0)
-    ap.add_argument("--cpu-rows", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              f"(the path runs on a single MI355X; multi-GPU sharding is not built).", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the path runs "
+              f"on a single MI355X and multi-GPU sharding is not built.", file=sys.stderr)
         sys.exit(2)
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
 
-    import numpy as np
     import torch
 
     import streaming_sinkhorn_amd as ssa
     import workloads
 
+    ssa.lib()  # fail loudly before any work if the HIP library is missing
     data = workloads.make(args.workload)
     w = data["w"]
     T = args.iters or w.iters
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    X = torch.from_numpy(data["X"]).to(dev)
-    Y = torch.from_numpy(data["Y"]).to(dev)
-    if w.dtype == "bf16":
-        X, Y = X.to(torch.bfloat16), Y.to(torch.bfloat16)
+
+    def to_dev(arr):
+        t = torch.from_numpy(arr).to(dev)
+        return t.to(torch.bfloat16) if w.dtype == "bf16" else t
+
+    X, Y = to_dev(data["X"]), to_dev(data["Y"])
     a = torch.from_numpy(data["a"]).to(dev)
     b = torch.from_numpy(data["b"]).to(dev)
+    V = to_dev(data["V"]) if w.v_cols else None
+    U = to_dev(data["U"]) if w.u_cols else None
     xs = torch.empty(w.n, device=dev)
     ys = torch.empty(w.m, device=dev)
     prob = ssa.problem(X, Y, w.eps, a, b, x_sqn=xs, y_sqn=ys)
     f = torch.zeros(w.n, device=dev)
     g = torch.zeros(w.m, device=dev)
     r = torch.empty(w.n, device=dev)
-    grad = torch.empty((w.n, w.d), device=dev)
+    c = torch.empty(w.m, device=dev)
+    out_grad = torch.empty((w.n, w.d), device=dev) if w.grad else None
+    out_pv = torch.empty((w.n, w.v_cols), device=dev) if w.v_cols else None
+    out_ptu = torch.empty((w.m, w.u_cols), device=dev) if w.u_cols else None
     stream = torch.cuda.Stream()
-
-    # Workspaces sized once, outside the timed region.
-    ws_solve = [None]
-    ws_apply = [None]
     infos = []
+    ws = {}
 
     def step(record):
         ssa.ot_sqnorms(X, xs)
         ssa.ot_sqnorms(Y, ys)
         info = ssa.ot_solve(prob, f, g, T, splits_f=args.splits, splits_g=args.splits,
-                            timing=True, ws=ws_solve[0])
-        ssa.ot_apply_plan(prob, f, g, flags=ssa.OT_GRAD, out=grad, marg=r, ws=ws_apply[0])
+                            timing=True, ws=ws.get("solve"))
+        if w.grad:
+            ssa.ot_apply_plan(prob, f, g, flags=ssa.OT_GRAD, out=out_grad, marg=r, ws=ws.get("grad"))
+        if w.v_cols:
+            ssa.ot_apply_plan(prob, f, g, V, out=out_pv, marg=r, ws=ws.get("pv"))
+        if w.u_cols:
+            ssa.ot_apply_plan(prob, f, g, U, flags=ssa.OT_TRANSPOSE, out=out_ptu, marg=c,
+                              ws=ws.get("ptu"))
         if record:
             infos.append(info)
 
     with torch.cuda.stream(stream):
-        # allocate workspaces via one untimed call each
-        import ctypes
-        sz = ctypes.c_size_t(0)
-        opts = ssa.OtSolveOpts(T, 0.0, 1, 0, 0, args.splits, args.splits, 0)
-        ssa._check(ssa.lib().ot_solve(ctypes.byref(prob.c), None, None, ctypes.byref(opts), None, None,
-                                      ctypes.byref(sz), None), "size")
-        ws_solve[0] = torch.empty(sz.value, dtype=torch.uint8, device=dev)
-        ssa._check(ssa.lib().ot_apply_plan(ctypes.byref(prob.c), None, None, None, 0, w.d, w.d,
-                                           ssa.OT_GRAD, None, None, None, ctypes.byref(sz), None), "size")
-        ws_apply[0] = torch.empty(sz.value, dtype=torch.uint8, device=dev)
+        # Workspaces sized and allocated once, outside the timed region.
+        ws["solve"] = ssa.solve_workspace(prob, T, splits_f=args.splits, splits_g=args.splits)
+        if w.grad:
+            ws["grad"] = ssa.apply_workspace(prob, flags=ssa.OT_GRAD)
+        if w.v_cols:
+            ws["pv"] = ssa.apply_workspace(prob, V)
+        if w.u_cols:
+            ws["ptu"] = ssa.apply_workspace(prob, U, flags=ssa.OT_TRANSPOSE)
         for _ in range(args.warmup):
             step(False)
         torch.cuda.synchronize()
@@ -143,11 +208,33 @@ def main():
     lse_ms = sum(i["lse_ms"] for i in infos)
     lse_n = sum(i["lse_launches"] for i in infos)
     avg_lse_s = lse_ms / lse_n / 1e3
-    flops_per_launch = 2.0 * w.n * w.m * w.d
-    achieved = flops_per_launch / avg_lse_s / 1e12
+    pairs = float(w.n) * w.m
+    flops = 2.0 * pairs * w.d
+    t_mfma = flops / (MFMA_PEAK_TFLOPS[w.dtype] * 1e12)
+    t_alu = pairs / ALU_PAIRS_PEAK
+    if t_mfma >= t_alu:
+        achieved = flops / avg_lse_s / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_PEAK_TFLOPS[w.dtype],
+                "unit": "TFLOP/s", "frac": achieved / MFMA_PEAK_TFLOPS[w.dtype]}
+        per_launch = {"algorithmic_flops_per_launch": flops}
+    else:
+        achieved = pairs / avg_lse_s / 1e9
+        roof = {"bound": "alu", "achieved": achieved, "peak": ALU_PAIRS_PEAK / 1e9,
+                "unit": "Gpair/s", "frac": achieved / (ALU_PAIRS_PEAK / 1e9)}
+        per_launch = {"algorithmic_pairs_per_launch": pairs}
+    roof["traffic"] = traffic_for(args.workload)
+    roof.update({"kernel": "lse_partial_kernel", "avg_launch_us": avg_lse_s * 1e6,
+                 "launches": lse_n, **per_launch})
     last = infos[-1]
+    outputs = ["f", "g", "marginal errors"]
+    if w.grad:
+        outputs.append("P*Y gradient")
+    if w.v_cols:
+        outputs.append(f"P*V (V m x {w.v_cols})")
+    if w.u_cols:
+        outputs.append(f"P^T*U (U n x {w.u_cols})")
     out = {
-        "metric": "Sinkhorn n*m*iters/sec + % MFMA/exp roofline at n=m=20k, d=64, eps=0.1",
+        "metric": METRIC,
         "value": value,
         "unit": "n*m*iters/s",
         "n_gpus": 1,
@@ -157,31 +244,20 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32" if w.dtype == "f32" else "bf16",
+        "dtype": w.dtype,
         "data": "synthetic",
         "config": {
-            "workload": f"{w.name}: n={w.n}, m={w.m}, d={w.d}, {w.dtype}, eps={w.eps}, {T} alternating "
-                        f"iterations from zero potentials + exact marginal errors + P*Y gradient",
+            "workload": f"{w.name}: n={w.n}, m={w.m}, d={w.d}, {w.dtype} points, eps={w.eps}, {T} "
+                        f"alternating iterations from zero potentials; outputs: {', '.join(outputs)}",
             "n": w.n, "m": w.m, "d": w.d, "eps": w.eps, "iters": T,
             "splits_f": last["splits_f"], "splits_g": last["splits_g"],
         },
-        "roofline": {
-            "bound": "mfma",
-            "achieved": achieved,
-            "peak": FP32_MFMA_PEAK_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": achieved / FP32_MFMA_PEAK_TFLOPS,
-            "traffic": None,
-            "kernel": "lse_partial_kernel",
-            "avg_launch_us": avg_lse_s * 1e6,
-            "launches": lse_n,
-            "algorithmic_flops_per_launch": flops_per_launch,
-        },
+        "roofline": roof,
         "marg_err_row": last["marg_err_row"],
         "marg_err_col": last["marg_err_col"],
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(data, args.cpu_rows)
+        out["cpu_baseline"] = cpu_baseline(data)
     print(json.dumps(out), flush=True)
 
 

@@ -259,5 +259,29 @@ def ot_apply_plan(prob: Problem, f, g, V=None, flags: int = 0, out=None, marg=No
     return out
 
 
+def solve_workspace(prob: Problem, iters: int, splits_f: int = 0, splits_g: int = 0) -> torch.Tensor:
+    """Allocate the workspace ot_solve needs for this problem (size query + torch allocation)."""
+    L = lib()
+    opts = OtSolveOpts(int(iters), 0.0, 1, OT_INIT_ZERO, 1, int(splits_f), int(splits_g), 0)
+    size = ctypes.c_size_t(0)
+    _check(L.ot_solve(ctypes.byref(prob.c), None, None, ctypes.byref(opts), None, None,
+                      ctypes.byref(size), None), "ot_solve workspace query")
+    return torch.empty(max(size.value, 256), dtype=torch.uint8, device=prob.device)
+
+
+def apply_workspace(prob: Problem, V=None, flags: int = 0) -> torch.Tensor:
+    """Allocate the workspace ot_apply_plan needs for this problem and value matrix."""
+    L = lib()
+    if flags & OT_GRAD:
+        vdt, cols, ldv = 0, prob.d, prob.d
+    else:
+        _, cols, ldv = _rows(V, "V")
+        vdt = _dtype_code(V)
+    size = ctypes.c_size_t(0)
+    _check(L.ot_apply_plan(ctypes.byref(prob.c), None, None, None, vdt, cols, ldv, int(flags),
+                           None, None, None, ctypes.byref(size), None), "ot_apply_plan workspace query")
+    return torch.empty(max(size.value, 256), dtype=torch.uint8, device=prob.device)
+
+
 def version() -> str:
     return lib().ot_version().decode()
