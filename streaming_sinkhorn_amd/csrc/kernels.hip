@@ -34,6 +34,7 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "kernels.h"
 
@@ -85,9 +86,12 @@ __device__ __forceinline__ void lse_tile(const f32x16& v, float& M, float& S, fl
   const float Mn = fmaxf(M, max16(v));
   const float cm = c * Mn;
   const float sc = __builtin_amdgcn_exp2f(fmaf(c, M, -cm));
-  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+  float s0 = __builtin_amdgcn_exp2f(fmaf(c, v[0], -cm));
+  float s1 = __builtin_amdgcn_exp2f(fmaf(c, v[1], -cm));
+  float s2 = __builtin_amdgcn_exp2f(fmaf(c, v[2], -cm));
+  float s3 = __builtin_amdgcn_exp2f(fmaf(c, v[3], -cm));
 #pragma unroll
-  for (int r = 0; r < 16; r += 4) {
+  for (int r = 4; r < 16; r += 4) {
     s0 += __builtin_amdgcn_exp2f(fmaf(c, v[r + 0], -cm));
     s1 += __builtin_amdgcn_exp2f(fmaf(c, v[r + 1], -cm));
     s2 += __builtin_amdgcn_exp2f(fmaf(c, v[r + 2], -cm));
@@ -194,6 +198,129 @@ __global__ __launch_bounds__(256) void lse_partial_kernel(
   }
 
   // Merge the two half-waves that share a row (App. D.3 merge of partial statistics).
+#pragma unroll
+  for (int ri = 0; ri < RI; ++ri) {
+    const float Mp = __shfl_xor(M[ri], 32);
+    const float Sp = __shfl_xor(S[ri], 32);
+    const float Mt = fmaxf(M[ri], Mp);
+    const float cm = c * Mt;
+    const float St = S[ri] * __builtin_amdgcn_exp2f(fmaf(c, M[ri], -cm)) +
+                     Sp * __builtin_amdgcn_exp2f(fmaf(c, Mp, -cm));
+    if (h == 0 && rt0 + ri < rtiles)
+      part[(size_t)s * rpad + (size_t)(rt0 + ri) * kTile + (lane & 31)] = make_float2(Mt, St);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Software-pipelined variant of the register-resident pass. Each wave keeps
+// two score tiles in flight: while the matrix cores form the scores of column
+// tile t+1, the vector unit runs the online LSE of tile t, so one wave keeps
+// both units busy. The column operand alternates between two register
+// buffers (the loop body is written twice with the roles swapped), so a
+// prefetched tile is never copied between registers.
+// ---------------------------------------------------------------------------
+template <bool BF16, int KB, int RI>
+__device__ __forceinline__ void score_tile(const u32x4 (&y)[KB], const u32x4 (&xr)[RI][KB],
+                                           float wv, int h, f32x16 (&acc)[RI]) {
+#pragma unroll
+  for (int ri = 0; ri < RI; ++ri) acc[ri] = f32x16{};
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int ri = 0; ri < RI; ++ri) acc[ri] = mfma_kblock<BF16>(y[kb], xr[ri][kb], acc[ri]);
+#pragma unroll
+  for (int ri = 0; ri < RI; ++ri) acc[ri] = mfma_bias(wv, h, acc[ri]);
+}
+
+template <int KB>
+__device__ __forceinline__ void load_ctile(const u32x4* __restrict__ Cp,
+                                           const float* __restrict__ cbias, int jt, int lane,
+                                           u32x4 (&y)[KB], float& w) {
+  w = cbias[jt * kTile + (lane & 31)];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) y[kb] = Cp[((size_t)jt * KB + kb) * 64 + lane];
+}
+
+// Orders one pipeline stage (one scheduling region): one matrix instruction
+// alternating with a few vector instructions, then the loads that refill the
+// column buffer the matrix instructions have just read.
+template <bool BF16, int KB, int RI>
+__device__ __forceinline__ void stage_schedule() {
+  constexpr int kMfma = RI * (KB * (BF16 ? 1 : 4) + 1);
+  constexpr int kValu = RI * 62;  // online LSE of RI score tiles
+  constexpr int kValuPer = (kValu + kMfma - 1) / kMfma;
+#pragma unroll
+  for (int i = 0; i < kMfma; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, kValuPer, 0);  // VALU
+  }
+  __builtin_amdgcn_sched_group_barrier(0x020, KB + 1, 0);      // VMEM reads
+}
+
+template <bool BF16, int KB, int RI>
+__global__ __launch_bounds__(256) void lse_pipe_kernel(
+    const u32x4* __restrict__ Rp, const u32x4* __restrict__ Cp, const float* __restrict__ cbias,
+    int rtiles, int ctiles, int splits, int tps, float c, float2* __restrict__ part, int rpad) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int h = lane >> 5;
+  const int s = blockIdx.x % splits;
+  const int rg = blockIdx.x / splits;
+  const int rt0 = (rg * kWaves + wave) * RI;
+  if (rt0 >= rtiles) return;
+  const int jt0 = s * tps;
+  const int last = min(jt0 + tps, ctiles) - 1 - jt0;  // split holds tiles 0..last, last >= 0
+
+  u32x4 xr[RI][KB];
+#pragma unroll
+  for (int ri = 0; ri < RI; ++ri) {
+    const int rt = min(rt0 + ri, rtiles - 1);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) xr[ri][kb] = Rp[((size_t)rt * KB + kb) * 64 + lane];
+  }
+  float M[RI], S[RI];
+#pragma unroll
+  for (int ri = 0; ri < RI; ++ri) {
+    M[ri] = -1.0e30f;
+    S[ri] = 0.f;
+  }
+
+  // Invariant at the top of the loop: accA holds the scores of tile k, yB
+  // holds (or is loading) tile k+1 and yA tile k+2; indices past the split's
+  // last tile are clamped to it (loaded, never reduced).
+  u32x4 yA[KB], yB[KB];
+  float wA, wB;
+  f32x16 accA[RI], accB[RI];
+  load_ctile<KB>(Cp, cbias, jt0, lane, yA, wA);
+  load_ctile<KB>(Cp, cbias, jt0 + min(1, last), lane, yB, wB);
+  score_tile<BF16, KB, RI>(yA, xr, wA, h, accA);
+  load_ctile<KB>(Cp, cbias, jt0 + min(2, last), lane, yA, wA);
+  int k = 0;
+  for (; k + 2 <= last; k += 2) {
+    score_tile<BF16, KB, RI>(yB, xr, wB, h, accB);
+#pragma unroll
+    for (int ri = 0; ri < RI; ++ri) lse_tile(accA[ri], M[ri], S[ri], c);
+    load_ctile<KB>(Cp, cbias, jt0 + min(k + 3, last), lane, yB, wB);
+    stage_schedule<BF16, KB, RI>();
+    __builtin_amdgcn_sched_barrier(0);
+    score_tile<BF16, KB, RI>(yA, xr, wA, h, accA);
+#pragma unroll
+    for (int ri = 0; ri < RI; ++ri) lse_tile(accB[ri], M[ri], S[ri], c);
+    load_ctile<KB>(Cp, cbias, jt0 + min(k + 4, last), lane, yA, wA);
+    stage_schedule<BF16, KB, RI>();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (k + 1 <= last) {  // tiles k and k+1 remain
+    score_tile<BF16, KB, RI>(yB, xr, wB, h, accB);
+#pragma unroll
+    for (int ri = 0; ri < RI; ++ri) lse_tile(accA[ri], M[ri], S[ri], c);
+#pragma unroll
+    for (int ri = 0; ri < RI; ++ri) lse_tile(accB[ri], M[ri], S[ri], c);
+  } else {  // tile k remains
+#pragma unroll
+    for (int ri = 0; ri < RI; ++ri) lse_tile(accA[ri], M[ri], S[ri], c);
+  }
+
 #pragma unroll
   for (int ri = 0; ri < RI; ++ri) {
     const float Mp = __shfl_xor(M[ri], 32);
@@ -328,9 +455,45 @@ static void lse_go(const PassShape& s, const void* Rp, const void* Cp, const flo
       part, s.rtiles * kTile);
 }
 
+template <bool BF16, int KB, int RI>
+static void lse_pipe_go(const PassShape& s, const void* Rp, const void* Cp, const float* cbias,
+                        float c, float2* part, hipStream_t st) {
+  lse_pipe_kernel<BF16, KB, RI><<<s.nrowgroups * s.splits, 256, 0, st>>>(
+      (const u32x4*)Rp, (const u32x4*)Cp, cbias, s.rtiles, s.ctiles, s.splits, s.tps, c, part,
+      s.rtiles * kTile);
+}
+
+static int lse_variant() {
+  static int v = [] {
+    const char* e = getenv("FLASHOT_LSE_V");
+    return (e && *e) ? atoi(e) : 2;
+  }();
+  return v;
+}
+
 template <bool BF16>
 static hipError_t lse_dispatch(const PassShape& s, const void* Rp, const void* Cp,
                                const float* cbias, float c, float2* part, hipStream_t st) {
+  if (s.xres && lse_variant() == 2) {
+#define FLASHOT_PIPE_CASE(KBV)                                      \
+  case KBV:                                                         \
+    if (s.ri == 2)                                                  \
+      lse_pipe_go<BF16, KBV, 2>(s, Rp, Cp, cbias, c, part, st);     \
+    else                                                            \
+      lse_pipe_go<BF16, KBV, 1>(s, Rp, Cp, cbias, c, part, st);     \
+    break;
+    switch (s.kb) {
+      FLASHOT_PIPE_CASE(1)
+      FLASHOT_PIPE_CASE(2)
+      FLASHOT_PIPE_CASE(4)
+      FLASHOT_PIPE_CASE(8)
+      FLASHOT_PIPE_CASE(16)
+      default:
+        return hipErrorInvalidValue;
+    }
+#undef FLASHOT_PIPE_CASE
+    return hipGetLastError();
+  }
   if (!s.xres) {
     if (s.ri == 2)
       lse_go<BF16, 8, 2, false>(s, Rp, Cp, cbias, c, part, st);
