@@ -53,7 +53,11 @@ ALU_PAIRS_PEAK = ALU_LANE_SLOTS_PER_S / ALU_SLOTS_PER_PAIR
 # HBM bytes of one launch of the dominant kernel, from rocprofv3 --pmc
 # FETCH_SIZE / WRITE_SIZE runs (scaled by the copy-kernel calibration), valid
 # only for the kernel source they were taken on.
-TRAFFIC = {}
+TRAFFIC = {
+    "c2": {"kernels_sha256": "200de97431eb9d8ec6b8054aaa87f50cae1c0b025cbfc185a79210a01628c819",
+           "bytes_per_launch": 51408528,
+           "source": "profiles/lse_pipe_c2_n20000_d64_f32_hbm_traffic.md"},
+}
 KERNEL_SRC = os.path.join(ROOT, "streaming_sinkhorn_amd", "csrc", "kernels.hip")
 
 METRIC = "Sinkhorn n*m*iters/sec + % MFMA/exp roofline at n=m=20k, d=64, eps=0.1"
