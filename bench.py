@@ -129,6 +129,9 @@ def main():
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB")
+    ap.add_argument("--native-f32", action="store_true",
+                    help="form fp32 scores with the fp32 matrix instruction instead of the "
+                         "three-part bf16 split")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the path runs "
@@ -161,7 +164,7 @@ def main():
     U = to_dev(data["U"]) if w.u_cols else None
     xs = torch.empty(w.n, device=dev)
     ys = torch.empty(w.m, device=dev)
-    prob = ssa.problem(X, Y, w.eps, a, b, x_sqn=xs, y_sqn=ys)
+    prob = ssa.problem(X, Y, w.eps, a, b, x_sqn=xs, y_sqn=ys, native_f32=args.native_f32)
     f = torch.zeros(w.n, device=dev)
     g = torch.zeros(w.m, device=dev)
     r = torch.empty(w.n, device=dev)
@@ -213,19 +216,27 @@ def main():
     lse_n = sum(i["lse_launches"] for i in infos)
     avg_lse_s = lse_ms / lse_n / 1e3
     pairs = float(w.n) * w.m
-    flops = 2.0 * pairs * w.d
-    t_mfma = flops / (MFMA_PEAK_TFLOPS[w.dtype] * 1e12)
+    mode = infos[-1]["operand_mode"]
+    alg_flops = 2.0 * pairs * w.d
+    if mode == 2:
+        # fp32 scores formed from three bf16 parts per coordinate: six bf16
+        # products per fp32 product on the bf16 matrix cores.
+        mat_flops, mat_peak, mat_dtype = 6.0 * alg_flops, MFMA_PEAK_TFLOPS["bf16"], "bf16 (fp32 split)"
+    else:
+        mat_flops, mat_peak, mat_dtype = alg_flops, MFMA_PEAK_TFLOPS[w.dtype], w.dtype
+    t_mfma = mat_flops / (mat_peak * 1e12)
     t_alu = pairs / ALU_PAIRS_PEAK
     if t_mfma >= t_alu:
-        achieved = flops / avg_lse_s / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_PEAK_TFLOPS[w.dtype],
-                "unit": "TFLOP/s", "frac": achieved / MFMA_PEAK_TFLOPS[w.dtype]}
-        per_launch = {"algorithmic_flops_per_launch": flops}
+        achieved = mat_flops / avg_lse_s / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": mat_peak,
+                "unit": "TFLOP/s", "frac": achieved / mat_peak}
+        per_launch = {"matrix_dtype": mat_dtype, "matrix_flops_per_launch": mat_flops}
     else:
         achieved = pairs / avg_lse_s / 1e9
         roof = {"bound": "alu", "achieved": achieved, "peak": ALU_PAIRS_PEAK / 1e9,
                 "unit": "Gpair/s", "frac": achieved / (ALU_PAIRS_PEAK / 1e9)}
         per_launch = {"algorithmic_pairs_per_launch": pairs}
+    per_launch["fp32_equivalent_tflops"] = alg_flops / avg_lse_s / 1e12
     roof["traffic"] = traffic_for(args.workload)
     roof.update({"kernel": "lse_partial_kernel", "avg_launch_us": avg_lse_s * 1e6,
                  "launches": lse_n, **per_launch})
@@ -255,6 +266,8 @@ def main():
                         f"alternating iterations from zero potentials; outputs: {', '.join(outputs)}",
             "n": w.n, "m": w.m, "d": w.d, "eps": w.eps, "iters": T,
             "splits_f": last["splits_f"], "splits_g": last["splits_g"],
+            "operand_mode": ["fp32 MFMA", "bf16 MFMA", "fp32 as 3-part bf16 split on bf16 MFMA"][
+                last["operand_mode"]],
         },
         "roofline": roof,
         "marg_err_row": last["marg_err_row"],

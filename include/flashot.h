@@ -74,6 +74,10 @@ extern "C" {
 #define OT_MAX_D    8192
 #define OT_MAX_COLS 8192
 
+/* ot_problem flags. */
+#define OT_NATIVE_F32 1  /* fp32 points: form scores with fp32 MFMA instead of the default
+                            exact-to-fp32 split into three bf16 parts on the bf16 MFMA */
+
 /*
  * The problem: two point clouds, their weights and eps (App. H.2 problem
  * statement: discrete measures, squared-Euclidean cost, entropic
@@ -87,6 +91,14 @@ extern "C" {
  *   a, b        device fp32 weights (n, m) or NULL for uniform
  *   x_sqn,y_sqn device fp32 squared norms ||x_i||^2, ||y_j||^2, or NULL to
  *               have them computed into the workspace
+ *   flags       0, or OT_NATIVE_F32. For fp32 points with d <= 64 the
+ *               log-sum-exp passes by default split every coordinate into
+ *               three bf16 parts (hi + mid + lo, 24 significant bits) and form
+ *               each score from the six largest partial products on the bf16
+ *               matrix cores; the dropped terms are below 2^-26 of each
+ *               product, finer than fp32 rounding. OT_NATIVE_F32 uses the
+ *               fp32 matrix instruction instead. Transport application always
+ *               uses fp32 products for fp32 points.
  */
 typedef struct ot_problem {
   const void* x;
@@ -98,6 +110,7 @@ typedef struct ot_problem {
   const float* b;
   const float* x_sqn;
   const float* y_sqn;
+  int32_t flags;  /* 0 or OT_NATIVE_F32 */
 } ot_problem;
 
 /* ot_solve options. Zero-initialise and set what you need. */
@@ -122,6 +135,8 @@ typedef struct ot_solve_info {
   int32_t lse_launches;  /* with opts.timing: number of log-sum-exp kernel launches timed */
   int32_t splits_f;      /* column splits used by the f half-step */
   int32_t splits_g;      /* column splits used by the g half-step */
+  int32_t operand_mode;  /* scores formed from: 0 fp32 MFMA, 1 bf16 MFMA, 2 fp32 split into
+                            three bf16 parts on the bf16 MFMA (six products per pair) */
 } ot_solve_info;
 
 /*

@@ -31,6 +31,7 @@ OT_OK, OT_ERR_INVALID_ARG, OT_ERR_UNSUPPORTED, OT_ERR_WORKSPACE, OT_ERR_HIP, OT_
 OT_F32, OT_BF16 = 0, 1
 OT_INIT_ZERO, OT_INIT_GIVEN = 0, 1
 OT_TRANSPOSE, OT_GRAD, OT_BARY = 1, 2, 4
+OT_NATIVE_F32 = 1
 
 
 class OtError(RuntimeError):
@@ -47,6 +48,7 @@ class OtProblem(ctypes.Structure):
         ("dtype", ctypes.c_int32), ("eps", ctypes.c_float),
         ("a", ctypes.c_void_p), ("b", ctypes.c_void_p),
         ("x_sqn", ctypes.c_void_p), ("y_sqn", ctypes.c_void_p),
+        ("flags", ctypes.c_int32),
     ]
 
 
@@ -64,6 +66,7 @@ class OtSolveInfo(ctypes.Structure):
         ("marg_err_row", ctypes.c_float), ("marg_err_col", ctypes.c_float),
         ("lse_ms", ctypes.c_float), ("lse_launches", ctypes.c_int32),
         ("splits_f", ctypes.c_int32), ("splits_g", ctypes.c_int32),
+        ("operand_mode", ctypes.c_int32),
     ]
 
     def as_dict(self):
@@ -153,6 +156,7 @@ class Problem:
     b: torch.Tensor | None = None
     x_sqn: torch.Tensor | None = None
     y_sqn: torch.Tensor | None = None
+    native_f32: bool = False
 
     def __post_init__(self):
         n, d, ldx = _rows(self.X, "X")
@@ -167,11 +171,13 @@ class Problem:
         self.c = OtProblem(
             _ptr(self.X), _ptr(self.Y), n, m, d, ldx, ldy, _dtype_code(self.X), float(self.eps),
             _ptr(_vec(self.a, "a", n, dev)), _ptr(_vec(self.b, "b", m, dev)),
-            _ptr(_vec(self.x_sqn, "x_sqn", n, dev)), _ptr(_vec(self.y_sqn, "y_sqn", m, dev)))
+            _ptr(_vec(self.x_sqn, "x_sqn", n, dev)), _ptr(_vec(self.y_sqn, "y_sqn", m, dev)),
+            OT_NATIVE_F32 if self.native_f32 else 0)
 
 
-def problem(X, Y, eps, a=None, b=None, x_sqn=None, y_sqn=None) -> Problem:
-    return Problem(X, Y, eps, a, b, x_sqn, y_sqn)
+def problem(X, Y, eps, a=None, b=None, x_sqn=None, y_sqn=None, native_f32=False) -> Problem:
+    """native_f32: form fp32 scores with fp32 MFMA instead of the three-part bf16 split."""
+    return Problem(X, Y, eps, a, b, x_sqn, y_sqn, native_f32)
 
 
 def _workspace(query, ws, device):

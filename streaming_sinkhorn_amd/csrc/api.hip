@@ -49,29 +49,45 @@ int env_int(const char* name, int dflt) {
 
 // Kernel configuration for a point dimension / storage type.
 struct KConf {
-  int kbw;      // dimension values per k-block (8 fp32, 16 bf16)
+  int mode;     // 0 fp32 operands, 1 bf16, 2 fp32 split into three bf16 parts
+  int kbw;      // dimension values per k-block (8 fp32, 16 bf16 / split)
   int kblocks;  // k-blocks needed to cover d
-  int kb;       // k-blocks in registers at a time
-  int kbp;      // padded k-blocks per tile
+  int kb;       // 1 KiB operand units per tile held in registers (3 per k-block in split mode)
+  int kbp;      // padded operand units per tile
   bool xres;    // row operand resident in registers
   int ri;       // row tiles per wave in the LSE pass
 };
 
-KConf kernel_conf(int64_t d, int bf16) {
+// Split mode (fp32 inputs on the bf16 matrix cores) is used by the
+// log-sum-exp passes for d <= 64 unless the problem asks for native fp32.
+KConf kernel_conf(int64_t d, int bf16, bool allow_split) {
   KConf k{};
-  k.kbw = bf16 ? 16 : 8;
-  k.kblocks = ceil_div(d, k.kbw);
-  if (k.kblocks <= 16) {
-    k.kb = 1;
-    while (k.kb < k.kblocks) k.kb *= 2;
+  if (!bf16 && allow_split && d <= 64) {
+    k.mode = 2;
+    k.kbw = 16;
+    k.kblocks = ceil_div(d, 16);
+    int kl = 1;
+    while (kl < k.kblocks) kl *= 2;
+    k.kb = 3 * kl;
     k.kbp = k.kb;
     k.xres = true;
-    k.ri = (k.kb <= 8) ? 2 : 1;
+    k.ri = kl <= 2 ? 2 : 1;
   } else {
-    k.kb = 8;
-    k.kbp = (k.kblocks + 7) / 8 * 8;
-    k.xres = false;
-    k.ri = 2;
+    k.mode = bf16 ? 1 : 0;
+    k.kbw = bf16 ? 16 : 8;
+    k.kblocks = ceil_div(d, k.kbw);
+    if (k.kblocks <= 16) {
+      k.kb = 1;
+      while (k.kb < k.kblocks) k.kb *= 2;
+      k.kbp = k.kb;
+      k.xres = true;
+      k.ri = (k.kb <= 8) ? 2 : 1;
+    } else {
+      k.kb = 8;
+      k.kbp = (k.kblocks + 7) / 8 * 8;
+      k.xres = false;
+      k.ri = 2;
+    }
   }
   const int ri_env = env_int("FLASHOT_RI", 0);
   if (ri_env == 1 || ri_env == 2) k.ri = ri_env;
@@ -118,6 +134,7 @@ int check_problem(const ot_problem* p) {
   if (p->d < 1) return fail(OT_ERR_INVALID_ARG, "d must be >= 1");
   if (p->ldx < p->d || p->ldy < p->d) return fail(OT_ERR_INVALID_ARG, "ldx and ldy must be >= d");
   if (p->dtype != OT_F32 && p->dtype != OT_BF16) return fail(OT_ERR_UNSUPPORTED, "dtype must be OT_F32 or OT_BF16");
+  if (p->flags & ~OT_NATIVE_F32) return fail(OT_ERR_INVALID_ARG, "unknown problem flag");
   if (p->d > OT_MAX_D) return fail(OT_ERR_UNSUPPORTED, "d exceeds OT_MAX_D");
   if (p->n > (int64_t)1 << 30 || p->m > (int64_t)1 << 30) return fail(OT_ERR_UNSUPPORTED, "n or m exceeds 2^30");
   if (!(p->eps > 0.f) || !std::isfinite(p->eps)) return fail(OT_ERR_INVALID_ARG, "eps must be finite and > 0");
@@ -140,7 +157,7 @@ struct SolveWs {
 
 SolveWs solve_layout(const ot_problem* p, int splits_f, int splits_g) {
   SolveWs w{};
-  w.k = kernel_conf(p->d, p->dtype == OT_BF16);
+  w.k = kernel_conf(p->d, p->dtype == OT_BF16, (p->flags & OT_NATIVE_F32) == 0);
   w.ntiles = ceil_div(p->n, kTile);
   w.mtiles = ceil_div(p->m, kTile);
   w.npad = w.ntiles * kTile;
@@ -179,6 +196,10 @@ struct Ctx {
   SolveWs L;
   char* ws;
   float c, eps;
+  // Units of the streamed LSE kernels: fp32 X is packed pre-multiplied by c
+  // and biases are written times c, so scores are log2 values (kc = 1); bf16
+  // operands stay in dot-product units and the kernel multiplies by kc = c.
+  float bscale, kc, xscale;
   const float* nx;
   const float* ny;
   float *wx, *hx, *bx, *wy, *hy, *by, *errp, *errv;
@@ -194,6 +215,10 @@ Ctx make_ctx(const ot_problem* p, const SolveWs& L, void* ws, float* f, float* g
   x.ws = (char*)ws;
   x.eps = p->eps;
   x.c = 2.f * kLog2e / p->eps;
+  const bool bf = p->dtype == OT_BF16;
+  x.bscale = bf ? 1.f : x.c;
+  x.kc = bf ? x.c : 1.f;
+  x.xscale = bf ? 1.f : x.c;
   x.xp = x.ws + L.o_xp;
   x.yp = x.ws + L.o_yp;
   x.nx = p->x_sqn ? p->x_sqn : (const float*)(x.ws + L.o_nx);
@@ -218,8 +243,15 @@ int prepare(const Ctx& x, hipStream_t st) {
   const int bf = p->dtype == OT_BF16;
   if (!p->x_sqn) OT_HIP(launch_sqnorms(p->x, bf, p->n, p->d, p->ldx, (float*)x.nx, st));
   if (!p->y_sqn) OT_HIP(launch_sqnorms(p->y, bf, p->m, p->d, p->ldy, (float*)x.ny, st));
-  OT_HIP(launch_pack_points(p->x, bf, p->n, p->d, p->ldx, x.L.ntiles, x.L.k.kbp, x.xp, st));
-  OT_HIP(launch_pack_points(p->y, bf, p->m, p->d, p->ldy, x.L.mtiles, x.L.k.kbp, x.yp, st));
+  if (x.L.k.mode == 2) {
+    OT_HIP(launch_pack_split((const float*)p->x, p->n, p->d, p->ldx, x.L.ntiles, x.L.k.kbp, x.xscale,
+                             x.xp, st));
+    OT_HIP(launch_pack_split((const float*)p->y, p->m, p->d, p->ldy, x.L.mtiles, x.L.k.kbp, 1.f, x.yp,
+                             st));
+  } else {
+    OT_HIP(launch_pack_points(p->x, bf, p->n, p->d, p->ldx, x.L.ntiles, x.L.k.kbp, x.xscale, x.xp, st));
+    OT_HIP(launch_pack_points(p->y, bf, p->m, p->d, p->ldy, x.L.mtiles, x.L.k.kbp, 1.f, x.yp, st));
+  }
   OT_HIP(launch_weights(p->a, (int)p->n, x.L.npad, x.eps, x.wx, x.hx, st));
   OT_HIP(launch_weights(p->b, (int)p->m, x.L.mpad, x.eps, x.wy, x.hy, st));
   return OT_OK;
@@ -227,15 +259,15 @@ int prepare(const Ctx& x, hipStream_t st) {
 
 // f half-step: LSE over columns y with bias by, merge into f (bias bx for the g side).
 int half_f(const Ctx& x, hipStream_t st, int with_err, int write) {
-  OT_HIP(launch_lse_partial(x.L.F, x.p->dtype == OT_BF16, x.xp, x.yp, x.by, x.c, x.part, st));
-  OT_HIP(launch_lse_merge(x.part, x.L.F.splits, x.L.npad, (int)x.p->n, x.c, x.eps, x.nx, x.hx, x.wx,
+  OT_HIP(launch_lse_partial(x.L.F, x.L.k.mode, x.xp, x.yp, x.by, x.kc, x.part, st));
+  OT_HIP(launch_lse_merge(x.part, x.L.F.splits, x.L.npad, (int)x.p->n, x.bscale, x.eps, x.nx, x.hx, x.wx,
                           x.f, x.bx, x.errp, with_err, write, st));
   return OT_OK;
 }
 
 int half_g(const Ctx& x, hipStream_t st, int with_err, int write) {
-  OT_HIP(launch_lse_partial(x.L.G, x.p->dtype == OT_BF16, x.yp, x.xp, x.bx, x.c, x.part, st));
-  OT_HIP(launch_lse_merge(x.part, x.L.G.splits, x.L.mpad, (int)x.p->m, x.c, x.eps, x.ny, x.hy, x.wy,
+  OT_HIP(launch_lse_partial(x.L.G, x.L.k.mode, x.yp, x.xp, x.bx, x.kc, x.part, st));
+  OT_HIP(launch_lse_merge(x.part, x.L.G.splits, x.L.mpad, (int)x.p->m, x.bscale, x.eps, x.ny, x.hy, x.wy,
                           x.g, x.by, x.errp + x.L.errblocks_f, with_err, write, st));
   return OT_OK;
 }
@@ -257,7 +289,7 @@ struct GraphKey {
   int64_t n, m, d;
   int dtype;
   float eps;
-  int count, with_err;
+  int count, with_err, mode;
   PassShape F, G;
   bool operator==(const GraphKey& o) const { return std::memcmp(this, &o, sizeof(*this)) == 0; }
 };
@@ -289,6 +321,7 @@ int get_graph(const Ctx& x, int count, int with_err, hipGraphExec_t* out) {
   key.eps = x.p->eps;
   key.count = count;
   key.with_err = with_err;
+  key.mode = x.L.k.mode;
   key.F = x.L.F;
   key.G = x.L.G;
   std::lock_guard<std::mutex> lk(g_graph_mu);
@@ -363,18 +396,17 @@ int run_iterations_timed(const Ctx& x, hipStream_t st, int count, int with_err, 
   const size_t need = (size_t)count * 4;
   int rc = g_events.ensure(need);
   if (rc) return rc;
-  const int bf = x.p->dtype == OT_BF16;
   for (int t = 0; t < count; ++t) {
     hipEvent_t* e = &g_events.ev[(size_t)t * 4];
     OT_HIP(hipEventRecord(e[0], st));
-    OT_HIP(launch_lse_partial(x.L.F, bf, x.xp, x.yp, x.by, x.c, x.part, st));
+    OT_HIP(launch_lse_partial(x.L.F, x.L.k.mode, x.xp, x.yp, x.by, x.kc, x.part, st));
     OT_HIP(hipEventRecord(e[1], st));
-    OT_HIP(launch_lse_merge(x.part, x.L.F.splits, x.L.npad, (int)x.p->n, x.c, x.eps, x.nx, x.hx,
+    OT_HIP(launch_lse_merge(x.part, x.L.F.splits, x.L.npad, (int)x.p->n, x.bscale, x.eps, x.nx, x.hx,
                             x.wx, x.f, x.bx, x.errp, with_err, 1, st));
     OT_HIP(hipEventRecord(e[2], st));
-    OT_HIP(launch_lse_partial(x.L.G, bf, x.yp, x.xp, x.bx, x.c, x.part, st));
+    OT_HIP(launch_lse_partial(x.L.G, x.L.k.mode, x.yp, x.xp, x.bx, x.kc, x.part, st));
     OT_HIP(hipEventRecord(e[3], st));
-    OT_HIP(launch_lse_merge(x.part, x.L.G.splits, x.L.mpad, (int)x.p->m, x.c, x.eps, x.ny, x.hy,
+    OT_HIP(launch_lse_merge(x.part, x.L.G.splits, x.L.mpad, (int)x.p->m, x.bscale, x.eps, x.ny, x.hy,
                             x.wy, x.g, x.by, x.errp + x.L.errblocks_f, 0, 1, st));
   }
   OT_HIP(hipStreamSynchronize(st));
@@ -419,12 +451,12 @@ int update_impl(const ot_problem* p, const float* other, float* pot, float* err,
   if (rc) return rc;
   const int with_err = err != nullptr;
   if (is_f) {
-    OT_HIP(launch_bias_from_pot(x.g, x.ny, x.hy, (int)p->m, L.mpad, x.by, st));
+    OT_HIP(launch_bias_from_pot(x.g, x.ny, x.hy, (int)p->m, L.mpad, x.bscale, x.by, st));
     rc = half_f(x, st, with_err, 1);
     if (rc) return rc;
     if (with_err) OT_HIP(launch_err_reduce(x.errp, L.errblocks_f, err, st));
   } else {
-    OT_HIP(launch_bias_from_pot(x.f, x.nx, x.hx, (int)p->n, L.npad, x.bx, st));
+    OT_HIP(launch_bias_from_pot(x.f, x.nx, x.hx, (int)p->n, L.npad, x.bscale, x.bx, st));
     rc = half_g(x, st, with_err, 1);
     if (rc) return rc;
     if (with_err) OT_HIP(launch_err_reduce(x.errp + L.errblocks_f, L.errblocks_g, err, st));
@@ -443,7 +475,7 @@ struct ApplyWs {
 
 ApplyWs apply_layout(const ot_problem* p, int64_t cols, bool transpose) {
   ApplyWs w{};
-  w.k = kernel_conf(p->d, p->dtype == OT_BF16);
+  w.k = kernel_conf(p->d, p->dtype == OT_BF16, false);
   const int64_t rows = transpose ? p->m : p->n;
   const int64_t strm = transpose ? p->n : p->m;
   w.rtiles = ceil_div(rows, kTile);
@@ -542,7 +574,7 @@ int ot_solve(const ot_problem* p, float* f, float* g, const ot_solve_opts* o,
       OT_HIP(launch_fill(f, 0.f, p->n, st));
       OT_HIP(launch_fill(g, 0.f, p->m, st));
     }
-    OT_HIP(launch_bias_from_pot(g, x.ny, x.hy, (int)p->m, L.mpad, x.by, st));
+    OT_HIP(launch_bias_from_pot(g, x.ny, x.hy, (int)p->m, L.mpad, x.bscale, x.by, st));
     const bool use_graph = o->use_graph != 0 && st != nullptr;
     float lse_ms = 0.f;
     int lse_launches = 0;
@@ -568,7 +600,7 @@ int ot_solve(const ot_problem* p, float* f, float* g, const ot_solve_opts* o,
     }
     if (info) {
       // Exact marginal errors of the returned (f, g): one dry pass per side.
-      if (done == 0) OT_HIP(launch_bias_from_pot(f, x.nx, x.hx, (int)p->n, L.npad, x.bx, st));
+      if (done == 0) OT_HIP(launch_bias_from_pot(f, x.nx, x.hx, (int)p->n, L.npad, x.bscale, x.bx, st));
       rc = half_f(x, st, 1, 0);
       if (rc) return rc;
       OT_HIP(launch_err_reduce(x.errp, L.errblocks_f, x.errv, st));
@@ -587,6 +619,7 @@ int ot_solve(const ot_problem* p, float* f, float* g, const ot_solve_opts* o,
       info->lse_launches = lse_launches;
       info->splits_f = L.F.splits;
       info->splits_g = L.G.splits;
+      info->operand_mode = L.k.mode;
       if (info->nonfinite) return fail(OT_ERR_NONFINITE, "potentials are not finite");
     }
     return OT_OK;
@@ -632,8 +665,8 @@ int ot_apply_plan(const ot_problem* p, const float* f, const float* g, const voi
     const float* ny = p->y_sqn ? p->y_sqn : (const float*)(w + L.o_ny);
     if (!p->x_sqn) OT_HIP(launch_sqnorms(p->x, bf, p->n, p->d, p->ldx, (float*)nx, st));
     if (!p->y_sqn) OT_HIP(launch_sqnorms(p->y, bf, p->m, p->d, p->ldy, (float*)ny, st));
-    OT_HIP(launch_pack_points(p->x, bf, p->n, p->d, p->ldx, ntiles, L.k.kbp, xp, st));
-    OT_HIP(launch_pack_points(p->y, bf, p->m, p->d, p->ldy, mtiles, L.k.kbp, yp, st));
+    OT_HIP(launch_pack_points(p->x, bf, p->n, p->d, p->ldx, ntiles, L.k.kbp, 1.f, xp, st));
+    OT_HIP(launch_pack_points(p->y, bf, p->m, p->d, p->ldy, mtiles, L.k.kbp, 1.f, yp, st));
     // Row side r (outputs) and column side s (streamed).
     const int64_t rows = tr ? p->m : p->n, srows = tr ? p->n : p->m;
     const float* wr_user = tr ? p->b : p->a;
@@ -654,7 +687,7 @@ int ot_apply_plan(const ot_problem* p, const float* f, const float* g, const voi
     float* po = (float*)(w + L.o_o);
     OT_HIP(launch_weights(wr_user, (int)rows, L.rpad, eps, wr, hr, st));
     OT_HIP(launch_weights(ws_user, (int)srows, L.cpad, eps, wc, hc, st));
-    OT_HIP(launch_bias_from_pot(pot_s, norm_s, hc, (int)srows, L.cpad, bc, st));
+    OT_HIP(launch_bias_from_pot(pot_s, norm_s, hc, (int)srows, L.cpad, 1.f, bc, st));
     OT_HIP(launch_pack_values(V, v_dtype == OT_BF16, srows, cols, ldv, L.ctiles, L.pblocks, vp, st));
     OT_HIP(launch_apply_partial(L.S, bf, L.pblocks, L.pb_per_pass, Rp, Cp, bc, vp, c, pms, po,
                                 L.ppad, st));

@@ -39,13 +39,16 @@ __device__ __forceinline__ float load_as_f32<uint16_t>(const uint16_t* p, int64_
 
 // ---------------------------------------------------------------------------
 // Merge of split partials + half-step epilogue (App. D.1 / D.2: write the
-// potential once). For row i:
-//   L = (2/eps) M + ln S over all splits,  shifted potential = -eps L = -2M - eps ln S,
-//   pot_i = norm_i + shifted, next bias_i = (pot_i - norm_i)/2 + (eps/2) log w_i,
+// potential once). Partials are (M2, S) in log2 units: the row's log-sum-exp
+// over split s is ln 2 * (M2 + log2 S). For row i:
+//   M = max_s M2_s, S = sum_s S_s 2^(M2_s - M),
+//   shifted potential = -eps ln 2 (M + log2 S),  pot_i = norm_i + shifted,
+//   next bias_i = bscale * ((pot_i - norm_i)/2 + (eps/2) log w_i),
 //   err_i = w_i |exp((pot_old_i - pot_i)/eps) - 1|   (App. E.1 induced marginal).
+// bscale = 2 log2(e)/eps when the streamed kernel works in log2 units (fp32
+// operands packed pre-scaled), 1 when it works in dot-product units.
 // The bias is rebuilt from the stored fp32 potential, so resuming from
 // returned potentials reproduces an uninterrupted run bit for bit.
-// ---------------------------------------------------------------------------
 __device__ __forceinline__ float block_sum_256(float v, float* sh) {
   const int t = threadIdx.x;
   sh[t] = v;
@@ -59,7 +62,7 @@ __device__ __forceinline__ float block_sum_256(float v, float* sh) {
 }
 
 __global__ __launch_bounds__(256) void lse_merge_kernel(
-    const float2* __restrict__ part, int splits, int rpad, int rows, float c, float eps,
+    const float2* __restrict__ part, int splits, int rpad, int rows, float bscale, float eps,
     const float* __restrict__ norm, const float* __restrict__ hlw, const float* __restrict__ wgt,
     float* __restrict__ pot, float* __restrict__ bias_out, float* __restrict__ err_part,
     int with_err, int write_pot) {
@@ -69,13 +72,12 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(
   if (i < rows) {
     float M = part[i].x;
     for (int s = 1; s < splits; ++s) M = fmaxf(M, part[(size_t)s * rpad + i].x);
-    const float cm = c * M;
     float S = 0.f;
     for (int s = 0; s < splits; ++s) {
       const float2 ps = part[(size_t)s * rpad + i];
-      S += ps.y * exp2f(fmaf(c, ps.x, -cm));
+      S += ps.y * exp2f(ps.x - M);
     }
-    const float shifted = -2.f * M - eps * kLn2 * log2f(S);
+    const float shifted = -eps * kLn2 * (M + log2f(S));
     const float nrm = norm[i];
     const float pnew = nrm + shifted;
     if (with_err) {
@@ -84,7 +86,7 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(
     }
     if (write_pot) {
       pot[i] = pnew;
-      bias_out[i] = 0.5f * (pnew - nrm) + hlw[i];
+      bias_out[i] = bscale * (0.5f * (pnew - nrm) + hlw[i]);
     }
   } else if (i < rpad && write_pot) {
     bias_out[i] = kSentinel;
@@ -211,11 +213,13 @@ __global__ __launch_bounds__(256) void sqnorms_kernel(const T* __restrict__ pts,
   if (lane == 0) out[row] = s;
 }
 
-// Packs a row-major point cloud into the MFMA operand layout of kernels.h.
+// Packs a row-major point cloud into the MFMA operand layout of kernels.h,
+// multiplying fp32 values by `scale` (bf16 values are copied unchanged).
 template <typename T>
 __global__ __launch_bounds__(256) void pack_points_kernel(const T* __restrict__ src, int64_t rows,
                                                            int64_t d, int64_t ld, int64_t total,
-                                                           int kbp, u32x4* __restrict__ dst) {
+                                                           int kbp, float scale,
+                                                           u32x4* __restrict__ dst) {
   constexpr int KW = 16 / sizeof(T);  // values per lane per k-block
   for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total;
        idx += (int64_t)gridDim.x * 256) {
@@ -229,7 +233,56 @@ __global__ __launch_bounds__(256) void pack_points_kernel(const T* __restrict__ 
 #pragma unroll
     for (int e = 0; e < KW; ++e)
       v[e] = (row < rows && k0 + e < d) ? src[row * ld + k0 + e] : T(0);
+    if constexpr (sizeof(T) == 4) {  // fp32 rows may be packed pre-scaled; bf16 never are
+#pragma unroll
+      for (int e = 0; e < KW; ++e) v[e] = v[e] * scale;
+    }
     dst[idx] = __builtin_bit_cast(u32x4, v);
+  }
+}
+
+// bf16 rounding (to nearest, ties to even) of an fp32 value, as bits; NaN
+// stays a quiet NaN.
+__device__ __forceinline__ uint32_t bf16_bits_rne(float v) {
+  const uint32_t u = __float_as_uint(v);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Splits scale * src into hi + mid + lo, each the bf16 rounding of what the
+// previous parts left (the differences are exact in fp32), and packs part p
+// of k-block kb into unit 3 kb + p of the tile, in the lane layout of a bf16
+// k-block: lane l holds row l % 32, values k = 16 kb + 8 (l / 32) ... + 7.
+__global__ __launch_bounds__(256) void pack_split_kernel(const float* __restrict__ src,
+                                                          int64_t rows, int64_t d, int64_t ld,
+                                                          int64_t total, int units, float scale,
+                                                          u32x4* __restrict__ dst) {
+  for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * 256) {
+    const int lane = (int)(idx & 63);
+    const int64_t tu = idx >> 6;
+    const int u = (int)(tu % units);
+    const int64_t t = tu / units;
+    const int kb = u / 3, part = u % 3;
+    const int64_t row = t * kTile + (lane & 31);
+    const int64_t k0 = (int64_t)kb * 16 + (lane >> 5) * 8;
+    uint32_t h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float v = (row < rows && k0 + e < d) ? src[row * ld + k0 + e] * scale : 0.f;
+      uint32_t b = bf16_bits_rne(v);
+      for (int q = 0; q < part; ++q) {
+        v = v - __uint_as_float(b << 16);
+        b = bf16_bits_rne(v);
+      }
+      h[e] = b;
+    }
+    u32x4 o;
+    o.x = h[0] | (h[1] << 16);
+    o.y = h[2] | (h[3] << 16);
+    o.z = h[4] | (h[5] << 16);
+    o.w = h[6] | (h[7] << 16);
+    dst[idx] = o;
   }
 }
 
@@ -284,11 +337,11 @@ __global__ __launch_bounds__(256) void fill_kernel(float* __restrict__ p, float 
 __global__ __launch_bounds__(256) void bias_from_pot_kernel(const float* __restrict__ pot,
                                                              const float* __restrict__ norm,
                                                              const float* __restrict__ hlw,
-                                                             int rows, int rpad,
+                                                             int rows, int rpad, float bscale,
                                                              float* __restrict__ bias) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= rpad) return;
-  bias[i] = (i < rows) ? 0.5f * (pot[i] - norm[i]) + hlw[i] : kSentinel;
+  bias[i] = (i < rows) ? bscale * (0.5f * (pot[i] - norm[i]) + hlw[i]) : kSentinel;
 }
 
 
@@ -310,15 +363,23 @@ hipError_t launch_sqnorms(const void* pts, int bf16, int64_t rows, int64_t d, in
 }
 
 hipError_t launch_pack_points(const void* src, int bf16, int64_t rows, int64_t d, int64_t ld,
-                              int rtiles, int kbp, void* dst, hipStream_t st) {
+                              int rtiles, int kbp, float scale, void* dst, hipStream_t st) {
   const int64_t total = (int64_t)rtiles * kbp * 64;
   const int grid = grid_for(total, 256, 65536);
   if (bf16)
     pack_points_kernel<uint16_t>
-        <<<grid, 256, 0, st>>>((const uint16_t*)src, rows, d, ld, total, kbp, (u32x4*)dst);
+        <<<grid, 256, 0, st>>>((const uint16_t*)src, rows, d, ld, total, kbp, 1.0f, (u32x4*)dst);
   else
     pack_points_kernel<float>
-        <<<grid, 256, 0, st>>>((const float*)src, rows, d, ld, total, kbp, (u32x4*)dst);
+        <<<grid, 256, 0, st>>>((const float*)src, rows, d, ld, total, kbp, scale, (u32x4*)dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_split(const float* src, int64_t rows, int64_t d, int64_t ld, int rtiles,
+                             int units, float scale, void* dst, hipStream_t st) {
+  const int64_t total = (int64_t)rtiles * units * 64;
+  pack_split_kernel<<<grid_for(total, 256, 65536), 256, 0, st>>>(src, rows, d, ld, total, units,
+                                                                 scale, (u32x4*)dst);
   return hipGetLastError();
 }
 
@@ -347,16 +408,17 @@ hipError_t launch_fill(float* p, float v, int64_t count, hipStream_t st) {
 }
 
 hipError_t launch_bias_from_pot(const float* pot, const float* norm, const float* hlw, int rows,
-                                int rpad, float* bias, hipStream_t st) {
-  bias_from_pot_kernel<<<(rpad + 255) / 256, 256, 0, st>>>(pot, norm, hlw, rows, rpad, bias);
+                                int rpad, float bscale, float* bias, hipStream_t st) {
+  bias_from_pot_kernel<<<(rpad + 255) / 256, 256, 0, st>>>(pot, norm, hlw, rows, rpad, bscale,
+                                                           bias);
   return hipGetLastError();
 }
 
-hipError_t launch_lse_merge(const float2* part, int splits, int rpad, int rows, float c, float eps,
+hipError_t launch_lse_merge(const float2* part, int splits, int rpad, int rows, float bscale, float eps,
                             const float* norm, const float* hlw, const float* wgt, float* pot,
                             float* bias_out, float* err_part, int with_err, int write_pot,
                             hipStream_t st) {
-  lse_merge_kernel<<<(rpad + 255) / 256, 256, 0, st>>>(part, splits, rpad, rows, c, eps, norm,
+  lse_merge_kernel<<<(rpad + 255) / 256, 256, 0, st>>>(part, splits, rpad, rows, bscale, eps, norm,
                                                        hlw, wgt, pot, bias_out, err_part,
                                                        with_err, write_pot);
   return hipGetLastError();

@@ -32,17 +32,23 @@ struct PassShape {
 hipError_t launch_sqnorms(const void* pts, int bf16, int64_t rows, int64_t d, int64_t ld,
                           float* out, hipStream_t st);
 hipError_t launch_pack_points(const void* src, int bf16, int64_t rows, int64_t d, int64_t ld,
-                              int rtiles, int kbp, void* dst, hipStream_t st);
+                              int rtiles, int kbp, float scale, void* dst, hipStream_t st);
+// Packs fp32 points (times `scale`) as three bf16 parts hi, mid, lo per
+// k-block of 16 values: units (3 kb, 3 kb + 1, 3 kb + 2) of a tile hold the
+// parts of k-block kb in the lane layout of a bf16 k-block.
+hipError_t launch_pack_split(const float* src, int64_t rows, int64_t d, int64_t ld, int rtiles,
+                             int units, float scale, void* dst, hipStream_t st);
 hipError_t launch_pack_values(const void* V, int bf16, int64_t rows, int64_t cols, int64_t ldv,
                               int ctiles, int pblocks, float* dst, hipStream_t st);
 hipError_t launch_weights(const float* w, int rows, int rpad, float eps, float* wgt, float* hlw,
                           hipStream_t st);
 hipError_t launch_fill(float* p, float v, int64_t count, hipStream_t st);
 hipError_t launch_bias_from_pot(const float* pot, const float* norm, const float* hlw, int rows,
-                                int rpad, float* bias, hipStream_t st);
-hipError_t launch_lse_partial(const PassShape& s, int bf16, const void* Rp, const void* Cp,
+                                int rpad, float bscale, float* bias, hipStream_t st);
+// mode: 0 fp32 operands, 1 bf16 operands, 2 fp32 operands packed as three bf16 parts.
+hipError_t launch_lse_partial(const PassShape& s, int mode, const void* Rp, const void* Cp,
                               const float* cbias, float c, float2* part, hipStream_t st);
-hipError_t launch_lse_merge(const float2* part, int splits, int rpad, int rows, float c, float eps,
+hipError_t launch_lse_merge(const float2* part, int splits, int rpad, int rows, float bscale, float eps,
                             const float* norm, const float* hlw, const float* wgt, float* pot,
                             float* bias_out, float* err_part, int with_err, int write_pot,
                             hipStream_t st);

@@ -64,6 +64,29 @@ __device__ __forceinline__ f32x16 mfma_kblock(u32x4 a, u32x4 b, f32x16 acc) {
   }
 }
 
+// Operand modes of the register-resident pass.
+constexpr int kModeF32 = 0;    // fp32 operands, fp32 MFMA (32x32x2)
+constexpr int kModeBF16 = 1;   // bf16 operands, bf16 MFMA (32x32x16)
+constexpr int kModeSplit = 2;  // fp32 operands as hi + mid + lo bf16 parts, bf16 MFMA
+
+// One k-block of 16 fp32 values held as three bf16 parts per operand
+// (v = hi + mid + lo, each part the bf16 rounding of what the previous ones
+// left, so |mid| <= 2^-9 |v| and |lo| <= 2^-18 |v|). Six partial products are
+// accumulated, smallest first; the three dropped ones (mid*lo, lo*mid, lo*lo)
+// are below 2^-26 of |x y|, finer than fp32 rounding.
+__device__ __forceinline__ f32x16 mfma_split(const u32x4* y, const u32x4* x, f32x16 acc) {
+  auto m = [](u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  };
+  acc = m(y[2], x[0], acc);  // lo * hi
+  acc = m(y[0], x[2], acc);  // hi * lo
+  acc = m(y[1], x[1], acc);  // mid * mid
+  acc = m(y[1], x[0], acc);  // mid * hi
+  acc = m(y[0], x[1], acc);  // hi * mid
+  return m(y[0], x[0], acc); // hi * hi
+}
+
 // Adds bias_j to every accumulator entry of column j: k-slot 0 carries
 // (bias_j, 1), k-slot 1 carries (0, 1).
 __device__ __forceinline__ f32x16 mfma_bias(float wv, int h, f32x16 acc) {
@@ -207,29 +230,104 @@ __global__ __launch_bounds__(256) void lse_partial_kernel(
     const float St = S[ri] * __builtin_amdgcn_exp2f(fmaf(c, M[ri], -cm)) +
                      Sp * __builtin_amdgcn_exp2f(fmaf(c, Mp, -cm));
     if (h == 0 && rt0 + ri < rtiles)
-      part[(size_t)s * rpad + (size_t)(rt0 + ri) * kTile + (lane & 31)] = make_float2(Mt, St);
+      part[(size_t)s * rpad + (size_t)(rt0 + ri) * kTile + (lane & 31)] = make_float2(c * Mt, St);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Software-pipelined variant of the register-resident pass. Each wave keeps
-// two score tiles in flight: while the matrix cores form the scores of column
-// tile t+1, the vector unit runs the online LSE of tile t, so one wave keeps
-// both units busy. The column operand alternates between two register
-// buffers (the loop body is written twice with the roles swapped), so a
-// prefetched tile is never copied between registers.
+// Software-pipelined register-resident pass with a lazily raised stabiliser.
+//
+// Pipelining: each wave keeps two score tiles in flight. While the matrix
+// cores form the scores of column tile t+1, the vector unit exponentiates
+// tile t. The column operand alternates between two register buffers (the
+// loop body is written twice with the roles swapped), so a prefetched tile is
+// never copied between registers.
+//
+// Lazy stabiliser: the online LSE of App. D.3 is exact for any running
+// stabiliser M, not only for the running maximum. The bias MFMA uses its
+// second k-slot to subtract M_i from every score (A = [bias_j, 1],
+// B = [1, -M_i]), so in the common case a tile costs one exp2 and one add per
+// score. Only when a tile could overflow (tile sum >= 2^64), or before M has
+// been set from data, does the wave take the exact path: tile maximum, raise
+// M, rescale S. M is kept identical in the two lanes (l, l ^ 32) that share a
+// row, because the bias MFMA reads it from lane l + 32.
+//
+// Units: for fp32 inputs the row operand X is packed pre-multiplied by
+// c = 2 log2(e) / eps and the biases are written in the same units, so scores
+// are log2 values and exp2 needs no multiply (KS = 1). bf16 operands cannot be
+// rescaled without rounding, so their scores stay in dot-product units and
+// are multiplied by c before exp2 (KS = c). Partials are written in log2
+// units: LSE_row = ln 2 * (M2 + log2 S).
 // ---------------------------------------------------------------------------
-template <bool BF16, int KB, int RI>
+constexpr float kUnset = -1.0e30f;  // stabiliser not yet taken from data
+
+// KB counts 1 KiB operand units per tile: one per k-block for fp32 / bf16,
+// three (hi, mid, lo) per k-block in split mode.
+template <int MODE, int KB, int RI>
 __device__ __forceinline__ void score_tile(const u32x4 (&y)[KB], const u32x4 (&xr)[RI][KB],
-                                           float wv, int h, f32x16 (&acc)[RI]) {
+                                           float wv, int h, const float (&Mf)[RI],
+                                           f32x16 (&acc)[RI]) {
 #pragma unroll
   for (int ri = 0; ri < RI; ++ri) acc[ri] = f32x16{};
+  if constexpr (MODE == kModeSplit) {
 #pragma unroll
-  for (int kb = 0; kb < KB; ++kb)
+    for (int kb = 0; kb < KB; kb += 3)
 #pragma unroll
-    for (int ri = 0; ri < RI; ++ri) acc[ri] = mfma_kblock<BF16>(y[kb], xr[ri][kb], acc[ri]);
+      for (int ri = 0; ri < RI; ++ri) acc[ri] = mfma_split(&y[kb], &xr[ri][kb], acc[ri]);
+  } else {
 #pragma unroll
-  for (int ri = 0; ri < RI; ++ri) acc[ri] = mfma_bias(wv, h, acc[ri]);
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int ri = 0; ri < RI; ++ri)
+        acc[ri] = mfma_kblock<MODE == kModeBF16>(y[kb], xr[ri][kb], acc[ri]);
+  }
+#pragma unroll
+  for (int ri = 0; ri < RI; ++ri)
+    acc[ri] = __builtin_amdgcn_mfma_f32_32x32x2f32(h ? 1.0f : wv, h ? -Mf[ri] : 1.0f, acc[ri],
+                                                   0, 0, 0);
+}
+
+// Stabiliser folded into the next tile's scores: the running M once set.
+__device__ __forceinline__ float fold_of(float M) { return M > 0.5f * kUnset ? M : 0.f; }
+
+// Common-case tile: s = sum exp2(ks * a_r) relative to the folded Mf; returns
+// the candidate new S and whether the exact path is needed.
+template <bool SCALED>
+__device__ __forceinline__ bool lse_fast(const f32x16& a, float Mf, float M, float S, float ks,
+                                         float& Snew) {
+  float e0 = __builtin_amdgcn_exp2f(SCALED ? a[0] : ks * a[0]);
+  float e1 = __builtin_amdgcn_exp2f(SCALED ? a[1] : ks * a[1]);
+  float e2 = __builtin_amdgcn_exp2f(SCALED ? a[2] : ks * a[2]);
+  float e3 = __builtin_amdgcn_exp2f(SCALED ? a[3] : ks * a[3]);
+#pragma unroll
+  for (int r = 4; r < 16; r += 4) {
+    e0 += __builtin_amdgcn_exp2f(SCALED ? a[r + 0] : ks * a[r + 0]);
+    e1 += __builtin_amdgcn_exp2f(SCALED ? a[r + 1] : ks * a[r + 1]);
+    e2 += __builtin_amdgcn_exp2f(SCALED ? a[r + 2] : ks * a[r + 2]);
+    e3 += __builtin_amdgcn_exp2f(SCALED ? a[r + 3] : ks * a[r + 3]);
+  }
+  const float s = (e0 + e1) + (e2 + e3);
+  Snew = fmaf(s, __builtin_amdgcn_exp2f(ks * (Mf - M)), S);
+  return !(s < 0x1p64f) || !(Snew >= 0x1p-64f) || !(M > 0.5f * kUnset);
+}
+
+// Exact tile: raise M to the tile maximum (shared by the lane pair), rescale.
+__device__ __forceinline__ void lse_exact(const f32x16& a, float Mf, float& M, float& S,
+                                          float ks) {
+  float m = max16(a) + Mf;
+  m = fmaxf(m, __shfl_xor(m, 32));
+  m = fmaxf(m, M);
+  const float t = Mf - m;
+  float e0 = 0.f, e1 = 0.f, e2 = 0.f, e3 = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; r += 4) {
+    e0 += __builtin_amdgcn_exp2f(ks * (a[r + 0] + t));
+    e1 += __builtin_amdgcn_exp2f(ks * (a[r + 1] + t));
+    e2 += __builtin_amdgcn_exp2f(ks * (a[r + 2] + t));
+    e3 += __builtin_amdgcn_exp2f(ks * (a[r + 3] + t));
+  }
+  S = fmaf(S, __builtin_amdgcn_exp2f(ks * (M - m)), (e0 + e1) + (e2 + e3));
+  M = m;
 }
 
 template <int KB>
@@ -244,10 +342,11 @@ __device__ __forceinline__ void load_ctile(const u32x4* __restrict__ Cp,
 // Orders one pipeline stage (one scheduling region): one matrix instruction
 // alternating with a few vector instructions, then the loads that refill the
 // column buffer the matrix instructions have just read.
-template <bool BF16, int KB, int RI>
+template <int MODE, int KB, int RI>
 __device__ __forceinline__ void stage_schedule() {
-  constexpr int kMfma = RI * (KB * (BF16 ? 1 : 4) + 1);
-  constexpr int kValu = RI * 62;  // online LSE of RI score tiles
+  constexpr int kPerUnit = MODE == kModeF32 ? 4 : (MODE == kModeBF16 ? 1 : 2);
+  constexpr int kMfma = RI * (KB * kPerUnit + 1);
+  constexpr int kValu = RI * (MODE == kModeBF16 ? 40 : 24);  // common-case LSE of RI tiles
   constexpr int kValuPer = (kValu + kMfma - 1) / kMfma;
 #pragma unroll
   for (int i = 0; i < kMfma; ++i) {
@@ -257,7 +356,55 @@ __device__ __forceinline__ void stage_schedule() {
   __builtin_amdgcn_sched_group_barrier(0x020, KB + 1, 0);      // VMEM reads
 }
 
-template <bool BF16, int KB, int RI>
+// One pipeline stage: scores of the next tile into accN (folding the current
+// stabiliser), common-case LSE of the current tile accC, refill of the buffer
+// yN just consumed; then, outside the scheduled region, the exact path for
+// the waves that need it.
+template <int MODE, int KB, int RI>
+__device__ __forceinline__ void pipe_stage(const u32x4* __restrict__ Cp,
+                                           const float* __restrict__ cbias, int jt_refill,
+                                           int lane, int h, float ks, const u32x4 (&xr)[RI][KB],
+                                           u32x4 (&yN)[KB], float& wN, f32x16 (&accN)[RI],
+                                           float (&MfN)[RI], const f32x16 (&accC)[RI],
+                                           const float (&MfC)[RI], float (&M)[RI],
+                                           float (&S)[RI]) {
+#pragma unroll
+  for (int ri = 0; ri < RI; ++ri) MfN[ri] = fold_of(M[ri]);
+  score_tile<MODE, KB, RI>(yN, xr, wN, h, MfN, accN);
+  float Sn[RI];
+  bool slow = false;
+#pragma unroll
+  for (int ri = 0; ri < RI; ++ri) slow |= lse_fast<MODE != kModeBF16>(accC[ri], MfC[ri], M[ri], S[ri], ks, Sn[ri]);
+  load_ctile<KB>(Cp, cbias, jt_refill, lane, yN, wN);
+  stage_schedule<MODE, KB, RI>();
+  __builtin_amdgcn_sched_barrier(0);
+  if (__builtin_amdgcn_ballot_w64(slow) != 0) {
+#pragma unroll
+    for (int ri = 0; ri < RI; ++ri) lse_exact(accC[ri], MfC[ri], M[ri], S[ri], ks);
+  } else {
+#pragma unroll
+    for (int ri = 0; ri < RI; ++ri) S[ri] = Sn[ri];
+  }
+}
+
+// LSE of a tile outside the pipelined loop (the last one or two of a split).
+template <int MODE, int RI>
+__device__ __forceinline__ void lse_tail(const f32x16 (&acc)[RI], const float (&Mf)[RI],
+                                         float (&M)[RI], float (&S)[RI], float ks) {
+  float Sn[RI];
+  bool slow = false;
+#pragma unroll
+  for (int ri = 0; ri < RI; ++ri) slow |= lse_fast<MODE != kModeBF16>(acc[ri], Mf[ri], M[ri], S[ri], ks, Sn[ri]);
+  if (__builtin_amdgcn_ballot_w64(slow) != 0) {
+#pragma unroll
+    for (int ri = 0; ri < RI; ++ri) lse_exact(acc[ri], Mf[ri], M[ri], S[ri], ks);
+  } else {
+#pragma unroll
+    for (int ri = 0; ri < RI; ++ri) S[ri] = Sn[ri];
+  }
+}
+
+template <int MODE, int KB, int RI>
 __global__ __launch_bounds__(256) void lse_pipe_kernel(
     const u32x4* __restrict__ Rp, const u32x4* __restrict__ Cp, const float* __restrict__ cbias,
     int rtiles, int ctiles, int splits, int tps, float c, float2* __restrict__ part, int rpad) {
@@ -270,6 +417,7 @@ __global__ __launch_bounds__(256) void lse_pipe_kernel(
   if (rt0 >= rtiles) return;
   const int jt0 = s * tps;
   const int last = min(jt0 + tps, ctiles) - 1 - jt0;  // split holds tiles 0..last, last >= 0
+  const float ks = MODE == kModeBF16 ? c : 1.0f;
 
   u32x4 xr[RI][KB];
 #pragma unroll
@@ -281,56 +429,48 @@ __global__ __launch_bounds__(256) void lse_pipe_kernel(
   float M[RI], S[RI];
 #pragma unroll
   for (int ri = 0; ri < RI; ++ri) {
-    M[ri] = -1.0e30f;
+    M[ri] = kUnset;
     S[ri] = 0.f;
   }
 
-  // Invariant at the top of the loop: accA holds the scores of tile k, yB
-  // holds (or is loading) tile k+1 and yA tile k+2; indices past the split's
-  // last tile are clamped to it (loaded, never reduced).
+  // Invariant at the top of the loop: accA holds the scores of tile k (with
+  // MfA folded in), yB holds (or is loading) tile k+1 and yA tile k+2;
+  // indices past the split's last tile are clamped to it (loaded, never
+  // reduced).
   u32x4 yA[KB], yB[KB];
   float wA, wB;
   f32x16 accA[RI], accB[RI];
+  float MfA[RI], MfB[RI];
   load_ctile<KB>(Cp, cbias, jt0, lane, yA, wA);
   load_ctile<KB>(Cp, cbias, jt0 + min(1, last), lane, yB, wB);
-  score_tile<BF16, KB, RI>(yA, xr, wA, h, accA);
+#pragma unroll
+  for (int ri = 0; ri < RI; ++ri) MfA[ri] = 0.f;
+  score_tile<MODE, KB, RI>(yA, xr, wA, h, MfA, accA);
   load_ctile<KB>(Cp, cbias, jt0 + min(2, last), lane, yA, wA);
   int k = 0;
   for (; k + 2 <= last; k += 2) {
-    score_tile<BF16, KB, RI>(yB, xr, wB, h, accB);
-#pragma unroll
-    for (int ri = 0; ri < RI; ++ri) lse_tile(accA[ri], M[ri], S[ri], c);
-    load_ctile<KB>(Cp, cbias, jt0 + min(k + 3, last), lane, yB, wB);
-    stage_schedule<BF16, KB, RI>();
-    __builtin_amdgcn_sched_barrier(0);
-    score_tile<BF16, KB, RI>(yA, xr, wA, h, accA);
-#pragma unroll
-    for (int ri = 0; ri < RI; ++ri) lse_tile(accB[ri], M[ri], S[ri], c);
-    load_ctile<KB>(Cp, cbias, jt0 + min(k + 4, last), lane, yA, wA);
-    stage_schedule<BF16, KB, RI>();
-    __builtin_amdgcn_sched_barrier(0);
+    pipe_stage<MODE, KB, RI>(Cp, cbias, jt0 + min(k + 3, last), lane, h, ks, xr, yB, wB, accB,
+                             MfB, accA, MfA, M, S);
+    pipe_stage<MODE, KB, RI>(Cp, cbias, jt0 + min(k + 4, last), lane, h, ks, xr, yA, wA, accA,
+                             MfA, accB, MfB, M, S);
   }
   if (k + 1 <= last) {  // tiles k and k+1 remain
-    score_tile<BF16, KB, RI>(yB, xr, wB, h, accB);
+    lse_tail<MODE, RI>(accA, MfA, M, S, ks);
 #pragma unroll
-    for (int ri = 0; ri < RI; ++ri) lse_tile(accA[ri], M[ri], S[ri], c);
-#pragma unroll
-    for (int ri = 0; ri < RI; ++ri) lse_tile(accB[ri], M[ri], S[ri], c);
+    for (int ri = 0; ri < RI; ++ri) MfB[ri] = fold_of(M[ri]);
+    score_tile<MODE, KB, RI>(yB, xr, wB, h, MfB, accB);
+    lse_tail<MODE, RI>(accB, MfB, M, S, ks);
   } else {  // tile k remains
-#pragma unroll
-    for (int ri = 0; ri < RI; ++ri) lse_tile(accA[ri], M[ri], S[ri], c);
+    lse_tail<MODE, RI>(accA, MfA, M, S, ks);
   }
 
+  // The lane pair shares M: the row's partial is (M in log2 units, S + S').
 #pragma unroll
   for (int ri = 0; ri < RI; ++ri) {
-    const float Mp = __shfl_xor(M[ri], 32);
-    const float Sp = __shfl_xor(S[ri], 32);
-    const float Mt = fmaxf(M[ri], Mp);
-    const float cm = c * Mt;
-    const float St = S[ri] * __builtin_amdgcn_exp2f(fmaf(c, M[ri], -cm)) +
-                     Sp * __builtin_amdgcn_exp2f(fmaf(c, Mp, -cm));
+    const float St = S[ri] + __shfl_xor(S[ri], 32);
     if (h == 0 && rt0 + ri < rtiles)
-      part[(size_t)s * rpad + (size_t)(rt0 + ri) * kTile + (lane & 31)] = make_float2(Mt, St);
+      part[(size_t)s * rpad + (size_t)(rt0 + ri) * kTile + (lane & 31)] =
+          make_float2(ks * M[ri], St);
   }
 }
 
@@ -455,32 +595,45 @@ static void lse_go(const PassShape& s, const void* Rp, const void* Cp, const flo
       part, s.rtiles * kTile);
 }
 
-template <bool BF16, int KB, int RI>
+template <int MODE, int KB, int RI>
 static void lse_pipe_go(const PassShape& s, const void* Rp, const void* Cp, const float* cbias,
                         float c, float2* part, hipStream_t st) {
-  lse_pipe_kernel<BF16, KB, RI><<<s.nrowgroups * s.splits, 256, 0, st>>>(
+  lse_pipe_kernel<MODE, KB, RI><<<s.nrowgroups * s.splits, 256, 0, st>>>(
       (const u32x4*)Rp, (const u32x4*)Cp, cbias, s.rtiles, s.ctiles, s.splits, s.tps, c, part,
       s.rtiles * kTile);
 }
 
-static int lse_variant() {
-  static int v = [] {
-    const char* e = getenv("FLASHOT_LSE_V");
-    return (e && *e) ? atoi(e) : 2;
-  }();
-  return v;
+static hipError_t lse_split_dispatch(const PassShape& s, const void* Rp, const void* Cp,
+                                     const float* cbias, float c, float2* part, hipStream_t st) {
+  switch (s.kb) {
+    case 3:
+      if (s.ri == 2) lse_pipe_go<kModeSplit, 3, 2>(s, Rp, Cp, cbias, c, part, st);
+      else lse_pipe_go<kModeSplit, 3, 1>(s, Rp, Cp, cbias, c, part, st);
+      break;
+    case 6:
+      if (s.ri == 2) lse_pipe_go<kModeSplit, 6, 2>(s, Rp, Cp, cbias, c, part, st);
+      else lse_pipe_go<kModeSplit, 6, 1>(s, Rp, Cp, cbias, c, part, st);
+      break;
+    case 12:
+      lse_pipe_go<kModeSplit, 12, 1>(s, Rp, Cp, cbias, c, part, st);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 template <bool BF16>
 static hipError_t lse_dispatch(const PassShape& s, const void* Rp, const void* Cp,
                                const float* cbias, float c, float2* part, hipStream_t st) {
-  if (s.xres && lse_variant() == 2) {
+  constexpr int kMode = BF16 ? kModeBF16 : kModeF32;
+  if (s.xres) {
 #define FLASHOT_PIPE_CASE(KBV)                                      \
   case KBV:                                                         \
     if (s.ri == 2)                                                  \
-      lse_pipe_go<BF16, KBV, 2>(s, Rp, Cp, cbias, c, part, st);     \
+      lse_pipe_go<kMode, KBV, 2>(s, Rp, Cp, cbias, c, part, st);    \
     else                                                            \
-      lse_pipe_go<BF16, KBV, 1>(s, Rp, Cp, cbias, c, part, st);     \
+      lse_pipe_go<kMode, KBV, 1>(s, Rp, Cp, cbias, c, part, st);    \
     break;
     switch (s.kb) {
       FLASHOT_PIPE_CASE(1)
@@ -501,30 +654,17 @@ static hipError_t lse_dispatch(const PassShape& s, const void* Rp, const void* C
       lse_go<BF16, 8, 1, false>(s, Rp, Cp, cbias, c, part, st);
     return hipGetLastError();
   }
-#define FLASHOT_LSE_CASE(KBV)                                  \
-  case KBV:                                                    \
-    if (s.ri == 2)                                             \
-      lse_go<BF16, KBV, 2, true>(s, Rp, Cp, cbias, c, part, st); \
-    else                                                       \
-      lse_go<BF16, KBV, 1, true>(s, Rp, Cp, cbias, c, part, st); \
-    break;
-  switch (s.kb) {
-    FLASHOT_LSE_CASE(1)
-    FLASHOT_LSE_CASE(2)
-    FLASHOT_LSE_CASE(4)
-    FLASHOT_LSE_CASE(8)
-    FLASHOT_LSE_CASE(16)
-    default:
-      return hipErrorInvalidValue;
-  }
-#undef FLASHOT_LSE_CASE
   return hipGetLastError();
 }
 
-hipError_t launch_lse_partial(const PassShape& s, int bf16, const void* Rp, const void* Cp,
+hipError_t launch_lse_partial(const PassShape& s, int mode, const void* Rp, const void* Cp,
                               const float* cbias, float c, float2* part, hipStream_t st) {
-  return bf16 ? lse_dispatch<true>(s, Rp, Cp, cbias, c, part, st)
-              : lse_dispatch<false>(s, Rp, Cp, cbias, c, part, st);
+  if (mode == kModeSplit) {
+    if (!s.xres) return hipErrorInvalidValue;
+    return lse_split_dispatch(s, Rp, Cp, cbias, c, part, st);
+  }
+  return mode == kModeBF16 ? lse_dispatch<true>(s, Rp, Cp, cbias, c, part, st)
+                           : lse_dispatch<false>(s, Rp, Cp, cbias, c, part, st);
 }
 
 

@@ -27,14 +27,14 @@ def host64(t):
     return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
 
 
-def make_problem(data, eps=None, dtype=None, weights=True):
+def make_problem(data, eps=None, dtype=None, weights=True, native_f32=False):
     w = data["w"]
     dtype = dtype or w.dtype
     X = dev(data["X"], dtype)
     Y = dev(data["Y"], dtype)
     a = dev(data["a"]) if weights else None
     b = dev(data["b"]) if weights else None
-    prob = ssa.problem(X, Y, float(w.eps if eps is None else eps), a, b)
+    prob = ssa.problem(X, Y, float(w.eps if eps is None else eps), a, b, native_f32=native_f32)
     return prob
 
 

@@ -69,6 +69,7 @@ def test_workspace_query_is_host_only_and_monotone():
     ("d", 100000, ssa.OT_ERR_UNSUPPORTED),
     ("x", 0, ssa.OT_ERR_INVALID_ARG),
     ("x", (1 << 20) + 2, ssa.OT_ERR_INVALID_ARG),   # fp32 data must be 4-byte aligned
+    ("flags", 2, ssa.OT_ERR_INVALID_ARG),            # unknown problem flag
 ])
 def test_problem_validation(field, value, code):
     L = ssa.lib()
@@ -80,6 +81,18 @@ def test_problem_validation(field, value, code):
         rc, _ = _size(fn, ctypes.byref(p), None, None, None)
         assert rc == code, (field, value, rc, L.ot_last_error())
     assert L.ot_last_error()
+
+
+def test_split_and_native_workspaces_differ():
+    """fp32 points with d <= 64 pack three bf16 parts per k-block (3 KiB per 16
+    values and 32 rows) unless OT_NATIVE_F32 asks for fp32 operands (2 KiB)."""
+    L = ssa.lib()
+    p = _problem(1024, 1024, 64)
+    _, split = _size(L.ot_update_f, ctypes.byref(p), None, None, None)
+    p.flags = ssa.OT_NATIVE_F32
+    _, native = _size(L.ot_update_f, ctypes.byref(p), None, None, None)
+    tiles = 1024 // 32
+    assert split - native == 2 * tiles * (3 * 4 - 8) * 1024
 
 
 def test_null_problem_and_null_sizes():

@@ -68,12 +68,18 @@ HALF_CASES = [
 ]
 
 
+NATIVE_HALF_CASES = [c for c in HALF_CASES if c[3] == "f32" and c[2] <= 64]
+
+
+@pytest.mark.parametrize("native", [False, True])
 @pytest.mark.parametrize("n,m,d,dtype,eps", HALF_CASES)
-def test_half_steps_teacher_forced(n, m, d, dtype, eps):
-    say(f"half-steps n={n} m={m} d={d} dtype={dtype} eps={eps}")
+def test_half_steps_teacher_forced(n, m, d, dtype, eps, native):
+    if native and (n, m, d, dtype, eps) not in NATIVE_HALF_CASES:
+        pytest.skip("the fp32 matrix-instruction option only differs for fp32 points with d <= 64")
+    say(f"half-steps n={n} m={m} d={d} dtype={dtype} eps={eps} native_f32={native}")
     base = "c3_d16_bf16" if dtype == "bf16" else "c3_d16_f32"
     data = workloads.make(base, n=n, m=m, d=d)
-    prob = make_problem(data, eps=eps)
+    prob = make_problem(data, eps=eps, native_f32=native)
     X, Y, a, b = oracle_inputs(prob)
     C = oracle.cost_matrix(X, Y)
     rng = np.random.default_rng(n * 7 + m)
@@ -125,13 +131,23 @@ TRAJ_CASES = [
 ]
 
 
-@pytest.mark.parametrize("name,n,m,d,iters", TRAJ_CASES)
-def test_solve_trajectory(name, n, m, d, iters):
+TRAJ_CASES += [
+    # the same fp32 workloads formed with the fp32 matrix instruction
+    ("c1", None, None, None, None, True),
+    ("c2", 700, 555, None, None, True),
+    ("c3_d16_f32", 500, 650, None, None, True),
+]
+
+
+@pytest.mark.parametrize("case", TRAJ_CASES, ids=lambda c: "-".join(str(v) for v in c if v is not None))
+def test_solve_trajectory(case):
+    name, n, m, d, iters = case[:5]
+    native = len(case) > 5 and case[5]
     data = workloads.make(name, n=n, m=m, d=d)
     w = data["w"]
     T = w.iters if iters is None else iters
-    say(f"trajectory {name} n={w.n} m={w.m} d={w.d} dtype={w.dtype} eps={w.eps} T={T}")
-    prob = make_problem(data)
+    say(f"trajectory {name} n={w.n} m={w.m} d={w.d} dtype={w.dtype} eps={w.eps} T={T} native_f32={native}")
+    prob = make_problem(data, native_f32=native)
     X, Y, a, b = oracle_inputs(prob)
     f = zeros(w.n)
     g = zeros(w.m)
@@ -269,7 +285,9 @@ def test_single_target_point_closed_form():
     pv = ssa.ot_apply_plan(prob, f, g, V)
     torch.cuda.synchronize()
     X, Y, a, b = oracle_inputs(prob)
-    np.testing.assert_allclose(host64(pv), a[:, None] * host64(V)[0][None, :], rtol=1e-5, atol=1e-9)
+    # P V gate (1e-4): P_i1 = a_i exp(rounding of f_i/eps), and f_i carries fp32
+    # rounding of order ulp(|f|), amplified by 1/eps.
+    np.testing.assert_allclose(host64(pv), a[:, None] * host64(V)[0][None, :], rtol=PV_TOL, atol=1e-9)
     assert abs(host64(g)[0]) < 1e-5
 
 
