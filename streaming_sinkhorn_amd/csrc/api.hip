@@ -55,6 +55,7 @@ struct KConf {
   int kb;       // 1 KiB operand units per tile held in registers (3 per k-block in split mode)
   int kbp;      // padded operand units per tile
   bool xres;    // row operand resident in registers
+  bool lds;     // column tiles shared by the workgroup's waves through LDS
   int ri;       // row tiles per wave in the LSE pass
 };
 
@@ -71,7 +72,8 @@ KConf kernel_conf(int64_t d, int bf16, bool allow_split) {
     k.kb = 3 * kl;
     k.kbp = k.kb;
     k.xres = true;
-    k.ri = kl <= 2 ? 2 : 1;
+    k.lds = k.kb >= 12;
+    k.ri = 2;
   } else {
     k.mode = bf16 ? 1 : 0;
     k.kbw = bf16 ? 16 : 8;
@@ -81,7 +83,10 @@ KConf kernel_conf(int64_t d, int bf16, bool allow_split) {
       while (k.kb < k.kblocks) k.kb *= 2;
       k.kbp = k.kb;
       k.xres = true;
-      k.ri = (k.kb <= 8) ? 2 : 1;
+      // Wide fp32 tiles: share the column tile through LDS, which leaves room
+      // for two resident row tiles per wave.
+      k.lds = !bf16 && k.kb >= 8;
+      k.ri = (k.kb <= 8 || k.lds) ? 2 : 1;
     } else {
       k.kb = 8;
       k.kbp = (k.kblocks + 7) / 8 * 8;
@@ -121,6 +126,7 @@ PassShape make_pass(int rtiles, int ctiles, const KConf& k, int ri, int forced, 
   s.kbp = k.kbp;
   s.kb = k.kb;
   s.xres = k.xres;
+  s.lds = k.lds;
   s.ri = ri;
   s.nrowgroups = ceil_div(rtiles, (int64_t)kWaves * ri);
   choose_splits(s, forced, max_splits);

@@ -24,6 +24,7 @@ struct PassShape {
   int kbp;              // k-blocks per tile (padded)
   int kb;               // k-blocks held in registers at a time (1,2,4,8,16)
   bool xres;            // row operand resident in registers (kbp == kb)
+  bool lds;             // resident pass with the column tile shared through LDS
   int ri;               // 32-row tiles per wave
   int splits, tps;      // column splits and column tiles per split
   int nrowgroups;       // workgroups along the rows

@@ -475,6 +475,185 @@ __global__ __launch_bounds__(256) void lse_pipe_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// LDS-shared variant of the pipelined pass. The four waves of a workgroup
+// own different row tiles but stream the same column tiles, so each column
+// tile is fetched from L2 once per workgroup into LDS (double-buffered, one
+// barrier per stage) and every wave reads its MFMA fragments from there:
+// one quarter of the L2 traffic of per-wave loads, and the register file
+// holds row tiles instead of column buffers.
+// ---------------------------------------------------------------------------
+// Column-tile staging without branches (a branch would split the scheduled
+// region): thread t moves entries t, t + 256, ... of the tile's KB * 64
+// 16-byte entries; threads past the end re-read the last entry and write it
+// into the padding of the LDS buffer, which holds a multiple of 256 entries.
+template <int KB>
+constexpr int stage_loads() { return (KB * 64 + 255) / 256; }
+
+template <int KB>
+__device__ __forceinline__ void stage_load(const u32x4* __restrict__ Cp, int jt, int tid,
+                                           u32x4 (&g)[stage_loads<KB>()]) {
+#pragma unroll
+  for (int i = 0; i < stage_loads<KB>(); ++i)
+    g[i] = Cp[(size_t)jt * KB * 64 + min(tid + 256 * i, KB * 64 - 1)];
+}
+
+template <int KB>
+__device__ __forceinline__ void stage_store(u32x4* __restrict__ buf, int tid,
+                                            const u32x4 (&g)[stage_loads<KB>()]) {
+#pragma unroll
+  for (int i = 0; i < stage_loads<KB>(); ++i) buf[tid + 256 * i] = g[i];
+}
+
+template <int MODE, int KB, int RI>
+__device__ __forceinline__ void score_tile_lds(const u32x4* __restrict__ buf, int lane,
+                                               const u32x4 (&xr)[RI][KB], float wv, int h,
+                                               const float (&Mf)[RI], f32x16 (&acc)[RI]) {
+#pragma unroll
+  for (int ri = 0; ri < RI; ++ri) acc[ri] = f32x16{};
+  if constexpr (MODE == kModeSplit) {
+#pragma unroll
+    for (int kb = 0; kb < KB; kb += 3) {
+      u32x4 y[3];
+#pragma unroll
+      for (int q = 0; q < 3; ++q) y[q] = buf[(kb + q) * 64 + lane];
+#pragma unroll
+      for (int ri = 0; ri < RI; ++ri) acc[ri] = mfma_split(y, &xr[ri][kb], acc[ri]);
+    }
+  } else {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const u32x4 y = buf[kb * 64 + lane];
+#pragma unroll
+      for (int ri = 0; ri < RI; ++ri)
+        acc[ri] = mfma_kblock<MODE == kModeBF16>(y, xr[ri][kb], acc[ri]);
+    }
+  }
+#pragma unroll
+  for (int ri = 0; ri < RI; ++ri)
+    acc[ri] = __builtin_amdgcn_mfma_f32_32x32x2f32(h ? 1.0f : wv, h ? -Mf[ri] : 1.0f, acc[ri],
+                                                   0, 0, 0);
+}
+
+template <int MODE, int KB, int RI>
+__device__ __forceinline__ void stage_schedule_lds() {
+  constexpr int kPerUnit = MODE == kModeF32 ? 4 : (MODE == kModeBF16 ? 1 : 2);
+  constexpr int kMfma = RI * (KB * kPerUnit + 1);
+  constexpr int kValu = RI * (MODE == kModeBF16 ? 40 : 24);
+  constexpr int kValuPer = (kValu + kMfma - 1) / kMfma;
+  constexpr int kLoads = stage_loads<KB>();
+  __builtin_amdgcn_sched_group_barrier(0x020, kLoads + 1, 0);  // next tile + bias from L2
+#pragma unroll
+  for (int i = 0; i < kMfma; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);         // LDS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, kValuPer, 0);  // VALU
+  }
+  __builtin_amdgcn_sched_group_barrier(0x200, kLoads, 0);      // LDS write of the next tile
+}
+
+template <int MODE, int KB, int RI>
+__global__ __launch_bounds__(256) void lse_lds_kernel(
+    const u32x4* __restrict__ Rp, const u32x4* __restrict__ Cp, const float* __restrict__ cbias,
+    int rtiles, int ctiles, int splits, int tps, float c, float2* __restrict__ part, int rpad) {
+  constexpr int kLoads = stage_loads<KB>();
+  __shared__ u32x4 lds[2][kLoads * 256];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int h = lane >> 5;
+  const int s = blockIdx.x % splits;
+  const int rg = blockIdx.x / splits;
+  const int rt0 = (rg * kWaves + wave) * RI;  // may be past the last row tile: the wave still
+                                              // takes part in loads and barriers
+  const int jt0 = s * tps;
+  const int last = min(jt0 + tps, ctiles) - 1 - jt0;
+  const float ks = MODE == kModeBF16 ? c : 1.0f;
+
+  u32x4 xr[RI][KB];
+#pragma unroll
+  for (int ri = 0; ri < RI; ++ri) {
+    const int rt = min(rt0 + ri, rtiles - 1);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) xr[ri][kb] = Rp[((size_t)rt * KB + kb) * 64 + lane];
+  }
+  float M[RI], S[RI];
+#pragma unroll
+  for (int ri = 0; ri < RI; ++ri) {
+    M[ri] = kUnset;
+    S[ri] = 0.f;
+  }
+
+  u32x4 g[kLoads];
+  stage_load<KB>(Cp, jt0, tid, g);
+  stage_store<KB>(lds[0], tid, g);
+  stage_load<KB>(Cp, jt0 + min(1, last), tid, g);
+  stage_store<KB>(lds[1], tid, g);
+  float wA = cbias[jt0 * kTile + (lane & 31)];
+  float wB = cbias[(jt0 + min(1, last)) * kTile + (lane & 31)];
+  __syncthreads();
+
+  // Invariant at stage k: accA / accB alternate holding the scores of tile k;
+  // LDS buffer (k + 1) & 1 holds tile k+1; buffer k & 1 is free once every
+  // wave has passed the stage barrier.
+  f32x16 accA[RI], accB[RI];
+  float MfA[RI], MfB[RI];
+#pragma unroll
+  for (int ri = 0; ri < RI; ++ri) MfA[ri] = 0.f;
+  score_tile_lds<MODE, KB, RI>(lds[0], lane, xr, wA, h, MfA, accA);
+
+  auto stage = [&](int k, f32x16(&accN)[RI], float(&MfN)[RI], float& wN, const f32x16(&accC)[RI],
+                   const float(&MfC)[RI], float& wC) {
+    __syncthreads();  // tile k+1 is in LDS; every wave is done reading tile k's buffer
+    const int jt2 = jt0 + min(k + 2, last);
+    stage_load<KB>(Cp, jt2, tid, g);
+    const float w2 = cbias[jt2 * kTile + (lane & 31)];
+#pragma unroll
+    for (int ri = 0; ri < RI; ++ri) MfN[ri] = fold_of(M[ri]);
+    score_tile_lds<MODE, KB, RI>(lds[(k + 1) & 1], lane, xr, wN, h, MfN, accN);
+    float Sn[RI];
+    bool slow = false;
+#pragma unroll
+    for (int ri = 0; ri < RI; ++ri)
+      slow |= lse_fast<MODE != kModeBF16>(accC[ri], MfC[ri], M[ri], S[ri], ks, Sn[ri]);
+    stage_store<KB>(lds[k & 1], tid, g);
+    wC = w2;  // the buffer of tile k now receives tile k+2
+    stage_schedule_lds<MODE, KB, RI>();
+    __builtin_amdgcn_sched_barrier(0);
+    if (__builtin_amdgcn_ballot_w64(slow) != 0) {
+#pragma unroll
+      for (int ri = 0; ri < RI; ++ri) lse_exact(accC[ri], MfC[ri], M[ri], S[ri], ks);
+    } else {
+#pragma unroll
+      for (int ri = 0; ri < RI; ++ri) S[ri] = Sn[ri];
+    }
+  };
+
+  int k = 0;
+  for (; k + 2 <= last; k += 2) {
+    stage(k, accB, MfB, wB, accA, MfA, wA);
+    stage(k + 1, accA, MfA, wA, accB, MfB, wB);
+  }
+  if (k + 1 <= last) {  // tiles k and k+1 remain; tile k+1 is in buffer (k+1)&1
+    __syncthreads();
+#pragma unroll
+    for (int ri = 0; ri < RI; ++ri) MfB[ri] = fold_of(M[ri]);
+    score_tile_lds<MODE, KB, RI>(lds[(k + 1) & 1], lane, xr, wB, h, MfB, accB);
+    lse_tail<MODE, RI>(accA, MfA, M, S, ks);
+    lse_tail<MODE, RI>(accB, MfB, M, S, ks);
+  } else {
+    lse_tail<MODE, RI>(accA, MfA, M, S, ks);
+  }
+
+#pragma unroll
+  for (int ri = 0; ri < RI; ++ri) {
+    const float St = S[ri] + __shfl_xor(S[ri], 32);
+    if (h == 0 && rt0 + ri < rtiles)
+      part[(size_t)s * rpad + (size_t)(rt0 + ri) * kTile + (lane & 31)] =
+          make_float2(ks * M[ri], St);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Streamed transport application partials (Algorithm 2 / 4 of the page).
 // Per split s and row i: (M, S) as in the LSE pass, and
 //   O[p] = sum_j exp2(c (v_ij - M)) V[j][p]
@@ -603,22 +782,33 @@ static void lse_pipe_go(const PassShape& s, const void* Rp, const void* Cp, cons
       s.rtiles * kTile);
 }
 
+template <int MODE, int KB, int RI>
+static void lse_lds_go(const PassShape& s, const void* Rp, const void* Cp, const float* cbias,
+                       float c, float2* part, hipStream_t st) {
+  lse_lds_kernel<MODE, KB, RI><<<s.nrowgroups * s.splits, 256, 0, st>>>(
+      (const u32x4*)Rp, (const u32x4*)Cp, cbias, s.rtiles, s.ctiles, s.splits, s.tps, c, part,
+      s.rtiles * kTile);
+}
+
+template <int MODE, int KB>
+static void resident_go(const PassShape& s, const void* Rp, const void* Cp, const float* cbias,
+                        float c, float2* part, hipStream_t st) {
+  if (s.lds) {
+    if (s.ri == 2) lse_lds_go<MODE, KB, 2>(s, Rp, Cp, cbias, c, part, st);
+    else lse_lds_go<MODE, KB, 1>(s, Rp, Cp, cbias, c, part, st);
+  } else {
+    if (s.ri == 2) lse_pipe_go<MODE, KB, 2>(s, Rp, Cp, cbias, c, part, st);
+    else lse_pipe_go<MODE, KB, 1>(s, Rp, Cp, cbias, c, part, st);
+  }
+}
+
 static hipError_t lse_split_dispatch(const PassShape& s, const void* Rp, const void* Cp,
                                      const float* cbias, float c, float2* part, hipStream_t st) {
   switch (s.kb) {
-    case 3:
-      if (s.ri == 2) lse_pipe_go<kModeSplit, 3, 2>(s, Rp, Cp, cbias, c, part, st);
-      else lse_pipe_go<kModeSplit, 3, 1>(s, Rp, Cp, cbias, c, part, st);
-      break;
-    case 6:
-      if (s.ri == 2) lse_pipe_go<kModeSplit, 6, 2>(s, Rp, Cp, cbias, c, part, st);
-      else lse_pipe_go<kModeSplit, 6, 1>(s, Rp, Cp, cbias, c, part, st);
-      break;
-    case 12:
-      lse_pipe_go<kModeSplit, 12, 1>(s, Rp, Cp, cbias, c, part, st);
-      break;
-    default:
-      return hipErrorInvalidValue;
+    case 3: resident_go<kModeSplit, 3>(s, Rp, Cp, cbias, c, part, st); break;
+    case 6: resident_go<kModeSplit, 6>(s, Rp, Cp, cbias, c, part, st); break;
+    case 12: resident_go<kModeSplit, 12>(s, Rp, Cp, cbias, c, part, st); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
@@ -628,32 +818,20 @@ static hipError_t lse_dispatch(const PassShape& s, const void* Rp, const void* C
                                const float* cbias, float c, float2* part, hipStream_t st) {
   constexpr int kMode = BF16 ? kModeBF16 : kModeF32;
   if (s.xres) {
-#define FLASHOT_PIPE_CASE(KBV)                                      \
-  case KBV:                                                         \
-    if (s.ri == 2)                                                  \
-      lse_pipe_go<kMode, KBV, 2>(s, Rp, Cp, cbias, c, part, st);    \
-    else                                                            \
-      lse_pipe_go<kMode, KBV, 1>(s, Rp, Cp, cbias, c, part, st);    \
-    break;
     switch (s.kb) {
-      FLASHOT_PIPE_CASE(1)
-      FLASHOT_PIPE_CASE(2)
-      FLASHOT_PIPE_CASE(4)
-      FLASHOT_PIPE_CASE(8)
-      FLASHOT_PIPE_CASE(16)
-      default:
-        return hipErrorInvalidValue;
+      case 1: resident_go<kMode, 1>(s, Rp, Cp, cbias, c, part, st); break;
+      case 2: resident_go<kMode, 2>(s, Rp, Cp, cbias, c, part, st); break;
+      case 4: resident_go<kMode, 4>(s, Rp, Cp, cbias, c, part, st); break;
+      case 8: resident_go<kMode, 8>(s, Rp, Cp, cbias, c, part, st); break;
+      case 16: resident_go<kMode, 16>(s, Rp, Cp, cbias, c, part, st); break;
+      default: return hipErrorInvalidValue;
     }
-#undef FLASHOT_PIPE_CASE
     return hipGetLastError();
   }
-  if (!s.xres) {
-    if (s.ri == 2)
-      lse_go<BF16, 8, 2, false>(s, Rp, Cp, cbias, c, part, st);
-    else
-      lse_go<BF16, 8, 1, false>(s, Rp, Cp, cbias, c, part, st);
-    return hipGetLastError();
-  }
+  if (s.ri == 2)
+    lse_go<BF16, 8, 2, false>(s, Rp, Cp, cbias, c, part, st);
+  else
+    lse_go<BF16, 8, 1, false>(s, Rp, Cp, cbias, c, part, st);
   return hipGetLastError();
 }
 
