@@ -54,18 +54,23 @@ ALU_PAIRS_PEAK = ALU_LANE_SLOTS_PER_S / ALU_SLOTS_PER_PAIR
 # FETCH_SIZE / WRITE_SIZE runs (scaled by the copy-kernel calibration), valid
 # only for the kernel source they were taken on.
 TRAFFIC = {
-    "c2": {"kernels_sha256": "200de97431eb9d8ec6b8054aaa87f50cae1c0b025cbfc185a79210a01628c819",
-           "bytes_per_launch": 51408528,
-           "source": "profiles/lse_pipe_c2_n20000_d64_f32_hbm_traffic.md"},
+    "c2": {"kernels_sha256": "bf23cc05854c547d44de565b26cc393094af7d3c0897319c42e1ac459592c278",
+           "bytes_per_launch": 74474247,
+           "source": "profiles/lse_lds_kernel_c2_n20000_d64_f32split_hbm_traffic.md"},
 }
-KERNEL_SRC = os.path.join(ROOT, "streaming_sinkhorn_amd", "csrc", "kernels.hip")
+# Sources of the register-resident log-sum-exp kernels the counters describe.
+KERNEL_SRCS = [os.path.join(ROOT, "streaming_sinkhorn_amd", "csrc", f)
+               for f in ("kernels.hip", "device_common.h")]
 
 METRIC = "Sinkhorn n*m*iters/sec + % MFMA/exp roofline at n=m=20k, d=64, eps=0.1"
 
 
 def kernel_sha():
-    with open(KERNEL_SRC, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
 
 
 def traffic_for(workload):
@@ -238,7 +243,7 @@ def main():
         per_launch = {"algorithmic_pairs_per_launch": pairs}
     per_launch["fp32_equivalent_tflops"] = alg_flops / avg_lse_s / 1e12
     roof["traffic"] = traffic_for(args.workload)
-    roof.update({"kernel": "lse_partial_kernel", "avg_launch_us": avg_lse_s * 1e6,
+    roof.update({"kernel": "streamed log-sum-exp pass (lse_*_kernel)", "avg_launch_us": avg_lse_s * 1e6,
                  "launches": lse_n, **per_launch})
     last = infos[-1]
     outputs = ["f", "g", "marginal errors"]

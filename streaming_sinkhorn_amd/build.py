@@ -26,12 +26,18 @@ COMMON = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
-# Hot-loop kernels only (kernels.hip): MFMA results in ordinary VGPRs (the LSE
+# Streamed kernels only (kernels*.hip, apply_kernels.hip): MFMA results in ordinary VGPRs (the LSE
 # reads them with the VALU right away) and no NaN canonicalisation around
 # fmaxf. The auxiliary kernels keep full NaN semantics.
 KERNEL_FLAGS = ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 
-SOURCES = [("kernels.hip", KERNEL_FLAGS), ("aux_kernels.hip", []), ("api.hip", [])]
+SOURCES = [
+    ("kernels.hip", KERNEL_FLAGS),
+    ("kernels_wide.hip", KERNEL_FLAGS),
+    ("apply_kernels.hip", KERNEL_FLAGS),
+    ("aux_kernels.hip", []),
+    ("api.hip", []),
+]
 
 
 def _run(cmd):

@@ -1,0 +1,193 @@
+// Device helpers shared by the streamed kernels of the Sinkhorn solver
+// (score tiles on the matrix cores, online log-sum-exp steps). Internal.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace flashot {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// One packed k-block of the score tile: acc[j][i] += sum_k A[j][k] B[k][i].
+template <bool BF16>
+__device__ __forceinline__ f32x16 mfma_kblock(u32x4 a, u32x4 b, f32x16 acc) {
+  if constexpr (BF16) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+  } else {
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0,
+                                               0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0,
+                                               0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0,
+                                               0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0,
+                                               0, 0);
+    return acc;
+  }
+}
+
+// Operand modes of the register-resident pass.
+constexpr int kModeF32 = 0;    // fp32 operands, fp32 MFMA (32x32x2)
+constexpr int kModeBF16 = 1;   // bf16 operands, bf16 MFMA (32x32x16)
+constexpr int kModeSplit = 2;  // fp32 operands as hi + mid + lo bf16 parts, bf16 MFMA
+
+// One k-block of 16 fp32 values held as three bf16 parts per operand
+// (v = hi + mid + lo, each part the bf16 rounding of what the previous ones
+// left, so |mid| <= 2^-9 |v| and |lo| <= 2^-18 |v|). Six partial products are
+// accumulated, smallest first; the three dropped ones (mid*lo, lo*mid, lo*lo)
+// are below 2^-26 of |x y|, finer than fp32 rounding.
+__device__ __forceinline__ f32x16 mfma_split(const u32x4* y, const u32x4* x, f32x16 acc) {
+  auto m = [](u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  };
+  acc = m(y[2], x[0], acc);  // lo * hi
+  acc = m(y[0], x[2], acc);  // hi * lo
+  acc = m(y[1], x[1], acc);  // mid * mid
+  acc = m(y[1], x[0], acc);  // mid * hi
+  acc = m(y[0], x[1], acc);  // hi * mid
+  return m(y[0], x[0], acc); // hi * hi
+}
+
+// Adds bias_j to every accumulator entry of column j: k-slot 0 carries
+// (bias_j, 1), k-slot 1 carries (0, 1).
+__device__ __forceinline__ f32x16 mfma_bias(float wv, int h, f32x16 acc) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(h ? 0.0f : wv, 1.0f, acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ float max16(const f32x16& v) {
+  float a = fmaxf(fmaxf(v[0], v[1]), v[2]);
+  float b = fmaxf(fmaxf(v[3], v[4]), v[5]);
+  float d = fmaxf(fmaxf(v[6], v[7]), v[8]);
+  float e = fmaxf(fmaxf(v[9], v[10]), v[11]);
+  float f = fmaxf(fmaxf(v[12], v[13]), v[14]);
+  return fmaxf(fmaxf(a, b), fmaxf(fmaxf(d, e), fmaxf(f, v[15])));
+}
+
+// Online LSE step of App. D.3 on 16 scores of one row, in "dot-product units":
+// the natural-log score is (2/eps) * v, and c = 2 log2(e) / eps, so
+// exp(score - max) = exp2(c * (v - M)).
+__device__ __forceinline__ void lse_tile(const f32x16& v, float& M, float& S, float c) {
+  const float Mn = fmaxf(M, max16(v));
+  const float cm = c * Mn;
+  const float sc = __builtin_amdgcn_exp2f(fmaf(c, M, -cm));
+  float s0 = __builtin_amdgcn_exp2f(fmaf(c, v[0], -cm));
+  float s1 = __builtin_amdgcn_exp2f(fmaf(c, v[1], -cm));
+  float s2 = __builtin_amdgcn_exp2f(fmaf(c, v[2], -cm));
+  float s3 = __builtin_amdgcn_exp2f(fmaf(c, v[3], -cm));
+#pragma unroll
+  for (int r = 4; r < 16; r += 4) {
+    s0 += __builtin_amdgcn_exp2f(fmaf(c, v[r + 0], -cm));
+    s1 += __builtin_amdgcn_exp2f(fmaf(c, v[r + 1], -cm));
+    s2 += __builtin_amdgcn_exp2f(fmaf(c, v[r + 2], -cm));
+    s3 += __builtin_amdgcn_exp2f(fmaf(c, v[r + 3], -cm));
+  }
+  S = fmaf(S, sc, (s0 + s1) + (s2 + s3));
+  M = Mn;
+}
+
+// ---------------------------------------------------------------------------
+// Software-pipelined register-resident pass with a lazily raised stabiliser.
+//
+// Pipelining: each wave keeps two score tiles in flight. While the matrix
+// cores form the scores of column tile t+1, the vector unit exponentiates
+// tile t. The column operand alternates between two register buffers (the
+// loop body is written twice with the roles swapped), so a prefetched tile is
+// never copied between registers.
+//
+// Lazy stabiliser: the online LSE of App. D.3 is exact for any running
+// stabiliser M, not only for the running maximum. The bias MFMA uses its
+// second k-slot to subtract M_i from every score (A = [bias_j, 1],
+// B = [1, -M_i]), so in the common case a tile costs one exp2 and one add per
+// score. Only when a tile could overflow (tile sum >= 2^64), or before M has
+// been set from data, does the wave take the exact path: tile maximum, raise
+// M, rescale S. M is kept identical in the two lanes (l, l ^ 32) that share a
+// row, because the bias MFMA reads it from lane l + 32.
+//
+// Units: for fp32 inputs the row operand X is packed pre-multiplied by
+// c = 2 log2(e) / eps and the biases are written in the same units, so scores
+// are log2 values and exp2 needs no multiply (KS = 1). bf16 operands cannot be
+// rescaled without rounding, so their scores stay in dot-product units and
+// are multiplied by c before exp2 (KS = c). Partials are written in log2
+// units: LSE_row = ln 2 * (M2 + log2 S).
+// ---------------------------------------------------------------------------
+constexpr float kUnset = -1.0e30f;  // stabiliser not yet taken from data
+
+// KB counts 1 KiB operand units per tile: one per k-block for fp32 / bf16,
+// three (hi, mid, lo) per k-block in split mode.
+template <int MODE, int KB, int RI>
+__device__ __forceinline__ void score_tile(const u32x4 (&y)[KB], const u32x4 (&xr)[RI][KB],
+                                           float wv, int h, const float (&Mf)[RI],
+                                           f32x16 (&acc)[RI]) {
+#pragma unroll
+  for (int ri = 0; ri < RI; ++ri) acc[ri] = f32x16{};
+  if constexpr (MODE == kModeSplit) {
+#pragma unroll
+    for (int kb = 0; kb < KB; kb += 3)
+#pragma unroll
+      for (int ri = 0; ri < RI; ++ri) acc[ri] = mfma_split(&y[kb], &xr[ri][kb], acc[ri]);
+  } else {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int ri = 0; ri < RI; ++ri)
+        acc[ri] = mfma_kblock<MODE == kModeBF16>(y[kb], xr[ri][kb], acc[ri]);
+  }
+#pragma unroll
+  for (int ri = 0; ri < RI; ++ri)
+    acc[ri] = __builtin_amdgcn_mfma_f32_32x32x2f32(h ? 1.0f : wv, h ? -Mf[ri] : 1.0f, acc[ri],
+                                                   0, 0, 0);
+}
+
+// Stabiliser folded into the next tile's scores: the running M once set.
+__device__ __forceinline__ float fold_of(float M) { return M > 0.5f * kUnset ? M : 0.f; }
+
+// Common-case tile: s = sum exp2(ks * a_r) relative to the folded Mf; returns
+// the candidate new S and whether the exact path is needed.
+template <bool SCALED>
+__device__ __forceinline__ bool lse_fast(const f32x16& a, float Mf, float M, float S, float ks,
+                                         float& Snew) {
+  float e0 = __builtin_amdgcn_exp2f(SCALED ? a[0] : ks * a[0]);
+  float e1 = __builtin_amdgcn_exp2f(SCALED ? a[1] : ks * a[1]);
+  float e2 = __builtin_amdgcn_exp2f(SCALED ? a[2] : ks * a[2]);
+  float e3 = __builtin_amdgcn_exp2f(SCALED ? a[3] : ks * a[3]);
+#pragma unroll
+  for (int r = 4; r < 16; r += 4) {
+    e0 += __builtin_amdgcn_exp2f(SCALED ? a[r + 0] : ks * a[r + 0]);
+    e1 += __builtin_amdgcn_exp2f(SCALED ? a[r + 1] : ks * a[r + 1]);
+    e2 += __builtin_amdgcn_exp2f(SCALED ? a[r + 2] : ks * a[r + 2]);
+    e3 += __builtin_amdgcn_exp2f(SCALED ? a[r + 3] : ks * a[r + 3]);
+  }
+  const float s = (e0 + e1) + (e2 + e3);
+  Snew = fmaf(s, __builtin_amdgcn_exp2f(ks * (Mf - M)), S);
+  return !(s < 0x1p64f) || !(Snew >= 0x1p-64f) || !(M > 0.5f * kUnset);
+}
+
+// Exact tile: raise M to the tile maximum (shared by the lane pair), rescale.
+__device__ __forceinline__ void lse_exact(const f32x16& a, float Mf, float& M, float& S,
+                                          float ks) {
+  float m = max16(a) + Mf;
+  m = fmaxf(m, __shfl_xor(m, 32));
+  m = fmaxf(m, M);
+  const float t = Mf - m;
+  float e0 = 0.f, e1 = 0.f, e2 = 0.f, e3 = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; r += 4) {
+    e0 += __builtin_amdgcn_exp2f(ks * (a[r + 0] + t));
+    e1 += __builtin_amdgcn_exp2f(ks * (a[r + 1] + t));
+    e2 += __builtin_amdgcn_exp2f(ks * (a[r + 2] + t));
+    e3 += __builtin_amdgcn_exp2f(ks * (a[r + 3] + t));
+  }
+  S = fmaf(S, __builtin_amdgcn_exp2f(ks * (M - m)), (e0 + e1) + (e2 + e3));
+  M = m;
+}
+
+}  // namespace flashot

@@ -1,5 +1,6 @@
 // Internal interface between the host driver (api.hip) and the gfx950 kernels
-// (kernels.hip). Not part of the public C ABI.
+// (kernels.hip, kernels_wide.hip, apply_kernels.hip, aux_kernels.hip). Not
+// part of the public C ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -47,8 +48,16 @@ hipError_t launch_fill(float* p, float v, int64_t count, hipStream_t st);
 hipError_t launch_bias_from_pot(const float* pot, const float* norm, const float* hlw, int rows,
                                 int rpad, float bscale, float* bias, hipStream_t st);
 // mode: 0 fp32 operands, 1 bf16 operands, 2 fp32 operands packed as three bf16 parts.
-hipError_t launch_lse_partial(const PassShape& s, int mode, const void* Rp, const void* Cp,
-                              const float* cbias, float c, float2* part, hipStream_t st);
+// Register-resident passes (s.xres, kernels.hip) and k-chunked wide passes (kernels_wide.hip).
+hipError_t launch_lse_resident(const PassShape& s, int mode, const void* Rp, const void* Cp,
+                               const float* cbias, float c, float2* part, hipStream_t st);
+hipError_t launch_lse_wide(const PassShape& s, int mode, const void* Rp, const void* Cp,
+                           const float* cbias, float c, float2* part, hipStream_t st);
+inline hipError_t launch_lse_partial(const PassShape& s, int mode, const void* Rp, const void* Cp,
+                                     const float* cbias, float c, float2* part, hipStream_t st) {
+  return s.xres ? launch_lse_resident(s, mode, Rp, Cp, cbias, c, part, st)
+                : launch_lse_wide(s, mode, Rp, Cp, cbias, c, part, st);
+}
 hipError_t launch_lse_merge(const float2* part, int splits, int rpad, int rows, float bscale, float eps,
                             const float* norm, const float* hlw, const float* wgt, float* pot,
                             float* bias_out, float* err_part, int with_err, int write_pot,
