@@ -57,13 +57,22 @@ struct KConf {
   bool xres;    // row operand resident in registers
   bool lds;     // column tiles shared by the workgroup's waves through LDS
   int ri;       // row tiles per wave in the LSE pass
+  int ct, bk;   // tiled wide pass: column tiles per block, k-blocks per LDS stage
 };
 
-// Split mode (fp32 inputs on the bf16 matrix cores) is used by the
-// log-sum-exp passes for d <= 64 unless the problem asks for native fp32.
-KConf kernel_conf(int64_t d, int bf16, bool allow_split) {
+// Operand layout and pass shape for a point dimension / storage type.
+//  - fp32 points use the three-part bf16 split unless the problem asks for
+//    native fp32 (allow_split false) or d is between 64 and 128, where the
+//    register-resident fp32 pass is faster;
+//  - d <= 128 fp32 / 256 bf16 / 64 split: register-resident rows;
+//  - wider: the tiled pass (column blocks of ct tiles, LDS stages of bk
+//    k-blocks), with the units per tile padded to whole stages.
+// Transport application keeps its own layout (for_apply): fp32 or bf16
+// operands, chunks of 8 k-blocks when the row operand is not resident.
+KConf kernel_conf(int64_t d, int bf16, bool allow_split, bool for_apply = false) {
   KConf k{};
-  if (!bf16 && allow_split && d <= 64) {
+  const bool split = !bf16 && allow_split && !for_apply && (d <= 64 || d > 128);
+  if (split && d <= 64) {
     k.mode = 2;
     k.kbw = 16;
     k.kblocks = ceil_div(d, 16);
@@ -75,10 +84,10 @@ KConf kernel_conf(int64_t d, int bf16, bool allow_split) {
     k.lds = k.kb >= 12;
     k.ri = 2;
   } else {
-    k.mode = bf16 ? 1 : 0;
-    k.kbw = bf16 ? 16 : 8;
+    k.mode = split ? 2 : (bf16 ? 1 : 0);
+    k.kbw = (bf16 || split) ? 16 : 8;
     k.kblocks = ceil_div(d, k.kbw);
-    if (k.kblocks <= 16) {
+    if (!split && k.kblocks <= 16) {
       k.kb = 1;
       while (k.kb < k.kblocks) k.kb *= 2;
       k.kbp = k.kb;
@@ -87,36 +96,47 @@ KConf kernel_conf(int64_t d, int bf16, bool allow_split) {
       // for two resident row tiles per wave.
       k.lds = !bf16 && k.kb >= 8;
       k.ri = (k.kb <= 8 || k.lds) ? 2 : 1;
-    } else {
+    } else if (for_apply) {
       k.kb = 8;
       k.kbp = (k.kblocks + 7) / 8 * 8;
       k.xres = false;
+      k.ri = 1;
+    } else {
+      const int ku = k.mode == 2 ? 3 : 1;
       k.ri = 2;
+      k.ct = k.mode == 2 ? 2 : 4;
+      k.bk = k.mode == 2 ? 1 : 2;
+      k.kb = k.bk * ku;
+      k.kbp = ceil_div(k.kblocks, k.bk) * k.bk * ku;
+      k.xres = false;
     }
   }
   const int ri_env = env_int("FLASHOT_RI", 0);
-  if (ri_env == 1 || ri_env == 2) k.ri = ri_env;
+  if (k.xres && (ri_env == 1 || ri_env == 2)) k.ri = ri_env;
   return k;
 }
 
 // Column splits: enough workgroups to fill 256 CUs several times over, at
 // least ~4 column tiles per split, a multiple of 8 when large (XCD locality).
-void choose_splits(PassShape& s, int forced, int max_splits) {
+// Column splits: enough workgroups to fill 256 CUs several times over, at
+// least ~4 column units (tiles, or blocks of the wide pass) per split, a
+// multiple of 8 when large (XCD locality).
+void choose_splits(PassShape& s, int cunits, int forced, int max_splits) {
   int S;
   if (forced > 0) {
     S = forced;
   } else {
     const int target = env_int("FLASHOT_TARGET_WG", 2048);
     S = ceil_div(target, s.nrowgroups);
-    const int most = s.ctiles / 4 > 1 ? s.ctiles / 4 : 1;
+    const int most = cunits / 4 > 1 ? cunits / 4 : 1;
     if (S > most) S = most;
     if (S >= 8) S = (S + 7) / 8 * 8;
   }
   if (S > max_splits) S = max_splits;
-  if (S > s.ctiles) S = s.ctiles;
+  if (S > cunits) S = cunits;
   if (S < 1) S = 1;
-  s.tps = ceil_div(s.ctiles, S);
-  s.splits = ceil_div(s.ctiles, s.tps);
+  s.tps = ceil_div(cunits, S);
+  s.splits = ceil_div(cunits, s.tps);
 }
 
 PassShape make_pass(int rtiles, int ctiles, const KConf& k, int ri, int forced, int max_splits) {
@@ -128,8 +148,11 @@ PassShape make_pass(int rtiles, int ctiles, const KConf& k, int ri, int forced, 
   s.xres = k.xres;
   s.lds = k.lds;
   s.ri = ri;
+  s.ct = k.ct;
+  s.bk = k.bk;
   s.nrowgroups = ceil_div(rtiles, (int64_t)kWaves * ri);
-  choose_splits(s, forced, max_splits);
+  const int cunits = (k.xres || k.ct == 0) ? ctiles : ceil_div(ctiles, k.ct);
+  choose_splits(s, cunits, forced, max_splits);
   return s;
 }
 
@@ -481,7 +504,7 @@ struct ApplyWs {
 
 ApplyWs apply_layout(const ot_problem* p, int64_t cols, bool transpose) {
   ApplyWs w{};
-  w.k = kernel_conf(p->d, p->dtype == OT_BF16, false);
+  w.k = kernel_conf(p->d, p->dtype == OT_BF16, false, true);
   const int64_t rows = transpose ? p->m : p->n;
   const int64_t strm = transpose ? p->n : p->m;
   w.rtiles = ceil_div(rows, kTile);

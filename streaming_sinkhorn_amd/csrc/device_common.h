@@ -72,28 +72,6 @@ __device__ __forceinline__ float max16(const f32x16& v) {
   return fmaxf(fmaxf(a, b), fmaxf(fmaxf(d, e), fmaxf(f, v[15])));
 }
 
-// Online LSE step of App. D.3 on 16 scores of one row, in "dot-product units":
-// the natural-log score is (2/eps) * v, and c = 2 log2(e) / eps, so
-// exp(score - max) = exp2(c * (v - M)).
-__device__ __forceinline__ void lse_tile(const f32x16& v, float& M, float& S, float c) {
-  const float Mn = fmaxf(M, max16(v));
-  const float cm = c * Mn;
-  const float sc = __builtin_amdgcn_exp2f(fmaf(c, M, -cm));
-  float s0 = __builtin_amdgcn_exp2f(fmaf(c, v[0], -cm));
-  float s1 = __builtin_amdgcn_exp2f(fmaf(c, v[1], -cm));
-  float s2 = __builtin_amdgcn_exp2f(fmaf(c, v[2], -cm));
-  float s3 = __builtin_amdgcn_exp2f(fmaf(c, v[3], -cm));
-#pragma unroll
-  for (int r = 4; r < 16; r += 4) {
-    s0 += __builtin_amdgcn_exp2f(fmaf(c, v[r + 0], -cm));
-    s1 += __builtin_amdgcn_exp2f(fmaf(c, v[r + 1], -cm));
-    s2 += __builtin_amdgcn_exp2f(fmaf(c, v[r + 2], -cm));
-    s3 += __builtin_amdgcn_exp2f(fmaf(c, v[r + 3], -cm));
-  }
-  S = fmaf(S, sc, (s0 + s1) + (s2 + s3));
-  M = Mn;
-}
-
 // ---------------------------------------------------------------------------
 // Software-pipelined register-resident pass with a lazily raised stabiliser.
 //
@@ -168,7 +146,10 @@ __device__ __forceinline__ bool lse_fast(const f32x16& a, float Mf, float M, flo
   }
   const float s = (e0 + e1) + (e2 + e3);
   Snew = fmaf(s, __builtin_amdgcn_exp2f(ks * (Mf - M)), S);
-  return !(s < 0x1p64f) || !(Snew >= 0x1p-64f) || !(M > 0.5f * kUnset);
+  // Exact path when: the tile could overflow; the stabiliser is not set; or the
+  // tile was folded before it was set (Mf = 0 above a lower M), where the
+  // rescale factor itself could overflow.
+  return !(s < 0x1p64f) || !(Snew >= 0x1p-64f) || !(M > 0.5f * kUnset) || !(Mf <= M);
 }
 
 // Exact tile: raise M to the tile maximum (shared by the lane pair), rescale.
@@ -188,6 +169,24 @@ __device__ __forceinline__ void lse_exact(const f32x16& a, float Mf, float& M, f
   }
   S = fmaf(S, __builtin_amdgcn_exp2f(ks * (M - m)), (e0 + e1) + (e2 + e3));
   M = m;
+}
+
+// Online LSE of RI score tiles (one per row tile) outside a scheduled
+// pipeline stage: common case, or the exact path for the whole wave.
+template <int MODE, int RI>
+__device__ __forceinline__ void lse_tail(const f32x16 (&acc)[RI], const float (&Mf)[RI],
+                                         float (&M)[RI], float (&S)[RI], float ks) {
+  float Sn[RI];
+  bool slow = false;
+#pragma unroll
+  for (int ri = 0; ri < RI; ++ri) slow |= lse_fast<MODE != kModeBF16>(acc[ri], Mf[ri], M[ri], S[ri], ks, Sn[ri]);
+  if (__builtin_amdgcn_ballot_w64(slow) != 0) {
+#pragma unroll
+    for (int ri = 0; ri < RI; ++ri) lse_exact(acc[ri], Mf[ri], M[ri], S[ri], ks);
+  } else {
+#pragma unroll
+    for (int ri = 0; ri < RI; ++ri) S[ri] = Sn[ri];
+  }
 }
 
 }  // namespace flashot

@@ -27,7 +27,8 @@ struct PassShape {
   bool xres;            // row operand resident in registers (kbp == kb)
   bool lds;             // resident pass with the column tile shared through LDS
   int ri;               // 32-row tiles per wave
-  int splits, tps;      // column splits and column tiles per split
+  int ct, bk;           // wide pass: column tiles per block, k-blocks per stage
+  int splits, tps;      // column splits and column tiles (wide pass: blocks) per split
   int nrowgroups;       // workgroups along the rows
 };
 

@@ -97,23 +97,6 @@ __device__ __forceinline__ void pipe_stage(const u32x4* __restrict__ Cp,
   }
 }
 
-// LSE of a tile outside the pipelined loop (the last one or two of a split).
-template <int MODE, int RI>
-__device__ __forceinline__ void lse_tail(const f32x16 (&acc)[RI], const float (&Mf)[RI],
-                                         float (&M)[RI], float (&S)[RI], float ks) {
-  float Sn[RI];
-  bool slow = false;
-#pragma unroll
-  for (int ri = 0; ri < RI; ++ri) slow |= lse_fast<MODE != kModeBF16>(acc[ri], Mf[ri], M[ri], S[ri], ks, Sn[ri]);
-  if (__builtin_amdgcn_ballot_w64(slow) != 0) {
-#pragma unroll
-    for (int ri = 0; ri < RI; ++ri) lse_exact(acc[ri], Mf[ri], M[ri], S[ri], ks);
-  } else {
-#pragma unroll
-    for (int ri = 0; ri < RI; ++ri) S[ri] = Sn[ri];
-  }
-}
-
 template <int MODE, int KB, int RI>
 __global__ __launch_bounds__(256) void lse_pipe_kernel(
     const u32x4* __restrict__ Rp, const u32x4* __restrict__ Cp, const float* __restrict__ cbias,

@@ -1,5 +1,6 @@
 // Streamed log-sum-exp pass for wide points (the row operand does not fit in
-// registers): both operands are streamed per column tile in k-chunks.
+// registers): a workgroup-tiled pass that stages k-slices of its row block and
+// of one column block at a time in LDS.
 //
 // Method: "FlashSinkhorn: IO-Aware Entropic Optimal Transport on GPU"
 // (arXiv 2602.03067), Algorithms 1 / 3, App. D.2 (the row block cannot stay
@@ -14,139 +15,178 @@
 namespace flashot {
 
 // ---------------------------------------------------------------------------
-// Streamed log-sum-exp partials (Algorithm 1 / 3 of the page).
-//   part[s][row] = (M, S) with LSE_row over split s = (2/eps) M + ln S.
-// Grid: nrowgroups * splits workgroups of 4 waves; wave w of row group g owns
-// row tiles (4 g + w) * RI ... + RI - 1 and streams the column tiles of its split.
+// Tiled pass for wide points. A workgroup owns 4 RT row tiles (each wave RT
+// of them) and walks its split's column blocks of CT tiles; for each block
+// the score tiles are accumulated over the whole dimension in stages of BK
+// k-blocks. Each stage's slice of the row block and of the column block is
+// staged once in LDS (double-buffered, one barrier per stage) and read by
+// all four waves, so a wave's RT + CT fragments feed RT * CT MFMA tiles.
+// After a block's last stage the bias MFMA folds in bias_j - M_i and the
+// online LSE (lazy stabiliser, device_common.h) consumes the RT x CT tiles.
+// Units: 1 KiB operand units of the packed layout; KU units per k-block
+// (3 in split mode), kbp units per tile, padded to whole stages.
 // ---------------------------------------------------------------------------
-template <bool BF16, int KB, int RI, bool XRES>
-__global__ __launch_bounds__(256) void lse_partial_kernel(
+template <int MODE>
+constexpr int wide_ku() { return MODE == kModeSplit ? 3 : 1; }
+
+template <int MODE, int RT, int CT, int BK>
+constexpr int wide_stage_elems() { return (4 * RT + CT) * BK * wide_ku<MODE>() * 64; }
+
+template <int MODE, int RT, int CT, int BK>
+constexpr int wide_loads() { return (wide_stage_elems<MODE, RT, CT, BK>() + 255) / 256; }
+
+template <int MODE, int RT, int CT, int BK>
+__global__ __launch_bounds__(256) void lse_wide_kernel(
     const u32x4* __restrict__ Rp, const u32x4* __restrict__ Cp, const float* __restrict__ cbias,
-    int rtiles, int ctiles, int kbp, int splits, int tps, float c, float2* __restrict__ part,
+    int rtiles, int ctiles, int kbp, int splits, int bps, float c, float2* __restrict__ part,
     int rpad) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  constexpr int KU = wide_ku<MODE>();
+  constexpr int SU = BK * KU;               // units per tile per stage
+  constexpr int NX = 4 * RT;                // row tiles of the workgroup
+  constexpr int NL = wide_loads<MODE, RT, CT, BK>();
+  constexpr int kPerUnit = MODE == kModeF32 ? 4 : 1;
+  __shared__ u32x4 lds[2][NL * 256];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int h = lane >> 5;
   const int s = blockIdx.x % splits;
   const int rg = blockIdx.x / splits;
-  const int rt0 = (rg * kWaves + wave) * RI;
-  if (rt0 >= rtiles) return;
-  const int jt0 = s * tps;
-  const int jt1 = min(jt0 + tps, ctiles);
+  const int rt0 = rg * NX;                  // first row tile of the workgroup
+  const int nblocks = (ctiles + CT - 1) / CT;
+  const int b0 = s * bps;
+  const int nb = min(b0 + bps, nblocks) - b0;  // >= 1 by construction of the split
+  const int nstages = kbp / SU;             // per column block
+  const int total = nb * nstages;
+  const float ks = MODE == kModeBF16 ? c : 1.0f;
 
-  int rt[RI];
+  // Per-thread staging slots: slot q < NX is row tile rt0 + q, else column
+  // tile q - NX of the current block; unit u of the stage; lane l.
+  int slot[NL], uo[NL];
 #pragma unroll
-  for (int ri = 0; ri < RI; ++ri) rt[ri] = min(rt0 + ri, rtiles - 1);
-
-  u32x4 xr[RI][KB];
-  if constexpr (XRES) {
-#pragma unroll
-    for (int ri = 0; ri < RI; ++ri)
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) xr[ri][kb] = Rp[((size_t)rt[ri] * KB + kb) * 64 + lane];
+  for (int i = 0; i < NL; ++i) {
+    const int e = min(tid + 256 * i, wide_stage_elems<MODE, RT, CT, BK>() - 1);
+    slot[i] = e / (SU * 64);
+    uo[i] = ((e / 64) % SU) * 64 + (e & 63);
   }
-
-  float M[RI], S[RI];
+  auto gload = [&](int step, u32x4 (&g)[NL]) {
+    const int blk = b0 + step / nstages;
+    const int st = step % nstages;
 #pragma unroll
-  for (int ri = 0; ri < RI; ++ri) {
-    M[ri] = -1.0e30f;
-    S[ri] = 0.f;
-  }
-
-  if constexpr (XRES) {
-    // Double-buffered column operand: tile jt+1 is in flight while jt is used.
-    u32x4 yn[KB];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) yn[kb] = Cp[((size_t)jt0 * KB + kb) * 64 + lane];
-    float wn = cbias[jt0 * kTile + (lane & 31)];
-    for (int jt = jt0; jt < jt1; ++jt) {
-      u32x4 yc[KB];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) yc[kb] = yn[kb];
-      const float wv = wn;
-      const int jn = min(jt + 1, jt1 - 1);
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) yn[kb] = Cp[((size_t)jn * KB + kb) * 64 + lane];
-      wn = cbias[jn * kTile + (lane & 31)];
-
-      f32x16 acc[RI];
-#pragma unroll
-      for (int ri = 0; ri < RI; ++ri) acc[ri] = f32x16{};
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int ri = 0; ri < RI; ++ri) acc[ri] = mfma_kblock<BF16>(yc[kb], xr[ri][kb], acc[ri]);
-#pragma unroll
-      for (int ri = 0; ri < RI; ++ri) acc[ri] = mfma_bias(wv, h, acc[ri]);
-#pragma unroll
-      for (int ri = 0; ri < RI; ++ri) lse_tile(acc[ri], M[ri], S[ri], c);
+    for (int i = 0; i < NL; ++i) {
+      const bool isx = slot[i] < NX;
+      const int tile = isx ? min(rt0 + slot[i], rtiles - 1)
+                           : min(blk * CT + slot[i] - NX, ctiles - 1);
+      const u32x4* base = isx ? Rp : Cp;
+      g[i] = base[((size_t)tile * kbp + st * SU) * 64 + uo[i]];
     }
-  } else {
-    for (int jt = jt0; jt < jt1; ++jt) {
-      f32x16 acc[RI];
+  };
+  auto sstore = [&](u32x4* buf, const u32x4 (&g)[NL]) {
 #pragma unroll
-      for (int ri = 0; ri < RI; ++ri) acc[ri] = f32x16{};
-      for (int kc = 0; kc < kbp; kc += KB) {
-        u32x4 yc[KB];
-        u32x4 xc[RI][KB];
+    for (int i = 0; i < NL; ++i) buf[tid + 256 * i] = g[i];
+  };
+
+  float M[RT], S[RT];
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) yc[kb] = Cp[((size_t)jt * kbp + kc + kb) * 64 + lane];
+  for (int r = 0; r < RT; ++r) {
+    M[r] = kUnset;
+    S[r] = 0.f;
+  }
+  f32x16 acc[RT][CT];
+  u32x4 g[NL];
+  gload(0, g);
+  sstore(lds[0], g);
+  __syncthreads();
+
+  for (int step = 0; step < total; ++step) {
+    const int st = step % nstages;
+    if (st == 0) {
 #pragma unroll
-        for (int ri = 0; ri < RI; ++ri)
+      for (int r = 0; r < RT; ++r)
 #pragma unroll
-          for (int kb = 0; kb < KB; ++kb)
-            xc[ri][kb] = Rp[((size_t)rt[ri] * kbp + kc + kb) * 64 + lane];
+        for (int q = 0; q < CT; ++q) acc[r][q] = f32x16{};
+    }
+    if (step + 1 < total) gload(step + 1, g);
+    const u32x4* buf = lds[step & 1];
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+    for (int kb = 0; kb < BK; ++kb) {
+      u32x4 xf[RT][KU], yf[CT][KU];
 #pragma unroll
-          for (int ri = 0; ri < RI; ++ri) acc[ri] = mfma_kblock<BF16>(yc[kb], xc[ri][kb], acc[ri]);
+      for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int u = 0; u < KU; ++u)
+          xf[r][u] = buf[((wave * RT + r) * SU + kb * KU + u) * 64 + lane];
+#pragma unroll
+      for (int q = 0; q < CT; ++q)
+#pragma unroll
+        for (int u = 0; u < KU; ++u) yf[q][u] = buf[((NX + q) * SU + kb * KU + u) * 64 + lane];
+#pragma unroll
+      for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int q = 0; q < CT; ++q) {
+          if constexpr (MODE == kModeSplit)
+            acc[r][q] = mfma_split(yf[q], xf[r], acc[r][q]);
+          else
+            acc[r][q] = mfma_kblock<MODE == kModeBF16>(yf[q][0], xf[r][0], acc[r][q]);
+        }
+    }
+    if (step + 1 < total) sstore(lds[(step + 1) & 1], g);
+    if (st == nstages - 1) {
+      // Block complete: bias minus stabiliser, then the online LSE.
+      const int blk = b0 + step / nstages;
+      float Mf[RT];
+#pragma unroll
+      for (int r = 0; r < RT; ++r) Mf[r] = fold_of(M[r]);
+#pragma unroll
+      for (int q = 0; q < CT; ++q) {
+        const int jt = blk * CT + q;
+        const float w = jt < ctiles ? cbias[jt * kTile + (lane & 31)] : kSentinel;
+#pragma unroll
+        for (int r = 0; r < RT; ++r)
+          acc[r][q] = __builtin_amdgcn_mfma_f32_32x32x2f32(h ? 1.0f : w, h ? -Mf[r] : 1.0f,
+                                                           acc[r][q], 0, 0, 0);
       }
-      const float wv = cbias[jt * kTile + (lane & 31)];
 #pragma unroll
-      for (int ri = 0; ri < RI; ++ri) acc[ri] = mfma_bias(wv, h, acc[ri]);
+      for (int q = 0; q < CT; ++q) {
+        f32x16 col[RT];
 #pragma unroll
-      for (int ri = 0; ri < RI; ++ri) lse_tile(acc[ri], M[ri], S[ri], c);
+        for (int r = 0; r < RT; ++r) col[r] = acc[r][q];
+        lse_tail<MODE, RT>(col, Mf, M, S, ks);
+      }
     }
+    __syncthreads();  // stage step+1 is in LDS; everyone is done with stage step
   }
+  (void)kPerUnit;
 
-  // Merge the two half-waves that share a row (App. D.3 merge of partial statistics).
 #pragma unroll
-  for (int ri = 0; ri < RI; ++ri) {
-    const float Mp = __shfl_xor(M[ri], 32);
-    const float Sp = __shfl_xor(S[ri], 32);
-    const float Mt = fmaxf(M[ri], Mp);
-    const float cm = c * Mt;
-    const float St = S[ri] * __builtin_amdgcn_exp2f(fmaf(c, M[ri], -cm)) +
-                     Sp * __builtin_amdgcn_exp2f(fmaf(c, Mp, -cm));
-    if (h == 0 && rt0 + ri < rtiles)
-      part[(size_t)s * rpad + (size_t)(rt0 + ri) * kTile + (lane & 31)] = make_float2(c * Mt, St);
+  for (int r = 0; r < RT; ++r) {
+    const float St = S[r] + __shfl_xor(S[r], 32);
+    const int rt = rt0 + wave * RT + r;
+    if (h == 0 && rt < rtiles)
+      part[(size_t)s * rpad + (size_t)rt * kTile + (lane & 31)] = make_float2(ks * M[r], St);
   }
 }
 
-template <bool BF16, int KB, int RI, bool XRES>
-static void lse_go(const PassShape& s, const void* Rp, const void* Cp, const float* cbias,
-                   float c, float2* part, hipStream_t st) {
-  lse_partial_kernel<BF16, KB, RI, XRES><<<s.nrowgroups * s.splits, 256, 0, st>>>(
+template <int MODE, int RT, int CT, int BK>
+static void lse_wide_go(const PassShape& s, const void* Rp, const void* Cp, const float* cbias,
+                        float c, float2* part, hipStream_t st) {
+  lse_wide_kernel<MODE, RT, CT, BK><<<s.nrowgroups * s.splits, 256, 0, st>>>(
       (const u32x4*)Rp, (const u32x4*)Cp, cbias, s.rtiles, s.ctiles, s.kbp, s.splits, s.tps, c,
       part, s.rtiles * kTile);
 }
 
-
-template <bool BF16>
-static hipError_t lse_wide_dispatch(const PassShape& s, const void* Rp, const void* Cp,
-                                    const float* cbias, float c, float2* part, hipStream_t st) {
-  if (s.ri == 2)
-    lse_go<BF16, 8, 2, false>(s, Rp, Cp, cbias, c, part, st);
-  else
-    lse_go<BF16, 8, 1, false>(s, Rp, Cp, cbias, c, part, st);
-  return hipGetLastError();
-}
-
 hipError_t launch_lse_wide(const PassShape& s, int mode, const void* Rp, const void* Cp,
                            const float* cbias, float c, float2* part, hipStream_t st) {
-  if (s.xres || mode == kModeSplit) return hipErrorInvalidValue;
-  return mode == kModeBF16 ? lse_wide_dispatch<true>(s, Rp, Cp, cbias, c, part, st)
-                           : lse_wide_dispatch<false>(s, Rp, Cp, cbias, c, part, st);
+  if (s.xres || s.ri != 2) return hipErrorInvalidValue;
+  if (mode == kModeSplit && s.ct == 2 && s.bk == 1)
+    lse_wide_go<kModeSplit, 2, 2, 1>(s, Rp, Cp, cbias, c, part, st);
+  else if (mode == kModeBF16 && s.ct == 4 && s.bk == 2)
+    lse_wide_go<kModeBF16, 2, 4, 2>(s, Rp, Cp, cbias, c, part, st);
+  else if (mode == kModeF32 && s.ct == 4 && s.bk == 2)
+    lse_wide_go<kModeF32, 2, 4, 2>(s, Rp, Cp, cbias, c, part, st);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 }  // namespace flashot

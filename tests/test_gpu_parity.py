@@ -65,6 +65,12 @@ HALF_CASES = [
     (150, 210, 256, "bf16", 0.1),
     (120, 140, 512, "bf16", 0.1),
     (97, 64, 1024, "bf16", 0.01),
+    # eps = 0.01 with few column tiles: scores far below zero in log2 units,
+    # where a tile folded before the row's stabiliser was set must take the
+    # exact path (its rescale factor would overflow)
+    (300, 40, 64, "f32", 0.01),
+    (260, 70, 17, "bf16", 0.01),
+    (150, 90, 300, "f32", 0.01),
 ]
 
 
