@@ -107,7 +107,7 @@ KConf kernel_conf(int64_t d, int bf16, bool allow_split, bool for_apply = false)
       k.ct = k.mode == 2 ? 2 : 4;
       k.bk = k.mode == 2 ? 1 : 2;
       k.kb = k.bk * ku;
-      k.kbp = ceil_div(k.kblocks, k.bk) * k.bk * ku;
+      k.kbp = ceil_div(k.kblocks, 2 * k.bk) * 2 * k.bk * ku;  // an even number of stages
       k.xres = false;
     }
   }

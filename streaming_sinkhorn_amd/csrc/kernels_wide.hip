@@ -38,20 +38,26 @@ constexpr int wide_loads() { return (wide_stage_elems<MODE, RT, CT, BK>() + 255)
 template <int MODE, int RT, int CT, int BK>
 __global__ __launch_bounds__(256) void lse_wide_kernel(
     const u32x4* __restrict__ Rp, const u32x4* __restrict__ Cp, const float* __restrict__ cbias,
-    int rtiles, int ctiles, int kbp, int splits, int bps, float c, float2* __restrict__ part,
-    int rpad) {
+    int rtiles, int ctiles, int kbp, int splits, int bps, int nrowgroups, float c,
+    float2* __restrict__ part, int rpad) {
   constexpr int KU = wide_ku<MODE>();
   constexpr int SU = BK * KU;               // units per tile per stage
   constexpr int NX = 4 * RT;                // row tiles of the workgroup
   constexpr int NL = wide_loads<MODE, RT, CT, BK>();
-  constexpr int kPerUnit = MODE == kModeF32 ? 4 : 1;
   __shared__ u32x4 lds[2][NL * 256];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int h = lane >> 5;
-  const int s = blockIdx.x % splits;
-  const int rg = blockIdx.x / splits;
+  // Workgroups are dispatched round-robin over the 8 XCDs. Workgroup w runs
+  // on XCD w % 8; the XCD's workgroups are ordered split-fastest over row
+  // groups xcd, xcd + 8, ..., so the few row blocks in flight on an XCD (each
+  // re-read once per column block) stay in its L2.
+  const int xcd = blockIdx.x & 7;
+  const int li = blockIdx.x >> 3;
+  const int s = li % splits;
+  const int rg = (li / splits) * 8 + xcd;
+  if (rg >= nrowgroups) return;             // whole workgroup: no barrier is skipped
   const int rt0 = rg * NX;                  // first row tile of the workgroup
   const int nblocks = (ctiles + CT - 1) / CT;
   const int b0 = s * bps;
@@ -61,24 +67,29 @@ __global__ __launch_bounds__(256) void lse_wide_kernel(
   const float ks = MODE == kModeBF16 ? c : 1.0f;
 
   // Per-thread staging slots: slot q < NX is row tile rt0 + q, else column
-  // tile q - NX of the current block; unit u of the stage; lane l.
-  int slot[NL], uo[NL];
+  // tile q - NX of the current block; unit u of the stage; lane l. Row-slot
+  // sources are fixed; column-slot sources move with the block.
+  const u32x4* src[NL];
+  bool isx[NL];
+  int cq[NL];
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
     const int e = min(tid + 256 * i, wide_stage_elems<MODE, RT, CT, BK>() - 1);
-    slot[i] = e / (SU * 64);
-    uo[i] = ((e / 64) % SU) * 64 + (e & 63);
+    const int q = e / (SU * 64);
+    const int uo = ((e / 64) % SU) * 64 + (e & 63);
+    isx[i] = q < NX;
+    cq[i] = q - NX;
+    src[i] = isx[i] ? Rp + (size_t)min(rt0 + q, rtiles - 1) * kbp * 64 + uo : Cp + uo;
   }
+  // Loads stage `step` (clamped to the last one) into registers: branch-free.
   auto gload = [&](int step, u32x4 (&g)[NL]) {
+    step = min(step, total - 1);
     const int blk = b0 + step / nstages;
-    const int st = step % nstages;
+    const size_t koff = (size_t)(step % nstages) * SU * 64;
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      const bool isx = slot[i] < NX;
-      const int tile = isx ? min(rt0 + slot[i], rtiles - 1)
-                           : min(blk * CT + slot[i] - NX, ctiles - 1);
-      const u32x4* base = isx ? Rp : Cp;
-      g[i] = base[((size_t)tile * kbp + st * SU) * 64 + uo[i]];
+      const size_t coff = (size_t)min(blk * CT + cq[i], ctiles - 1) * kbp * 64;
+      g[i] = src[i][(isx[i] ? 0 : coff) + koff];
     }
   };
   auto sstore = [&](u32x4* buf, const u32x4 (&g)[NL]) {
@@ -92,22 +103,16 @@ __global__ __launch_bounds__(256) void lse_wide_kernel(
     M[r] = kUnset;
     S[r] = 0.f;
   }
-  f32x16 acc[RT][CT];
-  u32x4 g[NL];
-  gload(0, g);
-  sstore(lds[0], g);
+  // Two register staging sets: the load of stage t is issued at the start of
+  // stage t - 2 and stored to LDS at the end of stage t - 1, so it has two
+  // stages of matrix work to arrive. nstages is even (padded by the host).
+  u32x4 gA[NL], gB[NL];
+  gload(0, gA);
+  sstore(lds[0], gA);
+  gload(1, gB);
   __syncthreads();
 
-  for (int step = 0; step < total; ++step) {
-    const int st = step % nstages;
-    if (st == 0) {
-#pragma unroll
-      for (int r = 0; r < RT; ++r)
-#pragma unroll
-        for (int q = 0; q < CT; ++q) acc[r][q] = f32x16{};
-    }
-    if (step + 1 < total) gload(step + 1, g);
-    const u32x4* buf = lds[step & 1];
+  auto compute = [&](const u32x4* buf, f32x16 (&acc)[RT][CT]) {
 #pragma unroll
     for (int kb = 0; kb < BK; ++kb) {
       u32x4 xf[RT][KU], yf[CT][KU];
@@ -119,7 +124,8 @@ __global__ __launch_bounds__(256) void lse_wide_kernel(
 #pragma unroll
       for (int q = 0; q < CT; ++q)
 #pragma unroll
-        for (int u = 0; u < KU; ++u) yf[q][u] = buf[((NX + q) * SU + kb * KU + u) * 64 + lane];
+        for (int u = 0; u < KU; ++u)
+          yf[q][u] = buf[((NX + q) * SU + kb * KU + u) * 64 + lane];
 #pragma unroll
       for (int r = 0; r < RT; ++r)
 #pragma unroll
@@ -130,33 +136,50 @@ __global__ __launch_bounds__(256) void lse_wide_kernel(
             acc[r][q] = mfma_kblock<MODE == kModeBF16>(yf[q][0], xf[r][0], acc[r][q]);
         }
     }
-    if (step + 1 < total) sstore(lds[(step + 1) & 1], g);
-    if (st == nstages - 1) {
-      // Block complete: bias minus stabiliser, then the online LSE.
-      const int blk = b0 + step / nstages;
-      float Mf[RT];
+  };
+
+  int step = 0;  // even at the top of every stage pair
+  for (int bi = 0; bi < nb; ++bi) {
+    f32x16 acc[RT][CT];
 #pragma unroll
-      for (int r = 0; r < RT; ++r) Mf[r] = fold_of(M[r]);
+    for (int r = 0; r < RT; ++r)
 #pragma unroll
-      for (int q = 0; q < CT; ++q) {
-        const int jt = blk * CT + q;
-        const float w = jt < ctiles ? cbias[jt * kTile + (lane & 31)] : kSentinel;
-#pragma unroll
-        for (int r = 0; r < RT; ++r)
-          acc[r][q] = __builtin_amdgcn_mfma_f32_32x32x2f32(h ? 1.0f : w, h ? -Mf[r] : 1.0f,
-                                                           acc[r][q], 0, 0, 0);
-      }
-#pragma unroll
-      for (int q = 0; q < CT; ++q) {
-        f32x16 col[RT];
-#pragma unroll
-        for (int r = 0; r < RT; ++r) col[r] = acc[r][q];
-        lse_tail<MODE, RT>(col, Mf, M, S, ks);
-      }
+      for (int q = 0; q < CT; ++q) acc[r][q] = f32x16{};
+    for (int st = 0; st < nstages; st += 2, step += 2) {
+      // stage `step` is in lds[0]; gB holds stage step + 1
+      gload(step + 2, gA);
+      compute(lds[0], acc);
+      sstore(lds[1], gB);  // lds[1] was last read in stage step - 1
+      __syncthreads();
+      // stage step + 1 is in lds[1]; gA holds stage step + 2
+      gload(step + 3, gB);
+      compute(lds[1], acc);
+      sstore(lds[0], gA);  // after the final stage nobody reads these stores
+      __syncthreads();
     }
-    __syncthreads();  // stage step+1 is in LDS; everyone is done with stage step
+    // Block complete: bias minus stabiliser, then the online LSE.
+    const int blk = b0 + bi;
+    float Mf[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) Mf[r] = fold_of(M[r]);
+#pragma unroll
+    for (int q = 0; q < CT; ++q) {
+      const int jt = blk * CT + q;
+      const float w = cbias[min(jt, ctiles - 1) * kTile + (lane & 31)];
+      const float wq = jt < ctiles ? w : kSentinel;
+#pragma unroll
+      for (int r = 0; r < RT; ++r)
+        acc[r][q] = __builtin_amdgcn_mfma_f32_32x32x2f32(h ? 1.0f : wq, h ? -Mf[r] : 1.0f,
+                                                         acc[r][q], 0, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < CT; ++q) {
+      f32x16 col[RT];
+#pragma unroll
+      for (int r = 0; r < RT; ++r) col[r] = acc[r][q];
+      lse_tail<MODE, RT>(col, Mf, M, S, ks);
+    }
   }
-  (void)kPerUnit;
 
 #pragma unroll
   for (int r = 0; r < RT; ++r) {
@@ -170,9 +193,12 @@ __global__ __launch_bounds__(256) void lse_wide_kernel(
 template <int MODE, int RT, int CT, int BK>
 static void lse_wide_go(const PassShape& s, const void* Rp, const void* Cp, const float* cbias,
                         float c, float2* part, hipStream_t st) {
-  lse_wide_kernel<MODE, RT, CT, BK><<<s.nrowgroups * s.splits, 256, 0, st>>>(
-      (const u32x4*)Rp, (const u32x4*)Cp, cbias, s.rtiles, s.ctiles, s.kbp, s.splits, s.tps, c,
-      part, s.rtiles * kTile);
+  // Row groups padded to a multiple of 8 (one slice per XCD); padding
+  // workgroups exit at once.
+  const int grid = (s.nrowgroups + 7) / 8 * 8 * s.splits;
+  lse_wide_kernel<MODE, RT, CT, BK><<<grid, 256, 0, st>>>(
+      (const u32x4*)Rp, (const u32x4*)Cp, cbias, s.rtiles, s.ctiles, s.kbp, s.splits, s.tps,
+      s.nrowgroups, c, part, s.rtiles * kTile);
 }
 
 hipError_t launch_lse_wide(const PassShape& s, int mode, const void* Rp, const void* Cp,
