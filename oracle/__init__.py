@@ -27,6 +27,7 @@ from .sinkhorn import (  # noqa: F401
     update_f,
     update_g,
     sinkhorn,
+    sinkhorn_symmetric,
     plan,
     marginals,
     marginal_errors,

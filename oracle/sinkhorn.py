@@ -123,6 +123,37 @@ def sinkhorn(C, a, b, eps, iters, f0=None, g0=None, record=False):
     return f, g
 
 
+def sinkhorn_symmetric(C, a, b, eps, iters, f0=None, g0=None, record=False):
+    """Symmetric (averaged) log-domain Sinkhorn for a fixed number of iterations.
+
+    §3.1 (the symmetric updates eq. 4-5, fused "in the same single-kernel
+    streaming form") and §4.1 / App. H.2 (the GeomLoss-style schedule, "flash(sym)").
+    The equations did not survive on the page; the reading implemented here is
+    the averaged update in which both half-steps read the previous iterate:
+
+        f_new = (f + T_f(g)) / 2,   g_new = (g + T_g(f)) / 2,
+
+    with T_f, T_g the half-steps of ``update_f`` / ``update_g``. Its fixed points
+    are those of the alternating schedule. Starts from f = g = 0 unless given.
+    """
+    C = _f64(C)
+    n, m = C.shape
+    f = np.zeros(n) if f0 is None else _f64(f0).copy()
+    g = np.zeros(m) if g0 is None else _f64(g0).copy()
+    fs, gs = [], []
+    for _ in range(int(iters)):
+        ft = update_f(C, g, b, eps)
+        gt = update_g(C, f, a, eps)
+        f = 0.5 * (f + ft)
+        g = 0.5 * (g + gt)
+        if record:
+            fs.append(f.copy())
+            gs.append(g.copy())
+    if record:
+        return f, g, fs, gs
+    return f, g
+
+
 def plan(C, a, b, f, g, eps):
     """Coupling induced by any potentials: P_ij = a_i b_j exp((f_i + g_j - C_ij)/eps).
 

@@ -363,3 +363,58 @@ def test_dimension_zero_and_single_point():
     C1 = oracle.cost_matrix([[1.0, 2.0]], [[0.0, 0.0]])
     f1, g1 = oracle.sinkhorn(C1, [1.0], [1.0], 0.1, 2)
     assert abs(f1[0] + g1[0] - C1[0, 0]) < 1e-13
+
+
+# --- symmetric (averaged) schedule ---------------------------------------------------
+
+def test_symmetric_schedule_matches_scaling_geometric_mean():
+    """The averaged log-domain update is the geometric mean of the old scaling
+    and the textbook scaling update, both taken from the old iterate:
+    u <- sqrt(u * a / (K v)), v <- sqrt(v * b / (K^T u)) with u = a exp(f/eps),
+    v = b exp(g/eps), K = exp(-C/eps). Written on the scalings, it shares no
+    code with the log-domain oracle and pins the averaging, the use of the old
+    iterate in both half-steps, and the weights."""
+    X, Y, a, b = _problem(9, 12, 3)
+    eps = 0.5
+    C = oracle.cost_matrix(X, Y)
+    K = np.exp(-C / eps)
+    u, v = a.copy(), b.copy()
+    for _ in range(30):
+        u, v = np.sqrt(u * a / (K @ v)), np.sqrt(v * b / (K.T @ u))
+    f, g = oracle.sinkhorn_symmetric(C, a, b, eps, 30)
+    np.testing.assert_allclose(f, eps * np.log(u / a), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(g, eps * np.log(v / b), rtol=1e-10, atol=1e-12)
+
+
+def test_symmetric_and_alternating_share_the_fixed_point():
+    """Both schedules converge to the Sinkhorn fixed point: the coupling has
+    marginals a and b, and the two converged couplings coincide (the potentials
+    themselves may differ by the constant mode f + k, g - k)."""
+    X, Y, a, b = _problem(11, 8, 2)
+    eps = 0.4
+    C = oracle.cost_matrix(X, Y)
+    fa, ga = oracle.sinkhorn(C, a, b, eps, 4000)
+    fs, gs = oracle.sinkhorn_symmetric(C, a, b, eps, 4000)
+    Pa = oracle.plan(C, a, b, fa, ga, eps)
+    Ps = oracle.plan(C, a, b, fs, gs, eps)
+    r, c = oracle.marginals(Ps)
+    np.testing.assert_allclose(r, a, rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(c, b, rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(Ps, Pa, rtol=1e-8, atol=1e-13)
+
+
+def test_symmetric_schedule_constant_shift():
+    """Starting from (f0 + k, g0 - k) shifts every iterate by (+k, -k) and leaves
+    the coupling unchanged: T_f(g - k) = T_f(g) + k and T_g(f + k) = T_g(f) - k."""
+    X, Y, a, b = _problem(7, 9, 3)
+    eps = 0.3
+    C = oracle.cost_matrix(X, Y)
+    f0 = RNG.standard_normal(7) * 0.2
+    g0 = RNG.standard_normal(9) * 0.2
+    k = 0.37
+    f1, g1 = oracle.sinkhorn_symmetric(C, a, b, eps, 6, f0, g0)
+    f2, g2 = oracle.sinkhorn_symmetric(C, a, b, eps, 6, f0 + k, g0 - k)
+    np.testing.assert_allclose(f2, f1 + k, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(g2, g1 - k, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(oracle.plan(C, a, b, f2, g2, eps), oracle.plan(C, a, b, f1, g1, eps),
+                               rtol=1e-11)
