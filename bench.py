@@ -134,6 +134,7 @@ def main():
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB")
+    ap.add_argument("--schedule", default="alternating", choices=["alternating", "symmetric"])
     ap.add_argument("--native-f32", action="store_true",
                     help="form fp32 scores with the fp32 matrix instruction instead of the "
                          "three-part bf16 split")
@@ -185,7 +186,7 @@ def main():
         ssa.ot_sqnorms(X, xs)
         ssa.ot_sqnorms(Y, ys)
         info = ssa.ot_solve(prob, f, g, T, splits_f=args.splits, splits_g=args.splits,
-                            timing=True, ws=ws.get("solve"))
+                            timing=True, ws=ws.get("solve"), schedule=args.schedule)
         if w.grad:
             ssa.ot_apply_plan(prob, f, g, flags=ssa.OT_GRAD, out=out_grad, marg=r, ws=ws.get("grad"))
         if w.v_cols:
@@ -268,7 +269,7 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": f"{w.name}: n={w.n}, m={w.m}, d={w.d}, {w.dtype} points, eps={w.eps}, {T} "
-                        f"alternating iterations from zero potentials; outputs: {', '.join(outputs)}",
+                        f"{args.schedule} iterations from zero potentials; outputs: {', '.join(outputs)}",
             "n": w.n, "m": w.m, "d": w.d, "eps": w.eps, "iters": T,
             "splits_f": last["splits_f"], "splits_g": last["splits_g"],
             "operand_mode": ["fp32 MFMA", "bf16 MFMA", "fp32 as 3-part bf16 split on bf16 MFMA"][

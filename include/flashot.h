@@ -65,6 +65,11 @@ extern "C" {
 #define OT_INIT_ZERO  0  /* start from f = g = 0 */
 #define OT_INIT_GIVEN 1  /* start from the caller's f, g (warm start / resume) */
 
+/* ot_solve schedules. */
+#define OT_SCHED_ALTERNATING 0  /* f from g, then g from the new f (§3.1 eq. 2-3) */
+#define OT_SCHED_SYMMETRIC   1  /* f <- (f + T_f(g))/2, g <- (g + T_g(f))/2 from the previous
+                                   iterate (§3.1 eq. 4-5, the GeomLoss-style schedule) */
+
 /* ot_apply_plan flags. */
 #define OT_TRANSPOSE 1  /* compute P^T U (U has n rows) instead of P V (V has m rows) */
 #define OT_GRAD      2  /* out = 2 (r * X - P Y), the X-gradient (Y-gradient with OT_TRANSPOSE); V is ignored */
@@ -123,6 +128,7 @@ typedef struct ot_solve_opts {
   int32_t splits_f;     /* column splits of the f half-step (0 = automatic) */
   int32_t splits_g;     /* column splits of the g half-step (0 = automatic) */
   int32_t timing;       /* 1: time every log-sum-exp kernel with HIP events (needs info) */
+  int32_t schedule;     /* OT_SCHED_ALTERNATING (0) or OT_SCHED_SYMMETRIC */
 } ot_solve_opts;
 
 /* ot_solve results (host memory). */
@@ -179,9 +185,13 @@ int ot_update_g(const ot_problem* p, const float* f, float* g, float* err,
                 void* ws, size_t* ws_bytes, void* stream);
 
 /*
- * ot_solve -- `opts->iters` alternating iterations (§3.1 eq. 2-3; §4.1 / App.
- * H.2: fixed iteration count, no eps-scaling, no debiasing): each iteration is
- * an f half-step from the current g followed by a g half-step from the new f.
+ * ot_solve -- `opts->iters` Sinkhorn iterations (§4.1 / App. H.2: fixed
+ * iteration count, no eps-scaling, no debiasing) in one of two schedules:
+ *   OT_SCHED_ALTERNATING (§3.1 eq. 2-3): an f half-step from the current g,
+ *     then a g half-step from the new f;
+ *   OT_SCHED_SYMMETRIC (§3.1 eq. 4-5, the GeomLoss-style schedule): both
+ *     half-steps read the previous iterate, f <- (f + T_f(g))/2 and
+ *     g <- (g + T_g(f))/2.
  *   f, g   device fp32 (n, m): output potentials; with OT_INIT_GIVEN also the
  *          starting point (k then k' iterations equal k + k' iterations).
  *   opts   host, required
@@ -189,10 +199,11 @@ int ot_update_g(const ot_problem* p, const float* f, float* g, float* err,
  *          end and fills every field; marg_err_row / marg_err_col are then the
  *          exact L1 marginal errors of the returned (f, g), at the cost of two
  *          extra streamed passes.
- *   With opts->tol > 0 the row-marginal error of the current coupling is
- *   evaluated inside every f half-step (it is r - a for r of App. E.1) and the
- *   host reads it every opts->check_every iterations (one synchronisation per
- *   check); the loop stops after the iteration in which it fell below tol.
+ *   With opts->tol > 0 the row-marginal error of the coupling of the previous
+ *   iterate is evaluated inside every f half-step (it is r - a for r of App.
+ *   E.1) and the host reads it every opts->check_every iterations (one
+ *   synchronisation per check); the loop stops after the iteration in which
+ *   it fell below tol.
  * Errors: as ot_update_f, plus OT_ERR_NONFINITE when info is given and the
  * final potentials are not finite.
  */

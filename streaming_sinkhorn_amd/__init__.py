@@ -32,6 +32,8 @@ OT_F32, OT_BF16 = 0, 1
 OT_INIT_ZERO, OT_INIT_GIVEN = 0, 1
 OT_TRANSPOSE, OT_GRAD, OT_BARY = 1, 2, 4
 OT_NATIVE_F32 = 1
+OT_SCHED_ALTERNATING, OT_SCHED_SYMMETRIC = 0, 1
+_SCHEDULES = {"alternating": OT_SCHED_ALTERNATING, "symmetric": OT_SCHED_SYMMETRIC}
 
 
 class OtError(RuntimeError):
@@ -57,6 +59,7 @@ class OtSolveOpts(ctypes.Structure):
         ("iters", ctypes.c_int32), ("tol", ctypes.c_float), ("check_every", ctypes.c_int32),
         ("init", ctypes.c_int32), ("use_graph", ctypes.c_int32),
         ("splits_f", ctypes.c_int32), ("splits_g", ctypes.c_int32), ("timing", ctypes.c_int32),
+        ("schedule", ctypes.c_int32),
     ]
 
 
@@ -223,12 +226,14 @@ def ot_update_g(prob: Problem, f, g, err=None, ws=None):
 
 def ot_solve(prob: Problem, f, g, iters: int, tol: float = 0.0, check_every: int = 1,
              init_given: bool = False, use_graph: bool = True, splits_f: int = 0,
-             splits_g: int = 0, timing: bool = False, want_info: bool = True, ws=None):
-    """Alternating Sinkhorn into f, g. Returns the info dict (None if want_info is False)."""
+             splits_g: int = 0, timing: bool = False, want_info: bool = True, ws=None,
+             schedule: str = "alternating"):
+    """Sinkhorn iterations into f, g (schedule "alternating" or "symmetric").
+    Returns the info dict (None if want_info is False)."""
     L = lib()
     opts = OtSolveOpts(int(iters), float(tol), int(check_every),
                        OT_INIT_GIVEN if init_given else OT_INIT_ZERO, int(bool(use_graph)),
-                       int(splits_f), int(splits_g), int(bool(timing)))
+                       int(splits_f), int(splits_g), int(bool(timing)), _SCHEDULES[schedule])
     info = OtSolveInfo()
     pinfo = ctypes.byref(info) if want_info else None
     st = _stream(prob.device)

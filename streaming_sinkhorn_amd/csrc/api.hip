@@ -179,7 +179,8 @@ struct SolveWs {
   KConf k;
   int ntiles, mtiles, npad, mpad;
   PassShape F, G;
-  size_t o_xp, o_yp, o_nx, o_ny, o_wx, o_hx, o_bx, o_wy, o_hy, o_by, o_part, o_errp, o_errv;
+  size_t o_xp, o_yp, o_nx, o_ny, o_wx, o_hx, o_bx, o_wy, o_hy, o_by, o_part, o_part2, o_errp,
+      o_errv;
   int errblocks_f, errblocks_g;
   size_t total;
 };
@@ -213,6 +214,7 @@ SolveWs solve_layout(const ot_problem* p, int splits_f, int splits_g) {
   w.o_by = take((size_t)w.mpad * 4);
   const size_t pf = (size_t)w.F.splits * w.npad, pg = (size_t)w.G.splits * w.mpad;
   w.o_part = take((pf > pg ? pf : pg) * 8);
+  w.o_part2 = take(pg * 8);  // g partials of the symmetric schedule (both passes in flight)
   w.o_errp = take((size_t)(w.errblocks_f + w.errblocks_g) * 4);
   w.o_errv = take(64);
   w.total = o;
@@ -233,6 +235,8 @@ struct Ctx {
   const float* ny;
   float *wx, *hx, *bx, *wy, *hy, *by, *errp, *errv;
   float2* part;
+  float2* part2;
+  bool sym;  // symmetric (averaged) schedule
   void *xp, *yp;
   float *f, *g;
 };
@@ -259,6 +263,7 @@ Ctx make_ctx(const ot_problem* p, const SolveWs& L, void* ws, float* f, float* g
   x.hy = (float*)(x.ws + L.o_hy);
   x.by = (float*)(x.ws + L.o_by);
   x.part = (float2*)(x.ws + L.o_part);
+  x.part2 = (float2*)(x.ws + L.o_part2);
   x.errp = (float*)(x.ws + L.o_errp);
   x.errv = (float*)(x.ws + L.o_errv);
   x.f = f;
@@ -290,22 +295,44 @@ int prepare(const Ctx& x, hipStream_t st) {
 int half_f(const Ctx& x, hipStream_t st, int with_err, int write) {
   OT_HIP(launch_lse_partial(x.L.F, x.L.k.mode, x.xp, x.yp, x.by, x.kc, x.part, st));
   OT_HIP(launch_lse_merge(x.part, x.L.F.splits, x.L.npad, (int)x.p->n, x.bscale, x.eps, x.nx, x.hx, x.wx,
-                          x.f, x.bx, x.errp, with_err, write, st));
+                          x.f, x.bx, x.errp, with_err, write, 0, st));
   return OT_OK;
 }
 
 int half_g(const Ctx& x, hipStream_t st, int with_err, int write) {
   OT_HIP(launch_lse_partial(x.L.G, x.L.k.mode, x.yp, x.xp, x.bx, x.kc, x.part, st));
   OT_HIP(launch_lse_merge(x.part, x.L.G.splits, x.L.mpad, (int)x.p->m, x.bscale, x.eps, x.ny, x.hy, x.wy,
-                          x.g, x.by, x.errp + x.L.errblocks_f, with_err, write, st));
+                          x.g, x.by, x.errp + x.L.errblocks_f, with_err, write, 0, st));
+  return OT_OK;
+}
+
+// One iteration on the stream. Alternating schedule (§3.1 eq. 2-3): the f
+// pass, its merge (new f and its bias), then the g pass from the new f.
+// Symmetric schedule (§3.1 eq. 4-5): both passes read the previous biases,
+// so both run before either merge; the merges average old and new values.
+// ev, if given, receives four events around the two log-sum-exp launches.
+int enqueue_iteration(const Ctx& x, hipStream_t st, int with_err, hipEvent_t* ev) {
+  if (ev) OT_HIP(hipEventRecord(ev[0], st));
+  OT_HIP(launch_lse_partial(x.L.F, x.L.k.mode, x.xp, x.yp, x.by, x.kc, x.part, st));
+  if (ev) OT_HIP(hipEventRecord(ev[1], st));
+  if (!x.sym)
+    OT_HIP(launch_lse_merge(x.part, x.L.F.splits, x.L.npad, (int)x.p->n, x.bscale, x.eps, x.nx, x.hx,
+                            x.wx, x.f, x.bx, x.errp, with_err, 1, 0, st));
+  float2* pg = x.sym ? x.part2 : x.part;
+  if (ev) OT_HIP(hipEventRecord(ev[2], st));
+  OT_HIP(launch_lse_partial(x.L.G, x.L.k.mode, x.yp, x.xp, x.bx, x.kc, pg, st));
+  if (ev) OT_HIP(hipEventRecord(ev[3], st));
+  if (x.sym)
+    OT_HIP(launch_lse_merge(x.part, x.L.F.splits, x.L.npad, (int)x.p->n, x.bscale, x.eps, x.nx, x.hx,
+                            x.wx, x.f, x.bx, x.errp, with_err, 1, 1, st));
+  OT_HIP(launch_lse_merge(pg, x.L.G.splits, x.L.mpad, (int)x.p->m, x.bscale, x.eps, x.ny, x.hy, x.wy,
+                          x.g, x.by, x.errp + x.L.errblocks_f, 0, 1, x.sym ? 1 : 0, st));
   return OT_OK;
 }
 
 int enqueue_iterations(const Ctx& x, hipStream_t st, int count, int with_err) {
   for (int t = 0; t < count; ++t) {
-    int rc = half_f(x, st, with_err, 1);
-    if (rc) return rc;
-    rc = half_g(x, st, 0, 1);
+    const int rc = enqueue_iteration(x, st, with_err, nullptr);
     if (rc) return rc;
   }
   return OT_OK;
@@ -318,7 +345,7 @@ struct GraphKey {
   int64_t n, m, d;
   int dtype;
   float eps;
-  int count, with_err, mode;
+  int count, with_err, mode, sym;
   PassShape F, G;
   bool operator==(const GraphKey& o) const { return std::memcmp(this, &o, sizeof(*this)) == 0; }
 };
@@ -351,6 +378,7 @@ int get_graph(const Ctx& x, int count, int with_err, hipGraphExec_t* out) {
   key.count = count;
   key.with_err = with_err;
   key.mode = x.L.k.mode;
+  key.sym = x.sym ? 1 : 0;
   key.F = x.L.F;
   key.G = x.L.G;
   std::lock_guard<std::mutex> lk(g_graph_mu);
@@ -426,17 +454,8 @@ int run_iterations_timed(const Ctx& x, hipStream_t st, int count, int with_err, 
   int rc = g_events.ensure(need);
   if (rc) return rc;
   for (int t = 0; t < count; ++t) {
-    hipEvent_t* e = &g_events.ev[(size_t)t * 4];
-    OT_HIP(hipEventRecord(e[0], st));
-    OT_HIP(launch_lse_partial(x.L.F, x.L.k.mode, x.xp, x.yp, x.by, x.kc, x.part, st));
-    OT_HIP(hipEventRecord(e[1], st));
-    OT_HIP(launch_lse_merge(x.part, x.L.F.splits, x.L.npad, (int)x.p->n, x.bscale, x.eps, x.nx, x.hx,
-                            x.wx, x.f, x.bx, x.errp, with_err, 1, st));
-    OT_HIP(hipEventRecord(e[2], st));
-    OT_HIP(launch_lse_partial(x.L.G, x.L.k.mode, x.yp, x.xp, x.bx, x.kc, x.part, st));
-    OT_HIP(hipEventRecord(e[3], st));
-    OT_HIP(launch_lse_merge(x.part, x.L.G.splits, x.L.mpad, (int)x.p->m, x.bscale, x.eps, x.ny, x.hy,
-                            x.wy, x.g, x.by, x.errp + x.L.errblocks_f, 0, 1, st));
+    rc = enqueue_iteration(x, st, with_err, &g_events.ev[(size_t)t * 4]);
+    if (rc) return rc;
   }
   OT_HIP(hipStreamSynchronize(st));
   float tot = 0.f;
@@ -590,6 +609,8 @@ int ot_solve(const ot_problem* p, float* f, float* g, const ot_solve_opts* o,
     if (o->init != OT_INIT_ZERO && o->init != OT_INIT_GIVEN) return fail(OT_ERR_INVALID_ARG, "init must be OT_INIT_ZERO or OT_INIT_GIVEN");
     if (o->splits_f < 0 || o->splits_g < 0) return fail(OT_ERR_INVALID_ARG, "splits must be >= 0");
     if (o->timing && !info) return fail(OT_ERR_INVALID_ARG, "timing needs info");
+    if (o->schedule != OT_SCHED_ALTERNATING && o->schedule != OT_SCHED_SYMMETRIC)
+      return fail(OT_ERR_INVALID_ARG, "schedule must be OT_SCHED_ALTERNATING or OT_SCHED_SYMMETRIC");
     const SolveWs L = solve_layout(p, o->splits_f, o->splits_g);
     bool query = false;
     rc = check_ws(ws, ws_bytes, L.total, &query);
@@ -603,7 +624,9 @@ int ot_solve(const ot_problem* p, float* f, float* g, const ot_solve_opts* o,
       OT_HIP(launch_fill(f, 0.f, p->n, st));
       OT_HIP(launch_fill(g, 0.f, p->m, st));
     }
+    x.sym = o->schedule == OT_SCHED_SYMMETRIC;
     OT_HIP(launch_bias_from_pot(g, x.ny, x.hy, (int)p->m, L.mpad, x.bscale, x.by, st));
+    if (x.sym) OT_HIP(launch_bias_from_pot(f, x.nx, x.hx, (int)p->n, L.npad, x.bscale, x.bx, st));
     const bool use_graph = o->use_graph != 0 && st != nullptr;
     float lse_ms = 0.f;
     int lse_launches = 0;

@@ -42,9 +42,11 @@ __device__ __forceinline__ float load_as_f32<uint16_t>(const uint16_t* p, int64_
 // potential once). Partials are (M2, S) in log2 units: the row's log-sum-exp
 // over split s is ln 2 * (M2 + log2 S). For row i:
 //   M = max_s M2_s, S = sum_s S_s 2^(M2_s - M),
-//   shifted potential = -eps ln 2 (M + log2 S),  pot_i = norm_i + shifted,
+//   shifted potential = -eps ln 2 (M + log2 S),  half-step value h_i = norm_i + shifted,
+//   pot_i = h_i, or (pot_i + h_i) / 2 for the symmetric schedule (avg),
 //   next bias_i = bscale * ((pot_i - norm_i)/2 + (eps/2) log w_i),
-//   err_i = w_i |exp((pot_old_i - pot_i)/eps) - 1|   (App. E.1 induced marginal).
+//   err_i = w_i |exp((pot_old_i - h_i)/eps) - 1|   (App. E.1 induced marginal of
+//   the coupling of the previous iterate).
 // bscale = 2 log2(e)/eps when the streamed kernel works in log2 units (fp32
 // operands packed pre-scaled), 1 when it works in dot-product units.
 // The bias is rebuilt from the stored fp32 potential, so resuming from
@@ -65,7 +67,7 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(
     const float2* __restrict__ part, int splits, int rpad, int rows, float bscale, float eps,
     const float* __restrict__ norm, const float* __restrict__ hlw, const float* __restrict__ wgt,
     float* __restrict__ pot, float* __restrict__ bias_out, float* __restrict__ err_part,
-    int with_err, int write_pot) {
+    int with_err, int write_pot, int avg) {
   __shared__ float sh[256];
   const int i = blockIdx.x * 256 + threadIdx.x;
   float e = 0.f;
@@ -79,11 +81,10 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(
     }
     const float shifted = -eps * kLn2 * (M + log2f(S));
     const float nrm = norm[i];
-    const float pnew = nrm + shifted;
-    if (with_err) {
-      const float pold = pot[i];
-      e = wgt[i] * fabsf(exp2f((pold - pnew) * (kLog2e / eps)) - 1.f);
-    }
+    const float half = nrm + shifted;
+    const float pold = (with_err || avg) ? pot[i] : 0.f;
+    if (with_err) e = wgt[i] * fabsf(exp2f((pold - half) * (kLog2e / eps)) - 1.f);
+    const float pnew = avg ? 0.5f * (pold + half) : half;
     if (write_pot) {
       pot[i] = pnew;
       bias_out[i] = bscale * (0.5f * (pnew - nrm) + hlw[i]);
@@ -417,10 +418,10 @@ hipError_t launch_bias_from_pot(const float* pot, const float* norm, const float
 hipError_t launch_lse_merge(const float2* part, int splits, int rpad, int rows, float bscale, float eps,
                             const float* norm, const float* hlw, const float* wgt, float* pot,
                             float* bias_out, float* err_part, int with_err, int write_pot,
-                            hipStream_t st) {
+                            int avg, hipStream_t st) {
   lse_merge_kernel<<<(rpad + 255) / 256, 256, 0, st>>>(part, splits, rpad, rows, bscale, eps, norm,
                                                        hlw, wgt, pot, bias_out, err_part,
-                                                       with_err, write_pot);
+                                                       with_err, write_pot, avg);
   return hipGetLastError();
 }
 

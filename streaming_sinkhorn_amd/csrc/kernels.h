@@ -59,10 +59,12 @@ inline hipError_t launch_lse_partial(const PassShape& s, int mode, const void* R
   return s.xres ? launch_lse_resident(s, mode, Rp, Cp, cbias, c, part, st)
                 : launch_lse_wide(s, mode, Rp, Cp, cbias, c, part, st);
 }
+// avg = 1: symmetric schedule, the new potential is the average of the old
+// one and the half-step value.
 hipError_t launch_lse_merge(const float2* part, int splits, int rpad, int rows, float bscale, float eps,
                             const float* norm, const float* hlw, const float* wgt, float* pot,
                             float* bias_out, float* err_part, int with_err, int write_pot,
-                            hipStream_t st);
+                            int avg, hipStream_t st);
 int lse_merge_blocks(int rows);
 hipError_t launch_err_reduce(const float* part, int count, float* out, hipStream_t st);
 hipError_t launch_nonfinite(const float* f, int n, const float* g, int m, float* out,

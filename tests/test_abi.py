@@ -136,6 +136,17 @@ def test_solve_option_validation():
         == ssa.OT_ERR_INVALID_ARG
 
 
+def test_solve_schedule_validation():
+    L = ssa.lib()
+    p = _problem()
+    sz = ctypes.c_size_t(0)
+    for sched, code in ((ssa.OT_SCHED_ALTERNATING, ssa.OT_OK), (ssa.OT_SCHED_SYMMETRIC, ssa.OT_OK),
+                        (2, ssa.OT_ERR_INVALID_ARG), (-1, ssa.OT_ERR_INVALID_ARG)):
+        opts = ssa.OtSolveOpts(5, 0.0, 1, 0, 1, 0, 0, 0, sched)
+        assert L.ot_solve(ctypes.byref(p), None, None, ctypes.byref(opts), None, None,
+                          ctypes.byref(sz), None) == code
+
+
 def test_apply_plan_validation():
     L = ssa.lib()
     p = _problem()

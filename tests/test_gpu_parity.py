@@ -174,6 +174,61 @@ def test_solve_trajectory(case):
     assert abs(info["marg_err_col"] - ec) <= 1e-2 * ec + slack
 
 
+# --- symmetric schedule ---------------------------------------------------------------
+
+SYM_CASES = [
+    # workload, n, m, d override, iters
+    ("c1", None, None, None, 30),
+    ("c2", 700, 555, None, 60),
+    ("c3_d16_bf16", 500, 650, None, 40),
+    ("c3_d128_f32", 400, 330, None, 40),
+    ("c3_d512_f32", 300, 420, None, 30),
+    ("c3_d1024_bf16", 260, 200, None, 30),
+    ("c5", 1000, 120, None, 60),
+]
+
+
+@pytest.mark.parametrize("case", SYM_CASES, ids=lambda c: c[0])
+def test_solve_symmetric_trajectory(case):
+    """Symmetric (averaged) schedule against the oracle's symmetric iteration."""
+    name, n, m, d, T = case
+    data = workloads.make(name, n=n, m=m, d=d)
+    w = data["w"]
+    say(f"symmetric {name} n={w.n} m={w.m} d={w.d} dtype={w.dtype} eps={w.eps} T={T}")
+    prob = make_problem(data)
+    X, Y, a, b = oracle_inputs(prob)
+    f, g = zeros(w.n), zeros(w.m)
+    info = ssa.ot_solve(prob, f, g, T, schedule="symmetric")
+    torch.cuda.synchronize()
+    C = oracle.cost_matrix(X, Y)
+    f_ref, g_ref = oracle.sinkhorn_symmetric(C, a, b, w.eps, T)
+    df = np.abs(host64(f) - f_ref).max()
+    dg = np.abs(host64(g) - g_ref).max()
+    say(f"  max|df|={df:.3e} max|dg|={dg:.3e}")
+    tol = POT_TOL[w.dtype]
+    assert df <= tol and dg <= tol
+    er, ec = oracle.marginal_errors(oracle.plan(C, a, b, host64(f), host64(g), w.eps), a, b)
+    slack = 5e-6 * (0.1 / w.eps)
+    assert abs(info["marg_err_row"] - er) <= 1e-2 * er + slack
+    assert abs(info["marg_err_col"] - ec) <= 1e-2 * ec + slack
+
+
+def test_symmetric_graph_eager_and_resume_bitwise():
+    data = workloads.make("c2", n=1100, m=900)
+    prob = make_problem(data)
+    outs = []
+    for use_graph in (True, False):
+        f, g = zeros(1100), zeros(900)
+        ssa.ot_solve(prob, f, g, 21, use_graph=use_graph, want_info=False, schedule="symmetric")
+        outs.append((f.clone(), g.clone()))
+    f, g = zeros(1100), zeros(900)
+    ssa.ot_solve(prob, f, g, 9, want_info=False, schedule="symmetric")
+    ssa.ot_solve(prob, f, g, 12, init_given=True, want_info=False, schedule="symmetric")
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    assert torch.equal(f, outs[0][0]) and torch.equal(g, outs[0][1])
+
+
 # --- transport application ------------------------------------------------------------
 
 APPLY_CASES = [
