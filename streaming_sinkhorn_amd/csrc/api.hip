@@ -62,17 +62,18 @@ struct KConf {
 
 // Operand layout and pass shape for a point dimension / storage type.
 //  - fp32 points use the three-part bf16 split unless the problem asks for
-//    native fp32 (allow_split false) or d is between 64 and 128, where the
-//    register-resident fp32 pass is faster;
-//  - d <= 128 fp32 / 256 bf16 / 64 split: register-resident rows;
+//    native fp32 (allow_split false);
+//  - d <= 128 (split or native fp32) / 256 bf16: register-resident rows; the
+//    split layout keeps one row tile per wave above d = 64 (24 KiB of row
+//    operand in registers);
 //  - wider: the tiled pass (column blocks of ct tiles, LDS stages of bk
 //    k-blocks), with the units per tile padded to whole stages.
 // Transport application keeps its own layout (for_apply): fp32 or bf16
 // operands, chunks of 8 k-blocks when the row operand is not resident.
 KConf kernel_conf(int64_t d, int bf16, bool allow_split, bool for_apply = false) {
   KConf k{};
-  const bool split = !bf16 && allow_split && !for_apply && (d <= 64 || d > 128);
-  if (split && d <= 64) {
+  const bool split = !bf16 && allow_split && !for_apply;
+  if (split && d <= 128) {
     k.mode = 2;
     k.kbw = 16;
     k.kblocks = ceil_div(d, 16);
@@ -82,7 +83,7 @@ KConf kernel_conf(int64_t d, int bf16, bool allow_split, bool for_apply = false)
     k.kbp = k.kb;
     k.xres = true;
     k.lds = k.kb >= 12;
-    k.ri = 2;
+    k.ri = k.kb <= 12 ? 2 : 1;
   } else {
     k.mode = split ? 2 : (bf16 ? 1 : 0);
     k.kbw = (bf16 || split) ? 16 : 8;

@@ -383,6 +383,10 @@ static hipError_t lse_split_dispatch(const PassShape& s, const void* Rp, const v
     case 3: resident_go<kModeSplit, 3>(s, Rp, Cp, cbias, c, part, st); break;
     case 6: resident_go<kModeSplit, 6>(s, Rp, Cp, cbias, c, part, st); break;
     case 12: resident_go<kModeSplit, 12>(s, Rp, Cp, cbias, c, part, st); break;
+    case 24:  // 64 < d <= 128: one resident row tile per wave, columns through LDS
+      if (!s.lds || s.ri != 1) return hipErrorInvalidValue;
+      lse_lds_go<kModeSplit, 24, 1>(s, Rp, Cp, cbias, c, part, st);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -74,7 +74,9 @@ HALF_CASES = [
 ]
 
 
-NATIVE_HALF_CASES = [c for c in HALF_CASES if c[3] == "f32" and c[2] <= 64]
+# fp32 with the fp32 matrix instruction: resident (d <= 128, LDS-shared
+# columns from d = 64) and the tiled wide pass (d > 128)
+NATIVE_HALF_CASES = [c for c in HALF_CASES if c[3] == "f32"]
 
 
 @pytest.mark.parametrize("native", [False, True])
@@ -142,6 +144,8 @@ TRAJ_CASES += [
     ("c1", None, None, None, None, True),
     ("c2", 700, 555, None, None, True),
     ("c3_d16_f32", 500, 650, None, None, True),
+    ("c3_d128_f32", 500, 650, None, None, True),
+    ("c3_d512_f32", 300, 420, None, None, True),
 ]
 
 
