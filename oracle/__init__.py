@@ -13,7 +13,10 @@ IO-Aware Entropic Optimal Transport on GPU" (arXiv 2602.03067):
 * a Sinkhorn half-step is a plain log-sum-exp over the full dense row or
   column, with no tiling, streaming or online merging;
 * the coupling, its marginals, P V, P^T U and the gradient are dense
-  products of the materialised coupling.
+  products of the materialised coupling;
+* the Hessian-vector product (``oracle.hvp``, §3.3 / App. F) is formed from
+  the dense coupling, with the pseudoinverse by eigendecomposition or the
+  damped Schur complement solved by textbook conjugate gradients.
 
 Every function is pinned by the ``-m "not gpu"`` tests in ``tests/`` against
 closed forms, textbook special cases and brute force (see each test's
@@ -41,3 +44,4 @@ from .sinkhorn import (  # noqa: F401
     plan_rows,
     plan_cols,
 )
+from . import hvp  # noqa: F401,E402
