@@ -96,8 +96,8 @@ extern "C" {
  *   a, b        device fp32 weights (n, m) or NULL for uniform
  *   x_sqn,y_sqn device fp32 squared norms ||x_i||^2, ||y_j||^2, or NULL to
  *               have them computed into the workspace
- *   flags       0, or OT_NATIVE_F32. For fp32 points with d <= 64 the
- *               log-sum-exp passes by default split every coordinate into
+ *   flags       0, or OT_NATIVE_F32. For fp32 points the log-sum-exp
+ *               passes by default split every coordinate into
  *               three bf16 parts (hi + mid + lo, 24 significant bits) and form
  *               each score from the six largest partial products on the bf16
  *               matrix cores; the dropped terms are below 2^-26 of each
@@ -237,6 +237,70 @@ int ot_solve(const ot_problem* p, float* f, float* g, const ot_solve_opts* opts,
 int ot_apply_plan(const ot_problem* p, const float* f, const float* g,
                   const void* V, int v_dtype, int64_t cols, int64_t ldv, int flags,
                   float* out, float* marg, void* ws, size_t* ws_bytes, void* stream);
+
+/*
+ * ot_apply_hadamard -- Hadamard-weighted transport from potentials
+ * (Algorithm 5 of the page, §3.3, App. F.3): out = (P . (A Y^T)) V, i.e.
+ * out_i = sum_j P_ij <a_i, y_j> v_j, without forming P or A Y^T. Used by the
+ * explicit term of the Hessian-vector product (B5 of App. F.1 with V = Y).
+ *   p       fp32 points only (OT_BF16: OT_ERR_UNSUPPORTED)
+ *   f, g    device fp32 (n, m)
+ *   A       device fp32, n x d, row stride lda >= d
+ *   V       device fp32, m x cols, row stride ldv >= cols; 1 <= cols <= OT_MAX_COLS
+ *   out     device fp32, n x cols, stride cols
+ * Errors: OT_ERR_INVALID_ARG, OT_ERR_UNSUPPORTED, OT_ERR_WORKSPACE, OT_ERR_HIP.
+ */
+int ot_apply_hadamard(const ot_problem* p, const float* f, const float* g,
+                      const float* A, int64_t lda, const float* V, int64_t cols,
+                      int64_t ldv, float* out, void* ws, size_t* ws_bytes, void* stream);
+
+/* ot_hvp options. Zero-initialise and set what you need. */
+typedef struct ot_hvp_opts {
+  float tau;          /* damping tau >= 0: the Schur system is solved as S + tau I */
+  int32_t max_iters;  /* conjugate-gradient iterations K >= 0 */
+  float tol;          /* > 0: stop once ||res|| <= tol ||rhs|| (relative residual eta);
+                         0: run all K iterations */
+} ot_hvp_opts;
+
+/* ot_hvp results (host memory). */
+typedef struct ot_hvp_info {
+  int32_t cg_iters;       /* conjugate-gradient iterations run */
+  int32_t breakdown;      /* 1: a direction with non-positive curvature stopped the solve */
+  float cg_rel_residual;  /* ||res|| / ||rhs|| when the solve ended (recursive residual) */
+} ot_hvp_info;
+
+/*
+ * ot_hvp -- Hessian-vector product G = T A of OT_eps in the source points X
+ * (Y fixed), streamed from the potentials (§3.3 Thm. 5, App. F, App. G.1
+ * "HVP"):
+ *     G = E A + (1/eps) R^T w,   H* w = R A,   H* = [[diag r, P], [P^T, diag c]]
+ * with r = P 1, c = P^T 1 the induced marginals of the coupling of (f, g).
+ *   - E A = 2 r*A - (4/eps)(B2 - B3 - B4 + B5) (App. F.1, F.3), with B5 the
+ *     Hadamard-weighted transport (P . A Y^T) Y;
+ *   - R A_i = 2 sum_j P_ij (x_i - y_j).a_i (rows), and the same sum over i
+ *     for the columns; R^T w_i = 2 sum_j P_ij (w1_i + w2_j)(x_i - y_j);
+ *   - w2 solves the damped Schur system (S + tau I) w2 = R2 - P^T (R1 / r),
+ *     S = diag c - P^T diag(1/r) P, by conjugate gradients from 0 (§3.3:
+ *     damping tau, stop at relative residual eta = tol or after K = max_iters
+ *     iterations); then w1 = (R1 - P w2) / r (App. F.2).
+ * Every transport product is streamed (3 with d or more value columns, one
+ * Hadamard-weighted, and 2 per conjugate-gradient iteration with one column);
+ * memory is O((n + m) d) beyond the split partials.
+ *   p       fp32 points only (OT_BF16: OT_ERR_UNSUPPORTED)
+ *   f, g    device fp32 (n, m): potentials, usually converged (ot_solve)
+ *   A       device fp32, n x d, row stride lda >= d: the direction
+ *   opts    host, required
+ *   out     device fp32, n x d, stride d
+ *   info    host or NULL. With tol > 0 the host reads the solver state after
+ *           every iteration (one synchronisation each); when info is non-NULL
+ *           the call synchronises the stream at the end and fills it.
+ * Errors: OT_ERR_INVALID_ARG (null pointer, lda < d, tau < 0, tol < 0,
+ * max_iters < 0, non-finite option), OT_ERR_UNSUPPORTED, OT_ERR_WORKSPACE,
+ * OT_ERR_HIP.
+ */
+int ot_hvp(const ot_problem* p, const float* f, const float* g, const float* A, int64_t lda,
+           const ot_hvp_opts* opts, float* out, ot_hvp_info* info, void* ws,
+           size_t* ws_bytes, void* stream);
 
 /* Text of the most recent error in this thread ("" if none). Host pointer, valid until the next call. */
 const char* ot_last_error(void);

@@ -76,6 +76,18 @@ class OtSolveInfo(ctypes.Structure):
         return {k: getattr(self, k) for k, _ in self._fields_}
 
 
+class OtHvpOpts(ctypes.Structure):
+    _fields_ = [("tau", ctypes.c_float), ("max_iters", ctypes.c_int32), ("tol", ctypes.c_float)]
+
+
+class OtHvpInfo(ctypes.Structure):
+    _fields_ = [("cg_iters", ctypes.c_int32), ("breakdown", ctypes.c_int32),
+                ("cg_rel_residual", ctypes.c_float)]
+
+    def as_dict(self):
+        return {k: getattr(self, k) for k, _ in self._fields_}
+
+
 _lib = None
 
 
@@ -95,7 +107,11 @@ def lib() -> ctypes.CDLL:
     L.ot_update_g.argtypes = [pp, vp, vp, vp, vp, szp, vp]
     L.ot_solve.argtypes = [pp, vp, vp, ctypes.POINTER(OtSolveOpts), ctypes.POINTER(OtSolveInfo), vp, szp, vp]
     L.ot_apply_plan.argtypes = [pp, vp, vp, vp, i32, i64, i64, i32, vp, vp, vp, szp, vp]
-    for fn in ("ot_sqnorms", "ot_update_f", "ot_update_g", "ot_solve", "ot_apply_plan"):
+    L.ot_apply_hadamard.argtypes = [pp, vp, vp, vp, i64, vp, i64, i64, vp, vp, szp, vp]
+    L.ot_hvp.argtypes = [pp, vp, vp, vp, i64, ctypes.POINTER(OtHvpOpts), vp,
+                         ctypes.POINTER(OtHvpInfo), vp, szp, vp]
+    for fn in ("ot_sqnorms", "ot_update_f", "ot_update_g", "ot_solve", "ot_apply_plan",
+               "ot_apply_hadamard", "ot_hvp"):
         getattr(L, fn).restype = ctypes.c_int
     L.ot_last_error.restype = ctypes.c_char_p
     L.ot_last_error.argtypes = []
@@ -268,6 +284,50 @@ def ot_apply_plan(prob: Problem, f, g, V=None, flags: int = 0, out=None, marg=No
     ws, size = _workspace(args, ws, prob.device)
     _check(args(_ptr(ws), ctypes.byref(size)), "ot_apply_plan")
     return out
+
+
+def _f32_rows(t, name, rows, cols, device):
+    r, c, ld = _rows(t, name)
+    if t.dtype != torch.float32 or r != rows or c != cols or t.device != device:
+        raise ValueError(f"{name} must be float32 of shape ({rows}, {cols}) on {device}")
+    return ld
+
+
+def ot_apply_hadamard(prob: Problem, f, g, A, V, out=None, ws=None):
+    """out = (P . (A Y^T)) V, streamed from the potentials (fp32 points)."""
+    L = lib()
+    lda = _f32_rows(A, "A", prob.n, prob.d, prob.device)
+    vrows, cols, ldv = _rows(V, "V")
+    _f32_rows(V, "V", prob.m, cols, prob.device)
+    if out is None:
+        out = torch.empty((prob.n, cols), dtype=torch.float32, device=prob.device)
+    st = _stream(prob.device)
+    pp = ctypes.byref(prob.c)
+    args = lambda w, s: L.ot_apply_hadamard(pp, _ptr(f), _ptr(g), _ptr(A), lda, _ptr(V), cols, ldv,
+                                            _ptr(out), w, s, st)
+    ws, size = _workspace(args, ws, prob.device)
+    _check(args(_ptr(ws), ctypes.byref(size)), "ot_apply_hadamard")
+    return out
+
+
+def ot_hvp(prob: Problem, f, g, A, tau: float = 1e-5, max_iters: int = 50, tol: float = 0.0,
+           out=None, want_info: bool = True, ws=None):
+    """Hessian-vector product T A of OT_eps in X (damped Schur complement solved by
+    conjugate gradients). Returns (out, info dict or None)."""
+    L = lib()
+    lda = _f32_rows(A, "A", prob.n, prob.d, prob.device)
+    if out is None:
+        out = torch.empty((prob.n, prob.d), dtype=torch.float32, device=prob.device)
+    opts = OtHvpOpts(float(tau), int(max_iters), float(tol))
+    info = OtHvpInfo()
+    pinfo = ctypes.byref(info) if want_info else None
+    st = _stream(prob.device)
+    pp = ctypes.byref(prob.c)
+    args = lambda w, s: L.ot_hvp(pp, _ptr(f), _ptr(g), _ptr(A), lda, ctypes.byref(opts), _ptr(out),
+                                 pinfo, w, s, st)
+    ws, size = _workspace(args, ws, prob.device)
+    _check(args(_ptr(ws), ctypes.byref(size)), "ot_hvp")
+    return out, (info.as_dict() if want_info else None)
 
 
 def solve_workspace(prob: Problem, iters: int, splits_f: int = 0, splits_g: int = 0) -> torch.Tensor:

@@ -36,7 +36,9 @@ SOURCES = [
     ("kernels_wide.hip", KERNEL_FLAGS),
     ("apply_kernels.hip", KERNEL_FLAGS),
     ("aux_kernels.hip", []),
+    ("hvp_kernels.hip", []),
     ("api.hip", []),
+    ("hvp_api.hip", []),
 ]
 
 

@@ -17,11 +17,13 @@
 #include <vector>
 
 #include "flashot.h"
+#include "host_common.h"
 #include "kernels.h"
 
 using namespace flashot;
 
-namespace {
+namespace flashot {
+namespace host {
 
 thread_local std::string g_err;
 
@@ -30,35 +32,12 @@ int fail(int code, const std::string& msg) {
   return code;
 }
 
-#define OT_HIP(expr)                                                                     \
-  do {                                                                                   \
-    hipError_t e_ = (expr);                                                              \
-    if (e_ != hipSuccess) return fail(OT_ERR_HIP, std::string(#expr) + ": " + hipGetErrorString(e_)); \
-  } while (0)
-
-constexpr float kLog2e = 1.4426950408889634f;
-
-size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
-int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
-
 int env_int(const char* name, int dflt) {
   const char* v = std::getenv(name);
   if (!v || !*v) return dflt;
   return std::atoi(v);
 }
 
-// Kernel configuration for a point dimension / storage type.
-struct KConf {
-  int mode;     // 0 fp32 operands, 1 bf16, 2 fp32 split into three bf16 parts
-  int kbw;      // dimension values per k-block (8 fp32, 16 bf16 / split)
-  int kblocks;  // k-blocks needed to cover d
-  int kb;       // 1 KiB operand units per tile held in registers (3 per k-block in split mode)
-  int kbp;      // padded operand units per tile
-  bool xres;    // row operand resident in registers
-  bool lds;     // column tiles shared by the workgroup's waves through LDS
-  int ri;       // row tiles per wave in the LSE pass
-  int ct, bk;   // tiled wide pass: column tiles per block, k-blocks per LDS stage
-};
 
 // Operand layout and pass shape for a point dimension / storage type.
 //  - fp32 points use the three-part bf16 split unless the problem asks for
@@ -70,7 +49,7 @@ struct KConf {
 //    k-blocks), with the units per tile padded to whole stages.
 // Transport application keeps its own layout (for_apply): fp32 or bf16
 // operands, chunks of 8 k-blocks when the row operand is not resident.
-KConf kernel_conf(int64_t d, int bf16, bool allow_split, bool for_apply = false) {
+KConf kernel_conf(int64_t d, int bf16, bool allow_split, bool for_apply) {
   KConf k{};
   const bool split = !bf16 && allow_split && !for_apply;
   if (split && d <= 128) {
@@ -174,6 +153,28 @@ int check_problem(const ot_problem* p) {
   if (((uintptr_t)p->x % es) || ((uintptr_t)p->y % es)) return fail(OT_ERR_INVALID_ARG, "x or y misaligned for its dtype");
   return OT_OK;
 }
+
+int check_ws(void* ws, size_t* ws_bytes, size_t need, bool* query) {
+  if (!ws_bytes) return fail(OT_ERR_INVALID_ARG, "ws_bytes is NULL");
+  if (!ws) {
+    *ws_bytes = need;
+    *query = true;
+    return OT_OK;
+  }
+  *query = false;
+  if (*ws_bytes < need) return fail(OT_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need) + " bytes");
+  if ((uintptr_t)ws % 256) return fail(OT_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  return OT_OK;
+}
+
+const char* last_error() { return g_err.c_str(); }
+
+}  // namespace host
+}  // namespace flashot
+
+namespace {
+
+using namespace flashot::host;
 
 // Workspace of the half-step / solve entry points.
 struct SolveWs {
@@ -472,18 +473,6 @@ int run_iterations_timed(const Ctx& x, hipStream_t st, int count, int with_err, 
   return OT_OK;
 }
 
-int check_ws(void* ws, size_t* ws_bytes, size_t need, bool* query) {
-  if (!ws_bytes) return fail(OT_ERR_INVALID_ARG, "ws_bytes is NULL");
-  if (!ws) {
-    *ws_bytes = need;
-    *query = true;
-    return OT_OK;
-  }
-  *query = false;
-  if (*ws_bytes < need) return fail(OT_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need) + " bytes");
-  if ((uintptr_t)ws % 256) return fail(OT_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  return OT_OK;
-}
 
 int update_impl(const ot_problem* p, const float* other, float* pot, float* err, void* ws,
                 size_t* ws_bytes, void* stream, bool is_f) {
@@ -562,7 +551,7 @@ ApplyWs apply_layout(const ot_problem* p, int64_t cols, bool transpose) {
 
 extern "C" {
 
-const char* ot_last_error(void) { return g_err.c_str(); }
+const char* ot_last_error(void) { return flashot::host::last_error(); }
 
 const char* ot_version(void) { return "flashot 0.1 gfx950"; }
 

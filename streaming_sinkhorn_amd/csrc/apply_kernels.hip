@@ -19,14 +19,20 @@ namespace flashot {
 //   O[p] = sum_j exp2(c (v_ij - M)) V[j][p]
 // accumulated as O^T (p x i) += V^T (p x j) P^T (j x i) on the matrix cores.
 // Both half-waves of a row share the running max, so O needs no merge.
+// HAD (Algorithm 5, Hadamard-weighted transport (P . A Y^T) V): a second
+// score tile W_ij = a_i . y_j is formed from the packed rows of A on the
+// same column operand, and each exponentiated score is multiplied by it
+// before the value product; S keeps the unweighted sum.
 // Grid: (nrowgroups * splits, passes); pass y covers value blocks
 // [y * PB, y * PB + PB) of 32 columns each.
 // ---------------------------------------------------------------------------
-template <bool BF16, int KB, bool XRES, int PB>
+template <bool BF16, int KB, bool XRES, int PB, bool HAD>
 __global__ __launch_bounds__(256) void apply_partial_kernel(
-    const u32x4* __restrict__ Rp, const u32x4* __restrict__ Cp, const float* __restrict__ cbias,
-    const f32x4* __restrict__ Vp, int rtiles, int ctiles, int kbp, int splits, int tps, float c,
-    int pblocks, float2* __restrict__ partMS, float* __restrict__ partO, int rpad, int ppad) {
+    const u32x4* __restrict__ Rp, const u32x4* __restrict__ Cp, const u32x4* __restrict__ Ap,
+    const float* __restrict__ cbias, const f32x4* __restrict__ Vp, int rtiles, int ctiles,
+    int kbp, int splits, int tps, float c, int pblocks, float2* __restrict__ partMS,
+    float* __restrict__ partO, int rpad, int ppad) {
+  static_assert(!(HAD && XRES), "the weighted pass streams its row operands per chunk");
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int h = lane >> 5;
@@ -50,20 +56,25 @@ __global__ __launch_bounds__(256) void apply_partial_kernel(
 
   for (int jt = jt0; jt < jt1; ++jt) {
     f32x16 acc = f32x16{};
+    f32x16 accw = f32x16{};
     if constexpr (XRES) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
         acc = mfma_kblock<BF16>(Cp[((size_t)jt * KB + kb) * 64 + lane], xr[kb], acc);
     } else {
       for (int kc = 0; kc < kbp; kc += KB) {
-        u32x4 yc[KB], xc[KB];
+        u32x4 yc[KB], xc[KB], ac[HAD ? KB : 1];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
           yc[kb] = Cp[((size_t)jt * kbp + kc + kb) * 64 + lane];
           xc[kb] = Rp[((size_t)rt * kbp + kc + kb) * 64 + lane];
+          if constexpr (HAD) ac[kb] = Ap[((size_t)rt * kbp + kc + kb) * 64 + lane];
         }
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) acc = mfma_kblock<BF16>(yc[kb], xc[kb], acc);
+        for (int kb = 0; kb < KB; ++kb) {
+          acc = mfma_kblock<BF16>(yc[kb], xc[kb], acc);
+          if constexpr (HAD) accw = mfma_kblock<BF16>(yc[kb], ac[kb], accw);
+        }
       }
     }
     acc = mfma_bias(cbias[jt * kTile + (lane & 31)], h, acc);
@@ -86,6 +97,10 @@ __global__ __launch_bounds__(256) void apply_partial_kernel(
       ssum += p[r];
     }
     S += ssum;
+    if constexpr (HAD) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) p[r] *= accw[r];
+    }
 #pragma unroll
     for (int pb = 0; pb < PB; ++pb) {
       if (pb0 + pb < pblocks) {
@@ -116,14 +131,14 @@ __global__ __launch_bounds__(256) void apply_partial_kernel(
   }
 }
 
-template <bool BF16, int KB, bool XRES, int PB>
+template <bool BF16, int KB, bool XRES, int PB, bool HAD = false>
 static void apply_go(const PassShape& s, int pblocks, const void* Rp, const void* Cp,
-                     const float* cbias, const float* Vp, float c, float2* partMS, float* partO,
-                     int ppad, hipStream_t st) {
+                     const void* Ap, const float* cbias, const float* Vp, float c,
+                     float2* partMS, float* partO, int ppad, hipStream_t st) {
   dim3 grid(s.nrowgroups * s.splits, (pblocks + PB - 1) / PB);
-  apply_partial_kernel<BF16, KB, XRES, PB><<<grid, 256, 0, st>>>(
-      (const u32x4*)Rp, (const u32x4*)Cp, cbias, (const f32x4*)Vp, s.rtiles, s.ctiles, s.kbp,
-      s.splits, s.tps, c, pblocks, partMS, partO, s.rtiles * kTile, ppad);
+  apply_partial_kernel<BF16, KB, XRES, PB, HAD><<<grid, 256, 0, st>>>(
+      (const u32x4*)Rp, (const u32x4*)Cp, (const u32x4*)Ap, cbias, (const f32x4*)Vp, s.rtiles,
+      s.ctiles, s.kbp, s.splits, s.tps, c, pblocks, partMS, partO, s.rtiles * kTile, ppad);
 }
 
 template <bool BF16, int PB>
@@ -131,15 +146,16 @@ static hipError_t apply_dispatch_kb(const PassShape& s, int pblocks, const void*
                                     const void* Cp, const float* cbias, const float* Vp, float c,
                                     float2* partMS, float* partO, int ppad, hipStream_t st) {
   if (!s.xres) {
-    apply_go<BF16, 8, false, PB>(s, pblocks, Rp, Cp, cbias, Vp, c, partMS, partO, ppad, st);
+    apply_go<BF16, 8, false, PB>(s, pblocks, Rp, Cp, nullptr, cbias, Vp, c, partMS, partO, ppad,
+                                 st);
     return hipGetLastError();
   }
   switch (s.kb) {
-    case 1: apply_go<BF16, 1, true, PB>(s, pblocks, Rp, Cp, cbias, Vp, c, partMS, partO, ppad, st); break;
-    case 2: apply_go<BF16, 2, true, PB>(s, pblocks, Rp, Cp, cbias, Vp, c, partMS, partO, ppad, st); break;
-    case 4: apply_go<BF16, 4, true, PB>(s, pblocks, Rp, Cp, cbias, Vp, c, partMS, partO, ppad, st); break;
-    case 8: apply_go<BF16, 8, true, PB>(s, pblocks, Rp, Cp, cbias, Vp, c, partMS, partO, ppad, st); break;
-    case 16: apply_go<BF16, 16, true, PB>(s, pblocks, Rp, Cp, cbias, Vp, c, partMS, partO, ppad, st); break;
+    case 1: apply_go<BF16, 1, true, PB>(s, pblocks, Rp, Cp, nullptr, cbias, Vp, c, partMS, partO, ppad, st); break;
+    case 2: apply_go<BF16, 2, true, PB>(s, pblocks, Rp, Cp, nullptr, cbias, Vp, c, partMS, partO, ppad, st); break;
+    case 4: apply_go<BF16, 4, true, PB>(s, pblocks, Rp, Cp, nullptr, cbias, Vp, c, partMS, partO, ppad, st); break;
+    case 8: apply_go<BF16, 8, true, PB>(s, pblocks, Rp, Cp, nullptr, cbias, Vp, c, partMS, partO, ppad, st); break;
+    case 16: apply_go<BF16, 16, true, PB>(s, pblocks, Rp, Cp, nullptr, cbias, Vp, c, partMS, partO, ppad, st); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -167,5 +183,36 @@ hipError_t launch_apply_partial(const PassShape& s, int bf16, int pblocks, int p
                                       partO, ppad, st);
 }
 
+// Hadamard-weighted pass, fp32 operands only. The rows of X and A are read
+// per column tile in chunks of min(kb, 8) k-blocks; every layout's unit count
+// per tile is a multiple of that chunk.
+template <int KB>
+static hipError_t hadamard_pb(const PassShape& s, int pblocks, int pb_per_pass, const void* Rp,
+                              const void* Cp, const void* Ap, const float* cbias,
+                              const float* Vp, float c, float2* partMS, float* partO, int ppad,
+                              hipStream_t st) {
+  switch (pb_per_pass) {
+    case 1: apply_go<false, KB, false, 1, true>(s, pblocks, Rp, Cp, Ap, cbias, Vp, c, partMS, partO, ppad, st); break;
+    case 2: apply_go<false, KB, false, 2, true>(s, pblocks, Rp, Cp, Ap, cbias, Vp, c, partMS, partO, ppad, st); break;
+    case 4: apply_go<false, KB, false, 4, true>(s, pblocks, Rp, Cp, Ap, cbias, Vp, c, partMS, partO, ppad, st); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_apply_hadamard(const PassShape& s, int pblocks, int pb_per_pass, const void* Rp,
+                                 const void* Cp, const void* Ap, const float* cbias,
+                                 const float* Vp, float c, float2* partMS, float* partO, int ppad,
+                                 hipStream_t st) {
+  const int chunk = s.kbp < 8 ? s.kbp : 8;
+  if (s.kbp % chunk) return hipErrorInvalidValue;
+  switch (chunk) {
+    case 1: return hadamard_pb<1>(s, pblocks, pb_per_pass, Rp, Cp, Ap, cbias, Vp, c, partMS, partO, ppad, st);
+    case 2: return hadamard_pb<2>(s, pblocks, pb_per_pass, Rp, Cp, Ap, cbias, Vp, c, partMS, partO, ppad, st);
+    case 4: return hadamard_pb<4>(s, pblocks, pb_per_pass, Rp, Cp, Ap, cbias, Vp, c, partMS, partO, ppad, st);
+    case 8: return hadamard_pb<8>(s, pblocks, pb_per_pass, Rp, Cp, Ap, cbias, Vp, c, partMS, partO, ppad, st);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 }  // namespace flashot

@@ -1,0 +1,55 @@
+// Host-side helpers shared by the C-ABI translation units: error text,
+// HIP status checks, operand layout / pass shape selection, argument and
+// workspace checks.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+#include "flashot.h"
+#include "kernels.h"
+
+namespace flashot {
+namespace host {
+
+// Records msg as the thread's last error and returns code.
+int fail(int code, const std::string& msg);
+const char* last_error();
+
+#define OT_HIP(expr)                                                                     \
+  do {                                                                                   \
+    hipError_t e_ = (expr);                                                              \
+    if (e_ != hipSuccess)                                                                \
+      return ::flashot::host::fail(OT_ERR_HIP, std::string(#expr) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+inline int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+// Kernel configuration for a point dimension / storage type.
+struct KConf {
+  int mode;     // 0 fp32 operands, 1 bf16, 2 fp32 split into three bf16 parts
+  int kbw;      // dimension values per k-block (8 fp32, 16 bf16 / split)
+  int kblocks;  // k-blocks needed to cover d
+  int kb;       // 1 KiB operand units per tile held in registers (3 per k-block in split mode)
+  int kbp;      // padded operand units per tile
+  bool xres;    // row operand resident in registers
+  bool lds;     // column tiles shared by the workgroup's waves through LDS
+  int ri;       // row tiles per wave in the LSE pass
+  int ct, bk;   // tiled wide pass: column tiles per block, k-blocks per LDS stage
+};
+
+KConf kernel_conf(int64_t d, int bf16, bool allow_split, bool for_apply = false);
+PassShape make_pass(int rtiles, int ctiles, const KConf& k, int ri, int forced, int max_splits);
+int check_problem(const ot_problem* p);
+// ws == NULL: writes need to *ws_bytes and sets *query; otherwise checks size
+// and alignment.
+int check_ws(void* ws, size_t* ws_bytes, size_t need, bool* query);
+
+}  // namespace host
+}  // namespace flashot

@@ -73,6 +73,12 @@ hipError_t launch_apply_partial(const PassShape& s, int bf16, int pblocks, int p
                                 const void* Rp, const void* Cp, const float* cbias,
                                 const float* Vp, float c, float2* partMS, float* partO, int ppad,
                                 hipStream_t st);
+// Hadamard-weighted transport (P . A Y^T) V (fp32 operands): Ap holds the rows
+// of A packed like Rp.
+hipError_t launch_apply_hadamard(const PassShape& s, int pblocks, int pb_per_pass, const void* Rp,
+                                 const void* Cp, const void* Ap, const float* cbias,
+                                 const float* Vp, float c, float2* partMS, float* partO, int ppad,
+                                 hipStream_t st);
 hipError_t launch_apply_merge(const float2* partMS, const float* partO, int splits, int rpad,
                               int ppad, int rows, int cols, float c, float eps, const float* pot,
                               const float* norm, const float* wgt, int mode, const void* Xsrc,
@@ -82,5 +88,38 @@ hipError_t launch_apply_merge(const float2* partMS, const float* partO, int spli
 constexpr int kApplyPlain = 0;
 constexpr int kApplyBary = 1;
 constexpr int kApplyGrad = 2;
+
+// ---- Hessian-vector product (hvp_kernels.hip) ------------------------------------
+// Conjugate-gradient state in device memory (scalars of the recurrence and
+// the stop flags), so that iterations need no host round trip.
+struct CgState {
+  float rr;      // ||res||^2
+  float bb;      // ||rhs||^2
+  float alpha;
+  float beta;
+  int iters;     // iterations completed
+  int breakdown; // non-positive curvature met
+  int done;      // converged, broke down, or zero right side
+  int pad;
+};
+constexpr int kCgMaxParts = 256;  // partial sums per reduction
+int cg_parts(int len);
+hipError_t launch_hvp_prep(int n, int d, const float* X, int64_t ldx, const float* A, int64_t lda,
+                           const float* PY, const float* r, float* xa, float* ra1, float* VB,
+                           hipStream_t st);
+hipError_t launch_hvp_rhs(int m, int d, const float* Y, int64_t ldy, const float* PTV, float* rhs,
+                          float* w2, float* res, float* pdir, hipStream_t st);
+hipError_t launch_cg_start(int m, const float* rhs, float* part, CgState* cs, hipStream_t st);
+hipError_t launch_cg_div(int n, const float* Pp, const float* r, float* u, const CgState* cs,
+                         hipStream_t st);
+hipError_t launch_cg_update(int m, const float* c, const float* PTu, float tau, float tol,
+                            float* pdir, float* q, float* w2, float* res, float* part,
+                            CgState* cs, hipStream_t st);
+hipError_t launch_hvp_vf(int m, int d, const float* Y, int64_t ldy, const float* w2, float* VF,
+                         hipStream_t st);
+hipError_t launch_hvp_final(int n, int d, float eps, const float* X, int64_t ldx, const float* A,
+                            int64_t lda, const float* PY, const float* r, const float* xa,
+                            const float* ra1, const float* PF, const float* B5, float* out,
+                            hipStream_t st);
 
 }  // namespace flashot

@@ -168,3 +168,64 @@ def test_binding_refuses_to_run_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(ssa, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         ssa.lib()
+
+
+# --- second-order entry points ------------------------------------------------------
+
+def _hvp_size(p, opts, lda=16):
+    L = ssa.lib()
+    sz = ctypes.c_size_t(0)
+    rc = L.ot_hvp(ctypes.byref(p), None, None, None, lda, None if opts is None else ctypes.byref(opts),
+                  None, None, None, ctypes.byref(sz), None)
+    return rc, sz.value
+
+
+def test_hvp_and_hadamard_workspace_queries():
+    L = ssa.lib()
+    opts = ssa.OtHvpOpts(1e-5, 50, 0.0)
+    rc1, s1 = _hvp_size(_problem(1000, 800, 16), opts)
+    rc2, s2 = _hvp_size(_problem(2000, 800, 16), opts)
+    assert rc1 == 0 and rc2 == 0 and 0 < s1 < s2
+    sz = ctypes.c_size_t(0)
+    assert L.ot_apply_hadamard(ctypes.byref(_problem(1000, 800, 16)), None, None, None, 16, None,
+                               8, 8, None, None, ctypes.byref(sz), None) == 0
+    assert 0 < sz.value < s1
+
+
+@pytest.mark.parametrize("tau,iters,tol,code", [
+    (-1e-5, 50, 0.0, ssa.OT_ERR_INVALID_ARG),
+    (float("nan"), 50, 0.0, ssa.OT_ERR_INVALID_ARG),
+    (float("inf"), 50, 0.0, ssa.OT_ERR_INVALID_ARG),
+    (1e-5, -1, 0.0, ssa.OT_ERR_INVALID_ARG),
+    (1e-5, 50, -1e-6, ssa.OT_ERR_INVALID_ARG),
+    (1e-5, 50, float("nan"), ssa.OT_ERR_INVALID_ARG),
+])
+def test_hvp_option_validation(tau, iters, tol, code):
+    rc, _ = _hvp_size(_problem(), ssa.OtHvpOpts(tau, iters, tol))
+    assert rc == code, ssa.lib().ot_last_error()
+
+
+def test_hvp_rejects_bf16_missing_opts_and_short_lda():
+    L = ssa.lib()
+    opts = ssa.OtHvpOpts(1e-5, 50, 0.0)
+    rc, _ = _hvp_size(_problem(dtype=ssa.OT_BF16), opts)
+    assert rc == ssa.OT_ERR_UNSUPPORTED
+    rc, _ = _hvp_size(_problem(), None)
+    assert rc == ssa.OT_ERR_INVALID_ARG
+    # past the size query: null potentials, then a short lda, are rejected on the host
+    p = _problem()
+    sz = ctypes.c_size_t(1 << 40)
+    fake = ctypes.c_void_p(1 << 24)
+    rc = L.ot_hvp(ctypes.byref(p), None, None, None, 16, ctypes.byref(opts), None, None, fake,
+                  ctypes.byref(sz), None)
+    assert rc == ssa.OT_ERR_INVALID_ARG and "NULL" in L.ot_last_error().decode()
+    rc = L.ot_hvp(ctypes.byref(p), fake, fake, fake, 15, ctypes.byref(opts), fake, None, fake,
+                  ctypes.byref(sz), None)
+    assert rc == ssa.OT_ERR_INVALID_ARG and "lda" in L.ot_last_error().decode()
+    sz = ctypes.c_size_t(0)
+    rc = L.ot_apply_hadamard(ctypes.byref(_problem(dtype=ssa.OT_BF16)), None, None, None, 16, None,
+                             8, 8, None, None, ctypes.byref(sz), None)
+    assert rc == ssa.OT_ERR_UNSUPPORTED
+    rc = L.ot_apply_hadamard(ctypes.byref(_problem()), None, None, None, 16, None, 0, 8, None,
+                             None, ctypes.byref(sz), None)
+    assert rc == ssa.OT_ERR_INVALID_ARG

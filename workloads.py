@@ -158,3 +158,17 @@ def make(name: str, n: int | None = None, m: int | None = None, d: int | None = 
         U = _rng(w, "U").standard_normal((n, u_cols)).astype(np.float32)
         out["U"] = bf16_round(U) if w.dtype == "bf16" else U
     return out
+
+
+def hvp_parity_inputs(n: int, m: int, d: int, seed: int) -> dict:
+    """Inputs of the Hessian-vector-product parity protocol of the page (App. H.2.3
+    "HVP Parity": X, Y ~ N(0, I_d), a, b random simplex weights), plus the
+    direction A ~ N(0, I) (n x d). float32 arrays X, Y, A, a, b."""
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((n, d))
+    Y = rng.standard_normal((m, d))
+    a = rng.exponential(1.0, n)
+    b = rng.exponential(1.0, m)
+    A = rng.standard_normal((n, d))
+    f32 = lambda v: np.ascontiguousarray(v, dtype=np.float32)
+    return dict(X=f32(X), Y=f32(Y), A=f32(A), a=f32(a / a.sum()), b=f32(b / b.sum()))
