@@ -124,6 +124,115 @@ def copy_probe(mib):
     print(json.dumps({"copy_probe_bytes": n * 4, "copies": 3}), flush=True)
 
 
+def hvp_cpu_baseline(data, tau, K, rows=3000):
+    """fp64 oracle HVP (dense coupling, damped Schur CG) on the first `rows` points
+    of each cloud; seconds per call, and that time scaled to the full n x m by
+    the pair count."""
+    import numpy as np
+
+    import oracle
+
+    w = data["w"]
+    X = data["X"][:rows].astype(np.float64)
+    Y = data["Y"][:rows].astype(np.float64)
+    A = data["A"][:rows].astype(np.float64)
+    a = np.full(rows, 1.0 / rows)
+    b = np.full(rows, 1.0 / rows)
+    f, g = oracle.sinkhorn(oracle.cost_matrix(X, Y), a, b, w.eps, 20)
+    t0 = time.perf_counter()
+    oracle.hvp.hvp_schur_cg(X, Y, a, b, f, g, w.eps, A, tau=tau, iters=K)
+    dt = time.perf_counter() - t0
+    return {
+        "value": dt * (float(w.n) * w.m) / (rows * rows),
+        "unit": "s per HVP (scaled to the full n*m by pair count)",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"fp64 numpy oracle HVP (dense coupling, K={K} CG iterations) on n=m={rows} "
+                  f"points of the same workload: {dt:.2f} s; scaled by n*m / {rows}^2",
+    }
+
+
+def hvp_main(args):
+    """Streaming Hessian-vector product on the page's HVP benchmark shape."""
+    import torch
+
+    import streaming_sinkhorn_amd as ssa
+    import workloads
+
+    ssa.lib()
+    name = args.workload if args.workload.startswith("hvp") else "hvp_n50k_d64"
+    data = workloads.make(name)
+    w = data["w"]
+    K, tau = args.hvp_iters, 1e-5
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    X = torch.from_numpy(data["X"]).to(dev)
+    Y = torch.from_numpy(data["Y"]).to(dev)
+    A = torch.from_numpy(data["A"]).to(dev)
+    prob = ssa.problem(X, Y, w.eps)
+    f = torch.zeros(w.n, device=dev)
+    g = torch.zeros(w.m, device=dev)
+    out = torch.empty((w.n, w.d), device=dev)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        ssa.ot_solve(prob, f, g, w.iters, want_info=False)  # potentials, outside the timed region
+        ws = ssa.hvp_workspace(prob)
+        for _ in range(args.warmup):
+            ssa.ot_hvp(prob, f, g, A, tau=tau, max_iters=K, out=out, want_info=False, ws=ws)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for k in range(args.steps):
+            ssa.ot_hvp(prob, f, g, A, tau=tau, max_iters=K, out=out, want_info=False, ws=ws)
+            print(f"# hvp {k + 1}/{args.steps} enqueued", file=sys.stderr, flush=True)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    sec = (t1 - t0) / args.steps
+    ev_sec = e0.elapsed_time(e1) / 1e3 / args.steps
+    pairs = float(w.n) * w.m
+    # Transport passes per HVP: (value columns, count, weighted). Algorithmic
+    # fp32 flops per pair: the score (2 d; twice in the weighted pass, which
+    # also forms A Y^T) plus the value product (2 per column).
+    passes = [(w.d, 1, False),      # P Y and r
+              (w.d + 2, 1, False),  # P^T [A, <x, a>, R1 / r] and c
+              (1, 2 * K, False),    # conjugate gradients: P p, P^T u
+              (w.d + 1, 1, False),  # back-substitution: P [w2 y, w2]
+              (w.d, 1, True)]       # (P . A Y^T) Y
+    alg = sum(cnt * pairs * (2.0 * w.d * (2 if wt else 1) + 2.0 * cols) for cols, cnt, wt in passes)
+    achieved = alg / ev_sec / 1e12
+    res = {
+        "metric": f"streaming HVP time per call (n=m={w.n}, d={w.d}, K={K} CG, tau={tau})",
+        "value": sec,
+        "unit": "s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": sec * 1e3,
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: n={w.n}, m={w.m}, d={w.d}, fp32 points uniform in "
+                               f"[0,1]^d, uniform weights, eps={w.eps}; potentials from {w.iters} "
+                               f"iterations (untimed); HVP with K={K} fixed CG iterations, tau={tau}",
+                   "n": w.n, "m": w.m, "d": w.d, "eps": w.eps, "cg_iters": K,
+                   "transport_passes": 2 * K + 4},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_PEAK_TFLOPS["f32"],
+                     "unit": "TFLOP/s", "frac": achieved / MFMA_PEAK_TFLOPS["f32"],
+                     "traffic": None,
+                     "kernel": "all transport passes of one HVP (apply_partial_kernel), "
+                               "algorithmic fp32 flops over the event-timed call",
+                     "event_sec_per_hvp": ev_sec},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = hvp_cpu_baseline(data, tau, K)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -138,6 +247,9 @@ def main():
     ap.add_argument("--native-f32", action="store_true",
                     help="form fp32 scores with the fp32 matrix instruction instead of the "
                          "three-part bf16 split")
+    ap.add_argument("--hvp", action="store_true",
+                    help="time the streaming Hessian-vector product instead of the solve")
+    ap.add_argument("--hvp-iters", type=int, default=50, help="CG iterations K of --hvp")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the path runs "
@@ -145,6 +257,9 @@ def main():
         sys.exit(2)
     if args.copy_probe:
         copy_probe(args.copy_probe)
+        return
+    if args.hvp:
+        hvp_main(args)
         return
 
     import torch

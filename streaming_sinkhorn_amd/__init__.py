@@ -330,6 +330,16 @@ def ot_hvp(prob: Problem, f, g, A, tau: float = 1e-5, max_iters: int = 50, tol: 
     return out, (info.as_dict() if want_info else None)
 
 
+def hvp_workspace(prob: Problem) -> torch.Tensor:
+    """Allocate the workspace ot_hvp needs for this problem."""
+    L = lib()
+    opts = OtHvpOpts(0.0, 0, 0.0)
+    size = ctypes.c_size_t(0)
+    _check(L.ot_hvp(ctypes.byref(prob.c), None, None, None, prob.d, ctypes.byref(opts), None, None,
+                    None, ctypes.byref(size), None), "ot_hvp workspace query")
+    return torch.empty(max(size.value, 256), dtype=torch.uint8, device=prob.device)
+
+
 def solve_workspace(prob: Problem, iters: int, splits_f: int = 0, splits_g: int = 0) -> torch.Tensor:
     """Allocate the workspace ot_solve needs for this problem (size query + torch allocation)."""
     L = lib()

@@ -2,22 +2,22 @@
 
 Every workload runs at its full shape (up to n = 200000, d = 1024) through
 the C ABI with the same entry points and the same automatic launch
-configuration (column splits, tile shapes, plain launches with event timing)
-that ``bench.py`` times. The dense oracle cannot run those sizes, so the
-check is teacher-forced on a seeded sample of outputs, each computed by the
-oracle one row or one column at a time:
+configuration (column splits, tile shapes) that ``bench.py`` times. The dense
+oracle cannot run those sizes, so the checks are teacher-forced on a seeded
+sample of outputs, each computed by the oracle one row or one column at a
+time, and every input of the oracle is seeded or the oracle's own:
 
-* the last f half-step: f_T[i] for sampled rows i equals the oracle's
-  f-update of row i from the GPU's own g_{T-1} (all m columns);
-* the last g half-step: g_T[j] for sampled columns j equals the oracle's
-  g-update of column j from the GPU's f_T (all n rows);
-* transport application: sampled rows of P V (and of the X-gradient) and
-  sampled columns-as-rows of P^T U against the oracle's rows / columns of the
-  coupling induced by the GPU's (f_T, g_T).
+* potentials f0 = ||x||^2 + u, g0 = ||y||^2 + v (norms from the oracle,
+  offsets u, v ~ 0.1 N(0, 1) from ``workloads``), rounded to fp32, are given
+  to both sides;
+* f half-step: the GPU's ot_update_f from g0 (the pass shape and split count
+  ot_solve uses) against the oracle's f-update of sampled rows i from g0;
+* g half-step: ot_update_g from f0 against sampled columns;
+* transport application of the coupling of (f0, g0): sampled rows of P V,
+  r and the X-gradient, sampled columns of P^T U and c;
+* the full solve (T iterations, launched as bench.py launches it) must end
+  with finite potentials and small reported marginal errors.
 
-Resuming from returned potentials is bit-identical to an uninterrupted run
-(checked in test_gpu_parity), so splitting the solve into T-1 iterations and
-one more iteration observes exactly the state of a T-iteration solve.
 Tolerances: 1e-4 (fp32 inputs) / 2e-2 (bf16 inputs) on potentials; relative
 error 1e-4 on rows of P V, P^T U and the marginals for fp32 inputs. For bf16
 inputs the P V gate is 1e-3, derived from the fp32 arithmetic of the score:
@@ -73,31 +73,30 @@ def test_full_size_sampled(name):
     a = torch.from_numpy(data["a"]).to(DEV)
     b = torch.from_numpy(data["b"]).to(DEV)
     prob = ssa.problem(X, Y, w.eps, a, b)
-    f, g = zeros(w.n), zeros(w.m)
-    # T-1 iterations, keep g_{T-1}, then the last iteration (same launches as bench.py).
-    ssa.ot_solve(prob, f, g, T - 1, timing=True)
-    g_prev = g.clone()
-    info = ssa.ot_solve(prob, f, g, 1, init_given=True, timing=True)
-    torch.cuda.synchronize()
-    assert not info["nonfinite"]
-    say(f"  splits f/g = {info['splits_f']}/{info['splits_g']}, marg err row {info['marg_err_row']:.3e}")
-
     Xh, Yh = host64(X), host64(Y)
     ah, bh = data["a"].astype(np.float64), data["b"].astype(np.float64)
-    fh, gh, gph = host64(f), host64(g), host64(g_prev)
+    u, v = workloads.potential_offsets(w.n, w.m, seed=w.config * 100 + w.variant)
+    f0 = (oracle.sqnorms(Xh) + u).astype(np.float32)
+    g0 = (oracle.sqnorms(Yh) + v).astype(np.float32)
+    f0h, g0h = f0.astype(np.float64), g0.astype(np.float64)
     tol = POT_TOL[w.dtype]
-
     rows = _sample(w.n, ROW_SAMPLES.get(name, 64), 1)
-    f_ref = oracle.update_f_rows(Xh[rows], Yh, gph, bh, w.eps)
-    df = np.abs(fh[rows] - f_ref).max()
     cols = _sample(w.m, COL_SAMPLES.get(name, 32), 2)
-    g_ref = oracle.update_g_cols(Xh, Yh[cols], fh, ah, w.eps)
-    dg = np.abs(gh[cols] - g_ref).max()
-    say(f"  sampled max|df|={df:.3e} ({len(rows)} rows)  max|dg|={dg:.3e} ({len(cols)} cols)")
+
+    # Teacher-forced half-steps.
+    f = torch.from_numpy(f0).to(DEV)
+    g = torch.from_numpy(g0).to(DEV)
+    f1, g1 = f.clone(), g.clone()
+    ssa.ot_update_f(prob, g, f1)
+    ssa.ot_update_g(prob, f, g1)
+    torch.cuda.synchronize()
+    df = np.abs(host64(f1)[rows] - oracle.update_f_rows(Xh[rows], Yh, g0h, bh, w.eps)).max()
+    dg = np.abs(host64(g1)[cols] - oracle.update_g_cols(Xh, Yh[cols], f0h, ah, w.eps)).max()
+    say(f"  half-steps: sampled max|df|={df:.3e} ({len(rows)} rows)  max|dg|={dg:.3e} ({len(cols)} cols)")
     assert df <= tol and dg <= tol
 
-    # Transport application with the workload's own value matrices.
-    Prow = oracle.plan_rows(Xh[rows], Yh, ah[rows], bh, fh[rows], gh, w.eps)
+    # Transport application of the coupling of (f0, g0).
+    Prow = oracle.plan_rows(Xh[rows], Yh, ah[rows], bh, f0h[rows], g0h, w.eps)
     if w.grad:
         grad = ssa.ot_apply_plan(prob, f, g, flags=ssa.OT_GRAD)
         torch.cuda.synchronize()
@@ -120,9 +119,19 @@ def test_full_size_sampled(name):
         c = torch.empty(w.m, dtype=torch.float32, device=DEV)
         ptu = ssa.ot_apply_plan(prob, f, g, U, flags=ssa.OT_TRANSPOSE, marg=c)
         torch.cuda.synchronize()
-        Pcol = oracle.plan_cols(Xh, Yh[cols], ah, bh[cols], fh, gh[cols], w.eps)
+        Pcol = oracle.plan_cols(Xh, Yh[cols], ah, bh[cols], f0h, g0h[cols], w.eps)
         ref = Pcol.T @ host64(U)
         err = np.linalg.norm(host64(ptu)[cols] - ref) / np.linalg.norm(ref)
         cerr = np.abs(host64(c)[cols] - Pcol.sum(axis=0)).max() / Pcol.sum(axis=0).max()
         say(f"  P^T U cols rel err {err:.3e}, c rel err {cerr:.3e}")
         assert err <= PV_TOL[w.dtype] and cerr <= PV_TOL[w.dtype]
+
+    # The full solve as bench.py runs it: T iterations from zero potentials.
+    fs, gs = zeros(w.n), zeros(w.m)
+    info = ssa.ot_solve(prob, fs, gs, T, timing=True)
+    torch.cuda.synchronize()
+    say(f"  solve: splits f/g = {info['splits_f']}/{info['splits_g']}, marg err row "
+        f"{info['marg_err_row']:.3e} col {info['marg_err_col']:.3e}")
+    assert not info["nonfinite"] and info["iters_done"] == T
+    # the last half-step fits the columns; the rows are within the iteration's progress
+    assert info["marg_err_col"] <= 1e-3 and info["marg_err_row"] <= 1e-2

@@ -19,7 +19,12 @@ representable values):
 
   seed(array) = 1000 * config + 10 * variant + index,
   index: x=0, y=1, a=2, b=3, V=4, U=5, x-mixture means=6, y-mixture means=7,
-         x labels=8, y labels=9.
+         x labels=8, y labels=9, HVP direction A=10.
+
+The Hessian-vector-product workload follows the page's own HVP benchmark
+(App. H.2: points uniform in [0,1]^d, uniform marginals, eps = 0.1, 100
+Sinkhorn iterations, then conjugate gradients with K = 50, tau = 1e-5), at
+its largest size n = m = 50000, d = 64, with a direction A ~ N(0, 1).
 """
 
 from __future__ import annotations
@@ -29,7 +34,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-_IDX = dict(x=0, y=1, a=2, b=3, V=4, U=5, mx=6, my=7, lx=8, ly=9)
+_IDX = dict(x=0, y=1, a=2, b=3, V=4, U=5, mx=6, my=7, lx=8, ly=9, A=10)
 
 
 @dataclass(frozen=True)
@@ -79,6 +84,10 @@ WORKLOADS = {
     # n=200000, m=10000, d=1024, fp32, eps=0.01, 300 iterations; P V and P^T U.
     "c5": Workload("c5", 5, 0, 200000, 10000, 1024, "f32", 0.01, 300,
                    "gauss", "uniform_box", "lognormal", v_cols=128, u_cols=128),
+    # Hessian-vector product: n=m=50000, d=64, uniform [0,1]^d points, eps=0.1,
+    # 100 iterations, then CG with K=50, tau=1e-5 (direction A ~ N(0,1)).
+    "hvp_n50k_d64": Workload("hvp_n50k_d64", 6, 0, 50000, 50000, 64, "f32", 0.1, 100,
+                             "unit_box", "unit_box", "uniform", extra={"hvp_A": True}),
 }
 
 
@@ -102,6 +111,8 @@ def _points(w: Workload, rows: int, dist: str, key: str, mkey: str, lkey: str) -
         P = rng.standard_normal((rows, d)) * s
     elif dist == "gauss_shift":            # (N(0, I_d) + 1) / sqrt(d): unit mean shift
         P = (rng.standard_normal((rows, d)) + 1.0) * s
+    elif dist == "unit_box":               # Uniform[0, 1]^d (page's synthetic benchmark points)
+        P = rng.uniform(0.0, 1.0, (rows, d))
     elif dist == "uniform_box":            # Uniform[-1, 1]^d / sqrt(d)
         P = rng.uniform(-1.0, 1.0, (rows, d)) * s
     elif dist == "mixture":                # 10 components, means ~ N(0, 4 I)/sqrt(d), std 0.5/sqrt(d)
@@ -157,6 +168,8 @@ def make(name: str, n: int | None = None, m: int | None = None, d: int | None = 
     if u_cols:
         U = _rng(w, "U").standard_normal((n, u_cols)).astype(np.float32)
         out["U"] = bf16_round(U) if w.dtype == "bf16" else U
+    if w.extra.get("hvp_A"):
+        out["A"] = _rng(w, "A").standard_normal((n, d)).astype(np.float32)
     return out
 
 
@@ -172,3 +185,12 @@ def hvp_parity_inputs(n: int, m: int, d: int, seed: int) -> dict:
     A = rng.standard_normal((n, d))
     f32 = lambda v: np.ascontiguousarray(v, dtype=np.float32)
     return dict(X=f32(X), Y=f32(Y), A=f32(A), a=f32(a / a.sum()), b=f32(b / b.sum()))
+
+
+def potential_offsets(n: int, m: int, seed: int, scale: float = 0.1) -> tuple[np.ndarray, np.ndarray]:
+    """Seeded offsets u (n), v (m) ~ scale * N(0, 1), float32: test potentials are
+    formed as f = ||x||^2 + u, g = ||y||^2 + v, so that both sides of a
+    teacher-forced check receive the same realistic-scale inputs."""
+    rng = np.random.default_rng(seed)
+    return ((rng.standard_normal(n) * scale).astype(np.float32),
+            (rng.standard_normal(m) * scale).astype(np.float32))
