@@ -14,6 +14,8 @@ IO-Aware Entropic Optimal Transport on GPU" (arXiv 2602.03067):
   column, with no tiling, streaming or online merging;
 * the coupling, its marginals, P V, P^T U and the gradient are dense
   products of the materialised coupling;
+* affine, cosine and label-augmented costs (``oracle.costs``, §3.1 "Scope
+  of cost structure", §4.2) are dense matrices from their plain definitions;
 * the Hessian-vector product (``oracle.hvp``, §3.3 / App. F) is formed from
   the dense coupling, with the pseudoinverse by eigendecomposition or the
   damped Schur complement solved by textbook conjugate gradients.
@@ -45,3 +47,4 @@ from .sinkhorn import (  # noqa: F401
     plan_cols,
 )
 from . import hvp  # noqa: F401,E402
+from . import costs  # noqa: F401,E402
