@@ -82,6 +82,9 @@ extern "C" {
 /* ot_problem flags. */
 #define OT_NATIVE_F32 1  /* fp32 points: form scores with fp32 MFMA instead of the default
                             exact-to-fp32 split into three bf16 parts on the bf16 MFMA */
+#define OT_COST_AFFINE 2 /* general affine cost C_ij = alpha_i + beta_j - <x_i, y_j>
+                            (§3.1 "Scope of cost structure"): x_sqn carries alpha and
+                            y_sqn carries beta, both required */
 
 /*
  * The problem: two point clouds, their weights and eps (App. H.2 problem
@@ -96,7 +99,17 @@ extern "C" {
  *   a, b        device fp32 weights (n, m) or NULL for uniform
  *   x_sqn,y_sqn device fp32 squared norms ||x_i||^2, ||y_j||^2, or NULL to
  *               have them computed into the workspace
- *   flags       0, or OT_NATIVE_F32. For fp32 points the log-sum-exp
+ *   flags       0, or OT_NATIVE_F32 and / or OT_COST_AFFINE.
+ *               OT_COST_AFFINE replaces the squared-Euclidean cost by
+ *               C_ij = alpha_i + beta_j - <x_i, y_j> with alpha = x_sqn and
+ *               beta = y_sqn (both must be given): x, y are the features Q, K
+ *               of §3.1. The kernels are the same (x is packed halved, which
+ *               is exact, so that the squared-Euclidean score 2 <x, y> becomes
+ *               <x, y>). The cosine and label-augmented costs are affine
+ *               costs built by ot_prep_cosine / ot_prep_labels. OT_GRAD,
+ *               ot_hvp and ot_apply_hadamard assume the squared-Euclidean
+ *               cost and reject the flag.
+ *               For fp32 points the log-sum-exp
  *               passes by default split every coordinate into
  *               three bf16 parts (hi + mid + lo, 24 significant bits) and form
  *               each score from the six largest partial products on the bf16
@@ -301,6 +314,47 @@ typedef struct ot_hvp_info {
 int ot_hvp(const ot_problem* p, const float* f, const float* g, const float* A, int64_t lda,
            const ot_hvp_opts* opts, float* out, ot_hvp_info* info, void* ws,
            size_t* ws_bytes, void* stream);
+
+/*
+ * ot_prep_cosine -- features of the cosine cost C_ij = 1 - <x_i, y_j> /
+ * (||x_i|| ||y_j||) as an affine cost (§3.1 "Scope of cost structure": the
+ * cosine cost is reached by L2-normalising the points). Writes
+ * out_i = pts_i / ||pts_i|| (a row of zero norm stays zero, giving cost 1
+ * against every point) and half_i = 1/2, so that with OT_COST_AFFINE,
+ * x = out_x, y = out_y, x_sqn = half_x, y_sqn = half_y the problem's cost is
+ * 1/2 + 1/2 - <x^_i, y^_j>.
+ *   pts     device, rows x d, row stride ld >= d, storage dtype (OT_F32 / OT_BF16)
+ *   out     device fp32, rows x d, stride d
+ *   half    device fp32, rows
+ * Errors: OT_ERR_INVALID_ARG (null pointer, rows or d < 1, ld < d),
+ * OT_ERR_UNSUPPORTED (dtype, d > OT_MAX_D), OT_ERR_HIP. Enqueued on stream.
+ */
+int ot_prep_cosine(const void* pts, int dtype, int64_t rows, int64_t d, int64_t ld, float* out,
+                   float* half, void* stream);
+
+/*
+ * ot_prep_labels -- features of the label-augmented cost
+ * C_ij = ||x_i - y_j||^2 + W[l_i, l_j] (the OTDD cost of §4.2: feature
+ * distance plus a label-to-label term, looked up per pair) as an affine
+ * cost. The lookup is folded into the matrix product by one-hot label
+ * features, with L = n_labels extra columns:
+ *   side 0 (source x):  out_i = [2 x_i, -W[l_i, 0..L-1]]
+ *   side 1 (target y):  out_j = [y_j, e_{l_j}]           (one-hot)
+ * so that <out_i, out_j> = 2 <x_i, y_j> - W[l_i, l_j]; sqn receives
+ * ||pts_i||^2 (alpha or beta). Use the outputs with OT_COST_AFFINE (x_sqn =
+ * source sqn, y_sqn = target sqn), dimension d + L.
+ *   pts      device, rows x d, row stride ld >= d, storage dtype
+ *   labels   device int32, rows, each in [0, n_labels); a label outside that
+ *            range gets zero label features (no label term for its pairs)
+ *   W        device fp32, n_labels x n_labels, row-major
+ *   out      device fp32, rows x (d + n_labels), stride d + n_labels
+ *   sqn      device fp32, rows
+ * Errors: OT_ERR_INVALID_ARG (null pointer, sizes < 1, ld < d, side not 0/1),
+ * OT_ERR_UNSUPPORTED (dtype, d + n_labels > OT_MAX_D), OT_ERR_HIP.
+ */
+int ot_prep_labels(const void* pts, int dtype, int64_t rows, int64_t d, int64_t ld,
+                   const int32_t* labels, const float* W, int32_t n_labels, int32_t side,
+                   float* out, float* sqn, void* stream);
 
 /* Text of the most recent error in this thread ("" if none). Host pointer, valid until the next call. */
 const char* ot_last_error(void);

@@ -32,6 +32,7 @@ OT_F32, OT_BF16 = 0, 1
 OT_INIT_ZERO, OT_INIT_GIVEN = 0, 1
 OT_TRANSPOSE, OT_GRAD, OT_BARY = 1, 2, 4
 OT_NATIVE_F32 = 1
+OT_COST_AFFINE = 2
 OT_SCHED_ALTERNATING, OT_SCHED_SYMMETRIC = 0, 1
 _SCHEDULES = {"alternating": OT_SCHED_ALTERNATING, "symmetric": OT_SCHED_SYMMETRIC}
 
@@ -107,11 +108,13 @@ def lib() -> ctypes.CDLL:
     L.ot_update_g.argtypes = [pp, vp, vp, vp, vp, szp, vp]
     L.ot_solve.argtypes = [pp, vp, vp, ctypes.POINTER(OtSolveOpts), ctypes.POINTER(OtSolveInfo), vp, szp, vp]
     L.ot_apply_plan.argtypes = [pp, vp, vp, vp, i32, i64, i64, i32, vp, vp, vp, szp, vp]
+    L.ot_prep_cosine.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp]
+    L.ot_prep_labels.argtypes = [vp, i32, i64, i64, i64, vp, vp, i32, i32, vp, vp, vp]
     L.ot_apply_hadamard.argtypes = [pp, vp, vp, vp, i64, vp, i64, i64, vp, vp, szp, vp]
     L.ot_hvp.argtypes = [pp, vp, vp, vp, i64, ctypes.POINTER(OtHvpOpts), vp,
                          ctypes.POINTER(OtHvpInfo), vp, szp, vp]
     for fn in ("ot_sqnorms", "ot_update_f", "ot_update_g", "ot_solve", "ot_apply_plan",
-               "ot_apply_hadamard", "ot_hvp"):
+               "ot_apply_hadamard", "ot_hvp", "ot_prep_cosine", "ot_prep_labels"):
         getattr(L, fn).restype = ctypes.c_int
     L.ot_last_error.restype = ctypes.c_char_p
     L.ot_last_error.argtypes = []
@@ -176,6 +179,7 @@ class Problem:
     x_sqn: torch.Tensor | None = None
     y_sqn: torch.Tensor | None = None
     native_f32: bool = False
+    affine: bool = False
 
     def __post_init__(self):
         n, d, ldx = _rows(self.X, "X")
@@ -191,12 +195,14 @@ class Problem:
             _ptr(self.X), _ptr(self.Y), n, m, d, ldx, ldy, _dtype_code(self.X), float(self.eps),
             _ptr(_vec(self.a, "a", n, dev)), _ptr(_vec(self.b, "b", m, dev)),
             _ptr(_vec(self.x_sqn, "x_sqn", n, dev)), _ptr(_vec(self.y_sqn, "y_sqn", m, dev)),
-            OT_NATIVE_F32 if self.native_f32 else 0)
+            (OT_NATIVE_F32 if self.native_f32 else 0) | (OT_COST_AFFINE if self.affine else 0))
 
 
-def problem(X, Y, eps, a=None, b=None, x_sqn=None, y_sqn=None, native_f32=False) -> Problem:
-    """native_f32: form fp32 scores with fp32 MFMA instead of the three-part bf16 split."""
-    return Problem(X, Y, eps, a, b, x_sqn, y_sqn, native_f32)
+def problem(X, Y, eps, a=None, b=None, x_sqn=None, y_sqn=None, native_f32=False,
+            affine=False) -> Problem:
+    """native_f32: form fp32 scores with fp32 MFMA instead of the three-part bf16 split.
+    affine: cost alpha_i + beta_j - <x_i, y_j> with alpha = x_sqn, beta = y_sqn (required)."""
+    return Problem(X, Y, eps, a, b, x_sqn, y_sqn, native_f32, affine)
 
 
 def _workspace(query, ws, device):
@@ -284,6 +290,34 @@ def ot_apply_plan(prob: Problem, f, g, V=None, flags: int = 0, out=None, marg=No
     ws, size = _workspace(args, ws, prob.device)
     _check(args(_ptr(ws), ctypes.byref(size)), "ot_apply_plan")
     return out
+
+
+def ot_prep_cosine(pts: torch.Tensor):
+    """Cosine-cost features: (rows normalised to unit length, fp32; alpha = 1/2 per row).
+    Use both clouds' outputs with problem(..., affine=True)."""
+    rows, d, ld = _rows(pts, "pts")
+    out = torch.empty((rows, d), dtype=torch.float32, device=pts.device)
+    half = torch.empty(rows, dtype=torch.float32, device=pts.device)
+    _check(lib().ot_prep_cosine(_ptr(pts), _dtype_code(pts), rows, d, ld, _ptr(out), _ptr(half),
+                                _stream(pts.device)), "ot_prep_cosine")
+    return out, half
+
+
+def ot_prep_labels(pts: torch.Tensor, labels: torch.Tensor, W: torch.Tensor, side: int):
+    """Label-augmented cost features (side 0: source [2x, -W[l, :]], side 1: target
+    [y, one-hot(l)]) and the squared norms; use with problem(..., affine=True)."""
+    rows, d, ld = _rows(pts, "pts")
+    L = W.shape[0]
+    if labels.dtype != torch.int32 or labels.numel() != rows or not labels.is_contiguous():
+        raise ValueError("labels must be a contiguous int32 vector with one entry per row")
+    if W.dtype != torch.float32 or W.shape != (L, L) or not W.is_contiguous():
+        raise ValueError("W must be a contiguous float32 square matrix")
+    out = torch.empty((rows, d + L), dtype=torch.float32, device=pts.device)
+    sqn = torch.empty(rows, dtype=torch.float32, device=pts.device)
+    _check(lib().ot_prep_labels(_ptr(pts), _dtype_code(pts), rows, d, ld, _ptr(labels), _ptr(W), L,
+                                int(side), _ptr(out), _ptr(sqn), _stream(pts.device)),
+           "ot_prep_labels")
+    return out, sqn
 
 
 def _f32_rows(t, name, rows, cols, device):

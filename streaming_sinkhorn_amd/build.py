@@ -39,6 +39,7 @@ SOURCES = [
     ("hvp_kernels.hip", []),
     ("api.hip", []),
     ("hvp_api.hip", []),
+    ("cost_prep.hip", []),
 ]
 
 

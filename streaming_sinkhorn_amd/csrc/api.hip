@@ -143,7 +143,9 @@ int check_problem(const ot_problem* p) {
   if (p->d < 1) return fail(OT_ERR_INVALID_ARG, "d must be >= 1");
   if (p->ldx < p->d || p->ldy < p->d) return fail(OT_ERR_INVALID_ARG, "ldx and ldy must be >= d");
   if (p->dtype != OT_F32 && p->dtype != OT_BF16) return fail(OT_ERR_UNSUPPORTED, "dtype must be OT_F32 or OT_BF16");
-  if (p->flags & ~OT_NATIVE_F32) return fail(OT_ERR_INVALID_ARG, "unknown problem flag");
+  if (p->flags & ~(OT_NATIVE_F32 | OT_COST_AFFINE)) return fail(OT_ERR_INVALID_ARG, "unknown problem flag");
+  if ((p->flags & OT_COST_AFFINE) && (!p->x_sqn || !p->y_sqn))
+    return fail(OT_ERR_INVALID_ARG, "OT_COST_AFFINE needs x_sqn (alpha) and y_sqn (beta)");
   if (p->d > OT_MAX_D) return fail(OT_ERR_UNSUPPORTED, "d exceeds OT_MAX_D");
   if (p->n > (int64_t)1 << 30 || p->m > (int64_t)1 << 30) return fail(OT_ERR_UNSUPPORTED, "n or m exceeds 2^30");
   if (!(p->eps > 0.f) || !std::isfinite(p->eps)) return fail(OT_ERR_INVALID_ARG, "eps must be finite and > 0");
@@ -253,7 +255,8 @@ Ctx make_ctx(const ot_problem* p, const SolveWs& L, void* ws, float* f, float* g
   const bool bf = p->dtype == OT_BF16;
   x.bscale = bf ? 1.f : x.c;
   x.kc = bf ? x.c : 1.f;
-  x.xscale = bf ? 1.f : x.c;
+  // affine cost: x packed halved (exact), so the score's 2 <x, y> is <x, y>
+  x.xscale = (bf ? 1.f : x.c) * ((p->flags & OT_COST_AFFINE) ? 0.5f : 1.f);
   x.xp = x.ws + L.o_xp;
   x.yp = x.ws + L.o_yp;
   x.nx = p->x_sqn ? p->x_sqn : (const float*)(x.ws + L.o_nx);
@@ -678,6 +681,8 @@ int ot_apply_plan(const ot_problem* p, const float* f, const float* g, const voi
     if (rc) return rc;
     if (flags & ~(OT_TRANSPOSE | OT_GRAD | OT_BARY)) return fail(OT_ERR_INVALID_ARG, "unknown flag");
     if ((flags & OT_GRAD) && (flags & OT_BARY)) return fail(OT_ERR_INVALID_ARG, "OT_GRAD and OT_BARY are exclusive");
+    if ((flags & OT_GRAD) && (p->flags & OT_COST_AFFINE))
+      return fail(OT_ERR_UNSUPPORTED, "OT_GRAD is the squared-Euclidean gradient: not with OT_COST_AFFINE");
     const bool tr = (flags & OT_TRANSPOSE) != 0;
     const bool grad = (flags & OT_GRAD) != 0;
     if (grad) {  // V is the other cloud itself
@@ -707,7 +712,8 @@ int ot_apply_plan(const ot_problem* p, const float* f, const float* g, const voi
     const float* ny = p->y_sqn ? p->y_sqn : (const float*)(w + L.o_ny);
     if (!p->x_sqn) OT_HIP(launch_sqnorms(p->x, bf, p->n, p->d, p->ldx, (float*)nx, st));
     if (!p->y_sqn) OT_HIP(launch_sqnorms(p->y, bf, p->m, p->d, p->ldy, (float*)ny, st));
-    OT_HIP(launch_pack_points(p->x, bf, p->n, p->d, p->ldx, ntiles, L.k.kbp, 1.f, xp, st));
+    const float xs = (p->flags & OT_COST_AFFINE) ? 0.5f : 1.f;
+    OT_HIP(launch_pack_points(p->x, bf, p->n, p->d, p->ldx, ntiles, L.k.kbp, xs, xp, st));
     OT_HIP(launch_pack_points(p->y, bf, p->m, p->d, p->ldy, mtiles, L.k.kbp, 1.f, yp, st));
     // Row side r (outputs) and column side s (streamed).
     const int64_t rows = tr ? p->m : p->n, srows = tr ? p->n : p->m;

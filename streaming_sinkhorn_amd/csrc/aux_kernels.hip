@@ -214,8 +214,18 @@ __global__ __launch_bounds__(256) void sqnorms_kernel(const T* __restrict__ pts,
   if (lane == 0) out[row] = s;
 }
 
+// bf16 rounding (to nearest, ties to even) of an fp32 value, as bits; NaN
+// stays a quiet NaN.
+__device__ __forceinline__ uint32_t bf16_bits_rne(float v) {
+  const uint32_t u = __float_as_uint(v);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
 // Packs a row-major point cloud into the MFMA operand layout of kernels.h,
-// multiplying fp32 values by `scale` (bf16 values are copied unchanged).
+// multiplying the values by `scale`. bf16 values are copied unchanged when
+// scale is 1; otherwise they are scaled in fp32 and rounded back to bf16
+// (exact for the power-of-two scales used).
 template <typename T>
 __global__ __launch_bounds__(256) void pack_points_kernel(const T* __restrict__ src, int64_t rows,
                                                            int64_t d, int64_t ld, int64_t total,
@@ -234,21 +244,18 @@ __global__ __launch_bounds__(256) void pack_points_kernel(const T* __restrict__ 
 #pragma unroll
     for (int e = 0; e < KW; ++e)
       v[e] = (row < rows && k0 + e < d) ? src[row * ld + k0 + e] : T(0);
-    if constexpr (sizeof(T) == 4) {  // fp32 rows may be packed pre-scaled; bf16 never are
+    if constexpr (sizeof(T) == 4) {
 #pragma unroll
       for (int e = 0; e < KW; ++e) v[e] = v[e] * scale;
+    } else if (scale != 1.0f) {
+#pragma unroll
+      for (int e = 0; e < KW; ++e)
+        v[e] = (T)bf16_bits_rne(__uint_as_float((uint32_t)v[e] << 16) * scale);
     }
     dst[idx] = __builtin_bit_cast(u32x4, v);
   }
 }
 
-// bf16 rounding (to nearest, ties to even) of an fp32 value, as bits; NaN
-// stays a quiet NaN.
-__device__ __forceinline__ uint32_t bf16_bits_rne(float v) {
-  const uint32_t u = __float_as_uint(v);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
 
 // Splits scale * src into hi + mid + lo, each the bf16 rounding of what the
 // previous parts left (the differences are exact in fp32), and packs part p
@@ -369,7 +376,7 @@ hipError_t launch_pack_points(const void* src, int bf16, int64_t rows, int64_t d
   const int grid = grid_for(total, 256, 65536);
   if (bf16)
     pack_points_kernel<uint16_t>
-        <<<grid, 256, 0, st>>>((const uint16_t*)src, rows, d, ld, total, kbp, 1.0f, (u32x4*)dst);
+        <<<grid, 256, 0, st>>>((const uint16_t*)src, rows, d, ld, total, kbp, scale, (u32x4*)dst);
   else
     pack_points_kernel<float>
         <<<grid, 256, 0, st>>>((const float*)src, rows, d, ld, total, kbp, scale, (u32x4*)dst);

@@ -161,6 +161,8 @@ int check_f32_problem(const ot_problem* p) {
   int rc = check_problem(p);
   if (rc) return rc;
   if (p->dtype != OT_F32) return fail(OT_ERR_UNSUPPORTED, "second-order entry points take fp32 points");
+  if (p->flags & OT_COST_AFFINE)
+    return fail(OT_ERR_UNSUPPORTED, "second-order entry points assume the squared-Euclidean cost");
   return OT_OK;
 }
 

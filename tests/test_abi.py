@@ -69,7 +69,8 @@ def test_workspace_query_is_host_only_and_monotone():
     ("d", 100000, ssa.OT_ERR_UNSUPPORTED),
     ("x", 0, ssa.OT_ERR_INVALID_ARG),
     ("x", (1 << 20) + 2, ssa.OT_ERR_INVALID_ARG),   # fp32 data must be 4-byte aligned
-    ("flags", 2, ssa.OT_ERR_INVALID_ARG),            # unknown problem flag
+    ("flags", 4, ssa.OT_ERR_INVALID_ARG),            # unknown problem flag
+    ("flags", ssa.OT_COST_AFFINE, ssa.OT_ERR_INVALID_ARG),  # affine cost without alpha, beta
 ])
 def test_problem_validation(field, value, code):
     L = ssa.lib()
@@ -229,3 +230,45 @@ def test_hvp_rejects_bf16_missing_opts_and_short_lda():
     rc = L.ot_apply_hadamard(ctypes.byref(_problem()), None, None, None, 16, None, 0, 8, None,
                              None, ctypes.byref(sz), None)
     assert rc == ssa.OT_ERR_INVALID_ARG
+
+
+def test_affine_cost_rejected_where_the_cost_must_be_euclidean():
+    L = ssa.lib()
+    p = _problem()
+    p.flags = ssa.OT_COST_AFFINE
+    p.x_sqn, p.y_sqn = 3 << 20, 4 << 20   # alpha, beta given: the problem itself is valid
+    rc, size = _size(L.ot_update_f, ctypes.byref(p), None, None, None)
+    assert rc == 0 and size > 0
+    sz = ctypes.c_size_t(0)
+    rc = L.ot_apply_plan(ctypes.byref(p), None, None, None, 0, 16, 16, ssa.OT_GRAD, None, None, None,
+                         ctypes.byref(sz), None)
+    assert rc == ssa.OT_ERR_UNSUPPORTED
+    rc, _ = _hvp_size(p, ssa.OtHvpOpts(1e-5, 50, 0.0))
+    assert rc == ssa.OT_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(pts=None), ssa.OT_ERR_INVALID_ARG),
+    (dict(rows=0), ssa.OT_ERR_INVALID_ARG),
+    (dict(ld=3), ssa.OT_ERR_INVALID_ARG),
+    (dict(dtype=5), ssa.OT_ERR_UNSUPPORTED),
+    (dict(out=None), ssa.OT_ERR_INVALID_ARG),
+    (dict(n_labels=0), ssa.OT_ERR_INVALID_ARG),
+    (dict(side=2), ssa.OT_ERR_INVALID_ARG),
+    (dict(d=8190), ssa.OT_ERR_UNSUPPORTED),
+])
+def test_prep_validation(args, code):
+    L = ssa.lib()
+    base = dict(pts=1 << 20, dtype=ssa.OT_F32, rows=10, d=4, ld=4, labels=2 << 20, W=3 << 20,
+                n_labels=5, side=0, out=4 << 20, sqn=5 << 20)
+    base.update(args)
+    if base["d"] > 4:
+        base["ld"] = base["d"]
+    if "n_labels" not in args and "side" not in args and "d" not in args:
+        rc = L.ot_prep_cosine(base["pts"], base["dtype"], base["rows"], base["d"], base["ld"],
+                              base["out"], base["sqn"], None)
+        assert rc == code, L.ot_last_error()
+    rc = L.ot_prep_labels(base["pts"], base["dtype"], base["rows"], base["d"], base["ld"],
+                          base["labels"], base["W"], base["n_labels"], base["side"], base["out"],
+                          base["sqn"], None)
+    assert rc == code, L.ot_last_error()

@@ -194,3 +194,31 @@ def potential_offsets(n: int, m: int, seed: int, scale: float = 0.1) -> tuple[np
     rng = np.random.default_rng(seed)
     return ((rng.standard_normal(n) * scale).astype(np.float32),
             (rng.standard_normal(m) * scale).astype(np.float32))
+
+
+def affine_inputs(n: int, m: int, d: int, seed: int) -> dict:
+    """Seeded inputs of a general affine cost alpha_i + beta_j - <Q_i, K_j> (§3.1
+    "Scope of cost structure"): features Q, K ~ N(0, I_d) / sqrt(d), offsets
+    alpha, beta ~ Uniform[0, 1], Dirichlet(1) weights. float32 arrays."""
+    rng = np.random.default_rng(seed)
+    s = 1.0 / math.sqrt(d)
+    f32 = lambda v: np.ascontiguousarray(v, dtype=np.float32)
+    a = rng.exponential(1.0, n)
+    b = rng.exponential(1.0, m)
+    return dict(Q=f32(rng.standard_normal((n, d)) * s), K=f32(rng.standard_normal((m, d)) * s),
+                alpha=f32(rng.uniform(0.0, 1.0, n)), beta=f32(rng.uniform(0.0, 1.0, m)),
+                a=f32(a / a.sum()), b=f32(b / b.sum()))
+
+
+def label_inputs(n: int, m: int, n_labels: int, seed: int) -> dict:
+    """Seeded class labels (uniform over n_labels classes) and a symmetric
+    label-to-label cost W with zero diagonal and entries ~ Uniform[0.5, 2]
+    off it, standing in for the OTDD label distances of §4.2 (whose embedding
+    data is not available). int32 labels, float32 W."""
+    rng = np.random.default_rng(seed)
+    W = rng.uniform(0.5, 2.0, (n_labels, n_labels))
+    W = 0.5 * (W + W.T)
+    np.fill_diagonal(W, 0.0)
+    return dict(lx=rng.integers(0, n_labels, n).astype(np.int32),
+                ly=rng.integers(0, n_labels, m).astype(np.int32),
+                W=np.ascontiguousarray(W, dtype=np.float32))
