@@ -16,6 +16,8 @@ IO-Aware Entropic Optimal Transport on GPU" (arXiv 2602.03067):
   products of the materialised coupling;
 * affine, cosine and label-augmented costs (``oracle.costs``, §3.1 "Scope
   of cost structure", §4.2) are dense matrices from their plain definitions;
+* eps-scaling and the debiased Sinkhorn divergence (``oracle.divergence``)
+  are the plain iteration at a decreasing eps and three dual values;
 * the Hessian-vector product (``oracle.hvp``, §3.3 / App. F) is formed from
   the dense coupling, with the pseudoinverse by eigendecomposition or the
   damped Schur complement solved by textbook conjugate gradients.
@@ -48,3 +50,4 @@ from .sinkhorn import (  # noqa: F401
 )
 from . import hvp  # noqa: F401,E402
 from . import costs  # noqa: F401,E402
+from . import divergence  # noqa: F401,E402
