@@ -42,36 +42,44 @@ def eps_schedule(eps, iters, eps_start=0.0, decay=0.5):
     return out
 
 
-def sinkhorn_eps_scaling(C, a, b, eps, iters, eps_start, decay, f0=None, g0=None):
-    """Alternating Sinkhorn where iteration k runs both half-steps at eps_k of
-    ``eps_schedule`` (the potentials carry over from one eps to the next)."""
+def sinkhorn_eps_scaling(C, a, b, eps, iters, eps_start, decay, f0=None, g0=None,
+                         schedule="alternating"):
+    """Sinkhorn where iteration k runs both half-steps at eps_k of ``eps_schedule``
+    (the potentials carry over from one eps to the next). schedule
+    "alternating": f from g, then g from the new f (§3.1 eq. 2-3);
+    "symmetric": both from the previous iterate, averaged (eq. 4-5)."""
     C = _f64(C)
     n, m = C.shape
     f = np.zeros(n) if f0 is None else _f64(f0).copy()
     g = np.zeros(m) if g0 is None else _f64(g0).copy()
     for e in eps_schedule(eps, iters, eps_start, decay):
-        f = update_f(C, g, b, e)
-        g = update_g(C, f, a, e)
+        if schedule == "symmetric":
+            ft = update_f(C, g, b, e)
+            gt = update_g(C, f, a, e)
+            f, g = 0.5 * (f + ft), 0.5 * (g + gt)
+        else:
+            f = update_f(C, g, b, e)
+            g = update_g(C, f, a, e)
     return f, g
 
 
-def _solve(C, a, b, eps, iters, eps_start, decay):
-    if eps_start > eps:
-        return sinkhorn_eps_scaling(C, a, b, eps, iters, eps_start, decay)
+def _solve(C, a, b, eps, iters, eps_start, decay, schedule):
+    if eps_start > eps or schedule == "symmetric":
+        return sinkhorn_eps_scaling(C, a, b, eps, iters, eps_start, decay, schedule=schedule)
     return sinkhorn(C, a, b, eps, iters)
 
 
-def sinkhorn_divergence(X, Y, a, b, eps, iters, eps_start=0.0, decay=0.5):
+def sinkhorn_divergence(X, Y, a, b, eps, iters, eps_start=0.0, decay=0.5, schedule="alternating"):
     """S_eps(mu, nu) = OT(mu, nu) - OT(mu, mu)/2 - OT(nu, nu)/2 with each OT the dual
-    value of its own alternating solve (same eps, iterations and eps-scaling).
+    value of its own solve (same schedule, eps, iterations and eps-scaling).
 
     Returns (S, OT(mu, nu), OT(mu, mu), OT(nu, nu), f, g, f_xx, g_yy) where
     (f, g) solve (mu, nu), f_xx is the f-side potential of (mu, mu) and g_yy
     the g-side potential of (nu, nu)."""
     X, Y, a, b = _f64(X), _f64(Y), _f64(a), _f64(b)
-    f, g = _solve(cost_matrix(X, Y), a, b, eps, iters, eps_start, decay)
-    fxx, gxx = _solve(cost_matrix(X, X), a, a, eps, iters, eps_start, decay)
-    fyy, gyy = _solve(cost_matrix(Y, Y), b, b, eps, iters, eps_start, decay)
+    f, g = _solve(cost_matrix(X, Y), a, b, eps, iters, eps_start, decay, schedule)
+    fxx, gxx = _solve(cost_matrix(X, X), a, a, eps, iters, eps_start, decay, schedule)
+    fyy, gyy = _solve(cost_matrix(Y, Y), b, b, eps, iters, eps_start, decay, schedule)
     ot_xy = dual_value(a, b, f, g)
     ot_xx = dual_value(a, a, fxx, gxx)
     ot_yy = dual_value(b, b, fyy, gyy)

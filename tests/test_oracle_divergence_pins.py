@@ -36,6 +36,20 @@ def test_eps_scaling_off_is_the_plain_iteration():
     assert np.array_equal(f1, f2) and np.array_equal(g1, g2)
 
 
+def test_symmetric_eps_scaling_off_is_the_plain_symmetric_iteration():
+    X, a = _cloud(6, 2)
+    Y, b = _cloud(8, 2, 0.3)
+    C = oracle.cost_matrix(X, Y)
+    f1, g1 = D.sinkhorn_eps_scaling(C, a, b, 0.2, 12, 0.0, 0.5, schedule="symmetric")
+    f2, g2 = oracle.sinkhorn_symmetric(C, a, b, 0.2, 12)
+    assert np.array_equal(f1, f2) and np.array_equal(g1, g2)
+    # annealed symmetric and alternating solves share the fixed point
+    fs, gs = D.sinkhorn_eps_scaling(C, a, b, 0.2, 4000, 3.0, 0.6, schedule="symmetric")
+    fa, ga = oracle.sinkhorn(C, a, b, 0.2, 4000)
+    np.testing.assert_allclose(oracle.plan(C, a, b, fs, gs, 0.2), oracle.plan(C, a, b, fa, ga, 0.2),
+                               rtol=0, atol=1e-10)
+
+
 def test_eps_scaling_reaches_the_same_coupling():
     X, a = _cloud(8, 2)
     Y, b = _cloud(9, 2, 0.5)
