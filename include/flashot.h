@@ -142,6 +142,9 @@ typedef struct ot_solve_opts {
   int32_t splits_g;     /* column splits of the g half-step (0 = automatic) */
   int32_t timing;       /* 1: time every log-sum-exp kernel with HIP events (needs info) */
   int32_t schedule;     /* OT_SCHED_ALTERNATING (0) or OT_SCHED_SYMMETRIC */
+  float eps_start;      /* eps-scaling: 0 = off; > eps: iteration k runs at
+                           max(eps, eps_start * eps_decay^k) */
+  float eps_decay;      /* eps-scaling factor per iteration, 0 < eps_decay < 1 */
 } ot_solve_opts;
 
 /* ot_solve results (host memory). */
@@ -217,11 +220,40 @@ int ot_update_g(const ot_problem* p, const float* f, float* g, float* err,
  *   E.1) and the host reads it every opts->check_every iterations (one
  *   synchronisation per check); the loop stops after the iteration in which
  *   it fell below tol.
+ *   eps-scaling (opts->eps_start > eps): the first iterations run at the
+ *   decreasing eps_k = eps_start * eps_decay^k while that exceeds eps (the
+ *   potentials carry over), then every iteration runs at eps; all of them
+ *   count in opts->iters. The page's benchmarks turn it off (App. H.2); the
+ *   geometric schedule is this library's reading. The tolerance check runs
+ *   only in the iterations at eps.
  * Errors: as ot_update_f, plus OT_ERR_NONFINITE when info is given and the
  * final potentials are not finite.
  */
 int ot_solve(const ot_problem* p, float* f, float* g, const ot_solve_opts* opts,
              ot_solve_info* info, void* ws, size_t* ws_bytes, void* stream);
+
+/*
+ * ot_sinkhorn_divergence -- debiased Sinkhorn divergence
+ *     S_eps(mu, nu) = OT_eps(mu, nu) - OT_eps(mu, mu) / 2 - OT_eps(nu, nu) / 2
+ * (the quantity of §1, "debiasing" of App. H.2), each OT_eps the dual value
+ * <a, f> + <b, g> of its own ot_solve with the same opts (schedule,
+ * iterations, eps-scaling), on the same stream.
+ *   f, g    device fp32 (n, m): potentials of (mu, nu) (outputs; with
+ *           OT_INIT_GIVEN also the start of that solve)
+ *   f_xx    device fp32 (n): f-side potential of (mu, mu) (output)
+ *   g_yy    device fp32 (m): g-side potential of (nu, nu) (output)
+ *   out     device fp32 [4]: S, OT(mu, nu), OT(mu, mu), OT(nu, nu); the dual
+ *           values are summed in fp64 in a fixed order before rounding
+ *   opts    host, required; OT_INIT_GIVEN applies to (mu, nu) only (the
+ *           self-transport solves start from zero); timing is ignored
+ * The self-transport problems reuse the problem's points, weights and norms
+ * (x against x, y against y). Errors: as ot_solve; OT_COST_AFFINE is
+ * rejected (OT_ERR_UNSUPPORTED: the roles of x and y differ in an affine
+ * cost, so x against x is not the same cost).
+ */
+int ot_sinkhorn_divergence(const ot_problem* p, const ot_solve_opts* opts, float* f, float* g,
+                           float* f_xx, float* g_yy, float* out, void* ws, size_t* ws_bytes,
+                           void* stream);
 
 /*
  * ot_apply_plan -- apply the coupling induced by (f, g) to a matrix without

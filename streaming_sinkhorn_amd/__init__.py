@@ -60,7 +60,7 @@ class OtSolveOpts(ctypes.Structure):
         ("iters", ctypes.c_int32), ("tol", ctypes.c_float), ("check_every", ctypes.c_int32),
         ("init", ctypes.c_int32), ("use_graph", ctypes.c_int32),
         ("splits_f", ctypes.c_int32), ("splits_g", ctypes.c_int32), ("timing", ctypes.c_int32),
-        ("schedule", ctypes.c_int32),
+        ("schedule", ctypes.c_int32), ("eps_start", ctypes.c_float), ("eps_decay", ctypes.c_float),
     ]
 
 
@@ -108,13 +108,16 @@ def lib() -> ctypes.CDLL:
     L.ot_update_g.argtypes = [pp, vp, vp, vp, vp, szp, vp]
     L.ot_solve.argtypes = [pp, vp, vp, ctypes.POINTER(OtSolveOpts), ctypes.POINTER(OtSolveInfo), vp, szp, vp]
     L.ot_apply_plan.argtypes = [pp, vp, vp, vp, i32, i64, i64, i32, vp, vp, vp, szp, vp]
+    L.ot_sinkhorn_divergence.argtypes = [pp, ctypes.POINTER(OtSolveOpts), vp, vp, vp, vp, vp, vp,
+                                         szp, vp]
     L.ot_prep_cosine.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp]
     L.ot_prep_labels.argtypes = [vp, i32, i64, i64, i64, vp, vp, i32, i32, vp, vp, vp]
     L.ot_apply_hadamard.argtypes = [pp, vp, vp, vp, i64, vp, i64, i64, vp, vp, szp, vp]
     L.ot_hvp.argtypes = [pp, vp, vp, vp, i64, ctypes.POINTER(OtHvpOpts), vp,
                          ctypes.POINTER(OtHvpInfo), vp, szp, vp]
     for fn in ("ot_sqnorms", "ot_update_f", "ot_update_g", "ot_solve", "ot_apply_plan",
-               "ot_apply_hadamard", "ot_hvp", "ot_prep_cosine", "ot_prep_labels"):
+               "ot_apply_hadamard", "ot_hvp", "ot_prep_cosine", "ot_prep_labels",
+               "ot_sinkhorn_divergence"):
         getattr(L, fn).restype = ctypes.c_int
     L.ot_last_error.restype = ctypes.c_char_p
     L.ot_last_error.argtypes = []
@@ -246,16 +249,46 @@ def ot_update_g(prob: Problem, f, g, err=None, ws=None):
     return _update("ot_update_g", "ot_update_g", prob, f, g, err, ws)
 
 
+def _solve_opts(iters, tol=0.0, check_every=1, init_given=False, use_graph=True, splits_f=0,
+                splits_g=0, timing=False, schedule="alternating", eps_start=0.0, eps_decay=0.5):
+    return OtSolveOpts(int(iters), float(tol), int(check_every),
+                       OT_INIT_GIVEN if init_given else OT_INIT_ZERO, int(bool(use_graph)),
+                       int(splits_f), int(splits_g), int(bool(timing)), _SCHEDULES[schedule],
+                       float(eps_start), float(eps_decay))
+
+
+def ot_sinkhorn_divergence(prob: Problem, iters: int, f=None, g=None, schedule: str = "alternating",
+                           eps_start: float = 0.0, eps_decay: float = 0.5, ws=None):
+    """Debiased Sinkhorn divergence. Returns (values, f, g, f_xx, g_yy) with values a
+    host tuple (S, OT(mu, nu), OT(mu, mu), OT(nu, nu)); the call synchronises."""
+    L = lib()
+    dev = prob.device
+    f = torch.zeros(prob.n, device=dev) if f is None else f
+    g = torch.zeros(prob.m, device=dev) if g is None else g
+    fxx = torch.empty(prob.n, device=dev)
+    gyy = torch.empty(prob.m, device=dev)
+    out = torch.empty(4, device=dev)
+    opts = _solve_opts(iters, schedule=schedule, eps_start=eps_start, eps_decay=eps_decay)
+    st = _stream(dev)
+    pp = ctypes.byref(prob.c)
+    args = lambda w, s: L.ot_sinkhorn_divergence(pp, ctypes.byref(opts), _ptr(f), _ptr(g), _ptr(fxx),
+                                                 _ptr(gyy), _ptr(out), w, s, st)
+    ws, size = _workspace(args, ws, dev)
+    _check(args(_ptr(ws), ctypes.byref(size)), "ot_sinkhorn_divergence")
+    vals = tuple(float(v) for v in out.cpu())
+    return vals, f, g, fxx, gyy
+
+
 def ot_solve(prob: Problem, f, g, iters: int, tol: float = 0.0, check_every: int = 1,
              init_given: bool = False, use_graph: bool = True, splits_f: int = 0,
              splits_g: int = 0, timing: bool = False, want_info: bool = True, ws=None,
-             schedule: str = "alternating"):
-    """Sinkhorn iterations into f, g (schedule "alternating" or "symmetric").
+             schedule: str = "alternating", eps_start: float = 0.0, eps_decay: float = 0.5):
+    """Sinkhorn iterations into f, g (schedule "alternating" or "symmetric"; eps-scaling
+    from eps_start by eps_decay per iteration when eps_start > eps).
     Returns the info dict (None if want_info is False)."""
     L = lib()
-    opts = OtSolveOpts(int(iters), float(tol), int(check_every),
-                       OT_INIT_GIVEN if init_given else OT_INIT_ZERO, int(bool(use_graph)),
-                       int(splits_f), int(splits_g), int(bool(timing)), _SCHEDULES[schedule])
+    opts = _solve_opts(iters, tol, check_every, init_given, use_graph, splits_f, splits_g, timing,
+                       schedule, eps_start, eps_decay)
     info = OtSolveInfo()
     pinfo = ctypes.byref(info) if want_info else None
     st = _stream(prob.device)

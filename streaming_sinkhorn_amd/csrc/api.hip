@@ -245,18 +245,24 @@ struct Ctx {
   float *f, *g;
 };
 
+// The eps-dependent constants of a context: score scale c = 2 log2(e) / eps and
+// the units of operands and biases.
+void set_eps_params(Ctx& x, float eps) {
+  x.eps = eps;
+  x.c = 2.f * kLog2e / eps;
+  const bool bf = x.p->dtype == OT_BF16;
+  x.bscale = bf ? 1.f : x.c;
+  x.kc = bf ? x.c : 1.f;
+  // affine cost: x packed halved (exact), so the score's 2 <x, y> is <x, y>
+  x.xscale = (bf ? 1.f : x.c) * ((x.p->flags & OT_COST_AFFINE) ? 0.5f : 1.f);
+}
+
 Ctx make_ctx(const ot_problem* p, const SolveWs& L, void* ws, float* f, float* g) {
   Ctx x{};
   x.p = p;
   x.L = L;
   x.ws = (char*)ws;
-  x.eps = p->eps;
-  x.c = 2.f * kLog2e / p->eps;
-  const bool bf = p->dtype == OT_BF16;
-  x.bscale = bf ? 1.f : x.c;
-  x.kc = bf ? x.c : 1.f;
-  // affine cost: x packed halved (exact), so the score's 2 <x, y> is <x, y>
-  x.xscale = (bf ? 1.f : x.c) * ((p->flags & OT_COST_AFFINE) ? 0.5f : 1.f);
+  set_eps_params(x, p->eps);
   x.xp = x.ws + L.o_xp;
   x.yp = x.ws + L.o_yp;
   x.nx = p->x_sqn ? p->x_sqn : (const float*)(x.ws + L.o_nx);
@@ -276,24 +282,71 @@ Ctx make_ctx(const ot_problem* p, const SolveWs& L, void* ws, float* f, float* g
   return x;
 }
 
+// The eps-dependent operands: X packed pre-scaled by xscale, and the
+// log-weights (eps/2) log a, (eps/2) log b.
+int prepare_eps(const Ctx& x, hipStream_t st) {
+  const ot_problem* p = x.p;
+  const int bf = p->dtype == OT_BF16;
+  if (x.L.k.mode == 2)
+    OT_HIP(launch_pack_split((const float*)p->x, p->n, p->d, p->ldx, x.L.ntiles, x.L.k.kbp, x.xscale,
+                             x.xp, st));
+  else
+    OT_HIP(launch_pack_points(p->x, bf, p->n, p->d, p->ldx, x.L.ntiles, x.L.k.kbp, x.xscale, x.xp, st));
+  OT_HIP(launch_weights(p->a, (int)p->n, x.L.npad, x.eps, x.wx, x.hx, st));
+  OT_HIP(launch_weights(p->b, (int)p->m, x.L.mpad, x.eps, x.wy, x.hy, st));
+  return OT_OK;
+}
+
 // Norms, packed operands, weights: once per call.
 int prepare(const Ctx& x, hipStream_t st) {
   const ot_problem* p = x.p;
   const int bf = p->dtype == OT_BF16;
   if (!p->x_sqn) OT_HIP(launch_sqnorms(p->x, bf, p->n, p->d, p->ldx, (float*)x.nx, st));
   if (!p->y_sqn) OT_HIP(launch_sqnorms(p->y, bf, p->m, p->d, p->ldy, (float*)x.ny, st));
-  if (x.L.k.mode == 2) {
-    OT_HIP(launch_pack_split((const float*)p->x, p->n, p->d, p->ldx, x.L.ntiles, x.L.k.kbp, x.xscale,
-                             x.xp, st));
+  if (x.L.k.mode == 2)
     OT_HIP(launch_pack_split((const float*)p->y, p->m, p->d, p->ldy, x.L.mtiles, x.L.k.kbp, 1.f, x.yp,
                              st));
-  } else {
-    OT_HIP(launch_pack_points(p->x, bf, p->n, p->d, p->ldx, x.L.ntiles, x.L.k.kbp, x.xscale, x.xp, st));
+  else
     OT_HIP(launch_pack_points(p->y, bf, p->m, p->d, p->ldy, x.L.mtiles, x.L.k.kbp, 1.f, x.yp, st));
-  }
-  OT_HIP(launch_weights(p->a, (int)p->n, x.L.npad, x.eps, x.wx, x.hx, st));
-  OT_HIP(launch_weights(p->b, (int)p->m, x.L.mpad, x.eps, x.wy, x.hy, st));
+  return prepare_eps(x, st);
+}
+
+// Bias of the next f half-step from the stored g (and of the g half-step
+// from f for the symmetric schedule), in the context's current units.
+int rebuild_biases(const Ctx& x, hipStream_t st) {
+  const ot_problem* p = x.p;
+  OT_HIP(launch_bias_from_pot(x.g, x.ny, x.hy, (int)p->m, x.L.mpad, x.bscale, x.by, st));
+  if (x.sym) OT_HIP(launch_bias_from_pot(x.f, x.nx, x.hx, (int)p->n, x.L.npad, x.bscale, x.bx, st));
   return OT_OK;
+}
+
+int enqueue_iteration(const Ctx& x, hipStream_t st, int with_err, hipEvent_t* ev);
+
+// eps-scaling: iterations at eps_k = eps_start * decay^k while that exceeds
+// the problem's eps (plain launches; X and the log-weights are rebuilt for
+// every eps_k), then the context is put back to the problem's eps. Returns
+// the number of iterations run in *done.
+int run_eps_scaling(Ctx& x, hipStream_t st, int max_iters, float eps_start, float decay,
+                    int* done) {
+  *done = 0;
+  float e = eps_start;
+  while (*done < max_iters && e > x.p->eps) {
+    set_eps_params(x, e);
+    int rc = prepare_eps(x, st);
+    if (rc) return rc;
+    rc = rebuild_biases(x, st);
+    if (rc) return rc;
+    rc = enqueue_iteration(x, st, 0, nullptr);
+    if (rc) return rc;
+    ++*done;
+    e *= decay;
+  }
+  if (*done > 0) {
+    set_eps_params(x, x.p->eps);
+    const int rc = prepare_eps(x, st);
+    if (rc) return rc;
+  }
+  return rebuild_biases(x, st);
 }
 
 // f half-step: LSE over columns y with bias by, merge into f (bias bx for the g side).
@@ -604,6 +657,13 @@ int ot_solve(const ot_problem* p, float* f, float* g, const ot_solve_opts* o,
     if (o->timing && !info) return fail(OT_ERR_INVALID_ARG, "timing needs info");
     if (o->schedule != OT_SCHED_ALTERNATING && o->schedule != OT_SCHED_SYMMETRIC)
       return fail(OT_ERR_INVALID_ARG, "schedule must be OT_SCHED_ALTERNATING or OT_SCHED_SYMMETRIC");
+    if (!(o->eps_start >= 0.f) || !std::isfinite(o->eps_start))
+      return fail(OT_ERR_INVALID_ARG, "eps_start must be finite and >= 0");
+    const bool scaling = o->eps_start > p->eps;
+    if (scaling && !(o->eps_decay > 0.f && o->eps_decay < 1.f))
+      return fail(OT_ERR_INVALID_ARG, "eps_decay must lie in (0, 1) with eps-scaling");
+    if (scaling && !std::isfinite(2.f * kLog2e / (o->eps_start)))
+      return fail(OT_ERR_UNSUPPORTED, "eps_start out of range");
     const SolveWs L = solve_layout(p, o->splits_f, o->splits_g);
     bool query = false;
     rc = check_ws(ws, ws_bytes, L.total, &query);
@@ -618,12 +678,18 @@ int ot_solve(const ot_problem* p, float* f, float* g, const ot_solve_opts* o,
       OT_HIP(launch_fill(g, 0.f, p->m, st));
     }
     x.sym = o->schedule == OT_SCHED_SYMMETRIC;
-    OT_HIP(launch_bias_from_pot(g, x.ny, x.hy, (int)p->m, L.mpad, x.bscale, x.by, st));
-    if (x.sym) OT_HIP(launch_bias_from_pot(f, x.nx, x.hx, (int)p->n, L.npad, x.bscale, x.bx, st));
+    int done = 0;
+    if (scaling) {
+      rc = run_eps_scaling(x, st, o->iters, o->eps_start, o->eps_decay, &done);
+      if (rc) return rc;
+    } else {
+      rc = rebuild_biases(x, st);
+      if (rc) return rc;
+    }
     const bool use_graph = o->use_graph != 0 && st != nullptr;
     float lse_ms = 0.f;
     int lse_launches = 0;
-    int done = 0;
+    const int annealed = done;
     if (o->tol > 0.f) {
       while (done < o->iters) {
         const int chunk = (o->iters - done) < o->check_every ? (o->iters - done) : o->check_every;
@@ -638,8 +704,9 @@ int ot_solve(const ot_problem* p, float* f, float* g, const ot_solve_opts* o,
         if (!(herr >= o->tol)) break;  // also stops on NaN
       }
     } else {
-      rc = o->timing ? run_iterations_timed(x, st, o->iters, 0, &lse_ms, &lse_launches)
-                     : run_iterations(x, st, o->iters, 0, use_graph);
+      const int rest = o->iters - annealed;
+      rc = o->timing ? run_iterations_timed(x, st, rest, 0, &lse_ms, &lse_launches)
+                     : run_iterations(x, st, rest, 0, use_graph);
       if (rc) return rc;
       done = o->iters;
     }
@@ -667,6 +734,63 @@ int ot_solve(const ot_problem* p, float* f, float* g, const ot_solve_opts* o,
       info->operand_mode = L.k.mode;
       if (info->nonfinite) return fail(OT_ERR_NONFINITE, "potentials are not finite");
     }
+    return OT_OK;
+  } catch (...) {
+    return fail(OT_ERR_HIP, "unexpected host exception");
+  }
+}
+
+int ot_sinkhorn_divergence(const ot_problem* p, const ot_solve_opts* opts, float* f, float* g,
+                           float* f_xx, float* g_yy, float* out, void* ws, size_t* ws_bytes,
+                           void* stream) {
+  try {
+    int rc = check_problem(p);
+    if (rc) return rc;
+    if (!opts) return fail(OT_ERR_INVALID_ARG, "opts is NULL");
+    if (p->flags & OT_COST_AFFINE)
+      return fail(OT_ERR_UNSUPPORTED, "the self-transport terms need the squared-Euclidean cost");
+    // (mu, nu), (mu, mu), (nu, nu): same points, weights and norms
+    ot_problem pxx = *p, pyy = *p;
+    pxx.y = p->x;
+    pxx.m = p->n;
+    pxx.ldy = p->ldx;
+    pxx.b = p->a;
+    pxx.y_sqn = p->x_sqn;
+    pyy.x = p->y;
+    pyy.n = p->m;
+    pyy.ldx = p->ldy;
+    pyy.a = p->b;
+    pyy.x_sqn = p->y_sqn;
+    ot_solve_opts o = *opts;
+    o.timing = 0;
+    ot_solve_opts oz = o;
+    oz.init = OT_INIT_ZERO;
+    size_t need[3] = {0, 0, 0};
+    const ot_problem* ps[3] = {p, &pxx, &pyy};
+    for (int k = 0; k < 3; ++k) {
+      rc = ot_solve(ps[k], nullptr, nullptr, k ? &oz : &o, nullptr, nullptr, &need[k], nullptr);
+      if (rc) return rc;
+    }
+    size_t solve_ws = need[0] > need[1] ? need[0] : need[1];
+    solve_ws = align_up(solve_ws > need[2] ? solve_ws : need[2], 256);
+    const size_t o_gxx = solve_ws, o_fyy = align_up(o_gxx + (size_t)p->n * 4, 256);
+    const size_t total = align_up(o_fyy + (size_t)p->m * 4, 256);
+    bool query = false;
+    rc = check_ws(ws, ws_bytes, total, &query);
+    if (rc || query) return rc;
+    if (!f || !g || !f_xx || !g_yy || !out) return fail(OT_ERR_INVALID_ARG, "f, g, f_xx, g_yy or out is NULL");
+    char* w = (char*)ws;
+    float* g_xx = (float*)(w + o_gxx);
+    float* f_yy = (float*)(w + o_fyy);
+    size_t sz = solve_ws;
+    rc = ot_solve(p, f, g, &o, nullptr, ws, &sz, stream);
+    if (rc) return rc;
+    rc = ot_solve(&pxx, f_xx, g_xx, &oz, nullptr, ws, &sz, stream);
+    if (rc) return rc;
+    rc = ot_solve(&pyy, f_yy, g_yy, &oz, nullptr, ws, &sz, stream);
+    if (rc) return rc;
+    OT_HIP(launch_dual_values(p->a, p->b, (int)p->n, (int)p->m, f, g, f_xx, g_xx, f_yy, g_yy, out,
+                              (hipStream_t)stream));
     return OT_OK;
   } catch (...) {
     return fail(OT_ERR_HIP, "unexpected host exception");

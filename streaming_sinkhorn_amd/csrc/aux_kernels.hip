@@ -100,6 +100,48 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(
 
 int lse_merge_blocks(int rows) { return (rows + 255) / 256; }
 
+// <w, pot> in fp64 over one workgroup in a fixed order (w = NULL: uniform 1/rows).
+__device__ double dual_term(const float* __restrict__ w, const float* __restrict__ pot, int rows,
+                            double* sh) {
+  double s = 0.0;
+  const double u = 1.0 / (double)rows;
+  for (int i = threadIdx.x; i < rows; i += 256) s += (w ? (double)w[i] : u) * (double)pot[i];
+  sh[threadIdx.x] = s;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) sh[threadIdx.x] += sh[threadIdx.x + o];
+    __syncthreads();
+  }
+  const double t = sh[0];
+  __syncthreads();
+  return t;
+}
+
+// out = [S, OT(mu, nu), OT(mu, mu), OT(nu, nu)] with OT = <a, f> + <b, g>.
+__global__ __launch_bounds__(256) void dual_values_kernel(
+    const float* __restrict__ a, const float* __restrict__ b, int n, int m,
+    const float* __restrict__ f, const float* __restrict__ g, const float* __restrict__ fxx,
+    const float* __restrict__ gxx, const float* __restrict__ fyy, const float* __restrict__ gyy,
+    float* __restrict__ out) {
+  __shared__ double sh[256];
+  const double xy = dual_term(a, f, n, sh) + dual_term(b, g, m, sh);
+  const double xx = dual_term(a, fxx, n, sh) + dual_term(a, gxx, n, sh);
+  const double yy = dual_term(b, fyy, m, sh) + dual_term(b, gyy, m, sh);
+  if (threadIdx.x == 0) {
+    out[0] = (float)(xy - 0.5 * xx - 0.5 * yy);
+    out[1] = (float)xy;
+    out[2] = (float)xx;
+    out[3] = (float)yy;
+  }
+}
+
+hipError_t launch_dual_values(const float* a, const float* b, int n, int m, const float* f,
+                              const float* g, const float* fxx, const float* gxx, const float* fyy,
+                              const float* gyy, float* out, hipStream_t st) {
+  dual_values_kernel<<<1, 256, 0, st>>>(a, b, n, m, f, g, fxx, gxx, fyy, gyy, out);
+  return hipGetLastError();
+}
+
 // Deterministic single-workgroup sum of `count` partials (fixed order).
 __global__ __launch_bounds__(256) void err_reduce_kernel(const float* __restrict__ part, int count,
                                                           float* __restrict__ out) {

@@ -66,6 +66,11 @@ hipError_t launch_lse_merge(const float2* part, int splits, int rpad, int rows, 
                             float* bias_out, float* err_part, int with_err, int write_pot,
                             int avg, hipStream_t st);
 int lse_merge_blocks(int rows);
+// Sinkhorn divergence from three potential pairs: out = [S, OT(mu, nu),
+// OT(mu, mu), OT(nu, nu)], dual values summed in fp64 (a, b NULL: uniform).
+hipError_t launch_dual_values(const float* a, const float* b, int n, int m, const float* f,
+                              const float* g, const float* fxx, const float* gxx, const float* fyy,
+                              const float* gyy, float* out, hipStream_t st);
 hipError_t launch_err_reduce(const float* part, int count, float* out, hipStream_t st);
 hipError_t launch_nonfinite(const float* f, int n, const float* g, int m, float* out,
                             hipStream_t st);

@@ -272,3 +272,41 @@ def test_prep_validation(args, code):
                           base["labels"], base["W"], base["n_labels"], base["side"], base["out"],
                           base["sqn"], None)
     assert rc == code, L.ot_last_error()
+
+
+@pytest.mark.parametrize("eps_start,decay,code", [
+    (-1.0, 0.5, ssa.OT_ERR_INVALID_ARG),
+    (float("nan"), 0.5, ssa.OT_ERR_INVALID_ARG),
+    (1.0, 0.0, ssa.OT_ERR_INVALID_ARG),
+    (1.0, 1.0, ssa.OT_ERR_INVALID_ARG),
+    (1.0, float("nan"), ssa.OT_ERR_INVALID_ARG),
+    (0.05, 7.0, ssa.OT_OK),            # eps_start below eps: scaling off, decay unused
+    (1.0, 0.5, ssa.OT_OK),
+])
+def test_eps_scaling_option_validation(eps_start, decay, code):
+    L = ssa.lib()
+    p = _problem(eps=0.1)
+    opts = ssa._solve_opts(10, eps_start=eps_start, eps_decay=decay)
+    sz = ctypes.c_size_t(0)
+    rc = L.ot_solve(ctypes.byref(p), None, None, ctypes.byref(opts), None, None, ctypes.byref(sz), None)
+    assert rc == code, L.ot_last_error()
+
+
+def test_divergence_workspace_and_validation():
+    L = ssa.lib()
+    p = _problem(300, 200, 16)
+    opts = ssa._solve_opts(10)
+    sz = ctypes.c_size_t(0)
+    assert L.ot_sinkhorn_divergence(ctypes.byref(p), ctypes.byref(opts), None, None, None, None, None,
+                                    None, ctypes.byref(sz), None) == 0
+    s_div = sz.value
+    sz = ctypes.c_size_t(0)
+    assert L.ot_solve(ctypes.byref(p), None, None, ctypes.byref(opts), None, None, ctypes.byref(sz),
+                      None) == 0
+    assert s_div >= sz.value + (300 + 200) * 4
+    assert L.ot_sinkhorn_divergence(ctypes.byref(p), None, None, None, None, None, None, None,
+                                    ctypes.byref(sz), None) == ssa.OT_ERR_INVALID_ARG
+    p.flags = ssa.OT_COST_AFFINE
+    p.x_sqn, p.y_sqn = 3 << 20, 4 << 20
+    assert L.ot_sinkhorn_divergence(ctypes.byref(p), ctypes.byref(opts), None, None, None, None, None,
+                                    None, ctypes.byref(sz), None) == ssa.OT_ERR_UNSUPPORTED
