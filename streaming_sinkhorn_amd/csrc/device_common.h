@@ -149,7 +149,7 @@ __device__ __forceinline__ bool lse_fast(const f32x16& a, float Mf, float M, flo
   // Exact path when: the tile could overflow; the stabiliser is not set; or the
   // tile was folded before it was set (Mf = 0 above a lower M), where the
   // rescale factor itself could overflow.
-  return !(s < 0x1p64f) || !(Snew >= 0x1p-64f) || !(M > 0.5f * kUnset) || !(Mf <= M);
+  return !(s < 0x1p64f) | !(Snew >= 0x1p-64f) | !(M > 0.5f * kUnset) | !(Mf <= M);
 }
 
 // Exact tile: raise M to the tile maximum (shared by the lane pair), rescale.
@@ -176,16 +176,19 @@ __device__ __forceinline__ void lse_exact(const f32x16& a, float Mf, float& M, f
 template <int MODE, int RI>
 __device__ __forceinline__ void lse_tail(const f32x16 (&acc)[RI], const float (&Mf)[RI],
                                          float (&M)[RI], float (&S)[RI], float ks) {
-  float Sn[RI];
-  bool slow = false;
+  float So[RI];
+  int slow = 0;
 #pragma unroll
-  for (int ri = 0; ri < RI; ++ri) slow |= lse_fast<MODE != kModeBF16>(acc[ri], Mf[ri], M[ri], S[ri], ks, Sn[ri]);
+  for (int ri = 0; ri < RI; ++ri) {
+    So[ri] = S[ri];
+    slow |= lse_fast<MODE != kModeBF16>(acc[ri], Mf[ri], M[ri], So[ri], ks, S[ri]);
+  }
   if (__builtin_amdgcn_ballot_w64(slow) != 0) {
 #pragma unroll
-    for (int ri = 0; ri < RI; ++ri) lse_exact(acc[ri], Mf[ri], M[ri], S[ri], ks);
-  } else {
-#pragma unroll
-    for (int ri = 0; ri < RI; ++ri) S[ri] = Sn[ri];
+    for (int ri = 0; ri < RI; ++ri) {
+      S[ri] = So[ri];
+      lse_exact(acc[ri], Mf[ri], M[ri], S[ri], ks);
+    }
   }
 }
 

@@ -81,19 +81,26 @@ __device__ __forceinline__ void pipe_stage(const u32x4* __restrict__ Cp,
 #pragma unroll
   for (int ri = 0; ri < RI; ++ri) MfN[ri] = fold_of(M[ri]);
   score_tile<MODE, KB, RI>(yN, xr, wN, h, MfN, accN);
-  float Sn[RI];
-  bool slow = false;
+  // The fast-path sums are taken unconditionally (the rare exact path restores
+  // the old ones): no row's work becomes conditional on another's, so the
+  // stage stays one scheduling region in which the exponentials of tile k
+  // interleave with the matrix work of tile k+1.
+  float So[RI];
+  int slow = 0;
 #pragma unroll
-  for (int ri = 0; ri < RI; ++ri) slow |= lse_fast<MODE != kModeBF16>(accC[ri], MfC[ri], M[ri], S[ri], ks, Sn[ri]);
+  for (int ri = 0; ri < RI; ++ri) {
+    So[ri] = S[ri];
+    slow |= lse_fast<MODE != kModeBF16>(accC[ri], MfC[ri], M[ri], So[ri], ks, S[ri]);
+  }
   load_ctile<KB>(Cp, cbias, jt_refill, lane, yN, wN);
   stage_schedule<MODE, KB, RI>();
   __builtin_amdgcn_sched_barrier(0);
   if (__builtin_amdgcn_ballot_w64(slow) != 0) {
 #pragma unroll
-    for (int ri = 0; ri < RI; ++ri) lse_exact(accC[ri], MfC[ri], M[ri], S[ri], ks);
-  } else {
-#pragma unroll
-    for (int ri = 0; ri < RI; ++ri) S[ri] = Sn[ri];
+    for (int ri = 0; ri < RI; ++ri) {
+      S[ri] = So[ri];
+      lse_exact(accC[ri], MfC[ri], M[ri], S[ri], ks);
+    }
   }
 }
 
@@ -303,21 +310,24 @@ __global__ __launch_bounds__(256) void lse_lds_kernel(
 #pragma unroll
     for (int ri = 0; ri < RI; ++ri) MfN[ri] = fold_of(M[ri]);
     score_tile_lds<MODE, KB, RI>(lds[(k + 1) & 1], lane, xr, wN, h, MfN, accN);
-    float Sn[RI];
-    bool slow = false;
+    // fast-path sums taken unconditionally (see pipe_stage)
+    float So[RI];
+    int slow = 0;
 #pragma unroll
-    for (int ri = 0; ri < RI; ++ri)
-      slow |= lse_fast<MODE != kModeBF16>(accC[ri], MfC[ri], M[ri], S[ri], ks, Sn[ri]);
+    for (int ri = 0; ri < RI; ++ri) {
+      So[ri] = S[ri];
+      slow |= lse_fast<MODE != kModeBF16>(accC[ri], MfC[ri], M[ri], So[ri], ks, S[ri]);
+    }
     stage_store<KB>(lds[k & 1], tid, g);
     wC = w2;  // the buffer of tile k now receives tile k+2
     stage_schedule_lds<MODE, KB, RI>();
     __builtin_amdgcn_sched_barrier(0);
     if (__builtin_amdgcn_ballot_w64(slow) != 0) {
 #pragma unroll
-      for (int ri = 0; ri < RI; ++ri) lse_exact(accC[ri], MfC[ri], M[ri], S[ri], ks);
-    } else {
-#pragma unroll
-      for (int ri = 0; ri < RI; ++ri) S[ri] = Sn[ri];
+      for (int ri = 0; ri < RI; ++ri) {
+        S[ri] = So[ri];
+        lse_exact(accC[ri], MfC[ri], M[ri], S[ri], ks);
+      }
     }
   };
 
