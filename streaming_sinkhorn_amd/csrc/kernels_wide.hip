@@ -18,22 +18,25 @@ namespace flashot {
 // Tiled pass for wide points. A workgroup owns 4 RT row tiles (each wave RT
 // of them) and walks its split's column blocks of CT tiles; for each block
 // the score tiles are accumulated over the whole dimension in stages of BK
-// k-blocks. Each stage's slice of the row block and of the column block is
-// staged once in LDS (double-buffered, one barrier per stage) and read by
-// all four waves, so a wave's RT + CT fragments feed RT * CT MFMA tiles.
-// After a block's last stage the bias MFMA folds in bias_j - M_i and the
-// online LSE (lazy stabiliser, device_common.h) consumes the RT x CT tiles.
+// k-blocks. The stage's slice of the column block, which all four waves
+// use, is staged once in LDS (double-buffered, one barrier per stage); each
+// wave loads the slice of its own row tiles straight into registers (two
+// register sets, each refilled right after the stage that read it), so LDS
+// carries only the shared operand. A wave's RT + CT fragments feed RT * CT
+// MFMA tiles. After a block's last stage the bias MFMA folds in
+// bias_j - M_i and the online LSE (lazy stabiliser, device_common.h)
+// consumes the RT x CT tiles.
 // Units: 1 KiB operand units of the packed layout; KU units per k-block
 // (3 in split mode), kbp units per tile, padded to whole stages.
 // ---------------------------------------------------------------------------
 template <int MODE>
 constexpr int wide_ku() { return MODE == kModeSplit ? 3 : 1; }
 
-template <int MODE, int RT, int CT, int BK>
-constexpr int wide_stage_elems() { return (4 * RT + CT) * BK * wide_ku<MODE>() * 64; }
+template <int MODE, int CT, int BK>
+constexpr int wide_stage_elems() { return CT * BK * wide_ku<MODE>() * 64; }
 
-template <int MODE, int RT, int CT, int BK>
-constexpr int wide_loads() { return (wide_stage_elems<MODE, RT, CT, BK>() + 255) / 256; }
+template <int MODE, int CT, int BK>
+constexpr int wide_loads() { return (wide_stage_elems<MODE, CT, BK>() + 255) / 256; }
 
 template <int MODE, int RT, int CT, int BK>
 __global__ __launch_bounds__(256) void lse_wide_kernel(
@@ -43,7 +46,7 @@ __global__ __launch_bounds__(256) void lse_wide_kernel(
   constexpr int KU = wide_ku<MODE>();
   constexpr int SU = BK * KU;               // units per tile per stage
   constexpr int NX = 4 * RT;                // row tiles of the workgroup
-  constexpr int NL = wide_loads<MODE, RT, CT, BK>();
+  constexpr int NL = wide_loads<MODE, CT, BK>();
   __shared__ u32x4 lds[2][NL * 256];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -66,35 +69,41 @@ __global__ __launch_bounds__(256) void lse_wide_kernel(
   const int total = nb * nstages;
   const float ks = MODE == kModeBF16 ? c : 1.0f;
 
-  // Per-thread staging slots: slot q < NX is row tile rt0 + q, else column
-  // tile q - NX of the current block; unit u of the stage; lane l. Row-slot
-  // sources are fixed; column-slot sources move with the block.
-  const u32x4* src[NL];
-  bool isx[NL];
-  int cq[NL];
+  // Column staging slots of this thread: column tile cq of the current block,
+  // unit offset uo within the stage.
+  int cq[NL], uo[NL];
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
-    const int e = min(tid + 256 * i, wide_stage_elems<MODE, RT, CT, BK>() - 1);
-    const int q = e / (SU * 64);
-    const int uo = ((e / 64) % SU) * 64 + (e & 63);
-    isx[i] = q < NX;
-    cq[i] = q - NX;
-    src[i] = isx[i] ? Rp + (size_t)min(rt0 + q, rtiles - 1) * kbp * 64 + uo : Cp + uo;
+    const int e = min(tid + 256 * i, wide_stage_elems<MODE, CT, BK>() - 1);
+    cq[i] = e / (SU * 64);
+    uo[i] = ((e / 64) % SU) * 64 + (e & 63);
   }
-  // Loads stage `step` (clamped to the last one) into registers: branch-free.
+  // Loads column stage `step` (clamped to the last one) into registers: branch-free.
   auto gload = [&](int step, u32x4 (&g)[NL]) {
     step = min(step, total - 1);
     const int blk = b0 + step / nstages;
     const size_t koff = (size_t)(step % nstages) * SU * 64;
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const size_t coff = (size_t)min(blk * CT + cq[i], ctiles - 1) * kbp * 64;
-      g[i] = src[i][(isx[i] ? 0 : coff) + koff];
-    }
+    for (int i = 0; i < NL; ++i)
+      g[i] = Cp[(size_t)min(blk * CT + cq[i], ctiles - 1) * kbp * 64 + koff + uo[i]];
   };
   auto sstore = [&](u32x4* buf, const u32x4 (&g)[NL]) {
 #pragma unroll
     for (int i = 0; i < NL; ++i) buf[tid + 256 * i] = g[i];
+  };
+  // This wave's row tiles (clamped; rows past the last tile are computed and
+  // never written) and their stage slices, loaded straight into registers.
+  const u32x4* xsrc[RT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r)
+    xsrc[r] = Rp + (size_t)min(rt0 + wave * RT + r, rtiles - 1) * kbp * 64 + lane;
+  auto rload = [&](int step, u32x4 (&x)[RT][SU]) {
+    step = min(step, total - 1);
+    const size_t koff = (size_t)(step % nstages) * SU * 64;
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int u = 0; u < SU; ++u) x[r][u] = xsrc[r][koff + u * 64];
   };
 
   float M[RT], S[RT];
@@ -103,37 +112,36 @@ __global__ __launch_bounds__(256) void lse_wide_kernel(
     M[r] = kUnset;
     S[r] = 0.f;
   }
-  // Two register staging sets: the load of stage t is issued at the start of
+  // Two column staging sets: the load of stage t is issued at the start of
   // stage t - 2 and stored to LDS at the end of stage t - 1, so it has two
-  // stages of matrix work to arrive. nstages is even (padded by the host).
+  // stages of matrix work to arrive. Row slices: set A holds the even stages,
+  // set B the odd ones; each is refilled once its stage has been computed.
+  // nstages is even (padded by the host).
   u32x4 gA[NL], gB[NL];
+  u32x4 xA[RT][SU], xB[RT][SU];
   gload(0, gA);
+  rload(0, xA);
   sstore(lds[0], gA);
   gload(1, gB);
+  rload(1, xB);
   __syncthreads();
 
-  auto compute = [&](const u32x4* buf, f32x16 (&acc)[RT][CT]) {
+  auto compute = [&](const u32x4* buf, const u32x4 (&x)[RT][SU], f32x16 (&acc)[RT][CT]) {
 #pragma unroll
     for (int kb = 0; kb < BK; ++kb) {
-      u32x4 xf[RT][KU], yf[CT][KU];
-#pragma unroll
-      for (int r = 0; r < RT; ++r)
-#pragma unroll
-        for (int u = 0; u < KU; ++u)
-          xf[r][u] = buf[((wave * RT + r) * SU + kb * KU + u) * 64 + lane];
+      u32x4 yf[CT][KU];
 #pragma unroll
       for (int q = 0; q < CT; ++q)
 #pragma unroll
-        for (int u = 0; u < KU; ++u)
-          yf[q][u] = buf[((NX + q) * SU + kb * KU + u) * 64 + lane];
+        for (int u = 0; u < KU; ++u) yf[q][u] = buf[(q * SU + kb * KU + u) * 64 + lane];
 #pragma unroll
       for (int r = 0; r < RT; ++r)
 #pragma unroll
         for (int q = 0; q < CT; ++q) {
           if constexpr (MODE == kModeSplit)
-            acc[r][q] = mfma_split(yf[q], xf[r], acc[r][q]);
+            acc[r][q] = mfma_split(yf[q], &x[r][kb * KU], acc[r][q]);
           else
-            acc[r][q] = mfma_kblock<MODE == kModeBF16>(yf[q][0], xf[r][0], acc[r][q]);
+            acc[r][q] = mfma_kblock<MODE == kModeBF16>(yf[q][0], x[r][kb], acc[r][q]);
         }
     }
   };
@@ -146,14 +154,16 @@ __global__ __launch_bounds__(256) void lse_wide_kernel(
 #pragma unroll
       for (int q = 0; q < CT; ++q) acc[r][q] = f32x16{};
     for (int st = 0; st < nstages; st += 2, step += 2) {
-      // stage `step` is in lds[0]; gB holds stage step + 1
+      // stage `step`: columns in lds[0], rows in xA; gB / xB hold stage step + 1
       gload(step + 2, gA);
-      compute(lds[0], acc);
+      compute(lds[0], xA, acc);
+      rload(step + 2, xA);
       sstore(lds[1], gB);  // lds[1] was last read in stage step - 1
       __syncthreads();
-      // stage step + 1 is in lds[1]; gA holds stage step + 2
+      // stage step + 1: columns in lds[1], rows in xB; gA / xA hold stage step + 2
       gload(step + 3, gB);
-      compute(lds[1], acc);
+      compute(lds[1], xB, acc);
+      rload(step + 3, xB);
       sstore(lds[0], gA);  // after the final stage nobody reads these stores
       __syncthreads();
     }
