@@ -32,12 +32,6 @@ int fail(int code, const std::string& msg) {
   return code;
 }
 
-int env_int(const char* name, int dflt) {
-  const char* v = std::getenv(name);
-  if (!v || !*v) return dflt;
-  return std::atoi(v);
-}
-
 
 // Operand layout and pass shape for a point dimension / storage type.
 //  - fp32 points use the three-part bf16 split unless the problem asks for
@@ -84,20 +78,16 @@ KConf kernel_conf(int64_t d, int bf16, bool allow_split, bool for_apply) {
     } else {
       const int ku = k.mode == 2 ? 3 : 1;
       k.ri = 2;
-      k.ct = k.mode == 2 ? 2 : 4;
+      k.ct = 4;
       k.bk = k.mode == 2 ? 1 : 2;
       k.kb = k.bk * ku;
       k.kbp = ceil_div(k.kblocks, 2 * k.bk) * 2 * k.bk * ku;  // an even number of stages
       k.xres = false;
     }
   }
-  const int ri_env = env_int("FLASHOT_RI", 0);
-  if (k.xres && (ri_env == 1 || ri_env == 2)) k.ri = ri_env;
   return k;
 }
 
-// Column splits: enough workgroups to fill 256 CUs several times over, at
-// least ~4 column tiles per split, a multiple of 8 when large (XCD locality).
 // Column splits: enough workgroups to fill 256 CUs several times over, at
 // least ~4 column units (tiles, or blocks of the wide pass) per split, a
 // multiple of 8 when large (XCD locality).
@@ -106,8 +96,8 @@ void choose_splits(PassShape& s, int cunits, int forced, int max_splits) {
   if (forced > 0) {
     S = forced;
   } else {
-    const int target = env_int("FLASHOT_TARGET_WG", 2048);
-    S = ceil_div(target, s.nrowgroups);
+    constexpr int kTargetWorkgroups = 2048;  // 8 per CU
+    S = ceil_div(kTargetWorkgroups, s.nrowgroups);
     const int most = cunits / 4 > 1 ? cunits / 4 : 1;
     if (S > most) S = most;
     if (S >= 8) S = (S + 7) / 8 * 8;

@@ -213,16 +213,19 @@ static void lse_wide_go(const PassShape& s, const void* Rp, const void* Cp, cons
 
 hipError_t launch_lse_wide(const PassShape& s, int mode, const void* Rp, const void* Cp,
                            const float* cbias, float c, float2* part, hipStream_t st) {
-  if (s.xres || s.ri != 2) return hipErrorInvalidValue;
-  if (mode == kModeSplit && s.ct == 2 && s.bk == 1)
-    lse_wide_go<kModeSplit, 2, 2, 1>(s, Rp, Cp, cbias, c, part, st);
-  else if (mode == kModeBF16 && s.ct == 4 && s.bk == 2)
-    lse_wide_go<kModeBF16, 2, 4, 2>(s, Rp, Cp, cbias, c, part, st);
-  else if (mode == kModeF32 && s.ct == 4 && s.bk == 2)
-    lse_wide_go<kModeF32, 2, 4, 2>(s, Rp, Cp, cbias, c, part, st);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+  if (s.xres) return hipErrorInvalidValue;
+#define WIDE_CASE(M, R, C, K)                                                   \
+  if (mode == M && s.ri == R && s.ct == C && s.bk == K) {                      \
+    lse_wide_go<M, R, C, K>(s, Rp, Cp, cbias, c, part, st);                    \
+    return hipGetLastError();                                                   \
+  }
+  // Shapes measured best on gfx950 among RT in {2, 4}, CT in {2, 4},
+  // BK in {1, 2, 4} (larger ones exceed 256 VGPRs or starve LDS / L2).
+  WIDE_CASE(kModeSplit, 2, 4, 1)
+  WIDE_CASE(kModeBF16, 2, 4, 2)
+  WIDE_CASE(kModeF32, 2, 4, 2)
+#undef WIDE_CASE
+  return hipErrorInvalidValue;
 }
 
 }  // namespace flashot
