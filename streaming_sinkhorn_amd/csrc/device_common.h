@@ -192,4 +192,88 @@ __device__ __forceinline__ void lse_tail(const f32x16 (&acc)[RI], const float (&
   }
 }
 
+// ---------------------------------------------------------------------------
+// Transport-vector variant (P v with one value column): next to S, the same
+// online recurrence carries T = sum_j exp2(score_ij - M) v_j, rescaled with S
+// whenever M moves, so (P v)_i = a_i 2^((f_i - alpha_i) log2(e)/eps + M) T.
+// ---------------------------------------------------------------------------
+// Values v_j of the 16 accumulator rows a lane holds in tile jt: row r of
+// the 32x32 accumulator is column j = 8 (r / 4) + 4 h + r % 4 of the tile.
+__device__ __forceinline__ f32x16 load_tile_values(const float* __restrict__ v, int jt, int h) {
+  const float4* p = reinterpret_cast<const float4*>(v + (size_t)jt * kTile + 4 * h);
+  f32x16 out;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float4 q = p[2 * k];
+    out[4 * k + 0] = q.x;
+    out[4 * k + 1] = q.y;
+    out[4 * k + 2] = q.z;
+    out[4 * k + 3] = q.w;
+  }
+  return out;
+}
+
+template <bool SCALED>
+__device__ __forceinline__ bool lse_fast_v(const f32x16& a, const f32x16& v, float Mf, float M,
+                                           float S, float T, float ks, float& Snew,
+                                           float& Tnew) {
+  float e0 = 0.f, e1 = 0.f, t0 = 0.f, t1 = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; r += 2) {
+    const float x0 = __builtin_amdgcn_exp2f(SCALED ? a[r] : ks * a[r]);
+    const float x1 = __builtin_amdgcn_exp2f(SCALED ? a[r + 1] : ks * a[r + 1]);
+    e0 += x0;
+    e1 += x1;
+    t0 = fmaf(x0, v[r], t0);
+    t1 = fmaf(x1, v[r + 1], t1);
+  }
+  const float s = e0 + e1;
+  const float f = __builtin_amdgcn_exp2f(ks * (Mf - M));
+  Snew = fmaf(s, f, S);
+  Tnew = fmaf(t0 + t1, f, T);
+  return !(s < 0x1p64f) | !(Snew >= 0x1p-64f) | !(M > 0.5f * kUnset) | !(Mf <= M);
+}
+
+__device__ __forceinline__ void lse_exact_v(const f32x16& a, const f32x16& v, float Mf, float& M,
+                                            float& S, float& T, float ks) {
+  float m = max16(a) + Mf;
+  m = fmaxf(m, __shfl_xor(m, 32));
+  m = fmaxf(m, M);
+  const float t = Mf - m;
+  float e = 0.f, tv = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const float x = __builtin_amdgcn_exp2f(ks * (a[r] + t));
+    e += x;
+    tv = fmaf(x, v[r], tv);
+  }
+  const float sc = __builtin_amdgcn_exp2f(ks * (M - m));
+  S = fmaf(S, sc, e);
+  T = fmaf(T, sc, tv);
+  M = m;
+}
+
+template <int MODE, int RI>
+__device__ __forceinline__ void lse_tail_v(const f32x16 (&acc)[RI], const f32x16& v,
+                                           const float (&Mf)[RI], float (&M)[RI], float (&S)[RI],
+                                           float (&T)[RI], float ks) {
+  float So[RI], To[RI];
+  int slow = 0;
+#pragma unroll
+  for (int ri = 0; ri < RI; ++ri) {
+    So[ri] = S[ri];
+    To[ri] = T[ri];
+    slow |= lse_fast_v<MODE != kModeBF16>(acc[ri], v, Mf[ri], M[ri], So[ri], To[ri], ks, S[ri],
+                                          T[ri]);
+  }
+  if (__builtin_amdgcn_ballot_w64(slow) != 0) {
+#pragma unroll
+    for (int ri = 0; ri < RI; ++ri) {
+      S[ri] = So[ri];
+      T[ri] = To[ri];
+      lse_exact_v(acc[ri], v, Mf[ri], M[ri], S[ri], T[ri], ks);
+    }
+  }
+}
+
 }  // namespace flashot

@@ -176,9 +176,23 @@ struct Carver {
   }
 };
 
-// HVP vectors beyond the transport workspace.
+// Transport-vector passes of the conjugate gradients (P p, P^T u) on the
+// log-sum-exp layout: both clouds packed as for the Sinkhorn half-steps
+// (three-part bf16 split by default), column biases in log2 units, and the
+// register-resident passes with a value column. Used when that layout is
+// register-resident (d <= 128); wider points use the apply passes.
+struct VecWs {
+  bool on;
+  KConf k;
+  PassShape F, G;  // F: rows x, columns y; G: rows y, columns x
+  size_t o_xs, o_ys, o_bx, o_by, o_part, o_partT, o_ones, o_rv, o_cv;
+};
+
+// HVP vectors beyond the transport workspace. pd and u are padded to whole
+// tiles (zeros) because the vector passes read their values tile by tile.
 struct HvpWs {
   TransportWs T;
+  VecWs V;
   size_t o_py, o_r, o_c, o_xa, o_ra1, o_vb, o_ptv, o_rhs, o_w2, o_res, o_pd, o_q, o_pp, o_u,
       o_ptu, o_vf, o_pf, o_b5, o_part, o_cs;
   size_t total;
@@ -199,18 +213,76 @@ HvpWs hvp_layout(const ot_problem* p) {
   w.o_rhs = take((size_t)m * 4);
   w.o_w2 = take((size_t)m * 4);
   w.o_res = take((size_t)m * 4);
-  w.o_pd = take((size_t)m * 4);
+  w.o_pd = take((size_t)w.T.mpad * 4);
   w.o_q = take((size_t)m * 4);
   w.o_pp = take((size_t)n * 4);
-  w.o_u = take((size_t)n * 4);
+  w.o_u = take((size_t)w.T.npad * 4);
   w.o_ptu = take((size_t)m * 4);
   w.o_vf = take((size_t)m * (d + 1) * 4);
   w.o_pf = take((size_t)n * (d + 1) * 4);
   w.o_b5 = take((size_t)n * d * 4);
   w.o_part = take((size_t)kCgMaxParts * 4);
   w.o_cs = take(sizeof(CgState));
+  VecWs& v = w.V;
+  v.k = kernel_conf(p->d, 0, (p->flags & OT_NATIVE_F32) == 0);
+  v.on = v.k.xres;
+  if (v.on) {
+    const int nt = w.T.ntiles, mt = w.T.mtiles;
+    v.F = make_pass(nt, mt, v.k, v.k.ri, 0, 4096);
+    v.G = make_pass(mt, nt, v.k, v.k.ri, 0, 4096);
+    v.o_xs = take((size_t)nt * v.k.kbp * 1024);
+    v.o_ys = take((size_t)mt * v.k.kbp * 1024);
+    v.o_bx = take((size_t)w.T.npad * 4);
+    v.o_by = take((size_t)w.T.mpad * 4);
+    const size_t pf = (size_t)v.F.splits * w.T.npad, pg = (size_t)v.G.splits * w.T.mpad;
+    const size_t pm = pf > pg ? pf : pg;
+    v.o_part = take(pm * 8);
+    v.o_partT = take(pm * 4);
+    v.o_ones = take((size_t)(w.T.npad > w.T.mpad ? w.T.npad : w.T.mpad) * 4);
+    v.o_rv = take((size_t)w.T.npad * 4);
+    v.o_cv = take((size_t)w.T.mpad * 4);
+  }
   w.total = take.o;
   return w;
+}
+
+// Operands of the vector passes: X packed pre-scaled by c = 2 log2(e) / eps
+// (split or fp32 layout), Y unscaled, biases c ((pot - |.|^2) / 2 + (eps/2) log w)
+// from the transport context's log-weights.
+int prepare_vec(const Transport& t, const VecWs& v, char* w, hipStream_t st) {
+  const ot_problem* p = t.p;
+  const TransportWs& L = t.L;
+  void* xs = w + v.o_xs;
+  void* ys = w + v.o_ys;
+  if (v.k.mode == 2) {
+    OT_HIP(launch_pack_split((const float*)p->x, p->n, p->d, p->ldx, L.ntiles, v.k.kbp, t.c, xs, st));
+    OT_HIP(launch_pack_split((const float*)p->y, p->m, p->d, p->ldy, L.mtiles, v.k.kbp, 1.f, ys, st));
+  } else {
+    OT_HIP(launch_pack_points(p->x, 0, p->n, p->d, p->ldx, L.ntiles, v.k.kbp, t.c, xs, st));
+    OT_HIP(launch_pack_points(p->y, 0, p->m, p->d, p->ldy, L.mtiles, v.k.kbp, 1.f, ys, st));
+  }
+  OT_HIP(launch_bias_from_pot(t.g, t.ny, t.hy, (int)p->m, L.mpad, t.c, (float*)(w + v.o_by), st));
+  OT_HIP(launch_bias_from_pot(t.f, t.nx, t.hx, (int)p->n, L.npad, t.c, (float*)(w + v.o_bx), st));
+  return OT_OK;
+}
+
+// out = P v (tr = false; v: m values padded to whole tiles) or P^T v (tr =
+// true; v: n values, padded), one streamed pass plus the merge.
+int vec_pass(const Transport& t, const VecWs& v, char* w, bool tr, const float* vals, float* out,
+             hipStream_t st) {
+  const ot_problem* p = t.p;
+  const PassShape& S = tr ? v.G : v.F;
+  const void* Rp = w + (tr ? v.o_ys : v.o_xs);
+  const void* Cp = w + (tr ? v.o_xs : v.o_ys);
+  const float* bias = (const float*)(w + (tr ? v.o_bx : v.o_by));
+  float2* part = (float2*)(w + v.o_part);
+  float* partT = (float*)(w + v.o_partT);
+  const int rows = (int)(tr ? p->m : p->n);
+  const int rpad = tr ? t.L.mpad : t.L.npad;
+  OT_HIP(launch_vec_resident(S, v.k.mode, Rp, Cp, bias, vals, 1.f, part, partT, st));
+  OT_HIP(launch_vec_merge(part, partT, S.splits, rpad, rows, t.eps, tr ? t.g : t.f,
+                          tr ? t.ny : t.nx, tr ? t.wy : t.wx, out, st));
+  return OT_OK;
 }
 
 }  // namespace
@@ -299,6 +371,30 @@ int ot_hvp(const ot_problem* p, const float* f, const float* g, const float* A, 
     rc = transport(t, true, VB, d + 2, d + 2, PTV, c, false, st);
     if (rc) return rc;
     OT_HIP(launch_hvp_rhs(m, d, Y, p->ldy, PTV, rhs, w2, res, pd, st));
+    // Marginals used by the conjugate gradients. With the vector passes they
+    // are taken from those passes too (P 1, P^T 1), so that the Schur
+    // operator diag c - P^T diag(1/r) P annihilates the constant vector in
+    // the same arithmetic as its products (its damped null direction then
+    // has eigenvalue tau exactly, whatever rounding the passes carry).
+    const float* rs = r;
+    const float* csum = c;
+    if (L.V.on) {
+      // zero tile padding of the CG vectors (finite values for padded columns)
+      OT_HIP(launch_fill(pd + m, 0.f, L.T.mpad - m, st));
+      OT_HIP(launch_fill(u, 0.f, L.T.npad, st));
+      rc = prepare_vec(t, L.V, w, st);
+      if (rc) return rc;
+      float* ones = (float*)(w + L.V.o_ones);
+      float* rv = (float*)(w + L.V.o_rv);
+      float* cv = (float*)(w + L.V.o_cv);
+      OT_HIP(launch_fill(ones, 1.f, L.T.npad > L.T.mpad ? L.T.npad : L.T.mpad, st));
+      rc = vec_pass(t, L.V, w, false, ones, rv, st);
+      if (rc) return rc;
+      rc = vec_pass(t, L.V, w, true, ones, cv, st);
+      if (rc) return rc;
+      rs = rv;
+      csum = cv;
+    }
     // Conjugate gradients on (S + tau I) w2 = rhs: two transport-vector
     // products per iteration.
     OT_HIP(launch_cg_start(m, rhs, part, cs, st));
@@ -309,12 +405,14 @@ int ot_hvp(const ot_problem* p, const float* f, const float* g, const float* A, 
         OT_HIP(hipStreamSynchronize(st));
         if (done) break;
       }
-      rc = transport(t, false, pd, 1, 1, Pp, nullptr, false, st);
+      rc = L.V.on ? vec_pass(t, L.V, w, false, pd, Pp, st)
+                  : transport(t, false, pd, 1, 1, Pp, nullptr, false, st);
       if (rc) return rc;
-      OT_HIP(launch_cg_div(n, Pp, r, u, cs, st));
-      rc = transport(t, true, u, 1, 1, PTu, nullptr, false, st);
+      OT_HIP(launch_cg_div(n, Pp, rs, u, cs, st));
+      rc = L.V.on ? vec_pass(t, L.V, w, true, u, PTu, st)
+                  : transport(t, true, u, 1, 1, PTu, nullptr, false, st);
       if (rc) return rc;
-      OT_HIP(launch_cg_update(m, c, PTu, opts->tau, opts->tol, pd, q, w2, res, part, cs, st));
+      OT_HIP(launch_cg_update(m, csum, PTu, opts->tau, opts->tol, pd, q, w2, res, part, cs, st));
     }
     // Back-substitution values [w2 y_j, w2_j]: P diag(w2) Y and P w2 in one pass.
     OT_HIP(launch_hvp_vf(m, d, Y, p->ldy, w2, VF, st));

@@ -270,7 +270,33 @@ __global__ __launch_bounds__(256) void hvp_final_kernel(
   }
 }
 
+// Transport-vector merge: (P v)_i = w_i 2^((pot_i - nrm_i) log2(e)/eps + M) T
+// over the split partials (M in log2 units, T rescaled to the common M), in a
+// fixed order.
+__global__ __launch_bounds__(256) void vec_merge_kernel(
+    const float2* __restrict__ part, const float* __restrict__ partT, int splits, int rpad,
+    int rows, float eps, const float* __restrict__ pot, const float* __restrict__ norm,
+    const float* __restrict__ wgt, float* __restrict__ out) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows) return;
+  float M = part[i].x;
+  for (int s = 1; s < splits; ++s) M = fmaxf(M, part[(size_t)s * rpad + i].x);
+  float T = 0.f;
+  for (int s = 0; s < splits; ++s)
+    T = fmaf(partT[(size_t)s * rpad + i], exp2f(part[(size_t)s * rpad + i].x - M), T);
+  const float log2e = 1.4426950408889634f;
+  out[i] = wgt[i] * exp2f(fmaf(pot[i] - norm[i], log2e / eps, M)) * T;
+}
+
 // ---- launchers -------------------------------------------------------------------
+hipError_t launch_vec_merge(const float2* part, const float* partT, int splits, int rpad,
+                            int rows, float eps, const float* pot, const float* norm,
+                            const float* wgt, float* out, hipStream_t st) {
+  vec_merge_kernel<<<(rows + 255) / 256, 256, 0, st>>>(part, partT, splits, rpad, rows, eps, pot,
+                                                       norm, wgt, out);
+  return hipGetLastError();
+}
+
 static int rows4(int rows) { return (rows + 3) / 4; }
 
 hipError_t launch_hvp_prep(int n, int d, const float* X, int64_t ldx, const float* A, int64_t lda,

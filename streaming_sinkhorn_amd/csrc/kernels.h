@@ -52,6 +52,13 @@ hipError_t launch_bias_from_pot(const float* pot, const float* norm, const float
 // Register-resident passes (s.xres, kernels.hip) and k-chunked wide passes (kernels_wide.hip).
 hipError_t launch_lse_resident(const PassShape& s, int mode, const void* Rp, const void* Cp,
                                const float* cbias, float c, float2* part, hipStream_t st);
+// Transport-vector pass (P v, one value column) on the register-resident
+// layouts: (M, S) partials as launch_lse_resident plus T = sum exp2(score -
+// M) v per split and row in partT. vcol: the column side's values, padded
+// with zeros to whole tiles.
+hipError_t launch_vec_resident(const PassShape& s, int mode, const void* Rp, const void* Cp,
+                               const float* cbias, const float* vcol, float c, float2* part,
+                               float* partT, hipStream_t st);
 hipError_t launch_lse_wide(const PassShape& s, int mode, const void* Rp, const void* Cp,
                            const float* cbias, float c, float2* part, hipStream_t st);
 inline hipError_t launch_lse_partial(const PassShape& s, int mode, const void* Rp, const void* Cp,
@@ -122,6 +129,9 @@ hipError_t launch_cg_update(int m, const float* c, const float* PTu, float tau, 
                             CgState* cs, hipStream_t st);
 hipError_t launch_hvp_vf(int m, int d, const float* Y, int64_t ldy, const float* w2, float* VF,
                          hipStream_t st);
+hipError_t launch_vec_merge(const float2* part, const float* partT, int splits, int rpad,
+                            int rows, float eps, const float* pot, const float* norm,
+                            const float* wgt, float* out, hipStream_t st);
 hipError_t launch_hvp_final(int n, int d, float eps, const float* X, int64_t ldx, const float* A,
                             int64_t lda, const float* PY, const float* r, const float* xa,
                             const float* ra1, const float* PF, const float* B5, float* out,

@@ -70,14 +70,19 @@ __device__ __forceinline__ void stage_schedule() {
 // stabiliser), common-case LSE of the current tile accC, refill of the buffer
 // yN just consumed; then, outside the scheduled region, the exact path for
 // the waves that need it.
-template <int MODE, int KB, int RI>
+// VEC (transport-vector pass): vN receives the values of the tile scored in
+// this stage (jt_vals), vC holds those of the tile reduced now, and T
+// carries sum exp2(score - M) v next to S.
+template <int MODE, int KB, int RI, bool VEC>
 __device__ __forceinline__ void pipe_stage(const u32x4* __restrict__ Cp,
-                                           const float* __restrict__ cbias, int jt_refill,
-                                           int lane, int h, float ks, const u32x4 (&xr)[RI][KB],
-                                           u32x4 (&yN)[KB], float& wN, f32x16 (&accN)[RI],
-                                           float (&MfN)[RI], const f32x16 (&accC)[RI],
-                                           const float (&MfC)[RI], float (&M)[RI],
-                                           float (&S)[RI]) {
+                                           const float* __restrict__ cbias,
+                                           const float* __restrict__ vcol, int jt_refill,
+                                           int jt_vals, int lane, int h, float ks,
+                                           const u32x4 (&xr)[RI][KB], u32x4 (&yN)[KB], float& wN,
+                                           f32x16 (&accN)[RI], float (&MfN)[RI],
+                                           const f32x16 (&accC)[RI], const float (&MfC)[RI],
+                                           f32x16& vN, const f32x16& vC, float (&M)[RI],
+                                           float (&S)[RI], float (&T)[RI]) {
 #pragma unroll
   for (int ri = 0; ri < RI; ++ri) MfN[ri] = fold_of(M[ri]);
   score_tile<MODE, KB, RI>(yN, xr, wN, h, MfN, accN);
@@ -85,29 +90,71 @@ __device__ __forceinline__ void pipe_stage(const u32x4* __restrict__ Cp,
   // the old ones): no row's work becomes conditional on another's, so the
   // stage stays one scheduling region in which the exponentials of tile k
   // interleave with the matrix work of tile k+1.
-  float So[RI];
+  float So[RI], To[RI];
   int slow = 0;
 #pragma unroll
   for (int ri = 0; ri < RI; ++ri) {
     So[ri] = S[ri];
-    slow |= lse_fast<MODE != kModeBF16>(accC[ri], MfC[ri], M[ri], So[ri], ks, S[ri]);
+    if constexpr (VEC) {
+      To[ri] = T[ri];
+      slow |= lse_fast_v<MODE != kModeBF16>(accC[ri], vC, MfC[ri], M[ri], So[ri], To[ri], ks,
+                                            S[ri], T[ri]);
+    } else {
+      slow |= lse_fast<MODE != kModeBF16>(accC[ri], MfC[ri], M[ri], So[ri], ks, S[ri]);
+    }
   }
   load_ctile<KB>(Cp, cbias, jt_refill, lane, yN, wN);
+  if constexpr (VEC) vN = load_tile_values(vcol, jt_vals, h);
   stage_schedule<MODE, KB, RI>();
   __builtin_amdgcn_sched_barrier(0);
   if (__builtin_amdgcn_ballot_w64(slow) != 0) {
 #pragma unroll
     for (int ri = 0; ri < RI; ++ri) {
       S[ri] = So[ri];
-      lse_exact(accC[ri], MfC[ri], M[ri], S[ri], ks);
+      if constexpr (VEC) {
+        T[ri] = To[ri];
+        lse_exact_v(accC[ri], vC, MfC[ri], M[ri], S[ri], T[ri], ks);
+      } else {
+        lse_exact(accC[ri], MfC[ri], M[ri], S[ri], ks);
+      }
     }
   }
 }
 
-template <int MODE, int KB, int RI>
+// Tail LSE of RI tiles (plain or transport-vector).
+template <int MODE, int RI, bool VEC>
+__device__ __forceinline__ void tail_any(const f32x16 (&acc)[RI], const f32x16& v,
+                                         const float (&Mf)[RI], float (&M)[RI], float (&S)[RI],
+                                         float (&T)[RI], float ks) {
+  if constexpr (VEC) lse_tail_v<MODE, RI>(acc, v, Mf, M, S, T, ks);
+  else lse_tail<MODE, RI>(acc, Mf, M, S, ks);
+}
+
+// Partials of a row: (M in log2 units, S + S'), and T + T' for VEC.
+template <int RI, bool VEC>
+__device__ __forceinline__ void write_partials(const float (&M)[RI], const float (&S)[RI],
+                                               const float (&T)[RI], int h, int lane, int rt0,
+                                               int rtiles, int s, int rpad, float ks,
+                                               float2* __restrict__ part,
+                                               float* __restrict__ partT) {
+#pragma unroll
+  for (int ri = 0; ri < RI; ++ri) {
+    const float St = S[ri] + __shfl_xor(S[ri], 32);
+    float Tt = 0.f;
+    if constexpr (VEC) Tt = T[ri] + __shfl_xor(T[ri], 32);
+    if (h == 0 && rt0 + ri < rtiles) {
+      const size_t at = (size_t)s * rpad + (size_t)(rt0 + ri) * kTile + (lane & 31);
+      part[at] = make_float2(ks * M[ri], St);
+      if constexpr (VEC) partT[at] = Tt;
+    }
+  }
+}
+
+template <int MODE, int KB, int RI, bool VEC>
 __global__ __launch_bounds__(256) void lse_pipe_kernel(
     const u32x4* __restrict__ Rp, const u32x4* __restrict__ Cp, const float* __restrict__ cbias,
-    int rtiles, int ctiles, int splits, int tps, float c, float2* __restrict__ part, int rpad) {
+    const float* __restrict__ vcol, int rtiles, int ctiles, int splits, int tps, float c,
+    float2* __restrict__ part, float* __restrict__ partT, int rpad) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int h = lane >> 5;
@@ -126,11 +173,12 @@ __global__ __launch_bounds__(256) void lse_pipe_kernel(
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) xr[ri][kb] = Rp[((size_t)rt * KB + kb) * 64 + lane];
   }
-  float M[RI], S[RI];
+  float M[RI], S[RI], T[RI];
 #pragma unroll
   for (int ri = 0; ri < RI; ++ri) {
     M[ri] = kUnset;
     S[ri] = 0.f;
+    T[ri] = 0.f;
   }
 
   // Invariant at the top of the loop: accA holds the scores of tile k (with
@@ -139,39 +187,35 @@ __global__ __launch_bounds__(256) void lse_pipe_kernel(
   // reduced).
   u32x4 yA[KB], yB[KB];
   float wA, wB;
-  f32x16 accA[RI], accB[RI];
+  f32x16 accA[RI], accB[RI], vA{}, vB{};
   float MfA[RI], MfB[RI];
   load_ctile<KB>(Cp, cbias, jt0, lane, yA, wA);
   load_ctile<KB>(Cp, cbias, jt0 + min(1, last), lane, yB, wB);
 #pragma unroll
   for (int ri = 0; ri < RI; ++ri) MfA[ri] = 0.f;
   score_tile<MODE, KB, RI>(yA, xr, wA, h, MfA, accA);
+  if constexpr (VEC) vA = load_tile_values(vcol, jt0, h);
   load_ctile<KB>(Cp, cbias, jt0 + min(2, last), lane, yA, wA);
   int k = 0;
   for (; k + 2 <= last; k += 2) {
-    pipe_stage<MODE, KB, RI>(Cp, cbias, jt0 + min(k + 3, last), lane, h, ks, xr, yB, wB, accB,
-                             MfB, accA, MfA, M, S);
-    pipe_stage<MODE, KB, RI>(Cp, cbias, jt0 + min(k + 4, last), lane, h, ks, xr, yA, wA, accA,
-                             MfA, accB, MfB, M, S);
+    pipe_stage<MODE, KB, RI, VEC>(Cp, cbias, vcol, jt0 + min(k + 3, last), jt0 + k + 1, lane, h,
+                                  ks, xr, yB, wB, accB, MfB, accA, MfA, vB, vA, M, S, T);
+    pipe_stage<MODE, KB, RI, VEC>(Cp, cbias, vcol, jt0 + min(k + 4, last), jt0 + k + 2, lane, h,
+                                  ks, xr, yA, wA, accA, MfA, accB, MfB, vA, vB, M, S, T);
   }
   if (k + 1 <= last) {  // tiles k and k+1 remain
-    lse_tail<MODE, RI>(accA, MfA, M, S, ks);
+    tail_any<MODE, RI, VEC>(accA, vA, MfA, M, S, T, ks);
 #pragma unroll
     for (int ri = 0; ri < RI; ++ri) MfB[ri] = fold_of(M[ri]);
     score_tile<MODE, KB, RI>(yB, xr, wB, h, MfB, accB);
-    lse_tail<MODE, RI>(accB, MfB, M, S, ks);
+    if constexpr (VEC) vB = load_tile_values(vcol, jt0 + k + 1, h);
+    tail_any<MODE, RI, VEC>(accB, vB, MfB, M, S, T, ks);
   } else {  // tile k remains
-    lse_tail<MODE, RI>(accA, MfA, M, S, ks);
+    tail_any<MODE, RI, VEC>(accA, vA, MfA, M, S, T, ks);
   }
 
   // The lane pair shares M: the row's partial is (M in log2 units, S + S').
-#pragma unroll
-  for (int ri = 0; ri < RI; ++ri) {
-    const float St = S[ri] + __shfl_xor(S[ri], 32);
-    if (h == 0 && rt0 + ri < rtiles)
-      part[(size_t)s * rpad + (size_t)(rt0 + ri) * kTile + (lane & 31)] =
-          make_float2(ks * M[ri], St);
-  }
+  write_partials<RI, VEC>(M, S, T, h, lane, rt0, rtiles, s, rpad, ks, part, partT);
 }
 
 // ---------------------------------------------------------------------------
@@ -251,10 +295,11 @@ __device__ __forceinline__ void stage_schedule_lds() {
   __builtin_amdgcn_sched_group_barrier(0x200, kLoads, 0);      // LDS write of the next tile
 }
 
-template <int MODE, int KB, int RI>
+template <int MODE, int KB, int RI, bool VEC>
 __global__ __launch_bounds__(256) void lse_lds_kernel(
     const u32x4* __restrict__ Rp, const u32x4* __restrict__ Cp, const float* __restrict__ cbias,
-    int rtiles, int ctiles, int splits, int tps, float c, float2* __restrict__ part, int rpad) {
+    const float* __restrict__ vcol, int rtiles, int ctiles, int splits, int tps, float c,
+    float2* __restrict__ part, float* __restrict__ partT, int rpad) {
   constexpr int kLoads = stage_loads<KB>();
   __shared__ u32x4 lds[2][kLoads * 256];
   const int tid = threadIdx.x;
@@ -276,11 +321,12 @@ __global__ __launch_bounds__(256) void lse_lds_kernel(
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) xr[ri][kb] = Rp[((size_t)rt * KB + kb) * 64 + lane];
   }
-  float M[RI], S[RI];
+  float M[RI], S[RI], T[RI];
 #pragma unroll
   for (int ri = 0; ri < RI; ++ri) {
     M[ri] = kUnset;
     S[ri] = 0.f;
+    T[ri] = 0.f;
   }
 
   u32x4 g[kLoads];
@@ -295,14 +341,15 @@ __global__ __launch_bounds__(256) void lse_lds_kernel(
   // Invariant at stage k: accA / accB alternate holding the scores of tile k;
   // LDS buffer (k + 1) & 1 holds tile k+1; buffer k & 1 is free once every
   // wave has passed the stage barrier.
-  f32x16 accA[RI], accB[RI];
+  f32x16 accA[RI], accB[RI], vA{}, vB{};
   float MfA[RI], MfB[RI];
 #pragma unroll
   for (int ri = 0; ri < RI; ++ri) MfA[ri] = 0.f;
   score_tile_lds<MODE, KB, RI>(lds[0], lane, xr, wA, h, MfA, accA);
+  if constexpr (VEC) vA = load_tile_values(vcol, jt0, h);
 
   auto stage = [&](int k, f32x16(&accN)[RI], float(&MfN)[RI], float& wN, const f32x16(&accC)[RI],
-                   const float(&MfC)[RI], float& wC) {
+                   const float(&MfC)[RI], float& wC, f32x16& vN, const f32x16& vC) {
     __syncthreads();  // tile k+1 is in LDS; every wave is done reading tile k's buffer
     const int jt2 = jt0 + min(k + 2, last);
     stage_load<KB>(Cp, jt2, tid, g);
@@ -311,13 +358,20 @@ __global__ __launch_bounds__(256) void lse_lds_kernel(
     for (int ri = 0; ri < RI; ++ri) MfN[ri] = fold_of(M[ri]);
     score_tile_lds<MODE, KB, RI>(lds[(k + 1) & 1], lane, xr, wN, h, MfN, accN);
     // fast-path sums taken unconditionally (see pipe_stage)
-    float So[RI];
+    float So[RI], To[RI];
     int slow = 0;
 #pragma unroll
     for (int ri = 0; ri < RI; ++ri) {
       So[ri] = S[ri];
-      slow |= lse_fast<MODE != kModeBF16>(accC[ri], MfC[ri], M[ri], So[ri], ks, S[ri]);
+      if constexpr (VEC) {
+        To[ri] = T[ri];
+        slow |= lse_fast_v<MODE != kModeBF16>(accC[ri], vC, MfC[ri], M[ri], So[ri], To[ri], ks,
+                                              S[ri], T[ri]);
+      } else {
+        slow |= lse_fast<MODE != kModeBF16>(accC[ri], MfC[ri], M[ri], So[ri], ks, S[ri]);
+      }
     }
+    if constexpr (VEC) vN = load_tile_values(vcol, jt0 + k + 1, h);
     stage_store<KB>(lds[k & 1], tid, g);
     wC = w2;  // the buffer of tile k now receives tile k+2
     stage_schedule_lds<MODE, KB, RI>();
@@ -326,102 +380,122 @@ __global__ __launch_bounds__(256) void lse_lds_kernel(
 #pragma unroll
       for (int ri = 0; ri < RI; ++ri) {
         S[ri] = So[ri];
-        lse_exact(accC[ri], MfC[ri], M[ri], S[ri], ks);
+        if constexpr (VEC) {
+          T[ri] = To[ri];
+          lse_exact_v(accC[ri], vC, MfC[ri], M[ri], S[ri], T[ri], ks);
+        } else {
+          lse_exact(accC[ri], MfC[ri], M[ri], S[ri], ks);
+        }
       }
     }
   };
 
   int k = 0;
   for (; k + 2 <= last; k += 2) {
-    stage(k, accB, MfB, wB, accA, MfA, wA);
-    stage(k + 1, accA, MfA, wA, accB, MfB, wB);
+    stage(k, accB, MfB, wB, accA, MfA, wA, vB, vA);
+    stage(k + 1, accA, MfA, wA, accB, MfB, wB, vA, vB);
   }
   if (k + 1 <= last) {  // tiles k and k+1 remain; tile k+1 is in buffer (k+1)&1
     __syncthreads();
 #pragma unroll
     for (int ri = 0; ri < RI; ++ri) MfB[ri] = fold_of(M[ri]);
     score_tile_lds<MODE, KB, RI>(lds[(k + 1) & 1], lane, xr, wB, h, MfB, accB);
-    lse_tail<MODE, RI>(accA, MfA, M, S, ks);
-    lse_tail<MODE, RI>(accB, MfB, M, S, ks);
+    if constexpr (VEC) vB = load_tile_values(vcol, jt0 + k + 1, h);
+    tail_any<MODE, RI, VEC>(accA, vA, MfA, M, S, T, ks);
+    tail_any<MODE, RI, VEC>(accB, vB, MfB, M, S, T, ks);
   } else {
-    lse_tail<MODE, RI>(accA, MfA, M, S, ks);
+    tail_any<MODE, RI, VEC>(accA, vA, MfA, M, S, T, ks);
   }
 
-#pragma unroll
-  for (int ri = 0; ri < RI; ++ri) {
-    const float St = S[ri] + __shfl_xor(S[ri], 32);
-    if (h == 0 && rt0 + ri < rtiles)
-      part[(size_t)s * rpad + (size_t)(rt0 + ri) * kTile + (lane & 31)] =
-          make_float2(ks * M[ri], St);
-  }
+  write_partials<RI, VEC>(M, S, T, h, lane, rt0, rtiles, s, rpad, ks, part, partT);
 }
 
 // ---------------------------------------------------------------------------
 // Launchers of the register-resident passes.
 // ---------------------------------------------------------------------------
-template <int MODE, int KB, int RI>
-static void lse_pipe_go(const PassShape& s, const void* Rp, const void* Cp, const float* cbias,
-                        float c, float2* part, hipStream_t st) {
-  lse_pipe_kernel<MODE, KB, RI><<<s.nrowgroups * s.splits, 256, 0, st>>>(
-      (const u32x4*)Rp, (const u32x4*)Cp, cbias, s.rtiles, s.ctiles, s.splits, s.tps, c, part,
-      s.rtiles * kTile);
+// Arguments shared by every resident launch; vcol / partT are used by the
+// transport-vector instantiations only.
+struct ResArgs {
+  const void* Rp;
+  const void* Cp;
+  const float* cbias;
+  const float* vcol;
+  float c;
+  float2* part;
+  float* partT;
+};
+
+template <int MODE, int KB, int RI, bool VEC>
+static void lse_pipe_go(const PassShape& s, const ResArgs& a, hipStream_t st) {
+  lse_pipe_kernel<MODE, KB, RI, VEC><<<s.nrowgroups * s.splits, 256, 0, st>>>(
+      (const u32x4*)a.Rp, (const u32x4*)a.Cp, a.cbias, a.vcol, s.rtiles, s.ctiles, s.splits,
+      s.tps, a.c, a.part, a.partT, s.rtiles * kTile);
 }
 
-template <int MODE, int KB, int RI>
-static void lse_lds_go(const PassShape& s, const void* Rp, const void* Cp, const float* cbias,
-                       float c, float2* part, hipStream_t st) {
-  lse_lds_kernel<MODE, KB, RI><<<s.nrowgroups * s.splits, 256, 0, st>>>(
-      (const u32x4*)Rp, (const u32x4*)Cp, cbias, s.rtiles, s.ctiles, s.splits, s.tps, c, part,
-      s.rtiles * kTile);
+template <int MODE, int KB, int RI, bool VEC>
+static void lse_lds_go(const PassShape& s, const ResArgs& a, hipStream_t st) {
+  lse_lds_kernel<MODE, KB, RI, VEC><<<s.nrowgroups * s.splits, 256, 0, st>>>(
+      (const u32x4*)a.Rp, (const u32x4*)a.Cp, a.cbias, a.vcol, s.rtiles, s.ctiles, s.splits,
+      s.tps, a.c, a.part, a.partT, s.rtiles * kTile);
 }
 
-template <int MODE, int KB>
-static void resident_go(const PassShape& s, const void* Rp, const void* Cp, const float* cbias,
-                        float c, float2* part, hipStream_t st) {
+template <int MODE, int KB, bool VEC>
+static void resident_go(const PassShape& s, const ResArgs& a, hipStream_t st) {
   if (s.lds) {
-    if (s.ri == 2) lse_lds_go<MODE, KB, 2>(s, Rp, Cp, cbias, c, part, st);
-    else lse_lds_go<MODE, KB, 1>(s, Rp, Cp, cbias, c, part, st);
+    if (s.ri == 2) lse_lds_go<MODE, KB, 2, VEC>(s, a, st);
+    else lse_lds_go<MODE, KB, 1, VEC>(s, a, st);
   } else {
-    if (s.ri == 2) lse_pipe_go<MODE, KB, 2>(s, Rp, Cp, cbias, c, part, st);
-    else lse_pipe_go<MODE, KB, 1>(s, Rp, Cp, cbias, c, part, st);
+    if (s.ri == 2) lse_pipe_go<MODE, KB, 2, VEC>(s, a, st);
+    else lse_pipe_go<MODE, KB, 1, VEC>(s, a, st);
   }
 }
 
-static hipError_t lse_split_dispatch(const PassShape& s, const void* Rp, const void* Cp,
-                                     const float* cbias, float c, float2* part, hipStream_t st) {
+template <bool VEC>
+static hipError_t lse_split_dispatch(const PassShape& s, const ResArgs& a, hipStream_t st) {
   switch (s.kb) {
-    case 3: resident_go<kModeSplit, 3>(s, Rp, Cp, cbias, c, part, st); break;
-    case 6: resident_go<kModeSplit, 6>(s, Rp, Cp, cbias, c, part, st); break;
-    case 12: resident_go<kModeSplit, 12>(s, Rp, Cp, cbias, c, part, st); break;
+    case 3: resident_go<kModeSplit, 3, VEC>(s, a, st); break;
+    case 6: resident_go<kModeSplit, 6, VEC>(s, a, st); break;
+    case 12: resident_go<kModeSplit, 12, VEC>(s, a, st); break;
     case 24:  // 64 < d <= 128: one resident row tile per wave, columns through LDS
       if (!s.lds || s.ri != 1) return hipErrorInvalidValue;
-      lse_lds_go<kModeSplit, 24, 1>(s, Rp, Cp, cbias, c, part, st);
+      lse_lds_go<kModeSplit, 24, 1, VEC>(s, a, st);
       break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <int MODE>
-static hipError_t lse_resident_dispatch(const PassShape& s, const void* Rp, const void* Cp,
-                                        const float* cbias, float c, float2* part, hipStream_t st) {
+template <int MODE, bool VEC>
+static hipError_t lse_resident_dispatch(const PassShape& s, const ResArgs& a, hipStream_t st) {
   switch (s.kb) {
-    case 1: resident_go<MODE, 1>(s, Rp, Cp, cbias, c, part, st); break;
-    case 2: resident_go<MODE, 2>(s, Rp, Cp, cbias, c, part, st); break;
-    case 4: resident_go<MODE, 4>(s, Rp, Cp, cbias, c, part, st); break;
-    case 8: resident_go<MODE, 8>(s, Rp, Cp, cbias, c, part, st); break;
-    case 16: resident_go<MODE, 16>(s, Rp, Cp, cbias, c, part, st); break;
+    case 1: resident_go<MODE, 1, VEC>(s, a, st); break;
+    case 2: resident_go<MODE, 2, VEC>(s, a, st); break;
+    case 4: resident_go<MODE, 4, VEC>(s, a, st); break;
+    case 8: resident_go<MODE, 8, VEC>(s, a, st); break;
+    case 16: resident_go<MODE, 16, VEC>(s, a, st); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+template <bool VEC>
+static hipError_t resident_dispatch(const PassShape& s, int mode, const ResArgs& a,
+                                    hipStream_t st) {
+  if (!s.xres) return hipErrorInvalidValue;
+  if (mode == kModeSplit) return lse_split_dispatch<VEC>(s, a, st);
+  if (mode == kModeBF16) return lse_resident_dispatch<kModeBF16, VEC>(s, a, st);
+  return lse_resident_dispatch<kModeF32, VEC>(s, a, st);
+}
+
 hipError_t launch_lse_resident(const PassShape& s, int mode, const void* Rp, const void* Cp,
                                const float* cbias, float c, float2* part, hipStream_t st) {
-  if (!s.xres) return hipErrorInvalidValue;
-  if (mode == kModeSplit) return lse_split_dispatch(s, Rp, Cp, cbias, c, part, st);
-  if (mode == kModeBF16) return lse_resident_dispatch<kModeBF16>(s, Rp, Cp, cbias, c, part, st);
-  return lse_resident_dispatch<kModeF32>(s, Rp, Cp, cbias, c, part, st);
+  return resident_dispatch<false>(s, mode, ResArgs{Rp, Cp, cbias, nullptr, c, part, nullptr}, st);
+}
+
+hipError_t launch_vec_resident(const PassShape& s, int mode, const void* Rp, const void* Cp,
+                               const float* cbias, const float* vcol, float c, float2* part,
+                               float* partT, hipStream_t st) {
+  return resident_dispatch<true>(s, mode, ResArgs{Rp, Cp, cbias, vcol, c, part, partT}, st);
 }
 
 }  // namespace flashot
