@@ -54,8 +54,8 @@ ALU_PAIRS_PEAK = ALU_LANE_SLOTS_PER_S / ALU_SLOTS_PER_PAIR
 # FETCH_SIZE / WRITE_SIZE runs (scaled by the copy-kernel calibration), valid
 # only for the kernel source they were taken on.
 TRAFFIC = {
-    "c2": {"kernels_sha256": "5440f92b979f2f9d5b0d5e30a60f08f02eb3322a10aaca545d041dafbe7a6b78",
-           "bytes_per_launch": 74467080,
+    "c2": {"kernels_sha256": "73bdc5aa91285e5d9dc6d8f08648af973cf3920c59d7cb8ad27dbeed7c15226e",
+           "bytes_per_launch": 74472219,
            "source": "profiles/lse_lds_kernel_c2_n20000_d64_f32split_hbm_traffic.md"},
 }
 # Sources of the register-resident log-sum-exp kernels the counters describe.
