@@ -63,22 +63,43 @@ __device__ __forceinline__ float block_sum_256(float v, float* sh) {
   return sh[0];
 }
 
+// Eight lanes per row: lane k merges splits k, k + 8, ... online in one pass,
+// then the eight (M, S) pairs are combined by a fixed xor butterfly (every
+// lane of the group ends with the same values, so the result does not depend
+// on the lane). Workgroups cover 32 rows, so even 20000 rows give 625 of them.
+constexpr int kMergeLanes = 8;
+constexpr int kMergeRows = 256 / kMergeLanes;
+
 __global__ __launch_bounds__(256) void lse_merge_kernel(
     const float2* __restrict__ part, int splits, int rpad, int rows, float bscale, float eps,
     const float* __restrict__ norm, const float* __restrict__ hlw, const float* __restrict__ wgt,
     float* __restrict__ pot, float* __restrict__ bias_out, float* __restrict__ err_part,
     int with_err, int write_pot, int avg) {
   __shared__ float sh[256];
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  float e = 0.f;
+  const int sub = threadIdx.x & (kMergeLanes - 1);
+  const int i = blockIdx.x * kMergeRows + threadIdx.x / kMergeLanes;
+  float M = -3.0e38f, S = 0.f;
   if (i < rows) {
-    float M = part[i].x;
-    for (int s = 1; s < splits; ++s) M = fmaxf(M, part[(size_t)s * rpad + i].x);
-    float S = 0.f;
-    for (int s = 0; s < splits; ++s) {
+    for (int s = sub; s < splits; s += kMergeLanes) {
       const float2 ps = part[(size_t)s * rpad + i];
-      S += ps.y * exp2f(ps.x - M);
+      if (ps.x > M) {
+        S = fmaf(S, exp2f(M - ps.x), ps.y);
+        M = ps.x;
+      } else {
+        S = fmaf(ps.y, exp2f(ps.x - M), S);
+      }
     }
+  }
+#pragma unroll
+  for (int o = 1; o < kMergeLanes; o <<= 1) {
+    const float Mo = __shfl_xor(M, o);
+    const float So = __shfl_xor(S, o);
+    const float Mn = fmaxf(M, Mo);
+    S = S * exp2f(M - Mn) + So * exp2f(Mo - Mn);
+    M = Mn;
+  }
+  float e = 0.f;
+  if (sub == 0 && i < rows) {
     const float shifted = -eps * kLn2 * (M + log2f(S));
     const float nrm = norm[i];
     const float half = nrm + shifted;
@@ -89,7 +110,7 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(
       pot[i] = pnew;
       bias_out[i] = bscale * (0.5f * (pnew - nrm) + hlw[i]);
     }
-  } else if (i < rpad && write_pot) {
+  } else if (sub == 0 && i < rpad && write_pot) {
     bias_out[i] = kSentinel;
   }
   if (with_err) {
@@ -98,7 +119,7 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(
   }
 }
 
-int lse_merge_blocks(int rows) { return (rows + 255) / 256; }
+int lse_merge_blocks(int rows) { return (rows + kMergeRows - 1) / kMergeRows; }
 
 // <w, pot> in fp64 over one workgroup in a fixed order (w = NULL: uniform 1/rows).
 __device__ double dual_term(const float* __restrict__ w, const float* __restrict__ pot, int rows,
@@ -468,7 +489,7 @@ hipError_t launch_lse_merge(const float2* part, int splits, int rpad, int rows, 
                             const float* norm, const float* hlw, const float* wgt, float* pot,
                             float* bias_out, float* err_part, int with_err, int write_pot,
                             int avg, hipStream_t st) {
-  lse_merge_kernel<<<(rpad + 255) / 256, 256, 0, st>>>(part, splits, rpad, rows, bscale, eps, norm,
+  lse_merge_kernel<<<lse_merge_blocks(rpad), 256, 0, st>>>(part, splits, rpad, rows, bscale, eps, norm,
                                                        hlw, wgt, pot, bias_out, err_part,
                                                        with_err, write_pot, avg);
   return hipGetLastError();

@@ -183,3 +183,33 @@ def test_hvp_is_symmetric():
     rhs = float(torch.sum(A.double() * GB.double()))
     scale = float(torch.linalg.norm(B.double()) * torch.linalg.norm(GA.double()))
     assert abs(lhs - rhs) <= 1e-4 * scale
+
+
+@pytest.mark.parametrize("n,m,d,eps", [(200, 150, 8, 0.3), (130, 90, 70, 0.5)])
+def test_hvp_native_fp32_operands(n, m, d, eps):
+    """OT_NATIVE_F32: the conjugate-gradient passes form scores with the fp32
+    matrix instruction (register-pipelined kernel for d = 8, LDS-shared for d = 70)."""
+    say(f"hvp native n={n} m={m} d={d} eps={eps}")
+    data = workloads.hvp_parity_inputs(n, m, d, seed=n + d)
+    X, Y, a, b = (data[k].astype(np.float64) for k in ("X", "Y", "a", "b"))
+    f, g = oracle.sinkhorn(oracle.cost_matrix(X, Y), a, b, eps, 200)
+    f32, g32 = f.astype(np.float32), g.astype(np.float32)
+    t = lambda v: torch.from_numpy(np.ascontiguousarray(v)).to(DEV)
+    prob = ssa.problem(t(data["X"]), t(data["Y"]), eps, t(data["a"]), t(data["b"]), native_f32=True)
+    G, info = ssa.ot_hvp(prob, t(f32), t(g32), t(data["A"]), tau=1e-5, max_iters=500, tol=1e-6)
+    torch.cuda.synchronize()
+    ref, _, _ = H.hvp_schur_cg(X, Y, a, b, f32.astype(np.float64), g32.astype(np.float64), eps,
+                               data["A"].astype(np.float64), tau=1e-5, iters=500, tol=1e-6)
+    err = _rel(host64(G), ref)
+    say(f"  rel err {err:.2e}, cg iters {info['cg_iters']}")
+    assert err <= PV_TOL
+
+
+def test_hvp_tiny_single_partial_tile():
+    """n, m below one 32-row tile: every tile is ragged."""
+    prob, f, g, A, h = _setup(5, 7, 3, 0.4, seed=13, iters=100)
+    G, info = ssa.ot_hvp(prob, f, g, A, tau=1e-6, max_iters=50, tol=1e-7)
+    torch.cuda.synchronize()
+    ref, _, _ = H.hvp_schur_cg(h["X"], h["Y"], h["a"], h["b"], h["f"], h["g"], 0.4, h["A"],
+                               tau=1e-6, iters=50, tol=1e-7)
+    assert _rel(host64(G), ref) <= PV_TOL
