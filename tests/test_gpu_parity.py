@@ -371,3 +371,45 @@ def test_nonfinite_reported():
     with pytest.raises(ssa.OtError) as ei:
         ssa.ot_solve(prob, f, g, 3)
     assert ei.value.code == ssa.OT_ERR_NONFINITE
+
+
+# --- size edges -------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d,dtype", [(8192, "f32"), (8192, "bf16"), (4097, "f32")])
+def test_largest_dimension(d, dtype):
+    """d at OT_MAX_D (and one past a power of two): the wide pass with its
+    longest k-loop, split and bf16 operands; half-steps against the oracle."""
+    say(f"largest d={d} {dtype}")
+    n, m, eps = 70, 45, 0.1
+    data = workloads.make("c3_d16_bf16" if dtype == "bf16" else "c3_d16_f32", n=n, m=m, d=d)
+    prob = make_problem(data, eps=eps)
+    X, Y, a, b = oracle_inputs(prob)
+    C = oracle.cost_matrix(X, Y)
+    g0 = (np.random.default_rng(d).standard_normal(m) * 0.3).astype(np.float32)
+    f = zeros(n)
+    ssa.ot_update_f(prob, torch.from_numpy(g0).to(DEV), f)
+    torch.cuda.synchronize()
+    f_ref = oracle.update_f(C, g0.astype(np.float64), b, eps)
+    assert np.abs(host64(f) - f_ref).max() <= POT_TOL[dtype]
+    # and a short trajectory
+    f, g = zeros(n), zeros(m)
+    ssa.ot_solve(prob, f, g, 10, want_info=False)
+    torch.cuda.synchronize()
+    f_ref, g_ref = oracle.sinkhorn(C, a, b, eps, 10)
+    assert np.abs(host64(f) - f_ref).max() <= POT_TOL[dtype]
+    assert np.abs(host64(g) - g_ref).max() <= POT_TOL[dtype]
+
+
+def test_one_point_each_side():
+    """n = m = 1: a single pair; the potentials match the oracle's and stay finite."""
+    data = workloads.make("c3_d16_f32", n=1, m=1, d=7)
+    prob = make_problem(data)
+    X, Y, a, b = oracle_inputs(prob)
+    f, g = zeros(1), zeros(1)
+    info = ssa.ot_solve(prob, f, g, 5)
+    torch.cuda.synchronize()
+    C = oracle.cost_matrix(X, Y)
+    f_ref, g_ref = oracle.sinkhorn(C, a, b, 0.1, 5)
+    assert abs(float(host64(f)[0]) - f_ref[0]) <= POT_TOL["f32"]
+    assert abs(float(host64(g)[0]) - g_ref[0]) <= POT_TOL["f32"]
+    assert not info["nonfinite"]
