@@ -1,6 +1,6 @@
-// Internal interface between the host driver (api.hip) and the gfx950 kernels
-// (kernels.hip, kernels_wide.hip, apply_kernels.hip, aux_kernels.hip). Not
-// part of the public C ABI.
+// Internal interface between the host drivers (api.hip, hvp_api.hip) and the
+// gfx950 kernels (kernels.hip, kernels_wide.hip, apply_kernels.hip,
+// aux_kernels.hip, hvp_kernels.hip). Not part of the public C ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -85,7 +85,7 @@ def test_problem_validation(field, value, code):
 
 
 def test_split_and_native_workspaces_differ():
-    """fp32 points with d <= 64 pack three bf16 parts per k-block (3 KiB per 16
+    """fp32 points pack three bf16 parts per k-block (here d = 64: 3 KiB per 16
     values and 32 rows) unless OT_NATIVE_F32 asks for fp32 operands (2 KiB)."""
     L = ssa.lib()
     p = _problem(1024, 1024, 64)

@@ -83,7 +83,7 @@ NATIVE_HALF_CASES = [c for c in HALF_CASES if c[3] == "f32"]
 @pytest.mark.parametrize("n,m,d,dtype,eps", HALF_CASES)
 def test_half_steps_teacher_forced(n, m, d, dtype, eps, native):
     if native and (n, m, d, dtype, eps) not in NATIVE_HALF_CASES:
-        pytest.skip("the fp32 matrix-instruction option only differs for fp32 points with d <= 64")
+        pytest.skip("the fp32 matrix-instruction option only applies to fp32 points")
     say(f"half-steps n={n} m={m} d={d} dtype={dtype} eps={eps} native_f32={native}")
     base = "c3_d16_bf16" if dtype == "bf16" else "c3_d16_f32"
     data = workloads.make(base, n=n, m=m, d=d)
