@@ -36,7 +36,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 # MI355X published dense peaks.
-MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}
+MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0, "f16": 2500.0}
 HBM_PEAK_GBS = 8000.0
 # ALU bound of the online log-sum-exp, derived from the unit counts. The
 # published fp32 vector peak (157.3 TFLOP/s = 256 CUs x 2.4 GHz x 128 FMA
@@ -253,7 +253,9 @@ def main():
     ap.add_argument("--schedule", default="alternating", choices=["alternating", "symmetric"])
     ap.add_argument("--native-f32", action="store_true",
                     help="form fp32 scores with the fp32 matrix instruction instead of the "
-                         "three-part bf16 split")
+                         "two-part fp16 split")
+    ap.add_argument("--split-bf16", action="store_true",
+                    help="form fp32 scores from three bf16 parts per value (six products)")
     ap.add_argument("--hvp", action="store_true",
                     help="time the streaming Hessian-vector product instead of the solve")
     ap.add_argument("--hvp-iters", type=int, default=50, help="CG iterations K of --hvp")
@@ -292,7 +294,8 @@ def main():
     U = to_dev(data["U"]) if w.u_cols else None
     xs = torch.empty(w.n, device=dev)
     ys = torch.empty(w.m, device=dev)
-    prob = ssa.problem(X, Y, w.eps, a, b, x_sqn=xs, y_sqn=ys, native_f32=args.native_f32)
+    prob = ssa.problem(X, Y, w.eps, a, b, x_sqn=xs, y_sqn=ys, native_f32=args.native_f32,
+                       split_bf16=args.split_bf16)
     f = torch.zeros(w.n, device=dev)
     g = torch.zeros(w.m, device=dev)
     r = torch.empty(w.n, device=dev)
@@ -346,7 +349,11 @@ def main():
     pairs = float(w.n) * w.m
     mode = infos[-1]["operand_mode"]
     alg_flops = 2.0 * pairs * w.d
-    if mode == 2:
+    if mode == 3:
+        # fp32 scores formed from two fp16 parts per coordinate: three fp16
+        # products per fp32 product on the fp16 matrix cores.
+        mat_flops, mat_peak, mat_dtype = 3.0 * alg_flops, MFMA_PEAK_TFLOPS["f16"], "f16 (fp32 split)"
+    elif mode == 2:
         # fp32 scores formed from three bf16 parts per coordinate: six bf16
         # products per fp32 product on the bf16 matrix cores.
         mat_flops, mat_peak, mat_dtype = 6.0 * alg_flops, MFMA_PEAK_TFLOPS["bf16"], "bf16 (fp32 split)"
@@ -394,8 +401,8 @@ def main():
                         f"{args.schedule} iterations from zero potentials; outputs: {', '.join(outputs)}",
             "n": w.n, "m": w.m, "d": w.d, "eps": w.eps, "iters": T,
             "splits_f": last["splits_f"], "splits_g": last["splits_g"],
-            "operand_mode": ["fp32 MFMA", "bf16 MFMA", "fp32 as 3-part bf16 split on bf16 MFMA"][
-                last["operand_mode"]],
+            "operand_mode": ["fp32 MFMA", "bf16 MFMA", "fp32 as 3-part bf16 split on bf16 MFMA",
+                             "fp32 as 2-part fp16 split on fp16 MFMA"][last["operand_mode"]],
         },
         "roofline": roof,
         "marg_err_row": last["marg_err_row"],

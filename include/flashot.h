@@ -81,10 +81,13 @@ extern "C" {
 
 /* ot_problem flags. */
 #define OT_NATIVE_F32 1  /* fp32 points: form scores with fp32 MFMA instead of the default
-                            exact-to-fp32 split into three bf16 parts on the bf16 MFMA */
+                            two-part fp16 split on the fp16 MFMA */
 #define OT_COST_AFFINE 2 /* general affine cost C_ij = alpha_i + beta_j - <x_i, y_j>
                             (§3.1 "Scope of cost structure"): x_sqn carries alpha and
                             y_sqn carries beta, both required */
+#define OT_SPLIT_BF16 4  /* fp32 points: form scores from three bf16 parts per value on the
+                            bf16 MFMA (full fp32 exponent range); exclusive with
+                            OT_NATIVE_F32 */
 
 /*
  * The problem: two point clouds, their weights and eps (App. H.2 problem
@@ -99,7 +102,8 @@ extern "C" {
  *   a, b        device fp32 weights (n, m) or NULL for uniform
  *   x_sqn,y_sqn device fp32 squared norms ||x_i||^2, ||y_j||^2, or NULL to
  *               have them computed into the workspace
- *   flags       0, or OT_NATIVE_F32 and / or OT_COST_AFFINE.
+ *   flags       0, or one of OT_NATIVE_F32 / OT_SPLIT_BF16, and / or
+ *               OT_COST_AFFINE.
  *               OT_COST_AFFINE replaces the squared-Euclidean cost by
  *               C_ij = alpha_i + beta_j - <x_i, y_j> with alpha = x_sqn and
  *               beta = y_sqn (both must be given): x, y are the features Q, K
@@ -109,14 +113,22 @@ extern "C" {
  *               costs built by ot_prep_cosine / ot_prep_labels. OT_GRAD,
  *               ot_hvp and ot_apply_hadamard assume the squared-Euclidean
  *               cost and reject the flag.
- *               For fp32 points the log-sum-exp
- *               passes by default split every coordinate into
- *               three bf16 parts (hi + mid + lo, 24 significant bits) and form
- *               each score from the six largest partial products on the bf16
- *               matrix cores; the dropped terms are below 2^-26 of each
- *               product, finer than fp32 rounding. OT_NATIVE_F32 uses the
- *               fp32 matrix instruction instead. Transport application always
- *               uses fp32 products for fp32 points.
+ *               For fp32 points the log-sum-exp passes by default write
+ *               every coordinate as two fp16 parts (hi + lo, 22 significant
+ *               bits; X scaled by 2^a and Y by 2^-a, exact powers of two
+ *               chosen on the device to fit fp16) and form each score from
+ *               the three largest partial products on the fp16 matrix cores:
+ *               each coordinate product is off by at most about 3 * 2^-22 of
+ *               its size, the order of fp32 rounding over a dot product.
+ *               This covers every problem with
+ *               (2/eps) log2(e) max|x_ik| max|y_jk| < 2^28 (scores in log2
+ *               units that fp32 still resolves); beyond it the potentials
+ *               come out NaN and ot_solve with info returns
+ *               OT_ERR_UNSUPPORTED. OT_SPLIT_BF16 uses three bf16 parts
+ *               (24 significant bits, six products, fp32 exponent range)
+ *               and OT_NATIVE_F32 the fp32 matrix instruction. Transport
+ *               application always uses fp32 products for fp32 points, and
+ *               the Hessian-vector product the three-part bf16 split.
  */
 typedef struct ot_problem {
   const void* x;
@@ -128,7 +140,7 @@ typedef struct ot_problem {
   const float* b;
   const float* x_sqn;
   const float* y_sqn;
-  int32_t flags;  /* 0 or OT_NATIVE_F32 */
+  int32_t flags;  /* OT_NATIVE_F32, OT_SPLIT_BF16, OT_COST_AFFINE */
 } ot_problem;
 
 /* ot_solve options. Zero-initialise and set what you need. */
@@ -158,7 +170,8 @@ typedef struct ot_solve_info {
   int32_t splits_f;      /* column splits used by the f half-step */
   int32_t splits_g;      /* column splits used by the g half-step */
   int32_t operand_mode;  /* scores formed from: 0 fp32 MFMA, 1 bf16 MFMA, 2 fp32 split into
-                            three bf16 parts on the bf16 MFMA (six products per pair) */
+                            three bf16 parts on the bf16 MFMA (six products per pair),
+                            3 fp32 split into two fp16 parts on the fp16 MFMA (three) */
 } ot_solve_info;
 
 /*
@@ -227,7 +240,9 @@ int ot_update_g(const ot_problem* p, const float* f, float* g, float* err,
  *   geometric schedule is this library's reading. The tolerance check runs
  *   only in the iterations at eps.
  * Errors: as ot_update_f, plus OT_ERR_NONFINITE when info is given and the
- * final potentials are not finite.
+ * final potentials are not finite, and OT_ERR_UNSUPPORTED when info is given
+ * and fp32 points are too large for the default two-part fp16 scores (see
+ * ot_problem flags).
  */
 int ot_solve(const ot_problem* p, float* f, float* g, const ot_solve_opts* opts,
              ot_solve_info* info, void* ws, size_t* ws_bytes, void* stream);

@@ -33,6 +33,7 @@ OT_INIT_ZERO, OT_INIT_GIVEN = 0, 1
 OT_TRANSPOSE, OT_GRAD, OT_BARY = 1, 2, 4
 OT_NATIVE_F32 = 1
 OT_COST_AFFINE = 2
+OT_SPLIT_BF16 = 4
 OT_SCHED_ALTERNATING, OT_SCHED_SYMMETRIC = 0, 1
 _SCHEDULES = {"alternating": OT_SCHED_ALTERNATING, "symmetric": OT_SCHED_SYMMETRIC}
 
@@ -183,6 +184,7 @@ class Problem:
     y_sqn: torch.Tensor | None = None
     native_f32: bool = False
     affine: bool = False
+    split_bf16: bool = False
 
     def __post_init__(self):
         n, d, ldx = _rows(self.X, "X")
@@ -198,14 +200,16 @@ class Problem:
             _ptr(self.X), _ptr(self.Y), n, m, d, ldx, ldy, _dtype_code(self.X), float(self.eps),
             _ptr(_vec(self.a, "a", n, dev)), _ptr(_vec(self.b, "b", m, dev)),
             _ptr(_vec(self.x_sqn, "x_sqn", n, dev)), _ptr(_vec(self.y_sqn, "y_sqn", m, dev)),
-            (OT_NATIVE_F32 if self.native_f32 else 0) | (OT_COST_AFFINE if self.affine else 0))
+            (OT_NATIVE_F32 if self.native_f32 else 0) | (OT_COST_AFFINE if self.affine else 0)
+            | (OT_SPLIT_BF16 if self.split_bf16 else 0))
 
 
 def problem(X, Y, eps, a=None, b=None, x_sqn=None, y_sqn=None, native_f32=False,
-            affine=False) -> Problem:
-    """native_f32: form fp32 scores with fp32 MFMA instead of the three-part bf16 split.
+            affine=False, split_bf16=False) -> Problem:
+    """fp32 points form their scores from two fp16 parts per value by default;
+    native_f32 uses fp32 MFMA and split_bf16 three bf16 parts instead.
     affine: cost alpha_i + beta_j - <x_i, y_j> with alpha = x_sqn, beta = y_sqn (required)."""
-    return Problem(X, Y, eps, a, b, x_sqn, y_sqn, native_f32, affine)
+    return Problem(X, Y, eps, a, b, x_sqn, y_sqn, native_f32, affine, split_bf16)
 
 
 def _workspace(query, ws, device):

@@ -33,32 +33,40 @@ int fail(int code, const std::string& msg) {
 }
 
 
+// fp32 operand mode of a problem: two fp16 parts per value by default, three
+// bf16 parts (OT_SPLIT_BF16) or fp32 MFMA (OT_NATIVE_F32) on request.
+int f32_operand_mode(int32_t flags) {
+  if (flags & OT_NATIVE_F32) return kModeF32;
+  return (flags & OT_SPLIT_BF16) ? kModeSplit : kModeHalf2;
+}
+
 // Operand layout and pass shape for a point dimension / storage type.
-//  - fp32 points use the three-part bf16 split unless the problem asks for
-//    native fp32 (allow_split false);
+//  - fp32 points (f32_mode: kModeHalf2, kModeSplit or kModeF32) use the
+//    requested split, or fp32 operands;
 //  - d <= 128 (split or native fp32) / 256 bf16: register-resident rows; the
-//    split layout keeps one row tile per wave above d = 64 (24 KiB of row
-//    operand in registers);
+//    split layouts keep one row tile per wave above d = 64 (16 or 24 KiB of
+//    row operand in registers);
 //  - wider: the tiled pass (column blocks of ct tiles, LDS stages of bk
 //    k-blocks), with the units per tile padded to whole stages.
 // Transport application keeps its own layout (for_apply): fp32 or bf16
 // operands, chunks of 8 k-blocks when the row operand is not resident.
-KConf kernel_conf(int64_t d, int bf16, bool allow_split, bool for_apply) {
+KConf kernel_conf(int64_t d, int bf16, int f32_mode, bool for_apply) {
   KConf k{};
-  const bool split = !bf16 && allow_split && !for_apply;
+  const bool split = !bf16 && f32_mode != kModeF32 && !for_apply;
+  const int ku = !split ? 1 : (f32_mode == kModeSplit ? 3 : 2);  // units per k-block
   if (split && d <= 128) {
-    k.mode = 2;
+    k.mode = f32_mode;
     k.kbw = 16;
     k.kblocks = ceil_div(d, 16);
     int kl = 1;
     while (kl < k.kblocks) kl *= 2;
-    k.kb = 3 * kl;
+    k.kb = ku * kl;
     k.kbp = k.kb;
     k.xres = true;
-    k.lds = k.kb >= 12;
-    k.ri = k.kb <= 12 ? 2 : 1;
+    k.lds = k.kb >= 4 * ku;
+    k.ri = k.kb <= 4 * ku ? 2 : 1;
   } else {
-    k.mode = split ? 2 : (bf16 ? 1 : 0);
+    k.mode = split ? f32_mode : (bf16 ? 1 : 0);
     k.kbw = (bf16 || split) ? 16 : 8;
     k.kblocks = ceil_div(d, k.kbw);
     if (!split && k.kblocks <= 16) {
@@ -76,10 +84,9 @@ KConf kernel_conf(int64_t d, int bf16, bool allow_split, bool for_apply) {
       k.xres = false;
       k.ri = 1;
     } else {
-      const int ku = k.mode == 2 ? 3 : 1;
       k.ri = 2;
       k.ct = 4;
-      k.bk = k.mode == 2 ? 1 : 2;
+      k.bk = k.mode == kModeSplit ? 1 : 2;
       k.kb = k.bk * ku;
       k.kbp = ceil_div(k.kblocks, 2 * k.bk) * 2 * k.bk * ku;  // an even number of stages
       k.xres = false;
@@ -133,7 +140,10 @@ int check_problem(const ot_problem* p) {
   if (p->d < 1) return fail(OT_ERR_INVALID_ARG, "d must be >= 1");
   if (p->ldx < p->d || p->ldy < p->d) return fail(OT_ERR_INVALID_ARG, "ldx and ldy must be >= d");
   if (p->dtype != OT_F32 && p->dtype != OT_BF16) return fail(OT_ERR_UNSUPPORTED, "dtype must be OT_F32 or OT_BF16");
-  if (p->flags & ~(OT_NATIVE_F32 | OT_COST_AFFINE)) return fail(OT_ERR_INVALID_ARG, "unknown problem flag");
+  if (p->flags & ~(OT_NATIVE_F32 | OT_COST_AFFINE | OT_SPLIT_BF16))
+    return fail(OT_ERR_INVALID_ARG, "unknown problem flag");
+  if ((p->flags & OT_NATIVE_F32) && (p->flags & OT_SPLIT_BF16))
+    return fail(OT_ERR_INVALID_ARG, "OT_NATIVE_F32 and OT_SPLIT_BF16 are exclusive");
   if ((p->flags & OT_COST_AFFINE) && (!p->x_sqn || !p->y_sqn))
     return fail(OT_ERR_INVALID_ARG, "OT_COST_AFFINE needs x_sqn (alpha) and y_sqn (beta)");
   if (p->d > OT_MAX_D) return fail(OT_ERR_UNSUPPORTED, "d exceeds OT_MAX_D");
@@ -174,14 +184,14 @@ struct SolveWs {
   int ntiles, mtiles, npad, mpad;
   PassShape F, G;
   size_t o_xp, o_yp, o_nx, o_ny, o_wx, o_hx, o_bx, o_wy, o_hy, o_by, o_part, o_part2, o_errp,
-      o_errv;
+      o_errv, o_plan;
   int errblocks_f, errblocks_g;
   size_t total;
 };
 
 SolveWs solve_layout(const ot_problem* p, int splits_f, int splits_g) {
   SolveWs w{};
-  w.k = kernel_conf(p->d, p->dtype == OT_BF16, (p->flags & OT_NATIVE_F32) == 0);
+  w.k = kernel_conf(p->d, p->dtype == OT_BF16, f32_operand_mode(p->flags));
   w.ntiles = ceil_div(p->n, kTile);
   w.mtiles = ceil_div(p->m, kTile);
   w.npad = w.ntiles * kTile;
@@ -211,6 +221,7 @@ SolveWs solve_layout(const ot_problem* p, int splits_f, int splits_g) {
   w.o_part2 = take(pg * 8);  // g partials of the symmetric schedule (both passes in flight)
   w.o_errp = take((size_t)(w.errblocks_f + w.errblocks_g) * 4);
   w.o_errv = take(64);
+  w.o_plan = take(sizeof(Half2Plan));
   w.total = o;
   return w;
 }
@@ -232,6 +243,7 @@ struct Ctx {
   float2* part2;
   bool sym;  // symmetric (averaged) schedule
   void *xp, *yp;
+  Half2Plan* plan;  // range plan of the half2 operand mode
   float *f, *g;
 };
 
@@ -267,6 +279,7 @@ Ctx make_ctx(const ot_problem* p, const SolveWs& L, void* ws, float* f, float* g
   x.part2 = (float2*)(x.ws + L.o_part2);
   x.errp = (float*)(x.ws + L.o_errp);
   x.errv = (float*)(x.ws + L.o_errv);
+  x.plan = (Half2Plan*)(x.ws + L.o_plan);
   x.f = f;
   x.g = g;
   return x;
@@ -277,7 +290,10 @@ Ctx make_ctx(const ot_problem* p, const SolveWs& L, void* ws, float* f, float* g
 int prepare_eps(const Ctx& x, hipStream_t st) {
   const ot_problem* p = x.p;
   const int bf = p->dtype == OT_BF16;
-  if (x.L.k.mode == 2)
+  if (x.L.k.mode == kModeHalf2)
+    OT_HIP(launch_pack_half2((const float*)p->x, p->n, p->d, p->ldx, x.L.ntiles, x.L.k.kbp, x.xscale,
+                             x.plan, 0, x.xp, st));
+  else if (x.L.k.mode == kModeSplit)
     OT_HIP(launch_pack_split((const float*)p->x, p->n, p->d, p->ldx, x.L.ntiles, x.L.k.kbp, x.xscale,
                              x.xp, st));
   else
@@ -293,7 +309,13 @@ int prepare(const Ctx& x, hipStream_t st) {
   const int bf = p->dtype == OT_BF16;
   if (!p->x_sqn) OT_HIP(launch_sqnorms(p->x, bf, p->n, p->d, p->ldx, (float*)x.nx, st));
   if (!p->y_sqn) OT_HIP(launch_sqnorms(p->y, bf, p->m, p->d, p->ldy, (float*)x.ny, st));
-  if (x.L.k.mode == 2)
+  if (x.L.k.mode == kModeHalf2) {
+    // the range plan is taken at the problem's eps, the largest X scale of the call
+    OT_HIP(launch_half2_plan((const float*)p->x, p->n, p->ldx, (const float*)p->y, p->m, p->ldy, p->d,
+                             x.xscale, x.plan, st));
+    OT_HIP(launch_pack_half2((const float*)p->y, p->m, p->d, p->ldy, x.L.mtiles, x.L.k.kbp, 1.f,
+                             x.plan, 1, x.yp, st));
+  } else if (x.L.k.mode == kModeSplit)
     OT_HIP(launch_pack_split((const float*)p->y, p->m, p->d, p->ldy, x.L.mtiles, x.L.k.kbp, 1.f, x.yp,
                              st));
   else
@@ -559,7 +581,7 @@ struct ApplyWs {
 
 ApplyWs apply_layout(const ot_problem* p, int64_t cols, bool transpose) {
   ApplyWs w{};
-  w.k = kernel_conf(p->d, p->dtype == OT_BF16, false, true);
+  w.k = kernel_conf(p->d, p->dtype == OT_BF16, kModeF32, true);
   const int64_t rows = transpose ? p->m : p->n;
   const int64_t strm = transpose ? p->n : p->m;
   w.rtiles = ceil_div(rows, kTile);
@@ -711,7 +733,10 @@ int ot_solve(const ot_problem* p, float* f, float* g, const ot_solve_opts* o,
       OT_HIP(launch_err_reduce(x.errp + L.errblocks_f, L.errblocks_g, x.errv + 1, st));
       OT_HIP(launch_nonfinite(f, (int)p->n, g, (int)p->m, x.errv + 2, st));
       float h[3] = {0.f, 0.f, 0.f};
+      int in_range = 1;
       OT_HIP(hipMemcpyAsync(h, x.errv, sizeof(h), hipMemcpyDeviceToHost, st));
+      if (L.k.mode == kModeHalf2)
+        OT_HIP(hipMemcpyAsync(&in_range, &x.plan->ok, sizeof(int), hipMemcpyDeviceToHost, st));
       OT_HIP(hipStreamSynchronize(st));
       info->iters_done = done;
       info->marg_err_row = h[0];
@@ -722,6 +747,10 @@ int ot_solve(const ot_problem* p, float* f, float* g, const ot_solve_opts* o,
       info->splits_f = L.F.splits;
       info->splits_g = L.G.splits;
       info->operand_mode = L.k.mode;
+      if (!in_range)
+        return fail(OT_ERR_UNSUPPORTED,
+                    "fp32 coordinates too large for the two-part fp16 scores "
+                    "((2/eps) log2(e) max|x| max|y| >= 2^28); OT_SPLIT_BF16 covers the fp32 range");
       if (info->nonfinite) return fail(OT_ERR_NONFINITE, "potentials are not finite");
     }
     return OT_OK;

@@ -357,6 +357,81 @@ __global__ __launch_bounds__(256) void pack_split_kernel(const float* __restrict
   }
 }
 
+// ---------------------------------------------------------------------------
+// Two fp16 parts per fp32 value (half2 operand mode). A value v is written
+// as hi = fp16(v) and lo = fp16(v - hi) (round to nearest even; v - hi is
+// exact in fp32), so v - hi - lo is below 2^-22 |v| while v is inside the
+// fp16 range. The X cloud is scaled by 2^a and the Y cloud by 2^-a, both
+// exact, so every product -- and the score -- is unchanged; a balances the
+// two clouds' largest magnitudes below 2^15 (fp16 holds up to 65504). When
+// no a does, the plan is marked out of range and X is written as NaN, so
+// the potentials come out non-finite rather than wrong.
+// ---------------------------------------------------------------------------
+// Largest |value| of a row-major cloud, as the bits of a non-negative float:
+// a NaN coordinate compares above every finite value and infinity.
+__global__ __launch_bounds__(256) void absmax_kernel(const float* __restrict__ src, int64_t rows,
+                                                     int64_t d, int64_t ld,
+                                                     unsigned* __restrict__ out) {
+  unsigned mx = 0;
+  for (int64_t i = blockIdx.x; i < rows; i += gridDim.x)
+    for (int64_t k = threadIdx.x; k < d; k += 256)
+      mx = max(mx, __float_as_uint(src[i * ld + k]) & 0x7fffffffu);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = max(mx, (unsigned)__shfl_xor((int)mx, o));
+  if ((threadIdx.x & 63) == 0) atomicMax(out, mx);
+}
+
+// cx: the factor X is packed with (score scale at the problem's eps; a
+// smaller eps-scaling factor only lowers |X|).
+__global__ void half2_plan_kernel(Half2Plan* __restrict__ p, float cx) {
+  const float mx = __uint_as_float(p->amax[0]) * cx;
+  const float my = __uint_as_float(p->amax[1]);
+  int ex = 0, ey = 0;  // m < 2^e
+  if (mx > 0.f) (void)frexpf(mx, &ex);
+  if (my > 0.f) (void)frexpf(my, &ey);
+  int a = (ey - ex) >> 1;  // floor: X' < 2^(ex + a), Y' < 2^(ey - a)
+  a = a < -100 ? -100 : (a > 100 ? 100 : a);
+  p->xmul = ldexpf(1.f, a);
+  p->ymul = ldexpf(1.f, -a);
+  p->ok = (isfinite(mx) && isfinite(my) && ex + a <= 15 && ey - a <= 15) ? 1 : 0;
+}
+
+// Layout of pack_split with two units per k-block: units (2 kb, 2 kb + 1) of
+// a tile hold hi and lo of k-block kb. side 0 packs X (times scale * xmul),
+// side 1 packs Y (times scale * ymul).
+__global__ __launch_bounds__(256) void pack_half2_kernel(const float* __restrict__ src,
+                                                         int64_t rows, int64_t d, int64_t ld,
+                                                         int64_t total, int units, float scale,
+                                                         const Half2Plan* __restrict__ plan,
+                                                         int side, u32x4* __restrict__ dst) {
+  const float mul = scale * (side ? plan->ymul : plan->xmul);
+  const bool poison = side == 0 && plan->ok == 0;
+  for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * 256) {
+    const int lane = (int)(idx & 63);
+    const int64_t tu = idx >> 6;
+    const int u = (int)(tu % units);
+    const int64_t t = tu / units;
+    const int kb = u >> 1, part = u & 1;
+    const int64_t row = t * kTile + (lane & 31);
+    const int64_t k0 = (int64_t)kb * 16 + (lane >> 5) * 8;
+    uint32_t h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float v = (row < rows && k0 + e < d) ? src[row * ld + k0 + e] * mul : 0.f;
+      const _Float16 hi = (_Float16)v;
+      const _Float16 q = part ? (_Float16)(v - (float)hi) : hi;
+      h[e] = poison ? 0x7e00u : (uint32_t)__builtin_bit_cast(uint16_t, q);
+    }
+    u32x4 o;
+    o.x = h[0] | (h[1] << 16);
+    o.y = h[2] | (h[3] << 16);
+    o.z = h[4] | (h[5] << 16);
+    o.w = h[6] | (h[7] << 16);
+    dst[idx] = o;
+  }
+}
+
 // Packs V (rows streamed x cols) as the A operand of O^T += V^T P^T: for
 // column tile t, column block pb (32 values of p), quad q and lane l the four
 // floats are V[32t + 8q + 4(l/32) + e][32pb + l%32], e = 0..3 -- the row order
@@ -451,6 +526,24 @@ hipError_t launch_pack_split(const float* src, int64_t rows, int64_t d, int64_t 
   const int64_t total = (int64_t)rtiles * units * 64;
   pack_split_kernel<<<grid_for(total, 256, 65536), 256, 0, st>>>(src, rows, d, ld, total, units,
                                                                  scale, (u32x4*)dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_half2_plan(const float* X, int64_t n, int64_t ldx, const float* Y, int64_t m,
+                             int64_t ldy, int64_t d, float cx, Half2Plan* plan, hipStream_t st) {
+  fill_kernel<<<1, 256, 0, st>>>((float*)plan->amax, 0.f, 2);
+  absmax_kernel<<<(int)(n < 4096 ? n : 4096), 256, 0, st>>>(X, n, d, ldx, &plan->amax[0]);
+  absmax_kernel<<<(int)(m < 4096 ? m : 4096), 256, 0, st>>>(Y, m, d, ldy, &plan->amax[1]);
+  half2_plan_kernel<<<1, 1, 0, st>>>(plan, cx);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_half2(const float* src, int64_t rows, int64_t d, int64_t ld, int rtiles,
+                             int units, float scale, const Half2Plan* plan, int side, void* dst,
+                             hipStream_t st) {
+  const int64_t total = (int64_t)rtiles * units * 64;
+  pack_half2_kernel<<<grid_for(total, 256, 65536), 256, 0, st>>>(src, rows, d, ld, total, units,
+                                                                 scale, plan, side, (u32x4*)dst);
   return hipGetLastError();
 }
 

@@ -13,6 +13,7 @@ namespace flashot {
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // One packed k-block of the score tile: acc[j][i] += sum_k A[j][k] B[k][i].
@@ -34,10 +35,14 @@ __device__ __forceinline__ f32x16 mfma_kblock(u32x4 a, u32x4 b, f32x16 acc) {
   }
 }
 
-// Operand modes of the register-resident pass.
-constexpr int kModeF32 = 0;    // fp32 operands, fp32 MFMA (32x32x2)
-constexpr int kModeBF16 = 1;   // bf16 operands, bf16 MFMA (32x32x16)
-constexpr int kModeSplit = 2;  // fp32 operands as hi + mid + lo bf16 parts, bf16 MFMA
+// 1 KiB operand units per k-block, and matrix instructions per tile of KB units.
+template <int MODE>
+constexpr int units_per_kblock() { return MODE == kModeSplit ? 3 : (MODE == kModeHalf2 ? 2 : 1); }
+template <int MODE, int KB>
+constexpr int tile_mfmas() {
+  return MODE == kModeF32 ? 4 * KB
+                          : (MODE == kModeSplit ? 2 * KB : (MODE == kModeHalf2 ? 3 * KB / 2 : KB));
+}
 
 // One k-block of 16 fp32 values held as three bf16 parts per operand
 // (v = hi + mid + lo, each part the bf16 rounding of what the previous ones
@@ -54,6 +59,21 @@ __device__ __forceinline__ f32x16 mfma_split(const u32x4* y, const u32x4* x, f32
   acc = m(y[1], x[1], acc);  // mid * mid
   acc = m(y[1], x[0], acc);  // mid * hi
   acc = m(y[0], x[1], acc);  // hi * mid
+  return m(y[0], x[0], acc); // hi * hi
+}
+
+// One k-block of 16 fp32 values held as two fp16 parts per operand (v = hi +
+// lo, lo the fp16 rounding of v - hi, so v - hi - lo is below 2^-22 |v|;
+// the values are pre-scaled by powers of two into the fp16 range). Three
+// partial products are accumulated, smallest first; the dropped lo * lo and
+// the two residuals are each below 2^-22 of |x y|.
+__device__ __forceinline__ f32x16 mfma_half2(const u32x4* y, const u32x4* x, f32x16 acc) {
+  auto m = [](u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  };
+  acc = m(y[1], x[0], acc);  // lo * hi
+  acc = m(y[0], x[1], acc);  // hi * lo
   return m(y[0], x[0], acc); // hi * hi
 }
 
@@ -92,7 +112,9 @@ __device__ __forceinline__ float max16(const f32x16& v) {
 //
 // Units: for fp32 inputs the row operand X is packed pre-multiplied by
 // c = 2 log2(e) / eps and the biases are written in the same units, so scores
-// are log2 values and exp2 needs no multiply (KS = 1). bf16 operands cannot be
+// are log2 values and exp2 needs no multiply (KS = 1). In half2 mode X is
+// further multiplied by 2^a and Y by 2^-a (exact), which leaves the product
+// unchanged. bf16 operands cannot be
 // rescaled without rounding, so their scores stay in dot-product units and
 // are multiplied by c before exp2 (KS = c). Partials are written in log2
 // units: LSE_row = ln 2 * (M2 + log2 S).
@@ -100,7 +122,7 @@ __device__ __forceinline__ float max16(const f32x16& v) {
 constexpr float kUnset = -1.0e30f;  // stabiliser not yet taken from data
 
 // KB counts 1 KiB operand units per tile: one per k-block for fp32 / bf16,
-// three (hi, mid, lo) per k-block in split mode.
+// three (hi, mid, lo) per k-block in split mode, two (hi, lo) in half2 mode.
 template <int MODE, int KB, int RI>
 __device__ __forceinline__ void score_tile(const u32x4 (&y)[KB], const u32x4 (&xr)[RI][KB],
                                            float wv, int h, const float (&Mf)[RI],
@@ -112,6 +134,11 @@ __device__ __forceinline__ void score_tile(const u32x4 (&y)[KB], const u32x4 (&x
     for (int kb = 0; kb < KB; kb += 3)
 #pragma unroll
       for (int ri = 0; ri < RI; ++ri) acc[ri] = mfma_split(&y[kb], &xr[ri][kb], acc[ri]);
+  } else if constexpr (MODE == kModeHalf2) {
+#pragma unroll
+    for (int kb = 0; kb < KB; kb += 2)
+#pragma unroll
+      for (int ri = 0; ri < RI; ++ri) acc[ri] = mfma_half2(&y[kb], &xr[ri][kb], acc[ri]);
   } else {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)

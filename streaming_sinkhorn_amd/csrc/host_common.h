@@ -33,10 +33,10 @@ inline int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
 // Kernel configuration for a point dimension / storage type.
 struct KConf {
-  int mode;     // 0 fp32 operands, 1 bf16, 2 fp32 split into three bf16 parts
+  int mode;     // 0 fp32 operands, 1 bf16, 2 fp32 as three bf16 parts, 3 as two fp16 parts
   int kbw;      // dimension values per k-block (8 fp32, 16 bf16 / split)
   int kblocks;  // k-blocks needed to cover d
-  int kb;       // 1 KiB operand units per tile held in registers (3 per k-block in split mode)
+  int kb;       // 1 KiB operand units per tile held in registers (3 / 2 per k-block when split)
   int kbp;      // padded operand units per tile
   bool xres;    // row operand resident in registers
   bool lds;     // column tiles shared by the workgroup's waves through LDS
@@ -44,7 +44,8 @@ struct KConf {
   int ct, bk;   // tiled wide pass: column tiles per block, k-blocks per LDS stage
 };
 
-KConf kernel_conf(int64_t d, int bf16, bool allow_split, bool for_apply = false);
+int f32_operand_mode(int32_t flags);
+KConf kernel_conf(int64_t d, int bf16, int f32_mode, bool for_apply = false);
 PassShape make_pass(int rtiles, int ctiles, const KConf& k, int ri, int forced, int max_splits);
 int check_problem(const ot_problem* p);
 // ws == NULL: writes need to *ws_bytes and sets *query; otherwise checks size

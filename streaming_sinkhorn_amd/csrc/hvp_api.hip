@@ -48,7 +48,7 @@ template <typename Take>
 TransportWs transport_layout(const ot_problem* p, int64_t cols_f, int64_t cols_t, bool with_a,
                              Take&& take) {
   TransportWs w{};
-  w.k = kernel_conf(p->d, 0, false, true);
+  w.k = kernel_conf(p->d, 0, kModeF32, true);
   w.ntiles = ceil_div(p->n, kTile);
   w.mtiles = ceil_div(p->m, kTile);
   w.npad = w.ntiles * kTile;
@@ -224,7 +224,7 @@ HvpWs hvp_layout(const ot_problem* p) {
   w.o_part = take((size_t)kCgMaxParts * 4);
   w.o_cs = take(sizeof(CgState));
   VecWs& v = w.V;
-  v.k = kernel_conf(p->d, 0, (p->flags & OT_NATIVE_F32) == 0);
+  v.k = kernel_conf(p->d, 0, (p->flags & OT_NATIVE_F32) ? kModeF32 : kModeSplit);
   v.on = v.k.xres;
   if (v.on) {
     const int nt = w.T.ntiles, mt = w.T.mtiles;

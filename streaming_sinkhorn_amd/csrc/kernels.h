@@ -18,6 +18,12 @@ constexpr int kTile = 32;
 constexpr int kWaves = 4;  // waves per workgroup of the streamed kernels
 constexpr float kSentinel = -1.0e20f;  // bias of padded columns: exp underflows to 0
 
+// Operand modes of the streamed passes.
+constexpr int kModeF32 = 0;    // fp32 operands, fp32 MFMA (32x32x2)
+constexpr int kModeBF16 = 1;   // bf16 operands, bf16 MFMA (32x32x16)
+constexpr int kModeSplit = 2;  // fp32 operands as hi + mid + lo bf16 parts, bf16 MFMA
+constexpr int kModeHalf2 = 3;  // fp32 operands as hi + lo fp16 parts, fp16 MFMA
+
 // Shape of one streamed pass: "rows" are the outputs (one LSE per row) and
 // "cols" are streamed. For the f half-step rows = x, cols = y.
 struct PassShape {
@@ -41,6 +47,24 @@ hipError_t launch_pack_points(const void* src, int bf16, int64_t rows, int64_t d
 // parts of k-block kb in the lane layout of a bf16 k-block.
 hipError_t launch_pack_split(const float* src, int64_t rows, int64_t d, int64_t ld, int rtiles,
                              int units, float scale, void* dst, hipStream_t st);
+// Range plan of the half2 operand mode (two fp16 parts per fp32 value):
+// the largest |x| and |y| (float bits), the exact factors 2^a, 2^-a applied
+// to X and Y, and whether both clouds fit fp16 with them.
+struct Half2Plan {
+  unsigned amax[2];
+  float xmul, ymul;
+  int ok;
+  int pad[3];
+};
+// Computes the plan from X, Y (fp32) and the factor cx that X is packed with.
+hipError_t launch_half2_plan(const float* X, int64_t n, int64_t ldx, const float* Y, int64_t m,
+                             int64_t ldy, int64_t d, float cx, Half2Plan* plan, hipStream_t st);
+// Packs fp32 points times scale * (side ? ymul : xmul) as hi, lo fp16 parts:
+// units (2 kb, 2 kb + 1) of a tile hold k-block kb in the lane layout of a
+// bf16 k-block. X (side 0) is written as NaN when the plan is out of range.
+hipError_t launch_pack_half2(const float* src, int64_t rows, int64_t d, int64_t ld, int rtiles,
+                             int units, float scale, const Half2Plan* plan, int side, void* dst,
+                             hipStream_t st);
 hipError_t launch_pack_values(const void* V, int bf16, int64_t rows, int64_t cols, int64_t ldv,
                               int ctiles, int pblocks, float* dst, hipStream_t st);
 hipError_t launch_weights(const float* w, int rows, int rpad, float eps, float* wgt, float* hlw,
@@ -48,7 +72,8 @@ hipError_t launch_weights(const float* w, int rows, int rpad, float eps, float* 
 hipError_t launch_fill(float* p, float v, int64_t count, hipStream_t st);
 hipError_t launch_bias_from_pot(const float* pot, const float* norm, const float* hlw, int rows,
                                 int rpad, float bscale, float* bias, hipStream_t st);
-// mode: 0 fp32 operands, 1 bf16 operands, 2 fp32 operands packed as three bf16 parts.
+// mode: 0 fp32 operands, 1 bf16 operands, 2 fp32 operands packed as three bf16 parts,
+// 3 fp32 operands packed as two fp16 parts.
 // Register-resident passes (s.xres, kernels.hip) and k-chunked wide passes (kernels_wide.hip).
 hipError_t launch_lse_resident(const PassShape& s, int mode, const void* Rp, const void* Cp,
                                const float* cbias, float c, float2* part, hipStream_t st);

@@ -18,8 +18,9 @@
 //  * one extra fp32 MFMA adds the per-column bias and subtracts the row's
 //    running stabiliser (A = [bias_j, 1], B = [1, -M_i]), so the common-case
 //    score costs one exp2 and one add on the vector unit;
-//  * fp32 points are formed on the bf16 matrix cores as an exact three-part
-//    split (device_common.h), bf16 points directly, or fp32 on request;
+//  * fp32 points are formed on the fp16 matrix cores from two fp16 parts per
+//    value (device_common.h), on request on the bf16 matrix cores from three
+//    bf16 parts or with fp32 MFMA; bf16 points directly;
 //  * operands are pre-packed once per call into the exact register layout of
 //    the MFMA (16 contiguous bytes per lane, zero-padded tiles), so every
 //    load in the hot loop is a full 1 KiB coalesced wave load with no masks;
@@ -54,8 +55,7 @@ __device__ __forceinline__ void load_ctile(const u32x4* __restrict__ Cp,
 // column buffer the matrix instructions have just read.
 template <int MODE, int KB, int RI>
 __device__ __forceinline__ void stage_schedule() {
-  constexpr int kPerUnit = MODE == kModeF32 ? 4 : (MODE == kModeBF16 ? 1 : 2);
-  constexpr int kMfma = RI * (KB * kPerUnit + 1);
+  constexpr int kMfma = RI * (tile_mfmas<MODE, KB>() + 1);
   constexpr int kValu = RI * (MODE == kModeBF16 ? 40 : 24);  // common-case LSE of RI tiles
   constexpr int kValuPer = (kValu + kMfma - 1) / kMfma;
 #pragma unroll
@@ -263,6 +263,15 @@ __device__ __forceinline__ void score_tile_lds(const u32x4* __restrict__ buf, in
 #pragma unroll
       for (int ri = 0; ri < RI; ++ri) acc[ri] = mfma_split(y, &xr[ri][kb], acc[ri]);
     }
+  } else if constexpr (MODE == kModeHalf2) {
+#pragma unroll
+    for (int kb = 0; kb < KB; kb += 2) {
+      u32x4 y[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) y[q] = buf[(kb + q) * 64 + lane];
+#pragma unroll
+      for (int ri = 0; ri < RI; ++ri) acc[ri] = mfma_half2(y, &xr[ri][kb], acc[ri]);
+    }
   } else {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
@@ -280,8 +289,7 @@ __device__ __forceinline__ void score_tile_lds(const u32x4* __restrict__ buf, in
 
 template <int MODE, int KB, int RI>
 __device__ __forceinline__ void stage_schedule_lds() {
-  constexpr int kPerUnit = MODE == kModeF32 ? 4 : (MODE == kModeBF16 ? 1 : 2);
-  constexpr int kMfma = RI * (KB * kPerUnit + 1);
+  constexpr int kMfma = RI * (tile_mfmas<MODE, KB>() + 1);
   constexpr int kValu = RI * (MODE == kModeBF16 ? 40 : 24);
   constexpr int kValuPer = (kValu + kMfma - 1) / kMfma;
   constexpr int kLoads = stage_loads<KB>();
@@ -465,6 +473,20 @@ static hipError_t lse_split_dispatch(const PassShape& s, const ResArgs& a, hipSt
   return hipGetLastError();
 }
 
+// Two fp16 parts per k-block: 2, 4, 8 units for d <= 64 (two row tiles per
+// wave, columns through LDS from 8 units), 16 for 64 < d <= 128.
+template <bool VEC>
+static hipError_t lse_half2_dispatch(const PassShape& s, const ResArgs& a, hipStream_t st) {
+  switch (s.kb) {
+    case 2: resident_go<kModeHalf2, 2, VEC>(s, a, st); break;
+    case 4: resident_go<kModeHalf2, 4, VEC>(s, a, st); break;
+    case 8: resident_go<kModeHalf2, 8, VEC>(s, a, st); break;
+    case 16: resident_go<kModeHalf2, 16, VEC>(s, a, st); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <int MODE, bool VEC>
 static hipError_t lse_resident_dispatch(const PassShape& s, const ResArgs& a, hipStream_t st) {
   switch (s.kb) {
@@ -483,6 +505,7 @@ static hipError_t resident_dispatch(const PassShape& s, int mode, const ResArgs&
                                     hipStream_t st) {
   if (!s.xres) return hipErrorInvalidValue;
   if (mode == kModeSplit) return lse_split_dispatch<VEC>(s, a, st);
+  if (mode == kModeHalf2) return lse_half2_dispatch<VEC>(s, a, st);
   if (mode == kModeBF16) return lse_resident_dispatch<kModeBF16, VEC>(s, a, st);
   return lse_resident_dispatch<kModeF32, VEC>(s, a, st);
 }

@@ -27,10 +27,11 @@ namespace flashot {
 // bias_j - M_i and the online LSE (lazy stabiliser, device_common.h)
 // consumes the RT x CT tiles.
 // Units: 1 KiB operand units of the packed layout; KU units per k-block
-// (3 in split mode), kbp units per tile, padded to whole stages.
+// (3 in split mode, 2 in half2 mode), kbp units per tile, padded to whole
+// stages.
 // ---------------------------------------------------------------------------
 template <int MODE>
-constexpr int wide_ku() { return MODE == kModeSplit ? 3 : 1; }
+constexpr int wide_ku() { return units_per_kblock<MODE>(); }
 
 template <int MODE, int CT, int BK>
 constexpr int wide_stage_elems() { return CT * BK * wide_ku<MODE>() * 64; }
@@ -140,6 +141,8 @@ __global__ __launch_bounds__(256) void lse_wide_kernel(
         for (int q = 0; q < CT; ++q) {
           if constexpr (MODE == kModeSplit)
             acc[r][q] = mfma_split(yf[q], &x[r][kb * KU], acc[r][q]);
+          else if constexpr (MODE == kModeHalf2)
+            acc[r][q] = mfma_half2(yf[q], &x[r][kb * KU], acc[r][q]);
           else
             acc[r][q] = mfma_kblock<MODE == kModeBF16>(yf[q][0], x[r][kb], acc[r][q]);
         }
@@ -222,6 +225,8 @@ hipError_t launch_lse_wide(const PassShape& s, int mode, const void* Rp, const v
   // Shapes measured best on gfx950 among RT in {2, 4}, CT in {2, 4},
   // BK in {1, 2, 4} (larger ones exceed 256 VGPRs or starve LDS / L2).
   WIDE_CASE(kModeSplit, 2, 4, 1)
+  WIDE_CASE(kModeHalf2, 2, 4, 1)
+  WIDE_CASE(kModeHalf2, 2, 4, 2)
   WIDE_CASE(kModeBF16, 2, 4, 2)
   WIDE_CASE(kModeF32, 2, 4, 2)
 #undef WIDE_CASE

@@ -27,14 +27,20 @@ def host64(t):
     return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
 
 
-def make_problem(data, eps=None, dtype=None, weights=True, native_f32=False):
+# fp32 operand modes of the log-sum-exp passes: the default two-part fp16
+# split, the three-part bf16 split, the fp32 matrix instruction
+F32_MODES = ("half2", "split_bf16", "native")
+
+
+def make_problem(data, eps=None, dtype=None, weights=True, native_f32=False, mode="half2"):
     w = data["w"]
     dtype = dtype or w.dtype
     X = dev(data["X"], dtype)
     Y = dev(data["Y"], dtype)
     a = dev(data["a"]) if weights else None
     b = dev(data["b"]) if weights else None
-    prob = ssa.problem(X, Y, float(w.eps if eps is None else eps), a, b, native_f32=native_f32)
+    prob = ssa.problem(X, Y, float(w.eps if eps is None else eps), a, b,
+                       native_f32=native_f32 or mode == "native", split_bf16=mode == "split_bf16")
     return prob
 
 

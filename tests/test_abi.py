@@ -69,8 +69,9 @@ def test_workspace_query_is_host_only_and_monotone():
     ("d", 100000, ssa.OT_ERR_UNSUPPORTED),
     ("x", 0, ssa.OT_ERR_INVALID_ARG),
     ("x", (1 << 20) + 2, ssa.OT_ERR_INVALID_ARG),   # fp32 data must be 4-byte aligned
-    ("flags", 4, ssa.OT_ERR_INVALID_ARG),            # unknown problem flag
+    ("flags", 8, ssa.OT_ERR_INVALID_ARG),            # unknown problem flag
     ("flags", ssa.OT_COST_AFFINE, ssa.OT_ERR_INVALID_ARG),  # affine cost without alpha, beta
+    ("flags", ssa.OT_NATIVE_F32 | ssa.OT_SPLIT_BF16, ssa.OT_ERR_INVALID_ARG),  # exclusive modes
 ])
 def test_problem_validation(field, value, code):
     L = ssa.lib()
@@ -84,16 +85,23 @@ def test_problem_validation(field, value, code):
     assert L.ot_last_error()
 
 
-def test_split_and_native_workspaces_differ():
-    """fp32 points pack three bf16 parts per k-block (here d = 64: 3 KiB per 16
-    values and 32 rows) unless OT_NATIVE_F32 asks for fp32 operands (2 KiB)."""
+def test_operand_mode_workspaces_differ():
+    """fp32 points pack two fp16 parts per k-block by default (here d = 64:
+    2 KiB per 16 values and 32 rows, as much as fp32 operands under
+    OT_NATIVE_F32), three bf16 parts (3 KiB) under OT_SPLIT_BF16."""
     L = ssa.lib()
     p = _problem(1024, 1024, 64)
-    _, split = _size(L.ot_update_f, ctypes.byref(p), None, None, None)
+    _, half2 = _size(L.ot_update_f, ctypes.byref(p), None, None, None)
     p.flags = ssa.OT_NATIVE_F32
     _, native = _size(L.ot_update_f, ctypes.byref(p), None, None, None)
+    p.flags = ssa.OT_SPLIT_BF16
+    _, split = _size(L.ot_update_f, ctypes.byref(p), None, None, None)
     tiles = 1024 // 32
+    assert half2 == native
     assert split - native == 2 * tiles * (3 * 4 - 8) * 1024
+    p.flags = ssa.OT_SPLIT_BF16 | ssa.OT_NATIVE_F32
+    rc, _ = _size(L.ot_update_f, ctypes.byref(p), None, None, None)
+    assert rc == ssa.OT_ERR_INVALID_ARG and b"exclusive" in L.ot_last_error()
 
 
 def test_null_problem_and_null_sizes():

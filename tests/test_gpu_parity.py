@@ -17,7 +17,7 @@ import torch
 import oracle
 import streaming_sinkhorn_amd as ssa
 import workloads
-from gpu_util import DEV, host64, make_problem, oracle_inputs, say, zeros
+from gpu_util import DEV, F32_MODES, host64, make_problem, oracle_inputs, say, zeros
 
 pytestmark = pytest.mark.gpu
 
@@ -74,20 +74,17 @@ HALF_CASES = [
 ]
 
 
-# fp32 with the fp32 matrix instruction: resident (d <= 128, LDS-shared
+# fp32 cases run in every fp32 operand mode: resident (d <= 128, LDS-shared
 # columns from d = 64) and the tiled wide pass (d > 128)
-NATIVE_HALF_CASES = [c for c in HALF_CASES if c[3] == "f32"]
-
-
-@pytest.mark.parametrize("native", [False, True])
+@pytest.mark.parametrize("mode", F32_MODES)
 @pytest.mark.parametrize("n,m,d,dtype,eps", HALF_CASES)
-def test_half_steps_teacher_forced(n, m, d, dtype, eps, native):
-    if native and (n, m, d, dtype, eps) not in NATIVE_HALF_CASES:
-        pytest.skip("the fp32 matrix-instruction option only applies to fp32 points")
-    say(f"half-steps n={n} m={m} d={d} dtype={dtype} eps={eps} native_f32={native}")
+def test_half_steps_teacher_forced(n, m, d, dtype, eps, mode):
+    if mode != "half2" and dtype != "f32":
+        pytest.skip("the fp32 operand options only apply to fp32 points")
+    say(f"half-steps n={n} m={m} d={d} dtype={dtype} eps={eps} mode={mode}")
     base = "c3_d16_bf16" if dtype == "bf16" else "c3_d16_f32"
     data = workloads.make(base, n=n, m=m, d=d)
-    prob = make_problem(data, eps=eps, native_f32=native)
+    prob = make_problem(data, eps=eps, mode=mode)
     X, Y, a, b = oracle_inputs(prob)
     C = oracle.cost_matrix(X, Y)
     rng = np.random.default_rng(n * 7 + m)
@@ -140,24 +137,27 @@ TRAJ_CASES = [
 
 
 TRAJ_CASES += [
-    # the same fp32 workloads formed with the fp32 matrix instruction
-    ("c1", None, None, None, None, True),
-    ("c2", 700, 555, None, None, True),
-    ("c3_d16_f32", 500, 650, None, None, True),
-    ("c3_d128_f32", 500, 650, None, None, True),
-    ("c3_d512_f32", 300, 420, None, None, True),
+    # the same fp32 workloads formed with the fp32 matrix instruction and
+    # with the three-part bf16 split
+    (*c, mode) for mode in ("native", "split_bf16") for c in [
+        ("c1", None, None, None, None),
+        ("c2", 700, 555, None, None),
+        ("c3_d16_f32", 500, 650, None, None),
+        ("c3_d128_f32", 500, 650, None, None),
+        ("c3_d512_f32", 300, 420, None, None),
+    ]
 ]
 
 
 @pytest.mark.parametrize("case", TRAJ_CASES, ids=lambda c: "-".join(str(v) for v in c if v is not None))
 def test_solve_trajectory(case):
     name, n, m, d, iters = case[:5]
-    native = len(case) > 5 and case[5]
+    mode = case[5] if len(case) > 5 else "half2"
     data = workloads.make(name, n=n, m=m, d=d)
     w = data["w"]
     T = w.iters if iters is None else iters
-    say(f"trajectory {name} n={w.n} m={w.m} d={w.d} dtype={w.dtype} eps={w.eps} T={T} native_f32={native}")
-    prob = make_problem(data, native_f32=native)
+    say(f"trajectory {name} n={w.n} m={w.m} d={w.d} dtype={w.dtype} eps={w.eps} T={T} mode={mode}")
+    prob = make_problem(data, mode=mode)
     X, Y, a, b = oracle_inputs(prob)
     f = zeros(w.n)
     g = zeros(w.m)
@@ -371,6 +371,51 @@ def test_nonfinite_reported():
     with pytest.raises(ssa.OtError) as ei:
         ssa.ot_solve(prob, f, g, 3)
     assert ei.value.code == ssa.OT_ERR_NONFINITE
+
+
+@pytest.mark.parametrize("scale_exp", [-12, 8])
+def test_half2_balances_point_scales(scale_exp):
+    """The two-part fp16 operands take X and Y to the fp16 range by exact powers
+    of two. Clouds scaled by s = 2^k with eps scaled by s^2 have potentials
+    scaled by s^2; at k = -12 the unbalanced low parts would be fp16
+    subnormals, at k = 8 the scaled X would be far from Y's magnitude. The
+    returned potentials match the oracle's on the scaled inputs to the fp32
+    gate times s^2."""
+    s = 2.0 ** scale_exp
+    data = workloads.make("c2", n=300, m=260)
+    data["X"] = (data["X"] * s).astype(np.float32)
+    data["Y"] = (data["Y"] * s).astype(np.float32)
+    eps = float(np.float32(0.1 * s * s))
+    say(f"half2 scale 2^{scale_exp} eps={eps}")
+    prob = make_problem(data, eps=eps)
+    X, Y, a, b = oracle_inputs(prob)
+    f, g = zeros(300), zeros(260)
+    info = ssa.ot_solve(prob, f, g, 20)
+    torch.cuda.synchronize()
+    assert info["operand_mode"] == 3
+    f_ref, g_ref = oracle.sinkhorn(oracle.cost_matrix(X, Y), a, b, float(np.float32(eps)), 20)
+    assert np.abs(host64(f) - f_ref).max() <= POT_TOL["f32"] * s * s
+    assert np.abs(host64(g) - g_ref).max() <= POT_TOL["f32"] * s * s
+
+
+def test_half2_range_exceeded_reported():
+    """Coordinates too large for the two-part fp16 scores ((2/eps) log2(e)
+    max|x| max|y| far above 2^28): ot_solve with info reports
+    OT_ERR_UNSUPPORTED; the three-part bf16 split covers the fp32 range."""
+    data = workloads.make("c1", n=100, m=90)
+    data["X"] = (data["X"] * 1e5).astype(np.float32)
+    data["Y"] = (data["Y"] * 1e5).astype(np.float32)
+    prob = make_problem(data, eps=1.0)
+    f, g = zeros(100), zeros(90)
+    with pytest.raises(ssa.OtError) as ei:
+        ssa.ot_solve(prob, f, g, 3)
+    assert ei.value.code == ssa.OT_ERR_UNSUPPORTED
+    prob = make_problem(data, eps=1.0, mode="split_bf16")
+    f, g = zeros(100), zeros(90)
+    info = ssa.ot_solve(prob, f, g, 3)
+    torch.cuda.synchronize()
+    assert info["operand_mode"] == 2 and not info["nonfinite"]
+    assert torch.isfinite(f).all() and torch.isfinite(g).all()
 
 
 # --- size edges -------------------------------------------------------------------------
