@@ -54,9 +54,9 @@ ALU_PAIRS_PEAK = ALU_LANE_SLOTS_PER_S / ALU_SLOTS_PER_PAIR
 # FETCH_SIZE / WRITE_SIZE runs (scaled by the copy-kernel calibration), valid
 # only for the kernel source they were taken on.
 TRAFFIC = {
-    "c2": {"kernels_sha256": "73bdc5aa91285e5d9dc6d8f08648af973cf3920c59d7cb8ad27dbeed7c15226e",
-           "bytes_per_launch": 74472219,
-           "source": "profiles/lse_lds_kernel_c2_n20000_d64_f32split_hbm_traffic.md"},
+    "c2": {"kernels_sha256": "8974d1b1a26b13b59e8e9b2680a609029efe6aa4f53773178e2f2a2718748ba9",
+           "bytes_per_launch": 51414951,
+           "source": "profiles/lse_pipe_kernel_c2_n20000_d64_f32half2_hbm_traffic.md"},
 }
 # Sources of the register-resident log-sum-exp kernels the counters describe.
 KERNEL_SRCS = [os.path.join(ROOT, "streaming_sinkhorn_amd", "csrc", f)
@@ -372,6 +372,10 @@ def main():
                 "unit": "Gpair/s", "frac": achieved / (ALU_PAIRS_PEAK / 1e9)}
         per_launch = {"algorithmic_pairs_per_launch": pairs}
     per_launch["fp32_equivalent_tflops"] = alg_flops / avg_lse_s / 1e12
+    if w.dtype == "f32":
+        # the same 2 d flops per pair against the fp32 matrix peak (the bound of
+        # a pass that used the fp32 matrix instruction)
+        per_launch["frac_of_fp32_matrix_peak"] = per_launch["fp32_equivalent_tflops"] / MFMA_PEAK_TFLOPS["f32"]
     roof["traffic"] = traffic_for(args.workload)
     roof.update({"kernel": "streamed log-sum-exp pass (lse_*_kernel)", "avg_launch_us": avg_lse_s * 1e6,
                  "launches": lse_n, **per_launch})

@@ -44,8 +44,8 @@ int f32_operand_mode(int32_t flags) {
 //  - fp32 points (f32_mode: kModeHalf2, kModeSplit or kModeF32) use the
 //    requested split, or fp32 operands;
 //  - d <= 128 (split or native fp32) / 256 bf16: register-resident rows; the
-//    split layouts keep one row tile per wave above d = 64 (16 or 24 KiB of
-//    row operand in registers);
+//    three-part split keeps one row tile per wave above d = 64 (24 KiB of
+//    row operand in registers), the two-part split two (16 KiB each);
 //  - wider: the tiled pass (column blocks of ct tiles, LDS stages of bk
 //    k-blocks), with the units per tile padded to whole stages.
 // Transport application keeps its own layout (for_apply): fp32 or bf16
@@ -63,8 +63,15 @@ KConf kernel_conf(int64_t d, int bf16, int f32_mode, bool for_apply) {
     k.kb = ku * kl;
     k.kbp = k.kb;
     k.xres = true;
-    k.lds = k.kb >= 4 * ku;
-    k.ri = k.kb <= 4 * ku ? 2 : 1;
+    if (f32_mode == kModeHalf2) {
+      // two row tiles per wave; per-wave column loads up to d = 64, columns
+      // through LDS above (measured best on gfx950)
+      k.lds = k.kb >= 16;
+      k.ri = 2;
+    } else {
+      k.lds = k.kb >= 12;
+      k.ri = k.kb <= 12 ? 2 : 1;
+    }
   } else {
     k.mode = split ? f32_mode : (bf16 ? 1 : 0);
     k.kbw = (bf16 || split) ? 16 : 8;

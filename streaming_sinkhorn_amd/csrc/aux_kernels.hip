@@ -367,25 +367,63 @@ __global__ __launch_bounds__(256) void pack_split_kernel(const float* __restrict
 // no a does, the plan is marked out of range and X is written as NaN, so
 // the potentials come out non-finite rather than wrong.
 // ---------------------------------------------------------------------------
-// Largest |value| of a row-major cloud, as the bits of a non-negative float:
-// a NaN coordinate compares above every finite value and infinity.
+// Largest |value| of a row-major cloud, as the bits of a non-negative float
+// (a NaN coordinate compares above every finite value and infinity): block b
+// scans a contiguous run of rows and writes its maximum to part[b].
 __global__ __launch_bounds__(256) void absmax_kernel(const float* __restrict__ src, int64_t rows,
                                                      int64_t d, int64_t ld,
-                                                     unsigned* __restrict__ out) {
+                                                     unsigned* __restrict__ part) {
+  __shared__ unsigned sh[256];
+  const int64_t per = (rows + gridDim.x - 1) / gridDim.x;
+  const int64_t r0 = (int64_t)blockIdx.x * per;
+  const int64_t r1 = r0 + per < rows ? r0 + per : rows;
+  const int64_t cnt = r1 > r0 ? (r1 - r0) * d : 0;
+  // element e = i d + k of the run; stepping e by 256 adds (q, rm) to (i, k)
+  const int64_t q = 256 / d, rm = 256 % d;
+  int64_t i = threadIdx.x / d, k = threadIdx.x % d;
   unsigned mx = 0;
-  for (int64_t i = blockIdx.x; i < rows; i += gridDim.x)
-    for (int64_t k = threadIdx.x; k < d; k += 256)
-      mx = max(mx, __float_as_uint(src[i * ld + k]) & 0x7fffffffu);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) mx = max(mx, (unsigned)__shfl_xor((int)mx, o));
-  if ((threadIdx.x & 63) == 0) atomicMax(out, mx);
+  for (int64_t e = threadIdx.x; e < cnt; e += 256) {
+    mx = max(mx, __float_as_uint(src[(r0 + i) * ld + k]) & 0x7fffffffu);
+    i += q;
+    k += rm;
+    if (k >= d) {
+      k -= d;
+      ++i;
+    }
+  }
+  sh[threadIdx.x] = mx;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) sh[threadIdx.x] = max(sh[threadIdx.x], sh[threadIdx.x + w]);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) part[blockIdx.x] = sh[0];
 }
 
-// cx: the factor X is packed with (score scale at the problem's eps; a
-// smaller eps-scaling factor only lowers |X|).
-__global__ void half2_plan_kernel(Half2Plan* __restrict__ p, float cx) {
-  const float mx = __uint_as_float(p->amax[0]) * cx;
-  const float my = __uint_as_float(p->amax[1]);
+// Reduces the block maxima of X (part[0..nx)) and Y (part[kHalf2Parts..))
+// and writes the plan. cx: the factor X is packed with (score scale at the
+// problem's eps; a smaller eps-scaling factor only lowers |X|).
+__global__ __launch_bounds__(256) void half2_plan_kernel(Half2Plan* __restrict__ p, int nx, int ny,
+                                                         float cx) {
+  __shared__ unsigned sh[2][256];
+  unsigned ax = 0, ay = 0;
+  for (int b = threadIdx.x; b < nx; b += 256) ax = max(ax, p->part[b]);
+  for (int b = threadIdx.x; b < ny; b += 256) ay = max(ay, p->part[kHalf2Parts + b]);
+  sh[0][threadIdx.x] = ax;
+  sh[1][threadIdx.x] = ay;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) {
+      sh[0][threadIdx.x] = max(sh[0][threadIdx.x], sh[0][threadIdx.x + w]);
+      sh[1][threadIdx.x] = max(sh[1][threadIdx.x], sh[1][threadIdx.x + w]);
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x != 0) return;
+  p->amax[0] = sh[0][0];
+  p->amax[1] = sh[1][0];
+  const float mx = __uint_as_float(sh[0][0]) * cx;
+  const float my = __uint_as_float(sh[1][0]);
   int ex = 0, ey = 0;  // m < 2^e
   if (mx > 0.f) (void)frexpf(mx, &ex);
   if (my > 0.f) (void)frexpf(my, &ey);
@@ -531,10 +569,12 @@ hipError_t launch_pack_split(const float* src, int64_t rows, int64_t d, int64_t 
 
 hipError_t launch_half2_plan(const float* X, int64_t n, int64_t ldx, const float* Y, int64_t m,
                              int64_t ldy, int64_t d, float cx, Half2Plan* plan, hipStream_t st) {
-  fill_kernel<<<1, 256, 0, st>>>((float*)plan->amax, 0.f, 2);
-  absmax_kernel<<<(int)(n < 4096 ? n : 4096), 256, 0, st>>>(X, n, d, ldx, &plan->amax[0]);
-  absmax_kernel<<<(int)(m < 4096 ? m : 4096), 256, 0, st>>>(Y, m, d, ldy, &plan->amax[1]);
-  half2_plan_kernel<<<1, 1, 0, st>>>(plan, cx);
+  // about 16 K elements per block, at most kHalf2Parts blocks per cloud
+  const int nx = grid_for(n * d, 16384, kHalf2Parts);
+  const int ny = grid_for(m * d, 16384, kHalf2Parts);
+  absmax_kernel<<<nx, 256, 0, st>>>(X, n, d, ldx, plan->part);
+  absmax_kernel<<<ny, 256, 0, st>>>(Y, m, d, ldy, plan->part + kHalf2Parts);
+  half2_plan_kernel<<<1, 256, 0, st>>>(plan, nx, ny, cx);
   return hipGetLastError();
 }
 

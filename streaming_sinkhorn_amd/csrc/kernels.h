@@ -49,12 +49,15 @@ hipError_t launch_pack_split(const float* src, int64_t rows, int64_t d, int64_t 
                              int units, float scale, void* dst, hipStream_t st);
 // Range plan of the half2 operand mode (two fp16 parts per fp32 value):
 // the largest |x| and |y| (float bits), the exact factors 2^a, 2^-a applied
-// to X and Y, and whether both clouds fit fp16 with them.
+// to X and Y, whether both clouds fit fp16 with them, and the per-block
+// maxima it is reduced from.
+constexpr int kHalf2Parts = 1024;
 struct Half2Plan {
   unsigned amax[2];
   float xmul, ymul;
   int ok;
   int pad[3];
+  unsigned part[2 * kHalf2Parts];
 };
 // Computes the plan from X, Y (fp32) and the factor cx that X is packed with.
 hipError_t launch_half2_plan(const float* X, int64_t n, int64_t ldx, const float* Y, int64_t m,
