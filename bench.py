@@ -18,6 +18,9 @@ bound of the online log-sum-exp in pairs per second. ``cpu_baseline`` times
 the fp64 oracle on a bounded sample of the same workload on the host.
 
 Other modes:
+  --gemm-probe       time torch.matmul (hipBLASLt) on random bf16 data at
+                     16384^3 and 20000 x 1024 x 20000 and exit: the matrix
+                     rate the chip sustains in a library GEMM, for context.
   --copy-probe MIB   copy a MIB-MiB buffer a few times with torch and exit:
                      the calibration run for the HBM byte counters.
 """
@@ -122,6 +125,29 @@ def copy_probe(mib):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes": n * 4, "copies": 3}), flush=True)
+
+
+def gemm_probe():
+    import torch
+
+    torch.manual_seed(0)
+    out = {}
+    for m, k, n, reps in ((16384, 16384, 16384, 5), (20000, 1024, 20000, 10)):
+        a = torch.randn(m, k, device="cuda:0", dtype=torch.bfloat16)
+        b = torch.randn(k, n, device="cuda:0", dtype=torch.bfloat16)
+        for _ in range(3):
+            c = a @ b
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            c = a @ b
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[f"bf16_{m}x{k}x{n}_tflops"] = 2.0 * m * n * k / ms / 1e9
+        del a, b, c
+    print(json.dumps(out), flush=True)
 
 
 def hvp_cpu_baseline(data, tau, K, rows=3000):
@@ -250,6 +276,7 @@ def main():
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB")
+    ap.add_argument("--gemm-probe", action="store_true")
     ap.add_argument("--schedule", default="alternating", choices=["alternating", "symmetric"])
     ap.add_argument("--native-f32", action="store_true",
                     help="form fp32 scores with the fp32 matrix instruction instead of the "
@@ -264,6 +291,9 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the path runs "
               f"on a single MI355X and multi-GPU sharding is not built.", file=sys.stderr)
         sys.exit(2)
+    if args.gemm_probe:
+        gemm_probe()
+        return
     if args.copy_probe:
         copy_probe(args.copy_probe)
         return
