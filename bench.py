@@ -222,18 +222,18 @@ def hvp_main(args):
     # Executed matrix work of one HVP, each pass against the peak of the unit
     # it runs on (the ideal time is the sum; frac = ideal / measured):
     # - 2 K + 2 transport-vector passes (conjugate gradients and the marginals
-    #   they use) on the log-sum-exp layout: fp32 scores as the three-part
-    #   bf16 split, 6 products x 2 d flops per pair, bf16 peak;
+    #   they use) on the log-sum-exp layout: fp32 scores as the two-part fp16
+    #   split, 3 products x 2 d flops per pair, fp16 peak;
     # - the transport-matrix passes on fp32 matrix instructions: the score
     #   (2 d per pair, twice in the weighted pass, which also forms A Y^T)
     #   and the value product over value columns padded to 32 (2 per column).
     pad32 = lambda cols: (cols + 31) // 32 * 32
-    vec_bf16 = (2 * K + 2) * pairs * 12.0 * w.d
+    vec_f16 = (2 * K + 2) * pairs * 6.0 * w.d
     mat_f32 = sum(pairs * (2.0 * w.d * (2 if wt else 1) + 2.0 * pad32(cols))
                   for cols, wt in [(w.d, False), (w.d + 2, False), (w.d + 1, False), (w.d, True)])
-    ideal = vec_bf16 / (MFMA_PEAK_TFLOPS["bf16"] * 1e12) + mat_f32 / (MFMA_PEAK_TFLOPS["f32"] * 1e12)
-    bf16_equiv = ideal * MFMA_PEAK_TFLOPS["bf16"] * 1e12
-    achieved = bf16_equiv / ev_sec / 1e12
+    ideal = vec_f16 / (MFMA_PEAK_TFLOPS["f16"] * 1e12) + mat_f32 / (MFMA_PEAK_TFLOPS["f32"] * 1e12)
+    f16_equiv = ideal * MFMA_PEAK_TFLOPS["f16"] * 1e12
+    achieved = f16_equiv / ev_sec / 1e12
     res = {
         "metric": f"streaming HVP time per call (n=m={w.n}, d={w.d}, K={K} CG, tau={tau})",
         "value": sec,
@@ -252,12 +252,12 @@ def hvp_main(args):
                                f"iterations (untimed); HVP with K={K} fixed CG iterations, tau={tau}",
                    "n": w.n, "m": w.m, "d": w.d, "eps": w.eps, "cg_iters": K,
                    "transport_passes": 2 * K + 4},
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_PEAK_TFLOPS["bf16"],
-                     "unit": "TFLOP/s (bf16-equivalent)", "frac": ideal / ev_sec,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_PEAK_TFLOPS["f16"],
+                     "unit": "TFLOP/s (fp16-equivalent)", "frac": ideal / ev_sec,
                      "traffic": None,
                      "kernel": "all streamed passes of one HVP (vector passes: lse_*_kernel with a "
                                "value column; matrix passes: apply_partial_kernel); executed matrix "
-                               "work with fp32 flops weighted by the bf16/fp32 peak ratio, over the "
+                               "work with fp32 flops weighted by the fp16/fp32 peak ratio, over the "
                                "event-timed call",
                      "ideal_sec": ideal, "event_sec_per_hvp": ev_sec},
     }

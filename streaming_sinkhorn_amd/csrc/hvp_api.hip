@@ -185,7 +185,7 @@ struct VecWs {
   bool on;
   KConf k;
   PassShape F, G;  // F: rows x, columns y; G: rows y, columns x
-  size_t o_xs, o_ys, o_bx, o_by, o_part, o_partT, o_ones, o_rv, o_cv;
+  size_t o_xs, o_ys, o_bx, o_by, o_part, o_partT, o_ones, o_rv, o_cv, o_plan;
 };
 
 // HVP vectors beyond the transport workspace. pd and u are padded to whole
@@ -224,7 +224,13 @@ HvpWs hvp_layout(const ot_problem* p) {
   w.o_part = take((size_t)kCgMaxParts * 4);
   w.o_cs = take(sizeof(CgState));
   VecWs& v = w.V;
-  v.k = kernel_conf(p->d, 0, (p->flags & OT_NATIVE_F32) ? kModeF32 : kModeSplit);
+  v.k = kernel_conf(p->d, 0, f32_operand_mode(p->flags));
+  if (v.k.mode == kModeHalf2 && v.k.xres) {
+    // the value column and T take registers: LDS-shared columns from d = 64
+    // and one row tile per wave at d = 128 keep two waves per SIMD
+    v.k.lds = v.k.kb >= 8;
+    v.k.ri = v.k.kb >= 16 ? 1 : 2;
+  }
   v.on = v.k.xres;
   if (v.on) {
     const int nt = w.T.ntiles, mt = w.T.mtiles;
@@ -241,20 +247,30 @@ HvpWs hvp_layout(const ot_problem* p) {
     v.o_ones = take((size_t)(w.T.npad > w.T.mpad ? w.T.npad : w.T.mpad) * 4);
     v.o_rv = take((size_t)w.T.npad * 4);
     v.o_cv = take((size_t)w.T.mpad * 4);
+    v.o_plan = take(sizeof(Half2Plan));
   }
   w.total = take.o;
   return w;
 }
 
 // Operands of the vector passes: X packed pre-scaled by c = 2 log2(e) / eps
-// (split or fp32 layout), Y unscaled, biases c ((pot - |.|^2) / 2 + (eps/2) log w)
-// from the transport context's log-weights.
+// (two-part fp16, three-part bf16 or fp32 layout; the fp16 one with its range
+// plan), Y unscaled, biases c ((pot - |.|^2) / 2 + (eps/2) log w) from the
+// transport context's log-weights.
 int prepare_vec(const Transport& t, const VecWs& v, char* w, hipStream_t st) {
   const ot_problem* p = t.p;
   const TransportWs& L = t.L;
   void* xs = w + v.o_xs;
   void* ys = w + v.o_ys;
-  if (v.k.mode == 2) {
+  if (v.k.mode == kModeHalf2) {
+    Half2Plan* plan = (Half2Plan*)(w + v.o_plan);
+    OT_HIP(launch_half2_plan((const float*)p->x, p->n, p->ldx, (const float*)p->y, p->m, p->ldy,
+                             p->d, t.c, plan, st));
+    OT_HIP(launch_pack_half2((const float*)p->x, p->n, p->d, p->ldx, L.ntiles, v.k.kbp, t.c, plan,
+                             0, xs, st));
+    OT_HIP(launch_pack_half2((const float*)p->y, p->m, p->d, p->ldy, L.mtiles, v.k.kbp, 1.f, plan,
+                             1, ys, st));
+  } else if (v.k.mode == kModeSplit) {
     OT_HIP(launch_pack_split((const float*)p->x, p->n, p->d, p->ldx, L.ntiles, v.k.kbp, t.c, xs, st));
     OT_HIP(launch_pack_split((const float*)p->y, p->m, p->d, p->ldy, L.mtiles, v.k.kbp, 1.f, ys, st));
   } else {
@@ -424,11 +440,19 @@ int ot_hvp(const ot_problem* p, const float* f, const float* g, const float* A, 
     OT_HIP(launch_hvp_final(n, d, p->eps, X, p->ldx, A, lda, PY, r, xa, ra1, PF, B5, out, st));
     if (info) {
       CgState h{};
+      int in_range = 1;
       OT_HIP(hipMemcpyAsync(&h, cs, sizeof(h), hipMemcpyDeviceToHost, st));
+      if (L.V.on && L.V.k.mode == kModeHalf2)
+        OT_HIP(hipMemcpyAsync(&in_range, &((const Half2Plan*)(w + L.V.o_plan))->ok, sizeof(int),
+                              hipMemcpyDeviceToHost, st));
       OT_HIP(hipStreamSynchronize(st));
       info->cg_iters = h.iters;
       info->breakdown = h.breakdown;
       info->cg_rel_residual = h.bb > 0.f ? std::sqrt(h.rr / h.bb) : 0.f;
+      if (!in_range)
+        return fail(OT_ERR_UNSUPPORTED,
+                    "fp32 coordinates too large for the two-part fp16 scores; OT_SPLIT_BF16 "
+                    "covers the fp32 range");
     }
     return OT_OK;
   } catch (...) {

@@ -475,25 +475,20 @@ static hipError_t lse_split_dispatch(const PassShape& s, const ResArgs& a, hipSt
 
 // Two fp16 parts per k-block: 2, 4, 8 units for d <= 64, 16 for
 // 64 < d <= 128 (columns through LDS; 32 KiB of row operand per wave).
-// (the transport-vector passes use the three-part split)
 template <bool VEC>
 static hipError_t lse_half2_dispatch(const PassShape& s, const ResArgs& a, hipStream_t st) {
-  if constexpr (VEC) {
-    return hipErrorInvalidValue;
-  } else {
-    switch (s.kb) {
-      case 2: resident_go<kModeHalf2, 2, false>(s, a, st); break;
-      case 4: resident_go<kModeHalf2, 4, false>(s, a, st); break;
-      case 8: resident_go<kModeHalf2, 8, false>(s, a, st); break;
-      case 16:
-        if (!s.lds) return hipErrorInvalidValue;
-        if (s.ri == 2) lse_lds_go<kModeHalf2, 16, 2, false>(s, a, st);
-        else lse_lds_go<kModeHalf2, 16, 1, false>(s, a, st);
-        break;
-      default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
+  switch (s.kb) {
+    case 2: resident_go<kModeHalf2, 2, VEC>(s, a, st); break;
+    case 4: resident_go<kModeHalf2, 4, VEC>(s, a, st); break;
+    case 8: resident_go<kModeHalf2, 8, VEC>(s, a, st); break;
+    case 16:
+      if (!s.lds) return hipErrorInvalidValue;
+      if (s.ri == 2) lse_lds_go<kModeHalf2, 16, 2, VEC>(s, a, st);
+      else lse_lds_go<kModeHalf2, 16, 1, VEC>(s, a, st);
+      break;
+    default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
 }
 
 template <int MODE, bool VEC>
