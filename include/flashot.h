@@ -124,11 +124,11 @@ extern "C" {
  *               (2/eps) log2(e) max|x_ik| max|y_jk| < 2^28 (scores in log2
  *               units that fp32 still resolves); beyond it the potentials
  *               come out NaN and ot_solve with info returns
- *               OT_ERR_UNSUPPORTED. OT_SPLIT_BF16 uses three bf16 parts
- *               (24 significant bits, six products, fp32 exponent range)
- *               and OT_NATIVE_F32 the fp32 matrix instruction. Transport
- *               application always uses fp32 products for fp32 points, and
- *               the Hessian-vector product the three-part bf16 split.
+ *               OT_ERR_UNSUPPORTED (ot_hvp likewise). OT_SPLIT_BF16 uses
+ *               three bf16 parts (24 significant bits, six products, fp32
+ *               exponent range) and OT_NATIVE_F32 the fp32 matrix
+ *               instruction. Transport application always uses fp32
+ *               products for fp32 points.
  */
 typedef struct ot_problem {
   const void* x;
@@ -354,9 +354,12 @@ typedef struct ot_hvp_info {
  *   info    host or NULL. With tol > 0 the host reads the solver state after
  *           every iteration (one synchronisation each); when info is non-NULL
  *           the call synchronises the stream at the end and fills it.
+ * The conjugate-gradient products (d <= 128) form their scores in the
+ * problem's fp32 operand mode (see ot_problem flags).
  * Errors: OT_ERR_INVALID_ARG (null pointer, lda < d, tau < 0, tol < 0,
- * max_iters < 0, non-finite option), OT_ERR_UNSUPPORTED, OT_ERR_WORKSPACE,
- * OT_ERR_HIP.
+ * max_iters < 0, non-finite option), OT_ERR_UNSUPPORTED (also, when info is
+ * given, points too large for the default two-part fp16 scores),
+ * OT_ERR_WORKSPACE, OT_ERR_HIP.
  */
 int ot_hvp(const ot_problem* p, const float* f, const float* g, const float* A, int64_t lda,
            const ot_hvp_opts* opts, float* out, ot_hvp_info* info, void* ws,

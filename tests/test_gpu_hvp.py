@@ -185,17 +185,20 @@ def test_hvp_is_symmetric():
     assert abs(lhs - rhs) <= 1e-4 * scale
 
 
+@pytest.mark.parametrize("mode", ["native", "split_bf16"])
 @pytest.mark.parametrize("n,m,d,eps", [(200, 150, 8, 0.3), (130, 90, 70, 0.5)])
-def test_hvp_native_fp32_operands(n, m, d, eps):
-    """OT_NATIVE_F32: the conjugate-gradient passes form scores with the fp32
-    matrix instruction (register-pipelined kernel for d = 8, LDS-shared for d = 70)."""
-    say(f"hvp native n={n} m={m} d={d} eps={eps}")
+def test_hvp_other_fp32_operand_modes(n, m, d, eps, mode):
+    """OT_NATIVE_F32 / OT_SPLIT_BF16: the conjugate-gradient passes form scores
+    with the fp32 matrix instruction or from three bf16 parts (register-
+    pipelined kernel for d = 8, LDS-shared for d = 70)."""
+    say(f"hvp {mode} n={n} m={m} d={d} eps={eps}")
     data = workloads.hvp_parity_inputs(n, m, d, seed=n + d)
     X, Y, a, b = (data[k].astype(np.float64) for k in ("X", "Y", "a", "b"))
     f, g = oracle.sinkhorn(oracle.cost_matrix(X, Y), a, b, eps, 200)
     f32, g32 = f.astype(np.float32), g.astype(np.float32)
     t = lambda v: torch.from_numpy(np.ascontiguousarray(v)).to(DEV)
-    prob = ssa.problem(t(data["X"]), t(data["Y"]), eps, t(data["a"]), t(data["b"]), native_f32=True)
+    prob = ssa.problem(t(data["X"]), t(data["Y"]), eps, t(data["a"]), t(data["b"]),
+                       native_f32=mode == "native", split_bf16=mode == "split_bf16")
     G, info = ssa.ot_hvp(prob, t(f32), t(g32), t(data["A"]), tau=1e-5, max_iters=500, tol=1e-6)
     torch.cuda.synchronize()
     ref, _, _ = H.hvp_schur_cg(X, Y, a, b, f32.astype(np.float64), g32.astype(np.float64), eps,
@@ -203,6 +206,18 @@ def test_hvp_native_fp32_operands(n, m, d, eps):
     err = _rel(host64(G), ref)
     say(f"  rel err {err:.2e}, cg iters {info['cg_iters']}")
     assert err <= PV_TOL
+
+
+def test_hvp_range_exceeded_reported():
+    """Clouds too large for the two-part fp16 scores: ot_hvp with info reports
+    OT_ERR_UNSUPPORTED instead of returning the NaN product."""
+    data = workloads.hvp_parity_inputs(60, 50, 6, seed=3)
+    t = lambda v: torch.from_numpy(np.ascontiguousarray(v)).to(DEV)
+    prob = ssa.problem(t(data["X"] * 1e5), t(data["Y"] * 1e5), 1.0, t(data["a"]), t(data["b"]))
+    f, g = torch.zeros(60, device=DEV), torch.zeros(50, device=DEV)
+    with pytest.raises(ssa.OtError) as ei:
+        ssa.ot_hvp(prob, f, g, t(data["A"]), tau=1e-5, max_iters=3)
+    assert ei.value.code == ssa.OT_ERR_UNSUPPORTED
 
 
 def test_hvp_tiny_single_partial_tile():
