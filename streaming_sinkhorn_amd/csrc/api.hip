@@ -52,6 +52,20 @@ int f32_operand_mode(int32_t flags) {
 // operands, chunks of 8 k-blocks when the row operand is not resident.
 KConf kernel_conf(int64_t d, int bf16, int f32_mode, bool for_apply) {
   KConf k{};
+  if (for_apply && !bf16 && f32_mode == kModeHalf2) {
+    // transport application on two fp16 parts: resident rows up to d = 128,
+    // else chunks of 4 k-blocks (8 units)
+    k.mode = kModeHalf2;
+    k.kbw = 16;
+    k.kblocks = ceil_div(d, 16);
+    int kl = 1;
+    while (kl < k.kblocks) kl *= 2;
+    k.xres = k.kblocks <= 8;
+    k.kb = k.xres ? 2 * kl : 8;
+    k.kbp = k.xres ? k.kb : ceil_div(k.kblocks, 4) * 8;
+    k.ri = 1;
+    return k;
+  }
   const bool split = !bf16 && f32_mode != kModeF32 && !for_apply;
   const int ku = !split ? 1 : (f32_mode == kModeSplit ? 3 : 2);  // units per k-block
   if (split && d <= 128) {
@@ -578,17 +592,21 @@ int update_impl(const ot_problem* p, const float* other, float* pot, float* err,
 }
 
 // ---- transport application ------------------------------------------------
+// Scores: two fp16 parts (fp32 points by default), bf16, or fp32 operands
+// (OT_NATIVE_F32 / OT_SPLIT_BF16). The value product runs on two fp16 parts
+// except in the fp32-operand case.
 struct ApplyWs {
   KConf k;
   int rtiles, ctiles, rpad, cpad, pblocks, pb_per_pass, ppad;
   PassShape S;
-  size_t o_xp, o_yp, o_nx, o_ny, o_wr, o_hr, o_wc, o_hc, o_bc, o_vp, o_ms, o_o;
+  size_t o_xp, o_yp, o_nx, o_ny, o_wr, o_hr, o_wc, o_hc, o_bc, o_vp, o_ms, o_o, o_vamax, o_plan;
   size_t total;
 };
 
 ApplyWs apply_layout(const ot_problem* p, int64_t cols, bool transpose) {
   ApplyWs w{};
-  w.k = kernel_conf(p->d, p->dtype == OT_BF16, kModeF32, true);
+  w.k = kernel_conf(p->d, p->dtype == OT_BF16,
+                    f32_operand_mode(p->flags) == kModeHalf2 ? kModeHalf2 : kModeF32, true);
   const int64_t rows = transpose ? p->m : p->n;
   const int64_t strm = transpose ? p->n : p->m;
   w.rtiles = ceil_div(rows, kTile);
@@ -618,6 +636,8 @@ ApplyWs apply_layout(const ot_problem* p, int64_t cols, bool transpose) {
   w.o_vp = take((size_t)w.ctiles * w.pblocks * 4096);
   w.o_ms = take((size_t)w.S.splits * w.rpad * 8);
   w.o_o = take((size_t)w.S.splits * w.ppad * w.rpad * 4);
+  w.o_vamax = take((size_t)w.ppad * 4);
+  w.o_plan = take(sizeof(Half2Plan));
   w.total = o;
   return w;
 }
@@ -863,8 +883,23 @@ int ot_apply_plan(const ot_problem* p, const float* f, const float* g, const voi
     if (!p->x_sqn) OT_HIP(launch_sqnorms(p->x, bf, p->n, p->d, p->ldx, (float*)nx, st));
     if (!p->y_sqn) OT_HIP(launch_sqnorms(p->y, bf, p->m, p->d, p->ldy, (float*)ny, st));
     const float xs = (p->flags & OT_COST_AFFINE) ? 0.5f : 1.f;
-    OT_HIP(launch_pack_points(p->x, bf, p->n, p->d, p->ldx, ntiles, L.k.kbp, xs, xp, st));
-    OT_HIP(launch_pack_points(p->y, bf, p->m, p->d, p->ldy, mtiles, L.k.kbp, 1.f, yp, st));
+    // Units of the scores: log2 units for the fp16 parts (X packed times c,
+    // the kernel's multiplier kc = 1), dot-product units otherwise (kc = c).
+    const bool h2 = L.k.mode == kModeHalf2;
+    const bool fp16_values = L.k.mode != kModeF32;
+    const float kc = h2 ? 1.f : c;
+    if (h2) {
+      Half2Plan* plan = (Half2Plan*)(w + L.o_plan);
+      OT_HIP(launch_half2_plan((const float*)p->x, p->n, p->ldx, (const float*)p->y, p->m, p->ldy,
+                               p->d, c * xs, plan, st));
+      OT_HIP(launch_pack_half2((const float*)p->x, p->n, p->d, p->ldx, ntiles, L.k.kbp, c * xs,
+                               plan, 0, xp, st));
+      OT_HIP(launch_pack_half2((const float*)p->y, p->m, p->d, p->ldy, mtiles, L.k.kbp, 1.f, plan,
+                               1, yp, st));
+    } else {
+      OT_HIP(launch_pack_points(p->x, bf, p->n, p->d, p->ldx, ntiles, L.k.kbp, xs, xp, st));
+      OT_HIP(launch_pack_points(p->y, bf, p->m, p->d, p->ldy, mtiles, L.k.kbp, 1.f, yp, st));
+    }
     // Row side r (outputs) and column side s (streamed).
     const int64_t rows = tr ? p->m : p->n, srows = tr ? p->n : p->m;
     const float* wr_user = tr ? p->b : p->a;
@@ -885,15 +920,25 @@ int ot_apply_plan(const ot_problem* p, const float* f, const float* g, const voi
     float* po = (float*)(w + L.o_o);
     OT_HIP(launch_weights(wr_user, (int)rows, L.rpad, eps, wr, hr, st));
     OT_HIP(launch_weights(ws_user, (int)srows, L.cpad, eps, wc, hc, st));
-    OT_HIP(launch_bias_from_pot(pot_s, norm_s, hc, (int)srows, L.cpad, 1.f, bc, st));
-    OT_HIP(launch_pack_values(V, v_dtype == OT_BF16, srows, cols, ldv, L.ctiles, L.pblocks, vp, st));
-    OT_HIP(launch_apply_partial(L.S, bf, L.pblocks, L.pb_per_pass, Rp, Cp, bc, vp, c, pms, po,
-                                L.ppad, st));
+    OT_HIP(launch_bias_from_pot(pot_s, norm_s, hc, (int)srows, L.cpad, h2 ? c : 1.f, bc, st));
+    unsigned* vamax = fp16_values ? (unsigned*)(w + L.o_vamax) : nullptr;
+    if (fp16_values) {
+      OT_HIP(launch_vcol_absmax(V, v_dtype == OT_BF16, srows, cols, ldv, vamax, st));
+      OT_HIP(launch_pack_values_h2(V, v_dtype == OT_BF16, srows, cols, ldv, L.ctiles, L.pblocks,
+                                   vamax, vp, st));
+      OT_HIP(launch_apply_h2(L.S, L.k.mode, L.pblocks, L.pb_per_pass, Rp, Cp, bc, vp, kc, pms,
+                             po, L.ppad, st));
+    } else {
+      OT_HIP(launch_pack_values(V, v_dtype == OT_BF16, srows, cols, ldv, L.ctiles, L.pblocks, vp,
+                                st));
+      OT_HIP(launch_apply_partial(L.S, bf, L.pblocks, L.pb_per_pass, Rp, Cp, bc, vp, c, pms, po,
+                                  L.ppad, st));
+    }
     const int mode = grad ? kApplyGrad : ((flags & OT_BARY) ? kApplyBary : kApplyPlain);
     const void* Xsrc = tr ? p->y : p->x;
     const int64_t ldx = tr ? p->ldy : p->ldx;
-    OT_HIP(launch_apply_merge(pms, po, L.S.splits, L.rpad, L.ppad, (int)rows, (int)cols, c, eps,
-                              pot_r, norm_r, wr, mode, Xsrc, bf, ldx, out, marg, st));
+    OT_HIP(launch_apply_merge(pms, po, L.S.splits, L.rpad, L.ppad, (int)rows, (int)cols, kc, eps,
+                              pot_r, norm_r, wr, mode, Xsrc, bf, ldx, vamax, out, marg, st));
     return OT_OK;
   } catch (...) {
     return fail(OT_ERR_HIP, "unexpected host exception");

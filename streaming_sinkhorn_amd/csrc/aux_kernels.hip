@@ -197,7 +197,8 @@ __global__ __launch_bounds__(256) void apply_merge_kernel(
     const float2* __restrict__ partMS, const float* __restrict__ partO, int splits, int rpad,
     int ppad, int rows, int cols, float c, float eps, const float* __restrict__ pot,
     const float* __restrict__ norm, const float* __restrict__ wgt, int mode,
-    const T* __restrict__ Xsrc, int64_t ldx, float* __restrict__ out, float* __restrict__ marg) {
+    const T* __restrict__ Xsrc, int64_t ldx, const unsigned* __restrict__ vamax,
+    float* __restrict__ out, float* __restrict__ marg) {
   __shared__ float scl[kMaxApplySplits][32];
   __shared__ float fac[32], rr[32], ss[32];
   __shared__ float tile[32][33];
@@ -217,7 +218,7 @@ __global__ __launch_bounds__(256) void apply_merge_kernel(
         scl[s][t] = e;
         S += ps.y * e;
       }
-      const float f = wgt[i] * exp2f((pot[i] - norm[i] + 2.f * M) * (kLog2e / eps));
+      const float f = wgt[i] * exp2f(fmaf(pot[i] - norm[i], kLog2e / eps, cm));
       fac[t] = f;
       ss[t] = S;
       rr[t] = f * S;
@@ -235,6 +236,7 @@ __global__ __launch_bounds__(256) void apply_merge_kernel(
     if (i < rows && p < cols) {
       float O = 0.f;
       for (int s = 0; s < splits; ++s) O += partO[((size_t)s * ppad + p) * rpad + i] * scl[s][tx];
+      if (vamax) O = ldexpf(O, -vcol_shift(vamax[p]));
       if (mode == kApplyBary) {
         val = O / ss[tx];
       } else if (mode == kApplyGrad) {
@@ -496,6 +498,57 @@ __global__ __launch_bounds__(256) void pack_values_kernel(const T* __restrict__ 
   }
 }
 
+// Column maxima of |V| for the fp16 value layout: thread = column, rows
+// strided over blockIdx.y, one atomic max per thread (amax zeroed first).
+template <typename T>
+__global__ __launch_bounds__(256) void vcol_absmax_kernel(const T* __restrict__ V, int64_t rows,
+                                                          int64_t cols, int64_t ldv,
+                                                          unsigned* __restrict__ amax) {
+  const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (col >= cols) return;
+  unsigned mx = 0;
+  for (int64_t r = blockIdx.y; r < rows; r += gridDim.y)
+    mx = max(mx, __float_as_uint(load_as_f32<T>(V, r * ldv + col)) & 0x7fffffffu);
+  atomicMax(&amax[col], mx);
+}
+
+// fp16 value layout (see launch_pack_values_h2): unit ((jt * pblocks + pb) * 2
+// + q) * 2 + part, 64 lanes of 8 fp16 values.
+template <typename T>
+__global__ __launch_bounds__(256) void pack_values_h2_kernel(const T* __restrict__ V, int64_t rows,
+                                                             int64_t cols, int64_t ldv,
+                                                             int64_t total, int pblocks,
+                                                             const unsigned* __restrict__ amax,
+                                                             u32x4* __restrict__ dst) {
+  for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * 256) {
+    const int lane = (int)(idx & 63);
+    const int part = (int)((idx >> 6) & 1);
+    const int q = (int)((idx >> 7) & 1);
+    const int64_t tp = idx >> 8;
+    const int pb = (int)(tp % pblocks);
+    const int64_t t = tp / pblocks;
+    const int64_t col = (int64_t)pb * 32 + (lane & 31);
+    const int shift = col < cols ? vcol_shift(amax[col]) : 0;
+    uint32_t h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int64_t row = t * kTile + 8 * (2 * q + (e >> 2)) + 4 * (lane >> 5) + (e & 3);
+      const float v = (col < cols && row < rows) ? ldexpf(load_as_f32<T>(V, row * ldv + col), shift)
+                                                 : 0.f;
+      const _Float16 hi = (_Float16)v;
+      const _Float16 x = part ? (_Float16)(v - (float)hi) : hi;
+      h[e] = (uint32_t)__builtin_bit_cast(uint16_t, x);
+    }
+    u32x4 o;
+    o.x = h[0] | (h[1] << 16);
+    o.y = h[2] | (h[3] << 16);
+    o.z = h[4] | (h[5] << 16);
+    o.w = h[6] | (h[7] << 16);
+    dst[idx] = o;
+  }
+}
+
 __global__ __launch_bounds__(256) void weights_kernel(const float* __restrict__ w, int rows,
                                                        int rpad, float eps,
                                                        float* __restrict__ wgt,
@@ -587,6 +640,31 @@ hipError_t launch_pack_half2(const float* src, int64_t rows, int64_t d, int64_t 
   return hipGetLastError();
 }
 
+hipError_t launch_vcol_absmax(const void* V, int bf16, int64_t rows, int64_t cols, int64_t ldv,
+                              unsigned* amax, hipStream_t st) {
+  fill_kernel<<<grid_for(cols, 256, 65536), 256, 0, st>>>((float*)amax, 0.f, cols);
+  dim3 grid((unsigned)((cols + 255) / 256), (unsigned)(rows < 256 ? rows : 256));
+  if (bf16)
+    vcol_absmax_kernel<uint16_t><<<grid, 256, 0, st>>>((const uint16_t*)V, rows, cols, ldv, amax);
+  else
+    vcol_absmax_kernel<float><<<grid, 256, 0, st>>>((const float*)V, rows, cols, ldv, amax);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_values_h2(const void* V, int bf16, int64_t rows, int64_t cols,
+                                 int64_t ldv, int ctiles, int pblocks, const unsigned* amax,
+                                 void* dst, hipStream_t st) {
+  const int64_t total = (int64_t)ctiles * pblocks * 4 * 64;
+  const int grid = grid_for(total, 256, 65536);
+  if (bf16)
+    pack_values_h2_kernel<uint16_t><<<grid, 256, 0, st>>>((const uint16_t*)V, rows, cols, ldv,
+                                                          total, pblocks, amax, (u32x4*)dst);
+  else
+    pack_values_h2_kernel<float><<<grid, 256, 0, st>>>((const float*)V, rows, cols, ldv, total,
+                                                       pblocks, amax, (u32x4*)dst);
+  return hipGetLastError();
+}
+
 hipError_t launch_pack_values(const void* V, int bf16, int64_t rows, int64_t cols, int64_t ldv,
                               int ctiles, int pblocks, float* dst, hipStream_t st) {
   const int64_t total = (int64_t)ctiles * pblocks * 4 * 64;
@@ -642,17 +720,18 @@ hipError_t launch_nonfinite(const float* f, int n, const float* g, int m, float*
 hipError_t launch_apply_merge(const float2* partMS, const float* partO, int splits, int rpad,
                               int ppad, int rows, int cols, float c, float eps, const float* pot,
                               const float* norm, const float* wgt, int mode, const void* Xsrc,
-                              int xbf16, int64_t ldx, float* out, float* marg, hipStream_t st) {
+                              int xbf16, int64_t ldx, const unsigned* vamax, float* out,
+                              float* marg, hipStream_t st) {
   if (splits > kMaxApplySplits) return hipErrorInvalidValue;
   dim3 grid((rows + 31) / 32, (cols + 31) / 32);
   if (xbf16)
     apply_merge_kernel<uint16_t><<<grid, 256, 0, st>>>(partMS, partO, splits, rpad, ppad, rows,
                                                        cols, c, eps, pot, norm, wgt, mode,
-                                                       (const uint16_t*)Xsrc, ldx, out, marg);
+                                                       (const uint16_t*)Xsrc, ldx, vamax, out, marg);
   else
     apply_merge_kernel<float><<<grid, 256, 0, st>>>(partMS, partO, splits, rpad, ppad, rows, cols,
                                                     c, eps, pot, norm, wgt, mode,
-                                                    (const float*)Xsrc, ldx, out, marg);
+                                                    (const float*)Xsrc, ldx, vamax, out, marg);
   return hipGetLastError();
 }
 

@@ -153,7 +153,7 @@ int transport(const Transport& t, bool tr, const float* V, int64_t cols, int64_t
                                 t.po, cc.ppad, st));
   OT_HIP(launch_apply_merge(t.pms, t.po, S.splits, rpad, cc.ppad, (int)rows, (int)cols, t.c,
                             t.eps, tr ? t.g : t.f, tr ? t.ny : t.nx, tr ? t.wy : t.wx, kApplyPlain,
-                            nullptr, 0, 0, out, marg, st));
+                            nullptr, 0, 0, nullptr, out, marg, st));
   return OT_OK;
 }
 

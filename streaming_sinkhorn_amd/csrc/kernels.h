@@ -68,6 +68,32 @@ hipError_t launch_half2_plan(const float* X, int64_t n, int64_t ldx, const float
 hipError_t launch_pack_half2(const float* src, int64_t rows, int64_t d, int64_t ld, int rtiles,
                              int units, float scale, const Half2Plan* plan, int side, void* dst,
                              hipStream_t st);
+// Value columns of the fp16 value product are scaled by 2^b, b from the
+// column's largest |v| (float bits), so that they lie in [2^14, 2^15); b = 0
+// for an all-zero or non-finite column. Shared by packing and merge.
+__host__ __device__ inline int vcol_shift(unsigned amax_bits) {
+  const int eb = (int)((amax_bits >> 23) & 0xff);
+  if (amax_bits == 0 || eb == 255) return 0;
+  const int b = 141 - (eb > 0 ? eb : 1);
+  return b < -100 ? -100 : (b > 100 ? 100 : b);
+}
+// Column maxima |V[:, p]| (float bits) into amax[0, cols), which is zeroed first.
+hipError_t launch_vcol_absmax(const void* V, int bf16, int64_t rows, int64_t cols, int64_t ldv,
+                              unsigned* amax, hipStream_t st);
+// Packs V (rows streamed x cols) for the fp16 value product: per column tile
+// jt, value block pb, k-chunk q (16 streamed rows) and part (hi, lo of
+// V[j][p] 2^b_p), lane l holds the 8 fp16 values of column 32 pb + l % 32 and
+// rows 32 jt + 8 (2q + e/4) + 4 (l/32) + e%4, e = 0..7 -- the order in which
+// a lane's score accumulator entries 8q .. 8q + 7 enter the matrix product.
+hipError_t launch_pack_values_h2(const void* V, int bf16, int64_t rows, int64_t cols,
+                                 int64_t ldv, int ctiles, int pblocks, const unsigned* amax,
+                                 void* dst, hipStream_t st);
+// Transport application with the exponentiated scores split into two fp16
+// parts against the fp16 value layout (three products per 16 streamed rows).
+// smode: kModeHalf2 (fp32 points, scores in log2 units, c = 1) or kModeBF16.
+hipError_t launch_apply_h2(const PassShape& s, int smode, int pblocks, int pb_per_pass,
+                           const void* Rp, const void* Cp, const float* cbias, const void* Vh,
+                           float c, float2* partMS, float* partO, int ppad, hipStream_t st);
 hipError_t launch_pack_values(const void* V, int bf16, int64_t rows, int64_t cols, int64_t ldv,
                               int ctiles, int pblocks, float* dst, hipStream_t st);
 hipError_t launch_weights(const float* w, int rows, int rpad, float eps, float* wgt, float* hlw,
@@ -119,10 +145,14 @@ hipError_t launch_apply_hadamard(const PassShape& s, int pblocks, int pb_per_pas
                                  const void* Cp, const void* Ap, const float* cbias,
                                  const float* Vp, float c, float2* partMS, float* partO, int ppad,
                                  hipStream_t st);
+// c: the partials' stabilisers are in units of c * M log2 units (c = 1:
+// log2 units). vamax (or NULL): column maxima of the fp16 value layout, whose
+// 2^b_p scale is removed.
 hipError_t launch_apply_merge(const float2* partMS, const float* partO, int splits, int rpad,
                               int ppad, int rows, int cols, float c, float eps, const float* pot,
                               const float* norm, const float* wgt, int mode, const void* Xsrc,
-                              int xbf16, int64_t ldx, float* out, float* marg, hipStream_t st);
+                              int xbf16, int64_t ldx, const unsigned* vamax, float* out,
+                              float* marg, hipStream_t st);
 
 // apply_merge modes
 constexpr int kApplyPlain = 0;
