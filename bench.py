@@ -224,14 +224,17 @@ def hvp_main(args):
     # - 2 K + 2 transport-vector passes (conjugate gradients and the marginals
     #   they use) on the log-sum-exp layout: fp32 scores as the two-part fp16
     #   split, 3 products x 2 d flops per pair, fp16 peak;
-    # - the transport-matrix passes on fp32 matrix instructions: the score
-    #   (2 d per pair, twice in the weighted pass, which also forms A Y^T)
-    #   and the value product over value columns padded to 32 (2 per column).
+    # - the transport-matrix passes: the score on fp32 matrix instructions
+    #   (2 d per pair, twice in the weighted pass, which also forms A Y^T);
+    #   the value product over value columns padded to 32 on fp16 parts
+    #   (3 products x 2 per column), or on fp32 (2 per column) in the
+    #   weighted pass.
     pad32 = lambda cols: (cols + 31) // 32 * 32
     vec_f16 = (2 * K + 2) * pairs * 6.0 * w.d
-    mat_f32 = sum(pairs * (2.0 * w.d * (2 if wt else 1) + 2.0 * pad32(cols))
-                  for cols, wt in [(w.d, False), (w.d + 2, False), (w.d + 1, False), (w.d, True)])
-    ideal = vec_f16 / (MFMA_PEAK_TFLOPS["f16"] * 1e12) + mat_f32 / (MFMA_PEAK_TFLOPS["f32"] * 1e12)
+    mat_f32 = pairs * (2.0 * w.d * 3 + 4.0 * w.d + 2.0 * pad32(w.d))
+    mat_f16 = sum(pairs * 6.0 * pad32(cols) for cols in (w.d, w.d + 2, w.d + 1))
+    ideal = ((vec_f16 + mat_f16) / (MFMA_PEAK_TFLOPS["f16"] * 1e12)
+             + mat_f32 / (MFMA_PEAK_TFLOPS["f32"] * 1e12))
     f16_equiv = ideal * MFMA_PEAK_TFLOPS["f16"] * 1e12
     achieved = f16_equiv / ev_sec / 1e12
     res = {

@@ -141,7 +141,7 @@ __global__ __launch_bounds__(256) void apply_partial_kernel(
 // 32x32x2 ones. A lane's accumulator entries 8q .. 8q + 7 are its B operand
 // for k-chunk q as they stand: the value layout follows that k order.
 // SMODE: kModeHalf2 scores (fp32 points as two fp16 parts, log2 units,
-// c = 1) or kModeBF16 scores (dot-product units, multiplied by c).
+// c = 1), kModeBF16 or kModeF32 scores (dot-product units, multiplied by c).
 // KB: operand units per tile (XRES) or per k-chunk.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t pack_f16x2(_Float16 a, _Float16 b) {
@@ -189,7 +189,7 @@ __global__ __launch_bounds__(256) void apply_h2_kernel(
       for (int kb = 0; kb < KB; kb += KU) {
         const u32x4* xo = XRES ? &xr[kb] : &xc[kb];
         if constexpr (SMODE == kModeHalf2) acc = mfma_half2(&yc[kb], xo, acc);
-        else acc = mfma_kblock<true>(yc[kb], xo[0], acc);
+        else acc = mfma_kblock<SMODE == kModeBF16>(yc[kb], xo[0], acc);
       }
     }
     acc = mfma_bias(cbias[jt * kTile + (lane & 31)], h, acc);
@@ -279,7 +279,7 @@ static hipError_t apply_h2_kb(const PassShape& s, int pblocks, const void* Rp, c
     return hipGetLastError();
   }
   switch (s.kb) {
-    case 1: if constexpr (SMODE == kModeBF16) { apply_h2_go<SMODE, 1, true, PB>(s, pblocks, Rp, Cp, cbias, Vh, c, partMS, partO, ppad, st); break; } else { return hipErrorInvalidValue; }
+    case 1: if constexpr (SMODE != kModeHalf2) { apply_h2_go<SMODE, 1, true, PB>(s, pblocks, Rp, Cp, cbias, Vh, c, partMS, partO, ppad, st); break; } else { return hipErrorInvalidValue; }
     case 2: apply_h2_go<SMODE, 2, true, PB>(s, pblocks, Rp, Cp, cbias, Vh, c, partMS, partO, ppad, st); break;
     case 4: apply_h2_go<SMODE, 4, true, PB>(s, pblocks, Rp, Cp, cbias, Vh, c, partMS, partO, ppad, st); break;
     case 8: apply_h2_go<SMODE, 8, true, PB>(s, pblocks, Rp, Cp, cbias, Vh, c, partMS, partO, ppad, st); break;
@@ -311,6 +311,9 @@ hipError_t launch_apply_h2(const PassShape& s, int smode, int pblocks, int pb_pe
   if (smode == kModeBF16)
     return apply_h2_dispatch<kModeBF16>(s, pblocks, pb_per_pass, Rp, Cp, cbias, Vh, c, partMS,
                                         partO, ppad, st);
+  if (smode == kModeF32)
+    return apply_h2_dispatch<kModeF32>(s, pblocks, pb_per_pass, Rp, Cp, cbias, Vh, c, partMS,
+                                       partO, ppad, st);
   return hipErrorInvalidValue;
 }
 

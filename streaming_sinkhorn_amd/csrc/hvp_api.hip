@@ -41,7 +41,8 @@ struct TransportWs {
   KConf k;
   int ntiles, mtiles, npad, mpad;
   PassShape F, T;
-  size_t o_xp, o_yp, o_ap, o_nx, o_ny, o_wx, o_hx, o_wy, o_hy, o_bx, o_by, o_vp, o_ms, o_o;
+  size_t o_xp, o_yp, o_ap, o_nx, o_ny, o_wx, o_hx, o_wy, o_hy, o_bx, o_by, o_vp, o_ms, o_o,
+      o_vamax;
 };
 
 template <typename Take>
@@ -73,6 +74,7 @@ TransportWs transport_layout(const ot_problem* p, int64_t cols_f, int64_t cols_t
   w.o_ms = take((mf > mt ? mf : mt) * 8);
   const size_t of = mf * cf.ppad, ot = mt * ct.ppad;
   w.o_o = take((of > ot ? of : ot) * 4);
+  w.o_vamax = take((size_t)(cf.ppad > ct.ppad ? cf.ppad : ct.ppad) * 4);
   return w;
 }
 
@@ -85,6 +87,7 @@ struct Transport {
   const float *nx, *ny, *f, *g;
   float *wx, *hx, *wy, *hy, *bx, *by, *vp, *po;
   float2* pms;
+  unsigned* vamax;
 };
 
 Transport make_transport(const ot_problem* p, const TransportWs& L, char* w, const float* f,
@@ -110,6 +113,7 @@ Transport make_transport(const ot_problem* p, const TransportWs& L, char* w, con
   t.vp = (float*)(w + L.o_vp);
   t.po = (float*)(w + L.o_o);
   t.pms = (float2*)(w + L.o_ms);
+  t.vamax = (unsigned*)(w + L.o_vamax);
   return t;
 }
 
@@ -133,7 +137,8 @@ int prepare_transport(const Transport& t, const float* A, int64_t lda, hipStream
 
 // out = P V (tr = false, V: m x cols) or P^T V (tr = true, V: n x cols), fp32
 // with row stride ldv; with hadamard, out = (P . A Y^T) V. marg (or NULL)
-// receives r = P 1 (resp. c = P^T 1).
+// receives r = P 1 (resp. c = P^T 1). Scores on fp32 operands; the value
+// product on fp16 parts, except in the Hadamard-weighted pass.
 int transport(const Transport& t, bool tr, const float* V, int64_t cols, int64_t ldv, float* out,
               float* marg, bool hadamard, hipStream_t st) {
   const ot_problem* p = t.p;
@@ -144,16 +149,19 @@ int transport(const Transport& t, bool tr, const float* V, int64_t cols, int64_t
   const void* Rp = tr ? t.yp : t.xp;
   const void* Cp = tr ? t.xp : t.yp;
   const float* bc = tr ? t.bx : t.by;
-  OT_HIP(launch_pack_values(V, 0, srows, cols, ldv, S.ctiles, cc.pblocks, t.vp, st));
-  if (hadamard)
+  if (hadamard) {
+    OT_HIP(launch_pack_values(V, 0, srows, cols, ldv, S.ctiles, cc.pblocks, t.vp, st));
     OT_HIP(launch_apply_hadamard(S, cc.pblocks, cc.pb_per_pass, Rp, Cp, t.ap, bc, t.vp, t.c,
                                  t.pms, t.po, cc.ppad, st));
-  else
-    OT_HIP(launch_apply_partial(S, 0, cc.pblocks, cc.pb_per_pass, Rp, Cp, bc, t.vp, t.c, t.pms,
-                                t.po, cc.ppad, st));
+  } else {
+    OT_HIP(launch_vcol_absmax(V, 0, srows, cols, ldv, t.vamax, st));
+    OT_HIP(launch_pack_values_h2(V, 0, srows, cols, ldv, S.ctiles, cc.pblocks, t.vamax, t.vp, st));
+    OT_HIP(launch_apply_h2(S, kModeF32, cc.pblocks, cc.pb_per_pass, Rp, Cp, bc, t.vp, t.c, t.pms,
+                           t.po, cc.ppad, st));
+  }
   OT_HIP(launch_apply_merge(t.pms, t.po, S.splits, rpad, cc.ppad, (int)rows, (int)cols, t.c,
                             t.eps, tr ? t.g : t.f, tr ? t.ny : t.nx, tr ? t.wy : t.wx, kApplyPlain,
-                            nullptr, 0, 0, nullptr, out, marg, st));
+                            nullptr, 0, 0, hadamard ? nullptr : t.vamax, out, marg, st));
   return OT_OK;
 }
 

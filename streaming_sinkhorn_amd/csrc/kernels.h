@@ -90,7 +90,8 @@ hipError_t launch_pack_values_h2(const void* V, int bf16, int64_t rows, int64_t 
                                  void* dst, hipStream_t st);
 // Transport application with the exponentiated scores split into two fp16
 // parts against the fp16 value layout (three products per 16 streamed rows).
-// smode: kModeHalf2 (fp32 points, scores in log2 units, c = 1) or kModeBF16.
+// smode: kModeHalf2 (fp32 points, scores in log2 units, c = 1), kModeBF16 or
+// kModeF32 (fp32 operands, dot-product units).
 hipError_t launch_apply_h2(const PassShape& s, int smode, int pblocks, int pb_per_pass,
                            const void* Rp, const void* Cp, const float* cbias, const void* Vh,
                            float c, float2* partMS, float* partO, int ppad, hipStream_t st);

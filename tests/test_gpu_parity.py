@@ -254,12 +254,17 @@ APPLY_CASES = [
 ]
 
 
+@pytest.mark.parametrize("mode", F32_MODES)
 @pytest.mark.parametrize("n,m,d,dtype,eps,cols", APPLY_CASES)
-def test_apply_plan(n, m, d, dtype, eps, cols):
-    say(f"apply n={n} m={m} d={d} dtype={dtype} eps={eps} cols={cols}")
+def test_apply_plan(n, m, d, dtype, eps, cols, mode):
+    """Default operands: scores and value product from fp16 parts (bf16 scores
+    for bf16 points); OT_NATIVE_F32 / OT_SPLIT_BF16: the fp32 kernel."""
+    if mode != "half2" and dtype != "f32":
+        pytest.skip("the fp32 operand options only apply to fp32 points")
+    say(f"apply n={n} m={m} d={d} dtype={dtype} eps={eps} cols={cols} mode={mode}")
     base = "c3_d16_bf16" if dtype == "bf16" else "c3_d16_f32"
     data = workloads.make(base, n=n, m=m, d=d)
-    prob = make_problem(data, eps=eps)
+    prob = make_problem(data, eps=eps, mode=mode)
     X, Y, a, b = oracle_inputs(prob)
     C = oracle.cost_matrix(X, Y)
     # the oracle's potentials after 20 iterations, rounded to fp32, for both sides
@@ -294,6 +299,33 @@ def test_apply_plan(n, m, d, dtype, eps, cols):
     assert _rel(host64(grad), g_ref) <= 10 * PV_TOL
     gy_ref = oracle.grad_x(Y, X, P.T)
     assert _rel(host64(gy), gy_ref) <= 10 * PV_TOL
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_apply_plan_value_column_scales(dtype):
+    """The fp16 value layout scales each value column by its own power of two:
+    columns of size 1e-6, 1 and 1e6 next to each other, and an all-zero one,
+    each come out to the fp32 gate relative to their own size."""
+    n, m, d, eps = 150, 170, 64, 0.1
+    base = "c3_d16_bf16" if dtype == "bf16" else "c3_d16_f32"
+    data = workloads.make(base, n=n, m=m, d=d)
+    prob = make_problem(data, eps=eps)
+    X, Y, a, b = oracle_inputs(prob)
+    C = oracle.cost_matrix(X, Y)
+    f32, g32 = (v.astype(np.float32) for v in oracle.sinkhorn(C, a, b, eps, 20))
+    P = oracle.plan(C, a, b, f32.astype(np.float64), g32.astype(np.float64), eps)
+    rng = np.random.default_rng(5)
+    V = rng.standard_normal((m, 4)) * np.array([1e-6, 1.0, 1e6, 0.0])
+    Vt = torch.from_numpy(V.astype(np.float32)).to(DEV)
+    if dtype == "bf16":
+        Vt = Vt.to(torch.bfloat16)
+    pv = ssa.ot_apply_plan(prob, torch.from_numpy(f32).to(DEV), torch.from_numpy(g32).to(DEV), Vt)
+    torch.cuda.synchronize()
+    ref = oracle.apply_plan(P, host64(Vt))
+    out = host64(pv)
+    for k in range(3):
+        assert _rel(out[:, k], ref[:, k]) <= PV_TOL, k
+    assert np.all(out[:, 3] == 0.0)
 
 
 # --- execution properties ---------------------------------------------------------------
