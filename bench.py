@@ -17,6 +17,9 @@ exponentials and vector work dominate (small d in bf16) -- against the ALU
 bound of the online log-sum-exp in pairs per second. ``cpu_baseline`` times
 the fp64 oracle on a bounded sample of the same workload on the host.
 
+With --graph the timed steps replay the iterations from HIP graphs (no
+per-launch events); the roofline then comes from one extra plain step.
+
 Other modes:
   --gemm-probe       time torch.matmul (hipBLASLt) on random bf16 data at
                      16384^3 and 20000 x 1024 x 20000 and exit: the matrix
@@ -280,6 +283,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB")
     ap.add_argument("--gemm-probe", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the steps with the iterations replayed from HIP graphs (the "
+                         "roofline's per-launch times then come from one extra plain step)")
     ap.add_argument("--schedule", default="alternating", choices=["alternating", "symmetric"])
     ap.add_argument("--native-f32", action="store_true",
                     help="form fp32 scores with the fp32 matrix instruction instead of the "
@@ -340,11 +346,11 @@ def main():
     infos = []
     ws = {}
 
-    def step(record):
+    def step(record, timing=True):
         ssa.ot_sqnorms(X, xs)
         ssa.ot_sqnorms(Y, ys)
         info = ssa.ot_solve(prob, f, g, T, splits_f=args.splits, splits_g=args.splits,
-                            timing=True, ws=ws.get("solve"), schedule=args.schedule)
+                            timing=timing, ws=ws.get("solve"), schedule=args.schedule)
         if w.grad:
             ssa.ot_apply_plan(prob, f, g, flags=ssa.OT_GRAD, out=out_grad, marg=r, ws=ws.get("grad"))
         if w.v_cols:
@@ -365,14 +371,18 @@ def main():
         if w.u_cols:
             ws["ptu"] = ssa.apply_workspace(prob, U, flags=ssa.OT_TRANSPOSE)
         for _ in range(args.warmup):
-            step(False)
+            step(False, not args.graph)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for k in range(args.steps):
-            step(True)
+            step(not args.graph, not args.graph)
             print(f"# step {k + 1}/{args.steps} done", file=sys.stderr, flush=True)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
+        if args.graph:
+            # per-launch events need plain launches: one more step, after the timed ones
+            step(True)
+            torch.cuda.synchronize()
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     value = w.n * w.m * T / ((t1 - t0) / args.steps)
@@ -438,6 +448,8 @@ def main():
                         f"{args.schedule} iterations from zero potentials; outputs: {', '.join(outputs)}",
             "n": w.n, "m": w.m, "d": w.d, "eps": w.eps, "iters": T,
             "splits_f": last["splits_f"], "splits_g": last["splits_g"],
+            "launch_mode": ("HIP graph replay (roofline from one extra plain step)" if args.graph
+                         else "plain launches with HIP events"),
             "operand_mode": ["fp32 MFMA", "bf16 MFMA", "fp32 as 3-part bf16 split on bf16 MFMA",
                              "fp32 as 2-part fp16 split on fp16 MFMA"][last["operand_mode"]],
         },
