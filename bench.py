@@ -60,8 +60,8 @@ ALU_PAIRS_PEAK = ALU_LANE_SLOTS_PER_S / ALU_SLOTS_PER_PAIR
 # FETCH_SIZE / WRITE_SIZE runs (scaled by the copy-kernel calibration), valid
 # only for the kernel source they were taken on.
 TRAFFIC = {
-    "c2": {"kernels_sha256": "8974d1b1a26b13b59e8e9b2680a609029efe6aa4f53773178e2f2a2718748ba9",
-           "bytes_per_launch": 51414951,
+    "c2": {"kernels_sha256": "3a67de960f8c4d542b93d62559e9182d09b274bda88a86d5de914852683e8a2b",
+           "bytes_per_launch": 51400124,
            "source": "profiles/lse_pipe_kernel_c2_n20000_d64_f32half2_hbm_traffic.md"},
 }
 # Sources of the register-resident log-sum-exp kernels the counters describe.
