@@ -47,6 +47,16 @@ def test_sqnorms(dtype, rows, d):
 
 # --- single half-steps (teacher-forced: identical inputs on both sides) -----------
 
+def with_modes(cases):
+    """Each case once per fp32 operand mode for fp32 points; bf16 points have
+    one operand mode (the modes only choose how fp32 values are multiplied)."""
+    out = []
+    for case in cases:
+        modes = F32_MODES if case[3] == "f32" else F32_MODES[:1]
+        out += [(*case, mode) for mode in modes]
+    return out
+
+
 HALF_CASES = [
     # (n, m, d, dtype, eps)
     (333, 517, 16, "f32", 0.1),
@@ -76,11 +86,8 @@ HALF_CASES = [
 
 # fp32 cases run in every fp32 operand mode: resident (d <= 128, LDS-shared
 # columns from d = 64) and the tiled wide pass (d > 128)
-@pytest.mark.parametrize("mode", F32_MODES)
-@pytest.mark.parametrize("n,m,d,dtype,eps", HALF_CASES)
+@pytest.mark.parametrize("n,m,d,dtype,eps,mode", with_modes(HALF_CASES))
 def test_half_steps_teacher_forced(n, m, d, dtype, eps, mode):
-    if mode != "half2" and dtype != "f32":
-        pytest.skip("the fp32 operand options only apply to fp32 points")
     say(f"half-steps n={n} m={m} d={d} dtype={dtype} eps={eps} mode={mode}")
     base = "c3_d16_bf16" if dtype == "bf16" else "c3_d16_f32"
     data = workloads.make(base, n=n, m=m, d=d)
@@ -254,13 +261,10 @@ APPLY_CASES = [
 ]
 
 
-@pytest.mark.parametrize("mode", F32_MODES)
-@pytest.mark.parametrize("n,m,d,dtype,eps,cols", APPLY_CASES)
+@pytest.mark.parametrize("n,m,d,dtype,eps,cols,mode", with_modes(APPLY_CASES))
 def test_apply_plan(n, m, d, dtype, eps, cols, mode):
     """Default operands: scores and value product from fp16 parts (bf16 scores
     for bf16 points); OT_NATIVE_F32 / OT_SPLIT_BF16: the fp32 kernel."""
-    if mode != "half2" and dtype != "f32":
-        pytest.skip("the fp32 operand options only apply to fp32 points")
     say(f"apply n={n} m={m} d={d} dtype={dtype} eps={eps} cols={cols} mode={mode}")
     base = "c3_d16_bf16" if dtype == "bf16" else "c3_d16_f32"
     data = workloads.make(base, n=n, m=m, d=d)
