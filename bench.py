@@ -86,35 +86,76 @@ def traffic_for(workload):
     return rec["bytes_per_launch"]
 
 
-def cpu_baseline(data, budget=1.05e10):
-    """fp64 oracle on a row sample: one f half-step for `rows` rows of X and one
-    g half-step for `rows` columns of Y, reported in n*m*iterations/s.
-    `budget` bounds pairs x d (about 10 s of single-threaded numpy)."""
-    import numpy as np
+# Inputs of the oracle sample, set before the worker pool forks (the workers
+# read them copy-on-write).
+_CPU_JOB = {}
 
+
+def _oracle_chunk(task):
+    """One block of the oracle sample in a worker: f half-step rows or g
+    half-step columns [lo, hi)."""
     import oracle
 
+    side, lo, hi = task
+    j = _CPU_JOB
+    if side == "f":
+        oracle.update_f_rows(j["X"][lo:hi], j["Y"], j["g"], j["b"], j["eps"])
+    else:
+        oracle.update_g_cols(j["X"], j["Y"][lo:hi], j["f"], j["a"], j["eps"])
+    return hi - lo
+
+
+def _noop(_):
+    return 0
+
+
+def host_workers():
+    """CPU threads for the oracle baseline: this process's CPUs, at most 16
+    (the host share of one GPU)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline(data, budget=1.05e10):
+    """fp64 oracle on a row sample of the same workload, one worker process per
+    host CPU: one f half-step for `rows` rows of X and one g half-step for
+    `rows` columns of Y, split into row blocks, reported in n*m*iterations/s.
+    `budget` bounds pairs x d per worker (about 10 s of numpy each).
+
+    Runs before the GPU is first used: the workers are forked from this
+    process and only run numpy."""
+    import multiprocessing
+
+    import numpy as np
+
     w = data["w"]
-    rows = int(max(8, min(w.n, w.m, budget / (w.d * (w.n + w.m)))))
-    X = data["X"].astype(np.float64)
-    Y = data["Y"].astype(np.float64)
-    a = data["a"].astype(np.float64)
-    b = data["b"].astype(np.float64)
-    g = np.zeros(w.m)
-    f = np.zeros(w.n)
-    t0 = time.perf_counter()
-    oracle.update_f_rows(X[:rows], Y, g, b, w.eps)
-    oracle.update_g_cols(X, Y[:rows], f, a, w.eps)
-    dt = time.perf_counter() - t0
+    workers = host_workers()
+    rows = int(max(8, min(w.n, w.m, budget * workers / (w.d * (w.n + w.m)))))
+    _CPU_JOB.update(X=data["X"].astype(np.float64), Y=data["Y"].astype(np.float64),
+                    a=data["a"].astype(np.float64), b=data["b"].astype(np.float64),
+                    f=np.zeros(w.n), g=np.zeros(w.m), eps=w.eps)
+    chunk = max(1, -(-rows // (2 * workers)))
+    tasks = [(side, lo, min(rows, lo + chunk)) for side in ("f", "g") for lo in range(0, rows, chunk)]
+    with multiprocessing.get_context("fork").Pool(workers) as pool:
+        pool.map(_noop, range(workers))  # workers started before the clock
+        t0 = time.perf_counter()
+        done = sum(pool.map(_oracle_chunk, tasks, chunksize=1))
+        dt = time.perf_counter() - t0
+    _CPU_JOB.clear()
+    assert done == 2 * rows
     pairs = rows * w.m + w.n * rows
     return {
         "value": pairs / 2.0 / dt,
         "unit": "n*m*iters/s",
-        "cores": 1,
+        "cores": workers,
         "kind": "oracle",
-        "sample": f"fp64 numpy oracle (single-threaded; host has {os.cpu_count()} CPUs): f half-step "
-                  f"on {rows} rows x {w.m} columns and g half-step on {rows} columns x {w.n} rows of "
-                  f"the same workload ({pairs} pairs, {dt:.1f} s); one iteration = two half-steps",
+        "sample": f"fp64 numpy oracle in {workers} worker processes (one per host CPU; host has "
+                  f"{os.cpu_count()} CPUs): f half-step on {rows} rows x {w.m} columns and g "
+                  f"half-step on {rows} columns x {w.n} rows of the same workload ({pairs} pairs, "
+                  f"{dt:.1f} s); one iteration = two half-steps",
     }
 
 
@@ -315,9 +356,14 @@ def main():
     import streaming_sinkhorn_amd as ssa
     import workloads
 
-    ssa.lib()  # fail loudly before any work if the HIP library is missing
+    if not os.path.exists(ssa.LIB_PATH):
+        ssa.lib()  # raises: fail loudly before any work if the HIP library is missing
     data = workloads.make(args.workload)
     w = data["w"]
+    # The oracle baseline runs first, in worker processes forked before this
+    # process touches the GPU.
+    cpu = None if args.no_cpu_baseline else cpu_baseline(data)
+    ssa.lib()
     T = args.iters or w.iters
     dev = "cuda:0"
     torch.cuda.set_device(0)
@@ -457,8 +503,8 @@ def main():
         "marg_err_row": last["marg_err_row"],
         "marg_err_col": last["marg_err_col"],
     }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(data)
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
 
 
