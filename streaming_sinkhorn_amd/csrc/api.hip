@@ -233,10 +233,10 @@ SolveWs solve_layout(const ot_problem* p, int splits_f, int splits_g) {
   w.o_ny = take((size_t)w.mpad * 4);
   w.o_wx = take((size_t)w.npad * 4);
   w.o_hx = take((size_t)w.npad * 4);
-  w.o_bx = take((size_t)w.npad * 4);
+  w.o_bx = take(bias_buffer_bytes(w.npad));  // biases + bias-MFMA operand (kernels.h)
   w.o_wy = take((size_t)w.mpad * 4);
   w.o_hy = take((size_t)w.mpad * 4);
-  w.o_by = take((size_t)w.mpad * 4);
+  w.o_by = take(bias_buffer_bytes(w.mpad));
   const size_t pf = (size_t)w.F.splits * w.npad, pg = (size_t)w.G.splits * w.mpad;
   w.o_part = take((pf > pg ? pf : pg) * 8);
   w.o_part2 = take(pg * 8);  // g partials of the symmetric schedule (both passes in flight)
@@ -348,8 +348,9 @@ int prepare(const Ctx& x, hipStream_t st) {
 // from f for the symmetric schedule), in the context's current units.
 int rebuild_biases(const Ctx& x, hipStream_t st) {
   const ot_problem* p = x.p;
-  OT_HIP(launch_bias_from_pot(x.g, x.ny, x.hy, (int)p->m, x.L.mpad, x.bscale, x.by, st));
-  if (x.sym) OT_HIP(launch_bias_from_pot(x.f, x.nx, x.hx, (int)p->n, x.L.npad, x.bscale, x.bx, st));
+  OT_HIP(launch_bias_from_pot(x.g, x.ny, x.hy, (int)p->m, x.L.mpad, x.bscale, x.by, 1, st));
+  if (x.sym)
+    OT_HIP(launch_bias_from_pot(x.f, x.nx, x.hx, (int)p->n, x.L.npad, x.bscale, x.bx, 1, st));
   return OT_OK;
 }
 
@@ -578,12 +579,12 @@ int update_impl(const ot_problem* p, const float* other, float* pot, float* err,
   if (rc) return rc;
   const int with_err = err != nullptr;
   if (is_f) {
-    OT_HIP(launch_bias_from_pot(x.g, x.ny, x.hy, (int)p->m, L.mpad, x.bscale, x.by, st));
+    OT_HIP(launch_bias_from_pot(x.g, x.ny, x.hy, (int)p->m, L.mpad, x.bscale, x.by, 1, st));
     rc = half_f(x, st, with_err, 1);
     if (rc) return rc;
     if (with_err) OT_HIP(launch_err_reduce(x.errp, L.errblocks_f, err, st));
   } else {
-    OT_HIP(launch_bias_from_pot(x.f, x.nx, x.hx, (int)p->n, L.npad, x.bscale, x.bx, st));
+    OT_HIP(launch_bias_from_pot(x.f, x.nx, x.hx, (int)p->n, L.npad, x.bscale, x.bx, 1, st));
     rc = half_g(x, st, with_err, 1);
     if (rc) return rc;
     if (with_err) OT_HIP(launch_err_reduce(x.errp + L.errblocks_f, L.errblocks_g, err, st));
@@ -751,7 +752,8 @@ int ot_solve(const ot_problem* p, float* f, float* g, const ot_solve_opts* o,
     }
     if (info) {
       // Exact marginal errors of the returned (f, g): one dry pass per side.
-      if (done == 0) OT_HIP(launch_bias_from_pot(f, x.nx, x.hx, (int)p->n, L.npad, x.bscale, x.bx, st));
+      if (done == 0)
+        OT_HIP(launch_bias_from_pot(f, x.nx, x.hx, (int)p->n, L.npad, x.bscale, x.bx, 1, st));
       rc = half_f(x, st, 1, 0);
       if (rc) return rc;
       OT_HIP(launch_err_reduce(x.errp, L.errblocks_f, x.errv, st));
@@ -920,7 +922,7 @@ int ot_apply_plan(const ot_problem* p, const float* f, const float* g, const voi
     float* po = (float*)(w + L.o_o);
     OT_HIP(launch_weights(wr_user, (int)rows, L.rpad, eps, wr, hr, st));
     OT_HIP(launch_weights(ws_user, (int)srows, L.cpad, eps, wc, hc, st));
-    OT_HIP(launch_bias_from_pot(pot_s, norm_s, hc, (int)srows, L.cpad, h2 ? c : 1.f, bc, st));
+    OT_HIP(launch_bias_from_pot(pot_s, norm_s, hc, (int)srows, L.cpad, h2 ? c : 1.f, bc, 0, st));
     unsigned* vamax = fp16_values ? (unsigned*)(w + L.o_vamax) : nullptr;
     if (fp16_values) {
       OT_HIP(launch_vcol_absmax(V, v_dtype == OT_BF16, srows, cols, ldv, vamax, st));

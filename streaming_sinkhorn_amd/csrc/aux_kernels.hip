@@ -70,6 +70,15 @@ __device__ __forceinline__ float block_sum_256(float v, float* sh) {
 constexpr int kMergeLanes = 8;
 constexpr int kMergeRows = 256 / kMergeLanes;
 
+// Bias-MFMA operand of column i (buffer layout in kernels.h): the parts of
+// its bias in lane i % 32 of its tile, three bf16 ones in lane 32 + i % 32.
+__device__ __forceinline__ void write_bias_parts(float* bias, int rpad, int i, float v) {
+  uint2* parts = reinterpret_cast<uint2*>(bias + rpad);
+  const size_t at = (size_t)(i / kTile) * 64 + (i % kTile);
+  parts[at] = bf16x3_parts(v);
+  parts[at + kTile] = make_uint2(kBf16OnesLo, kBf16OnesHi);
+}
+
 __global__ __launch_bounds__(256) void lse_merge_kernel(
     const float2* __restrict__ part, int splits, int rpad, int rows, float bscale, float eps,
     const float* __restrict__ norm, const float* __restrict__ hlw, const float* __restrict__ wgt,
@@ -108,10 +117,13 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(
     const float pnew = avg ? 0.5f * (pold + half) : half;
     if (write_pot) {
       pot[i] = pnew;
-      bias_out[i] = bscale * (0.5f * (pnew - nrm) + hlw[i]);
+      const float v = bscale * (0.5f * (pnew - nrm) + hlw[i]);
+      bias_out[i] = v;
+      write_bias_parts(bias_out, rpad, i, v);
     }
   } else if (sub == 0 && i < rpad && write_pot) {
     bias_out[i] = kSentinel;
+    write_bias_parts(bias_out, rpad, i, kSentinel);
   }
   if (with_err) {
     const float tot = block_sum_256(e, sh);
@@ -277,14 +289,6 @@ __global__ __launch_bounds__(256) void sqnorms_kernel(const T* __restrict__ pts,
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
   if (lane == 0) out[row] = s;
-}
-
-// bf16 rounding (to nearest, ties to even) of an fp32 value, as bits; NaN
-// stays a quiet NaN.
-__device__ __forceinline__ uint32_t bf16_bits_rne(float v) {
-  const uint32_t u = __float_as_uint(v);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
 // Packs a row-major point cloud into the MFMA operand layout of kernels.h,
@@ -575,10 +579,12 @@ __global__ __launch_bounds__(256) void bias_from_pot_kernel(const float* __restr
                                                              const float* __restrict__ norm,
                                                              const float* __restrict__ hlw,
                                                              int rows, int rpad, float bscale,
-                                                             float* __restrict__ bias) {
+                                                             float* __restrict__ bias, int parts) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= rpad) return;
-  bias[i] = (i < rows) ? bscale * (0.5f * (pot[i] - norm[i]) + hlw[i]) : kSentinel;
+  const float v = (i < rows) ? bscale * (0.5f * (pot[i] - norm[i]) + hlw[i]) : kSentinel;
+  bias[i] = v;
+  if (parts) write_bias_parts(bias, rpad, i, v);
 }
 
 
@@ -690,9 +696,9 @@ hipError_t launch_fill(float* p, float v, int64_t count, hipStream_t st) {
 }
 
 hipError_t launch_bias_from_pot(const float* pot, const float* norm, const float* hlw, int rows,
-                                int rpad, float bscale, float* bias, hipStream_t st) {
+                                int rpad, float bscale, float* bias, int parts, hipStream_t st) {
   bias_from_pot_kernel<<<(rpad + 255) / 256, 256, 0, st>>>(pot, norm, hlw, rows, rpad, bscale,
-                                                           bias);
+                                                           bias, parts);
   return hipGetLastError();
 }
 

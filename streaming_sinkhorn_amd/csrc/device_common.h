@@ -6,6 +6,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace flashot {
@@ -15,6 +17,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // One packed k-block of the score tile: acc[j][i] += sum_k A[j][k] B[k][i].
 template <bool BF16>
@@ -77,6 +80,28 @@ __device__ __forceinline__ f32x16 mfma_half2(const u32x4* y, const u32x4* x, f32
   return m(y[0], x[0], acc); // hi * hi
 }
 
+// Adds bias_j - Mf_i to accumulator entry (j, i) on the bf16 matrix cores
+// (32x32x8, the same 8 passes as the wider bf16 shape, and half the cycles of
+// the fp32 32x32x2 instruction). Each lane supplies four bf16 k-values:
+// a (column side, lane l): lanes < 32 the three bf16 parts of bias_j (j = l)
+// and 0, lanes >= 32 three bf16 ones and 0; b (row side): lanes < 32 three
+// ones and 0, lanes >= 32 the parts of -Mf_i (i = l - 32) and 0. So k-slots
+// 0..2 carry (parts of bias_j, 1) and k-slots 4..6 carry (1, parts of
+// -Mf_i). The parts sum to the fp32 values exactly and the products are exact.
+// Measured on gfx950, this instruction's rounding is biased when it adds onto
+// a nonzero accumulator (mean error about -0.2 ulp at score magnitudes) and
+// unbiased from a zero one, so the passes form bias - stabiliser first and
+// accumulate the score products onto it.
+__device__ __forceinline__ f32x16 mfma_bias_stab(uint2 a, uint2 b, f32x16 acc) {
+  return __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                  __builtin_bit_cast(s16x4, b), acc, 0, 0, 0);
+}
+
+// Row-side operand of mfma_bias_stab for the folded stabiliser Mf.
+__device__ __forceinline__ uint2 stab_operand(float Mf, int h) {
+  return h ? bf16x3_parts(-Mf) : make_uint2(kBf16OnesLo, kBf16OnesHi);
+}
+
 // Adds bias_j to every accumulator entry of column j: k-slot 0 carries
 // (bias_j, 1), k-slot 1 carries (0, 1).
 __device__ __forceinline__ f32x16 mfma_bias(float wv, int h, f32x16 acc) {
@@ -102,9 +127,9 @@ __device__ __forceinline__ float max16(const f32x16& v) {
 // never copied between registers.
 //
 // Lazy stabiliser: the online LSE of App. D.3 is exact for any running
-// stabiliser M, not only for the running maximum. The bias MFMA uses its
-// second k-slot to subtract M_i from every score (A = [bias_j, 1],
-// B = [1, -M_i]), so in the common case a tile costs one exp2 and one add per
+// stabiliser M, not only for the running maximum. The bias MFMA
+// (mfma_bias_stab) also subtracts M_i from every score, so in the common
+// case a tile costs one exp2 and one add per
 // score. Only when a tile could overflow (tile sum >= 2^64), or before M has
 // been set from data, does the wave take the exact path: tile maximum, raise
 // M, rescale S. M is kept identical in the two lanes (l, l ^ 32) that share a
@@ -121,14 +146,58 @@ __device__ __forceinline__ float max16(const f32x16& v) {
 // ---------------------------------------------------------------------------
 constexpr float kUnset = -1.0e30f;  // stabiliser not yet taken from data
 
+// How a pass adds bias_j - Mf_i, per operand mode. The fp32-precision modes
+// (three-part bf16 split, fp32 MFMA) keep the fp32 32x32x2 instruction after
+// the score products, which adds in round-to-nearest without disturbing
+// their smallest-first product order. The default fp16 split and bf16 points
+// start each tile from mfma_bias_stab (bf16 parts, half the cycles).
+template <int MODE>
+constexpr bool f32_bias() { return MODE == kModeSplit || MODE == kModeF32; }
+// Column-side operand: the fp32 bias, or the lane's entry of the parts layout.
+template <int MODE>
+using BiasOp = typename std::conditional<f32_bias<MODE>(), float, uint2>::type;
+
+template <int MODE>
+__device__ __forceinline__ BiasOp<MODE> load_bias(const float* __restrict__ cbias,
+                                                  const uint2* __restrict__ cb3, size_t jt,
+                                                  int lane) {
+  if constexpr (f32_bias<MODE>()) return cbias[jt * kTile + (lane & 31)];
+  else return cb3[jt * 64 + lane];
+}
+// Column-side operand of tiles past the end of the columns: the sentinel bias.
+template <int MODE>
+__device__ __forceinline__ BiasOp<MODE> sentinel_bias(int h) {
+  if constexpr (f32_bias<MODE>()) return kSentinel;
+  else return h ? make_uint2(kBf16OnesLo, kBf16OnesHi) : bf16x3_parts(kSentinel);
+}
+// Row-side operand for the folded stabiliser Mf.
+template <int MODE>
+__device__ __forceinline__ BiasOp<MODE> stab_of(float Mf, int h) {
+  if constexpr (f32_bias<MODE>()) return h ? -Mf : 1.0f;
+  else return stab_operand(Mf, h);
+}
+// Accumulator a tile's score products start from.
+template <int MODE>
+__device__ __forceinline__ f32x16 bias_start(BiasOp<MODE> a, BiasOp<MODE> b) {
+  if constexpr (f32_bias<MODE>()) return f32x16{};
+  else return mfma_bias_stab(a, b, f32x16{});
+}
+// After the products: the fp32 modes add bias_j - Mf_i here (k-slot 0 carries
+// (bias_j, 1), k-slot 1 carries (1, -Mf_i)).
+template <int MODE>
+__device__ __forceinline__ f32x16 bias_finish(BiasOp<MODE> a, BiasOp<MODE> b, int h, f32x16 acc) {
+  if constexpr (f32_bias<MODE>()) return __builtin_amdgcn_mfma_f32_32x32x2f32(h ? 1.0f : a, b, acc, 0, 0, 0);
+  else return acc;
+}
+
 // KB counts 1 KiB operand units per tile: one per k-block for fp32 / bf16,
 // three (hi, mid, lo) per k-block in split mode, two (hi, lo) in half2 mode.
 template <int MODE, int KB, int RI>
 __device__ __forceinline__ void score_tile(const u32x4 (&y)[KB], const u32x4 (&xr)[RI][KB],
-                                           float wv, int h, const float (&Mf)[RI],
+                                           BiasOp<MODE> ab, const BiasOp<MODE> (&Bst)[RI], int h,
                                            f32x16 (&acc)[RI]) {
 #pragma unroll
-  for (int ri = 0; ri < RI; ++ri) acc[ri] = f32x16{};
+  for (int ri = 0; ri < RI; ++ri) acc[ri] = bias_start<MODE>(ab, Bst[ri]);
   if constexpr (MODE == kModeSplit) {
 #pragma unroll
     for (int kb = 0; kb < KB; kb += 3)
@@ -147,13 +216,23 @@ __device__ __forceinline__ void score_tile(const u32x4 (&y)[KB], const u32x4 (&x
         acc[ri] = mfma_kblock<MODE == kModeBF16>(y[kb], xr[ri][kb], acc[ri]);
   }
 #pragma unroll
-  for (int ri = 0; ri < RI; ++ri)
-    acc[ri] = __builtin_amdgcn_mfma_f32_32x32x2f32(h ? 1.0f : wv, h ? -Mf[ri] : 1.0f, acc[ri],
-                                                   0, 0, 0);
+  for (int ri = 0; ri < RI; ++ri) acc[ri] = bias_finish<MODE>(ab, Bst[ri], h, acc[ri]);
 }
 
 // Stabiliser folded into the next tile's scores: the running M once set.
 __device__ __forceinline__ float fold_of(float M) { return M > 0.5f * kUnset ? M : 0.f; }
+
+// After M may have moved (the exact path): the folded stabiliser of the next
+// tiles and its row-side bias operand.
+template <int MODE, int RI>
+__device__ __forceinline__ void refold(const float (&M)[RI], int h, float (&Mfc)[RI],
+                                       BiasOp<MODE> (&Bst)[RI]) {
+#pragma unroll
+  for (int ri = 0; ri < RI; ++ri) {
+    Mfc[ri] = fold_of(M[ri]);
+    Bst[ri] = stab_of<MODE>(Mfc[ri], h);
+  }
+}
 
 // Common-case tile: s = sum exp2(ks * a_r) relative to the folded Mf; returns
 // the candidate new S and whether the exact path is needed.
@@ -180,19 +259,25 @@ __device__ __forceinline__ bool lse_fast(const f32x16& a, float Mf, float M, flo
 }
 
 // Exact tile: raise M to the tile maximum (shared by the lane pair), rescale.
+// The maximum is taken over the scores u = a + Mf as rounded, and every
+// exponent is u - m of those same values: it is <= 0, and exactly 0 at the
+// maximum, however large |u| is (writing it as a + (Mf - m) instead lets
+// rounding push the maximum's exponent far from 0 once |scores| reach fp32's
+// integer range). A NaN score still reaches S.
 __device__ __forceinline__ void lse_exact(const f32x16& a, float Mf, float& M, float& S,
                                           float ks) {
-  float m = max16(a) + Mf;
+  float m = a[0] + Mf;
+#pragma unroll
+  for (int r = 1; r < 16; ++r) m = fmaxf(m, a[r] + Mf);
   m = fmaxf(m, __shfl_xor(m, 32));
   m = fmaxf(m, M);
-  const float t = Mf - m;
   float e0 = 0.f, e1 = 0.f, e2 = 0.f, e3 = 0.f;
 #pragma unroll
   for (int r = 0; r < 16; r += 4) {
-    e0 += __builtin_amdgcn_exp2f(ks * (a[r + 0] + t));
-    e1 += __builtin_amdgcn_exp2f(ks * (a[r + 1] + t));
-    e2 += __builtin_amdgcn_exp2f(ks * (a[r + 2] + t));
-    e3 += __builtin_amdgcn_exp2f(ks * (a[r + 3] + t));
+    e0 += __builtin_amdgcn_exp2f(ks * ((a[r + 0] + Mf) - m));
+    e1 += __builtin_amdgcn_exp2f(ks * ((a[r + 1] + Mf) - m));
+    e2 += __builtin_amdgcn_exp2f(ks * ((a[r + 2] + Mf) - m));
+    e3 += __builtin_amdgcn_exp2f(ks * ((a[r + 3] + Mf) - m));
   }
   S = fmaf(S, __builtin_amdgcn_exp2f(ks * (M - m)), (e0 + e1) + (e2 + e3));
   M = m;
@@ -263,14 +348,16 @@ __device__ __forceinline__ bool lse_fast_v(const f32x16& a, const f32x16& v, flo
 
 __device__ __forceinline__ void lse_exact_v(const f32x16& a, const f32x16& v, float Mf, float& M,
                                             float& S, float& T, float ks) {
-  float m = max16(a) + Mf;
+  // the same exponents as lse_exact
+  float m = a[0] + Mf;
+#pragma unroll
+  for (int r = 1; r < 16; ++r) m = fmaxf(m, a[r] + Mf);
   m = fmaxf(m, __shfl_xor(m, 32));
   m = fmaxf(m, M);
-  const float t = Mf - m;
   float e = 0.f, tv = 0.f;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const float x = __builtin_amdgcn_exp2f(ks * (a[r] + t));
+    const float x = __builtin_amdgcn_exp2f(ks * ((a[r] + Mf) - m));
     e += x;
     tv = fmaf(x, v[r], tv);
   }

@@ -130,8 +130,8 @@ int prepare_transport(const Transport& t, const float* A, int64_t lda, hipStream
   if (A) OT_HIP(launch_pack_points(A, 0, p->n, p->d, lda, L.ntiles, L.k.kbp, 1.f, t.ap, st));
   OT_HIP(launch_weights(p->a, (int)p->n, L.npad, t.eps, t.wx, t.hx, st));
   OT_HIP(launch_weights(p->b, (int)p->m, L.mpad, t.eps, t.wy, t.hy, st));
-  OT_HIP(launch_bias_from_pot(t.g, t.ny, t.hy, (int)p->m, L.mpad, 1.f, t.by, st));
-  OT_HIP(launch_bias_from_pot(t.f, t.nx, t.hx, (int)p->n, L.npad, 1.f, t.bx, st));
+  OT_HIP(launch_bias_from_pot(t.g, t.ny, t.hy, (int)p->m, L.mpad, 1.f, t.by, 0, st));
+  OT_HIP(launch_bias_from_pot(t.f, t.nx, t.hx, (int)p->n, L.npad, 1.f, t.bx, 0, st));
   return OT_OK;
 }
 
@@ -246,8 +246,8 @@ HvpWs hvp_layout(const ot_problem* p) {
     v.G = make_pass(mt, nt, v.k, v.k.ri, 0, 4096);
     v.o_xs = take((size_t)nt * v.k.kbp * 1024);
     v.o_ys = take((size_t)mt * v.k.kbp * 1024);
-    v.o_bx = take((size_t)w.T.npad * 4);
-    v.o_by = take((size_t)w.T.mpad * 4);
+    v.o_bx = take(bias_buffer_bytes(w.T.npad));  // feed log-sum-exp passes: with the
+    v.o_by = take(bias_buffer_bytes(w.T.mpad));  // bias-MFMA operand (kernels.h)
     const size_t pf = (size_t)v.F.splits * w.T.npad, pg = (size_t)v.G.splits * w.T.mpad;
     const size_t pm = pf > pg ? pf : pg;
     v.o_part = take(pm * 8);
@@ -285,8 +285,8 @@ int prepare_vec(const Transport& t, const VecWs& v, char* w, hipStream_t st) {
     OT_HIP(launch_pack_points(p->x, 0, p->n, p->d, p->ldx, L.ntiles, v.k.kbp, t.c, xs, st));
     OT_HIP(launch_pack_points(p->y, 0, p->m, p->d, p->ldy, L.mtiles, v.k.kbp, 1.f, ys, st));
   }
-  OT_HIP(launch_bias_from_pot(t.g, t.ny, t.hy, (int)p->m, L.mpad, t.c, (float*)(w + v.o_by), st));
-  OT_HIP(launch_bias_from_pot(t.f, t.nx, t.hx, (int)p->n, L.npad, t.c, (float*)(w + v.o_bx), st));
+  OT_HIP(launch_bias_from_pot(t.g, t.ny, t.hy, (int)p->m, L.mpad, t.c, (float*)(w + v.o_by), 1, st));
+  OT_HIP(launch_bias_from_pot(t.f, t.nx, t.hx, (int)p->n, L.npad, t.c, (float*)(w + v.o_bx), 1, st));
   return OT_OK;
 }
 

@@ -100,8 +100,42 @@ hipError_t launch_pack_values(const void* V, int bf16, int64_t rows, int64_t col
 hipError_t launch_weights(const float* w, int rows, int rpad, float eps, float* wgt, float* hlw,
                           hipStream_t st);
 hipError_t launch_fill(float* p, float v, int64_t count, hipStream_t st);
+// Column-bias buffers of the log-sum-exp passes hold rpad fp32 biases followed
+// by the operand of the bias MFMA: per 32-column tile, 64 entries of 8 bytes
+// (one per lane). Entry l < 32 holds the three bf16 parts of the bias of
+// column l of the tile (bits: part1 | part2 << 16, part3); entries 32..63
+// hold three bf16 ones. A buffer that feeds only transport applications
+// needs the fp32 biases alone.
+inline size_t bias_buffer_bytes(int rpad) { return (size_t)rpad * 4 + (size_t)(rpad / kTile) * 512; }
+__host__ __device__ inline const uint2* bias_parts(const float* bias, int rpad) {
+  return reinterpret_cast<const uint2*>(bias + rpad);
+}
+constexpr uint32_t kBf16OnesLo = 0x3F803F80u;  // bf16 1.0, 1.0
+constexpr uint32_t kBf16OnesHi = 0x00003F80u;  // bf16 1.0, 0
+// bf16 rounding (to nearest, ties to even) of an fp32 value, as bits; NaN
+// stays a quiet NaN.
+__device__ __forceinline__ uint32_t bf16_bits_rne(float v) {
+  const uint32_t u = __float_as_uint(v);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+// v as three bf16 parts p1 + p2 + p3 (each the rounding of what the previous
+// ones left); for normal fp32 v the sum is exact. Packed as (p1 | p2 << 16, p3).
+// No contraction: a product that produced v must not be fused into the first
+// remainder, or the parts would describe the unrounded product instead of the
+// stored v (and differ between kernels that compute v the same way).
+__device__ __forceinline__ uint2 bf16x3_parts(float v) {
+#pragma clang fp contract(off)
+  const uint32_t b1 = bf16_bits_rne(v);
+  const float r1 = v - __uint_as_float(b1 << 16);
+  const uint32_t b2 = bf16_bits_rne(r1);
+  const float r2 = r1 - __uint_as_float(b2 << 16);
+  return make_uint2(b1 | (b2 << 16), bf16_bits_rne(r2));
+}
+// parts = 1: also write the bias-MFMA operand after the rpad biases (the
+// buffer then has bias_buffer_bytes(rpad) bytes).
 hipError_t launch_bias_from_pot(const float* pot, const float* norm, const float* hlw, int rows,
-                                int rpad, float bscale, float* bias, hipStream_t st);
+                                int rpad, float bscale, float* bias, int parts, hipStream_t st);
 // mode: 0 fp32 operands, 1 bf16 operands, 2 fp32 operands packed as three bf16 parts,
 // 3 fp32 operands packed as two fp16 parts.
 // Register-resident passes (s.xres, kernels.hip) and k-chunked wide passes (kernels_wide.hip).
@@ -122,7 +156,8 @@ inline hipError_t launch_lse_partial(const PassShape& s, int mode, const void* R
                 : launch_lse_wide(s, mode, Rp, Cp, cbias, c, part, st);
 }
 // avg = 1: symmetric schedule, the new potential is the average of the old
-// one and the half-step value.
+// one and the half-step value. With write_pot, bias_out receives the biases
+// and the bias-MFMA operand (bias_buffer_bytes(rpad) bytes).
 hipError_t launch_lse_merge(const float2* part, int splits, int rpad, int rows, float bscale, float eps,
                             const float* norm, const float* hlw, const float* wgt, float* pot,
                             float* bias_out, float* err_part, int with_err, int write_pot,

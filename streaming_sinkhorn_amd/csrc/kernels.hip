@@ -15,9 +15,11 @@
 //    ONE output row (i = l % 32), so the online LSE is lane-local: no
 //    cross-lane traffic inside the column loop, one exchange with lane
 //    l ^ 32 at the very end;
-//  * one extra fp32 MFMA adds the per-column bias and subtracts the row's
-//    running stabiliser (A = [bias_j, 1], B = [1, -M_i]), so the common-case
-//    score costs one exp2 and one add on the vector unit;
+//  * one extra bf16 MFMA adds the per-column bias and subtracts the row's
+//    running stabiliser, both as three exact bf16 parts (the column side's
+//    parts are written next to the biases; the row side's are rebuilt only
+//    when the stabiliser moves), so the common-case score costs one exp2
+//    and one add on the vector unit;
 //  * fp32 points are formed on the fp16 matrix cores from two fp16 parts per
 //    value (device_common.h), on request on the bf16 matrix cores from three
 //    bf16 parts or with fp32 MFMA; bf16 points directly;
@@ -41,11 +43,12 @@
 
 namespace flashot {
 
-template <int KB>
+template <int MODE, int KB>
 __device__ __forceinline__ void load_ctile(const u32x4* __restrict__ Cp,
-                                           const float* __restrict__ cbias, int jt, int lane,
-                                           u32x4 (&y)[KB], float& w) {
-  w = cbias[jt * kTile + (lane & 31)];
+                                           const float* __restrict__ cbias,
+                                           const uint2* __restrict__ cb3, int jt, int lane,
+                                           u32x4 (&y)[KB], BiasOp<MODE>& ab) {
+  ab = load_bias<MODE>(cbias, cb3, jt, lane);
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) y[kb] = Cp[((size_t)jt * KB + kb) * 64 + lane];
 }
@@ -76,16 +79,19 @@ __device__ __forceinline__ void stage_schedule() {
 template <int MODE, int KB, int RI, bool VEC>
 __device__ __forceinline__ void pipe_stage(const u32x4* __restrict__ Cp,
                                            const float* __restrict__ cbias,
+                                           const uint2* __restrict__ cb3,
                                            const float* __restrict__ vcol, int jt_refill,
                                            int jt_vals, int lane, int h, float ks,
-                                           const u32x4 (&xr)[RI][KB], u32x4 (&yN)[KB], float& wN,
+                                           const u32x4 (&xr)[RI][KB], u32x4 (&yN)[KB],
+                                           BiasOp<MODE>& aN,
                                            f32x16 (&accN)[RI], float (&MfN)[RI],
                                            const f32x16 (&accC)[RI], const float (&MfC)[RI],
                                            f32x16& vN, const f32x16& vC, float (&M)[RI],
-                                           float (&S)[RI], float (&T)[RI]) {
+                                           float (&S)[RI], float (&T)[RI], float (&Mfc)[RI],
+                                           BiasOp<MODE> (&Bst)[RI]) {
 #pragma unroll
-  for (int ri = 0; ri < RI; ++ri) MfN[ri] = fold_of(M[ri]);
-  score_tile<MODE, KB, RI>(yN, xr, wN, h, MfN, accN);
+  for (int ri = 0; ri < RI; ++ri) MfN[ri] = Mfc[ri];
+  score_tile<MODE, KB, RI>(yN, xr, aN, Bst, h, accN);
   // The fast-path sums are taken unconditionally (the rare exact path restores
   // the old ones): no row's work becomes conditional on another's, so the
   // stage stays one scheduling region in which the exponentials of tile k
@@ -103,7 +109,7 @@ __device__ __forceinline__ void pipe_stage(const u32x4* __restrict__ Cp,
       slow |= lse_fast<MODE != kModeBF16>(accC[ri], MfC[ri], M[ri], So[ri], ks, S[ri]);
     }
   }
-  load_ctile<KB>(Cp, cbias, jt_refill, lane, yN, wN);
+  load_ctile<MODE, KB>(Cp, cbias, cb3, jt_refill, lane, yN, aN);
   if constexpr (VEC) vN = load_tile_values(vcol, jt_vals, h);
   stage_schedule<MODE, KB, RI>();
   __builtin_amdgcn_sched_barrier(0);
@@ -118,6 +124,7 @@ __device__ __forceinline__ void pipe_stage(const u32x4* __restrict__ Cp,
         lse_exact(accC[ri], MfC[ri], M[ri], S[ri], ks);
       }
     }
+    refold<MODE, RI>(M, h, Mfc, Bst);
   }
 }
 
@@ -165,6 +172,7 @@ __global__ __launch_bounds__(256) void lse_pipe_kernel(
   const int jt0 = s * tps;
   const int last = min(jt0 + tps, ctiles) - 1 - jt0;  // split holds tiles 0..last, last >= 0
   const float ks = MODE == kModeBF16 ? c : 1.0f;
+  const uint2* __restrict__ cb3 = bias_parts(cbias, ctiles * kTile);
 
   u32x4 xr[RI][KB];
 #pragma unroll
@@ -173,41 +181,44 @@ __global__ __launch_bounds__(256) void lse_pipe_kernel(
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) xr[ri][kb] = Rp[((size_t)rt * KB + kb) * 64 + lane];
   }
-  float M[RI], S[RI], T[RI];
+  float M[RI], S[RI], T[RI], Mfc[RI];
+  BiasOp<MODE> Bst[RI];
 #pragma unroll
   for (int ri = 0; ri < RI; ++ri) {
     M[ri] = kUnset;
     S[ri] = 0.f;
     T[ri] = 0.f;
   }
+  refold<MODE, RI>(M, h, Mfc, Bst);
 
   // Invariant at the top of the loop: accA holds the scores of tile k (with
   // MfA folded in), yB holds (or is loading) tile k+1 and yA tile k+2;
   // indices past the split's last tile are clamped to it (loaded, never
   // reduced).
   u32x4 yA[KB], yB[KB];
-  float wA, wB;
+  BiasOp<MODE> aA, aB;
   f32x16 accA[RI], accB[RI], vA{}, vB{};
   float MfA[RI], MfB[RI];
-  load_ctile<KB>(Cp, cbias, jt0, lane, yA, wA);
-  load_ctile<KB>(Cp, cbias, jt0 + min(1, last), lane, yB, wB);
+  load_ctile<MODE, KB>(Cp, cbias, cb3, jt0, lane, yA, aA);
+  load_ctile<MODE, KB>(Cp, cbias, cb3, jt0 + min(1, last), lane, yB, aB);
 #pragma unroll
-  for (int ri = 0; ri < RI; ++ri) MfA[ri] = 0.f;
-  score_tile<MODE, KB, RI>(yA, xr, wA, h, MfA, accA);
+  for (int ri = 0; ri < RI; ++ri) MfA[ri] = Mfc[ri];
+  score_tile<MODE, KB, RI>(yA, xr, aA, Bst, h, accA);
   if constexpr (VEC) vA = load_tile_values(vcol, jt0, h);
-  load_ctile<KB>(Cp, cbias, jt0 + min(2, last), lane, yA, wA);
+  load_ctile<MODE, KB>(Cp, cbias, cb3, jt0 + min(2, last), lane, yA, aA);
   int k = 0;
   for (; k + 2 <= last; k += 2) {
-    pipe_stage<MODE, KB, RI, VEC>(Cp, cbias, vcol, jt0 + min(k + 3, last), jt0 + k + 1, lane, h,
-                                  ks, xr, yB, wB, accB, MfB, accA, MfA, vB, vA, M, S, T);
-    pipe_stage<MODE, KB, RI, VEC>(Cp, cbias, vcol, jt0 + min(k + 4, last), jt0 + k + 2, lane, h,
-                                  ks, xr, yA, wA, accA, MfA, accB, MfB, vA, vB, M, S, T);
+    pipe_stage<MODE, KB, RI, VEC>(Cp, cbias, cb3, vcol, jt0 + min(k + 3, last), jt0 + k + 1, lane, h,
+                                  ks, xr, yB, aB, accB, MfB, accA, MfA, vB, vA, M, S, T, Mfc, Bst);
+    pipe_stage<MODE, KB, RI, VEC>(Cp, cbias, cb3, vcol, jt0 + min(k + 4, last), jt0 + k + 2, lane, h,
+                                  ks, xr, yA, aA, accA, MfA, accB, MfB, vA, vB, M, S, T, Mfc, Bst);
   }
   if (k + 1 <= last) {  // tiles k and k+1 remain
     tail_any<MODE, RI, VEC>(accA, vA, MfA, M, S, T, ks);
+    refold<MODE, RI>(M, h, Mfc, Bst);
 #pragma unroll
-    for (int ri = 0; ri < RI; ++ri) MfB[ri] = fold_of(M[ri]);
-    score_tile<MODE, KB, RI>(yB, xr, wB, h, MfB, accB);
+    for (int ri = 0; ri < RI; ++ri) MfB[ri] = Mfc[ri];
+    score_tile<MODE, KB, RI>(yB, xr, aB, Bst, h, accB);
     if constexpr (VEC) vB = load_tile_values(vcol, jt0 + k + 1, h);
     tail_any<MODE, RI, VEC>(accB, vB, MfB, M, S, T, ks);
   } else {  // tile k remains
@@ -250,10 +261,11 @@ __device__ __forceinline__ void stage_store(u32x4* __restrict__ buf, int tid,
 
 template <int MODE, int KB, int RI>
 __device__ __forceinline__ void score_tile_lds(const u32x4* __restrict__ buf, int lane,
-                                               const u32x4 (&xr)[RI][KB], float wv, int h,
-                                               const float (&Mf)[RI], f32x16 (&acc)[RI]) {
+                                               const u32x4 (&xr)[RI][KB], BiasOp<MODE> ab,
+                                               const BiasOp<MODE> (&Bst)[RI], int h,
+                                               f32x16 (&acc)[RI]) {
 #pragma unroll
-  for (int ri = 0; ri < RI; ++ri) acc[ri] = f32x16{};
+  for (int ri = 0; ri < RI; ++ri) acc[ri] = bias_start<MODE>(ab, Bst[ri]);
   if constexpr (MODE == kModeSplit) {
 #pragma unroll
     for (int kb = 0; kb < KB; kb += 3) {
@@ -282,9 +294,7 @@ __device__ __forceinline__ void score_tile_lds(const u32x4* __restrict__ buf, in
     }
   }
 #pragma unroll
-  for (int ri = 0; ri < RI; ++ri)
-    acc[ri] = __builtin_amdgcn_mfma_f32_32x32x2f32(h ? 1.0f : wv, h ? -Mf[ri] : 1.0f, acc[ri],
-                                                   0, 0, 0);
+  for (int ri = 0; ri < RI; ++ri) acc[ri] = bias_finish<MODE>(ab, Bst[ri], h, acc[ri]);
 }
 
 template <int MODE, int KB, int RI>
@@ -321,6 +331,7 @@ __global__ __launch_bounds__(256) void lse_lds_kernel(
   const int jt0 = s * tps;
   const int last = min(jt0 + tps, ctiles) - 1 - jt0;
   const float ks = MODE == kModeBF16 ? c : 1.0f;
+  const uint2* __restrict__ cb3 = bias_parts(cbias, ctiles * kTile);
 
   u32x4 xr[RI][KB];
 #pragma unroll
@@ -329,21 +340,23 @@ __global__ __launch_bounds__(256) void lse_lds_kernel(
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) xr[ri][kb] = Rp[((size_t)rt * KB + kb) * 64 + lane];
   }
-  float M[RI], S[RI], T[RI];
+  float M[RI], S[RI], T[RI], Mfc[RI];
+  BiasOp<MODE> Bst[RI];
 #pragma unroll
   for (int ri = 0; ri < RI; ++ri) {
     M[ri] = kUnset;
     S[ri] = 0.f;
     T[ri] = 0.f;
   }
+  refold<MODE, RI>(M, h, Mfc, Bst);
 
   u32x4 g[kLoads];
   stage_load<KB>(Cp, jt0, tid, g);
   stage_store<KB>(lds[0], tid, g);
   stage_load<KB>(Cp, jt0 + min(1, last), tid, g);
   stage_store<KB>(lds[1], tid, g);
-  float wA = cbias[jt0 * kTile + (lane & 31)];
-  float wB = cbias[(jt0 + min(1, last)) * kTile + (lane & 31)];
+  BiasOp<MODE> aA = load_bias<MODE>(cbias, cb3, jt0, lane);
+  BiasOp<MODE> aB = load_bias<MODE>(cbias, cb3, jt0 + min(1, last), lane);
   __syncthreads();
 
   // Invariant at stage k: accA / accB alternate holding the scores of tile k;
@@ -352,19 +365,20 @@ __global__ __launch_bounds__(256) void lse_lds_kernel(
   f32x16 accA[RI], accB[RI], vA{}, vB{};
   float MfA[RI], MfB[RI];
 #pragma unroll
-  for (int ri = 0; ri < RI; ++ri) MfA[ri] = 0.f;
-  score_tile_lds<MODE, KB, RI>(lds[0], lane, xr, wA, h, MfA, accA);
+  for (int ri = 0; ri < RI; ++ri) MfA[ri] = Mfc[ri];
+  score_tile_lds<MODE, KB, RI>(lds[0], lane, xr, aA, Bst, h, accA);
   if constexpr (VEC) vA = load_tile_values(vcol, jt0, h);
 
-  auto stage = [&](int k, f32x16(&accN)[RI], float(&MfN)[RI], float& wN, const f32x16(&accC)[RI],
-                   const float(&MfC)[RI], float& wC, f32x16& vN, const f32x16& vC) {
+  auto stage = [&](int k, f32x16(&accN)[RI], float(&MfN)[RI], BiasOp<MODE>& aN,
+                   const f32x16(&accC)[RI], const float(&MfC)[RI], BiasOp<MODE>& aC, f32x16& vN,
+                   const f32x16& vC) {
     __syncthreads();  // tile k+1 is in LDS; every wave is done reading tile k's buffer
     const int jt2 = jt0 + min(k + 2, last);
     stage_load<KB>(Cp, jt2, tid, g);
-    const float w2 = cbias[jt2 * kTile + (lane & 31)];
+    const BiasOp<MODE> a2 = load_bias<MODE>(cbias, cb3, jt2, lane);
 #pragma unroll
-    for (int ri = 0; ri < RI; ++ri) MfN[ri] = fold_of(M[ri]);
-    score_tile_lds<MODE, KB, RI>(lds[(k + 1) & 1], lane, xr, wN, h, MfN, accN);
+    for (int ri = 0; ri < RI; ++ri) MfN[ri] = Mfc[ri];
+    score_tile_lds<MODE, KB, RI>(lds[(k + 1) & 1], lane, xr, aN, Bst, h, accN);
     // fast-path sums taken unconditionally (see pipe_stage)
     float So[RI], To[RI];
     int slow = 0;
@@ -381,7 +395,7 @@ __global__ __launch_bounds__(256) void lse_lds_kernel(
     }
     if constexpr (VEC) vN = load_tile_values(vcol, jt0 + k + 1, h);
     stage_store<KB>(lds[k & 1], tid, g);
-    wC = w2;  // the buffer of tile k now receives tile k+2
+    aC = a2;  // the buffer of tile k now receives tile k+2
     stage_schedule_lds<MODE, KB, RI>();
     __builtin_amdgcn_sched_barrier(0);
     if (__builtin_amdgcn_ballot_w64(slow) != 0) {
@@ -395,19 +409,20 @@ __global__ __launch_bounds__(256) void lse_lds_kernel(
           lse_exact(accC[ri], MfC[ri], M[ri], S[ri], ks);
         }
       }
+      refold<MODE, RI>(M, h, Mfc, Bst);
     }
   };
 
   int k = 0;
   for (; k + 2 <= last; k += 2) {
-    stage(k, accB, MfB, wB, accA, MfA, wA, vB, vA);
-    stage(k + 1, accA, MfA, wA, accB, MfB, wB, vA, vB);
+    stage(k, accB, MfB, aB, accA, MfA, aA, vB, vA);
+    stage(k + 1, accA, MfA, aA, accB, MfB, aB, vA, vB);
   }
   if (k + 1 <= last) {  // tiles k and k+1 remain; tile k+1 is in buffer (k+1)&1
     __syncthreads();
 #pragma unroll
-    for (int ri = 0; ri < RI; ++ri) MfB[ri] = fold_of(M[ri]);
-    score_tile_lds<MODE, KB, RI>(lds[(k + 1) & 1], lane, xr, wB, h, MfB, accB);
+    for (int ri = 0; ri < RI; ++ri) MfB[ri] = Mfc[ri];  // M has not moved since the last refold
+    score_tile_lds<MODE, KB, RI>(lds[(k + 1) & 1], lane, xr, aB, Bst, h, accB);
     if constexpr (VEC) vB = load_tile_values(vcol, jt0 + k + 1, h);
     tail_any<MODE, RI, VEC>(accA, vA, MfA, M, S, T, ks);
     tail_any<MODE, RI, VEC>(accB, vB, MfB, M, S, T, ks);

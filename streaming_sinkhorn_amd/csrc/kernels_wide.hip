@@ -23,9 +23,10 @@ namespace flashot {
 // wave loads the slice of its own row tiles straight into registers (two
 // register sets, each refilled right after the stage that read it), so LDS
 // carries only the shared operand. A wave's RT + CT fragments feed RT * CT
-// MFMA tiles. After a block's last stage the bias MFMA folds in
-// bias_j - M_i and the online LSE (lazy stabiliser, device_common.h)
-// consumes the RT x CT tiles.
+// MFMA tiles. bias_j - M_i enters by one MFMA per tile: at the block's start
+// (bf16 parts) or, in the fp32-precision modes, after its last stage (fp32).
+// Then the online LSE (lazy stabiliser, device_common.h) consumes the RT x CT
+// tiles.
 // Units: 1 KiB operand units of the packed layout; KU units per k-block
 // (3 in split mode, 2 in half2 mode), kbp units per tile, padded to whole
 // stages.
@@ -69,6 +70,8 @@ __global__ __launch_bounds__(256) void lse_wide_kernel(
   const int nstages = kbp / SU;             // per column block
   const int total = nb * nstages;
   const float ks = MODE == kModeBF16 ? c : 1.0f;
+  const uint2* __restrict__ cb3 = bias_parts(cbias, ctiles * kTile);
+  const BiasOp<MODE> sent = sentinel_bias<MODE>(h);
 
   // Column staging slots of this thread: column tile cq of the current block,
   // unit offset uo within the stage.
@@ -151,11 +154,26 @@ __global__ __launch_bounds__(256) void lse_wide_kernel(
 
   int step = 0;  // even at the top of every stage pair
   for (int bi = 0; bi < nb; ++bi) {
+    // bias minus stabiliser first (from zero; see mfma_bias_stab), then the
+    // block's score products accumulate onto it. M moves only in the LSE
+    // after the block, so the fold taken here is the one the block uses.
+    const int blk = b0 + bi;
+    float Mf[RT];
+    BiasOp<MODE> Bst[RT], aq[CT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      Mf[r] = fold_of(M[r]);
+      Bst[r] = stab_of<MODE>(Mf[r], h);
+    }
     f32x16 acc[RT][CT];
 #pragma unroll
-    for (int r = 0; r < RT; ++r)
+    for (int q = 0; q < CT; ++q) {
+      const int jt = blk * CT + q;
+      const BiasOp<MODE> a = load_bias<MODE>(cbias, cb3, min(jt, ctiles - 1), lane);
+      aq[q] = jt < ctiles ? a : sent;  // tiles past the end: sentinel bias
 #pragma unroll
-      for (int q = 0; q < CT; ++q) acc[r][q] = f32x16{};
+      for (int r = 0; r < RT; ++r) acc[r][q] = bias_start<MODE>(aq[q], Bst[r]);
+    }
     for (int st = 0; st < nstages; st += 2, step += 2) {
       // stage `step`: columns in lds[0], rows in xA; gB / xB hold stage step + 1
       gload(step + 2, gA);
@@ -170,21 +188,11 @@ __global__ __launch_bounds__(256) void lse_wide_kernel(
       sstore(lds[0], gA);  // after the final stage nobody reads these stores
       __syncthreads();
     }
-    // Block complete: bias minus stabiliser, then the online LSE.
-    const int blk = b0 + bi;
-    float Mf[RT];
+    // Block complete: the fp32 modes' bias instruction, then the online LSE.
 #pragma unroll
-    for (int r = 0; r < RT; ++r) Mf[r] = fold_of(M[r]);
+    for (int q = 0; q < CT; ++q)
 #pragma unroll
-    for (int q = 0; q < CT; ++q) {
-      const int jt = blk * CT + q;
-      const float w = cbias[min(jt, ctiles - 1) * kTile + (lane & 31)];
-      const float wq = jt < ctiles ? w : kSentinel;
-#pragma unroll
-      for (int r = 0; r < RT; ++r)
-        acc[r][q] = __builtin_amdgcn_mfma_f32_32x32x2f32(h ? 1.0f : wq, h ? -Mf[r] : 1.0f,
-                                                         acc[r][q], 0, 0, 0);
-    }
+      for (int r = 0; r < RT; ++r) acc[r][q] = bias_finish<MODE>(aq[q], Bst[r], h, acc[r][q]);
 #pragma unroll
     for (int q = 0; q < CT; ++q) {
       f32x16 col[RT];
