@@ -60,8 +60,8 @@ ALU_PAIRS_PEAK = ALU_LANE_SLOTS_PER_S / ALU_SLOTS_PER_PAIR
 # FETCH_SIZE / WRITE_SIZE runs (scaled by the copy-kernel calibration), valid
 # only for the kernel source they were taken on.
 TRAFFIC = {
-    "c2": {"kernels_sha256": "3a67de960f8c4d542b93d62559e9182d09b274bda88a86d5de914852683e8a2b",
-           "bytes_per_launch": 51400124,
+    "c2": {"kernels_sha256": "4c6ff96ef1ae25059b83cbf604dfd486e0096889c954b339cba04a0cb8b4876e",
+           "bytes_per_launch": 51683968,
            "source": "profiles/lse_pipe_kernel_c2_n20000_d64_f32half2_hbm_traffic.md"},
 }
 # Sources of the register-resident log-sum-exp kernels the counters describe.
