@@ -354,6 +354,32 @@ def test_deterministic_graph_eager_and_resume():
     assert torch.equal(f, outs[0][0]) and torch.equal(g, outs[0][1])
 
 
+def test_constant_mode_drift_and_rest_of_error():
+    """Potentials after 100 iterations (n = m = 2000, the 20000-point workload's
+    distributions) against the fp64 oracle, split into the drift along the
+    constant direction (f + k, g - k), which leaves the coupling unchanged and
+    along which any rounding bias of the score arithmetic accumulates
+    (eigenvalue 1), and the rest of the error. Measured on gfx950: drift
+    3.3e-6, rest 4.0e-7; a bias instruction adding onto a nonzero accumulator
+    (rounding biased by about -0.2 ulp) had drifted 6.6e-6."""
+    say("constant-mode drift n=m=2000")
+    data = workloads.make("c2", n=2000, m=2000)
+    prob = make_problem(data)
+    X, Y, a, b = oracle_inputs(prob)
+    f, g = zeros(2000), zeros(2000)
+    ssa.ot_solve(prob, f, g, 100, want_info=False)
+    torch.cuda.synchronize()
+    f_ref, g_ref = oracle.sinkhorn(oracle.cost_matrix(X, Y), a, b, data["w"].eps, 100)
+    df = host64(f) - f_ref
+    dg = host64(g) - g_ref
+    drift = 0.5 * (df.mean() - dg.mean())
+    rest = max(np.abs(df - df.mean()).max(), np.abs(dg - dg.mean()).max())
+    say(f"  drift {drift:.2e}, rest {rest:.2e}")
+    assert abs(drift) <= 5e-6
+    assert rest <= 1e-6
+    assert abs(df.mean() + dg.mean()) <= 1e-6  # the drift is along (1, -1)
+
+
 def test_split_count_changes_only_rounding():
     """The ⊕ merge of partial (max, sum) pairs is exact (App. D.3): any split count
     gives the same potentials up to fp32 rounding."""
