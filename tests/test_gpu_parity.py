@@ -480,6 +480,22 @@ def test_half2_range_exceeded_reported():
     assert torch.isfinite(f).all() and torch.isfinite(g).all()
 
 
+def test_bf16_points_at_extreme_scale_stay_finite():
+    """bf16 points scaled by 1e5 at eps = 1 (scores near 2^34 in dot-product
+    units, where fp32 resolves them only to thousands): the exact path's
+    exponents are taken against the maximum of the rounded scores, so no row
+    sum overflows or empties; potentials stay finite."""
+    data = workloads.make("c1", n=100, m=90)
+    data["X"] = (data["X"] * 1e5).astype(np.float32)
+    data["Y"] = (data["Y"] * 1e5).astype(np.float32)
+    prob = make_problem(data, eps=1.0, dtype="bf16")
+    f, g = zeros(100), zeros(90)
+    info = ssa.ot_solve(prob, f, g, 3)
+    torch.cuda.synchronize()
+    assert info["operand_mode"] == 1 and not info["nonfinite"]
+    assert torch.isfinite(f).all() and torch.isfinite(g).all()
+
+
 # --- size edges -------------------------------------------------------------------------
 
 @pytest.mark.parametrize("d,dtype", [(8192, "f32"), (8192, "bf16"), (4097, "f32")])
