@@ -116,16 +116,15 @@ KConf kernel_conf(int64_t d, int bf16, int f32_mode, bool for_apply) {
   return k;
 }
 
-// Column splits: enough workgroups to fill 256 CUs several times over, at
-// least ~4 column units (tiles, or blocks of the wide pass) per split, a
-// multiple of 8 when large (XCD locality).
-void choose_splits(PassShape& s, int cunits, int forced, int max_splits) {
+// Column splits: enough workgroups to fill 256 CUs several times over
+// (`target` workgroups), at least ~4 column units (tiles, or blocks of the
+// wide pass) per split, a multiple of 8 when large (XCD locality).
+void choose_splits(PassShape& s, int cunits, int forced, int max_splits, int target) {
   int S;
   if (forced > 0) {
     S = forced;
   } else {
-    constexpr int kTargetWorkgroups = 2048;  // 8 per CU
-    S = ceil_div(kTargetWorkgroups, s.nrowgroups);
+    S = ceil_div(target, s.nrowgroups);
     const int most = cunits / 4 > 1 ? cunits / 4 : 1;
     if (S > most) S = most;
     if (S >= 8) S = (S + 7) / 8 * 8;
@@ -137,7 +136,8 @@ void choose_splits(PassShape& s, int cunits, int forced, int max_splits) {
   s.splits = ceil_div(cunits, s.tps);
 }
 
-PassShape make_pass(int rtiles, int ctiles, const KConf& k, int ri, int forced, int max_splits) {
+PassShape make_pass(int rtiles, int ctiles, const KConf& k, int ri, int forced, int max_splits,
+                    int target) {
   PassShape s{};
   s.rtiles = rtiles;
   s.ctiles = ctiles;
@@ -150,7 +150,7 @@ PassShape make_pass(int rtiles, int ctiles, const KConf& k, int ri, int forced, 
   s.bk = k.bk;
   s.nrowgroups = ceil_div(rtiles, (int64_t)kWaves * ri);
   const int cunits = (k.xres || k.ct == 0) ? ctiles : ceil_div(ctiles, k.ct);
-  choose_splits(s, cunits, forced, max_splits);
+  choose_splits(s, cunits, forced, max_splits, target);
   return s;
 }
 
@@ -217,8 +217,9 @@ SolveWs solve_layout(const ot_problem* p, int splits_f, int splits_g) {
   w.mtiles = ceil_div(p->m, kTile);
   w.npad = w.ntiles * kTile;
   w.mpad = w.mtiles * kTile;
-  w.F = make_pass(w.ntiles, w.mtiles, w.k, w.k.ri, splits_f, 4096);
-  w.G = make_pass(w.mtiles, w.ntiles, w.k, w.k.ri, splits_g, 4096);
+  const int target = w.k.xres ? kTargetWorkgroupsResident : kTargetWorkgroups;
+  w.F = make_pass(w.ntiles, w.mtiles, w.k, w.k.ri, splits_f, 4096, target);
+  w.G = make_pass(w.mtiles, w.ntiles, w.k, w.k.ri, splits_g, 4096, target);
   w.errblocks_f = lse_merge_blocks(w.npad);
   w.errblocks_g = lse_merge_blocks(w.mpad);
   size_t o = 0;

@@ -46,7 +46,15 @@ struct KConf {
 
 int f32_operand_mode(int32_t flags);
 KConf kernel_conf(int64_t d, int bf16, int f32_mode, bool for_apply = false);
-PassShape make_pass(int rtiles, int ctiles, const KConf& k, int ri, int forced, int max_splits);
+// Workgroup targets measured on MI355X: the solve's register-resident
+// log-sum-exp passes run best with about 1024 workgroups (16 column splits
+// at 20000 rows: 2-4.5 % faster than 32 at d = 16, 64 and 128, fp32 and
+// bf16); the wide pass, the transport applications and the HVP's
+// transport-vector passes with about 2048.
+constexpr int kTargetWorkgroups = 2048;
+constexpr int kTargetWorkgroupsResident = 1024;
+PassShape make_pass(int rtiles, int ctiles, const KConf& k, int ri, int forced, int max_splits,
+                    int target = kTargetWorkgroups);
 int check_problem(const ot_problem* p);
 // ws == NULL: writes need to *ws_bytes and sets *query; otherwise checks size
 // and alignment.

@@ -242,6 +242,9 @@ HvpWs hvp_layout(const ot_problem* p) {
   v.on = v.k.xres;
   if (v.on) {
     const int nt = w.T.ntiles, mt = w.T.mtiles;
+    // transport-vector passes keep the 2048-workgroup target: at n = m = 50000
+    // (196 row groups) it gives 16 column splits instead of 6, about 1 %
+    // faster per HVP
     v.F = make_pass(nt, mt, v.k, v.k.ri, 0, 4096);
     v.G = make_pass(mt, nt, v.k, v.k.ri, 0, 4096);
     v.o_xs = take((size_t)nt * v.k.kbp * 1024);
