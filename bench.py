@@ -61,7 +61,8 @@ ALU_PAIRS_PEAK = ALU_LANE_SLOTS_PER_S / ALU_SLOTS_PER_PAIR
 # only for the kernel source they were taken on.
 TRAFFIC = {
     "c2": {"kernels_sha256": "4c6ff96ef1ae25059b83cbf604dfd486e0096889c954b339cba04a0cb8b4876e",
-           "bytes_per_launch": 51683968,
+           "splits": 16,
+           "bytes_per_launch": 49124096,
            "source": "profiles/lse_pipe_kernel_c2_n20000_d64_f32half2_hbm_traffic.md"},
 }
 # Sources of the register-resident log-sum-exp kernels the counters describe.
@@ -79,9 +80,11 @@ def kernel_sha():
     return h.hexdigest()
 
 
-def traffic_for(workload):
+def traffic_for(workload, splits):
+    """Counter-measured HBM bytes per launch, if taken on these kernel sources
+    and this column-split count (it sets the partials written)."""
     rec = TRAFFIC.get(workload)
-    if not rec or rec["kernels_sha256"] != kernel_sha():
+    if not rec or rec["kernels_sha256"] != kernel_sha() or rec["splits"] != splits:
         return None
     return rec["bytes_per_launch"]
 
@@ -465,7 +468,7 @@ def main():
         # the same 2 d flops per pair against the fp32 matrix peak (the bound of
         # a pass that used the fp32 matrix instruction)
         per_launch["frac_of_fp32_matrix_peak"] = per_launch["fp32_equivalent_tflops"] / MFMA_PEAK_TFLOPS["f32"]
-    roof["traffic"] = traffic_for(args.workload)
+    roof["traffic"] = traffic_for(args.workload, infos[-1]["splits_f"])
     roof.update({"kernel": "streamed log-sum-exp pass (lse_*_kernel)", "avg_launch_us": avg_lse_s * 1e6,
                  "launches": lse_n, **per_launch})
     last = infos[-1]
