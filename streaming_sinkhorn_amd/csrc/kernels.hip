@@ -103,10 +103,10 @@ __device__ __forceinline__ void pipe_stage(const u32x4* __restrict__ Cp,
     So[ri] = S[ri];
     if constexpr (VEC) {
       To[ri] = T[ri];
-      slow |= lse_fast_v<MODE != kModeBF16>(accC[ri], vC, MfC[ri], M[ri], So[ri], To[ri], ks,
+      slow |= lse_fast_v<MODE != kModeBF16, lazy_lse<MODE, KB>()>(accC[ri], vC, MfC[ri], M[ri], So[ri], To[ri], ks,
                                             S[ri], T[ri]);
     } else {
-      slow |= lse_fast<MODE != kModeBF16>(accC[ri], MfC[ri], M[ri], So[ri], ks, S[ri]);
+      slow |= lse_fast<MODE != kModeBF16, lazy_lse<MODE, KB>()>(accC[ri], MfC[ri], M[ri], So[ri], ks, S[ri]);
     }
   }
   load_ctile<MODE, KB>(Cp, cbias, cb3, jt_refill, lane, yN, aN);
@@ -119,9 +119,9 @@ __device__ __forceinline__ void pipe_stage(const u32x4* __restrict__ Cp,
       S[ri] = So[ri];
       if constexpr (VEC) {
         T[ri] = To[ri];
-        lse_exact_v(accC[ri], vC, MfC[ri], M[ri], S[ri], T[ri], ks);
+        lse_exact_v<lazy_lse<MODE, KB>()>(accC[ri], vC, MfC[ri], M[ri], S[ri], T[ri], ks);
       } else {
-        lse_exact(accC[ri], MfC[ri], M[ri], S[ri], ks);
+        lse_exact<lazy_lse<MODE, KB>()>(accC[ri], MfC[ri], M[ri], S[ri], ks);
       }
     }
     refold<MODE, RI>(M, h, Mfc, Bst);
@@ -129,12 +129,12 @@ __device__ __forceinline__ void pipe_stage(const u32x4* __restrict__ Cp,
 }
 
 // Tail LSE of RI tiles (plain or transport-vector).
-template <int MODE, int RI, bool VEC>
+template <int MODE, int KB, int RI, bool VEC>
 __device__ __forceinline__ void tail_any(const f32x16 (&acc)[RI], const f32x16& v,
                                          const float (&Mf)[RI], float (&M)[RI], float (&S)[RI],
                                          float (&T)[RI], float ks) {
-  if constexpr (VEC) lse_tail_v<MODE, RI>(acc, v, Mf, M, S, T, ks);
-  else lse_tail<MODE, RI>(acc, Mf, M, S, ks);
+  if constexpr (VEC) lse_tail_v<MODE, RI, lazy_lse<MODE, KB>()>(acc, v, Mf, M, S, T, ks);
+  else lse_tail<MODE, RI, lazy_lse<MODE, KB>()>(acc, Mf, M, S, ks);
 }
 
 // Partials of a row: (M in log2 units, S + S'), and T + T' for VEC.
@@ -214,15 +214,15 @@ __global__ __launch_bounds__(256) void lse_pipe_kernel(
                                   ks, xr, yA, aA, accA, MfA, accB, MfB, vA, vB, M, S, T, Mfc, Bst);
   }
   if (k + 1 <= last) {  // tiles k and k+1 remain
-    tail_any<MODE, RI, VEC>(accA, vA, MfA, M, S, T, ks);
+    tail_any<MODE, KB, RI, VEC>(accA, vA, MfA, M, S, T, ks);
     refold<MODE, RI>(M, h, Mfc, Bst);
 #pragma unroll
     for (int ri = 0; ri < RI; ++ri) MfB[ri] = Mfc[ri];
     score_tile<MODE, KB, RI>(yB, xr, aB, Bst, h, accB);
     if constexpr (VEC) vB = load_tile_values(vcol, jt0 + k + 1, h);
-    tail_any<MODE, RI, VEC>(accB, vB, MfB, M, S, T, ks);
+    tail_any<MODE, KB, RI, VEC>(accB, vB, MfB, M, S, T, ks);
   } else {  // tile k remains
-    tail_any<MODE, RI, VEC>(accA, vA, MfA, M, S, T, ks);
+    tail_any<MODE, KB, RI, VEC>(accA, vA, MfA, M, S, T, ks);
   }
 
   // The lane pair shares M: the row's partial is (M in log2 units, S + S').
@@ -387,10 +387,10 @@ __global__ __launch_bounds__(256) void lse_lds_kernel(
       So[ri] = S[ri];
       if constexpr (VEC) {
         To[ri] = T[ri];
-        slow |= lse_fast_v<MODE != kModeBF16>(accC[ri], vC, MfC[ri], M[ri], So[ri], To[ri], ks,
+        slow |= lse_fast_v<MODE != kModeBF16, lazy_lse<MODE, KB>()>(accC[ri], vC, MfC[ri], M[ri], So[ri], To[ri], ks,
                                               S[ri], T[ri]);
       } else {
-        slow |= lse_fast<MODE != kModeBF16>(accC[ri], MfC[ri], M[ri], So[ri], ks, S[ri]);
+        slow |= lse_fast<MODE != kModeBF16, lazy_lse<MODE, KB>()>(accC[ri], MfC[ri], M[ri], So[ri], ks, S[ri]);
       }
     }
     if constexpr (VEC) vN = load_tile_values(vcol, jt0 + k + 1, h);
@@ -404,9 +404,9 @@ __global__ __launch_bounds__(256) void lse_lds_kernel(
         S[ri] = So[ri];
         if constexpr (VEC) {
           T[ri] = To[ri];
-          lse_exact_v(accC[ri], vC, MfC[ri], M[ri], S[ri], T[ri], ks);
+          lse_exact_v<lazy_lse<MODE, KB>()>(accC[ri], vC, MfC[ri], M[ri], S[ri], T[ri], ks);
         } else {
-          lse_exact(accC[ri], MfC[ri], M[ri], S[ri], ks);
+          lse_exact<lazy_lse<MODE, KB>()>(accC[ri], MfC[ri], M[ri], S[ri], ks);
         }
       }
       refold<MODE, RI>(M, h, Mfc, Bst);
@@ -424,10 +424,10 @@ __global__ __launch_bounds__(256) void lse_lds_kernel(
     for (int ri = 0; ri < RI; ++ri) MfB[ri] = Mfc[ri];  // M has not moved since the last refold
     score_tile_lds<MODE, KB, RI>(lds[(k + 1) & 1], lane, xr, aB, Bst, h, accB);
     if constexpr (VEC) vB = load_tile_values(vcol, jt0 + k + 1, h);
-    tail_any<MODE, RI, VEC>(accA, vA, MfA, M, S, T, ks);
-    tail_any<MODE, RI, VEC>(accB, vB, MfB, M, S, T, ks);
+    tail_any<MODE, KB, RI, VEC>(accA, vA, MfA, M, S, T, ks);
+    tail_any<MODE, KB, RI, VEC>(accB, vB, MfB, M, S, T, ks);
   } else {
-    tail_any<MODE, RI, VEC>(accA, vA, MfA, M, S, T, ks);
+    tail_any<MODE, KB, RI, VEC>(accA, vA, MfA, M, S, T, ks);
   }
 
   write_partials<RI, VEC>(M, S, T, h, lane, rt0, rtiles, s, rpad, ks, part, partT);

@@ -198,7 +198,7 @@ __global__ __launch_bounds__(256) void lse_wide_kernel(
       f32x16 col[RT];
 #pragma unroll
       for (int r = 0; r < RT; ++r) col[r] = acc[r][q];
-      lse_tail<MODE, RT>(col, Mf, M, S, ks);
+      lse_tail<MODE, RT, false>(col, Mf, M, S, ks);
     }
   }
 
