@@ -81,6 +81,11 @@ HALF_CASES = [
     (300, 40, 64, "f32", 0.01),
     (260, 70, 17, "bf16", 0.01),
     (150, 90, 300, "f32", 0.01),
+    # passes with the lazily raised stabiliser (at most three score MFMAs per
+    # tile: fp16 split d <= 16, bf16 d <= 48), also at eps = 0.01
+    (300, 40, 16, "f32", 0.01),
+    (210, 170, 40, "bf16", 0.05),
+    (180, 45, 48, "bf16", 0.01),
 ]
 
 
@@ -140,6 +145,9 @@ TRAJ_CASES = [
     ("c3_d1024_bf16", 300, 250, None, None),
     ("c4", 800, 700, None, 200),
     ("c5", 1000, 120, None, 300),
+    # the eps = 0.01 workload at d = 16: passes with the lazily raised
+    # stabiliser over 300 iterations
+    ("c5", 600, 300, 16, 300),
 ]
 
 
