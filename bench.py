@@ -17,6 +17,10 @@ exponentials and vector work dominate (small d in bf16) -- against the ALU
 bound of the online log-sum-exp in pairs per second. ``cpu_baseline`` times
 the fp64 oracle on a bounded sample of the same workload on the host.
 
+Without --graph the line also carries ``graph_replay``: the same steps with
+the iterations replayed from HIP graphs (how ot_solve runs by default),
+timed after the event-timed ones, for reference.
+
 With --graph the timed steps replay the iterations from HIP graphs (no
 per-launch events); the roofline then comes from one extra plain step.
 
@@ -432,6 +436,21 @@ def main():
             # per-launch events need plain launches: one more step, after the timed ones
             step(True)
             torch.cuda.synchronize()
+        else:
+            # the same steps with the iterations replayed from HIP graphs (how
+            # ot_solve runs by default), timed separately, for reference
+            for _ in range(args.warmup):
+                step(False, False)
+            torch.cuda.synchronize()
+            g0 = time.perf_counter()
+            for _ in range(args.steps):
+                step(False, False)
+            torch.cuda.synchronize()
+            g1 = time.perf_counter()
+            graph_replay = {"value": w.n * w.m * T / ((g1 - g0) / args.steps),
+                            "ms_per_step": (g1 - g0) * 1e3 / args.steps,
+                            "note": "same steps, iterations replayed from HIP graphs (16 per "
+                                    "graph), timed after the event-timed steps"}
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     value = w.n * w.m * T / ((t1 - t0) / args.steps)
@@ -505,6 +524,7 @@ def main():
         "roofline": roof,
         "marg_err_row": last["marg_err_row"],
         "marg_err_col": last["marg_err_col"],
+        **({} if args.graph else {"graph_replay": graph_replay}),
     }
     if cpu is not None:
         out["cpu_baseline"] = cpu
