@@ -216,13 +216,21 @@ def hvp_cpu_baseline(data, tau, K, rows=3000):
     a = np.full(rows, 1.0 / rows)
     b = np.full(rows, 1.0 / rows)
     f, g = oracle.sinkhorn(oracle.cost_matrix(X, Y), a, b, w.eps, 20)
+    # the oracle's dense products run in numpy's BLAS: its thread count is the
+    # number of host threads the sample used
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([1] + [p.get("num_threads", 1) for p in threadpool_info()
+                           if p.get("user_api") == "blas"])
+    except Exception:  # threadpoolctl missing: numpy's BLAS thread count unknown
+        cores = None
     t0 = time.perf_counter()
     oracle.hvp.hvp_schur_cg(X, Y, a, b, f, g, w.eps, A, tau=tau, iters=K)
     dt = time.perf_counter() - t0
     return {
         "value": dt * (float(w.n) * w.m) / (rows * rows),
         "unit": "s per HVP (scaled to the full n*m by pair count)",
-        "cores": 1,
+        "cores": cores,
         "kind": "oracle",
         "sample": f"fp64 numpy oracle HVP (dense coupling, K={K} CG iterations) on n=m={rows} "
                   f"points of the same workload: {dt:.2f} s; scaled by n*m / {rows}^2",
