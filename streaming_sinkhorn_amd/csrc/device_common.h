@@ -135,12 +135,13 @@ __device__ __forceinline__ float max16(const f32x16& v) {
 // Lazy stabiliser: the online LSE of App. D.3 is exact for any running
 // stabiliser M, not only for the running maximum. The bias MFMA
 // (mfma_bias_stab) also subtracts M_i from every score, so in the common
-// case a tile costs one exp2 and one add per score, with no rescale. Only
-// when a tile could overflow (tile sum >= 2^64), before M has been set from
-// data, or for the tile already scored when M moved, does the wave take the
-// exact path: tile maximum, raise M if the tile could reach 2^32, rescale S.
-// M is kept identical in the two lanes (l, l ^ 32) that share a row, because
-// the bias MFMA reads it from lane l + 32.
+// case a tile costs one exp2 and one add per score (plus one rescale per
+// tile in the eager variant, none in the lazy one; see lse_fast). Only when
+// a tile could overflow (tile sum >= 2^64), before M has been set from data,
+// or (lazy variant) for the tile already scored when M moved, does the wave
+// take the exact path: tile maximum, raise M, rescale S. M is kept identical
+// in the two lanes (l, l ^ 32) that share a row, because the bias MFMA reads
+// it from lane l + 32.
 //
 // Units: for fp32 inputs the row operand X is packed pre-multiplied by
 // c = 2 log2(e) / eps and the biases are written in the same units, so scores
