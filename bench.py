@@ -64,9 +64,9 @@ ALU_PAIRS_PEAK = ALU_LANE_SLOTS_PER_S / ALU_SLOTS_PER_PAIR
 # FETCH_SIZE / WRITE_SIZE runs (scaled by the copy-kernel calibration), valid
 # only for the kernel source they were taken on.
 TRAFFIC = {
-    "c2": {"kernels_sha256": "832f4c40a0a8412159f5d7bddb0dcc75d43584c7437bee62d4a44518009c1586",
+    "c2": {"kernels_sha256": "1fe26356f929a3b5ecbd87abb0cfc92acf097df376cddbde5f066a15080fc350",
            "splits": 16,
-           "bytes_per_launch": 49124032,
+           "bytes_per_launch": 49124512,
            "source": "profiles/lse_pipe_kernel_c2_n20000_d64_f32half2_hbm_traffic.md"},
 }
 # Sources of the register-resident log-sum-exp kernels the counters describe.
