@@ -30,6 +30,18 @@ Other modes:
                      rate the chip sustains in a library GEMM, for context.
   --copy-probe MIB   copy a MIB-MiB buffer a few times with torch and exit:
                      the calibration run for the HBM byte counters.
+  --exp-probe        time the library's throughput probes (v_exp_f32 and the
+                     32x32x16 fp16 matrix instruction, include/flashot_probe.h)
+                     and exit.
+
+Roofline pricing: the method's own work per launch, 2 d flops and one
+exponential per (i, j) pair, each against the published peak of the unit it
+runs on (fp16 matrix cores for the default fp32 operands, which form every
+fp32 product from two fp16 parts; bf16 for bf16 points and the three-part
+split; fp32 for OT_NATIVE_F32; exponentials at EXP_PEAK_PER_S). The bound is
+the larger of the two ideal times and frac = that time / the measured one.
+``executed_frac`` gives the matrix work the kernel actually issues (three
+products per fp32 product in the default mode) against the same peak.
 """
 
 from __future__ import annotations
@@ -48,17 +60,12 @@ if ROOT not in sys.path:
 # MI355X published dense peaks.
 MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0, "f16": 2500.0}
 HBM_PEAK_GBS = 8000.0
-# ALU bound of the online log-sum-exp, derived from the unit counts. The
-# published fp32 vector peak (157.3 TFLOP/s = 256 CUs x 2.4 GHz x 128 FMA
-# lanes) gives 7.86e13 full-rate lane-ops/s, i.e. 32 lanes per clock per SIMD
-# for plain (unpacked) fp32 ops; an exponential is taken at a quarter of that
-# rate (1.97e13/s; 1.64e13/s measured with dependent chains). Per (i, j) pair
-# and half-step the online LSE needs one exponential (4 lane-op slots), one
-# FMA (scale and subtract the running max), one add (the sum) and half of a
-# three-input max: 6.5 slots.
-ALU_LANE_SLOTS_PER_S = 256 * 2.4e9 * 128
-ALU_SLOTS_PER_PAIR = 6.5
-ALU_PAIRS_PEAK = ALU_LANE_SLOTS_PER_S / ALU_SLOTS_PER_PAIR
+# Exponential peak of the online log-sum-exp, from the unit counts: 256 CUs x
+# 4 SIMDs x 8 lanes per clock x 2.4 GHz. v_exp_f32 issues at half the rate of
+# a plain fp32 op on gfx950 (16 lanes per clock per SIMD unpacked); the
+# probe (--exp-probe, and the `probe` object of every default line) measures
+# what the chip sustains. One exponential per (i, j) pair and half-step.
+EXP_PEAK_PER_S = 256 * 4 * 8 * 2.4e9
 
 # HBM bytes of one launch of the dominant kernel, from rocprofv3 --pmc
 # FETCH_SIZE / WRITE_SIZE runs (scaled by the copy-kernel calibration), valid
@@ -74,6 +81,44 @@ KERNEL_SRCS = [os.path.join(ROOT, "streaming_sinkhorn_amd", "csrc", f)
                for f in ("kernels.hip", "device_common.h")]
 
 METRIC = "Sinkhorn n*m*iters/sec + % MFMA/exp roofline at n=m=20k, d=64, eps=0.1"
+
+
+# What the fp32 products of each operand mode run as (ot_solve_info.operand_mode).
+DTYPE_LABEL = {0: "f32", 1: "bf16", 2: "f32 (3xbf16 split)", 3: "f32 (2xfp16 split)"}
+
+
+def lse_roofline(pairs, d, dtype, mode, avg_s):
+    """Roofline of one log-sum-exp launch over `pairs` (i, j) pairs at dimension d.
+
+    Method work per launch: 2 d flops per pair on the matrix cores and one
+    exponential per pair. The matrix work is priced at the peak of the unit
+    the contraction runs on: fp16 for fp32 points in the default two-part fp16
+    split (mode 3), bf16 for the three-part bf16 split (mode 2) and for bf16
+    points (mode 1), fp32 for OT_NATIVE_F32 (mode 0). frac = the larger ideal
+    time over the measured one. executed_frac prices what the kernel issues:
+    3 (mode 3) or 6 (mode 2) products per fp32 product, plus nothing for the
+    bias instruction."""
+    unit = {3: "f16", 2: "bf16", 1: "bf16", 0: "f32"}[mode]
+    peak = MFMA_PEAK_TFLOPS[unit]
+    alg_flops = 2.0 * pairs * d
+    executed = alg_flops * {3: 3.0, 2: 6.0}.get(mode, 1.0)
+    t_mfma = alg_flops / (peak * 1e12)
+    t_exp = pairs / EXP_PEAK_PER_S
+    if t_mfma >= t_exp:
+        roof = {"bound": "mfma", "achieved": alg_flops / avg_s / 1e12, "peak": peak,
+                "unit": "TFLOP/s", "frac": t_mfma / avg_s}
+    else:
+        roof = {"bound": "alu", "achieved": pairs / avg_s / 1e9, "peak": EXP_PEAK_PER_S / 1e9,
+                "unit": "Gexp/s", "frac": t_exp / avg_s}
+    roof.update({
+        "matrix_unit": unit,
+        "method_flops_per_launch": alg_flops,
+        "exps_per_launch": pairs,
+        "ideal_us": {"mfma": t_mfma * 1e6, "exp": t_exp * 1e6},
+        "executed_matrix_flops_per_launch": executed,
+        "executed_frac": executed / (peak * 1e12) / avg_s,
+    })
+    return roof
 
 
 def kernel_sha():
@@ -178,6 +223,36 @@ def copy_probe(mib):
     print(json.dumps({"copy_probe_bytes": n * 4, "copies": 3}), flush=True)
 
 
+def rate_probes(reps=3):
+    """Throughput of the exponential and of the fp16 matrix instruction, each
+    from the library's probe kernel timed with HIP events on its stream."""
+    import torch
+
+    import streaming_sinkhorn_amd as ssa
+
+    out = {}
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for kind, name, iters in ((ssa.OT_PROBE_EXP2, "exp2_per_s", 4096),
+                                  (ssa.OT_PROBE_MFMA_F16, "mfma_f16_tflops", 1024)):
+            ssa.ot_probe_rate(kind, iters)  # warm-up
+            best = None
+            for _ in range(reps):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                buf, work = ssa.ot_probe_rate(kind, iters)
+                e1.record(stream)
+                stream.synchronize()
+                rate = work / (e0.elapsed_time(e1) / 1e3)
+                best = rate if best is None else max(best, rate)
+                del buf
+            out[name] = best / 1e12 if name.endswith("tflops") else best
+    out["note"] = ("best of 3 launches, 2048 workgroups of 256 threads; exp2: 8 independent "
+                   "chains per lane; fp16 MFMA: 4 independent 32x32x16 chains per wave")
+    return out
+
+
 def gemm_probe():
     import torch
 
@@ -278,24 +353,26 @@ def hvp_main(args):
     sec = (t1 - t0) / args.steps
     ev_sec = e0.elapsed_time(e1) / 1e3 / args.steps
     pairs = float(w.n) * w.m
-    # Executed matrix work of one HVP, each pass against the peak of the unit
-    # it runs on (the ideal time is the sum; frac = ideal / measured):
+    # Method work of one HVP, pass by pass, each contraction against the peak
+    # of the unit it runs on and one exponential per pair; the ideal time of a
+    # pass is the larger of its matrix and exponential times, and the HVP's is
+    # their sum (frac = ideal / measured):
     # - 2 K + 2 transport-vector passes (conjugate gradients and the marginals
-    #   they use) on the log-sum-exp layout: fp32 scores as the two-part fp16
-    #   split, 3 products x 2 d flops per pair, fp16 peak;
-    # - the transport-matrix passes: the score on fp32 matrix instructions
-    #   (2 d per pair, twice in the weighted pass, which also forms A Y^T);
-    #   the value product over value columns padded to 32 on fp16 parts
-    #   (3 products x 2 per column), or on fp32 (2 per column) in the
-    #   weighted pass.
-    pad32 = lambda cols: (cols + 31) // 32 * 32
-    vec_f16 = (2 * K + 2) * pairs * 6.0 * w.d
-    mat_f32 = pairs * (2.0 * w.d * 3 + 4.0 * w.d + 2.0 * pad32(w.d))
-    mat_f16 = sum(pairs * 6.0 * pad32(cols) for cols in (w.d, w.d + 2, w.d + 1))
-    ideal = ((vec_f16 + mat_f16) / (MFMA_PEAK_TFLOPS["f16"] * 1e12)
-             + mat_f32 / (MFMA_PEAK_TFLOPS["f32"] * 1e12))
-    f16_equiv = ideal * MFMA_PEAK_TFLOPS["f16"] * 1e12
-    achieved = f16_equiv / ev_sec / 1e12
+    #   they use): 2 d flops per pair on the fp16 matrix cores (fp32 points as
+    #   the two-part fp16 split); the value sum is vector work;
+    # - 3 transport-matrix passes with d, d + 2 and d + 1 value columns: scores
+    #   on the fp32 matrix instruction (2 d per pair), values on the fp16
+    #   matrix cores (2 per pair and column);
+    # - the Hadamard-weighted pass: two score tiles and the values, all fp32
+    #   (4 d + 2 d per pair).
+    f16 = MFMA_PEAK_TFLOPS["f16"] * 1e12
+    f32 = MFMA_PEAK_TFLOPS["f32"] * 1e12
+    t_exp = pairs / EXP_PEAK_PER_S
+    vec = (2 * K + 2) * max(pairs * 2.0 * w.d / f16, t_exp)
+    mat = sum(max(pairs * 2.0 * w.d / f32 + pairs * 2.0 * cols / f16, t_exp)
+              for cols in (w.d, w.d + 2, w.d + 1))
+    had = max(pairs * 6.0 * w.d / f32, t_exp)
+    ideal = vec + mat + had
     res = {
         "metric": f"streaming HVP time per call (n=m={w.n}, d={w.d}, K={K} CG, tau={tau})",
         "value": sec,
@@ -307,20 +384,21 @@ def hvp_main(args):
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f32 (2xfp16 split scores; fp32 transport-matrix scores)",
         "data": "synthetic",
         "config": {"workload": f"{w.name}: n={w.n}, m={w.m}, d={w.d}, fp32 points uniform in "
                                f"[0,1]^d, uniform weights, eps={w.eps}; potentials from {w.iters} "
                                f"iterations (untimed); HVP with K={K} fixed CG iterations, tau={tau}",
                    "n": w.n, "m": w.m, "d": w.d, "eps": w.eps, "cg_iters": K,
                    "transport_passes": 2 * K + 4},
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_PEAK_TFLOPS["f16"],
+        "roofline": {"bound": "mfma", "achieved": ideal / ev_sec * MFMA_PEAK_TFLOPS["f16"],
+                     "peak": MFMA_PEAK_TFLOPS["f16"],
                      "unit": "TFLOP/s (fp16-equivalent)", "frac": ideal / ev_sec,
                      "traffic": None,
                      "kernel": "all streamed passes of one HVP (vector passes: lse_*_kernel with a "
-                               "value column; matrix passes: apply_partial_kernel); executed matrix "
-                               "work with fp32 flops weighted by the fp16/fp32 peak ratio, over the "
-                               "event-timed call",
+                               "value column; matrix passes: apply_*_kernel); the method's work of "
+                               "each pass against the peak of the unit it runs on (fp32 work "
+                               "weighted by the fp16/fp32 peak ratio), over the event-timed call",
                      "ideal_sec": ideal, "event_sec_per_hvp": ev_sec},
     }
     if not args.no_cpu_baseline:
@@ -339,6 +417,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB")
     ap.add_argument("--gemm-probe", action="store_true")
+    ap.add_argument("--exp-probe", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="time the steps with the iterations replayed from HIP graphs (the "
                          "roofline's per-launch times then come from one extra plain step)")
@@ -361,6 +440,15 @@ def main():
         return
     if args.copy_probe:
         copy_probe(args.copy_probe)
+        return
+    if args.exp_probe:
+        import streaming_sinkhorn_amd as ssa
+
+        ssa.lib()
+        res = rate_probes()
+        res["exp2_peak_per_s"] = EXP_PEAK_PER_S
+        res["mfma_f16_peak_tflops"] = MFMA_PEAK_TFLOPS["f16"]
+        print(json.dumps(res), flush=True)
         return
     if args.hvp:
         hvp_main(args)
@@ -467,37 +555,10 @@ def main():
     avg_lse_s = lse_ms / lse_n / 1e3
     pairs = float(w.n) * w.m
     mode = infos[-1]["operand_mode"]
-    alg_flops = 2.0 * pairs * w.d
-    if mode == 3:
-        # fp32 scores formed from two fp16 parts per coordinate: three fp16
-        # products per fp32 product on the fp16 matrix cores.
-        mat_flops, mat_peak, mat_dtype = 3.0 * alg_flops, MFMA_PEAK_TFLOPS["f16"], "f16 (fp32 split)"
-    elif mode == 2:
-        # fp32 scores formed from three bf16 parts per coordinate: six bf16
-        # products per fp32 product on the bf16 matrix cores.
-        mat_flops, mat_peak, mat_dtype = 6.0 * alg_flops, MFMA_PEAK_TFLOPS["bf16"], "bf16 (fp32 split)"
-    else:
-        mat_flops, mat_peak, mat_dtype = alg_flops, MFMA_PEAK_TFLOPS[w.dtype], w.dtype
-    t_mfma = mat_flops / (mat_peak * 1e12)
-    t_alu = pairs / ALU_PAIRS_PEAK
-    if t_mfma >= t_alu:
-        achieved = mat_flops / avg_lse_s / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": mat_peak,
-                "unit": "TFLOP/s", "frac": achieved / mat_peak}
-        per_launch = {"matrix_dtype": mat_dtype, "matrix_flops_per_launch": mat_flops}
-    else:
-        achieved = pairs / avg_lse_s / 1e9
-        roof = {"bound": "alu", "achieved": achieved, "peak": ALU_PAIRS_PEAK / 1e9,
-                "unit": "Gpair/s", "frac": achieved / (ALU_PAIRS_PEAK / 1e9)}
-        per_launch = {"algorithmic_pairs_per_launch": pairs}
-    per_launch["fp32_equivalent_tflops"] = alg_flops / avg_lse_s / 1e12
-    if w.dtype == "f32":
-        # the same 2 d flops per pair against the fp32 matrix peak (the bound of
-        # a pass that used the fp32 matrix instruction)
-        per_launch["frac_of_fp32_matrix_peak"] = per_launch["fp32_equivalent_tflops"] / MFMA_PEAK_TFLOPS["f32"]
+    roof = lse_roofline(pairs, w.d, w.dtype, mode, avg_lse_s)
     roof["traffic"] = traffic_for(args.workload, infos[-1]["splits_f"])
-    roof.update({"kernel": "streamed log-sum-exp pass (lse_*_kernel)", "avg_launch_us": avg_lse_s * 1e6,
-                 "launches": lse_n, **per_launch})
+    roof.update({"kernel": "streamed log-sum-exp pass (lse_*_kernel)",
+                 "avg_launch_us": avg_lse_s * 1e6, "launches": lse_n})
     last = infos[-1]
     outputs = ["f", "g", "marginal errors"]
     if w.grad:
@@ -517,7 +578,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        "dtype": DTYPE_LABEL[mode] if w.dtype == "f32" else w.dtype,
         "data": "synthetic",
         "config": {
             "workload": f"{w.name}: n={w.n}, m={w.m}, d={w.d}, {w.dtype} points, eps={w.eps}, {T} "
@@ -534,6 +595,8 @@ def main():
         "marg_err_col": last["marg_err_col"],
         **({} if args.graph else {"graph_replay": graph_replay}),
     }
+    with torch.cuda.stream(stream):
+        out["probe"] = rate_probes()
     if cpu is not None:
         out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)

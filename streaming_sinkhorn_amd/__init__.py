@@ -25,7 +25,8 @@ import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libflashot.so")
-HEADER_PATH = os.path.join(os.path.dirname(HERE), "include", "flashot.h")
+INCLUDE_DIR = os.path.join(os.path.dirname(HERE), "include")
+HEADER_PATH = os.path.join(INCLUDE_DIR, "flashot.h")
 
 OT_OK, OT_ERR_INVALID_ARG, OT_ERR_UNSUPPORTED, OT_ERR_WORKSPACE, OT_ERR_HIP, OT_ERR_NONFINITE = range(6)
 OT_F32, OT_BF16 = 0, 1
@@ -35,6 +36,7 @@ OT_NATIVE_F32 = 1
 OT_COST_AFFINE = 2
 OT_SPLIT_BF16 = 4
 OT_SCHED_ALTERNATING, OT_SCHED_SYMMETRIC = 0, 1
+OT_PROBE_EXP2, OT_PROBE_MFMA_F16 = 0, 1
 _SCHEDULES = {"alternating": OT_SCHED_ALTERNATING, "symmetric": OT_SCHED_SYMMETRIC}
 
 
@@ -116,9 +118,10 @@ def lib() -> ctypes.CDLL:
     L.ot_apply_hadamard.argtypes = [pp, vp, vp, vp, i64, vp, i64, i64, vp, vp, szp, vp]
     L.ot_hvp.argtypes = [pp, vp, vp, vp, i64, ctypes.POINTER(OtHvpOpts), vp,
                          ctypes.POINTER(OtHvpInfo), vp, szp, vp]
+    L.ot_probe_rate.argtypes = [i32, i64, ctypes.c_int32, vp, ctypes.POINTER(ctypes.c_double), vp]
     for fn in ("ot_sqnorms", "ot_update_f", "ot_update_g", "ot_solve", "ot_apply_plan",
                "ot_apply_hadamard", "ot_hvp", "ot_prep_cosine", "ot_prep_labels",
-               "ot_sinkhorn_divergence"):
+               "ot_sinkhorn_divergence", "ot_probe_rate"):
         getattr(L, fn).restype = ctypes.c_int
     L.ot_last_error.restype = ctypes.c_char_p
     L.ot_last_error.argtypes = []
@@ -129,9 +132,13 @@ def lib() -> ctypes.CDLL:
 
 
 def header_entry_points() -> list[str]:
-    """Names of the functions declared in include/flashot.h."""
-    txt = open(HEADER_PATH).read()
-    return re.findall(r"^\s*(?:int|const char\*)\s+(ot_\w+)\s*\(", txt, re.M)
+    """Names of the functions declared in the headers under include/."""
+    names = []
+    for fn in sorted(os.listdir(INCLUDE_DIR)):
+        if fn.endswith(".h"):
+            txt = open(os.path.join(INCLUDE_DIR, fn)).read()
+            names += re.findall(r"^\s*(?:int|const char\*)\s+(ot_\w+)\s*\(", txt, re.M)
+    return names
 
 
 def _check(code: int, where: str):
@@ -433,6 +440,17 @@ def apply_workspace(prob: Problem, V=None, flags: int = 0) -> torch.Tensor:
     _check(L.ot_apply_plan(ctypes.byref(prob.c), None, None, None, vdt, cols, ldv, int(flags),
                            None, None, None, ctypes.byref(size), None), "ot_apply_plan workspace query")
     return torch.empty(max(size.value, 256), dtype=torch.uint8, device=prob.device)
+
+
+def ot_probe_rate(kind: int, iters: int, blocks: int = 2048):
+    """Enqueue one throughput probe (OT_PROBE_EXP2 or OT_PROBE_MFMA_F16) on the
+    current stream. Returns (output tensor, work of the launch: exponentials or
+    flops); the caller times the launch."""
+    out = torch.empty(int(blocks) * 256, dtype=torch.float32, device="cuda")
+    work = ctypes.c_double(0.0)
+    _check(lib().ot_probe_rate(int(kind), int(iters), int(blocks), _ptr(out), ctypes.byref(work),
+                               _stream(out.device)), "ot_probe_rate")
+    return out, work.value
 
 
 def version() -> str:

@@ -40,6 +40,7 @@ SOURCES = [
     ("api.hip", []),
     ("hvp_api.hip", []),
     ("cost_prep.hip", []),
+    ("probe_kernels.hip", []),
 ]
 
 
