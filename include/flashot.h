@@ -28,6 +28,10 @@
  *    *ws_bytes and does nothing else (returns OT_OK).
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
  *    and returns without synchronising, except where a function says so.
+ *    One such case is shared by every entry point that forms scores: fp32
+ *    points in the default operand mode (see ot_problem flags) are checked
+ *    against the fp16 range on the device, and the call waits for that
+ *    check (one stream synchronisation, before its passes are enqueued).
  *  - Point arrays are row-major: element (i, k) of X is at x[i * ldx + k],
  *    ldx >= d. Their storage type is OT_F32 (float) or OT_BF16 (bfloat16);
  *    products are accumulated in fp32, potentials and weights are fp32.
@@ -121,14 +125,23 @@ extern "C" {
  *               each coordinate product is off by at most about 3 * 2^-22 of
  *               its size, the order of fp32 rounding over a dot product.
  *               This covers every problem with
- *               (2/eps) log2(e) max|x_ik| max|y_jk| < 2^28 (scores in log2
- *               units that fp32 still resolves); beyond it the potentials
- *               come out NaN and ot_solve with info returns
- *               OT_ERR_UNSUPPORTED (ot_hvp likewise). OT_SPLIT_BF16 uses
- *               three bf16 parts (24 significant bits, six products, fp32
- *               exponent range) and OT_NATIVE_F32 the fp32 matrix
- *               instruction. Transport application always uses fp32
- *               products for fp32 points.
+ *               (2/eps) log2(e) max|x_ik| max|y_jk| < 2^29 (scores in log2
+ *               units that fp32 still resolves) and none at or above 2^30.
+ *               The check runs on the device before the passes; a problem
+ *               outside the range makes ot_update_f, ot_update_g, ot_solve,
+ *               ot_apply_plan and ot_hvp return OT_ERR_UNSUPPORTED (after
+ *               one stream synchronisation, the same in range) without
+ *               enqueuing their passes. OT_SPLIT_BF16 uses three bf16 parts
+ *               (24 significant bits, six products, fp32 exponent range) and
+ *               OT_NATIVE_F32 the fp32 matrix instruction; neither
+ *               synchronises. Transport application (ot_apply_plan) forms
+ *               its scores the same way, and multiplies the exponentiated
+ *               scores into the values on the fp16 matrix cores: each score
+ *               p (at most 1 after the running maximum) as two fp16 parts
+ *               and each value column, scaled by a power of two, as two fp16
+ *               parts, three partial products per term, each within about
+ *               2^-22 of its size. Under OT_NATIVE_F32 / OT_SPLIT_BF16 both
+ *               products are fp32.
  */
 typedef struct ot_problem {
   const void* x;
@@ -163,8 +176,12 @@ typedef struct ot_solve_opts {
 typedef struct ot_solve_info {
   int32_t iters_done;    /* iterations actually run */
   int32_t nonfinite;     /* 1 if the final f or g holds NaN / Inf */
-  float marg_err_row;    /* ||P 1 - a||_1 of the returned (f, g) */
-  float marg_err_col;    /* ||P^T 1 - b||_1 of the returned (f, g) */
+  float marg_err_row;    /* ||P 1 - a||_1 of the returned (f, g), from one extra row pass */
+  float marg_err_col;    /* ||P^T 1 - b||_1 of the returned (f, g). Alternating schedule with
+                            its last iteration at eps: the last g half-step fit the columns,
+                            and this is 0 by construction (no pass; the true value is that
+                            half-step's fp32 rounding). Symmetric schedule, iters = 0 or
+                            every iteration annealed: from one extra column pass. */
   float lse_ms;          /* with opts.timing: summed duration of the log-sum-exp kernels (ms) */
   int32_t lse_launches;  /* with opts.timing: number of log-sum-exp kernel launches timed */
   int32_t splits_f;      /* column splits used by the f half-step */
@@ -197,7 +214,8 @@ int ot_sqnorms(const void* pts, int dtype, int64_t rows, int64_t d, int64_t ld,
  *         = sum_i a_i |exp((f_old_i - f_i)/eps) - 1| (App. E.1 induced row
  *         marginal), the row-marginal error of the coupling before the update.
  *   ws, ws_bytes  workspace (see conventions)
- * Errors: OT_ERR_INVALID_ARG, OT_ERR_UNSUPPORTED, OT_ERR_WORKSPACE, OT_ERR_HIP.
+ * Errors: OT_ERR_INVALID_ARG, OT_ERR_UNSUPPORTED (also for fp32 points out
+ * of the fp16 range, see ot_problem flags), OT_ERR_WORKSPACE, OT_ERR_HIP.
  */
 int ot_update_f(const ot_problem* p, const float* g, float* f, float* err,
                 void* ws, size_t* ws_bytes, void* stream);
@@ -225,9 +243,9 @@ int ot_update_g(const ot_problem* p, const float* f, float* g, float* err,
  *          starting point (k then k' iterations equal k + k' iterations).
  *   opts   host, required
  *   info   host or NULL. When non-NULL the call synchronises the stream at the
- *          end and fills every field; marg_err_row / marg_err_col are then the
- *          exact L1 marginal errors of the returned (f, g), at the cost of two
- *          extra streamed passes.
+ *          end and fills every field; marg_err_row is then the L1 row-marginal
+ *          error of the returned (f, g), from one extra streamed pass, and
+ *          marg_err_col the column one (see ot_solve_info).
  *   With opts->tol > 0 the row-marginal error of the coupling of the previous
  *   iterate is evaluated inside every f half-step (it is r - a for r of App.
  *   E.1) and the host reads it every opts->check_every iterations (one
@@ -240,9 +258,8 @@ int ot_update_g(const ot_problem* p, const float* f, float* g, float* err,
  *   geometric schedule is this library's reading. The tolerance check runs
  *   only in the iterations at eps.
  * Errors: as ot_update_f, plus OT_ERR_NONFINITE when info is given and the
- * final potentials are not finite, and OT_ERR_UNSUPPORTED when info is given
- * and fp32 points are too large for the default two-part fp16 scores (see
- * ot_problem flags).
+ * final potentials are not finite. OT_ERR_UNSUPPORTED also when fp32 points
+ * are too large for the default two-part fp16 scores (see ot_problem flags).
  */
 int ot_solve(const ot_problem* p, float* f, float* g, const ot_solve_opts* opts,
              ot_solve_info* info, void* ws, size_t* ws_bytes, void* stream);
@@ -277,7 +294,10 @@ int ot_sinkhorn_divergence(const ot_problem* p, const ot_solve_opts* opts, float
  * potentials (§3.2), so early-stopped potentials apply their own coupling.
  *   f, g    device fp32 (n, m)
  *   V       device, (m x cols) for P V or (n x cols) for P^T U, row stride ldv,
- *           storage v_dtype (OT_F32 / OT_BF16); products run in fp32
+ *           storage v_dtype (OT_F32 / OT_BF16). The value product runs on
+ *           the fp16 matrix cores with two fp16 parts per score and per
+ *           (power-of-two scaled) value, three partial products per term;
+ *           fp32 under OT_NATIVE_F32 / OT_SPLIT_BF16 (see ot_problem flags)
  *   cols    1 <= cols <= OT_MAX_COLS
  *   flags   0 or OT_TRANSPOSE, optionally with one of OT_GRAD / OT_BARY
  *   out     device fp32, row-major (n x cols) or (m x cols), stride cols
@@ -292,7 +312,8 @@ int ot_sinkhorn_divergence(const ot_problem* p, const ot_solve_opts* opts, float
  *                           the other cloud is the value matrix.
  *   marg    device fp32 (n, or m with OT_TRANSPOSE) or NULL: receives the
  *           induced marginal r = P 1 (resp. c = P^T 1)
- * Errors: OT_ERR_INVALID_ARG, OT_ERR_UNSUPPORTED, OT_ERR_WORKSPACE, OT_ERR_HIP.
+ * Errors: OT_ERR_INVALID_ARG, OT_ERR_UNSUPPORTED (also for fp32 points out
+ * of the fp16 range, see ot_problem flags), OT_ERR_WORKSPACE, OT_ERR_HIP.
  */
 int ot_apply_plan(const ot_problem* p, const float* f, const float* g,
                   const void* V, int v_dtype, int64_t cols, int64_t ldv, int flags,
@@ -357,8 +378,8 @@ typedef struct ot_hvp_info {
  * The conjugate-gradient products (d <= 128) form their scores in the
  * problem's fp32 operand mode (see ot_problem flags).
  * Errors: OT_ERR_INVALID_ARG (null pointer, lda < d, tau < 0, tol < 0,
- * max_iters < 0, non-finite option), OT_ERR_UNSUPPORTED (also, when info is
- * given, points too large for the default two-part fp16 scores),
+ * max_iters < 0, non-finite option), OT_ERR_UNSUPPORTED (also for points
+ * too large for the default two-part fp16 scores),
  * OT_ERR_WORKSPACE, OT_ERR_HIP.
  */
 int ot_hvp(const ot_problem* p, const float* f, const float* g, const float* A, int64_t lda,

@@ -192,6 +192,18 @@ int check_ws(void* ws, size_t* ws_bytes, size_t need, bool* query) {
 
 const char* last_error() { return g_err.c_str(); }
 
+int check_half2_range(const Half2Plan* plan, hipStream_t st) {
+  int ok = 0;
+  OT_HIP(hipMemcpyAsync(&ok, &plan->ok, sizeof(int), hipMemcpyDeviceToHost, st));
+  OT_HIP(hipStreamSynchronize(st));
+  if (!ok)
+    return fail(OT_ERR_UNSUPPORTED,
+                "fp32 coordinates too large for the two-part fp16 scores "
+                "((2/eps) log2(e) max|x| max|y| at or above 2^29); OT_SPLIT_BF16 or OT_NATIVE_F32 "
+                "cover the fp32 range");
+  return OT_OK;
+}
+
 }  // namespace host
 }  // namespace flashot
 
@@ -335,6 +347,8 @@ int prepare(const Ctx& x, hipStream_t st) {
     // the range plan is taken at the problem's eps, the largest X scale of the call
     OT_HIP(launch_half2_plan((const float*)p->x, p->n, p->ldx, (const float*)p->y, p->m, p->ldy, p->d,
                              x.xscale, x.plan, st));
+    const int rc = check_half2_range(x.plan, st);
+    if (rc) return rc;
     OT_HIP(launch_pack_half2((const float*)p->y, p->m, p->d, p->ldy, x.L.mtiles, x.L.k.kbp, 1.f,
                              x.plan, 1, x.yp, st));
   } else if (x.L.k.mode == kModeSplit)
@@ -634,7 +648,7 @@ ApplyWs apply_layout(const ot_problem* p, int64_t cols, bool transpose) {
   w.o_hr = take((size_t)w.rpad * 4);
   w.o_wc = take((size_t)w.cpad * 4);
   w.o_hc = take((size_t)w.cpad * 4);
-  w.o_bc = take((size_t)w.cpad * 4);
+  w.o_bc = take(bias_buffer_bytes(w.cpad));  // biases + bias-MFMA operand
   w.o_vp = take((size_t)w.ctiles * w.pblocks * 4096);
   w.o_ms = take((size_t)w.S.splits * w.rpad * 8);
   w.o_o = take((size_t)w.S.splits * w.ppad * w.rpad * 4);
@@ -752,21 +766,29 @@ int ot_solve(const ot_problem* p, float* f, float* g, const ot_solve_opts* o,
       done = o->iters;
     }
     if (info) {
-      // Exact marginal errors of the returned (f, g): one dry pass per side.
-      if (done == 0)
-        OT_HIP(launch_bias_from_pot(f, x.nx, x.hx, (int)p->n, L.npad, x.bscale, x.bx, 1, st));
+      // Marginal errors of the returned (f, g). Rows: one dry f pass from g
+      // (the bias `by` is current: written by the last g merge or by
+      // rebuild_biases). Columns: in the alternating schedule, when the last
+      // iteration ran at the problem's eps, its g half-step fit the columns
+      // and the error is 0 by construction (a dry pass would reproduce g
+      // bitwise); otherwise (symmetric schedule, no iteration, or every
+      // iteration annealed) one dry g pass from f, with the bias of f rebuilt
+      // at the problem's eps where it is stale.
       rc = half_f(x, st, 1, 0);
       if (rc) return rc;
       OT_HIP(launch_err_reduce(x.errp, L.errblocks_f, x.errv, st));
-      rc = half_g(x, st, 1, 0);
-      if (rc) return rc;
-      OT_HIP(launch_err_reduce(x.errp + L.errblocks_f, L.errblocks_g, x.errv + 1, st));
+      if (!x.sym && done > annealed) {
+        OT_HIP(launch_fill(x.errv + 1, 0.f, 1, st));
+      } else {
+        if (!x.sym)
+          OT_HIP(launch_bias_from_pot(f, x.nx, x.hx, (int)p->n, L.npad, x.bscale, x.bx, 1, st));
+        rc = half_g(x, st, 1, 0);
+        if (rc) return rc;
+        OT_HIP(launch_err_reduce(x.errp + L.errblocks_f, L.errblocks_g, x.errv + 1, st));
+      }
       OT_HIP(launch_nonfinite(f, (int)p->n, g, (int)p->m, x.errv + 2, st));
       float h[3] = {0.f, 0.f, 0.f};
-      int in_range = 1;
       OT_HIP(hipMemcpyAsync(h, x.errv, sizeof(h), hipMemcpyDeviceToHost, st));
-      if (L.k.mode == kModeHalf2)
-        OT_HIP(hipMemcpyAsync(&in_range, &x.plan->ok, sizeof(int), hipMemcpyDeviceToHost, st));
       OT_HIP(hipStreamSynchronize(st));
       info->iters_done = done;
       info->marg_err_row = h[0];
@@ -777,10 +799,6 @@ int ot_solve(const ot_problem* p, float* f, float* g, const ot_solve_opts* o,
       info->splits_f = L.F.splits;
       info->splits_g = L.G.splits;
       info->operand_mode = L.k.mode;
-      if (!in_range)
-        return fail(OT_ERR_UNSUPPORTED,
-                    "fp32 coordinates too large for the two-part fp16 scores "
-                    "((2/eps) log2(e) max|x| max|y| >= 2^28); OT_SPLIT_BF16 covers the fp32 range");
       if (info->nonfinite) return fail(OT_ERR_NONFINITE, "potentials are not finite");
     }
     return OT_OK;
@@ -895,6 +913,8 @@ int ot_apply_plan(const ot_problem* p, const float* f, const float* g, const voi
       Half2Plan* plan = (Half2Plan*)(w + L.o_plan);
       OT_HIP(launch_half2_plan((const float*)p->x, p->n, p->ldx, (const float*)p->y, p->m, p->ldy,
                                p->d, c * xs, plan, st));
+      rc = check_half2_range(plan, st);
+      if (rc) return rc;
       OT_HIP(launch_pack_half2((const float*)p->x, p->n, p->d, p->ldx, ntiles, L.k.kbp, c * xs,
                                plan, 0, xp, st));
       OT_HIP(launch_pack_half2((const float*)p->y, p->m, p->d, p->ldy, mtiles, L.k.kbp, 1.f, plan,
@@ -923,14 +943,14 @@ int ot_apply_plan(const ot_problem* p, const float* f, const float* g, const voi
     float* po = (float*)(w + L.o_o);
     OT_HIP(launch_weights(wr_user, (int)rows, L.rpad, eps, wr, hr, st));
     OT_HIP(launch_weights(ws_user, (int)srows, L.cpad, eps, wc, hc, st));
-    OT_HIP(launch_bias_from_pot(pot_s, norm_s, hc, (int)srows, L.cpad, h2 ? c : 1.f, bc, 0, st));
+    OT_HIP(launch_bias_from_pot(pot_s, norm_s, hc, (int)srows, L.cpad, h2 ? c : 1.f, bc, 1, st));
     unsigned* vamax = fp16_values ? (unsigned*)(w + L.o_vamax) : nullptr;
     if (fp16_values) {
       OT_HIP(launch_vcol_absmax(V, v_dtype == OT_BF16, srows, cols, ldv, vamax, st));
       OT_HIP(launch_pack_values_h2(V, v_dtype == OT_BF16, srows, cols, ldv, L.ctiles, L.pblocks,
                                    vamax, vp, st));
-      OT_HIP(launch_apply_h2(L.S, L.k.mode, L.pblocks, L.pb_per_pass, Rp, Cp, bc, vp, kc, pms,
-                             po, L.ppad, st));
+      OT_HIP(launch_apply_stream(L.S, L.k.mode, L.pblocks, L.pb_per_pass, Rp, Cp, bc, vp, kc, pms,
+                                 po, L.ppad, st));
     } else {
       OT_HIP(launch_pack_values(V, v_dtype == OT_BF16, srows, cols, ldv, L.ctiles, L.pblocks, vp,
                                 st));
@@ -940,7 +960,9 @@ int ot_apply_plan(const ot_problem* p, const float* f, const float* g, const voi
     const int mode = grad ? kApplyGrad : ((flags & OT_BARY) ? kApplyBary : kApplyPlain);
     const void* Xsrc = tr ? p->y : p->x;
     const int64_t ldx = tr ? p->ldy : p->ldx;
-    OT_HIP(launch_apply_merge(pms, po, L.S.splits, L.rpad, L.ppad, (int)rows, (int)cols, kc, eps,
+    // the fp16-value kernels write their stabilisers in log2 units
+    OT_HIP(launch_apply_merge(pms, po, L.S.splits, L.rpad, L.ppad, (int)rows, (int)cols,
+                              fp16_values ? 1.f : c, eps,
                               pot_r, norm_r, wr, mode, Xsrc, bf, ldx, vamax, out, marg, st));
     return OT_OK;
   } catch (...) {

@@ -247,7 +247,7 @@ __global__ __launch_bounds__(256) void apply_h2_kernel(
 
   S += __shfl_xor(S, 32);
   const size_t row = (size_t)rt * kTile + (lane & 31);
-  if (blockIdx.y == 0 && h == 0) partMS[(size_t)s * rpad + row] = make_float2(M, S);
+  if (blockIdx.y == 0 && h == 0) partMS[(size_t)s * rpad + row] = make_float2(c * M, S);
 #pragma unroll
   for (int pb = 0; pb < PB; ++pb) {
     if (pb0 + pb < pblocks) {
@@ -260,6 +260,341 @@ __global__ __launch_bounds__(256) void apply_h2_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Pipelined transport application for register-resident row tiles: the
+// log-sum-exp pass's machinery (device_common.h) with the value product
+// added. Per wave one row tile (32 rows) in registers; the four waves of a
+// workgroup share each column tile -- its score operand and its PB blocks of
+// fp16 value parts -- through a four-slot LDS ring. Stage k
+//  * scores tile k+1 on the matrix cores (two score tiles in flight),
+//  * multiplies the values of tile k-1 into O (its p parts were formed in
+//    stage k-1), so that stage's matrix work does not wait for its own
+//    exponentials,
+//  * exponentiates tile k and splits p into fp16 parts on the vector unit,
+//  * and stages tile k+2 into the slot of tile k-2 (one barrier per stage).
+// The stabiliser is raised lazily: p = exp2(score - M) is used as computed
+// while the tile sum stays below 2^15 (so every p fits the fp16 parts), and
+// only a tile past that (or, with M folded into the bias MFMA, scored with
+// an older M) takes the exact path that raises M to the tile maximum and
+// rescales S and O.
+// Partials per split and row: (M in log2 units, S) and O, as the merge
+// (apply_merge_kernel, c = 1) expects.
+// ---------------------------------------------------------------------------
+constexpr float kApplyTileSumLimit = 0x1p15f;
+
+// Two ways the stabiliser M enters a tile, chosen by the operand mode:
+//  * FOLD (two-part fp16 scores, already in log2 units): M is folded into the
+//    bias MFMA like in the log-sum-exp pass, so a tile's exponent is the
+//    accumulator itself; a tile scored with an older M takes the exact path;
+//  * not FOLD (fp32 or bf16 scores in dot-product units, multiplied by c):
+//    the accumulator holds score + bias and p = exp2(fma(c, a, -c M)) with
+//    the current M, one rounding at the exponent's magnitude, as in the
+//    fp32-value application pass.
+// Common-case tile: p and their sum s. Returns whether the exact path is
+// needed: the sum (hence some p) could leave the fp16 range, is NaN, M is not
+// yet set from data, or (FOLD) the tile was scored with an older M.
+template <bool FOLD>
+__device__ __forceinline__ bool apply_fast(const f32x16& a, float Mf, float M, float ks, f32x16& p,
+                                           float& s) {
+  float e[4] = {0.f, 0.f, 0.f, 0.f};
+  const float kM = -ks * M;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    p[r] = __builtin_amdgcn_exp2f(FOLD ? a[r] : fmaf(ks, a[r], kM));
+    e[r & 3] += p[r];
+  }
+  s = (e[0] + e[1]) + (e[2] + e[3]);
+  if constexpr (FOLD) return !(s < kApplyTileSumLimit) | (Mf != M);
+  else return !(s < kApplyTileSumLimit) | !(M > 0.5f * kUnset);
+}
+
+// Exact path: p recomputed against a stabiliser M that bounds every p of
+// the tile by 2^8. M stays while the tile maximum (shared by the lane pair
+// that holds the row) is within 8 of it in log2 units, else it is raised to
+// that maximum and S and O are rescaled. Raising only past that margin
+// keeps the raises, and the exact path of the tile already scored with the
+// old M that each raise costs, rare once a row's first tiles are in; a tile
+// that took the path for its sum (>= 2^15, so some p >= 2^11) always raises.
+// FOLD: exponents from the scores u = a + Mf as rounded, as in lse_exact.
+constexpr float kApplyRaiseMargin = 8.0f;
+
+template <bool FOLD, int PB>
+__device__ __forceinline__ void apply_exact(const f32x16& a, float Mf, float& M, float& S,
+                                            f32x16 (&O)[PB], float ks, f32x16& p) {
+  float m = FOLD ? a[0] + Mf : a[0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) m = fmaxf(m, FOLD ? a[r] + Mf : a[r]);
+  m = fmaxf(m, __shfl_xor(m, 32));
+  // M not set (kUnset): the tile maximum
+  const float Mn = (M > 0.5f * kUnset && ks * (m - M) <= kApplyRaiseMargin) ? M : fmaxf(m, M);
+  const float sc = __builtin_amdgcn_exp2f(ks * (M - Mn));  // 0 when M was not set
+  const float kM = -ks * Mn;
+  float e[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    p[r] = __builtin_amdgcn_exp2f(FOLD ? ks * ((a[r] + Mf) - Mn) : fmaf(ks, a[r], kM));
+    e[r & 3] += p[r];
+  }
+  S = fmaf(S, sc, (e[0] + e[1]) + (e[2] + e[3]));
+#pragma unroll
+  for (int pb = 0; pb < PB; ++pb) O[pb] *= sc;
+  M = Mn;
+}
+
+// p (accumulator entries 8q .. 8q+7 are the B operand of k-chunk q) as fp16
+// parts: hi = fp16(p) and lo = fp16(p - hi), both rounded to nearest.
+__device__ __forceinline__ void split_p(const f32x16& p, u32x4 (&ph)[2], u32x4 (&pl)[2]) {
+  typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+  typedef float f2v __attribute__((ext_vector_type(2)));
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const f2v v = {p[8 * q + 2 * w], p[8 * q + 2 * w + 1]};
+      const h2v hi = __builtin_convertvector(v, h2v);
+      const h2v lo = __builtin_convertvector(v - __builtin_convertvector(hi, f2v), h2v);
+      ph[q][w] = __builtin_bit_cast(uint32_t, hi);
+      pl[q][w] = __builtin_bit_cast(uint32_t, lo);
+    }
+}
+
+// Value product of one tile for one 32-column value block: O^T += V^T P^T
+// with V's hi / lo parts at units vb[0..3] = (chunk 0 hi, chunk 0 lo,
+// chunk 1 hi, chunk 1 lo), smallest products first.
+__device__ __forceinline__ f32x16 value_block(const u32x4* __restrict__ vb, int lane,
+                                              const u32x4 (&ph)[2], const u32x4 (&pl)[2],
+                                              f32x16 o) {
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const f16x8 vh = __builtin_bit_cast(f16x8, vb[(2 * q) * 64 + lane]);
+    const f16x8 vl = __builtin_bit_cast(f16x8, vb[(2 * q + 1) * 64 + lane]);
+    o = __builtin_amdgcn_mfma_f32_32x32x16_f16(vl, __builtin_bit_cast(f16x8, ph[q]), o, 0, 0, 0);
+    o = __builtin_amdgcn_mfma_f32_32x32x16_f16(vh, __builtin_bit_cast(f16x8, pl[q]), o, 0, 0, 0);
+    o = __builtin_amdgcn_mfma_f32_32x32x16_f16(vh, __builtin_bit_cast(f16x8, ph[q]), o, 0, 0, 0);
+  }
+  return o;
+}
+
+template <int SMODE, int KB, int PB>
+__global__ __launch_bounds__(256) void apply_res_kernel(
+    const u32x4* __restrict__ Rp, const u32x4* __restrict__ Cp, const float* __restrict__ cbias,
+    const u32x4* __restrict__ Vh, int rtiles, int ctiles, int splits, int tps, float c,
+    int pblocks, float2* __restrict__ partMS, float* __restrict__ partO, int rpad, int ppad) {
+  constexpr int TU = KB + 4 * PB;             // staged 1 KiB units per column tile
+  constexpr int NL = (TU * 64 + 255) / 256;   // staging loads per thread
+  constexpr bool FOLD = SMODE == kModeHalf2;  // scores in log2 units, M folded into the bias MFMA
+  __shared__ u32x4 lds[4][NL * 256];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int h = lane >> 5;
+  const int s = blockIdx.x % splits;
+  const int rg = blockIdx.x / splits;
+  // may be past the last row tile: the wave still takes part in loads and barriers
+  const int rt = rg * kWaves + wave;
+  const int pb0 = blockIdx.y * PB;
+  const int npb = min(PB, pblocks - pb0);     // value blocks of this pass, >= 1
+  const int jt0 = s * tps;
+  const int last = min(jt0 + tps, ctiles) - 1 - jt0;  // split holds tiles 0..last
+  const float ks = FOLD ? 1.0f : c;
+  const uint2* __restrict__ cb3 = bias_parts(cbias, ctiles * kTile);
+
+  // Staging slots of this thread: unit u of the staged tile (score operand
+  // units first, then the pass's value units), lane le of the unit. A wave's
+  // 64 threads take one unit, so the source choice is wave-uniform; threads
+  // past the end re-read the last unit into the padding.
+  const u32x4* src[NL];
+  size_t stride[NL];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int e = min(tid + 256 * i, TU * 64 - 1);
+    const int u = e >> 6, le = e & 63;
+    if (u < KB) {
+      src[i] = Cp + (size_t)u * 64 + le;
+      stride[i] = (size_t)KB * 64;
+    } else {
+      src[i] = Vh + ((size_t)pb0 * 4 + min(u - KB, 4 * npb - 1)) * 64 + le;
+      stride[i] = (size_t)pblocks * 4 * 64;
+    }
+  }
+  auto gload = [&](int jt, u32x4 (&g)[NL]) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) g[i] = src[i][(size_t)jt * stride[i]];
+  };
+  auto sstore = [&](int slot, const u32x4 (&g)[NL]) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) lds[slot][tid + 256 * i] = g[i];
+  };
+
+  u32x4 xr[1][KB];
+  {
+    const int rtc = min(rt, rtiles - 1);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) xr[0][kb] = Rp[((size_t)rtc * KB + kb) * 64 + lane];
+  }
+  float M[1] = {kUnset}, S = 0.f, Mfc[1];
+  BiasOp<SMODE> Bst[1];
+  refold<SMODE, 1>(M, h, Mfc, Bst);
+  f32x16 O[PB];
+#pragma unroll
+  for (int pb = 0; pb < PB; ++pb) O[pb] = f32x16{};
+
+  auto score = [&](int slot, BiasOp<SMODE> ab, f32x16& acc) {
+    u32x4 y[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) y[kb] = lds[slot][kb * 64 + lane];
+    f32x16 a1[1];
+    score_tile<SMODE, KB, 1>(y, xr, ab, Bst, h, a1);
+    acc = a1[0];
+  };
+  // Every block of the pass is multiplied (a pass's last blocks past npb
+  // repeat the last staged unit and are never written): no branch inside
+  // the scheduled stage.
+  auto values = [&](int slot, const u32x4 (&ph)[2], const u32x4 (&pl)[2]) {
+    const u32x4* vb = &lds[slot][KB * 64];
+#pragma unroll
+    for (int pb = 0; pb < PB; ++pb) O[pb] = value_block(vb + pb * 4 * 64, lane, ph, pl, O[pb]);
+  };
+
+  // Prologue: tiles 0 and 1 staged, tile 0 scored.
+  u32x4 g[NL];
+  gload(jt0, g);
+  sstore(0, g);
+  gload(jt0 + min(1, last), g);
+  sstore(1, g);
+  BiasOp<SMODE> aA = load_bias<SMODE>(cbias, cb3, jt0, lane);
+  BiasOp<SMODE> aB = load_bias<SMODE>(cbias, cb3, jt0 + min(1, last), lane);
+  __syncthreads();
+  f32x16 accA, accB;
+  float MfA = Mfc[0], MfB = 0.f;
+  score(0, aA, accA);
+  u32x4 phA[2], plA[2], phB[2], plB[2];
+
+  // Stage k: tile k (accC, scored with MfC) is exponentiated and split into
+  // phC / plC; with PREV the values of tile k-1 (parts phP / plP) enter O;
+  // with NEXT tile k+1 is scored into accN and tile k+2 is staged.
+  auto stage = [&](int k, auto next, auto prev, f32x16& accN, float& MfN, BiasOp<SMODE>& aN,
+                   const f32x16& accC, float MfC, BiasOp<SMODE>& aC, const u32x4 (&phP)[2],
+                   const u32x4 (&plP)[2], u32x4 (&phC)[2], u32x4 (&plC)[2]) {
+    constexpr bool NEXT = decltype(next)::value;
+    constexpr bool PREV = decltype(prev)::value;
+    __syncthreads();  // tile k+1 is in its slot; every wave is done with stage k-1
+    BiasOp<SMODE> a2{};
+    if constexpr (NEXT) {
+      const int jt2 = jt0 + min(k + 2, last);
+      gload(jt2, g);
+      a2 = load_bias<SMODE>(cbias, cb3, jt2, lane);
+      MfN = Mfc[0];
+      score((k + 1) & 3, aN, accN);
+    }
+    if constexpr (PREV) values((k - 1) & 3, phP, plP);
+    f32x16 p;
+    float ts;
+    const bool slow = apply_fast<FOLD>(accC, MfC, M[0], ks, p, ts);
+    split_p(p, phC, plC);
+    if constexpr (NEXT || PREV) {
+      constexpr int kMfma = (NEXT ? tile_mfmas<SMODE, KB>() + 1 : 0) + (PREV ? 6 * PB : 0);
+      constexpr int kValu = 16 + 16 + 48 + 8;  // exponentials, sums, split, checks
+      constexpr int kValuPer = (kValu + kMfma - 1) / kMfma;
+      if constexpr (NEXT) __builtin_amdgcn_sched_group_barrier(0x020, NL + 1, 0);  // global loads
+#pragma unroll
+      for (int i = 0; i < kMfma; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);         // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, kValuPer, 0);  // VALU
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (__builtin_amdgcn_ballot_w64(slow) != 0) {
+      apply_exact<FOLD, PB>(accC, MfC, M[0], S, O, ks, p);
+      split_p(p, phC, plC);
+      if constexpr (FOLD) refold<SMODE, 1>(M, h, Mfc, Bst);
+    } else {
+      S += ts;
+    }
+    if constexpr (NEXT) {
+      sstore((k + 2) & 3, g);
+      aC = a2;  // tile k's operand slot now belongs to tile k+2
+    }
+  };
+
+  using Yes = std::integral_constant<bool, true>;
+  using No = std::integral_constant<bool, false>;
+  if (last == 0) {
+    stage(0, No{}, No{}, accB, MfB, aB, accA, MfA, aA, phB, plB, phA, plA);
+    values(0, phA, plA);
+  } else {
+    stage(0, Yes{}, No{}, accB, MfB, aB, accA, MfA, aA, phB, plB, phA, plA);
+    int k = 1;  // at the top: tile k's scores in accB, tile k-1's parts in phA / plA
+    for (; k + 2 <= last; k += 2) {
+      stage(k, Yes{}, Yes{}, accA, MfA, aA, accB, MfB, aB, phA, plA, phB, plB);
+      stage(k + 1, Yes{}, Yes{}, accB, MfB, aB, accA, MfA, aA, phB, plB, phA, plA);
+    }
+    if (k + 1 == last) {  // stages k and k+1 = last remain
+      stage(k, Yes{}, Yes{}, accA, MfA, aA, accB, MfB, aB, phA, plA, phB, plB);
+      stage(k + 1, No{}, Yes{}, accB, MfB, aB, accA, MfA, aA, phB, plB, phA, plA);
+      values((k + 1) & 3, phA, plA);
+    } else {              // stage k = last remains
+      stage(k, No{}, Yes{}, accA, MfA, aA, accB, MfB, aB, phA, plA, phB, plB);
+      values(k & 3, phB, plB);
+    }
+  }
+
+  S += __shfl_xor(S, 32);
+  if (rt >= rtiles) return;
+  const size_t row = (size_t)rt * kTile + (lane & 31);
+  if (blockIdx.y == 0 && h == 0) partMS[(size_t)s * rpad + row] = make_float2(ks * M[0], S);
+#pragma unroll
+  for (int pb = 0; pb < PB; ++pb) {
+    if (pb < npb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int pcol = 32 * (pb0 + pb) + 8 * (r >> 2) + 4 * h + (r & 3);
+        partO[((size_t)s * ppad + pcol) * rpad + row] = O[pb][r];
+      }
+    }
+  }
+}
+
+template <int SMODE, int KB, int PB>
+static void apply_res_go(const PassShape& s, int pblocks, const void* Rp, const void* Cp,
+                         const float* cbias, const void* Vh, float c, float2* partMS,
+                         float* partO, int ppad, hipStream_t st) {
+  dim3 grid(s.nrowgroups * s.splits, (pblocks + PB - 1) / PB);
+  apply_res_kernel<SMODE, KB, PB><<<grid, 256, 0, st>>>(
+      (const u32x4*)Rp, (const u32x4*)Cp, cbias, (const u32x4*)Vh, s.rtiles, s.ctiles, s.splits,
+      s.tps, c, pblocks, partMS, partO, s.rtiles * kTile, ppad);
+}
+
+template <int SMODE, int PB>
+static hipError_t apply_res_kb(const PassShape& s, int pblocks, const void* Rp, const void* Cp,
+                               const float* cbias, const void* Vh, float c, float2* partMS,
+                               float* partO, int ppad, hipStream_t st) {
+  // Value blocks per pass: at most two (16 units of row operand: one), which
+  // keeps the kernel at two waves per SIMD without register spills; wider
+  // value matrices take more passes over the same scores.
+#define RES_CASE(K)                                                                         \
+  case K:                                                                                   \
+    apply_res_go<SMODE, K, (K >= 16 ? 1 : (PB > 2 ? 2 : PB))>(s, pblocks, Rp, Cp, cbias, Vh, \
+                                                             c, partMS, partO, ppad, st);    \
+    break;
+  switch (s.kb) {
+    case 1:
+      if constexpr (SMODE == kModeHalf2) return hipErrorInvalidValue;
+      else
+        apply_res_go<SMODE, 1, (PB > 2 ? 2 : PB)>(s, pblocks, Rp, Cp, cbias, Vh, c, partMS, partO,
+                                                 ppad, st);
+      break;
+    RES_CASE(2)
+    RES_CASE(4)
+    RES_CASE(8)
+    RES_CASE(16)
+    default: return hipErrorInvalidValue;
+  }
+#undef RES_CASE
+  return hipGetLastError();
+}
+
 template <int SMODE, int KB, bool XRES, int PB>
 static void apply_h2_go(const PassShape& s, int pblocks, const void* Rp, const void* Cp,
                         const float* cbias, const void* Vh, float c, float2* partMS, float* partO,
@@ -270,50 +605,42 @@ static void apply_h2_go(const PassShape& s, int pblocks, const void* Rp, const v
       s.splits, s.tps, c, pblocks, partMS, partO, s.rtiles * kTile, ppad);
 }
 
+// Pass with the value product on fp16 parts: the pipelined resident kernel,
+// or the chunked kernel when the row operand is not resident.
 template <int SMODE, int PB>
-static hipError_t apply_h2_kb(const PassShape& s, int pblocks, const void* Rp, const void* Cp,
-                              const float* cbias, const void* Vh, float c, float2* partMS,
-                              float* partO, int ppad, hipStream_t st) {
-  if (!s.xres) {
-    apply_h2_go<SMODE, 8, false, PB>(s, pblocks, Rp, Cp, cbias, Vh, c, partMS, partO, ppad, st);
-    return hipGetLastError();
-  }
-  switch (s.kb) {
-    case 1: if constexpr (SMODE != kModeHalf2) { apply_h2_go<SMODE, 1, true, PB>(s, pblocks, Rp, Cp, cbias, Vh, c, partMS, partO, ppad, st); break; } else { return hipErrorInvalidValue; }
-    case 2: apply_h2_go<SMODE, 2, true, PB>(s, pblocks, Rp, Cp, cbias, Vh, c, partMS, partO, ppad, st); break;
-    case 4: apply_h2_go<SMODE, 4, true, PB>(s, pblocks, Rp, Cp, cbias, Vh, c, partMS, partO, ppad, st); break;
-    case 8: apply_h2_go<SMODE, 8, true, PB>(s, pblocks, Rp, Cp, cbias, Vh, c, partMS, partO, ppad, st); break;
-    case 16: apply_h2_go<SMODE, 16, true, PB>(s, pblocks, Rp, Cp, cbias, Vh, c, partMS, partO, ppad, st); break;
-    default: return hipErrorInvalidValue;
-  }
+static hipError_t apply_stream_pb(const PassShape& s, int pblocks, const void* Rp, const void* Cp,
+                                  const float* cbias, const void* Vh, float c, float2* partMS,
+                                  float* partO, int ppad, hipStream_t st) {
+  if (s.xres) return apply_res_kb<SMODE, PB>(s, pblocks, Rp, Cp, cbias, Vh, c, partMS, partO, ppad, st);
+  apply_h2_go<SMODE, 8, false, PB>(s, pblocks, Rp, Cp, cbias, Vh, c, partMS, partO, ppad, st);
   return hipGetLastError();
 }
 
 template <int SMODE>
-static hipError_t apply_h2_dispatch(const PassShape& s, int pblocks, int pb_per_pass,
-                                    const void* Rp, const void* Cp, const float* cbias,
-                                    const void* Vh, float c, float2* partMS, float* partO,
-                                    int ppad, hipStream_t st) {
+static hipError_t apply_stream_dispatch(const PassShape& s, int pblocks, int pb_per_pass,
+                                        const void* Rp, const void* Cp, const float* cbias,
+                                        const void* Vh, float c, float2* partMS, float* partO,
+                                        int ppad, hipStream_t st) {
   switch (pb_per_pass) {
-    case 1: return apply_h2_kb<SMODE, 1>(s, pblocks, Rp, Cp, cbias, Vh, c, partMS, partO, ppad, st);
-    case 2: return apply_h2_kb<SMODE, 2>(s, pblocks, Rp, Cp, cbias, Vh, c, partMS, partO, ppad, st);
-    case 4: return apply_h2_kb<SMODE, 4>(s, pblocks, Rp, Cp, cbias, Vh, c, partMS, partO, ppad, st);
+    case 1: return apply_stream_pb<SMODE, 1>(s, pblocks, Rp, Cp, cbias, Vh, c, partMS, partO, ppad, st);
+    case 2: return apply_stream_pb<SMODE, 2>(s, pblocks, Rp, Cp, cbias, Vh, c, partMS, partO, ppad, st);
+    case 4: return apply_stream_pb<SMODE, 4>(s, pblocks, Rp, Cp, cbias, Vh, c, partMS, partO, ppad, st);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_apply_h2(const PassShape& s, int smode, int pblocks, int pb_per_pass,
-                           const void* Rp, const void* Cp, const float* cbias, const void* Vh,
-                           float c, float2* partMS, float* partO, int ppad, hipStream_t st) {
+hipError_t launch_apply_stream(const PassShape& s, int smode, int pblocks, int pb_per_pass,
+                               const void* Rp, const void* Cp, const float* cbias, const void* Vh,
+                               float c, float2* partMS, float* partO, int ppad, hipStream_t st) {
   if (smode == kModeHalf2)
-    return apply_h2_dispatch<kModeHalf2>(s, pblocks, pb_per_pass, Rp, Cp, cbias, Vh, c, partMS,
-                                         partO, ppad, st);
+    return apply_stream_dispatch<kModeHalf2>(s, pblocks, pb_per_pass, Rp, Cp, cbias, Vh, c, partMS,
+                                             partO, ppad, st);
   if (smode == kModeBF16)
-    return apply_h2_dispatch<kModeBF16>(s, pblocks, pb_per_pass, Rp, Cp, cbias, Vh, c, partMS,
-                                        partO, ppad, st);
+    return apply_stream_dispatch<kModeBF16>(s, pblocks, pb_per_pass, Rp, Cp, cbias, Vh, c, partMS,
+                                            partO, ppad, st);
   if (smode == kModeF32)
-    return apply_h2_dispatch<kModeF32>(s, pblocks, pb_per_pass, Rp, Cp, cbias, Vh, c, partMS,
-                                       partO, ppad, st);
+    return apply_stream_dispatch<kModeF32>(s, pblocks, pb_per_pass, Rp, Cp, cbias, Vh, c, partMS,
+                                           partO, ppad, st);
   return hipErrorInvalidValue;
 }
 

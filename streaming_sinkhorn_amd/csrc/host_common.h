@@ -59,6 +59,10 @@ int check_problem(const ot_problem* p);
 // ws == NULL: writes need to *ws_bytes and sets *query; otherwise checks size
 // and alignment.
 int check_ws(void* ws, size_t* ws_bytes, size_t need, bool* query);
+// fp32 points in the two-part fp16 operand mode: waits for the range plan on
+// `st` (one stream synchronisation) and returns OT_ERR_UNSUPPORTED when the
+// points do not fit the fp16 parts, before the passes that read them.
+int check_half2_range(const Half2Plan* plan, hipStream_t st);
 
 }  // namespace host
 }  // namespace flashot

@@ -156,10 +156,12 @@ int transport(const Transport& t, bool tr, const float* V, int64_t cols, int64_t
   } else {
     OT_HIP(launch_vcol_absmax(V, 0, srows, cols, ldv, t.vamax, st));
     OT_HIP(launch_pack_values_h2(V, 0, srows, cols, ldv, S.ctiles, cc.pblocks, t.vamax, t.vp, st));
-    OT_HIP(launch_apply_h2(S, kModeF32, cc.pblocks, cc.pb_per_pass, Rp, Cp, bc, t.vp, t.c, t.pms,
-                           t.po, cc.ppad, st));
+    OT_HIP(launch_apply_stream(S, kModeF32, cc.pblocks, cc.pb_per_pass, Rp, Cp, bc, t.vp, t.c,
+                               t.pms, t.po, cc.ppad, st));
   }
-  OT_HIP(launch_apply_merge(t.pms, t.po, S.splits, rpad, cc.ppad, (int)rows, (int)cols, t.c,
+  // the fp16-value kernels write their stabilisers in log2 units
+  OT_HIP(launch_apply_merge(t.pms, t.po, S.splits, rpad, cc.ppad, (int)rows, (int)cols,
+                            hadamard ? t.c : 1.f,
                             t.eps, tr ? t.g : t.f, tr ? t.ny : t.nx, tr ? t.wy : t.wx, kApplyPlain,
                             nullptr, 0, 0, hadamard ? nullptr : t.vamax, out, marg, st));
   return OT_OK;
@@ -277,6 +279,8 @@ int prepare_vec(const Transport& t, const VecWs& v, char* w, hipStream_t st) {
     Half2Plan* plan = (Half2Plan*)(w + v.o_plan);
     OT_HIP(launch_half2_plan((const float*)p->x, p->n, p->ldx, (const float*)p->y, p->m, p->ldy,
                              p->d, t.c, plan, st));
+    const int rc = check_half2_range(plan, st);
+    if (rc) return rc;
     OT_HIP(launch_pack_half2((const float*)p->x, p->n, p->d, p->ldx, L.ntiles, v.k.kbp, t.c, plan,
                              0, xs, st));
     OT_HIP(launch_pack_half2((const float*)p->y, p->m, p->d, p->ldy, L.mtiles, v.k.kbp, 1.f, plan,
@@ -451,19 +455,11 @@ int ot_hvp(const ot_problem* p, const float* f, const float* g, const float* A, 
     OT_HIP(launch_hvp_final(n, d, p->eps, X, p->ldx, A, lda, PY, r, xa, ra1, PF, B5, out, st));
     if (info) {
       CgState h{};
-      int in_range = 1;
       OT_HIP(hipMemcpyAsync(&h, cs, sizeof(h), hipMemcpyDeviceToHost, st));
-      if (L.V.on && L.V.k.mode == kModeHalf2)
-        OT_HIP(hipMemcpyAsync(&in_range, &((const Half2Plan*)(w + L.V.o_plan))->ok, sizeof(int),
-                              hipMemcpyDeviceToHost, st));
       OT_HIP(hipStreamSynchronize(st));
       info->cg_iters = h.iters;
       info->breakdown = h.breakdown;
       info->cg_rel_residual = h.bb > 0.f ? std::sqrt(h.rr / h.bb) : 0.f;
-      if (!in_range)
-        return fail(OT_ERR_UNSUPPORTED,
-                    "fp32 coordinates too large for the two-part fp16 scores; OT_SPLIT_BF16 "
-                    "covers the fp32 range");
     }
     return OT_OK;
   } catch (...) {

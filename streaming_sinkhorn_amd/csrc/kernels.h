@@ -91,10 +91,13 @@ hipError_t launch_pack_values_h2(const void* V, int bf16, int64_t rows, int64_t 
 // Transport application with the exponentiated scores split into two fp16
 // parts against the fp16 value layout (three products per 16 streamed rows).
 // smode: kModeHalf2 (fp32 points, scores in log2 units, c = 1), kModeBF16 or
-// kModeF32 (fp32 operands, dot-product units).
-hipError_t launch_apply_h2(const PassShape& s, int smode, int pblocks, int pb_per_pass,
-                           const void* Rp, const void* Cp, const float* cbias, const void* Vh,
-                           float c, float2* partMS, float* partO, int ppad, hipStream_t st);
+// kModeF32 (fp32 operands, dot-product units, times c). cbias: a column-bias
+// buffer with the bias-MFMA parts (bias_buffer_bytes) for kModeHalf2 and
+// kModeBF16, fp32 biases alone for kModeF32. Partial stabilisers are written
+// in log2 units (merge with c = 1).
+hipError_t launch_apply_stream(const PassShape& s, int smode, int pblocks, int pb_per_pass,
+                               const void* Rp, const void* Cp, const float* cbias, const void* Vh,
+                               float c, float2* partMS, float* partO, int ppad, hipStream_t st);
 hipError_t launch_pack_values(const void* V, int bf16, int64_t rows, int64_t cols, int64_t ldv,
                               int ctiles, int pblocks, float* dst, hipStream_t st);
 hipError_t launch_weights(const float* w, int rows, int rpad, float eps, float* wgt, float* hlw,

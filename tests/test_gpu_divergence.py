@@ -50,6 +50,18 @@ def test_eps_scaling_trajectory(case):
     say(f"  max|df|={df:.2e} max|dg|={dg:.2e}")
     assert info["iters_done"] == T and not info["nonfinite"]
     assert df <= POT_TOL[w.dtype] and dg <= POT_TOL[w.dtype]
+    # The reported marginal errors are those of the returned potentials at the
+    # problem's eps, also when every iteration ran at a larger eps_k (then the
+    # columns are not fit either). The returned potentials differ from the
+    # oracle's by at most df, dg, so every coupling entry by a factor within
+    # exp(+-(df + dg)/eps): the L1 errors by at most expm1((df + dg)/eps) sum(P).
+    P = oracle.plan(C, a, b, f_ref, g_ref, w.eps)
+    er, ec = oracle.marginal_errors(P, a, b)
+    bound = np.expm1((df + dg) / w.eps) * P.sum() * 1.01 + 2e-6
+    say(f"  marg err row {info['marg_err_row']:.3e} (oracle {er:.3e}), "
+        f"col {info['marg_err_col']:.3e} (oracle {ec:.3e}), bound {bound:.1e}")
+    assert abs(info["marg_err_row"] - er) <= bound + 1e-2 * er
+    assert abs(info["marg_err_col"] - ec) <= bound + 1e-2 * ec
 
 
 def test_eps_scaling_then_plain_graph_replay_is_repeatable():

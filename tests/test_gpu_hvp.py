@@ -209,15 +209,20 @@ def test_hvp_other_fp32_operand_modes(n, m, d, eps, mode):
 
 
 def test_hvp_range_exceeded_reported():
-    """Clouds too large for the two-part fp16 scores: ot_hvp with info reports
-    OT_ERR_UNSUPPORTED instead of returning the NaN product."""
+    """Clouds too large for the two-part fp16 scores: ot_hvp reports
+    OT_ERR_UNSUPPORTED (with or without info) instead of returning a NaN
+    product, and leaves its output unwritten."""
     data = workloads.hvp_parity_inputs(60, 50, 6, seed=3)
     t = lambda v: torch.from_numpy(np.ascontiguousarray(v)).to(DEV)
     prob = ssa.problem(t(data["X"] * 1e5), t(data["Y"] * 1e5), 1.0, t(data["a"]), t(data["b"]))
     f, g = torch.zeros(60, device=DEV), torch.zeros(50, device=DEV)
-    with pytest.raises(ssa.OtError) as ei:
-        ssa.ot_hvp(prob, f, g, t(data["A"]), tau=1e-5, max_iters=3)
-    assert ei.value.code == ssa.OT_ERR_UNSUPPORTED
+    for want_info in (True, False):
+        out = torch.full((60, 6), 7.0, device=DEV)
+        with pytest.raises(ssa.OtError) as ei:
+            ssa.ot_hvp(prob, f, g, t(data["A"]), tau=1e-5, max_iters=3, out=out, want_info=want_info)
+        torch.cuda.synchronize()
+        assert ei.value.code == ssa.OT_ERR_UNSUPPORTED
+        assert bool((out == 7.0).all())
 
 
 def test_hvp_tiny_single_partial_tile():

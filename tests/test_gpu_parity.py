@@ -17,7 +17,7 @@ import torch
 import oracle
 import streaming_sinkhorn_amd as ssa
 import workloads
-from gpu_util import DEV, F32_MODES, host64, make_problem, oracle_inputs, say, zeros
+from gpu_util import DEV, F32_MODES, dev, host64, make_problem, oracle_inputs, say, zeros
 
 pytestmark = pytest.mark.gpu
 
@@ -470,16 +470,38 @@ def test_half2_balances_point_scales(scale_exp):
 
 def test_half2_range_exceeded_reported():
     """Coordinates too large for the two-part fp16 scores ((2/eps) log2(e)
-    max|x| max|y| far above 2^28): ot_solve with info reports
-    OT_ERR_UNSUPPORTED; the three-part bf16 split covers the fp32 range."""
+    max|x| max|y| far above 2^30): every entry point that forms scores from
+    fp32 points in the default mode returns OT_ERR_UNSUPPORTED before
+    enqueuing its passes (outputs untouched), with or without an info struct;
+    the three-part bf16 split covers the fp32 range."""
     data = workloads.make("c1", n=100, m=90)
     data["X"] = (data["X"] * 1e5).astype(np.float32)
     data["Y"] = (data["Y"] * 1e5).astype(np.float32)
     prob = make_problem(data, eps=1.0)
+    V = dev(np.ones((90, 3), dtype=np.float32))
+    U = dev(np.ones((100, 3), dtype=np.float32))
+
+    def refused(call, *outs):
+        marks = [o.fill_(7.0) for o in outs]
+        with pytest.raises(ssa.OtError) as ei:
+            call()
+        torch.cuda.synchronize()
+        assert ei.value.code == ssa.OT_ERR_UNSUPPORTED
+        for o in marks:
+            assert bool((o == 7.0).all()), "a refused call must not write its outputs"
+
     f, g = zeros(100), zeros(90)
-    with pytest.raises(ssa.OtError) as ei:
-        ssa.ot_solve(prob, f, g, 3)
-    assert ei.value.code == ssa.OT_ERR_UNSUPPORTED
+    refused(lambda: ssa.ot_solve(prob, f, g, 3), f, g)
+    refused(lambda: ssa.ot_solve(prob, f, g, 3, want_info=False), f, g)
+    refused(lambda: ssa.ot_solve(prob, f, g, 3, use_graph=False, want_info=False), f, g)
+    refused(lambda: ssa.ot_update_f(prob, g, f), f)
+    refused(lambda: ssa.ot_update_g(prob, f, g), g)
+    out = torch.empty((100, 3), device=DEV)
+    refused(lambda: ssa.ot_apply_plan(prob, f, g, V, out=out), out)
+    outg = torch.empty((100, 16), device=DEV)
+    refused(lambda: ssa.ot_apply_plan(prob, f, g, flags=ssa.OT_GRAD, out=outg), outg)
+    outt = torch.empty((90, 3), device=DEV)
+    refused(lambda: ssa.ot_apply_plan(prob, f, g, U, flags=ssa.OT_TRANSPOSE, out=outt), outt)
     prob = make_problem(data, eps=1.0, mode="split_bf16")
     f, g = zeros(100), zeros(90)
     info = ssa.ot_solve(prob, f, g, 3)
