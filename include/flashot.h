@@ -265,6 +265,31 @@ int ot_solve(const ot_problem* p, float* f, float* g, const ot_solve_opts* opts,
              ot_solve_info* info, void* ws, size_t* ws_bytes, void* stream);
 
 /*
+ * ot_solve_static -- ot_solve for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same iterations and results as ot_solve, with the
+ * library's own static device scratch as the workspace instead of a
+ * caller-supplied one. The call allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine): it launches plain kernels (opts->use_graph
+ * and opts->timing are ignored, since capturing a graph and the timing
+ * events allocate).
+ *   p, f, g, opts, info, stream   as in ot_solve (info may be NULL)
+ * Scratch: ot_static_scratch_bytes() bytes (64 MiB) per device, held from
+ * the library's load on that device until the process ends. Every call on a
+ * device shares that device's scratch and leaves the last call's contents in
+ * it; calls that overlap on one device (concurrent streams or threads) race
+ * and must be serialised by the caller.
+ * Errors: as ot_solve, plus OT_ERR_WORKSPACE when the problem needs more
+ * scratch than the static array holds (its ot_solve workspace size query,
+ * ws == NULL, exceeds ot_static_scratch_bytes()).
+ */
+int ot_solve_static(const ot_problem* p, float* f, float* g, const ot_solve_opts* opts,
+                    ot_solve_info* info, void* stream);
+
+/* Bytes of the static device scratch ot_solve_static uses (per device). */
+size_t ot_static_scratch_bytes(void);
+
+/*
  * ot_sinkhorn_divergence -- debiased Sinkhorn divergence
  *     S_eps(mu, nu) = OT_eps(mu, nu) - OT_eps(mu, mu) / 2 - OT_eps(nu, nu) / 2
  * (the quantity of §1, "debiasing" of App. H.2), each OT_eps the dual value

@@ -119,6 +119,10 @@ def lib() -> ctypes.CDLL:
     L.ot_hvp.argtypes = [pp, vp, vp, vp, i64, ctypes.POINTER(OtHvpOpts), vp,
                          ctypes.POINTER(OtHvpInfo), vp, szp, vp]
     L.ot_probe_rate.argtypes = [i32, i64, ctypes.c_int32, vp, ctypes.POINTER(ctypes.c_double), vp]
+    L.ot_solve_static.argtypes = [pp, vp, vp, ctypes.POINTER(OtSolveOpts), ctypes.POINTER(OtSolveInfo), vp]
+    L.ot_solve_static.restype = ctypes.c_int
+    L.ot_static_scratch_bytes.argtypes = []
+    L.ot_static_scratch_bytes.restype = ctypes.c_size_t
     for fn in ("ot_sqnorms", "ot_update_f", "ot_update_g", "ot_solve", "ot_apply_plan",
                "ot_apply_hadamard", "ot_hvp", "ot_prep_cosine", "ot_prep_labels",
                "ot_sinkhorn_divergence", "ot_probe_rate"):
@@ -137,7 +141,7 @@ def header_entry_points() -> list[str]:
     for fn in sorted(os.listdir(INCLUDE_DIR)):
         if fn.endswith(".h"):
             txt = open(os.path.join(INCLUDE_DIR, fn)).read()
-            names += re.findall(r"^\s*(?:int|const char\*)\s+(ot_\w+)\s*\(", txt, re.M)
+            names += re.findall(r"^\s*(?:int|size_t|const char\*)\s+(ot_\w+)\s*\(", txt, re.M)
     return names
 
 
@@ -266,6 +270,25 @@ def _solve_opts(iters, tol=0.0, check_every=1, init_given=False, use_graph=True,
                        OT_INIT_GIVEN if init_given else OT_INIT_ZERO, int(bool(use_graph)),
                        int(splits_f), int(splits_g), int(bool(timing)), _SCHEDULES[schedule],
                        float(eps_start), float(eps_decay))
+
+
+def ot_solve_static(prob: Problem, f, g, iters: int, tol: float = 0.0, check_every: int = 1,
+                    init_given: bool = False, want_info: bool = True, schedule: str = "alternating",
+                    eps_start: float = 0.0, eps_decay: float = 0.5):
+    """ot_solve on the library's static device scratch (no workspace, no allocation,
+    plain launches). Returns the info dict (None if want_info is False)."""
+    L = lib()
+    opts = _solve_opts(iters, tol, check_every, init_given, False, 0, 0, False, schedule,
+                       eps_start, eps_decay)
+    info = OtSolveInfo()
+    pinfo = ctypes.byref(info) if want_info else None
+    _check(L.ot_solve_static(ctypes.byref(prob.c), _ptr(f), _ptr(g), ctypes.byref(opts), pinfo,
+                             _stream(prob.device)), "ot_solve_static")
+    return info.as_dict() if want_info else None
+
+
+def static_scratch_bytes() -> int:
+    return int(lib().ot_static_scratch_bytes())
 
 
 def ot_sinkhorn_divergence(prob: Problem, iters: int, f=None, g=None, schedule: str = "alternating",

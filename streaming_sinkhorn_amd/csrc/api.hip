@@ -658,9 +658,67 @@ ApplyWs apply_layout(const ot_problem* p, int64_t cols, bool transpose) {
   return w;
 }
 
+// ---- static scratch of ot_solve_static ---------------------------------------
+// For callers that cannot allocate device memory: ot_solve_static runs
+// ot_solve with this array as its workspace. Each device the library runs on
+// holds one copy from module load until the process ends. In host code the
+// array's name is only a stand-in: its device address on the current device
+// comes from hipGetSymbolAddress, taken once per device and kept.
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch (looked up on first use).
+int static_scratch(void** out) {
+  int dev = 0;
+  OT_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(OT_ERR_UNSUPPORTED, "device index >= 64");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(OT_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return OT_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t ot_static_scratch_bytes(void) { return kStaticScratchBytes; }
+
+int ot_solve_static(const ot_problem* p, float* f, float* g, const ot_solve_opts* opts,
+                    ot_solve_info* info, void* stream) {
+  try {
+    if (!opts) return fail(OT_ERR_INVALID_ARG, "opts is NULL");
+    // Plain launches only: capturing and instantiating a HIP graph, and the
+    // per-launch timing events, would allocate.
+    ot_solve_opts o = *opts;
+    o.use_graph = 0;
+    o.timing = 0;
+    size_t need = 0;
+    int rc = ot_solve(p, nullptr, nullptr, &o, nullptr, nullptr, &need, nullptr);
+    if (rc) return rc;
+    if (need > kStaticScratchBytes)
+      return fail(OT_ERR_WORKSPACE, "problem needs " + std::to_string(need) +
+                                        " bytes of scratch; ot_solve_static holds " +
+                                        std::to_string(kStaticScratchBytes) +
+                                        " (use ot_solve with a workspace)");
+    void* ws = nullptr;
+    rc = static_scratch(&ws);
+    if (rc) return rc;
+    size_t sz = kStaticScratchBytes;
+    return ot_solve(p, f, g, &o, info, ws, &sz, stream);
+  } catch (...) {
+    return fail(OT_ERR_HIP, "unexpected host exception");
+  }
+}
 
 const char* ot_last_error(void) { return flashot::host::last_error(); }
 

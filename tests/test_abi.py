@@ -318,3 +318,16 @@ def test_divergence_workspace_and_validation():
     p.x_sqn, p.y_sqn = 3 << 20, 4 << 20
     assert L.ot_sinkhorn_divergence(ctypes.byref(p), ctypes.byref(opts), None, None, None, None, None,
                                     None, ctypes.byref(sz), None) == ssa.OT_ERR_UNSUPPORTED
+
+
+def test_solve_static_validates_on_the_host():
+    """ot_solve_static (no workspace, no allocation) rejects a missing opts
+    struct and a problem whose workspace exceeds its static scratch before
+    any HIP call (fake device addresses, never dereferenced)."""
+    L = ssa.lib()
+    p = _problem(1000, 1000, 64)
+    assert L.ot_solve_static(ctypes.byref(p), None, None, None, None, None) == ssa.OT_ERR_INVALID_ARG
+    big = _problem(400000, 400000, 512)
+    opts = ssa.OtSolveOpts(10, 0.0, 1, 0, 1, 0, 0, 0)
+    assert L.ot_solve_static(ctypes.byref(big), None, None, ctypes.byref(opts), None, None) == ssa.OT_ERR_WORKSPACE
+    assert ssa.static_scratch_bytes() == 64 << 20
