@@ -633,6 +633,7 @@ ApplyWs apply_layout(const ot_problem* p, int64_t cols, bool transpose) {
   w.pb_per_pass = w.pblocks >= 4 ? 4 : (w.pblocks >= 2 ? 2 : 1);
   w.ppad = w.pblocks * 32;
   w.S = make_pass(w.rtiles, w.ctiles, w.k, 1, 0, 64);
+  if (!w.k.xres) whole_block_splits(w.S);
   const int ntiles = ceil_div(p->n, kTile), mtiles = ceil_div(p->m, kTile);
   size_t o = 0;
   auto take = [&](size_t bytes) {

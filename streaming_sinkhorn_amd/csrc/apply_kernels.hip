@@ -605,15 +605,251 @@ static void apply_h2_go(const PassShape& s, int pblocks, const void* Rp, const v
       s.splits, s.tps, c, pblocks, partMS, partO, s.rtiles * kTile, ppad);
 }
 
+// ---------------------------------------------------------------------------
+// Transport application for wide points (row operand not resident): the
+// k-chunked pass of the log-sum-exp kernel for wide points (kernels_wide.hip)
+// with a value epilogue per column block. A workgroup owns 4 row tiles (one
+// per wave) and walks its split's column blocks of CT tiles; a block's score
+// tiles are accumulated over the whole dimension in stages of BK k-blocks,
+// the column slice staged once in LDS for the four waves (double-buffered)
+// and each wave's row slice loaded straight into registers (two sets). After
+// the block's last stage the bias and the stabiliser are added (fp32
+// instruction), then, tile by tile: the lazy-stabiliser softmax of the
+// resident pass (apply_fast / apply_exact), the fp16 split of p, and the
+// value product against the tile's value parts, staged in a second,
+// double-buffered LDS area while the previous tile is multiplied. The
+// stabiliser a block's tiles are scored against is the one at the block's
+// start, so a raise inside a block sends the block's later tiles down the
+// exact path (FOLD modes). Splits hold whole blocks: the host rounds the
+// tiles per split to a multiple of CT. The fp16-split (FOLD) and bf16
+// scores only: fp32 scores keep the chunked kernel above.
+// ---------------------------------------------------------------------------
+template <int SMODE, int CT, int BK, int PB>
+__global__ __launch_bounds__(256) void apply_wide_kernel(
+    const u32x4* __restrict__ Rp, const u32x4* __restrict__ Cp, const float* __restrict__ cbias,
+    const u32x4* __restrict__ Vh, int rtiles, int ctiles, int kbp, int splits, int tps,
+    int nrowgroups, float c, int pblocks, float2* __restrict__ partMS, float* __restrict__ partO,
+    int rpad, int ppad) {
+  constexpr int KU = units_per_kblock<SMODE>();
+  constexpr int SU = BK * KU;                     // units per tile per stage
+  constexpr int NL = (CT * SU * 64 + 255) / 256;  // column staging loads per thread
+  constexpr int VE = PB * 4 * 64;                 // value entries (16 B) per tile
+  constexpr int NV = (VE + 255) / 256;            // value staging loads per thread
+  constexpr bool FOLD = SMODE == kModeHalf2;
+  __shared__ u32x4 lds[2][NL * 256];
+  __shared__ u32x4 vlds[2][NV * 256];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int h = lane >> 5;
+  // XCD-aware order, as in the wide log-sum-exp pass: workgroup w runs on XCD
+  // w % 8, and an XCD's workgroups take row groups xcd, xcd + 8, ... with the
+  // split index fastest.
+  const int xcd = blockIdx.x & 7;
+  const int li = blockIdx.x >> 3;
+  const int s = li % splits;
+  const int rg = (li / splits) * 8 + xcd;
+  if (rg >= nrowgroups) return;                   // whole workgroup: no barrier is skipped
+  const int rt = rg * kWaves + wave;              // may be past the last row tile
+  const int pb0 = blockIdx.y * PB;
+  const int npb = min(PB, pblocks - pb0);
+  const int jtb = s * tps;                        // first column tile of the split
+  const int nb = (min(jtb + tps, ctiles) - jtb + CT - 1) / CT;  // >= 1
+  const int nstages = kbp / SU;                   // per column block (even)
+  const int total = nb * nstages;
+  const float ks = FOLD ? 1.0f : c;
+
+  int cq[NL], uo[NL];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int e = min(tid + 256 * i, CT * SU * 64 - 1);
+    cq[i] = e / (SU * 64);
+    uo[i] = ((e / 64) % SU) * 64 + (e & 63);
+  }
+  auto gload = [&](int step, u32x4 (&g)[NL]) {
+    step = min(step, total - 1);
+    const int jt = jtb + (step / nstages) * CT;
+    const size_t koff = (size_t)(step % nstages) * SU * 64;
+#pragma unroll
+    for (int i = 0; i < NL; ++i)
+      g[i] = Cp[(size_t)min(jt + cq[i], ctiles - 1) * kbp * 64 + koff + uo[i]];
+  };
+  auto sstore = [&](u32x4* buf, const u32x4 (&g)[NL]) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) buf[tid + 256 * i] = g[i];
+  };
+  const u32x4* xsrc = Rp + (size_t)min(rt, rtiles - 1) * kbp * 64 + lane;
+  auto rload = [&](int step, u32x4 (&x)[1][SU]) {
+    step = min(step, total - 1);
+    const size_t koff = (size_t)(step % nstages) * SU * 64;
+#pragma unroll
+    for (int u = 0; u < SU; ++u) x[0][u] = xsrc[koff + u * 64];
+  };
+  // Value staging: entry e of a tile's PB * 4 units (the pass's blocks; units
+  // past npb repeat the last one and are never written out).
+  int vu[NV], vl[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int e = min(tid + 256 * i, VE - 1);
+    vu[i] = min(e >> 6, 4 * npb - 1);
+    vl[i] = e & 63;
+  }
+  auto vload = [&](int jt, u32x4 (&gv)[NV]) {
+    jt = min(jt, ctiles - 1);
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      gv[i] = Vh[(((size_t)jt * pblocks + pb0) * 4 + vu[i]) * 64 + vl[i]];
+  };
+  auto vstore = [&](int buf, const u32x4 (&gv)[NV]) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) vlds[buf][tid + 256 * i] = gv[i];
+  };
+
+  float M = kUnset, S = 0.f;
+  f32x16 O[PB];
+#pragma unroll
+  for (int pb = 0; pb < PB; ++pb) O[pb] = f32x16{};
+
+  u32x4 gA[NL], gB[NL];
+  u32x4 xA[1][SU], xB[1][SU];
+  gload(0, gA);
+  rload(0, xA);
+  sstore(lds[0], gA);
+  gload(1, gB);
+  rload(1, xB);
+  __syncthreads();
+
+  auto compute = [&](const u32x4* buf, const u32x4 (&x)[1][SU], f32x16 (&acc)[CT]) {
+#pragma unroll
+    for (int kb = 0; kb < BK; ++kb) {
+      u32x4 yf[CT][KU];
+#pragma unroll
+      for (int q = 0; q < CT; ++q)
+#pragma unroll
+        for (int u = 0; u < KU; ++u) yf[q][u] = buf[(q * SU + kb * KU + u) * 64 + lane];
+#pragma unroll
+      for (int q = 0; q < CT; ++q) {
+        if constexpr (SMODE == kModeHalf2)
+          acc[q] = mfma_half2(yf[q], &x[0][kb * KU], acc[q]);
+        else
+          acc[q] = mfma_kblock<SMODE == kModeBF16>(yf[q][0], x[0][kb], acc[q]);
+      }
+    }
+  };
+
+  int step = 0;
+  for (int bi = 0; bi < nb; ++bi) {
+    const int jt0 = jtb + bi * CT;
+    const float Mf = FOLD ? fold_of(M) : 0.f;
+    f32x16 acc[CT];
+#pragma unroll
+    for (int q = 0; q < CT; ++q) acc[q] = f32x16{};
+    for (int st = 0; st < nstages; st += 2, step += 2) {
+      gload(step + 2, gA);
+      compute(lds[0], xA, acc);
+      rload(step + 2, xA);
+      sstore(lds[1], gB);
+      __syncthreads();
+      gload(step + 3, gB);
+      compute(lds[1], xB, acc);
+      rload(step + 3, xB);
+      sstore(lds[0], gA);
+      __syncthreads();
+    }
+    // bias_j - Mf_i after the products, on the fp32 instruction (k-slot 0:
+    // (bias_j, 1), k-slot 1: (1, -Mf_i)): over a whole dimension of products
+    // the partial sums then round at the products' magnitude, not at the
+    // bias's, and the one addition is rounded to nearest.
+#pragma unroll
+    for (int q = 0; q < CT; ++q) {
+      const int jt = jt0 + q;
+      const float bj = jt < ctiles ? cbias[(size_t)min(jt, ctiles - 1) * kTile + (lane & 31)]
+                                   : kSentinel;
+      acc[q] = __builtin_amdgcn_mfma_f32_32x32x2f32(h ? 1.0f : bj, h ? -Mf : 1.0f, acc[q], 0, 0, 0);
+    }
+
+    // Value epilogue of the block, tile by tile.
+    u32x4 gv[NV];
+    vload(jt0, gv);
+    vstore(0, gv);
+#pragma unroll
+    for (int q = 0; q < CT; ++q) {
+      __syncthreads();  // tile q's values are in vlds[q & 1]; the other slot is free
+      if (q + 1 < CT) vload(jt0 + q + 1, gv);
+      f32x16 p;
+      float ts;
+      const bool slow = apply_fast<FOLD>(acc[q], Mf, M, ks, p, ts);
+      if (__builtin_amdgcn_ballot_w64(slow) != 0) {
+        apply_exact<FOLD, PB>(acc[q], Mf, M, S, O, ks, p);
+      } else {
+        S += ts;
+      }
+      u32x4 ph[2], pl[2];
+      split_p(p, ph, pl);
+#pragma unroll
+      for (int pb = 0; pb < PB; ++pb)
+        O[pb] = value_block(&vlds[q & 1][pb * 4 * 64], lane, ph, pl, O[pb]);
+      if (q + 1 < CT) vstore((q + 1) & 1, gv);
+    }
+  }
+
+  S += __shfl_xor(S, 32);
+  if (rt >= rtiles) return;
+  const size_t row = (size_t)rt * kTile + (lane & 31);
+  if (blockIdx.y == 0 && h == 0) partMS[(size_t)s * rpad + row] = make_float2(ks * M, S);
+#pragma unroll
+  for (int pb = 0; pb < PB; ++pb) {
+    if (pb < npb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int pcol = 32 * (pb0 + pb) + 8 * (r >> 2) + 4 * h + (r & 3);
+        partO[((size_t)s * ppad + pcol) * rpad + row] = O[pb][r];
+      }
+    }
+  }
+}
+
+template <int SMODE, int PB>
+static hipError_t apply_wide_go(const PassShape& s, int pblocks, const void* Rp, const void* Cp,
+                                const float* cbias, const void* Vh, float c, float2* partMS,
+                                float* partO, int ppad, hipStream_t st) {
+  constexpr int CT = kApplyWideCT;
+  constexpr int BK = SMODE == kModeHalf2 ? 1 : 2;
+  constexpr int SU = BK * units_per_kblock<SMODE>();
+  if (s.tps % CT || s.kbp % (2 * SU)) return hipErrorInvalidValue;
+  dim3 grid((s.nrowgroups + 7) / 8 * 8 * s.splits, (pblocks + PB - 1) / PB);
+  apply_wide_kernel<SMODE, CT, BK, PB><<<grid, 256, 0, st>>>(
+      (const u32x4*)Rp, (const u32x4*)Cp, cbias, (const u32x4*)Vh, s.rtiles, s.ctiles, s.kbp,
+      s.splits, s.tps, s.nrowgroups, c, pblocks, partMS, partO, s.rtiles * kTile, ppad);
+  return hipGetLastError();
+}
+
 // Pass with the value product on fp16 parts: the pipelined resident kernel,
-// or the chunked kernel when the row operand is not resident.
+// or the block-tiled kernel when the row operand is not resident.
 template <int SMODE, int PB>
 static hipError_t apply_stream_pb(const PassShape& s, int pblocks, const void* Rp, const void* Cp,
                                   const float* cbias, const void* Vh, float c, float2* partMS,
                                   float* partO, int ppad, hipStream_t st) {
-  if (s.xres) return apply_res_kb<SMODE, PB>(s, pblocks, Rp, Cp, cbias, Vh, c, partMS, partO, ppad, st);
-  apply_h2_go<SMODE, 8, false, PB>(s, pblocks, Rp, Cp, cbias, Vh, c, partMS, partO, ppad, st);
-  return hipGetLastError();
+  if constexpr (SMODE == kModeF32) {
+    // fp32 scores (the Hessian-vector product's transport-matrix passes, whose
+    // damped Schur solve is sensitive to how their arithmetic differs from the
+    // vector passes'): the plain per-tile kernel, eager running maximum.
+    switch (s.xres ? s.kb : 8) {
+      case 1: apply_h2_go<SMODE, 1, true, PB>(s, pblocks, Rp, Cp, cbias, Vh, c, partMS, partO, ppad, st); break;
+      case 2: apply_h2_go<SMODE, 2, true, PB>(s, pblocks, Rp, Cp, cbias, Vh, c, partMS, partO, ppad, st); break;
+      case 4: apply_h2_go<SMODE, 4, true, PB>(s, pblocks, Rp, Cp, cbias, Vh, c, partMS, partO, ppad, st); break;
+      case 8:
+        if (s.xres) apply_h2_go<SMODE, 8, true, PB>(s, pblocks, Rp, Cp, cbias, Vh, c, partMS, partO, ppad, st);
+        else apply_h2_go<SMODE, 8, false, PB>(s, pblocks, Rp, Cp, cbias, Vh, c, partMS, partO, ppad, st);
+        break;
+      case 16: apply_h2_go<SMODE, 16, true, PB>(s, pblocks, Rp, Cp, cbias, Vh, c, partMS, partO, ppad, st); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  } else {
+    if (s.xres) return apply_res_kb<SMODE, PB>(s, pblocks, Rp, Cp, cbias, Vh, c, partMS, partO, ppad, st);
+    return apply_wide_go<SMODE, PB>(s, pblocks, Rp, Cp, cbias, Vh, c, partMS, partO, ppad, st);
+  }
 }
 
 template <int SMODE>

@@ -55,6 +55,13 @@ constexpr int kTargetWorkgroups = 2048;
 constexpr int kTargetWorkgroupsResident = 1024;
 PassShape make_pass(int rtiles, int ctiles, const KConf& k, int ri, int forced, int max_splits,
                     int target = kTargetWorkgroups);
+// Non-resident transport passes stream whole blocks of kApplyWideCT column
+// tiles: the tiles per split are rounded up to a multiple of it (the split
+// count shrinks accordingly).
+inline void whole_block_splits(PassShape& s) {
+  s.tps = ceil_div(s.tps, kApplyWideCT) * kApplyWideCT;
+  s.splits = ceil_div(s.ctiles, s.tps);
+}
 int check_problem(const ot_problem* p);
 // ws == NULL: writes need to *ws_bytes and sets *query; otherwise checks size
 // and alignment.

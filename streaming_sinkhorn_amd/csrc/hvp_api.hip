@@ -56,6 +56,10 @@ TransportWs transport_layout(const ot_problem* p, int64_t cols_f, int64_t cols_t
   w.mpad = w.mtiles * kTile;
   w.F = make_pass(w.ntiles, w.mtiles, w.k, 1, 0, 64);
   w.T = make_pass(w.mtiles, w.ntiles, w.k, 1, 0, 64);
+  if (!w.k.xres) {
+    whole_block_splits(w.F);
+    whole_block_splits(w.T);
+  }
   const Cols cf = cols_of(cols_f), ct = cols_of(cols_t > 0 ? cols_t : 1);
   w.o_xp = take((size_t)w.ntiles * w.k.kbp * 1024);
   w.o_yp = take((size_t)w.mtiles * w.k.kbp * 1024);

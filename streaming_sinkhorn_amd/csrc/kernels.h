@@ -95,6 +95,9 @@ hipError_t launch_pack_values_h2(const void* V, int bf16, int64_t rows, int64_t 
 // buffer with the bias-MFMA parts (bias_buffer_bytes) for kModeHalf2 and
 // kModeBF16, fp32 biases alone for kModeF32. Partial stabilisers are written
 // in log2 units (merge with c = 1).
+// Column tiles per block of the wide transport application; its passes need
+// the column tiles per split (PassShape::tps) to be a multiple of it.
+constexpr int kApplyWideCT = 4;
 hipError_t launch_apply_stream(const PassShape& s, int smode, int pblocks, int pb_per_pass,
                                const void* Rp, const void* Cp, const float* cbias, const void* Vh,
                                float c, float2* partMS, float* partO, int ppad, hipStream_t st);
