@@ -13,6 +13,8 @@
 
 namespace flashot {
 
+static inline int ceil_div_dev(int a, int b) { return (a + b - 1) / b; }
+
 // ---------------------------------------------------------------------------
 // Streamed transport application partials (Algorithm 2 / 4 of the page).
 // Per split s and row i: (M, S) as in the LSE pass, and
@@ -608,7 +610,7 @@ static void apply_h2_go(const PassShape& s, int pblocks, const void* Rp, const v
 // ---------------------------------------------------------------------------
 // Transport application for wide points (row operand not resident): the
 // k-chunked pass of the log-sum-exp kernel for wide points (kernels_wide.hip)
-// with a value epilogue per column block. A workgroup owns 4 row tiles (one
+// with a value epilogue per column block. A workgroup owns 4 RT row tiles (RT
 // per wave) and walks its split's column blocks of CT tiles; a block's score
 // tiles are accumulated over the whole dimension in stages of BK k-blocks,
 // the column slice staged once in LDS for the four waves (double-buffered)
@@ -624,7 +626,7 @@ static void apply_h2_go(const PassShape& s, int pblocks, const void* Rp, const v
 // tiles per split to a multiple of CT. The fp16-split (FOLD) and bf16
 // scores only: fp32 scores keep the chunked kernel above.
 // ---------------------------------------------------------------------------
-template <int SMODE, int CT, int BK, int PB>
+template <int SMODE, int RT, int CT, int BK, int PB>
 __global__ __launch_bounds__(256) void apply_wide_kernel(
     const u32x4* __restrict__ Rp, const u32x4* __restrict__ Cp, const float* __restrict__ cbias,
     const u32x4* __restrict__ Vh, int rtiles, int ctiles, int kbp, int splits, int tps,
@@ -650,7 +652,7 @@ __global__ __launch_bounds__(256) void apply_wide_kernel(
   const int s = li % splits;
   const int rg = (li / splits) * 8 + xcd;
   if (rg >= nrowgroups) return;                   // whole workgroup: no barrier is skipped
-  const int rt = rg * kWaves + wave;              // may be past the last row tile
+  const int rt0 = (rg * kWaves + wave) * RT;      // this wave's row tiles (may be past the last)
   const int pb0 = blockIdx.y * PB;
   const int npb = min(PB, pblocks - pb0);
   const int jtb = s * tps;                        // first column tile of the split
@@ -678,12 +680,17 @@ __global__ __launch_bounds__(256) void apply_wide_kernel(
 #pragma unroll
     for (int i = 0; i < NL; ++i) buf[tid + 256 * i] = g[i];
   };
-  const u32x4* xsrc = Rp + (size_t)min(rt, rtiles - 1) * kbp * 64 + lane;
-  auto rload = [&](int step, u32x4 (&x)[1][SU]) {
+  const u32x4* xsrc[RT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r)
+    xsrc[r] = Rp + (size_t)min(rt0 + r, rtiles - 1) * kbp * 64 + lane;
+  auto rload = [&](int step, u32x4 (&x)[RT][SU]) {
     step = min(step, total - 1);
     const size_t koff = (size_t)(step % nstages) * SU * 64;
 #pragma unroll
-    for (int u = 0; u < SU; ++u) x[0][u] = xsrc[koff + u * 64];
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int u = 0; u < SU; ++u) x[r][u] = xsrc[r][koff + u * 64];
   };
   // Value staging: entry e of a tile's PB * 4 units (the pass's blocks; units
   // past npb repeat the last one and are never written out).
@@ -705,13 +712,18 @@ __global__ __launch_bounds__(256) void apply_wide_kernel(
     for (int i = 0; i < NV; ++i) vlds[buf][tid + 256 * i] = gv[i];
   };
 
-  float M = kUnset, S = 0.f;
-  f32x16 O[PB];
+  float M[RT], S[RT];
+  f32x16 O[RT][PB];
 #pragma unroll
-  for (int pb = 0; pb < PB; ++pb) O[pb] = f32x16{};
+  for (int r = 0; r < RT; ++r) {
+    M[r] = kUnset;
+    S[r] = 0.f;
+#pragma unroll
+    for (int pb = 0; pb < PB; ++pb) O[r][pb] = f32x16{};
+  }
 
   u32x4 gA[NL], gB[NL];
-  u32x4 xA[1][SU], xB[1][SU];
+  u32x4 xA[RT][SU], xB[RT][SU];
   gload(0, gA);
   rload(0, xA);
   sstore(lds[0], gA);
@@ -719,7 +731,7 @@ __global__ __launch_bounds__(256) void apply_wide_kernel(
   rload(1, xB);
   __syncthreads();
 
-  auto compute = [&](const u32x4* buf, const u32x4 (&x)[1][SU], f32x16 (&acc)[CT]) {
+  auto compute = [&](const u32x4* buf, const u32x4 (&x)[RT][SU], f32x16 (&acc)[RT][CT]) {
 #pragma unroll
     for (int kb = 0; kb < BK; ++kb) {
       u32x4 yf[CT][KU];
@@ -728,22 +740,28 @@ __global__ __launch_bounds__(256) void apply_wide_kernel(
 #pragma unroll
         for (int u = 0; u < KU; ++u) yf[q][u] = buf[(q * SU + kb * KU + u) * 64 + lane];
 #pragma unroll
-      for (int q = 0; q < CT; ++q) {
-        if constexpr (SMODE == kModeHalf2)
-          acc[q] = mfma_half2(yf[q], &x[0][kb * KU], acc[q]);
-        else
-          acc[q] = mfma_kblock<SMODE == kModeBF16>(yf[q][0], x[0][kb], acc[q]);
-      }
+      for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int q = 0; q < CT; ++q) {
+          if constexpr (SMODE == kModeHalf2)
+            acc[r][q] = mfma_half2(yf[q], &x[r][kb * KU], acc[r][q]);
+          else
+            acc[r][q] = mfma_kblock<SMODE == kModeBF16>(yf[q][0], x[r][kb], acc[r][q]);
+        }
     }
   };
 
   int step = 0;
   for (int bi = 0; bi < nb; ++bi) {
     const int jt0 = jtb + bi * CT;
-    const float Mf = FOLD ? fold_of(M) : 0.f;
-    f32x16 acc[CT];
+    float Mf[RT];
+    f32x16 acc[RT][CT];
 #pragma unroll
-    for (int q = 0; q < CT; ++q) acc[q] = f32x16{};
+    for (int r = 0; r < RT; ++r) {
+      Mf[r] = FOLD ? fold_of(M[r]) : 0.f;
+#pragma unroll
+      for (int q = 0; q < CT; ++q) acc[r][q] = f32x16{};
+    }
     for (int st = 0; st < nstages; st += 2, step += 2) {
       gload(step + 2, gA);
       compute(lds[0], xA, acc);
@@ -765,7 +783,10 @@ __global__ __launch_bounds__(256) void apply_wide_kernel(
       const int jt = jt0 + q;
       const float bj = jt < ctiles ? cbias[(size_t)min(jt, ctiles - 1) * kTile + (lane & 31)]
                                    : kSentinel;
-      acc[q] = __builtin_amdgcn_mfma_f32_32x32x2f32(h ? 1.0f : bj, h ? -Mf : 1.0f, acc[q], 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < RT; ++r)
+        acc[r][q] = __builtin_amdgcn_mfma_f32_32x32x2f32(h ? 1.0f : bj, h ? -Mf[r] : 1.0f,
+                                                         acc[r][q], 0, 0, 0);
     }
 
     // Value epilogue of the block, tile by tile.
@@ -776,34 +797,41 @@ __global__ __launch_bounds__(256) void apply_wide_kernel(
     for (int q = 0; q < CT; ++q) {
       __syncthreads();  // tile q's values are in vlds[q & 1]; the other slot is free
       if (q + 1 < CT) vload(jt0 + q + 1, gv);
-      f32x16 p;
-      float ts;
-      const bool slow = apply_fast<FOLD>(acc[q], Mf, M, ks, p, ts);
-      if (__builtin_amdgcn_ballot_w64(slow) != 0) {
-        apply_exact<FOLD, PB>(acc[q], Mf, M, S, O, ks, p);
-      } else {
-        S += ts;
-      }
-      u32x4 ph[2], pl[2];
-      split_p(p, ph, pl);
 #pragma unroll
-      for (int pb = 0; pb < PB; ++pb)
-        O[pb] = value_block(&vlds[q & 1][pb * 4 * 64], lane, ph, pl, O[pb]);
+      for (int r = 0; r < RT; ++r) {
+        f32x16 p;
+        float ts;
+        const bool slow = apply_fast<FOLD>(acc[r][q], Mf[r], M[r], ks, p, ts);
+        if (__builtin_amdgcn_ballot_w64(slow) != 0) {
+          apply_exact<FOLD, PB>(acc[r][q], Mf[r], M[r], S[r], O[r], ks, p);
+        } else {
+          S[r] += ts;
+        }
+        u32x4 ph[2], pl[2];
+        split_p(p, ph, pl);
+#pragma unroll
+        for (int pb = 0; pb < PB; ++pb)
+          O[r][pb] = value_block(&vlds[q & 1][pb * 4 * 64], lane, ph, pl, O[r][pb]);
+      }
       if (q + 1 < CT) vstore((q + 1) & 1, gv);
     }
   }
 
-  S += __shfl_xor(S, 32);
-  if (rt >= rtiles) return;
-  const size_t row = (size_t)rt * kTile + (lane & 31);
-  if (blockIdx.y == 0 && h == 0) partMS[(size_t)s * rpad + row] = make_float2(ks * M, S);
 #pragma unroll
-  for (int pb = 0; pb < PB; ++pb) {
-    if (pb < npb) {
+  for (int r = 0; r < RT; ++r) {
+    const float St = S[r] + __shfl_xor(S[r], 32);
+    const int rt = rt0 + r;
+    if (rt >= rtiles) continue;
+    const size_t row = (size_t)rt * kTile + (lane & 31);
+    if (blockIdx.y == 0 && h == 0) partMS[(size_t)s * rpad + row] = make_float2(ks * M[r], St);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int pcol = 32 * (pb0 + pb) + 8 * (r >> 2) + 4 * h + (r & 3);
-        partO[((size_t)s * ppad + pcol) * rpad + row] = O[pb][r];
+    for (int pb = 0; pb < PB; ++pb) {
+      if (pb < npb) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int pcol = 32 * (pb0 + pb) + 8 * (e >> 2) + 4 * h + (e & 3);
+          partO[((size_t)s * ppad + pcol) * rpad + row] = O[r][pb][e];
+        }
       }
     }
   }
@@ -813,14 +841,22 @@ template <int SMODE, int PB>
 static hipError_t apply_wide_go(const PassShape& s, int pblocks, const void* Rp, const void* Cp,
                                 const float* cbias, const void* Vh, float c, float2* partMS,
                                 float* partO, int ppad, hipStream_t st) {
-  constexpr int CT = kApplyWideCT;
+  // One row tile per wave: its O accumulators next to the block's score tiles
+  // fit two waves per SIMD with four column tiles per block for up to two
+  // value blocks, two column tiles for four (two row tiles per wave, which
+  // would halve the LDS reads per matrix instruction, need more registers
+  // than two waves per SIMD allow).
+  constexpr int RT = 1;
+  constexpr int CT = PB >= 4 ? 2 : 4;
   constexpr int BK = SMODE == kModeHalf2 ? 1 : 2;
   constexpr int SU = BK * units_per_kblock<SMODE>();
+  static_assert(kApplyWideCT % CT == 0, "splits hold whole blocks");
   if (s.tps % CT || s.kbp % (2 * SU)) return hipErrorInvalidValue;
-  dim3 grid((s.nrowgroups + 7) / 8 * 8 * s.splits, (pblocks + PB - 1) / PB);
-  apply_wide_kernel<SMODE, CT, BK, PB><<<grid, 256, 0, st>>>(
+  const int nrg = ceil_div_dev(s.rtiles, kWaves * RT);
+  dim3 grid((nrg + 7) / 8 * 8 * s.splits, (pblocks + PB - 1) / PB);
+  apply_wide_kernel<SMODE, RT, CT, BK, PB><<<grid, 256, 0, st>>>(
       (const u32x4*)Rp, (const u32x4*)Cp, cbias, (const u32x4*)Vh, s.rtiles, s.ctiles, s.kbp,
-      s.splits, s.tps, s.nrowgroups, c, pblocks, partMS, partO, s.rtiles * kTile, ppad);
+      s.splits, s.tps, nrg, c, pblocks, partMS, partO, s.rtiles * kTile, ppad);
   return hipGetLastError();
 }
 

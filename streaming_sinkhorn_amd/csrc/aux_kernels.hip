@@ -185,17 +185,20 @@ __global__ __launch_bounds__(256) void err_reduce_kernel(const float* __restrict
   if (threadIdx.x == 0) out[0] = tot;
 }
 
+// Sets *out to 1.0f when f or g holds a NaN or an infinity (*out is zeroed
+// first by the launcher). Grid-stride over both vectors; one flag per
+// workgroup, set by an atomic OR of the bits of 1.0f (same result in any order).
 __global__ __launch_bounds__(256) void nonfinite_kernel(const float* __restrict__ f, int n,
                                                          const float* __restrict__ g, int m,
                                                          float* __restrict__ out) {
-  __shared__ float sh[256];
   // Exponent-bit test: independent of the no-NaN compile flags of this file.
-  auto bad = [](float x) { return ((__float_as_uint(x) >> 23) & 0xffu) == 0xffu ? 1.f : 0.f; };
-  float v = 0.f;
-  for (int k = threadIdx.x; k < n; k += 256) v += bad(f[k]);
-  for (int k = threadIdx.x; k < m; k += 256) v += bad(g[k]);
-  const float tot = block_sum_256(v, sh);
-  if (threadIdx.x == 0) out[0] = tot;
+  auto bad = [](float x) { return ((__float_as_uint(x) >> 23) & 0xffu) == 0xffu; };
+  int any = 0;
+  const int64_t total = (int64_t)n + m;
+  for (int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x; k < total; k += (int64_t)gridDim.x * 256)
+    any |= bad(k < n ? f[k] : g[k - n]) ? 1 : 0;
+  if (__syncthreads_or(any) && threadIdx.x == 0)
+    atomicOr(reinterpret_cast<unsigned int*>(out), 0x3f800000u);
 }
 
 // Merge of P V partials and epilogue. For row i of the coupling induced by
@@ -628,9 +631,10 @@ hipError_t launch_pack_split(const float* src, int64_t rows, int64_t d, int64_t 
 
 hipError_t launch_half2_plan(const float* X, int64_t n, int64_t ldx, const float* Y, int64_t m,
                              int64_t ldy, int64_t d, float cx, Half2Plan* plan, hipStream_t st) {
-  // about 16 K elements per block, at most kHalf2Parts blocks per cloud
-  const int nx = grid_for(n * d, 16384, kHalf2Parts);
-  const int ny = grid_for(m * d, 16384, kHalf2Parts);
+  // about 4 K elements per block (enough workgroups to stream at full
+  // bandwidth), at most kHalf2Parts blocks per cloud
+  const int nx = grid_for(n * d, 4096, kHalf2Parts);
+  const int ny = grid_for(m * d, 4096, kHalf2Parts);
   absmax_kernel<<<nx, 256, 0, st>>>(X, n, d, ldx, plan->part);
   absmax_kernel<<<ny, 256, 0, st>>>(Y, m, d, ldy, plan->part + kHalf2Parts);
   half2_plan_kernel<<<1, 256, 0, st>>>(plan, nx, ny, cx);
@@ -719,7 +723,8 @@ hipError_t launch_err_reduce(const float* part, int count, float* out, hipStream
 
 hipError_t launch_nonfinite(const float* f, int n, const float* g, int m, float* out,
                             hipStream_t st) {
-  nonfinite_kernel<<<1, 256, 0, st>>>(f, n, g, m, out);
+  fill_kernel<<<1, 256, 0, st>>>(out, 0.f, 1);
+  nonfinite_kernel<<<grid_for((int64_t)n + m, 256, 512), 256, 0, st>>>(f, n, g, m, out);
   return hipGetLastError();
 }
 
