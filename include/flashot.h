@@ -163,7 +163,9 @@ typedef struct ot_solve_opts {
   int32_t check_every;  /* iterations between tolerance checks (>= 1 when tol > 0) */
   int32_t init;         /* OT_INIT_ZERO or OT_INIT_GIVEN */
   int32_t use_graph;    /* 1: replay a captured HIP graph per block of iterations; 0: plain launches */
-  int32_t splits_f;     /* column splits of the f half-step (0 = automatic) */
+  int32_t splits_f;     /* column splits of the f half-step (0 = automatic; automatic runs
+                           the half-steps of small problems, at most 3072 points a side,
+                           as one launch each in the alternating schedule) */
   int32_t splits_g;     /* column splits of the g half-step (0 = automatic) */
   int32_t timing;       /* 1: time every log-sum-exp kernel with HIP events (needs info) */
   int32_t schedule;     /* OT_SCHED_ALTERNATING (0) or OT_SCHED_SYMMETRIC */
@@ -184,7 +186,8 @@ typedef struct ot_solve_info {
                             every iteration annealed: from one extra column pass. */
   float lse_ms;          /* with opts.timing: summed duration of the log-sum-exp kernels (ms) */
   int32_t lse_launches;  /* with opts.timing: number of log-sum-exp kernel launches timed */
-  int32_t splits_f;      /* column splits used by the f half-step */
+  int32_t splits_f;      /* column splits used by the f half-step (single-launch half-step:
+                            the waves of a workgroup that hold column tiles) */
   int32_t splits_g;      /* column splits used by the g half-step */
   int32_t operand_mode;  /* scores formed from: 0 fp32 MFMA, 1 bf16 MFMA, 2 fp32 split into
                             three bf16 parts on the bf16 MFMA (six products per pair),

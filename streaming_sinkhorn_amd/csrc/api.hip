@@ -222,6 +222,27 @@ struct SolveWs {
   size_t total;
 };
 
+// The single-launch half-step serves problems whose passes are too small to
+// fill the chip: at most kSoloMaxTiles 32-row tiles on either side and at
+// most kSoloMaxWork tile pairs x operand units. Measured on MI355X against
+// the best split count, per iteration: it wins up to 2048 x 2048 at d = 64
+// fp32 and bf16 d = 128, and at 3000 x 3000 bf16 d = 16; it ties at
+// 4096 x 4096 d = 16 fp32 and loses at 4096 x 4096 d = 64.
+constexpr int kSoloMaxTiles = 96;
+constexpr int64_t kSoloMaxWork = 64 * 64 * 8;
+bool solo_fits(const PassShape& s, int mode) {
+  return lse_solo_supported(s, mode) && s.rtiles <= kSoloMaxTiles && s.ctiles <= kSoloMaxTiles &&
+         (int64_t)s.rtiles * s.ctiles * s.kb <= kSoloMaxWork;
+}
+
+// Column splits a half-step runs with: the split count, or, for the
+// single-launch pass, the waves that hold column tiles.
+int used_splits(const PassShape& s, bool sym) {
+  if (!s.solo || sym) return s.splits;
+  const int tpw = ceil_div(s.ctiles, kSoloWaves);
+  return ceil_div(s.ctiles, tpw);
+}
+
 SolveWs solve_layout(const ot_problem* p, int splits_f, int splits_g) {
   SolveWs w{};
   w.k = kernel_conf(p->d, p->dtype == OT_BF16, f32_operand_mode(p->flags));
@@ -232,6 +253,10 @@ SolveWs solve_layout(const ot_problem* p, int splits_f, int splits_g) {
   const int target = w.k.xres ? kTargetWorkgroupsResident : kTargetWorkgroups;
   w.F = make_pass(w.ntiles, w.mtiles, w.k, w.k.ri, splits_f, 4096, target);
   w.G = make_pass(w.mtiles, w.ntiles, w.k, w.k.ri, splits_g, 4096, target);
+  // Small problems run each half-step as one launch (unless a split count is
+  // forced); the split shapes stay valid for the symmetric schedule.
+  w.F.solo = splits_f == 0 && solo_fits(w.F, w.k.mode);
+  w.G.solo = splits_g == 0 && solo_fits(w.G, w.k.mode);
   w.errblocks_f = lse_merge_blocks(w.npad);
   w.errblocks_g = lse_merge_blocks(w.mpad);
   size_t o = 0;
@@ -398,42 +423,73 @@ int run_eps_scaling(Ctx& x, hipStream_t st, int max_iters, float eps_start, floa
   return rebuild_biases(x, st);
 }
 
-// f half-step: LSE over columns y with bias by, merge into f (bias bx for the g side).
-int half_f(const Ctx& x, hipStream_t st, int with_err, int write) {
+RowFinish finish_f(const Ctx& x, int with_err, int write, int avg) {
+  return RowFinish{x.bscale, x.eps, x.nx, x.hx, x.wx, x.f, x.bx, (int)x.p->n, x.L.npad,
+                   with_err, write, avg};
+}
+
+RowFinish finish_g(const Ctx& x, int with_err, int write, int avg) {
+  return RowFinish{x.bscale, x.eps, x.ny, x.hy, x.wy, x.g, x.by, (int)x.p->m, x.L.mpad,
+                   with_err, write, avg};
+}
+
+// f half-step: LSE over columns y with bias by, ending in f (and, when
+// written, the g side's bias bx); as one launch for small problems, else the
+// split pass and the merge of its partials. ev, if given, receives two
+// events around the log-sum-exp launch.
+int half_f(const Ctx& x, hipStream_t st, int with_err, int write, hipEvent_t* ev = nullptr) {
+  const RowFinish fin = finish_f(x, with_err, write, 0);
+  if (ev) OT_HIP(hipEventRecord(ev[0], st));
+  if (x.L.F.solo) {
+    OT_HIP(launch_lse_solo(x.L.F, x.L.k.mode, x.xp, x.yp, x.by, x.kc, fin, x.errp, st));
+    if (ev) OT_HIP(hipEventRecord(ev[1], st));
+    return OT_OK;
+  }
   OT_HIP(launch_lse_partial(x.L.F, x.L.k.mode, x.xp, x.yp, x.by, x.kc, x.part, st));
+  if (ev) OT_HIP(hipEventRecord(ev[1], st));
   OT_HIP(launch_lse_merge(x.part, x.L.F.splits, x.L.npad, (int)x.p->n, x.bscale, x.eps, x.nx, x.hx, x.wx,
                           x.f, x.bx, x.errp, with_err, write, 0, st));
   return OT_OK;
 }
 
-int half_g(const Ctx& x, hipStream_t st, int with_err, int write) {
+int half_g(const Ctx& x, hipStream_t st, int with_err, int write, hipEvent_t* ev = nullptr) {
+  const RowFinish fin = finish_g(x, with_err, write, 0);
+  float* errp = x.errp + x.L.errblocks_f;
+  if (ev) OT_HIP(hipEventRecord(ev[0], st));
+  if (x.L.G.solo) {
+    OT_HIP(launch_lse_solo(x.L.G, x.L.k.mode, x.yp, x.xp, x.bx, x.kc, fin, errp, st));
+    if (ev) OT_HIP(hipEventRecord(ev[1], st));
+    return OT_OK;
+  }
   OT_HIP(launch_lse_partial(x.L.G, x.L.k.mode, x.yp, x.xp, x.bx, x.kc, x.part, st));
+  if (ev) OT_HIP(hipEventRecord(ev[1], st));
   OT_HIP(launch_lse_merge(x.part, x.L.G.splits, x.L.mpad, (int)x.p->m, x.bscale, x.eps, x.ny, x.hy, x.wy,
-                          x.g, x.by, x.errp + x.L.errblocks_f, with_err, write, 0, st));
+                          x.g, x.by, errp, with_err, write, 0, st));
   return OT_OK;
 }
 
 // One iteration on the stream. Alternating schedule (§3.1 eq. 2-3): the f
-// pass, its merge (new f and its bias), then the g pass from the new f.
+// half-step (new f and its bias), then the g half-step from the new f.
 // Symmetric schedule (§3.1 eq. 4-5): both passes read the previous biases,
-// so both run before either merge; the merges average old and new values.
-// ev, if given, receives four events around the two log-sum-exp launches.
+// so both split passes run before either merge; the merges average old and
+// new values. ev, if given, receives four events around the two log-sum-exp
+// launches.
 int enqueue_iteration(const Ctx& x, hipStream_t st, int with_err, hipEvent_t* ev) {
+  if (!x.sym) {
+    const int rc = half_f(x, st, with_err, 1, ev);
+    if (rc) return rc;
+    return half_g(x, st, 0, 1, ev ? ev + 2 : nullptr);
+  }
   if (ev) OT_HIP(hipEventRecord(ev[0], st));
   OT_HIP(launch_lse_partial(x.L.F, x.L.k.mode, x.xp, x.yp, x.by, x.kc, x.part, st));
   if (ev) OT_HIP(hipEventRecord(ev[1], st));
-  if (!x.sym)
-    OT_HIP(launch_lse_merge(x.part, x.L.F.splits, x.L.npad, (int)x.p->n, x.bscale, x.eps, x.nx, x.hx,
-                            x.wx, x.f, x.bx, x.errp, with_err, 1, 0, st));
-  float2* pg = x.sym ? x.part2 : x.part;
   if (ev) OT_HIP(hipEventRecord(ev[2], st));
-  OT_HIP(launch_lse_partial(x.L.G, x.L.k.mode, x.yp, x.xp, x.bx, x.kc, pg, st));
+  OT_HIP(launch_lse_partial(x.L.G, x.L.k.mode, x.yp, x.xp, x.bx, x.kc, x.part2, st));
   if (ev) OT_HIP(hipEventRecord(ev[3], st));
-  if (x.sym)
-    OT_HIP(launch_lse_merge(x.part, x.L.F.splits, x.L.npad, (int)x.p->n, x.bscale, x.eps, x.nx, x.hx,
-                            x.wx, x.f, x.bx, x.errp, with_err, 1, 1, st));
-  OT_HIP(launch_lse_merge(pg, x.L.G.splits, x.L.mpad, (int)x.p->m, x.bscale, x.eps, x.ny, x.hy, x.wy,
-                          x.g, x.by, x.errp + x.L.errblocks_f, 0, 1, x.sym ? 1 : 0, st));
+  OT_HIP(launch_lse_merge(x.part, x.L.F.splits, x.L.npad, (int)x.p->n, x.bscale, x.eps, x.nx, x.hx,
+                          x.wx, x.f, x.bx, x.errp, with_err, 1, 1, st));
+  OT_HIP(launch_lse_merge(x.part2, x.L.G.splits, x.L.mpad, (int)x.p->m, x.bscale, x.eps, x.ny, x.hy, x.wy,
+                          x.g, x.by, x.errp + x.L.errblocks_f, 0, 1, 1, st));
   return OT_OK;
 }
 
@@ -855,8 +911,8 @@ int ot_solve(const ot_problem* p, float* f, float* g, const ot_solve_opts* o,
       info->nonfinite = h[2] != 0.f;
       info->lse_ms = lse_ms;
       info->lse_launches = lse_launches;
-      info->splits_f = L.F.splits;
-      info->splits_g = L.G.splits;
+      info->splits_f = used_splits(L.F, x.sym);
+      info->splits_g = used_splits(L.G, x.sym);
       info->operand_mode = L.k.mode;
       if (info->nonfinite) return fail(OT_ERR_NONFINITE, "potentials are not finite");
     }

@@ -18,8 +18,6 @@ namespace flashot {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kMaxApplySplits = 64;
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t u) {
@@ -70,15 +68,6 @@ __device__ __forceinline__ float block_sum_256(float v, float* sh) {
 constexpr int kMergeLanes = 8;
 constexpr int kMergeRows = 256 / kMergeLanes;
 
-// Bias-MFMA operand of column i (buffer layout in kernels.h): the parts of
-// its bias in lane i % 32 of its tile, three bf16 ones in lane 32 + i % 32.
-__device__ __forceinline__ void write_bias_parts(float* bias, int rpad, int i, float v) {
-  uint2* parts = reinterpret_cast<uint2*>(bias + rpad);
-  const size_t at = (size_t)(i / kTile) * 64 + (i % kTile);
-  parts[at] = bf16x3_parts(v);
-  parts[at + kTile] = make_uint2(kBf16OnesLo, kBf16OnesHi);
-}
-
 __global__ __launch_bounds__(256) void lse_merge_kernel(
     const float2* __restrict__ part, int splits, int rpad, int rows, float bscale, float eps,
     const float* __restrict__ norm, const float* __restrict__ hlw, const float* __restrict__ wgt,
@@ -107,24 +96,10 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(
     S = S * exp2f(M - Mn) + So * exp2f(Mo - Mn);
     M = Mn;
   }
+  const RowFinish fin{bscale, eps, norm, hlw, wgt, pot, bias_out, rows, rpad, with_err, write_pot, avg};
   float e = 0.f;
-  if (sub == 0 && i < rows) {
-    const float shifted = -eps * kLn2 * (M + log2f(S));
-    const float nrm = norm[i];
-    const float half = nrm + shifted;
-    const float pold = (with_err || avg) ? pot[i] : 0.f;
-    if (with_err) e = wgt[i] * fabsf(exp2f((pold - half) * (kLog2e / eps)) - 1.f);
-    const float pnew = avg ? 0.5f * (pold + half) : half;
-    if (write_pot) {
-      pot[i] = pnew;
-      const float v = bscale * (0.5f * (pnew - nrm) + hlw[i]);
-      bias_out[i] = v;
-      write_bias_parts(bias_out, rpad, i, v);
-    }
-  } else if (sub == 0 && i < rpad && write_pot) {
-    bias_out[i] = kSentinel;
-    write_bias_parts(bias_out, rpad, i, kSentinel);
-  }
+  if (sub == 0 && i < rows) e = finish_row(fin, i, M, S, load_row_in(fin, i));
+  else if (sub == 0 && i < rpad) finish_pad_row(fin, i);
   if (with_err) {
     const float tot = block_sum_256(e, sh);
     if (threadIdx.x == 0) err_part[blockIdx.x] = tot;

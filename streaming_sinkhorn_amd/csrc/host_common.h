@@ -26,7 +26,6 @@ const char* last_error();
       return ::flashot::host::fail(OT_ERR_HIP, std::string(#expr) + ": " + hipGetErrorString(e_)); \
   } while (0)
 
-constexpr float kLog2e = 1.4426950408889634f;
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 inline int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }

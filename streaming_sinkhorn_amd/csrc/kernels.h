@@ -17,6 +17,8 @@ namespace flashot {
 constexpr int kTile = 32;
 constexpr int kWaves = 4;  // waves per workgroup of the streamed kernels
 constexpr float kSentinel = -1.0e20f;  // bias of padded columns: exp underflows to 0
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 // Operand modes of the streamed passes.
 constexpr int kModeF32 = 0;    // fp32 operands, fp32 MFMA (32x32x2)
@@ -36,7 +38,10 @@ struct PassShape {
   int ct, bk;           // wide pass: column tiles per block, k-blocks per stage
   int splits, tps;      // column splits and column tiles (wide pass: blocks) per split
   int nrowgroups;       // workgroups along the rows
+  int solo;             // small problem: the half-step may run as one launch (launch_lse_solo)
 };
+// Waves per workgroup of the single-launch half-step (launch_lse_solo).
+constexpr int kSoloWaves = 4;
 
 hipError_t launch_sqnorms(const void* pts, int bf16, int64_t rows, int64_t d, int64_t ld,
                           float* out, hipStream_t st);
@@ -138,6 +143,68 @@ __device__ __forceinline__ uint2 bf16x3_parts(float v) {
   const float r2 = r1 - __uint_as_float(b2 << 16);
   return make_uint2(b1 | (b2 << 16), bf16_bits_rne(r2));
 }
+// Bias-MFMA operand of column i of a bias buffer of rpad columns: the parts
+// of its bias in lane i % 32 of its tile, three bf16 ones in lane 32 + i % 32.
+__device__ __forceinline__ void write_bias_parts(float* bias, int rpad, int i, float v) {
+  uint2* parts = reinterpret_cast<uint2*>(bias + rpad);
+  const size_t at = (size_t)(i / kTile) * 64 + (i % kTile);
+  parts[at] = bf16x3_parts(v);
+  parts[at + kTile] = make_uint2(kBf16OnesLo, kBf16OnesHi);
+}
+// End of a half-step for one row, shared by the merge of split partials and
+// the single-launch small pass ("FlashSinkhorn: IO-Aware Entropic Optimal
+// Transport on GPU", App. D.1-D.2: the potential is written once; App. E.1:
+// the induced marginal of the previous iterate). From the row's merged
+// (M in log2 units, S):
+//   h_i = norm_i - eps ln2 (M + log2 S)            (the half-step value),
+//   pot_i = h_i, or (pot_old_i + h_i) / 2 when avg (symmetric schedule),
+//   next bias_i = bscale ((pot_i - norm_i) / 2 + hlw_i) with its MFMA operand,
+// written only when write_pot; returns w_i |exp((pot_old_i - h_i)/eps) - 1|
+// when with_err, else 0. bscale = 2 log2(e)/eps when the streamed kernels
+// work in log2 units, 1 in dot-product units. Rows rows..rpad-1 of a written
+// bias buffer hold the sentinel (finish_pad_row).
+struct RowFinish {
+  float bscale, eps;
+  const float* norm;
+  const float* hlw;
+  const float* wgt;
+  float* pot;
+  float* bias_out;
+  int rows, rpad, with_err, write_pot, avg;
+};
+// The row's inputs of finish_row, loaded ahead of the reduction that feeds it.
+struct RowIn {
+  float nrm, hlw, wgt, pold;
+};
+__device__ __forceinline__ RowIn load_row_in(const RowFinish& r, int i) {
+  RowIn in;
+  in.nrm = r.norm[i];
+  in.hlw = r.write_pot ? r.hlw[i] : 0.f;
+  in.wgt = r.with_err ? r.wgt[i] : 0.f;
+  in.pold = (r.with_err || r.avg) ? r.pot[i] : 0.f;
+  return in;
+}
+__device__ __forceinline__ float finish_row(const RowFinish& r, int i, float M, float S,
+                                            const RowIn& in) {
+  const float shifted = -r.eps * kLn2 * (M + log2f(S));
+  const float half = in.nrm + shifted;
+  float e = 0.f;
+  if (r.with_err) e = in.wgt * fabsf(exp2f((in.pold - half) * (kLog2e / r.eps)) - 1.f);
+  const float pnew = r.avg ? 0.5f * (in.pold + half) : half;
+  if (r.write_pot) {
+    r.pot[i] = pnew;
+    const float v = r.bscale * (0.5f * (pnew - in.nrm) + in.hlw);
+    r.bias_out[i] = v;
+    write_bias_parts(r.bias_out, r.rpad, i, v);
+  }
+  return e;
+}
+__device__ __forceinline__ void finish_pad_row(const RowFinish& r, int i) {
+  if (r.write_pot) {
+    r.bias_out[i] = kSentinel;
+    write_bias_parts(r.bias_out, r.rpad, i, kSentinel);
+  }
+}
 // parts = 1: also write the bias-MFMA operand after the rpad biases (the
 // buffer then has bias_buffer_bytes(rpad) bytes).
 hipError_t launch_bias_from_pot(const float* pot, const float* norm, const float* hlw, int rows,
@@ -156,6 +223,19 @@ hipError_t launch_vec_resident(const PassShape& s, int mode, const void* Rp, con
                                float* partT, hipStream_t st);
 hipError_t launch_lse_wide(const PassShape& s, int mode, const void* Rp, const void* Cp,
                            const float* cbias, float c, float2* part, hipStream_t st);
+// Single-launch half-step of a small problem (s.solo; modes 1 and 3, row
+// operand resident, per-wave column loads): one workgroup of kSoloWaves
+// waves per 32-row tile, the waves splitting the column tiles; the waves' partials
+// are merged in a fixed order on chip and the row end (finish_row) follows
+// in the same launch. err_part receives one weighted marginal-error sum per
+// row tile (as launch_lse_merge's per-block sums, lse_merge_blocks(rpad) of
+// them) when fin.with_err. Not for the symmetric schedule, whose second pass
+// must read the biases this one overwrites.
+hipError_t launch_lse_solo(const PassShape& s, int mode, const void* Rp, const void* Cp,
+                           const float* cbias, float c, const RowFinish& fin, float* err_part,
+                           hipStream_t st);
+// Whether launch_lse_solo serves this shape and mode.
+bool lse_solo_supported(const PassShape& s, int mode);
 inline hipError_t launch_lse_partial(const PassShape& s, int mode, const void* Rp, const void* Cp,
                                      const float* cbias, float c, float2* part, hipStream_t st) {
   return s.xres ? launch_lse_resident(s, mode, Rp, Cp, cbias, c, part, st)

@@ -157,23 +157,18 @@ __device__ __forceinline__ void write_partials(const float (&M)[RI], const float
   }
 }
 
+// One wave's sweep over column tiles jt0 .. jt0 + last (last >= 0) for its
+// RI row tiles from rt0 (indices past the operand are clamped; their rows
+// are never written): running (M, S[, T]) per lane, the lane pair l, l ^ 32
+// sharing M and holding halves of the row's sums.
 template <int MODE, int KB, int RI, bool VEC>
-__global__ __launch_bounds__(256) void lse_pipe_kernel(
-    const u32x4* __restrict__ Rp, const u32x4* __restrict__ Cp, const float* __restrict__ cbias,
-    const float* __restrict__ vcol, int rtiles, int ctiles, int splits, int tps, float c,
-    float2* __restrict__ part, float* __restrict__ partT, int rpad) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+__device__ __forceinline__ void pipe_sweep(const u32x4* __restrict__ Rp, const u32x4* __restrict__ Cp,
+                                           const float* __restrict__ cbias,
+                                           const float* __restrict__ vcol, int rt0, int rtiles,
+                                           int ctiles, int jt0, int last, int lane, float ks,
+                                           float (&M)[RI], float (&S)[RI], float (&T)[RI]) {
   const int h = lane >> 5;
-  const int s = blockIdx.x % splits;
-  const int rg = blockIdx.x / splits;
-  const int rt0 = (rg * kWaves + wave) * RI;
-  if (rt0 >= rtiles) return;
-  const int jt0 = s * tps;
-  const int last = min(jt0 + tps, ctiles) - 1 - jt0;  // split holds tiles 0..last, last >= 0
-  const float ks = MODE == kModeBF16 ? c : 1.0f;
   const uint2* __restrict__ cb3 = bias_parts(cbias, ctiles * kTile);
-
   u32x4 xr[RI][KB];
 #pragma unroll
   for (int ri = 0; ri < RI; ++ri) {
@@ -181,7 +176,7 @@ __global__ __launch_bounds__(256) void lse_pipe_kernel(
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) xr[ri][kb] = Rp[((size_t)rt * KB + kb) * 64 + lane];
   }
-  float M[RI], S[RI], T[RI], Mfc[RI];
+  float Mfc[RI];
   BiasOp<MODE> Bst[RI];
 #pragma unroll
   for (int ri = 0; ri < RI; ++ri) {
@@ -224,9 +219,78 @@ __global__ __launch_bounds__(256) void lse_pipe_kernel(
   } else {  // tile k remains
     tail_any<MODE, KB, RI, VEC>(accA, vA, MfA, M, S, T, ks);
   }
+}
 
+template <int MODE, int KB, int RI, bool VEC>
+__global__ __launch_bounds__(256) void lse_pipe_kernel(
+    const u32x4* __restrict__ Rp, const u32x4* __restrict__ Cp, const float* __restrict__ cbias,
+    const float* __restrict__ vcol, int rtiles, int ctiles, int splits, int tps, float c,
+    float2* __restrict__ part, float* __restrict__ partT, int rpad) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int s = blockIdx.x % splits;
+  const int rg = blockIdx.x / splits;
+  const int rt0 = (rg * kWaves + wave) * RI;
+  if (rt0 >= rtiles) return;
+  const int jt0 = s * tps;
+  const int last = min(jt0 + tps, ctiles) - 1 - jt0;  // split holds tiles 0..last, last >= 0
+  const float ks = MODE == kModeBF16 ? c : 1.0f;
+  float M[RI], S[RI], T[RI];
+  pipe_sweep<MODE, KB, RI, VEC>(Rp, Cp, cbias, vcol, rt0, rtiles, ctiles, jt0, last, lane, ks, M, S, T);
   // The lane pair shares M: the row's partial is (M in log2 units, S + S').
-  write_partials<RI, VEC>(M, S, T, h, lane, rt0, rtiles, s, rpad, ks, part, partT);
+  write_partials<RI, VEC>(M, S, T, lane >> 5, lane, rt0, rtiles, s, rpad, ks, part, partT);
+}
+
+// Single-launch half-step of a small problem. A workgroup of W waves owns
+// one 32-row tile; wave w sweeps column tiles [w tpw, (w + 1) tpw) and leaves
+// the rows' (M in log2 units, S) in LDS; wave 0 merges the W pairs of each
+// row in wave order with the exact merge (App. D.3) and ends the half-step
+// (potential, next bias, marginal-error term) in the same launch, with the
+// row's inputs loaded before the sweep. A problem too small to fill the chip
+// is bound by launches and the latency of their dependent steps: this removes
+// the separate merge launch and its global partials, with no
+// cross-workgroup synchronisation.
+template <int MODE, int KB, int W>
+__global__ __launch_bounds__(W * 64) void lse_solo_kernel(
+    const u32x4* __restrict__ Rp, const u32x4* __restrict__ Cp, const float* __restrict__ cbias,
+    int rtiles, int ctiles, int tpw, float c, RowFinish fin, float* __restrict__ err_part) {
+  __shared__ float2 ms[W][kTile];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int rt = blockIdx.x;
+  const int i = rt * kTile + lane;
+  const bool owner = wave == 0 && lane < kTile && i < fin.rows;
+  RowIn in{};
+  if (owner) in = load_row_in(fin, i);
+  const int jt0 = wave * tpw;
+  const float ks = MODE == kModeBF16 ? c : 1.0f;
+  float M[1] = {kUnset}, S[1] = {0.f}, T[1] = {0.f};
+  if (jt0 < ctiles)  // waves past the last column tile contribute (M unset, S = 0)
+    pipe_sweep<MODE, KB, 1, false>(Rp, Cp, cbias, nullptr, rt, rtiles, ctiles, jt0,
+                                   min(jt0 + tpw, ctiles) - 1 - jt0, lane, ks, M, S, T);
+  const float St = S[0] + __shfl_xor(S[0], 32);
+  if (lane < kTile) ms[wave][lane] = make_float2(ks * M[0], St);
+  __syncthreads();
+  if (wave != 0) return;
+  float Mm = -3.0e38f, Sm = 0.f;
+#pragma unroll
+  for (int w = 0; w < W; ++w) {
+    const float2 ps = ms[w][lane & 31];
+    if (ps.x > Mm) {
+      Sm = fmaf(Sm, exp2f(Mm - ps.x), ps.y);
+      Mm = ps.x;
+    } else {
+      Sm = fmaf(ps.y, exp2f(ps.x - Mm), Sm);
+    }
+  }
+  float e = 0.f;
+  if (owner) e = finish_row(fin, i, Mm, Sm, in);
+  else if (lane < kTile) finish_pad_row(fin, i);
+  if (fin.with_err) {
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) e += __shfl_xor(e, o);
+    if (lane == 0) err_part[rt] = e;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -515,6 +579,45 @@ static hipError_t lse_resident_dispatch(const PassShape& s, const ResArgs& a, hi
     case 8: resident_go<MODE, 8, VEC>(s, a, st); break;
     case 16: resident_go<MODE, 16, VEC>(s, a, st); break;
     default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int MODE, int KB>
+static void lse_solo_go(const PassShape& s, const void* Rp, const void* Cp, const float* cbias,
+                        float c, const RowFinish& fin, float* err_part, hipStream_t st) {
+  constexpr int W = kSoloWaves;
+  const int tpw = (s.ctiles + W - 1) / W;
+  lse_solo_kernel<MODE, KB, W><<<s.rtiles, W * 64, 0, st>>>(
+      (const u32x4*)Rp, (const u32x4*)Cp, cbias, s.rtiles, s.ctiles, tpw, c, fin, err_part);
+}
+
+bool lse_solo_supported(const PassShape& s, int mode) {
+  if (!s.xres || s.lds) return false;
+  if (mode == kModeHalf2) return s.kb == 2 || s.kb == 4 || s.kb == 8;
+  if (mode == kModeBF16) return s.kb == 1 || s.kb == 2 || s.kb == 4 || s.kb == 8 || s.kb == 16;
+  return false;
+}
+
+hipError_t launch_lse_solo(const PassShape& s, int mode, const void* Rp, const void* Cp,
+                           const float* cbias, float c, const RowFinish& fin, float* err_part,
+                           hipStream_t st) {
+  if (!lse_solo_supported(s, mode) || fin.avg || fin.rpad != s.rtiles * kTile)
+    return hipErrorInvalidValue;
+  if (mode == kModeHalf2) {
+    switch (s.kb) {
+      case 2: lse_solo_go<kModeHalf2, 2>(s, Rp, Cp, cbias, c, fin, err_part, st); break;
+      case 4: lse_solo_go<kModeHalf2, 4>(s, Rp, Cp, cbias, c, fin, err_part, st); break;
+      default: lse_solo_go<kModeHalf2, 8>(s, Rp, Cp, cbias, c, fin, err_part, st); break;
+    }
+  } else {
+    switch (s.kb) {
+      case 1: lse_solo_go<kModeBF16, 1>(s, Rp, Cp, cbias, c, fin, err_part, st); break;
+      case 2: lse_solo_go<kModeBF16, 2>(s, Rp, Cp, cbias, c, fin, err_part, st); break;
+      case 4: lse_solo_go<kModeBF16, 4>(s, Rp, Cp, cbias, c, fin, err_part, st); break;
+      case 8: lse_solo_go<kModeBF16, 8>(s, Rp, Cp, cbias, c, fin, err_part, st); break;
+      default: lse_solo_go<kModeBF16, 16>(s, Rp, Cp, cbias, c, fin, err_part, st); break;
+    }
   }
   return hipGetLastError();
 }

@@ -406,6 +406,46 @@ def test_split_count_changes_only_rounding():
             assert np.abs(host64(g) - ref[1]).max() <= 2e-5
 
 
+# (n, m, d, dtype, waves per workgroup)
+SOLO_CASES = [(1000, 700, 16, "f32", 4), (64, 100, 64, "f32", 4), (33, 1, 5, "bf16", 4),
+              (1024, 1024, 128, "bf16", 4), (2048, 2048, 16, "f32", 4), (300, 2000, 32, "f32", 4)]
+
+
+@pytest.mark.parametrize("n,m,d,dtype,waves", SOLO_CASES)
+def test_single_launch_half_step_matches_split_path(n, m, d, dtype, waves):
+    """Small problems run each half-step as one launch: the workgroup's waves
+    split the columns and their (max, sum) pairs are merged on chip (App. D.3)
+    before the potential is written. Against the oracle that is the same
+    iteration; against the split pass + merge it differs only by the merge
+    order's rounding. Waves past the last column tile (m = 1) contribute
+    nothing."""
+    data = workloads.make("c3_d16_f32", n=n, m=m, d=d)
+    prob = make_problem(data, dtype=dtype)
+    T = 20
+    f, g = zeros(n), zeros(m)
+    info = ssa.ot_solve(prob, f, g, T, want_info=True)
+    f2, g2 = zeros(n), zeros(m)
+    info2 = ssa.ot_solve(prob, f2, g2, T, splits_f=1, splits_g=1, want_info=True)
+    torch.cuda.synchronize()
+    ctiles = (m + 31) // 32
+    tpw = (ctiles + waves - 1) // waves  # column tiles per wave
+    say(f"single launch {n}x{m} d={d} {dtype}: splits used {info['splits_f']},{info['splits_g']} "
+        f"(forced path {info2['splits_f']},{info2['splits_g']})")
+    assert info["splits_f"] == (ctiles + tpw - 1) // tpw
+    df = np.abs(host64(f) - host64(f2)).max()
+    dg = np.abs(host64(g) - host64(g2)).max()
+    say(f"  vs split path: max|df|={df:.2e} max|dg|={dg:.2e}")
+    assert df <= 5e-5 and dg <= 5e-5
+    X, Y, a, b = oracle_inputs(prob)
+    f_ref, g_ref = oracle.sinkhorn(oracle.cost_matrix(X, Y), a, b, float(data["w"].eps), T)
+    ef = np.abs(host64(f) - f_ref).max()
+    eg = np.abs(host64(g) - g_ref).max()
+    say(f"  vs oracle: max|df|={ef:.2e} max|dg|={eg:.2e}")
+    assert ef <= POT_TOL["f32"] and eg <= POT_TOL["f32"]
+    e1, e2 = info["marg_err_row"], info2["marg_err_row"]
+    assert abs(e1 - e2) <= 1e-2 * max(e1, e2) + 1e-6
+
+
 def test_tolerance_stops_early():
     data = workloads.make("c1", n=400, m=300)
     prob = make_problem(data)
