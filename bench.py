@@ -223,18 +223,25 @@ def copy_probe(mib):
     print(json.dumps({"copy_probe_bytes": n * 4, "copies": 3}), flush=True)
 
 
-def rate_probes(reps=3):
+def rate_probes(reps=3, all_kinds=False):
     """Throughput of the exponential and of the fp16 matrix instruction, each
-    from the library's probe kernel timed with HIP events on its stream."""
+    from the library's probe kernel timed with HIP events on its stream; with
+    all_kinds also the fp16 matrix rate at two waves per SIMD with one and two
+    accumulation chains per wave, and that of the d = 64 fp32 pass's per-stage
+    instruction mix (include/flashot_probe.h)."""
     import torch
 
     import streaming_sinkhorn_amd as ssa
 
     out = {}
+    kinds = [(ssa.OT_PROBE_EXP2, "exp2_per_s", 4096), (ssa.OT_PROBE_MFMA_F16, "mfma_f16_tflops", 1024)]
+    if all_kinds:
+        kinds += [(ssa.OT_PROBE_MFMA_F16_1C2W, "mfma_f16_1chain_2waves_tflops", 2048),
+                  (ssa.OT_PROBE_MFMA_F16_2C2W, "mfma_f16_2chains_2waves_tflops", 1024),
+                  (ssa.OT_PROBE_MIX_2W, "mix_2waves_mfma_f16_tflops", 128)]
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
-        for kind, name, iters in ((ssa.OT_PROBE_EXP2, "exp2_per_s", 4096),
-                                  (ssa.OT_PROBE_MFMA_F16, "mfma_f16_tflops", 1024)):
+        for kind, name, iters in kinds:
             ssa.ot_probe_rate(kind, iters)  # warm-up
             best = None
             for _ in range(reps):
@@ -445,7 +452,7 @@ def main():
         import streaming_sinkhorn_amd as ssa
 
         ssa.lib()
-        res = rate_probes()
+        res = rate_probes(all_kinds=True)
         res["exp2_peak_per_s"] = EXP_PEAK_PER_S
         res["mfma_f16_peak_tflops"] = MFMA_PEAK_TFLOPS["f16"]
         print(json.dumps(res), flush=True)

@@ -19,16 +19,24 @@
 extern "C" {
 #endif
 
-#define OT_PROBE_EXP2     0  /* v_exp_f32 throughput: exponentials */
-#define OT_PROBE_MFMA_F16 1  /* 32x32x16 fp16 matrix instruction throughput: flops */
+#define OT_PROBE_EXP2         0  /* v_exp_f32 throughput: exponentials */
+#define OT_PROBE_MFMA_F16     1  /* 32x32x16 fp16 matrix instruction throughput: flops */
+#define OT_PROBE_MFMA_F16_1C2W 2 /* the same with 1 chain per wave, 2 waves per SIMD */
+#define OT_PROBE_MFMA_F16_2C2W 3 /* 2 chains per wave, 2 waves per SIMD */
+#define OT_PROBE_MIX_2W       4  /* 2 chains of 13 matrix instructions per wave interleaved with
+                                    34 exponentials and 48 fp32 additions, 2 waves per SIMD
+                                    (the d = 64 fp32 pass's per-stage mix): matrix flops */
 
 /*
  * ot_probe_rate -- enqueue one probe kernel of `blocks` workgroups of 256
  * threads, each thread (OT_PROBE_EXP2) running 8 independent chains of
  * `iters` exponentials x <- exp2(-x), or each wave (OT_PROBE_MFMA_F16)
  * running 4 independent chains of `iters` 32x32x16 fp16 matrix
- * instructions. The caller times the launch on `stream` (HIP events) and
- * divides *work by the time.
+ * instructions. The *_2W kinds reserve 64 KiB of LDS per workgroup so that
+ * two waves share each SIMD (the occupancy of the register-resident pass)
+ * and run 1 or 2 chains per wave, or (OT_PROBE_MIX_2W) `iters` copies of
+ * that pass's per-stage instruction mix on independent data. The caller
+ * times the launch on `stream` (HIP events) and divides *work by the time.
  *   iters   >= 1
  *   blocks  >= 1 (several per compute unit fill the chip: 2048 is plenty)
  *   out     device fp32, blocks * 256 values (one per thread; keeps the work live)

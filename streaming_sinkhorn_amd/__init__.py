@@ -36,7 +36,7 @@ OT_NATIVE_F32 = 1
 OT_COST_AFFINE = 2
 OT_SPLIT_BF16 = 4
 OT_SCHED_ALTERNATING, OT_SCHED_SYMMETRIC = 0, 1
-OT_PROBE_EXP2, OT_PROBE_MFMA_F16 = 0, 1
+OT_PROBE_EXP2, OT_PROBE_MFMA_F16, OT_PROBE_MFMA_F16_1C2W, OT_PROBE_MFMA_F16_2C2W, OT_PROBE_MIX_2W = range(5)
 _SCHEDULES = {"alternating": OT_SCHED_ALTERNATING, "symmetric": OT_SCHED_SYMMETRIC}
 
 
@@ -466,9 +466,9 @@ def apply_workspace(prob: Problem, V=None, flags: int = 0) -> torch.Tensor:
 
 
 def ot_probe_rate(kind: int, iters: int, blocks: int = 2048):
-    """Enqueue one throughput probe (OT_PROBE_EXP2 or OT_PROBE_MFMA_F16) on the
-    current stream. Returns (output tensor, work of the launch: exponentials or
-    flops); the caller times the launch."""
+    """Enqueue one throughput probe (an OT_PROBE_* kind) on the current stream.
+    Returns (output tensor, work of the launch: exponentials or flops); the
+    caller times the launch."""
     out = torch.empty(int(blocks) * 256, dtype=torch.float32, device="cuda")
     work = ctypes.c_double(0.0)
     _check(lib().ot_probe_rate(int(kind), int(iters), int(blocks), _ptr(out), ctypes.byref(work),
