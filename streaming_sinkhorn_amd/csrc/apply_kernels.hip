@@ -869,7 +869,11 @@ static hipError_t apply_stream_pb(const PassShape& s, int pblocks, const void* R
   if constexpr (SMODE == kModeF32) {
     // fp32 scores (the Hessian-vector product's transport-matrix passes, whose
     // damped Schur solve is sensitive to how their arithmetic differs from the
-    // vector passes'): the plain per-tile kernel, eager running maximum.
+    // vector passes'): the pipelined resident kernel for d <= 64 (it holds two
+    // waves per SIMD up to 8 resident units), else the plain per-tile kernel
+    // with an eager running maximum.
+    if (s.xres && s.kb <= 8)
+      return apply_res_kb<SMODE, PB>(s, pblocks, Rp, Cp, cbias, Vh, c, partMS, partO, ppad, st);
     switch (s.xres ? s.kb : 8) {
       case 1: apply_h2_go<SMODE, 1, true, PB>(s, pblocks, Rp, Cp, cbias, Vh, c, partMS, partO, ppad, st); break;
       case 2: apply_h2_go<SMODE, 2, true, PB>(s, pblocks, Rp, Cp, cbias, Vh, c, partMS, partO, ppad, st); break;

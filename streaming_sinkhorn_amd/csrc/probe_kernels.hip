@@ -86,7 +86,6 @@ __global__ __launch_bounds__(256) void probe_mfma_chains_kernel(int64_t iters,
   f32x16 acc[CHAINS];
 #pragma unroll
   for (int c = 0; c < CHAINS; ++c) acc[c] = f32x16{};
-#pragma unroll 8
   for (int64_t t = 0; t < iters; ++t) {
 #pragma unroll
     for (int c = 0; c < CHAINS; ++c)
