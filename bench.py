@@ -71,9 +71,9 @@ EXP_PEAK_PER_S = 256 * 4 * 8 * 2.4e9
 # FETCH_SIZE / WRITE_SIZE runs (scaled by the copy-kernel calibration), valid
 # only for the kernel source they were taken on.
 TRAFFIC = {
-    "c2": {"kernels_sha256": "1fe26356f929a3b5ecbd87abb0cfc92acf097df376cddbde5f066a15080fc350",
+    "c2": {"kernels_sha256": "2b1ad7b9e57213b3317c05d1b3276a4983bde06ba1b494af3aa61ecafd3b46d7",
            "splits": 16,
-           "bytes_per_launch": 49124512,
+           "bytes_per_launch": 49111450,
            "source": "profiles/lse_pipe_kernel_c2_n20000_d64_f32half2_hbm_traffic.md"},
 }
 # Sources of the register-resident log-sum-exp kernels the counters describe.
