@@ -19,7 +19,10 @@ the fp64 oracle on a bounded sample of the same workload on the host.
 
 Without --graph the line also carries ``graph_replay``: the same steps with
 the iterations replayed from HIP graphs (how ot_solve runs by default),
-timed after the event-timed ones, for reference.
+timed after the event-timed ones, for reference. Workloads of at most 4e8
+pairs also report ``iteration_graph_us``: one iteration with graph replay,
+from the difference of a 60- and a 20-iteration solve (the launch-bound
+latency of small problems; not part of ``value``).
 
 With --graph the timed steps replay the iterations from HIP graphs (no
 per-launch events); the roofline then comes from one extra plain step.
@@ -604,9 +607,37 @@ def main():
     }
     with torch.cuda.stream(stream):
         out["probe"] = rate_probes()
+        if pairs <= 4.0e8:
+            out["iteration_graph_us"] = iteration_latency(
+                ssa, prob, f, g, ws["solve"], stream,
+                dict(splits_f=args.splits, splits_g=args.splits, schedule=args.schedule))
     if cpu is not None:
         out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
+
+
+def iteration_latency(ssa, prob, f, g, ws, stream, opts, short=20, long=60, reps=3):
+    """Time of one iteration with graph replay, without the per-call work
+    (norms, operand packing, final marginal errors): the difference of a
+    `long`- and a `short`-iteration ot_solve (best of `reps` each, HIP events
+    on the stream), divided by long - short. After the timed steps; not part
+    of `value`."""
+    import torch
+
+    best = {}
+    for T in (short, long):
+        ssa.ot_solve(prob, f, g, T, want_info=False, ws=ws, **opts)  # graph capture for this count
+        times = []
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            ssa.ot_solve(prob, f, g, T, want_info=False, ws=ws, **opts)
+            e1.record(stream)
+            stream.synchronize()
+            times.append(e0.elapsed_time(e1))
+        best[T] = min(times)
+    return (best[long] - best[short]) * 1e3 / (long - short)
 
 
 if __name__ == "__main__":
