@@ -74,9 +74,9 @@ EXP_PEAK_PER_S = 256 * 4 * 8 * 2.4e9
 # FETCH_SIZE / WRITE_SIZE runs (scaled by the copy-kernel calibration), valid
 # only for the kernel source they were taken on.
 TRAFFIC = {
-    "c2": {"kernels_sha256": "2b1ad7b9e57213b3317c05d1b3276a4983bde06ba1b494af3aa61ecafd3b46d7",
+    "c2": {"kernels_sha256": "dd5737e67627a0ae4f96b9dc64cb80305379398140e06dd5f7a77b55d2aefd60",
            "splits": 16,
-           "bytes_per_launch": 49111450,
+           "bytes_per_launch": 34082816,
            "source": "profiles/lse_pipe_kernel_c2_n20000_d64_f32half2_hbm_traffic.md"},
 }
 # Sources of the register-resident log-sum-exp kernels the counters describe.

@@ -32,9 +32,11 @@
 //  * the streamed axis is split over workgroups when the output axis alone
 //    cannot fill 256 CUs; partial (stabiliser, sum) pairs are merged
 //    afterwards in a fixed order with the exact merge of App. D.3, so results
-//    are deterministic. Split indices are the fastest-varying part of the
-//    workgroup index, which keeps one split's column tiles on one XCD (its
-//    own L2) when the split count is a multiple of 8.
+//    are deterministic. In the per-wave pass, when the split count is a
+//    multiple of 4, the workgroups' (split, row group) pairs are laid over
+//    the 8 XCDs as a 2 x 4 grid (pipe_block below), so each XCD's L2 serves
+//    half of the rows and a quarter of the columns; the LDS-shared pass keeps
+//    the split index fastest in the workgroup index.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -221,6 +223,33 @@ __device__ __forceinline__ void pipe_sweep(const u32x4* __restrict__ Rp, const u
   }
 }
 
+// Workgroup -> (column split, row group) of the per-wave resident pass
+// (lse_pipe_kernel; the LDS-shared pass measured 1 % slower with it and keeps
+// the split index fastest). Workgroups
+// go to the 8 XCDs round robin (workgroup w on XCD w % 8), each XCD with its
+// own L2. When the split count is a multiple of 4 the XCDs form a 2 x 4
+// grid: XCD x takes the row
+// groups of half x / 4 and the splits of quarter x % 4, so it reads half of
+// the row operand and a quarter of the column operand from memory, not all
+// rows and a split's share of the columns (about two thirds of the HBM / MALL
+// fetch at a square problem). The grid then holds an even number of row
+// groups (the padding one exits at once). Other split counts keep the split
+// index fastest.
+__host__ __device__ inline int pipe_rowgroups(int nrowgroups, int splits) {
+  return splits % 4 == 0 ? (nrowgroups + 1) / 2 * 2 : nrowgroups;
+}
+__device__ __forceinline__ void pipe_block(int bid, int splits, int nrgp, int& s, int& rg) {
+  if (splits % 4 == 0) {
+    const int xcd = bid & 7, li = bid >> 3;
+    const int sq = splits >> 2;
+    s = (xcd & 3) * sq + li % sq;
+    rg = (xcd >> 2) * (nrgp >> 1) + li / sq;
+  } else {
+    s = bid % splits;
+    rg = bid / splits;
+  }
+}
+
 template <int MODE, int KB, int RI, bool VEC>
 __global__ __launch_bounds__(256) void lse_pipe_kernel(
     const u32x4* __restrict__ Rp, const u32x4* __restrict__ Cp, const float* __restrict__ cbias,
@@ -228,8 +257,8 @@ __global__ __launch_bounds__(256) void lse_pipe_kernel(
     float2* __restrict__ part, float* __restrict__ partT, int rpad) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int s = blockIdx.x % splits;
-  const int rg = blockIdx.x / splits;
+  int s, rg;
+  pipe_block(blockIdx.x, splits, gridDim.x / splits, s, rg);
   const int rt0 = (rg * kWaves + wave) * RI;
   if (rt0 >= rtiles) return;
   const int jt0 = s * tps;
@@ -514,7 +543,7 @@ struct ResArgs {
 
 template <int MODE, int KB, int RI, bool VEC>
 static void lse_pipe_go(const PassShape& s, const ResArgs& a, hipStream_t st) {
-  lse_pipe_kernel<MODE, KB, RI, VEC><<<s.nrowgroups * s.splits, 256, 0, st>>>(
+  lse_pipe_kernel<MODE, KB, RI, VEC><<<pipe_rowgroups(s.nrowgroups, s.splits) * s.splits, 256, 0, st>>>(
       (const u32x4*)a.Rp, (const u32x4*)a.Cp, a.cbias, a.vcol, s.rtiles, s.ctiles, s.splits,
       s.tps, a.c, a.part, a.partT, s.rtiles * kTile);
 }
