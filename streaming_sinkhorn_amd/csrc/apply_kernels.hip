@@ -24,7 +24,9 @@ static inline int ceil_div_dev(int a, int b) { return (a + b - 1) / b; }
 // HAD (Algorithm 5, Hadamard-weighted transport (P . A Y^T) V): a second
 // score tile W_ij = a_i . y_j is formed from the packed rows of A on the
 // same column operand, and each exponentiated score is multiplied by it
-// before the value product; S keeps the unweighted sum.
+// before the value product; S keeps the unweighted sum. With XRES the rows
+// of X and of A stay in registers for the whole sweep (d <= 64 in fp32);
+// wider rows are streamed per k-chunk.
 // Grid: (nrowgroups * splits, passes); pass y covers value blocks
 // [y * PB, y * PB + PB) of 32 columns each.
 // ---------------------------------------------------------------------------
@@ -34,7 +36,6 @@ __global__ __launch_bounds__(256) void apply_partial_kernel(
     const float* __restrict__ cbias, const f32x4* __restrict__ Vp, int rtiles, int ctiles,
     int kbp, int splits, int tps, float c, int pblocks, float2* __restrict__ partMS,
     float* __restrict__ partO, int rpad, int ppad) {
-  static_assert(!(HAD && XRES), "the weighted pass streams its row operands per chunk");
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int h = lane >> 5;
@@ -46,10 +47,13 @@ __global__ __launch_bounds__(256) void apply_partial_kernel(
   const int jt0 = s * tps;
   const int jt1 = min(jt0 + tps, ctiles);
 
-  u32x4 xr[KB];
+  u32x4 xr[KB], ar[HAD && XRES ? KB : 1];
   if constexpr (XRES) {
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) xr[kb] = Rp[((size_t)rt * KB + kb) * 64 + lane];
+    for (int kb = 0; kb < KB; ++kb) {
+      xr[kb] = Rp[((size_t)rt * KB + kb) * 64 + lane];
+      if constexpr (HAD) ar[kb] = Ap[((size_t)rt * KB + kb) * 64 + lane];
+    }
   }
   float M = -1.0e30f, S = 0.f;
   f32x16 O[PB];
@@ -61,8 +65,11 @@ __global__ __launch_bounds__(256) void apply_partial_kernel(
     f32x16 accw = f32x16{};
     if constexpr (XRES) {
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-        acc = mfma_kblock<BF16>(Cp[((size_t)jt * KB + kb) * 64 + lane], xr[kb], acc);
+      for (int kb = 0; kb < KB; ++kb) {
+        const u32x4 y = Cp[((size_t)jt * KB + kb) * 64 + lane];
+        acc = mfma_kblock<BF16>(y, xr[kb], acc);
+        if constexpr (HAD) accw = mfma_kblock<BF16>(y, ar[kb], accw);
+      }
     } else {
       for (int kc = 0; kc < kbp; kc += KB) {
         u32x4 yc[KB], xc[KB], ac[HAD ? KB : 1];
@@ -975,15 +982,15 @@ hipError_t launch_apply_partial(const PassShape& s, int bf16, int pblocks, int p
 // Hadamard-weighted pass, fp32 operands only. The rows of X and A are read
 // per column tile in chunks of min(kb, 8) k-blocks; every layout's unit count
 // per tile is a multiple of that chunk.
-template <int KB>
+template <int KB, bool XRES>
 static hipError_t hadamard_pb(const PassShape& s, int pblocks, int pb_per_pass, const void* Rp,
                               const void* Cp, const void* Ap, const float* cbias,
                               const float* Vp, float c, float2* partMS, float* partO, int ppad,
                               hipStream_t st) {
   switch (pb_per_pass) {
-    case 1: apply_go<false, KB, false, 1, true>(s, pblocks, Rp, Cp, Ap, cbias, Vp, c, partMS, partO, ppad, st); break;
-    case 2: apply_go<false, KB, false, 2, true>(s, pblocks, Rp, Cp, Ap, cbias, Vp, c, partMS, partO, ppad, st); break;
-    case 4: apply_go<false, KB, false, 4, true>(s, pblocks, Rp, Cp, Ap, cbias, Vp, c, partMS, partO, ppad, st); break;
+    case 1: apply_go<false, KB, XRES, 1, true>(s, pblocks, Rp, Cp, Ap, cbias, Vp, c, partMS, partO, ppad, st); break;
+    case 2: apply_go<false, KB, XRES, 2, true>(s, pblocks, Rp, Cp, Ap, cbias, Vp, c, partMS, partO, ppad, st); break;
+    case 4: apply_go<false, KB, XRES, 4, true>(s, pblocks, Rp, Cp, Ap, cbias, Vp, c, partMS, partO, ppad, st); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -995,11 +1002,20 @@ hipError_t launch_apply_hadamard(const PassShape& s, int pblocks, int pb_per_pas
                                  hipStream_t st) {
   const int chunk = s.kbp < 8 ? s.kbp : 8;
   if (s.kbp % chunk) return hipErrorInvalidValue;
+  if (s.xres) {  // d <= 64 fp32: rows of X and A resident in registers (kbp = 1, 2, 4, 8)
+    switch (s.kbp) {
+      case 1: return hadamard_pb<1, true>(s, pblocks, pb_per_pass, Rp, Cp, Ap, cbias, Vp, c, partMS, partO, ppad, st);
+      case 2: return hadamard_pb<2, true>(s, pblocks, pb_per_pass, Rp, Cp, Ap, cbias, Vp, c, partMS, partO, ppad, st);
+      case 4: return hadamard_pb<4, true>(s, pblocks, pb_per_pass, Rp, Cp, Ap, cbias, Vp, c, partMS, partO, ppad, st);
+      case 8: return hadamard_pb<8, true>(s, pblocks, pb_per_pass, Rp, Cp, Ap, cbias, Vp, c, partMS, partO, ppad, st);
+      default: break;  // wider resident layouts stream per chunk below
+    }
+  }
   switch (chunk) {
-    case 1: return hadamard_pb<1>(s, pblocks, pb_per_pass, Rp, Cp, Ap, cbias, Vp, c, partMS, partO, ppad, st);
-    case 2: return hadamard_pb<2>(s, pblocks, pb_per_pass, Rp, Cp, Ap, cbias, Vp, c, partMS, partO, ppad, st);
-    case 4: return hadamard_pb<4>(s, pblocks, pb_per_pass, Rp, Cp, Ap, cbias, Vp, c, partMS, partO, ppad, st);
-    case 8: return hadamard_pb<8>(s, pblocks, pb_per_pass, Rp, Cp, Ap, cbias, Vp, c, partMS, partO, ppad, st);
+    case 1: return hadamard_pb<1, false>(s, pblocks, pb_per_pass, Rp, Cp, Ap, cbias, Vp, c, partMS, partO, ppad, st);
+    case 2: return hadamard_pb<2, false>(s, pblocks, pb_per_pass, Rp, Cp, Ap, cbias, Vp, c, partMS, partO, ppad, st);
+    case 4: return hadamard_pb<4, false>(s, pblocks, pb_per_pass, Rp, Cp, Ap, cbias, Vp, c, partMS, partO, ppad, st);
+    case 8: return hadamard_pb<8, false>(s, pblocks, pb_per_pass, Rp, Cp, Ap, cbias, Vp, c, partMS, partO, ppad, st);
     default: return hipErrorInvalidValue;
   }
 }
