@@ -19,14 +19,15 @@ namespace flashot {
 // of them) and walks its split's column blocks of CT tiles; for each block
 // the score tiles are accumulated over the whole dimension in stages of BK
 // k-blocks. The stage's slice of the column block, which all four waves
-// use, is staged once in LDS (double-buffered, one barrier per stage); each
-// wave loads the slice of its own row tiles straight into registers (two
+// use, is staged once in LDS with one barrier per stage (three buffers and
+// the next stage's first k-block read ahead for one-unit k-blocks, a double
+// buffer for the split modes); each wave loads the slice of its own row
+// tiles straight into registers (two
 // register sets, each refilled right after the stage that read it), so LDS
 // carries only the shared operand. A wave's RT + CT fragments feed RT * CT
 // MFMA tiles. bias_j - M_i enters by one MFMA per tile: at the block's start
 // (bf16 parts) or, in the fp32-precision modes, after its last stage (fp32).
-// Then the online LSE (lazy stabiliser, device_common.h) consumes the RT x CT
-// tiles.
+// Then the online LSE (device_common.h) consumes the RT x CT tiles.
 // Units: 1 KiB operand units of the packed layout; KU units per k-block
 // (3 in split mode, 2 in half2 mode), kbp units per tile, padded to whole
 // stages.
