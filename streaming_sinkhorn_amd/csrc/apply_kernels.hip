@@ -367,29 +367,45 @@ __device__ __forceinline__ void split_p(const f32x16& p, u32x4 (&ph)[2], u32x4 (
     }
 }
 
-// Value product of one tile for one 32-column value block: O^T += V^T P^T
-// with V's hi / lo parts at units vb[0..3] = (chunk 0 hi, chunk 0 lo,
-// chunk 1 hi, chunk 1 lo), smallest products first.
+// Value product of one tile for one 32-column value block: O^T += V^T P^T,
+// smallest products first. VP = 2: V's hi / lo parts at units vb[0..3] =
+// (chunk 0 hi, chunk 0 lo, chunk 1 hi, chunk 1 lo), three products per
+// chunk. VP = 1 (bf16 values): hi parts alone at vb[0..1] = (chunk 0 hi,
+// chunk 1 hi), two products per chunk: a bf16 value's lo part is zero. Its
+// 8 significant bits fit fp16 wherever the scaled value is at least 2^-17,
+// and below that the hi part is the nearest multiple of 2^-24, which leaves
+// at most 2^-25, and that rounds to zero in fp16 (ties to even).
+template <int VP = 2>
 __device__ __forceinline__ f32x16 value_block(const u32x4* __restrict__ vb, int lane,
                                               const u32x4 (&ph)[2], const u32x4 (&pl)[2],
                                               f32x16 o) {
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
-    const f16x8 vh = __builtin_bit_cast(f16x8, vb[(2 * q) * 64 + lane]);
-    const f16x8 vl = __builtin_bit_cast(f16x8, vb[(2 * q + 1) * 64 + lane]);
-    o = __builtin_amdgcn_mfma_f32_32x32x16_f16(vl, __builtin_bit_cast(f16x8, ph[q]), o, 0, 0, 0);
+    const f16x8 vh = __builtin_bit_cast(f16x8, vb[(VP * q) * 64 + lane]);
+    if constexpr (VP == 2) {
+      const f16x8 vl = __builtin_bit_cast(f16x8, vb[(2 * q + 1) * 64 + lane]);
+      o = __builtin_amdgcn_mfma_f32_32x32x16_f16(vl, __builtin_bit_cast(f16x8, ph[q]), o, 0, 0, 0);
+    }
     o = __builtin_amdgcn_mfma_f32_32x32x16_f16(vh, __builtin_bit_cast(f16x8, pl[q]), o, 0, 0, 0);
     o = __builtin_amdgcn_mfma_f32_32x32x16_f16(vh, __builtin_bit_cast(f16x8, ph[q]), o, 0, 0, 0);
   }
   return o;
 }
 
-template <int SMODE, int KB, int PB>
+// Source unit, within a pass's PB value blocks of 4 units each, of staged
+// value unit vi (2 VP units per block); blocks past npb repeat the last one.
+template <int VP>
+__device__ __forceinline__ int value_src_unit(int vi, int npb) {
+  if constexpr (VP == 2) return min(vi, 4 * npb - 1);
+  else return min(vi >> 1, npb - 1) * 4 + 2 * (vi & 1);
+}
+
+template <int SMODE, int KB, int PB, int VP>
 __global__ __launch_bounds__(256) void apply_res_kernel(
     const u32x4* __restrict__ Rp, const u32x4* __restrict__ Cp, const float* __restrict__ cbias,
     const u32x4* __restrict__ Vh, int rtiles, int ctiles, int splits, int tps, float c,
     int pblocks, float2* __restrict__ partMS, float* __restrict__ partO, int rpad, int ppad) {
-  constexpr int TU = KB + 4 * PB;             // staged 1 KiB units per column tile
+  constexpr int TU = KB + 2 * VP * PB;        // staged 1 KiB units per column tile
   constexpr int NL = (TU * 64 + 255) / 256;   // staging loads per thread
   constexpr bool FOLD = SMODE == kModeHalf2;  // scores in log2 units, M folded into the bias MFMA
   __shared__ u32x4 lds[4][NL * 256];
@@ -422,7 +438,7 @@ __global__ __launch_bounds__(256) void apply_res_kernel(
       src[i] = Cp + (size_t)u * 64 + le;
       stride[i] = (size_t)KB * 64;
     } else {
-      src[i] = Vh + ((size_t)pb0 * 4 + min(u - KB, 4 * npb - 1)) * 64 + le;
+      src[i] = Vh + ((size_t)pb0 * 4 + value_src_unit<VP>(u - KB, npb)) * 64 + le;
       stride[i] = (size_t)pblocks * 4 * 64;
     }
   }
@@ -462,7 +478,8 @@ __global__ __launch_bounds__(256) void apply_res_kernel(
   auto values = [&](int slot, const u32x4 (&ph)[2], const u32x4 (&pl)[2]) {
     const u32x4* vb = &lds[slot][KB * 64];
 #pragma unroll
-    for (int pb = 0; pb < PB; ++pb) O[pb] = value_block(vb + pb * 4 * 64, lane, ph, pl, O[pb]);
+    for (int pb = 0; pb < PB; ++pb)
+      O[pb] = value_block<VP>(vb + pb * 2 * VP * 64, lane, ph, pl, O[pb]);
   };
 
   // Prologue: tiles 0 and 1 staged, tile 0 scored.
@@ -502,7 +519,7 @@ __global__ __launch_bounds__(256) void apply_res_kernel(
     const bool slow = apply_fast<FOLD>(accC, MfC, M[0], ks, p, ts);
     split_p(p, phC, plC);
     if constexpr (NEXT || PREV) {
-      constexpr int kMfma = (NEXT ? tile_mfmas<SMODE, KB>() + 1 : 0) + (PREV ? 6 * PB : 0);
+      constexpr int kMfma = (NEXT ? tile_mfmas<SMODE, KB>() + 1 : 0) + (PREV ? 2 * (VP + 1) * PB : 0);
       constexpr int kValu = 16 + 16 + 48 + 8;  // exponentials, sums, split, checks
       constexpr int kValuPer = (kValu + kMfma - 1) / kMfma;
       if constexpr (NEXT) __builtin_amdgcn_sched_group_barrier(0x020, NL + 1, 0);  // global loads
@@ -565,17 +582,17 @@ __global__ __launch_bounds__(256) void apply_res_kernel(
   }
 }
 
-template <int SMODE, int KB, int PB>
+template <int SMODE, int KB, int PB, int VP>
 static void apply_res_go(const PassShape& s, int pblocks, const void* Rp, const void* Cp,
                          const float* cbias, const void* Vh, float c, float2* partMS,
                          float* partO, int ppad, hipStream_t st) {
   dim3 grid(s.nrowgroups * s.splits, (pblocks + PB - 1) / PB);
-  apply_res_kernel<SMODE, KB, PB><<<grid, 256, 0, st>>>(
+  apply_res_kernel<SMODE, KB, PB, VP><<<grid, 256, 0, st>>>(
       (const u32x4*)Rp, (const u32x4*)Cp, cbias, (const u32x4*)Vh, s.rtiles, s.ctiles, s.splits,
       s.tps, c, pblocks, partMS, partO, s.rtiles * kTile, ppad);
 }
 
-template <int SMODE, int PB>
+template <int SMODE, int PB, int VP>
 static hipError_t apply_res_kb(const PassShape& s, int pblocks, const void* Rp, const void* Cp,
                                const float* cbias, const void* Vh, float c, float2* partMS,
                                float* partO, int ppad, hipStream_t st) {
@@ -584,15 +601,15 @@ static hipError_t apply_res_kb(const PassShape& s, int pblocks, const void* Rp, 
   // value matrices take more passes over the same scores.
 #define RES_CASE(K)                                                                         \
   case K:                                                                                   \
-    apply_res_go<SMODE, K, (K >= 16 ? 1 : (PB > 2 ? 2 : PB))>(s, pblocks, Rp, Cp, cbias, Vh, \
-                                                             c, partMS, partO, ppad, st);    \
+    apply_res_go<SMODE, K, (K >= 16 ? 1 : (PB > 2 ? 2 : PB)), VP>(s, pblocks, Rp, Cp, cbias, \
+                                                                 Vh, c, partMS, partO, ppad, st); \
     break;
   switch (s.kb) {
     case 1:
       if constexpr (SMODE == kModeHalf2) return hipErrorInvalidValue;
       else
-        apply_res_go<SMODE, 1, (PB > 2 ? 2 : PB)>(s, pblocks, Rp, Cp, cbias, Vh, c, partMS, partO,
-                                                 ppad, st);
+        apply_res_go<SMODE, 1, (PB > 2 ? 2 : PB), VP>(s, pblocks, Rp, Cp, cbias, Vh, c, partMS,
+                                                     partO, ppad, st);
       break;
     RES_CASE(2)
     RES_CASE(4)
@@ -633,7 +650,7 @@ static void apply_h2_go(const PassShape& s, int pblocks, const void* Rp, const v
 // tiles per split to a multiple of CT. The fp16-split (FOLD) and bf16
 // scores only: fp32 scores keep the chunked kernel above.
 // ---------------------------------------------------------------------------
-template <int SMODE, int RT, int CT, int BK, int PB>
+template <int SMODE, int RT, int CT, int BK, int PB, int VP>
 __global__ __launch_bounds__(256) void apply_wide_kernel(
     const u32x4* __restrict__ Rp, const u32x4* __restrict__ Cp, const float* __restrict__ cbias,
     const u32x4* __restrict__ Vh, int rtiles, int ctiles, int kbp, int splits, int tps,
@@ -642,7 +659,7 @@ __global__ __launch_bounds__(256) void apply_wide_kernel(
   constexpr int KU = units_per_kblock<SMODE>();
   constexpr int SU = BK * KU;                     // units per tile per stage
   constexpr int NL = (CT * SU * 64 + 255) / 256;  // column staging loads per thread
-  constexpr int VE = PB * 4 * 64;                 // value entries (16 B) per tile
+  constexpr int VE = PB * 2 * VP * 64;            // value entries (16 B) per tile
   constexpr int NV = (VE + 255) / 256;            // value staging loads per thread
   constexpr bool FOLD = SMODE == kModeHalf2;
   __shared__ u32x4 lds[2][NL * 256];
@@ -699,13 +716,13 @@ __global__ __launch_bounds__(256) void apply_wide_kernel(
 #pragma unroll
       for (int u = 0; u < SU; ++u) x[r][u] = xsrc[r][koff + u * 64];
   };
-  // Value staging: entry e of a tile's PB * 4 units (the pass's blocks; units
-  // past npb repeat the last one and are never written out).
+  // Value staging: entry e of a tile's PB * 2 VP units (the pass's blocks;
+  // units past npb repeat the last one and are never written out).
   int vu[NV], vl[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int e = min(tid + 256 * i, VE - 1);
-    vu[i] = min(e >> 6, 4 * npb - 1);
+    vu[i] = value_src_unit<VP>(e >> 6, npb);
     vl[i] = e & 63;
   }
   auto vload = [&](int jt, u32x4 (&gv)[NV]) {
@@ -818,7 +835,7 @@ __global__ __launch_bounds__(256) void apply_wide_kernel(
         split_p(p, ph, pl);
 #pragma unroll
         for (int pb = 0; pb < PB; ++pb)
-          O[r][pb] = value_block(&vlds[q & 1][pb * 4 * 64], lane, ph, pl, O[r][pb]);
+          O[r][pb] = value_block<VP>(&vlds[q & 1][pb * 2 * VP * 64], lane, ph, pl, O[r][pb]);
       }
       if (q + 1 < CT) vstore((q + 1) & 1, gv);
     }
@@ -844,7 +861,7 @@ __global__ __launch_bounds__(256) void apply_wide_kernel(
   }
 }
 
-template <int SMODE, int PB>
+template <int SMODE, int PB, int VP>
 static hipError_t apply_wide_go(const PassShape& s, int pblocks, const void* Rp, const void* Cp,
                                 const float* cbias, const void* Vh, float c, float2* partMS,
                                 float* partO, int ppad, hipStream_t st) {
@@ -861,7 +878,7 @@ static hipError_t apply_wide_go(const PassShape& s, int pblocks, const void* Rp,
   if (s.tps % CT || s.kbp % (2 * SU)) return hipErrorInvalidValue;
   const int nrg = ceil_div_dev(s.rtiles, kWaves * RT);
   dim3 grid((nrg + 7) / 8 * 8 * s.splits, (pblocks + PB - 1) / PB);
-  apply_wide_kernel<SMODE, RT, CT, BK, PB><<<grid, 256, 0, st>>>(
+  apply_wide_kernel<SMODE, RT, CT, BK, PB, VP><<<grid, 256, 0, st>>>(
       (const u32x4*)Rp, (const u32x4*)Cp, cbias, (const u32x4*)Vh, s.rtiles, s.ctiles, s.kbp,
       s.splits, s.tps, nrg, c, pblocks, partMS, partO, s.rtiles * kTile, ppad);
   return hipGetLastError();
@@ -869,7 +886,7 @@ static hipError_t apply_wide_go(const PassShape& s, int pblocks, const void* Rp,
 
 // Pass with the value product on fp16 parts: the pipelined resident kernel,
 // or the block-tiled kernel when the row operand is not resident.
-template <int SMODE, int PB>
+template <int SMODE, int PB, int VP>
 static hipError_t apply_stream_pb(const PassShape& s, int pblocks, const void* Rp, const void* Cp,
                                   const float* cbias, const void* Vh, float c, float2* partMS,
                                   float* partO, int ppad, hipStream_t st) {
@@ -880,7 +897,7 @@ static hipError_t apply_stream_pb(const PassShape& s, int pblocks, const void* R
     // waves per SIMD up to 8 resident units), else the plain per-tile kernel
     // with an eager running maximum.
     if (s.xres && s.kb <= 8)
-      return apply_res_kb<SMODE, PB>(s, pblocks, Rp, Cp, cbias, Vh, c, partMS, partO, ppad, st);
+      return apply_res_kb<SMODE, PB, 2>(s, pblocks, Rp, Cp, cbias, Vh, c, partMS, partO, ppad, st);
     switch (s.xres ? s.kb : 8) {
       case 1: apply_h2_go<SMODE, 1, true, PB>(s, pblocks, Rp, Cp, cbias, Vh, c, partMS, partO, ppad, st); break;
       case 2: apply_h2_go<SMODE, 2, true, PB>(s, pblocks, Rp, Cp, cbias, Vh, c, partMS, partO, ppad, st); break;
@@ -894,36 +911,45 @@ static hipError_t apply_stream_pb(const PassShape& s, int pblocks, const void* R
     }
     return hipGetLastError();
   } else {
-    if (s.xres) return apply_res_kb<SMODE, PB>(s, pblocks, Rp, Cp, cbias, Vh, c, partMS, partO, ppad, st);
-    return apply_wide_go<SMODE, PB>(s, pblocks, Rp, Cp, cbias, Vh, c, partMS, partO, ppad, st);
+    if (s.xres) return apply_res_kb<SMODE, PB, VP>(s, pblocks, Rp, Cp, cbias, Vh, c, partMS, partO, ppad, st);
+    return apply_wide_go<SMODE, PB, VP>(s, pblocks, Rp, Cp, cbias, Vh, c, partMS, partO, ppad, st);
   }
 }
 
-template <int SMODE>
+template <int SMODE, int VP>
 static hipError_t apply_stream_dispatch(const PassShape& s, int pblocks, int pb_per_pass,
                                         const void* Rp, const void* Cp, const float* cbias,
                                         const void* Vh, float c, float2* partMS, float* partO,
                                         int ppad, hipStream_t st) {
   switch (pb_per_pass) {
-    case 1: return apply_stream_pb<SMODE, 1>(s, pblocks, Rp, Cp, cbias, Vh, c, partMS, partO, ppad, st);
-    case 2: return apply_stream_pb<SMODE, 2>(s, pblocks, Rp, Cp, cbias, Vh, c, partMS, partO, ppad, st);
-    case 4: return apply_stream_pb<SMODE, 4>(s, pblocks, Rp, Cp, cbias, Vh, c, partMS, partO, ppad, st);
+    case 1: return apply_stream_pb<SMODE, 1, VP>(s, pblocks, Rp, Cp, cbias, Vh, c, partMS, partO, ppad, st);
+    case 2: return apply_stream_pb<SMODE, 2, VP>(s, pblocks, Rp, Cp, cbias, Vh, c, partMS, partO, ppad, st);
+    case 4: return apply_stream_pb<SMODE, 4, VP>(s, pblocks, Rp, Cp, cbias, Vh, c, partMS, partO, ppad, st);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_apply_stream(const PassShape& s, int smode, int pblocks, int pb_per_pass,
-                               const void* Rp, const void* Cp, const float* cbias, const void* Vh,
-                               float c, float2* partMS, float* partO, int ppad, hipStream_t st) {
+                               int vparts, const void* Rp, const void* Cp, const float* cbias,
+                               const void* Vh, float c, float2* partMS, float* partO, int ppad,
+                               hipStream_t st) {
+  if (vparts != 1 && vparts != 2) return hipErrorInvalidValue;
   if (smode == kModeHalf2)
-    return apply_stream_dispatch<kModeHalf2>(s, pblocks, pb_per_pass, Rp, Cp, cbias, Vh, c, partMS,
-                                             partO, ppad, st);
+    return vparts == 1
+               ? apply_stream_dispatch<kModeHalf2, 1>(s, pblocks, pb_per_pass, Rp, Cp, cbias, Vh,
+                                                      c, partMS, partO, ppad, st)
+               : apply_stream_dispatch<kModeHalf2, 2>(s, pblocks, pb_per_pass, Rp, Cp, cbias, Vh,
+                                                      c, partMS, partO, ppad, st);
   if (smode == kModeBF16)
-    return apply_stream_dispatch<kModeBF16>(s, pblocks, pb_per_pass, Rp, Cp, cbias, Vh, c, partMS,
-                                            partO, ppad, st);
+    return vparts == 1
+               ? apply_stream_dispatch<kModeBF16, 1>(s, pblocks, pb_per_pass, Rp, Cp, cbias, Vh, c,
+                                                     partMS, partO, ppad, st)
+               : apply_stream_dispatch<kModeBF16, 2>(s, pblocks, pb_per_pass, Rp, Cp, cbias, Vh, c,
+                                                     partMS, partO, ppad, st);
+  // fp32 scores (the Hessian-vector product's passes): fp32 values, both parts
   if (smode == kModeF32)
-    return apply_stream_dispatch<kModeF32>(s, pblocks, pb_per_pass, Rp, Cp, cbias, Vh, c, partMS,
-                                           partO, ppad, st);
+    return apply_stream_dispatch<kModeF32, 2>(s, pblocks, pb_per_pass, Rp, Cp, cbias, Vh, c, partMS,
+                                              partO, ppad, st);
   return hipErrorInvalidValue;
 }
 

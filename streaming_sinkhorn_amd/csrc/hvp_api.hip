@@ -160,7 +160,7 @@ int transport(const Transport& t, bool tr, const float* V, int64_t cols, int64_t
   } else {
     OT_HIP(launch_vcol_absmax(V, 0, srows, cols, ldv, t.vamax, st));
     OT_HIP(launch_pack_values_h2(V, 0, srows, cols, ldv, S.ctiles, cc.pblocks, t.vamax, t.vp, st));
-    OT_HIP(launch_apply_stream(S, kModeF32, cc.pblocks, cc.pb_per_pass, Rp, Cp, bc, t.vp, t.c,
+    OT_HIP(launch_apply_stream(S, kModeF32, cc.pblocks, cc.pb_per_pass, 2, Rp, Cp, bc, t.vp, t.c,
                                t.pms, t.po, cc.ppad, st));
   }
   // the fp16-value kernels write their stabilisers in log2 units

@@ -103,9 +103,13 @@ hipError_t launch_pack_values_h2(const void* V, int bf16, int64_t rows, int64_t 
 // Column tiles per block of the wide transport application; its passes need
 // the column tiles per split (PassShape::tps) to be a multiple of it.
 constexpr int kApplyWideCT = 4;
+// vparts: fp16 parts of each value the product uses, 2 (hi and lo: fp32
+// values) or 1 (hi alone: bf16 values, whose lo part in the layout is always
+// zero); kModeF32 scores always take both.
 hipError_t launch_apply_stream(const PassShape& s, int smode, int pblocks, int pb_per_pass,
-                               const void* Rp, const void* Cp, const float* cbias, const void* Vh,
-                               float c, float2* partMS, float* partO, int ppad, hipStream_t st);
+                               int vparts, const void* Rp, const void* Cp, const float* cbias,
+                               const void* Vh, float c, float2* partMS, float* partO, int ppad,
+                               hipStream_t st);
 hipError_t launch_pack_values(const void* V, int bf16, int64_t rows, int64_t cols, int64_t ldv,
                               int ctiles, int pblocks, float* dst, hipStream_t st);
 hipError_t launch_weights(const float* w, int rows, int rpad, float eps, float* wgt, float* hlw,

@@ -340,6 +340,39 @@ def test_apply_plan_value_column_scales(dtype):
     assert np.all(out[:, 3] == 0.0)
 
 
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("f32", 1024), ("bf16", 64), ("bf16", 512)])
+def test_apply_plan_bf16_values_take_one_part(dtype, d):
+    """bf16 values enter the value product by their fp16 hi parts alone (their
+    lo parts in the layout are zero): the result equals, bitwise, that of the
+    same values given as fp32 (hi and lo parts), and matches the oracle, for
+    register-resident and wide rows, columns spanning twelve decades included."""
+    n, m, eps = 170, 150, 0.1
+    say(f"bf16 values dtype={dtype} d={d}")
+    base = "c3_d16_bf16" if dtype == "bf16" else "c3_d16_f32"
+    data = workloads.make(base, n=n, m=m, d=d)
+    prob = make_problem(data, eps=eps)
+    X, Y, a, b = oracle_inputs(prob)
+    C = oracle.cost_matrix(X, Y)
+    f32, g32 = (v.astype(np.float32) for v in oracle.sinkhorn(C, a, b, eps, 20))
+    P = oracle.plan(C, a, b, f32.astype(np.float64), g32.astype(np.float64), eps)
+    f, g = torch.from_numpy(f32).to(DEV), torch.from_numpy(g32).to(DEV)
+    rng = np.random.default_rng(d)
+    V = rng.standard_normal((m, 3))
+    V[:, 1] *= 10.0 ** rng.uniform(-12, 0, m)
+    V[:, 2] *= 3e-20
+    U = rng.standard_normal((n, 40))
+    for M, flags, ref_fn in ((V, 0, oracle.apply_plan), (U, ssa.OT_TRANSPOSE, oracle.apply_plan_t)):
+        Mb = torch.from_numpy(M.astype(np.float32)).to(DEV).to(torch.bfloat16)
+        one = ssa.ot_apply_plan(prob, f, g, Mb, flags=flags)
+        two = ssa.ot_apply_plan(prob, f, g, Mb.float(), flags=flags)
+        torch.cuda.synchronize()
+        assert torch.equal(one, two)
+        ref = ref_fn(P, host64(Mb))
+        out = host64(one)
+        for k in range(M.shape[1]):
+            assert _rel(out[:, k], ref[:, k]) <= PV_TOL, k
+
+
 # --- execution properties ---------------------------------------------------------------
 
 def test_deterministic_graph_eager_and_resume():
