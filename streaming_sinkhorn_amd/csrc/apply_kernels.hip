@@ -305,12 +305,12 @@ constexpr float kApplyTileSumLimit = 0x1p15f;
 template <bool FOLD>
 __device__ __forceinline__ bool apply_fast(const f32x16& a, float Mf, float M, float ks, f32x16& p,
                                            float& s) {
-  float e[4] = {0.f, 0.f, 0.f, 0.f};
+  float e[4];
   const float kM = -ks * M;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     p[r] = __builtin_amdgcn_exp2f(FOLD ? a[r] : fmaf(ks, a[r], kM));
-    e[r & 3] += p[r];
+    e[r & 3] = r < 4 ? p[r] : e[r & 3] + p[r];
   }
   s = (e[0] + e[1]) + (e[2] + e[3]);
   if constexpr (FOLD) return !(s < kApplyTileSumLimit) | (Mf != M);
@@ -338,11 +338,11 @@ __device__ __forceinline__ void apply_exact(const f32x16& a, float Mf, float& M,
   const float Mn = (M > 0.5f * kUnset && ks * (m - M) <= kApplyRaiseMargin) ? M : fmaxf(m, M);
   const float sc = __builtin_amdgcn_exp2f(ks * (M - Mn));  // 0 when M was not set
   const float kM = -ks * Mn;
-  float e[4] = {0.f, 0.f, 0.f, 0.f};
+  float e[4];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     p[r] = __builtin_amdgcn_exp2f(FOLD ? ks * ((a[r] + Mf) - Mn) : fmaf(ks, a[r], kM));
-    e[r & 3] += p[r];
+    e[r & 3] = r < 4 ? p[r] : e[r & 3] + p[r];
   }
   S = fmaf(S, sc, (e[0] + e[1]) + (e[2] + e[3]));
 #pragma unroll
@@ -350,18 +350,31 @@ __device__ __forceinline__ void apply_exact(const f32x16& a, float Mf, float& M,
   M = Mn;
 }
 
+// -1.0f that the compiler cannot see through: p - hi written as
+// fma(hi, -1, p) with it is selected as one mixed-precision fma that reads hi
+// straight from its fp16 half (a literal -1 folds back into a conversion and
+// a subtraction). The product is exact and p - hi is exact in fp32, so the
+// value is the difference itself.
+__device__ __forceinline__ float opaque_minus_one() {
+  float r;
+  asm("s_mov_b32 %0, -1.0" : "=s"(r));
+  return r;
+}
+
 // p (accumulator entries 8q .. 8q+7 are the B operand of k-chunk q) as fp16
 // parts: hi = fp16(p) and lo = fp16(p - hi), both rounded to nearest.
 __device__ __forceinline__ void split_p(const f32x16& p, u32x4 (&ph)[2], u32x4 (&pl)[2]) {
   typedef _Float16 h2v __attribute__((ext_vector_type(2)));
   typedef float f2v __attribute__((ext_vector_type(2)));
+  const float m1 = opaque_minus_one();
 #pragma unroll
   for (int q = 0; q < 2; ++q)
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const f2v v = {p[8 * q + 2 * w], p[8 * q + 2 * w + 1]};
       const h2v hi = __builtin_convertvector(v, h2v);
-      const h2v lo = __builtin_convertvector(v - __builtin_convertvector(hi, f2v), h2v);
+      const f2v d = {__builtin_fmaf((float)hi[0], m1, v[0]), __builtin_fmaf((float)hi[1], m1, v[1])};
+      const h2v lo = __builtin_convertvector(d, h2v);
       ph[q][w] = __builtin_bit_cast(uint32_t, hi);
       pl[q][w] = __builtin_bit_cast(uint32_t, lo);
     }
@@ -384,6 +397,24 @@ __device__ __forceinline__ f32x16 value_block(const u32x4* __restrict__ vb, int 
     const f16x8 vh = __builtin_bit_cast(f16x8, vb[(VP * q) * 64 + lane]);
     if constexpr (VP == 2) {
       const f16x8 vl = __builtin_bit_cast(f16x8, vb[(2 * q + 1) * 64 + lane]);
+      o = __builtin_amdgcn_mfma_f32_32x32x16_f16(vl, __builtin_bit_cast(f16x8, ph[q]), o, 0, 0, 0);
+    }
+    o = __builtin_amdgcn_mfma_f32_32x32x16_f16(vh, __builtin_bit_cast(f16x8, pl[q]), o, 0, 0, 0);
+    o = __builtin_amdgcn_mfma_f32_32x32x16_f16(vh, __builtin_bit_cast(f16x8, ph[q]), o, 0, 0, 0);
+  }
+  return o;
+}
+
+// value_block on fragments already in registers: v[0 .. 2 VP) are this
+// lane's entries of the units in the staging order above.
+template <int VP>
+__device__ __forceinline__ f32x16 value_block_frag(const u32x4* v, const u32x4 (&ph)[2],
+                                                   const u32x4 (&pl)[2], f32x16 o) {
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const f16x8 vh = __builtin_bit_cast(f16x8, v[VP * q]);
+    if constexpr (VP == 2) {
+      const f16x8 vl = __builtin_bit_cast(f16x8, v[2 * q + 1]);
       o = __builtin_amdgcn_mfma_f32_32x32x16_f16(vl, __builtin_bit_cast(f16x8, ph[q]), o, 0, 0, 0);
     }
     o = __builtin_amdgcn_mfma_f32_32x32x16_f16(vh, __builtin_bit_cast(f16x8, pl[q]), o, 0, 0, 0);
@@ -662,8 +693,11 @@ __global__ __launch_bounds__(256) void apply_wide_kernel(
   constexpr int VE = PB * 2 * VP * 64;            // value entries (16 B) per tile
   constexpr int NV = (VE + 255) / 256;            // value staging loads per thread
   constexpr bool FOLD = SMODE == kModeHalf2;
+  // Value fragments of at most two units per block: read by each wave into
+  // registers (RV), else staged in LDS tile by tile.
+  constexpr bool RV = RT == 1 && PB * VP <= 2;
   __shared__ u32x4 lds[2][NL * 256];
-  __shared__ u32x4 vlds[2][NV * 256];
+  __shared__ u32x4 vlds[RV ? 1 : 2][RV ? 1 : NV * 256];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -813,31 +847,74 @@ __global__ __launch_bounds__(256) void apply_wide_kernel(
                                                          acc[r][q], 0, 0, 0);
     }
 
-    // Value epilogue of the block, tile by tile.
-    u32x4 gv[NV];
-    vload(jt0, gv);
-    vstore(0, gv);
+    if constexpr (RV) {
+      // Value epilogue with the fragments in registers, fetched one tile
+      // ahead, and no barrier: the exponentials and the fp16 split of tile
+      // q + 1 (after tile q's exact path, which may raise M) are formed while
+      // tile q's value products run.
+      constexpr int NF = PB * 2 * VP;
+      auto vfetch = [&](int jt, u32x4 (&v)[NF]) {
+        jt = min(jt, ctiles - 1);
 #pragma unroll
-    for (int q = 0; q < CT; ++q) {
-      __syncthreads();  // tile q's values are in vlds[q & 1]; the other slot is free
-      if (q + 1 < CT) vload(jt0 + q + 1, gv);
+        for (int i = 0; i < NF; ++i)
+          v[i] = Vh[(((size_t)jt * pblocks + pb0) * 4 + value_src_unit<VP>(i, npb)) * 64 + lane];
+      };
+      u32x4 vA[NF], vB[NF];
+      vfetch(jt0, vA);
+      f32x16 pn;
+      float tsn;
+      bool slown = apply_fast<FOLD>(acc[0][0], Mf[0], M[0], ks, pn, tsn);
 #pragma unroll
-      for (int r = 0; r < RT; ++r) {
-        f32x16 p;
-        float ts;
-        const bool slow = apply_fast<FOLD>(acc[r][q], Mf[r], M[r], ks, p, ts);
-        if (__builtin_amdgcn_ballot_w64(slow) != 0) {
-          apply_exact<FOLD, PB>(acc[r][q], Mf[r], M[r], S[r], O[r], ks, p);
-        } else {
-          S[r] += ts;
-        }
+      for (int q = 0; q < CT; ++q) {
+        u32x4 (&vc)[NF] = (q & 1) ? vB : vA;
+        u32x4 (&vn)[NF] = (q & 1) ? vA : vB;
+        if (q + 1 < CT) vfetch(jt0 + q + 1, vn);
+        f32x16 p = pn;
+        if (__builtin_amdgcn_ballot_w64(slown) != 0)
+          apply_exact<FOLD, PB>(acc[0][q], Mf[0], M[0], S[0], O[0], ks, p);
+        else
+          S[0] += tsn;
         u32x4 ph[2], pl[2];
         split_p(p, ph, pl);
+        if (q + 1 < CT) slown = apply_fast<FOLD>(acc[0][q + 1], Mf[0], M[0], ks, pn, tsn);
 #pragma unroll
         for (int pb = 0; pb < PB; ++pb)
-          O[r][pb] = value_block<VP>(&vlds[q & 1][pb * 2 * VP * 64], lane, ph, pl, O[r][pb]);
+          O[0][pb] = value_block_frag<VP>(&vc[pb * 2 * VP], ph, pl, O[0][pb]);
       }
-      if (q + 1 < CT) vstore((q + 1) & 1, gv);
+    } else {
+      // Value epilogue with the fragments staged in LDS, tile by tile.
+      u32x4 gv[NV];
+      vload(jt0, gv);
+      vstore(0, gv);
+#pragma unroll
+      for (int q = 0; q < CT; ++q) {
+        __syncthreads();  // tile q's values are in vlds[q & 1]; the other slot is free
+        if (q + 1 < CT) vload(jt0 + q + 1, gv);
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+          // p's fp16 parts times the tile's values; written out in both
+          // branches below, so that the common one keeps p and O in place
+          // (one join after the exact path costs register copies per tile)
+          auto values = [&](const f32x16& p) {
+            u32x4 ph[2], pl[2];
+            split_p(p, ph, pl);
+#pragma unroll
+            for (int pb = 0; pb < PB; ++pb)
+              O[r][pb] = value_block<VP>(&vlds[q & 1][pb * 2 * VP * 64], lane, ph, pl, O[r][pb]);
+          };
+          f32x16 p;
+          float ts;
+          const bool slow = apply_fast<FOLD>(acc[r][q], Mf[r], M[r], ks, p, ts);
+          if (__builtin_amdgcn_ballot_w64(slow) != 0) {
+            apply_exact<FOLD, PB>(acc[r][q], Mf[r], M[r], S[r], O[r], ks, p);
+            values(p);
+          } else {
+            S[r] += ts;
+            values(p);
+          }
+        }
+        if (q + 1 < CT) vstore((q + 1) & 1, gv);
+      }
     }
   }
 
