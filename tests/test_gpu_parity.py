@@ -266,6 +266,7 @@ APPLY_CASES = [
     (150, 170, 512, "bf16", 0.1, 33),
     (90, 75, 17, "f32", 0.05, 1),
     (64, 1, 8, "f32", 0.1, 5),
+    (170, 190, 300, "f32", 0.1, 20),
 ]
 
 
@@ -338,6 +339,30 @@ def test_apply_plan_value_column_scales(dtype):
     for k in range(3):
         assert _rel(out[:, k], ref[:, k]) <= PV_TOL, k
     assert np.all(out[:, 3] == 0.0)
+
+
+@pytest.mark.parametrize("d,cols", [(64, 20), (512, 20), (512, 64)])
+def test_apply_plan_f32_values_on_bf16_points(d, cols):
+    """fp32 values (hi and lo fp16 parts) with bf16 points: resident rows, and
+    wide rows with one value block (fragments read into registers) or two
+    (staged in LDS)."""
+    n, m, eps = 150, 210, 0.1
+    say(f"f32 values on bf16 points d={d} cols={cols}")
+    data = workloads.make("c3_d16_bf16", n=n, m=m, d=d)
+    prob = make_problem(data, eps=eps)
+    X, Y, a, b = oracle_inputs(prob)
+    C = oracle.cost_matrix(X, Y)
+    f32, g32 = (v.astype(np.float32) for v in oracle.sinkhorn(C, a, b, eps, 20))
+    P = oracle.plan(C, a, b, f32.astype(np.float64), g32.astype(np.float64), eps)
+    f, g = torch.from_numpy(f32).to(DEV), torch.from_numpy(g32).to(DEV)
+    rng = np.random.default_rng(d + cols)
+    V = rng.standard_normal((m, cols)).astype(np.float32)
+    U = rng.standard_normal((n, cols)).astype(np.float32)
+    pv = ssa.ot_apply_plan(prob, f, g, torch.from_numpy(V).to(DEV))
+    ptu = ssa.ot_apply_plan(prob, f, g, torch.from_numpy(U).to(DEV), flags=ssa.OT_TRANSPOSE)
+    torch.cuda.synchronize()
+    assert _rel(host64(pv), oracle.apply_plan(P, V.astype(np.float64))) <= PV_TOL
+    assert _rel(host64(ptu), oracle.apply_plan_t(P, U.astype(np.float64))) <= PV_TOL
 
 
 @pytest.mark.parametrize("dtype,d", [("f32", 64), ("f32", 1024), ("bf16", 64), ("bf16", 512)])
