@@ -137,11 +137,12 @@ extern "C" {
  *               synchronises. Transport application (ot_apply_plan) forms
  *               its scores the same way, and multiplies the exponentiated
  *               scores into the values on the fp16 matrix cores: each score
- *               p (at most 1 after the running maximum) as two fp16 parts
- *               and each value column, scaled by a power of two, as two fp16
- *               parts, three partial products per term, each within about
- *               2^-22 of its size. Under OT_NATIVE_F32 / OT_SPLIT_BF16 both
- *               products are fp32.
+ *               p (below 2^15 against a lazily raised stabiliser) as two
+ *               fp16 parts and each value column, scaled by a power of two,
+ *               as two fp16 parts, three partial products per term, each
+ *               within about 2^-22 of its size (bf16 values: their lo part
+ *               is zero, two products). Under OT_NATIVE_F32 / OT_SPLIT_BF16
+ *               both products are fp32.
  */
 typedef struct ot_problem {
   const void* x;
@@ -324,8 +325,9 @@ int ot_sinkhorn_divergence(const ot_problem* p, const ot_solve_opts* opts, float
  *   V       device, (m x cols) for P V or (n x cols) for P^T U, row stride ldv,
  *           storage v_dtype (OT_F32 / OT_BF16). The value product runs on
  *           the fp16 matrix cores with two fp16 parts per score and per
- *           (power-of-two scaled) value, three partial products per term;
- *           fp32 under OT_NATIVE_F32 / OT_SPLIT_BF16 (see ot_problem flags)
+ *           (power-of-two scaled) value, three partial products per term
+ *           (two for OT_BF16 values, whose lo part is zero); fp32 under
+ *           OT_NATIVE_F32 / OT_SPLIT_BF16 (see ot_problem flags)
  *   cols    1 <= cols <= OT_MAX_COLS
  *   flags   0 or OT_TRANSPOSE, optionally with one of OT_GRAD / OT_BARY
  *   out     device fp32, row-major (n x cols) or (m x cols), stride cols
