@@ -332,6 +332,18 @@ def test_apply_plan_identities():
     np.testing.assert_allclose(oracle.barycentric(Pp, V), V[perm], rtol=1e-14)
 
 
+def test_marginals_and_errors_worked_by_hand():
+    """A 2 x 2 coupling worked by hand: row sums (0.3, 0.7), column sums
+    (0.4, 0.6); against a = (0.25, 0.75), b = (0.5, 0.5) the L1 errors are
+    0.05 + 0.05 = 0.1 and 0.1 + 0.1 = 0.2 (rows and columns not swapped)."""
+    P = np.array([[0.1, 0.2], [0.3, 0.4]])
+    r, c = oracle.marginals(P)
+    np.testing.assert_allclose(r, [0.3, 0.7], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(c, [0.4, 0.6], rtol=0, atol=1e-15)
+    er, ec = oracle.marginal_errors(P, np.array([0.25, 0.75]), np.array([0.5, 0.5]))
+    assert abs(er - 0.1) < 1e-15 and abs(ec - 0.2) < 1e-15
+
+
 def test_row_and_column_evaluators_agree_with_dense():
     """The one-at-a-time evaluators are the dense definitions on a slice."""
     X, Y, a, b = _problem(20, 15, 4)
