@@ -673,8 +673,11 @@ static void apply_h2_go(const PassShape& s, int pblocks, const void* Rp, const v
 // the block's last stage the bias and the stabiliser are added (fp32
 // instruction), then, tile by tile: the lazy-stabiliser softmax of the
 // resident pass (apply_fast / apply_exact), the fp16 split of p, and the
-// value product against the tile's value parts, staged in a second,
-// double-buffered LDS area while the previous tile is multiplied. The
+// value product against the tile's value parts: with at most two value
+// units per tile, read by each wave straight into registers one tile ahead,
+// the next tile's exponentials formed while this tile's value products run
+// (no barrier in the epilogue); wider, staged in a second, double-buffered
+// LDS area while the previous tile is multiplied. The
 // stabiliser a block's tiles are scored against is the one at the block's
 // start, so a raise inside a block sends the block's later tiles down the
 // exact path (FOLD modes). Splits hold whole blocks: the host rounds the
