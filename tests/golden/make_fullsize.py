@@ -29,10 +29,15 @@ processes:
 ``tests/test_golden_fullsize_script.py`` checks on a small workload that this
 equals the dense ``oracle.sinkhorn`` bitwise.
 
-Usage: python tests/golden/make_fullsize.py c2 c5 ... [--workers K] [--scratch DIR]
+Usage: python tests/golden/make_fullsize.py c2 c5 ... [--workers K] [--scratch DIR] [--resume]
 Each workload writes ``tests/golden/fullsize/<name>.npz`` (f, g as float64 and
 the marginal errors). The scratch folder holds the cached cost (up to 39 GB
-for the 70000-point workload) and is deleted afterwards.
+for the 70000-point workload) and a checkpoint of (f, g) every 10
+iterations; it is deleted afterwards. ``--resume`` continues an interrupted
+run from that folder: the cached cost is kept once sampled rows of it,
+recomputed, match it bitwise, and the iterations restart from the last
+checkpoint (the half-steps are deterministic, so the result is the one an
+uninterrupted run gives).
 """
 
 from __future__ import annotations
@@ -102,7 +107,14 @@ def _init_worker(niceness):
         pass
 
 
-def solve_sliced(X, Y, a, b, eps, iters, workers, scratch, log=print):
+def _cached_cost_valid(C, X, Y, rows):
+    """Whether a cost file left by an earlier run holds this workload's cost:
+    first, middle and last row slices recomputed and compared bitwise."""
+    picks = [rows[0], rows[len(rows) // 2], rows[-1]]
+    return all(np.array_equal(C[r0:r1], oracle.cost_matrix(X[r0:r1], Y)) for r0, r1 in picks)
+
+
+def solve_sliced(X, Y, a, b, eps, iters, workers, scratch, log=print, resume=False):
     """``oracle.sinkhorn`` from zero potentials, evaluated on row / column slices.
 
     Returns (f, g, err_row, err_col) with the L1 marginal errors of the final
@@ -116,29 +128,47 @@ def solve_sliced(X, Y, a, b, eps, iters, workers, scratch, log=print):
     n, m = X.shape[0], Y.shape[0]
     os.makedirs(scratch, exist_ok=True)
     cpath = os.path.join(scratch, "cost.f64")
-    C = np.memmap(cpath, dtype=np.float64, mode="w+", shape=(n, m))
-    F = np.memmap(os.path.join(scratch, "f.f64"), dtype=np.float64, mode="w+", shape=(n,))
-    G = np.memmap(os.path.join(scratch, "g.f64"), dtype=np.float64, mode="w+", shape=(m,))
-    F[:] = 0.0
-    G[:] = 0.0
-    _S.update(C=C, F=F, G=G, X=X, Y=Y, a=a, b=b, eps=float(eps))
+    ckpt = os.path.join(scratch, "checkpoint.npz")
     rows = _ranges(n, max(1, BLOCK_ELEMS // m))
     cols = _ranges(m, max(1, BLOCK_ELEMS // n))
     # cost rows: the direct difference materialises rows x m x d temporaries
     cost_rows = _ranges(n, max(1, (BLOCK_ELEMS * 4) // (m * max(1, X.shape[1]))))
+    reuse = (resume and os.path.exists(cpath) and os.path.getsize(cpath) == n * m * 8)
+    C = np.memmap(cpath, dtype=np.float64, mode="r+" if reuse else "w+", shape=(n, m))
+    if reuse and not _cached_cost_valid(C, X, Y, cost_rows):
+        log("  cached cost does not match this workload: recomputing it")
+        reuse = False
+    F = np.memmap(os.path.join(scratch, "f.f64"), dtype=np.float64, mode="w+", shape=(n,))
+    G = np.memmap(os.path.join(scratch, "g.f64"), dtype=np.float64, mode="w+", shape=(m,))
+    F[:] = 0.0
+    G[:] = 0.0
+    start = 0
+    if reuse and os.path.exists(ckpt):
+        with np.load(ckpt) as z:
+            if int(z["iters"]) == int(iters) and z["f"].shape == (n,) and z["g"].shape == (m,):
+                start = int(z["t"])
+                F[:] = z["f"]
+                G[:] = z["g"]
+    _S.update(C=C, F=F, G=G, X=X, Y=Y, a=a, b=b, eps=float(eps))
     ctx = mp.get_context("fork")
     t0 = time.perf_counter()
     with ctx.Pool(workers, initializer=_init_worker, initargs=(10,)) as pool:
-        for _ in pool.imap_unordered(_cost_task, cost_rows, chunksize=4):
-            pass
-        log(f"  cost {n}x{m}: {time.perf_counter() - t0:.1f} s")
-        for t in range(int(iters)):
+        if reuse:
+            log(f"  cost {n}x{m}: reused from {cpath}; from iteration {start}")
+        else:
+            for _ in pool.imap_unordered(_cost_task, cost_rows, chunksize=4):
+                pass
+            log(f"  cost {n}x{m}: {time.perf_counter() - t0:.1f} s")
+        for t in range(start, int(iters)):
             for _ in pool.imap_unordered(_f_task, rows):
                 pass
             for _ in pool.imap_unordered(_g_task, cols):
                 pass
             if t % 10 == 9 or t == iters - 1:
                 log(f"  iteration {t + 1}/{iters}: {time.perf_counter() - t0:.1f} s")
+                tmp = ckpt + ".tmp.npz"
+                np.savez(tmp, t=t + 1, iters=int(iters), f=np.array(F), g=np.array(G))
+                os.replace(tmp, ckpt)
         r = np.empty(n)
         c = np.empty(m)
         for r0, v in pool.imap_unordered(_r_task, rows):
@@ -153,13 +183,13 @@ def solve_sliced(X, Y, a, b, eps, iters, workers, scratch, log=print):
     return f, g, float(np.abs(r - a).sum()), float(np.abs(c - b).sum())
 
 
-def make_one(name, workers, scratch, log=print):
+def make_one(name, workers, scratch, log=print, resume=False):
     data = workloads.make(name)
     w = data["w"]
     log(f"{name}: n={w.n} m={w.m} d={w.d} {w.dtype} eps={w.eps} T={w.iters}, {workers} workers")
     t0 = time.perf_counter()
     f, g, er, ec = solve_sliced(data["X"], data["Y"], data["a"], data["b"], w.eps, w.iters,
-                                workers, os.path.join(scratch, name), log=log)
+                                workers, os.path.join(scratch, name), log=log, resume=resume)
     os.makedirs(OUT_DIR, exist_ok=True)
     path = os.path.join(OUT_DIR, f"{name}.npz")
     np.savez_compressed(path, f=f, g=g, marg_err_row=er, marg_err_col=ec,
@@ -174,11 +204,14 @@ def main(argv=None):
     ap.add_argument("names", nargs="+", help="workload names (workloads.WORKLOADS)")
     ap.add_argument("--workers", type=int, default=max(1, (os.cpu_count() or 2) - 1))
     ap.add_argument("--scratch", default=os.path.join(ROOT, ".golden_scratch"))
+    ap.add_argument("--resume", action="store_true",
+                    help="reuse the scratch folder of an interrupted run")
     args = ap.parse_args(argv)
     for name in args.names:
         if name not in workloads.WORKLOADS:
             raise SystemExit(f"unknown workload {name}")
-        make_one(name, args.workers, args.scratch, log=lambda s: print(s, flush=True))
+        make_one(name, args.workers, args.scratch, log=lambda s: print(s, flush=True),
+                 resume=args.resume)
 
 
 if __name__ == "__main__":

@@ -41,6 +41,34 @@ def test_sliced_solve_equals_dense_oracle(tmp_path, n, m, d, iters, workers, mon
     assert not os.path.exists(tmp_path / "scratch")
 
 
+def test_resumed_run_equals_dense_oracle(tmp_path, monkeypatch):
+    """An interrupted run resumed from its scratch folder (cached cost, a
+    checkpoint of (f, g) after 10 of 20 iterations) ends where the dense
+    iteration does, bitwise; a cost file of another workload is recomputed."""
+    n, m, d, eps, iters = 90, 70, 6, 0.08, 20
+    data = workloads.make("c3_d16_f32", n=n, m=m, d=d)
+    monkeypatch.setattr(make_fullsize, "BLOCK_ELEMS", 1000)
+    X, Y = data["X"].astype(np.float64), data["Y"].astype(np.float64)
+    a, b = data["a"].astype(np.float64), data["b"].astype(np.float64)
+    C = oracle.cost_matrix(X, Y)
+    scratch = tmp_path / "scratch"
+    scratch.mkdir()
+    f10, g10 = oracle.sinkhorn(C, a, b, eps, 10)
+    np.savez(scratch / "checkpoint.npz", t=10, iters=iters, f=f10, g=g10)
+    C.tofile(scratch / "cost.f64")
+    f, g, _, _ = make_fullsize.solve_sliced(data["X"], data["Y"], data["a"], data["b"], eps,
+                                           iters, 2, str(scratch), resume=True)
+    f_ref, g_ref = oracle.sinkhorn(C, a, b, eps, iters)
+    assert np.array_equal(f, f_ref) and np.array_equal(g, g_ref)
+    # a cost file that is not this workload's is not trusted
+    scratch.mkdir()
+    np.savez(scratch / "checkpoint.npz", t=10, iters=iters, f=f10, g=g10)
+    (C + 1.0).tofile(scratch / "cost.f64")
+    f, g, _, _ = make_fullsize.solve_sliced(data["X"], data["Y"], data["a"], data["b"], eps,
+                                           iters, 2, str(scratch), resume=True)
+    assert np.array_equal(f, f_ref) and np.array_equal(g, g_ref)
+
+
 def test_stored_references_describe_their_workloads():
     gold = os.path.join(HERE, "golden", "fullsize")
     names = sorted(fn[:-4] for fn in os.listdir(gold) if fn.endswith(".npz")) if os.path.isdir(gold) else []
