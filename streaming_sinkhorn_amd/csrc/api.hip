@@ -117,14 +117,17 @@ KConf kernel_conf(int64_t d, int bf16, int f32_mode, bool for_apply) {
 }
 
 // Column splits: enough workgroups to fill 256 CUs several times over
-// (`target` workgroups), at least ~4 column units (tiles, or blocks of the
-// wide pass) per split, a multiple of 8 when large (XCD locality).
-void choose_splits(PassShape& s, int cunits, int forced, int max_splits, int target) {
+// (`target` workgroups, and at least `min_splits` splits), at least ~4
+// column units (tiles, or blocks of the wide pass) per split, a multiple of 8
+// when large (XCD locality).
+void choose_splits(PassShape& s, int cunits, int forced, int max_splits, int target,
+                   int min_splits) {
   int S;
   if (forced > 0) {
     S = forced;
   } else {
     S = ceil_div(target, s.nrowgroups);
+    if (S < min_splits) S = min_splits;
     const int most = cunits / 4 > 1 ? cunits / 4 : 1;
     if (S > most) S = most;
     if (S >= 8) S = (S + 7) / 8 * 8;
@@ -137,7 +140,7 @@ void choose_splits(PassShape& s, int cunits, int forced, int max_splits, int tar
 }
 
 PassShape make_pass(int rtiles, int ctiles, const KConf& k, int ri, int forced, int max_splits,
-                    int target) {
+                    int target, int min_splits) {
   PassShape s{};
   s.rtiles = rtiles;
   s.ctiles = ctiles;
@@ -150,7 +153,7 @@ PassShape make_pass(int rtiles, int ctiles, const KConf& k, int ri, int forced, 
   s.bk = k.bk;
   s.nrowgroups = ceil_div(rtiles, (int64_t)kWaves * ri);
   const int cunits = (k.xres || k.ct == 0) ? ctiles : ceil_div(ctiles, k.ct);
-  choose_splits(s, cunits, forced, max_splits, target);
+  choose_splits(s, cunits, forced, max_splits, target, min_splits);
   return s;
 }
 
@@ -251,8 +254,9 @@ SolveWs solve_layout(const ot_problem* p, int splits_f, int splits_g) {
   w.npad = w.ntiles * kTile;
   w.mpad = w.mtiles * kTile;
   const int target = w.k.xres ? kTargetWorkgroupsResident : kTargetWorkgroups;
-  w.F = make_pass(w.ntiles, w.mtiles, w.k, w.k.ri, splits_f, 4096, target);
-  w.G = make_pass(w.mtiles, w.ntiles, w.k, w.k.ri, splits_g, 4096, target);
+  const int min_splits = w.k.xres ? 1 : kMinSplitsWide;
+  w.F = make_pass(w.ntiles, w.mtiles, w.k, w.k.ri, splits_f, 4096, target, min_splits);
+  w.G = make_pass(w.mtiles, w.ntiles, w.k, w.k.ri, splits_g, 4096, target, min_splits);
   // Small problems run each half-step as one launch (unless a split count is
   // forced); the split shapes stay valid for the symmetric schedule.
   w.F.solo = splits_f == 0 && solo_fits(w.F, w.k.mode);

@@ -52,8 +52,14 @@ KConf kernel_conf(int64_t d, int bf16, int f32_mode, bool for_apply = false);
 // transport-vector passes with about 2048.
 constexpr int kTargetWorkgroups = 2048;
 constexpr int kTargetWorkgroupsResident = 1024;
+// The solve's wide passes take at least 8 column splits: at n = 200000,
+// m = 10000, d = 1024 (782 row groups, 79 column blocks) the 2048 target
+// alone gives 3, and 8 splits ran 19.5-19.6 ms per iteration against
+// 20.5-20.6 ms (12 and 16 splits: 19.3-19.4 ms). The floor only changes
+// passes of more than 256 row groups (over 65536 rows).
+constexpr int kMinSplitsWide = 8;
 PassShape make_pass(int rtiles, int ctiles, const KConf& k, int ri, int forced, int max_splits,
-                    int target = kTargetWorkgroups);
+                    int target = kTargetWorkgroups, int min_splits = 1);
 // Non-resident transport passes stream whole blocks of kApplyWideCT column
 // tiles: the tiles per split are rounded up to a multiple of it (the split
 // count shrinks accordingly).
