@@ -423,7 +423,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="c2")
     ap.add_argument("--iters", type=int, default=None)
-    ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--splits", type=int, default=0,
+                    help="column splits of both half-steps (0: the library's choice)")
+    ap.add_argument("--splits-f", type=int, default=None, help="column splits of the f half-step")
+    ap.add_argument("--splits-g", type=int, default=None, help="column splits of the g half-step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB")
     ap.add_argument("--gemm-probe", action="store_true")
@@ -478,6 +481,8 @@ def main():
     cpu = None if args.no_cpu_baseline else cpu_baseline(data)
     ssa.lib()
     T = args.iters or w.iters
+    sf = args.splits if args.splits_f is None else args.splits_f
+    sg = args.splits if args.splits_g is None else args.splits_g
     dev = "cuda:0"
     torch.cuda.set_device(0)
 
@@ -508,7 +513,7 @@ def main():
     def step(record, timing=True):
         ssa.ot_sqnorms(X, xs)
         ssa.ot_sqnorms(Y, ys)
-        info = ssa.ot_solve(prob, f, g, T, splits_f=args.splits, splits_g=args.splits,
+        info = ssa.ot_solve(prob, f, g, T, splits_f=sf, splits_g=sg,
                             timing=timing, ws=ws.get("solve"), schedule=args.schedule)
         if w.grad:
             ssa.ot_apply_plan(prob, f, g, flags=ssa.OT_GRAD, out=out_grad, marg=r, ws=ws.get("grad"))
@@ -522,7 +527,7 @@ def main():
 
     with torch.cuda.stream(stream):
         # Workspaces sized and allocated once, outside the timed region.
-        ws["solve"] = ssa.solve_workspace(prob, T, splits_f=args.splits, splits_g=args.splits)
+        ws["solve"] = ssa.solve_workspace(prob, T, splits_f=sf, splits_g=sg)
         if w.grad:
             ws["grad"] = ssa.apply_workspace(prob, flags=ssa.OT_GRAD)
         if w.v_cols:
@@ -610,7 +615,7 @@ def main():
         if pairs <= 4.0e8:
             out["iteration_graph_us"] = iteration_latency(
                 ssa, prob, f, g, ws["solve"], stream,
-                dict(splits_f=args.splits, splits_g=args.splits, schedule=args.schedule))
+                dict(splits_f=sf, splits_g=sg, schedule=args.schedule))
     if cpu is not None:
         out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)

@@ -54,9 +54,9 @@ constexpr int kTargetWorkgroups = 2048;
 constexpr int kTargetWorkgroupsResident = 1024;
 // The solve's wide passes take at least 8 column splits: at n = 200000,
 // m = 10000, d = 1024 (782 row groups, 79 column blocks) the 2048 target
-// alone gives 3, and 8 splits ran 19.5-19.6 ms per iteration against
-// 20.5-20.6 ms (12 and 16 splits: 19.3-19.4 ms). The floor only changes
-// passes of more than 256 row groups (over 65536 rows).
+// alone gives 3, and a log-sum-exp launch averaged 9.80-9.85 ms with 8
+// against 10.37-10.40 ms with 3 (9.73-9.75 ms with 16). The floor only
+// changes passes of more than 256 row groups (over 65536 rows).
 constexpr int kMinSplitsWide = 8;
 PassShape make_pass(int rtiles, int ctiles, const KConf& k, int ri, int forced, int max_splits,
                     int target = kTargetWorkgroups, int min_splits = 1);
