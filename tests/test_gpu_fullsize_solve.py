@@ -29,7 +29,8 @@ graph replay) and compares:
   ``test_gpu_fullsize.py``).
 
 A workload whose reference file has not been generated is skipped with that
-reason (the 70000-point workload needs a 39 GB cost matrix in host memory).
+reason (the 70000-point workload's takes about three hours of host CPU and a
+39 GB file-backed cost to regenerate).
 """
 
 import os
