@@ -8,7 +8,9 @@ What it computes is ``oracle.sinkhorn(C, a, b, eps, T)`` from zero potentials
 for the workload's own seeded inputs ("FlashSinkhorn: IO-Aware Entropic
 Optimal Transport on GPU", §3.1 alternating updates, §4.1 / App. H.2 fixed
 iteration count from f = g = 0), followed by the L1 marginal errors of the
-final coupling (§2.2, App. E.1). The page compares its fp32 results with an
+final coupling (§2.2, App. E.1); with ``--schedule symmetric``,
+``oracle.sinkhorn_symmetric`` (§3.1 symmetric updates, both half-steps from
+the previous iterate, then averaged) into ``<name>_symmetric.npz``. The page compares its fp32 results with an
 fp64 dense reference at benchmark sizes (§4.1 "Low-eps regime", Table 20);
 this is that reference for the five workloads.
 
@@ -30,6 +32,7 @@ processes:
 equals the dense ``oracle.sinkhorn`` bitwise.
 
 Usage: python tests/golden/make_fullsize.py c2 c5 ... [--workers K] [--scratch DIR] [--resume]
+       [--schedule symmetric]
 Each workload writes ``tests/golden/fullsize/<name>.npz`` (f, g as float64 and
 the marginal errors). The scratch folder holds the cached cost (up to 39 GB
 for the 70000-point workload) and a checkpoint of (f, g) every 10
@@ -84,6 +87,20 @@ def _g_task(c):
     return 0
 
 
+# Symmetric schedule: both half-steps read the previous iterate (into FT, GT),
+# then each potential is averaged with its half-step in the parent process.
+def _ft_task(r):
+    r0, r1 = r
+    _S["FT"][r0:r1] = oracle.update_f(_S["C"][r0:r1], _S["G"], _S["b"], _S["eps"])
+    return 0
+
+
+def _gt_task(c):
+    c0, c1 = c
+    _S["GT"][c0:c1] = oracle.update_g(_S["C"][:, c0:c1], _S["F"], _S["a"], _S["eps"])
+    return 0
+
+
 def _r_task(r):
     r0, r1 = r
     P = oracle.plan(_S["C"][r0:r1], _S["a"][r0:r1], _S["b"], _S["F"][r0:r1], _S["G"], _S["eps"])
@@ -114,8 +131,10 @@ def _cached_cost_valid(C, X, Y, rows):
     return all(np.array_equal(C[r0:r1], oracle.cost_matrix(X[r0:r1], Y)) for r0, r1 in picks)
 
 
-def solve_sliced(X, Y, a, b, eps, iters, workers, scratch, log=print, resume=False):
-    """``oracle.sinkhorn`` from zero potentials, evaluated on row / column slices.
+def solve_sliced(X, Y, a, b, eps, iters, workers, scratch, log=print, resume=False,
+                 schedule="alternating"):
+    """``oracle.sinkhorn`` from zero potentials, evaluated on row / column slices
+    (``oracle.sinkhorn_symmetric`` with ``schedule="symmetric"``).
 
     Returns (f, g, err_row, err_col) with the L1 marginal errors of the final
     coupling. X, Y, a, b are the exact values the GPU receives (float32 or
@@ -142,6 +161,11 @@ def solve_sliced(X, Y, a, b, eps, iters, workers, scratch, log=print, resume=Fal
     G = np.memmap(os.path.join(scratch, "g.f64"), dtype=np.float64, mode="w+", shape=(m,))
     F[:] = 0.0
     G[:] = 0.0
+    sym = schedule == "symmetric"
+    if sym:
+        FT = np.memmap(os.path.join(scratch, "ft.f64"), dtype=np.float64, mode="w+", shape=(n,))
+        GT = np.memmap(os.path.join(scratch, "gt.f64"), dtype=np.float64, mode="w+", shape=(m,))
+        _S.update(FT=FT, GT=GT)
     start = 0
     if reuse and os.path.exists(ckpt):
         with np.load(ckpt) as z:
@@ -160,10 +184,18 @@ def solve_sliced(X, Y, a, b, eps, iters, workers, scratch, log=print, resume=Fal
                 pass
             log(f"  cost {n}x{m}: {time.perf_counter() - t0:.1f} s")
         for t in range(start, int(iters)):
-            for _ in pool.imap_unordered(_f_task, rows):
-                pass
-            for _ in pool.imap_unordered(_g_task, cols):
-                pass
+            if sym:
+                for _ in pool.imap_unordered(_ft_task, rows):
+                    pass
+                for _ in pool.imap_unordered(_gt_task, cols):
+                    pass
+                F[:] = 0.5 * (np.asarray(F) + np.asarray(FT))
+                G[:] = 0.5 * (np.asarray(G) + np.asarray(GT))
+            else:
+                for _ in pool.imap_unordered(_f_task, rows):
+                    pass
+                for _ in pool.imap_unordered(_g_task, cols):
+                    pass
             if t % 10 == 9 or t == iters - 1:
                 log(f"  iteration {t + 1}/{iters}: {time.perf_counter() - t0:.1f} s")
                 tmp = ckpt + ".tmp.npz"
@@ -179,22 +211,27 @@ def solve_sliced(X, Y, a, b, eps, iters, workers, scratch, log=print, resume=Fal
     g = np.array(G)
     _S.clear()
     del C, F, G
+    if sym:
+        del FT, GT
     shutil.rmtree(scratch, ignore_errors=True)
     return f, g, float(np.abs(r - a).sum()), float(np.abs(c - b).sum())
 
 
-def make_one(name, workers, scratch, log=print, resume=False):
+def make_one(name, workers, scratch, log=print, resume=False, schedule="alternating"):
     data = workloads.make(name)
     w = data["w"]
-    log(f"{name}: n={w.n} m={w.m} d={w.d} {w.dtype} eps={w.eps} T={w.iters}, {workers} workers")
+    tag = name if schedule == "alternating" else f"{name}_{schedule}"
+    log(f"{tag}: n={w.n} m={w.m} d={w.d} {w.dtype} eps={w.eps} T={w.iters}, {workers} workers")
     t0 = time.perf_counter()
     f, g, er, ec = solve_sliced(data["X"], data["Y"], data["a"], data["b"], w.eps, w.iters,
-                                workers, os.path.join(scratch, name), log=log, resume=resume)
+                                workers, os.path.join(scratch, tag), log=log, resume=resume,
+                                schedule=schedule)
     os.makedirs(OUT_DIR, exist_ok=True)
-    path = os.path.join(OUT_DIR, f"{name}.npz")
+    path = os.path.join(OUT_DIR, f"{tag}.npz")
     np.savez_compressed(path, f=f, g=g, marg_err_row=er, marg_err_col=ec,
-                        n=w.n, m=w.m, d=w.d, eps=w.eps, iters=w.iters, dtype=w.dtype)
-    log(f"{name}: wrote {path} in {time.perf_counter() - t0:.0f} s; "
+                        n=w.n, m=w.m, d=w.d, eps=w.eps, iters=w.iters, dtype=w.dtype,
+                        schedule=schedule)
+    log(f"{tag}: wrote {path} in {time.perf_counter() - t0:.0f} s; "
         f"marginal errors row {er:.3e} col {ec:.3e}")
     return path
 
@@ -206,12 +243,14 @@ def main(argv=None):
     ap.add_argument("--scratch", default=os.path.join(ROOT, ".golden_scratch"))
     ap.add_argument("--resume", action="store_true",
                     help="reuse the scratch folder of an interrupted run")
+    ap.add_argument("--schedule", default="alternating", choices=["alternating", "symmetric"],
+                    help="symmetric: writes <name>_symmetric.npz")
     args = ap.parse_args(argv)
     for name in args.names:
         if name not in workloads.WORKLOADS:
             raise SystemExit(f"unknown workload {name}")
         make_one(name, args.workers, args.scratch, log=lambda s: print(s, flush=True),
-                 resume=args.resume)
+                 resume=args.resume, schedule=args.schedule)
 
 
 if __name__ == "__main__":

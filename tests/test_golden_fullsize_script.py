@@ -41,6 +41,24 @@ def test_sliced_solve_equals_dense_oracle(tmp_path, n, m, d, iters, workers, mon
     assert not os.path.exists(tmp_path / "scratch")
 
 
+def test_sliced_symmetric_solve_equals_dense_oracle(tmp_path, monkeypatch):
+    """The symmetric schedule (both half-steps from the previous iterate, then
+    averaged) sliced over workers equals ``oracle.sinkhorn_symmetric`` bitwise."""
+    n, m, d, eps, iters = 110, 85, 7, 0.09, 6
+    data = workloads.make("c3_d16_f32", n=n, m=m, d=d)
+    monkeypatch.setattr(make_fullsize, "BLOCK_ELEMS", 1000)
+    f, g, er, ec = make_fullsize.solve_sliced(data["X"], data["Y"], data["a"], data["b"], eps,
+                                             iters, 3, str(tmp_path / "scratch"),
+                                             schedule="symmetric")
+    X, Y = data["X"].astype(np.float64), data["Y"].astype(np.float64)
+    a, b = data["a"].astype(np.float64), data["b"].astype(np.float64)
+    C = oracle.cost_matrix(X, Y)
+    f_ref, g_ref = oracle.sinkhorn_symmetric(C, a, b, eps, iters)
+    assert np.array_equal(f, f_ref) and np.array_equal(g, g_ref)
+    er_ref, ec_ref = oracle.marginal_errors(oracle.plan(C, a, b, f_ref, g_ref, eps), a, b)
+    assert er == pytest.approx(er_ref, rel=1e-12) and ec == pytest.approx(ec_ref, rel=1e-12)
+
+
 def test_resumed_run_equals_dense_oracle(tmp_path, monkeypatch):
     """An interrupted run resumed from its scratch folder (cached cost, a
     checkpoint of (f, g) after 10 of 20 iterations) ends where the dense
@@ -75,10 +93,14 @@ def test_stored_references_describe_their_workloads():
     assert "c2" in names, "the headline workload's reference potentials are committed"
     for name in names:
         z = np.load(os.path.join(gold, f"{name}.npz"))
-        w = workloads.WORKLOADS[name]
+        sym = name.endswith("_symmetric")
+        w = workloads.WORKLOADS[name[:-len("_symmetric")] if sym else name]
+        assert str(z["schedule"]) == ("symmetric" if sym else "alternating") if "schedule" in z \
+            else not sym
         assert (int(z["n"]), int(z["m"]), int(z["d"]), int(z["iters"])) == (w.n, w.m, w.d, w.iters)
         assert float(z["eps"]) == w.eps and str(z["dtype"]) == w.dtype
         assert z["f"].shape == (w.n,) and z["g"].shape == (w.m,)
         assert np.all(np.isfinite(z["f"])) and np.all(np.isfinite(z["g"]))
-        # after a g half-step the column marginal is met to fp64 rounding
-        assert float(z["marg_err_col"]) < 1e-9
+        if not sym:
+            # after a g half-step the column marginal is met to fp64 rounding
+            assert float(z["marg_err_col"]) < 1e-9

@@ -66,11 +66,13 @@ def _to_dev(arr, dtype):
     return t.to(torch.bfloat16) if dtype == "bf16" else t
 
 
-def _golden(name):
-    path = os.path.join(GOLDEN, f"{name}.npz")
+def _golden(name, schedule="alternating"):
+    tag = name if schedule == "alternating" else f"{name}_{schedule}"
+    path = os.path.join(GOLDEN, f"{tag}.npz")
     if not os.path.exists(path):
+        extra = "" if schedule == "alternating" else f" --schedule {schedule}"
         pytest.skip(f"reference potentials {path} not generated "
-                    f"(python tests/golden/make_fullsize.py {name})")
+                    f"(python tests/golden/make_fullsize.py {name}{extra})")
     return np.load(path)
 
 
@@ -149,3 +151,41 @@ def test_full_size_solve_matches_oracle(name):
         cerr = np.abs(host64(c)[cols] - Pcol.sum(axis=0)).max() / Pcol.sum(axis=0).max()
         say(f"  P^T U cols rel err {err:.3e}, c {cerr:.3e} (gate {ptol:g})")
         assert err <= ptol and cerr <= ptol
+
+
+# The symmetric schedule (both half-steps from the previous iterate, then
+# averaged; §3.1 "symmetric updates"), against oracle.sinkhorn_symmetric at
+# full shape. Neither marginal is fit exactly by its last update, so both
+# reported errors are gated against the oracle's.
+SYM_NAMES = ["c1", "c2"]
+
+
+@pytest.mark.parametrize("name", SYM_NAMES)
+def test_full_size_symmetric_solve_matches_oracle(name):
+    ref = _golden(name, "symmetric")
+    data = workloads.make(name)
+    w = data["w"]
+    assert (int(ref["n"]), int(ref["m"]), int(ref["d"]), int(ref["iters"])) == (w.n, w.m, w.d, w.iters)
+    assert str(ref["schedule"]) == "symmetric"
+    say(f"full-size symmetric solve {name}: n={w.n} m={w.m} d={w.d} {w.dtype} eps={w.eps} T={w.iters}")
+    prob = ssa.problem(_to_dev(data["X"], w.dtype), _to_dev(data["Y"], w.dtype), w.eps,
+                       torch.from_numpy(data["a"]).to(DEV), torch.from_numpy(data["b"]).to(DEV))
+    f, g = zeros(w.n), zeros(w.m)
+    info = ssa.ot_solve(prob, f, g, w.iters, schedule="symmetric")
+    torch.cuda.synchronize()
+    assert not info["nonfinite"] and info["iters_done"] == w.iters
+    df = host64(f) - ref["f"]
+    dg = host64(g) - ref["g"]
+    kappa = 0.5 * (df.mean() - dg.mean())
+    rest = max(np.abs(df - kappa).max(), np.abs(dg + kappa).max())
+    tol = POT_TOL[w.dtype]
+    say(f"  max|df|={np.abs(df).max():.3e} max|dg|={np.abs(dg).max():.3e} (gate {tol:g}); "
+        f"constant mode {kappa:.3e}, rest {rest:.3e}")
+    assert np.abs(df).max() <= tol and np.abs(dg).max() <= tol
+    for side, pot in (("row", ref["f"]), ("col", ref["g"])):
+        e_ref = float(ref[f"marg_err_{side}"])
+        e_gpu = info[f"marg_err_{side}"]
+        floor = 8.0 * np.spacing(np.float32(np.abs(pot).max())) / w.eps
+        say(f"  marg err {side}: GPU {e_gpu:.3e}, oracle {e_ref:.3e} (gate 1e-2 rel + {floor:.2e})")
+        assert abs(e_gpu - e_ref) <= 1e-2 * e_ref + floor
+
