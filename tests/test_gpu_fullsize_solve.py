@@ -189,3 +189,28 @@ def test_full_size_symmetric_solve_matches_oracle(name):
         say(f"  marg err {side}: GPU {e_gpu:.3e}, oracle {e_ref:.3e} (gate 1e-2 rel + {floor:.2e})")
         assert abs(e_gpu - e_ref) <= 1e-2 * e_ref + floor
 
+
+# The other fp32 operand modes against the same stored potentials: three bf16
+# parts (six products) and the fp32 matrix instruction form the same scores.
+@pytest.mark.parametrize("mode", ["split_bf16", "native"])
+@pytest.mark.parametrize("name", ["c2", "c3_d128_f32"])
+def test_full_size_solve_other_fp32_modes(name, mode):
+    ref = _golden(name)
+    data = workloads.make(name)
+    w = data["w"]
+    say(f"full-size solve {name} mode={mode}: n={w.n} m={w.m} d={w.d} eps={w.eps} T={w.iters}")
+    prob = ssa.problem(_to_dev(data["X"], w.dtype), _to_dev(data["Y"], w.dtype), w.eps,
+                       torch.from_numpy(data["a"]).to(DEV), torch.from_numpy(data["b"]).to(DEV),
+                       native_f32=mode == "native", split_bf16=mode == "split_bf16")
+    f, g = zeros(w.n), zeros(w.m)
+    info = ssa.ot_solve(prob, f, g, w.iters)
+    torch.cuda.synchronize()
+    assert not info["nonfinite"] and info["iters_done"] == w.iters
+    df = host64(f) - ref["f"]
+    dg = host64(g) - ref["g"]
+    kappa = 0.5 * (df.mean() - dg.mean())
+    rest = max(np.abs(df - kappa).max(), np.abs(dg + kappa).max())
+    say(f"  max|df|={np.abs(df).max():.3e} max|dg|={np.abs(dg).max():.3e} (gate {POT_TOL['f32']:g}); "
+        f"constant mode {kappa:.3e}, rest {rest:.3e}")
+    assert np.abs(df).max() <= POT_TOL["f32"] and np.abs(dg).max() <= POT_TOL["f32"]
+
