@@ -74,7 +74,7 @@ EXP_PEAK_PER_S = 256 * 4 * 8 * 2.4e9
 # FETCH_SIZE / WRITE_SIZE runs (scaled by the copy-kernel calibration), valid
 # only for the kernel source they were taken on.
 TRAFFIC = {
-    "c2": {"kernels_sha256": "dd5737e67627a0ae4f96b9dc64cb80305379398140e06dd5f7a77b55d2aefd60",
+    "c2": {"kernels_sha256": "8926fdd03eec55c0dffccb62985e1fa693923b4386f689ad302bc020c3d180aa",
            "splits": 16,
            "bytes_per_launch": 34082816,
            "source": "profiles/lse_pipe_kernel_c2_n20000_d64_f32half2_hbm_traffic.md"},

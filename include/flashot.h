@@ -168,7 +168,9 @@ typedef struct ot_solve_opts {
                            the half-steps of small problems, at most 3072 points a side,
                            as one launch each in the alternating schedule) */
   int32_t splits_g;     /* column splits of the g half-step (0 = automatic) */
-  int32_t timing;       /* 1: time every log-sum-exp kernel with HIP events (needs info) */
+  int32_t timing;       /* 1: time every log-sum-exp kernel with HIP events that its
+                           dispatch records (needs info; the iterations then run as
+                           plain launches) */
   int32_t schedule;     /* OT_SCHED_ALTERNATING (0) or OT_SCHED_SYMMETRIC */
   float eps_start;      /* eps-scaling: 0 = off; > eps: iteration k runs at
                            max(eps, eps_start * eps_decay^k) */

@@ -439,18 +439,17 @@ RowFinish finish_g(const Ctx& x, int with_err, int write, int avg) {
 
 // f half-step: LSE over columns y with bias by, ending in f (and, when
 // written, the g side's bias bx); as one launch for small problems, else the
-// split pass and the merge of its partials. ev, if given, receives two
-// events around the log-sum-exp launch.
+// split pass and the merge of its partials. ev, if given, holds two events
+// that the log-sum-exp dispatch records at its start and end.
 int half_f(const Ctx& x, hipStream_t st, int with_err, int write, hipEvent_t* ev = nullptr) {
   const RowFinish fin = finish_f(x, with_err, write, 0);
-  if (ev) OT_HIP(hipEventRecord(ev[0], st));
+  const LaunchTimer tm{ev ? ev[0] : nullptr, ev ? ev[1] : nullptr};
+  const LaunchTimer* t = ev ? &tm : nullptr;
   if (x.L.F.solo) {
-    OT_HIP(launch_lse_solo(x.L.F, x.L.k.mode, x.xp, x.yp, x.by, x.kc, fin, x.errp, st));
-    if (ev) OT_HIP(hipEventRecord(ev[1], st));
+    OT_HIP(launch_lse_solo(x.L.F, x.L.k.mode, x.xp, x.yp, x.by, x.kc, fin, x.errp, st, t));
     return OT_OK;
   }
-  OT_HIP(launch_lse_partial(x.L.F, x.L.k.mode, x.xp, x.yp, x.by, x.kc, x.part, st));
-  if (ev) OT_HIP(hipEventRecord(ev[1], st));
+  OT_HIP(launch_lse_partial(x.L.F, x.L.k.mode, x.xp, x.yp, x.by, x.kc, x.part, st, t));
   OT_HIP(launch_lse_merge(x.part, x.L.F.splits, x.L.npad, (int)x.p->n, x.bscale, x.eps, x.nx, x.hx, x.wx,
                           x.f, x.bx, x.errp, with_err, write, 0, st));
   return OT_OK;
@@ -459,14 +458,13 @@ int half_f(const Ctx& x, hipStream_t st, int with_err, int write, hipEvent_t* ev
 int half_g(const Ctx& x, hipStream_t st, int with_err, int write, hipEvent_t* ev = nullptr) {
   const RowFinish fin = finish_g(x, with_err, write, 0);
   float* errp = x.errp + x.L.errblocks_f;
-  if (ev) OT_HIP(hipEventRecord(ev[0], st));
+  const LaunchTimer tm{ev ? ev[0] : nullptr, ev ? ev[1] : nullptr};
+  const LaunchTimer* t = ev ? &tm : nullptr;
   if (x.L.G.solo) {
-    OT_HIP(launch_lse_solo(x.L.G, x.L.k.mode, x.yp, x.xp, x.bx, x.kc, fin, errp, st));
-    if (ev) OT_HIP(hipEventRecord(ev[1], st));
+    OT_HIP(launch_lse_solo(x.L.G, x.L.k.mode, x.yp, x.xp, x.bx, x.kc, fin, errp, st, t));
     return OT_OK;
   }
-  OT_HIP(launch_lse_partial(x.L.G, x.L.k.mode, x.yp, x.xp, x.bx, x.kc, x.part, st));
-  if (ev) OT_HIP(hipEventRecord(ev[1], st));
+  OT_HIP(launch_lse_partial(x.L.G, x.L.k.mode, x.yp, x.xp, x.bx, x.kc, x.part, st, t));
   OT_HIP(launch_lse_merge(x.part, x.L.G.splits, x.L.mpad, (int)x.p->m, x.bscale, x.eps, x.ny, x.hy, x.wy,
                           x.g, x.by, errp, with_err, write, 0, st));
   return OT_OK;
@@ -476,20 +474,20 @@ int half_g(const Ctx& x, hipStream_t st, int with_err, int write, hipEvent_t* ev
 // half-step (new f and its bias), then the g half-step from the new f.
 // Symmetric schedule (§3.1 eq. 4-5): both passes read the previous biases,
 // so both split passes run before either merge; the merges average old and
-// new values. ev, if given, receives four events around the two log-sum-exp
-// launches.
+// new values. ev, if given, holds four events: the start and end of each of
+// the two log-sum-exp dispatches, recorded by the dispatches themselves.
 int enqueue_iteration(const Ctx& x, hipStream_t st, int with_err, hipEvent_t* ev) {
   if (!x.sym) {
     const int rc = half_f(x, st, with_err, 1, ev);
     if (rc) return rc;
     return half_g(x, st, 0, 1, ev ? ev + 2 : nullptr);
   }
-  if (ev) OT_HIP(hipEventRecord(ev[0], st));
-  OT_HIP(launch_lse_partial(x.L.F, x.L.k.mode, x.xp, x.yp, x.by, x.kc, x.part, st));
-  if (ev) OT_HIP(hipEventRecord(ev[1], st));
-  if (ev) OT_HIP(hipEventRecord(ev[2], st));
-  OT_HIP(launch_lse_partial(x.L.G, x.L.k.mode, x.yp, x.xp, x.bx, x.kc, x.part2, st));
-  if (ev) OT_HIP(hipEventRecord(ev[3], st));
+  const LaunchTimer tf{ev ? ev[0] : nullptr, ev ? ev[1] : nullptr};
+  const LaunchTimer tg{ev ? ev[2] : nullptr, ev ? ev[3] : nullptr};
+  OT_HIP(launch_lse_partial(x.L.F, x.L.k.mode, x.xp, x.yp, x.by, x.kc, x.part, st,
+                            ev ? &tf : nullptr));
+  OT_HIP(launch_lse_partial(x.L.G, x.L.k.mode, x.yp, x.xp, x.bx, x.kc, x.part2, st,
+                            ev ? &tg : nullptr));
   OT_HIP(launch_lse_merge(x.part, x.L.F.splits, x.L.npad, (int)x.p->n, x.bscale, x.eps, x.nx, x.hx,
                           x.wx, x.f, x.bx, x.errp, with_err, 1, 1, st));
   OT_HIP(launch_lse_merge(x.part2, x.L.G.splits, x.L.mpad, (int)x.p->m, x.bscale, x.eps, x.ny, x.hy, x.wy,

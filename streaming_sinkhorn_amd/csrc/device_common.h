@@ -2,6 +2,7 @@
 // (score tiles on the matrix cores, online log-sum-exp steps). Internal.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -18,6 +19,17 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Launches `kernel` on `st`; with a timer the dispatch itself records the
+// start and end events (no event commands of their own between launches).
+template <typename... F, typename... A>
+static void launch_timed(void (*kernel)(F...), dim3 grid, dim3 block, hipStream_t st,
+                         const LaunchTimer* timer, A... args) {
+  if (timer)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, st, timer->start, timer->stop, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
+}
 
 // One packed k-block of the score tile: acc[j][i] += sum_k A[j][k] B[k][i].
 template <bool BF16>

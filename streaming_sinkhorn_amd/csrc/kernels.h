@@ -216,8 +216,16 @@ hipError_t launch_bias_from_pot(const float* pot, const float* norm, const float
 // mode: 0 fp32 operands, 1 bf16 operands, 2 fp32 operands packed as three bf16 parts,
 // 3 fp32 operands packed as two fp16 parts.
 // Register-resident passes (s.xres, kernels.hip) and k-chunked wide passes (kernels_wide.hip).
+// Per-launch timing: when a LaunchTimer is given, the kernel is launched with
+// hipExtLaunchKernelGGL, whose dispatch records its own start and end into
+// the two events, so no separate event commands sit between launches.
+struct LaunchTimer {
+  hipEvent_t start;
+  hipEvent_t stop;
+};
 hipError_t launch_lse_resident(const PassShape& s, int mode, const void* Rp, const void* Cp,
-                               const float* cbias, float c, float2* part, hipStream_t st);
+                               const float* cbias, float c, float2* part, hipStream_t st,
+                               const LaunchTimer* timer = nullptr);
 // Transport-vector pass (P v, one value column) on the register-resident
 // layouts: (M, S) partials as launch_lse_resident plus T = sum exp2(score -
 // M) v per split and row in partT. vcol: the column side's values, padded
@@ -226,7 +234,8 @@ hipError_t launch_vec_resident(const PassShape& s, int mode, const void* Rp, con
                                const float* cbias, const float* vcol, float c, float2* part,
                                float* partT, hipStream_t st);
 hipError_t launch_lse_wide(const PassShape& s, int mode, const void* Rp, const void* Cp,
-                           const float* cbias, float c, float2* part, hipStream_t st);
+                           const float* cbias, float c, float2* part, hipStream_t st,
+                           const LaunchTimer* timer = nullptr);
 // Single-launch half-step of a small problem (s.solo; modes 1 and 3, row
 // operand resident, per-wave column loads): one workgroup of kSoloWaves
 // waves per 32-row tile, the waves splitting the column tiles; the waves' partials
@@ -237,13 +246,14 @@ hipError_t launch_lse_wide(const PassShape& s, int mode, const void* Rp, const v
 // must read the biases this one overwrites.
 hipError_t launch_lse_solo(const PassShape& s, int mode, const void* Rp, const void* Cp,
                            const float* cbias, float c, const RowFinish& fin, float* err_part,
-                           hipStream_t st);
+                           hipStream_t st, const LaunchTimer* timer = nullptr);
 // Whether launch_lse_solo serves this shape and mode.
 bool lse_solo_supported(const PassShape& s, int mode);
 inline hipError_t launch_lse_partial(const PassShape& s, int mode, const void* Rp, const void* Cp,
-                                     const float* cbias, float c, float2* part, hipStream_t st) {
-  return s.xres ? launch_lse_resident(s, mode, Rp, Cp, cbias, c, part, st)
-                : launch_lse_wide(s, mode, Rp, Cp, cbias, c, part, st);
+                                     const float* cbias, float c, float2* part, hipStream_t st,
+                                     const LaunchTimer* timer = nullptr) {
+  return s.xres ? launch_lse_resident(s, mode, Rp, Cp, cbias, c, part, st, timer)
+                : launch_lse_wide(s, mode, Rp, Cp, cbias, c, part, st, timer);
 }
 // avg = 1: symmetric schedule, the new potential is the average of the old
 // one and the half-step value. With write_pot, bias_out receives the biases

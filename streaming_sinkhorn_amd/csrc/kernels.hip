@@ -539,20 +539,22 @@ struct ResArgs {
   float c;
   float2* part;
   float* partT;
+  const LaunchTimer* timer;  // null: plain launch
 };
 
 template <int MODE, int KB, int RI, bool VEC>
 static void lse_pipe_go(const PassShape& s, const ResArgs& a, hipStream_t st) {
-  lse_pipe_kernel<MODE, KB, RI, VEC><<<pipe_rowgroups(s.nrowgroups, s.splits) * s.splits, 256, 0, st>>>(
-      (const u32x4*)a.Rp, (const u32x4*)a.Cp, a.cbias, a.vcol, s.rtiles, s.ctiles, s.splits,
-      s.tps, a.c, a.part, a.partT, s.rtiles * kTile);
+  launch_timed(lse_pipe_kernel<MODE, KB, RI, VEC>,
+               dim3(pipe_rowgroups(s.nrowgroups, s.splits) * s.splits), dim3(256), st, a.timer,
+               (const u32x4*)a.Rp, (const u32x4*)a.Cp, a.cbias, a.vcol, s.rtiles, s.ctiles,
+               s.splits, s.tps, a.c, a.part, a.partT, s.rtiles * kTile);
 }
 
 template <int MODE, int KB, int RI, bool VEC>
 static void lse_lds_go(const PassShape& s, const ResArgs& a, hipStream_t st) {
-  lse_lds_kernel<MODE, KB, RI, VEC><<<s.nrowgroups * s.splits, 256, 0, st>>>(
-      (const u32x4*)a.Rp, (const u32x4*)a.Cp, a.cbias, a.vcol, s.rtiles, s.ctiles, s.splits,
-      s.tps, a.c, a.part, a.partT, s.rtiles * kTile);
+  launch_timed(lse_lds_kernel<MODE, KB, RI, VEC>, dim3(s.nrowgroups * s.splits), dim3(256), st,
+               a.timer, (const u32x4*)a.Rp, (const u32x4*)a.Cp, a.cbias, a.vcol, s.rtiles,
+               s.ctiles, s.splits, s.tps, a.c, a.part, a.partT, s.rtiles * kTile);
 }
 
 template <int MODE, int KB, bool VEC>
@@ -614,11 +616,13 @@ static hipError_t lse_resident_dispatch(const PassShape& s, const ResArgs& a, hi
 
 template <int MODE, int KB>
 static void lse_solo_go(const PassShape& s, const void* Rp, const void* Cp, const float* cbias,
-                        float c, const RowFinish& fin, float* err_part, hipStream_t st) {
+                        float c, const RowFinish& fin, float* err_part, hipStream_t st,
+                        const LaunchTimer* t) {
   constexpr int W = kSoloWaves;
   const int tpw = (s.ctiles + W - 1) / W;
-  lse_solo_kernel<MODE, KB, W><<<s.rtiles, W * 64, 0, st>>>(
-      (const u32x4*)Rp, (const u32x4*)Cp, cbias, s.rtiles, s.ctiles, tpw, c, fin, err_part);
+  launch_timed(lse_solo_kernel<MODE, KB, W>, dim3(s.rtiles), dim3(W * 64), st, t,
+               (const u32x4*)Rp, (const u32x4*)Cp, cbias, s.rtiles, s.ctiles, tpw, c, fin,
+               err_part);
 }
 
 bool lse_solo_supported(const PassShape& s, int mode) {
@@ -630,22 +634,22 @@ bool lse_solo_supported(const PassShape& s, int mode) {
 
 hipError_t launch_lse_solo(const PassShape& s, int mode, const void* Rp, const void* Cp,
                            const float* cbias, float c, const RowFinish& fin, float* err_part,
-                           hipStream_t st) {
+                           hipStream_t st, const LaunchTimer* t) {
   if (!lse_solo_supported(s, mode) || fin.avg || fin.rpad != s.rtiles * kTile)
     return hipErrorInvalidValue;
   if (mode == kModeHalf2) {
     switch (s.kb) {
-      case 2: lse_solo_go<kModeHalf2, 2>(s, Rp, Cp, cbias, c, fin, err_part, st); break;
-      case 4: lse_solo_go<kModeHalf2, 4>(s, Rp, Cp, cbias, c, fin, err_part, st); break;
-      default: lse_solo_go<kModeHalf2, 8>(s, Rp, Cp, cbias, c, fin, err_part, st); break;
+      case 2: lse_solo_go<kModeHalf2, 2>(s, Rp, Cp, cbias, c, fin, err_part, st, t); break;
+      case 4: lse_solo_go<kModeHalf2, 4>(s, Rp, Cp, cbias, c, fin, err_part, st, t); break;
+      default: lse_solo_go<kModeHalf2, 8>(s, Rp, Cp, cbias, c, fin, err_part, st, t); break;
     }
   } else {
     switch (s.kb) {
-      case 1: lse_solo_go<kModeBF16, 1>(s, Rp, Cp, cbias, c, fin, err_part, st); break;
-      case 2: lse_solo_go<kModeBF16, 2>(s, Rp, Cp, cbias, c, fin, err_part, st); break;
-      case 4: lse_solo_go<kModeBF16, 4>(s, Rp, Cp, cbias, c, fin, err_part, st); break;
-      case 8: lse_solo_go<kModeBF16, 8>(s, Rp, Cp, cbias, c, fin, err_part, st); break;
-      default: lse_solo_go<kModeBF16, 16>(s, Rp, Cp, cbias, c, fin, err_part, st); break;
+      case 1: lse_solo_go<kModeBF16, 1>(s, Rp, Cp, cbias, c, fin, err_part, st, t); break;
+      case 2: lse_solo_go<kModeBF16, 2>(s, Rp, Cp, cbias, c, fin, err_part, st, t); break;
+      case 4: lse_solo_go<kModeBF16, 4>(s, Rp, Cp, cbias, c, fin, err_part, st, t); break;
+      case 8: lse_solo_go<kModeBF16, 8>(s, Rp, Cp, cbias, c, fin, err_part, st, t); break;
+      default: lse_solo_go<kModeBF16, 16>(s, Rp, Cp, cbias, c, fin, err_part, st, t); break;
     }
   }
   return hipGetLastError();
@@ -662,14 +666,17 @@ static hipError_t resident_dispatch(const PassShape& s, int mode, const ResArgs&
 }
 
 hipError_t launch_lse_resident(const PassShape& s, int mode, const void* Rp, const void* Cp,
-                               const float* cbias, float c, float2* part, hipStream_t st) {
-  return resident_dispatch<false>(s, mode, ResArgs{Rp, Cp, cbias, nullptr, c, part, nullptr}, st);
+                               const float* cbias, float c, float2* part, hipStream_t st,
+                               const LaunchTimer* t) {
+  return resident_dispatch<false>(s, mode,
+                                  ResArgs{Rp, Cp, cbias, nullptr, c, part, nullptr, t}, st);
 }
 
 hipError_t launch_vec_resident(const PassShape& s, int mode, const void* Rp, const void* Cp,
                                const float* cbias, const float* vcol, float c, float2* part,
                                float* partT, hipStream_t st) {
-  return resident_dispatch<true>(s, mode, ResArgs{Rp, Cp, cbias, vcol, c, part, partT}, st);
+  return resident_dispatch<true>(s, mode, ResArgs{Rp, Cp, cbias, vcol, c, part, partT, nullptr},
+                                 st);
 }
 
 }  // namespace flashot

@@ -311,21 +311,22 @@ __global__ __launch_bounds__(256) void lse_wide_kernel(
 
 template <int MODE, int RT, int CT, int BK>
 static void lse_wide_go(const PassShape& s, const void* Rp, const void* Cp, const float* cbias,
-                        float c, float2* part, hipStream_t st) {
+                        float c, float2* part, hipStream_t st, const LaunchTimer* t) {
   // Row groups padded to a multiple of 8 (one slice per XCD); padding
   // workgroups exit at once.
   const int grid = (s.nrowgroups + 7) / 8 * 8 * s.splits;
-  lse_wide_kernel<MODE, RT, CT, BK><<<grid, 256, 0, st>>>(
-      (const u32x4*)Rp, (const u32x4*)Cp, cbias, s.rtiles, s.ctiles, s.kbp, s.splits, s.tps,
-      s.nrowgroups, c, part, s.rtiles * kTile);
+  launch_timed(lse_wide_kernel<MODE, RT, CT, BK>, dim3(grid), dim3(256), st, t,
+               (const u32x4*)Rp, (const u32x4*)Cp, cbias, s.rtiles, s.ctiles, s.kbp, s.splits,
+               s.tps, s.nrowgroups, c, part, s.rtiles * kTile);
 }
 
 hipError_t launch_lse_wide(const PassShape& s, int mode, const void* Rp, const void* Cp,
-                           const float* cbias, float c, float2* part, hipStream_t st) {
+                           const float* cbias, float c, float2* part, hipStream_t st,
+                           const LaunchTimer* t) {
   if (s.xres) return hipErrorInvalidValue;
 #define WIDE_CASE(M, R, C, K)                                                   \
   if (mode == M && s.ri == R && s.ct == C && s.bk == K) {                      \
-    lse_wide_go<M, R, C, K>(s, Rp, Cp, cbias, c, part, st);                    \
+    lse_wide_go<M, R, C, K>(s, Rp, Cp, cbias, c, part, st, t);                 \
     return hipGetLastError();                                                   \
   }
   // Shapes measured best on gfx950 among RT in {2, 4}, CT in {2, 4},
