@@ -599,7 +599,8 @@ int run_iterations(const Ctx& x, hipStream_t st, int count, int with_err, bool u
   return OT_OK;
 }
 
-// Timed variant: plain launches with a HIP event pair around every LSE kernel.
+// Timed variant: plain launches, every LSE kernel recording a HIP event pair
+// at its start and end.
 struct EventPool {
   std::vector<hipEvent_t> ev;
   int ensure(size_t count) {

@@ -420,6 +420,31 @@ def test_deterministic_graph_eager_and_resume():
     assert torch.equal(f, outs[0][0]) and torch.equal(g, outs[0][1])
 
 
+@pytest.mark.parametrize("shape,schedule", [((300, 200), "alternating"),
+                                            ((1500, 1300), "alternating"),
+                                            ((1500, 1300), "symmetric")])
+def test_timed_solve_equals_untimed(shape, schedule):
+    """Timing every log-sum-exp dispatch (events recorded by the dispatch
+    itself) changes no output bit: the single-launch half-steps of small
+    problems, the split passes, and both passes of the symmetric schedule."""
+    n, m = shape
+    data = workloads.make("c2", n=n, m=m)
+    prob = make_problem(data)
+    T = 9
+    f0, g0 = zeros(n), zeros(m)
+    ref = ssa.ot_solve(prob, f0, g0, T, schedule=schedule)
+    f, g = zeros(n), zeros(m)
+    info = ssa.ot_solve(prob, f, g, T, schedule=schedule, timing=True)
+    torch.cuda.synchronize()
+    assert torch.equal(f, f0) and torch.equal(g, g0)
+    assert info["marg_err_row"] == ref["marg_err_row"]
+    assert info["marg_err_col"] == ref["marg_err_col"]
+    assert info["lse_launches"] == 2 * T and ref["lse_launches"] == 0
+    per = info["lse_ms"] / info["lse_launches"]
+    say(f"timed solve {n}x{m} {schedule}: {1e3 * per:.1f} us per log-sum-exp launch")
+    assert 0.0 < per < 100.0
+
+
 def test_constant_mode_drift_and_rest_of_error():
     """Potentials after 100 iterations (n = m = 2000, the 20000-point workload's
     distributions) against the fp64 oracle, split into the drift along the
