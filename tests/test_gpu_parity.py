@@ -420,6 +420,34 @@ def test_deterministic_graph_eager_and_resume():
     assert torch.equal(f, outs[0][0]) and torch.equal(g, outs[0][1])
 
 
+@pytest.mark.parametrize("schedule", ["alternating", "symmetric"])
+def test_graph_replays_match_eager_with_work_between(schedule):
+    """The cached iteration graphs, replayed by four solves in a row on one
+    workspace with eager launches of the library and of torch and host
+    synchronizations between them, give the eager result bitwise every time
+    (a replay that reused stale state from the previous one would differ)."""
+    n, m, T = 1400, 1100, 37  # two replays of the 16-iteration graph + 5 single ones
+    data = workloads.make("c2", n=n, m=m)
+    prob = make_problem(data)
+    ws = ssa.solve_workspace(prob, T)
+    fe, ge = zeros(n), zeros(m)
+    ssa.ot_solve(prob, fe, ge, T, use_graph=False, want_info=False, ws=ws, schedule=schedule)
+    torch.cuda.synchronize()
+    scratch = torch.randn(1 << 20, device=DEV)
+    for rep in range(4):
+        f, g = zeros(n), zeros(m)
+        ssa.ot_solve(prob, f, g, T, want_info=False, ws=ws, schedule=schedule)
+        torch.cuda.synchronize()
+        assert torch.equal(f, fe) and torch.equal(g, ge), rep
+        # eager work between replays: the library's own half-steps on the same
+        # workspace, a torch reduction, and a host round trip
+        f2, g2 = f.clone(), g.clone()
+        ssa.ot_update_f(prob, g2, f2, ws=ws)
+        ssa.ot_update_g(prob, f2, g2, ws=ws)
+        scratch.mul_(1.0001).sum().item()
+        torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("shape,schedule", [((300, 200), "alternating"),
                                             ((1500, 1300), "alternating"),
                                             ((1500, 1300), "symmetric")])
