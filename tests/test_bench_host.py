@@ -17,6 +17,17 @@ def test_traffic_record_only_for_its_sources_and_split_count():
     assert bench.traffic_for("no such workload", splits) is None
 
 
+def test_traffic_record_matches_its_committed_summary():
+    """The counter summary the record names exists and states the same
+    source hash and the same bytes per launch."""
+    import os
+    rec = bench.TRAFFIC["c2"]
+    path = os.path.join(bench.ROOT, rec["source"])
+    text = open(path).read()
+    assert rec["kernels_sha256"] in text
+    assert f"{rec['bytes_per_launch'] / 1e6:.2f} MB" in text
+
+
 def test_host_workers_within_the_host_share():
     n = bench.host_workers()
     assert 1 <= n <= 16
